@@ -1,0 +1,513 @@
+/*
+ * mra_oracle.c — plain, slow CPU oracle for the MRA-2 forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and the
+ * cpu_baseline leg of bench.py may load this library.  The product path (the
+ * HIP library under block_sparse_approximate_amd/) never calls it, shares no
+ * code, header, table or helper with it, and must fail loudly when its own
+ * extension is missing.
+ *
+ * Source of the method: the page "深入解析 Transformers 中的 MRA 模型"
+ * ("A deep dive into the MRA model in Transformers"; cited below as [MRA]),
+ * sections "MraConfig：四个专属参数" (the four MRA parameters and the
+ * num_block formula), "第一步" (step 1: pooling and low-resolution logits),
+ * "第二步" (step 2: block selection with priors), "第三步" (step 3: exact
+ * attention on the selected blocks), "第四步" (step 4: merging the two
+ * resolutions), the engineering notes after step 4 (block size 32, N a
+ * multiple of 32) and "使用边界与结论" (bidirectional only).
+ * The dense reference follows the textbook scaled-dot-product softmax
+ * attention printed as "global MHRA" on the page "UniFormer ... MHRA"
+ * (cited as [MHRA]).
+ *
+ * Precision: selection is decided in fp32 in the fixed order written out
+ * below (sequential sums and fused multiply-add chains, no reassociation);
+ * every output value is computed in fp64.  Build with -O2 -ffp-contract=off
+ * and no fast-math so that the fp32 steps are exactly the operations
+ * written here.
+ *
+ * Readings of points the pages leave open (each one also appears in the
+ * design notes of the repository):
+ *   R1  logit scale tau = 1/sqrt(d) on both resolutions.
+ *   R2  the top-k ranks the row-max-normalised low-res logits
+ *       S_ij - max_j S_ij, globally over the (N/32)^2 block grid.
+ *   R3  num_block is a total per (batch, head), not per row.
+ *   R4  the budget uses the sequence length N.
+ *   R5  ties at the k-th score go to the smaller flat index i*nb + j.
+ *   R6  first-n prior: +5000 for rows i < n and +5000 for columns j < n
+ *       (additive).
+ *   R7  diagonal prior: +5000 where |i - j| <= floor(n/2).
+ *   R8  the low-resolution branch covers exactly the unselected blocks.
+ *   R9  a low-res cell stands for cnt_j keys, so its weight is
+ *       cnt_j * exp(S_ij).
+ *   R10 the shared row max cancels; the oracle uses one shift per token.
+ *   R11 no epsilon in the normaliser; 0/0 gives 0.
+ *   R12 empty query or key blocks score -inf; masked keys weigh 0; masked
+ *       query rows output 0; an empty block pools to the zero vector.
+ *   R13 selections are reported as ascending flat indices i*nb + j.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define MRA_BLOCK 32          /* [MRA] engineering notes: block size 32 */
+#define MRA_PRIOR_BIAS 5000.0f /* [MRA] step 2: a 5e3 bias forces priors */
+
+/* ------------------------------------------------------------------------ */
+/* Budget. [MRA] "MraConfig": num_block = (len // 32) * block_per_row,
+ * capped at (len // 32)^2 (reading R4: len is the sequence length).
+ * Returns -1 for an invalid argument. */
+int64_t oracle_num_block(int32_t seq_len, int32_t block_per_row)
+{
+    if (seq_len < MRA_BLOCK || seq_len % MRA_BLOCK != 0 || block_per_row < 1)
+        return -1;
+    int64_t nb = seq_len / MRA_BLOCK;
+    int64_t k = nb * (int64_t)block_per_row;
+    int64_t cap = nb * nb;
+    return k < cap ? k : cap;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Step 1, pooling ([MRA] "第一步"): the masked mean of each 32-token block.
+ * fp32 version, in the canonical order: acc starts at +0.0f and adds the
+ * valid tokens t = 0..31 of the block one after another; the mean is
+ * acc / (float)cnt, correctly rounded; an empty block gives zeros.
+ * x: [N, d] one head; mask: [N] (1 = valid) or NULL; xhat: [nb, d];
+ * cnt: [nb] (may be NULL). */
+void oracle_pool_f32(int32_t N, int32_t d, const float* x, const uint8_t* mask,
+                     float* xhat, int32_t* cnt)
+{
+    int32_t nb = N / MRA_BLOCK;
+    for (int32_t i = 0; i < nb; i++) {
+        int32_t c = 0;
+        for (int32_t t = 0; t < MRA_BLOCK; t++)
+            c += (mask == NULL || mask[i * MRA_BLOCK + t]) ? 1 : 0;
+        if (cnt)
+            cnt[i] = c;
+        for (int32_t ch = 0; ch < d; ch++) {
+            float acc = 0.0f;
+            for (int32_t t = 0; t < MRA_BLOCK; t++) {
+                int32_t tok = i * MRA_BLOCK + t;
+                if (mask == NULL || mask[tok])
+                    acc = acc + x[(int64_t)tok * d + ch];
+            }
+            xhat[(int64_t)i * d + ch] = c > 0 ? acc / (float)c : 0.0f;
+        }
+    }
+}
+
+/* The same masked block mean in fp64, used for output values only. */
+void oracle_pool_f64(int32_t N, int32_t d, const float* x, const uint8_t* mask,
+                     double* xhat)
+{
+    int32_t nb = N / MRA_BLOCK;
+    for (int32_t i = 0; i < nb; i++) {
+        int32_t c = 0;
+        for (int32_t t = 0; t < MRA_BLOCK; t++)
+            c += (mask == NULL || mask[i * MRA_BLOCK + t]) ? 1 : 0;
+        for (int32_t ch = 0; ch < d; ch++) {
+            double acc = 0.0;
+            for (int32_t t = 0; t < MRA_BLOCK; t++) {
+                int32_t tok = i * MRA_BLOCK + t;
+                if (mask == NULL || mask[tok])
+                    acc += (double)x[(int64_t)tok * d + ch];
+            }
+            xhat[(int64_t)i * d + ch] = c > 0 ? acc / (double)c : 0.0;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Step 1, low-resolution logits ([MRA] "第一步": query_hat @ key_hat^T),
+ * scaled by tau (reading R1).  Canonical fp32 order: a fused multiply-add
+ * chain over channels c = 0..d-1 starting from +0.0f, then one multiply by
+ * tau_f32 = (float)(1/sqrt(d)).  S: [nb, nb] row-major. */
+void oracle_lowres_logits_f32(int32_t nb, int32_t d, const float* qhat,
+                              const float* khat, float* S)
+{
+    float tau = (float)(1.0 / sqrt((double)d));
+    for (int32_t i = 0; i < nb; i++)
+        for (int32_t j = 0; j < nb; j++) {
+            float acc = 0.0f;
+            for (int32_t c = 0; c < d; c++)
+                acc = fmaf(qhat[(int64_t)i * d + c], khat[(int64_t)j * d + c], acc);
+            S[(int64_t)i * nb + j] = acc * tau;
+        }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Step 2, selection scores ([MRA] "第二步"; readings R2, R6, R7, R12).
+ *   rowmax_i = max over key blocks j with cnt_j > 0 of S_ij (-inf if none);
+ *   score_ij = S_ij - rowmax_i                                      (fp32)
+ *            + 5000 if the diagonal prior is on and |i-j| <= floor(g/2)
+ *            + 5000 if i < f   + 5000 if j < f                  (fp32 adds)
+ *   score_ij = -inf if cnt_i == 0 or cnt_j == 0;  -0.0 becomes +0.0.
+ * rowmax: [nb] (may be NULL), score: [nb, nb]. */
+void oracle_scores_f32(int32_t nb, const float* S, const int32_t* cnt,
+                       int32_t prior_first, int32_t prior_diag,
+                       float* rowmax, float* score)
+{
+    for (int32_t i = 0; i < nb; i++) {
+        float m = -INFINITY;
+        for (int32_t j = 0; j < nb; j++)
+            if (cnt[j] > 0 && S[(int64_t)i * nb + j] > m)
+                m = S[(int64_t)i * nb + j];
+        if (rowmax)
+            rowmax[i] = m;
+        for (int32_t j = 0; j < nb; j++) {
+            float s;
+            if (cnt[i] == 0 || cnt[j] == 0) {
+                s = -INFINITY;
+            } else {
+                s = S[(int64_t)i * nb + j] - m;
+                int32_t dist = i > j ? i - j : j - i;
+                if (prior_diag > 0 && dist <= prior_diag / 2)
+                    s = s + MRA_PRIOR_BIAS;
+                if (i < prior_first)
+                    s = s + MRA_PRIOR_BIAS;
+                if (j < prior_first)
+                    s = s + MRA_PRIOR_BIAS;
+                if (s == 0.0f)
+                    s = 0.0f; /* canonical +0.0 */
+            }
+            score[(int64_t)i * nb + j] = s;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Step 2, global top-k ([MRA] "第二步"; readings R3, R5, R13): the K cells
+ * that come first in the order (score descending, flat index ascending),
+ * written as ascending flat indices.  A library sort is the only tool. */
+typedef struct {
+    float s;
+    int32_t flat;
+} cell_t;
+
+static int cell_cmp(const void* a, const void* b)
+{
+    const cell_t* x = (const cell_t*)a;
+    const cell_t* y = (const cell_t*)b;
+    if (x->s > y->s) return -1;
+    if (x->s < y->s) return 1;
+    return x->flat < y->flat ? -1 : (x->flat > y->flat ? 1 : 0);
+}
+
+static int int_cmp(const void* a, const void* b)
+{
+    int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+    return x < y ? -1 : (x > y ? 1 : 0);
+}
+
+int oracle_select_top(int32_t nb, const float* score, int64_t K, int32_t* sel)
+{
+    int64_t n = (int64_t)nb * nb;
+    if (K < 0 || K > n)
+        return -1;
+    cell_t* cells = (cell_t*)malloc(sizeof(cell_t) * (size_t)n);
+    if (!cells)
+        return -2;
+    for (int64_t f = 0; f < n; f++) {
+        cells[f].s = score[f];
+        cells[f].flat = (int32_t)f;
+    }
+    qsort(cells, (size_t)n, sizeof(cell_t), cell_cmp);
+    for (int64_t r = 0; r < K; r++)
+        sel[r] = cells[r].flat;
+    qsort(sel, (size_t)K, sizeof(int32_t), int_cmp);
+    free(cells);
+    return 0;
+}
+
+/* Selection from given fp32 low-res logits and block counts (what the GPU
+ * selector is compared against on identical logits). */
+int oracle_select_from_logits(int32_t nb, const float* S, const int32_t* cnt,
+                              int64_t K, int32_t prior_first, int32_t prior_diag,
+                              int32_t* sel)
+{
+    float* score = (float*)malloc(sizeof(float) * (size_t)nb * nb);
+    if (!score)
+        return -2;
+    oracle_scores_f32(nb, S, cnt, prior_first, prior_diag, NULL, score);
+    int rc = oracle_select_top(nb, score, K, sel);
+    free(score);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* One (batch, head) unit of the whole forward pass.
+ * q,k,v: [N, d] fp32 values (bf16 inputs arrive widened exactly);
+ * mask: [N] or NULL; out: [N, d] fp64; sel: [K] or NULL (ascending flat). */
+typedef struct {
+    int32_t N, d, block_per_row, mode, prior_first, prior_diag;
+} head_args_t;
+
+static int oracle_mra_head(const head_args_t* a, const float* q, const float* k,
+                           const float* v, const uint8_t* mask, double* out,
+                           int32_t* sel_out)
+{
+    const int32_t N = a->N, d = a->d, nb = N / MRA_BLOCK;
+    const int64_t K = oracle_num_block(N, a->block_per_row);
+    const double tau = 1.0 / sqrt((double)d);
+    int rc = 0;
+
+    float* qh = (float*)malloc(sizeof(float) * (size_t)nb * d);
+    float* kh = (float*)malloc(sizeof(float) * (size_t)nb * d);
+    int32_t* cnt = (int32_t*)malloc(sizeof(int32_t) * (size_t)nb);
+    float* S = (float*)malloc(sizeof(float) * (size_t)nb * nb);
+    float* score = (float*)malloc(sizeof(float) * (size_t)nb * nb);
+    int32_t* sel = (int32_t*)malloc(sizeof(int32_t) * (size_t)(K > 0 ? K : 1));
+    uint8_t* chosen = (uint8_t*)calloc((size_t)nb * nb, 1);
+    double* qh64 = (double*)malloc(sizeof(double) * (size_t)nb * d);
+    double* kh64 = (double*)malloc(sizeof(double) * (size_t)nb * d);
+    double* vh64 = (double*)malloc(sizeof(double) * (size_t)nb * d);
+    double* s_hi = (double*)malloc(sizeof(double) * (size_t)N);
+    double* s_lo = (double*)malloc(sizeof(double) * (size_t)nb);
+    if (!qh || !kh || !cnt || !S || !score || !sel || !chosen || !qh64 || !kh64 ||
+        !vh64 || !s_hi || !s_lo) {
+        rc = -2;
+        goto done;
+    }
+
+    /* Steps 1 and 2 in fp32: pooled vectors, low-res logits, scores, top-k. */
+    oracle_pool_f32(N, d, q, mask, qh, cnt);
+    oracle_pool_f32(N, d, k, mask, kh, NULL);
+    oracle_lowres_logits_f32(nb, d, qh, kh, S);
+    oracle_scores_f32(nb, S, cnt, a->prior_first, a->prior_diag, NULL, score);
+    rc = oracle_select_top(nb, score, K, sel);
+    if (rc)
+        goto done;
+    for (int64_t r = 0; r < K; r++)
+        chosen[sel[r]] = 1;
+    if (sel_out)
+        memcpy(sel_out, sel, sizeof(int32_t) * (size_t)K);
+
+    /* fp64 pooled vectors for the low-resolution values (step 4). */
+    oracle_pool_f64(N, d, q, mask, qh64);
+    oracle_pool_f64(N, d, k, mask, kh64);
+    oracle_pool_f64(N, d, v, mask, vh64);
+
+    for (int32_t i = 0; i < nb; i++) {
+        /* Low-res logits of row i in fp64 for unselected, non-empty key
+         * blocks (full mode only; [MRA] step 4 and reading R8). */
+        if (a->mode == 0)
+            for (int32_t j = 0; j < nb; j++) {
+                s_lo[j] = -INFINITY;
+                if (!chosen[(int64_t)i * nb + j] && cnt[j] > 0) {
+                    double dot = 0.0;
+                    for (int32_t c = 0; c < d; c++)
+                        dot += qh64[(int64_t)i * d + c] * kh64[(int64_t)j * d + c];
+                    s_lo[j] = tau * dot;
+                }
+            }
+        for (int32_t t = i * MRA_BLOCK; t < (i + 1) * MRA_BLOCK; t++) {
+            double* o = out + (int64_t)t * d;
+            for (int32_t c = 0; c < d; c++)
+                o[c] = 0.0;
+            if (mask && !mask[t])
+                continue; /* reading R12: padded query rows output 0 */
+            /* Step 3: exact logits on the selected blocks of row i. */
+            double shift = -INFINITY;
+            for (int32_t j = 0; j < nb; j++) {
+                if (!chosen[(int64_t)i * nb + j])
+                    continue;
+                for (int32_t u = j * MRA_BLOCK; u < (j + 1) * MRA_BLOCK; u++) {
+                    s_hi[u] = -INFINITY;
+                    if (mask && !mask[u])
+                        continue;
+                    double dot = 0.0;
+                    for (int32_t c = 0; c < d; c++)
+                        dot += (double)q[(int64_t)t * d + c] * (double)k[(int64_t)u * d + c];
+                    s_hi[u] = tau * dot;
+                    if (s_hi[u] > shift)
+                        shift = s_hi[u];
+                }
+            }
+            if (a->mode == 0)
+                for (int32_t j = 0; j < nb; j++)
+                    if (s_lo[j] > shift)
+                        shift = s_lo[j];
+            if (shift == -INFINITY)
+                continue; /* nothing to attend to: 0/0 gives 0 (R11) */
+            double den = 0.0;
+            for (int32_t c = 0; c < d; c++)
+                o[c] = 0.0;
+            for (int32_t j = 0; j < nb; j++) {
+                if (!chosen[(int64_t)i * nb + j])
+                    continue;
+                for (int32_t u = j * MRA_BLOCK; u < (j + 1) * MRA_BLOCK; u++) {
+                    if (s_hi[u] == -INFINITY)
+                        continue;
+                    double w = exp(s_hi[u] - shift);
+                    den += w;
+                    for (int32_t c = 0; c < d; c++)
+                        o[c] += w * (double)v[(int64_t)u * d + c];
+                }
+            }
+            /* Step 4, full mode: the low-resolution attention on the
+             * unselected blocks, each cell weighted by its count (R9). */
+            if (a->mode == 0)
+                for (int32_t j = 0; j < nb; j++) {
+                    if (s_lo[j] == -INFINITY)
+                        continue;
+                    double w = (double)cnt[j] * exp(s_lo[j] - shift);
+                    den += w;
+                    for (int32_t c = 0; c < d; c++)
+                        o[c] += w * vh64[(int64_t)j * d + c];
+                }
+            if (den > 0.0)
+                for (int32_t c = 0; c < d; c++)
+                    o[c] /= den;
+            else
+                for (int32_t c = 0; c < d; c++)
+                    o[c] = 0.0;
+        }
+    }
+
+done:
+    free(qh); free(kh); free(cnt); free(S); free(score); free(sel); free(chosen);
+    free(qh64); free(kh64); free(vh64); free(s_hi); free(s_lo);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dense reference: softmax(tau * q k^T over valid keys) v for each valid
+ * query token ([MHRA] "global MHRA", reading R1 for tau); masked query
+ * rows and rows with no valid key give 0. */
+static int oracle_dense_head(int32_t N, int32_t d, const float* q, const float* k,
+                             const float* v, const uint8_t* mask, double* out)
+{
+    const double tau = 1.0 / sqrt((double)d);
+    double* s = (double*)malloc(sizeof(double) * (size_t)N);
+    if (!s)
+        return -2;
+    for (int32_t t = 0; t < N; t++) {
+        double* o = out + (int64_t)t * d;
+        for (int32_t c = 0; c < d; c++)
+            o[c] = 0.0;
+        if (mask && !mask[t])
+            continue;
+        double shift = -INFINITY;
+        for (int32_t u = 0; u < N; u++) {
+            s[u] = -INFINITY;
+            if (mask && !mask[u])
+                continue;
+            double dot = 0.0;
+            for (int32_t c = 0; c < d; c++)
+                dot += (double)q[(int64_t)t * d + c] * (double)k[(int64_t)u * d + c];
+            s[u] = tau * dot;
+            if (s[u] > shift)
+                shift = s[u];
+        }
+        if (shift == -INFINITY)
+            continue;
+        double den = 0.0;
+        for (int32_t u = 0; u < N; u++) {
+            if (s[u] == -INFINITY)
+                continue;
+            double w = exp(s[u] - shift);
+            den += w;
+            for (int32_t c = 0; c < d; c++)
+                o[c] += w * (double)v[(int64_t)u * d + c];
+        }
+        for (int32_t c = 0; c < d; c++)
+            o[c] /= den;
+    }
+    free(s);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Batched drivers: independent (batch, head) units spread over nthreads
+ * POSIX threads.  Each unit is computed by exactly the code above; the
+ * threads only decide which unit runs where. */
+typedef struct {
+    int32_t B, H, N, d;
+    const float *q, *k, *v;
+    const uint8_t* mask;
+    head_args_t ha;
+    double* out;
+    int32_t* sel;
+    int64_t K;
+    int dense;
+    int next; /* shared unit counter */
+    int rc;
+} job_t;
+
+static void* worker(void* p)
+{
+    job_t* j = (job_t*)p;
+    const int units = j->B * j->H;
+    for (;;) {
+        int u = __atomic_fetch_add(&j->next, 1, __ATOMIC_RELAXED);
+        if (u >= units)
+            break;
+        int b = u / j->H;
+        int64_t off = (int64_t)u * j->N * j->d;
+        const uint8_t* m = j->mask ? j->mask + (int64_t)b * j->N : NULL;
+        int rc;
+        if (j->dense)
+            rc = oracle_dense_head(j->N, j->d, j->q + off, j->k + off, j->v + off, m,
+                                   j->out + off);
+        else
+            rc = oracle_mra_head(&j->ha, j->q + off, j->k + off, j->v + off, m,
+                                 j->out + off, j->sel ? j->sel + (int64_t)u * j->K : NULL);
+        if (rc)
+            __atomic_store_n(&j->rc, rc, __ATOMIC_RELAXED);
+    }
+    return NULL;
+}
+
+static int run_jobs(job_t* j, int nthreads)
+{
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    pthread_t th[256];
+    int started = 0;
+    for (int t = 1; t < nthreads; t++)
+        if (pthread_create(&th[started], NULL, worker, j) == 0)
+            started++;
+    worker(j);
+    for (int t = 0; t < started; t++)
+        pthread_join(th[t], NULL);
+    return j->rc;
+}
+
+/* MRA-2 forward over [B, H, N, d] inputs.  mode 0 = "full", 1 = "sparse".
+ * Returns 0, or -1 for invalid arguments, -2 when out of memory. */
+int oracle_mra_fwd(int32_t B, int32_t H, int32_t N, int32_t d, const float* q,
+                   const float* k, const float* v, const uint8_t* mask,
+                   int32_t block_per_row, int32_t mode, int32_t prior_first,
+                   int32_t prior_diag, double* out, int32_t* sel, int32_t nthreads)
+{
+    int64_t K = oracle_num_block(N, block_per_row);
+    if (B < 1 || H < 1 || d < 1 || K < 0 || (mode != 0 && mode != 1) ||
+        prior_first < 0 || prior_diag < 0 || !q || !k || !v || !out)
+        return -1;
+    job_t j;
+    memset(&j, 0, sizeof(j));
+    j.B = B; j.H = H; j.N = N; j.d = d;
+    j.q = q; j.k = k; j.v = v; j.mask = mask;
+    j.ha.N = N; j.ha.d = d; j.ha.block_per_row = block_per_row; j.ha.mode = mode;
+    j.ha.prior_first = prior_first; j.ha.prior_diag = prior_diag;
+    j.out = out; j.sel = sel; j.K = K; j.dense = 0;
+    return run_jobs(&j, nthreads);
+}
+
+/* Dense softmax attention over [B, H, N, d] inputs (any N >= 1). */
+int oracle_dense_fwd(int32_t B, int32_t H, int32_t N, int32_t d, const float* q,
+                     const float* k, const float* v, const uint8_t* mask,
+                     double* out, int32_t nthreads)
+{
+    if (B < 1 || H < 1 || N < 1 || d < 1 || !q || !k || !v || !out)
+        return -1;
+    job_t j;
+    memset(&j, 0, sizeof(j));
+    j.B = B; j.H = H; j.N = N; j.d = d;
+    j.q = q; j.k = k; j.v = v; j.mask = mask;
+    j.out = out; j.dense = 1;
+    return run_jobs(&j, nthreads);
+}

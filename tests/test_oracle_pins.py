@@ -1,0 +1,371 @@
+"""Pins for the CPU oracle: each test ties it to something other than itself.
+
+These tests use the pages' worked example, closed forms, invariants,
+special cases that reduce to a library routine (torch's fp64 CPU
+scaled-dot-product attention, numpy's lexsort), and brute force on tiny
+inputs.  Each pin is chosen so that a plausible mistake in the oracle fails
+it: a dropped term, a wrong sign or index, or a transposed operand.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def sdpa64(q, k, v, allowed=None):
+    """torch fp64 CPU softmax(q k^T / sqrt(d)) v; allowed: bool [.., N, N] or None."""
+    tq, tk, tv = (torch.from_numpy(np.asarray(x, np.float64)) for x in (q, k, v))
+    m = None if allowed is None else torch.from_numpy(allowed)
+    return torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=m).numpy()
+
+
+def rand_qkv(B, H, N, d=64, seed=0, scale=1.0):
+    rng = np.random.default_rng(seed)
+    return [(rng.standard_normal((B, H, N, d)) * scale).astype(np.float32) for _ in range(3)]
+
+
+# ---------------------------------------------------------------- budget ----
+def test_budget_matches_worked_examples():
+    ex = json.load(open(os.path.join(GOLDEN, "budget_examples.json")))["examples"]
+    for e in ex:
+        assert e["seq_len"] // 32 == e["num_blocks_per_row"]
+        assert (e["seq_len"] // 32) ** 2 == e["full_grid"]
+        assert oracle.num_block(e["seq_len"], e["block_per_row"]) == e["num_block"]
+
+
+@pytest.mark.parametrize("N,bpr,expect", [
+    (16384, 8, 4096), (4096, 4, 512), (512, 16, 256), (512, 17, 256), (32, 1, 1), (32, 5, 1),
+    (48, 4, -1), (0, 4, -1), (512, 0, -1), (-32, 4, -1)])
+def test_budget_closed_form(N, bpr, expect):
+    assert oracle.num_block(N, bpr) == expect
+
+
+# ---------------------------------------------------------------- pooling ---
+def test_pool_hand_example():
+    N, d = 64, 4
+    x = np.tile(np.arange(N, dtype=np.float32)[:, None], (1, d))
+    x[:, 1] *= -1
+    mask = np.zeros(N, np.uint8)
+    mask[[0, 5, 31]] = 1          # block 0: tokens 0, 5, 31
+    mask[32:64] = 1               # block 1: all valid
+    xh, cnt = oracle.pool_f32(x, mask)
+    assert cnt.tolist() == [3, 32]
+    assert xh[0].tolist() == [12.0, -12.0, 12.0, 12.0]
+    assert xh[1, 0] == np.float32(np.mean(np.arange(32, 64)))
+    # an empty block pools to zeros
+    mask[:32] = 0
+    xh, cnt = oracle.pool_f32(x, mask)
+    assert cnt.tolist() == [0, 32] and np.all(xh[0] == 0)
+
+
+def test_pool_matches_fp64_mean():
+    rng = np.random.default_rng(7)
+    N, d = 256, 64
+    x = rng.standard_normal((N, d)).astype(np.float32)
+    mask = (rng.random(N) < 0.6).astype(np.uint8)
+    mask[64:96] = 0
+    xh, cnt = oracle.pool_f32(x, mask)
+    xh64 = oracle.pool_f64(x, mask)
+    for i in range(N // 32):
+        sel = mask[32 * i: 32 * i + 32].astype(bool)
+        assert cnt[i] == sel.sum()
+        ref = x[32 * i: 32 * i + 32][sel].astype(np.float64).mean(0) if sel.any() else np.zeros(d)
+        np.testing.assert_allclose(xh64[i], ref, rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(xh[i], ref, rtol=0, atol=4e-7 * max(1, np.abs(x).max()))
+
+
+# ---------------------------------------------------------------- logits ----
+def test_logits_match_scaled_matmul():
+    rng = np.random.default_rng(3)
+    nb, d = 24, 64
+    qh = rng.standard_normal((nb, d)).astype(np.float32)
+    kh = rng.standard_normal((nb, d)).astype(np.float32)
+    S = oracle.lowres_logits_f32(qh, kh)
+    ref = qh.astype(np.float64) @ kh.astype(np.float64).T / math.sqrt(d)
+    np.testing.assert_allclose(S, ref, rtol=0, atol=2e-5)
+    # not transposed: row i belongs to query block i
+    qh2 = qh.copy()
+    qh2[0] = 0
+    assert np.all(oracle.lowres_logits_f32(qh2, kh)[0] == 0)
+    assert np.any(oracle.lowres_logits_f32(qh2, kh)[:, 0] != 0)
+
+
+def test_logits_exact_on_small_integers():
+    # small integers: every product and partial sum is exact in fp32
+    rng = np.random.default_rng(4)
+    nb, d = 8, 64
+    qh = rng.integers(-8, 9, (nb, d)).astype(np.float32)
+    kh = rng.integers(-8, 9, (nb, d)).astype(np.float32)
+    S = oracle.lowres_logits_f32(qh, kh)
+    exact = (qh.astype(np.int64) @ kh.astype(np.int64).T).astype(np.float64) / 8.0
+    assert np.array_equal(S.astype(np.float64), exact)
+
+
+# ---------------------------------------------------------------- scores ----
+def test_scores_rowmax_priors_and_empty_blocks():
+    nb = 8
+    rng = np.random.default_rng(5)
+    S = rng.standard_normal((nb, nb)).astype(np.float32)
+    cnt = np.full(nb, 32, np.int32)
+    cnt[6] = 0
+    rowmax, sc = oracle.scores_f32(S, cnt, prior_first=2, prior_diag=3)
+    for i in range(nb):
+        valid = cnt > 0
+        assert rowmax[i] == S[i, valid].max()
+        for j in range(nb):
+            if cnt[i] == 0 or cnt[j] == 0:
+                assert sc[i, j] == -np.inf
+                continue
+            nprior = int(abs(i - j) <= 1) + int(i < 2) + int(j < 2)
+            s = np.float32(S[i, j] - rowmax[i])
+            for _ in range(nprior):
+                s = np.float32(s + np.float32(5000.0))
+            assert sc[i, j] == s, (i, j)
+    # each non-empty row's best block scores exactly 0 before priors
+    _, sc0 = oracle.scores_f32(S, cnt)
+    for i in range(nb):
+        if cnt[i]:
+            assert sc0[i].max() == 0.0 and not np.signbit(sc0[i].max())
+
+
+@pytest.mark.parametrize("g,half", [(1, 0), (2, 1), (3, 1), (5, 2)])
+def test_diagonal_band_width(g, half):
+    nb = 9
+    S = np.zeros((nb, nb), np.float32)
+    cnt = np.full(nb, 32, np.int32)
+    _, sc = oracle.scores_f32(S, cnt, prior_diag=g)
+    band = np.abs(np.subtract.outer(np.arange(nb), np.arange(nb))) <= half
+    assert np.array_equal(sc == 5000.0, band) and np.all(sc[~band] == 0.0)
+
+
+# ---------------------------------------------------------------- selection -
+def test_selection_matches_lexsort_with_ties():
+    rng = np.random.default_rng(11)
+    for nb, K in [(16, 64), (32, 100), (8, 64), (8, 1)]:
+        score = rng.integers(-5, 3, (nb, nb)).astype(np.float32)   # many ties
+        score[0, 3] = -np.inf
+        flat = np.arange(nb * nb)
+        order = np.lexsort((flat, -score.reshape(-1)))
+        ref = np.sort(order[:K])
+        assert np.array_equal(oracle.select_top(score, K), ref)
+
+
+def test_selection_all_equal_takes_first_flat_indices():
+    nb = 16
+    sel = oracle.select_top(np.zeros((nb, nb), np.float32), 37)
+    assert sel.tolist() == list(range(37))
+
+
+def test_selection_one_per_row_is_row_argmax():
+    # bpr = 1, no priors: each row's maximum scores exactly 0 and every other
+    # cell is negative, so the nb selected cells are the row argmaxes.
+    rng = np.random.default_rng(12)
+    nb = 16
+    S = rng.standard_normal((nb, nb)).astype(np.float32)
+    sel = oracle.select_from_logits(S, np.full(nb, 32, np.int32), nb)
+    assert np.array_equal(sel, np.arange(nb) * nb + S.argmax(1))
+
+
+# -------------------------------------------------------- closed-form sets --
+@pytest.mark.parametrize("pf,pd,bpr,cells", [
+    (0, 1, 1, lambda i, j: i == j),
+    (4, 0, 7, lambda i, j: i < 4 or j < 4),
+    (8, 0, 12, lambda i, j: i < 8 or j < 8),
+])
+def test_prior_sets_fill_budget_exactly(pf, pd, bpr, cells):
+    q, k, v = rand_qkv(1, 2, 512, seed=21)
+    out, sel = oracle.mra_forward(q, k, v, block_per_row=bpr, approx_mode="sparse",
+                                  prior_first=pf, prior_diag=pd, return_selection=True)
+    nb = 16
+    ref = [i * nb + j for i in range(nb) for j in range(nb) if cells(i, j)]
+    assert len(ref) == oracle.num_block(512, bpr)
+    for h in range(2):
+        assert sel[0, h].tolist() == ref
+
+
+# ----------------------------------------------------- reductions to dense --
+@pytest.mark.parametrize("mode", ["full", "sparse"])
+@pytest.mark.parametrize("N,bpr", [(512, 16), (64, 4)])
+def test_all_blocks_selected_equals_dense(mode, N, bpr):
+    q, k, v = rand_qkv(1, 2, N, seed=31)
+    assert oracle.num_block(N, bpr) == (N // 32) ** 2
+    out = oracle.mra_forward(q, k, v, block_per_row=bpr, approx_mode=mode)
+    np.testing.assert_allclose(out, sdpa64(q, k, v), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(oracle.dense_forward(q, k, v), sdpa64(q, k, v), rtol=0, atol=1e-12)
+
+
+def test_all_pairs_selected_with_mask_equals_masked_dense():
+    N = 256
+    q, k, v = rand_qkv(2, 2, N, seed=32)
+    mask = np.ones((2, N), np.uint8)
+    mask[0, 200:] = 0
+    mask[1, ::3] = 0
+    allowed = np.broadcast_to(mask[:, None, None, :].astype(bool), (2, 2, N, N)).copy()
+    ref = sdpa64(q, k, v, allowed)
+    ref[mask[:, None, :, None].repeat(2, 1).repeat(64, 3) == 0] = 0
+    for mode in ("full", "sparse"):
+        out = oracle.mra_forward(q, k, v, mask, block_per_row=8, approx_mode=mode)
+        np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(oracle.dense_forward(q, k, v, mask), ref, rtol=0, atol=1e-12)
+
+
+def test_priors_only_sparse_equals_block_masked_dense():
+    N, nb = 512, 16
+    q, k, v = rand_qkv(1, 2, N, seed=33)
+    out = oracle.mra_forward(q, k, v, block_per_row=7, approx_mode="sparse", prior_first=4)
+    blk = np.arange(N) // 32
+    allowed = (blk[:, None] < 4) | (blk[None, :] < 4)
+    np.testing.assert_allclose(out, sdpa64(q, k, v, allowed), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("masked", [False, True])
+def test_block_constant_qk_full_equals_dense(masked):
+    # Q and K constant over the valid tokens of each block: the exact logits of
+    # an unselected block all equal its low-res logit, so full mode must equal
+    # dense attention whatever the selection (pins the cnt_j weights and the merge).
+    N, nb, d = 256, 8, 64
+    rng = np.random.default_rng(34)
+    qb = rng.standard_normal((1, 2, nb, d)).astype(np.float32)
+    kb = rng.standard_normal((1, 2, nb, d)).astype(np.float32)
+    q = np.repeat(qb, 32, axis=2)
+    k = np.repeat(kb, 32, axis=2)
+    v = rng.standard_normal((1, 2, N, d)).astype(np.float32)
+    mask = None
+    allowed = None
+    if masked:
+        mask = (rng.random((1, N)) < 0.7).astype(np.uint8)
+        mask[0, 64:96] = 0
+        allowed = np.broadcast_to(mask[:, None, None, :].astype(bool), (1, 2, N, N)).copy()
+    ref = sdpa64(q, k, v, allowed)
+    if masked:
+        ref[:, :, mask[0] == 0, :] = 0
+    for bpr, pf, pd in [(1, 0, 0), (2, 1, 3), (3, 0, 1)]:
+        out = oracle.mra_forward(q, k, v, mask, block_per_row=bpr, approx_mode="full",
+                                 prior_first=pf, prior_diag=pd)
+        np.testing.assert_allclose(out, ref, rtol=0, atol=1e-11)
+
+
+# ------------------------------------------------------------ brute force ---
+def brute_force(q, k, v, mask, sel, mode):
+    """Materialise the N x N approximate weight matrix of one head: exact
+    exp(s) on selected blocks, exp(low-res logit) on every valid key of an
+    unselected block (full mode), nothing elsewhere."""
+    N, d = q.shape
+    nb = N // 32
+    q64, k64, v64 = (x.astype(np.float64) for x in (q, k, v))
+    m = np.ones(N, bool) if mask is None else mask.astype(bool)
+    chosen = np.zeros((nb, nb), bool)
+    chosen.reshape(-1)[sel] = True
+    logit = np.full((N, N), -np.inf)
+    exact = q64 @ k64.T / math.sqrt(d)
+    blk = np.arange(N) // 32
+    cnt = np.array([m[32 * j:32 * j + 32].sum() for j in range(nb)])
+    pooled = lambda x: np.stack([x[32 * j:32 * j + 32][m[32 * j:32 * j + 32]].mean(0)
+                                 if cnt[j] else np.zeros(d) for j in range(nb)])
+    low = pooled(q64) @ pooled(k64).T / math.sqrt(d)
+    for t in range(N):
+        for u in range(N):
+            if not m[u]:
+                continue
+            if chosen[blk[t], blk[u]]:
+                logit[t, u] = exact[t, u]
+            elif mode == "full":
+                logit[t, u] = low[blk[t], blk[u]]
+    out = np.zeros((N, d))
+    for t in range(N):
+        if not m[t] or np.all(logit[t] == -np.inf):
+            continue
+        w = np.exp(logit[t] - logit[t].max())
+        out[t] = w @ v64 / w.sum()
+    return out
+
+
+@pytest.mark.parametrize("mode,bpr,pf,pd,masked", [
+    ("full", 2, 0, 0, False), ("full", 3, 1, 1, True), ("sparse", 2, 0, 3, False),
+    ("sparse", 1, 0, 0, True), ("full", 1, 0, 0, False)])
+def test_brute_force_materialisation(mode, bpr, pf, pd, masked):
+    N = 256
+    q, k, v = rand_qkv(1, 2, N, seed=41 + bpr)
+    mask = None
+    if masked:
+        rng = np.random.default_rng(5)
+        mask = (rng.random((1, N)) < 0.8).astype(np.uint8)
+        mask[0, 32:64] = 0
+    out, sel = oracle.mra_forward(q, k, v, mask, block_per_row=bpr, approx_mode=mode,
+                                  prior_first=pf, prior_diag=pd, return_selection=True)
+    for h in range(2):
+        ref = brute_force(q[0, h], k[0, h], v[0, h], None if mask is None else mask[0],
+                          sel[0, h], mode)
+        np.testing.assert_allclose(out[0, h], ref, rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------- invariants ---
+@pytest.mark.parametrize("mode", ["full", "sparse"])
+def test_value_shift_and_scale_invariance(mode):
+    N = 512
+    q, k, v = rand_qkv(1, 2, N, seed=51)
+    # V on a 1/64 grid and shifts on a 1/4 grid keep v + c exact in fp32
+    v = (np.random.default_rng(9).integers(-256, 256, v.shape) / 64).astype(np.float32)
+    kw = dict(block_per_row=3, approx_mode=mode, prior_first=1, prior_diag=1)
+    base, sel = oracle.mra_forward(q, k, v, return_selection=True, **kw)
+    c = (np.arange(64) / 4 - 8).astype(np.float32)
+    shifted = oracle.mra_forward(q, k, v + c, **kw)
+    rows = np.any(base != 0, axis=-1)          # rows that attend to something
+    np.testing.assert_allclose(shifted[rows], (base + c)[rows], rtol=0, atol=1e-12)
+    scaled = oracle.mra_forward(q, k, v * np.float32(4.0), **kw)
+    np.testing.assert_allclose(scaled, 4 * base, rtol=1e-14, atol=1e-13)
+
+
+def test_sparse_rows_in_convex_hull_of_selected_values():
+    N, nb = 512, 16
+    q, k, v = rand_qkv(1, 1, N, seed=52)
+    out, sel = oracle.mra_forward(q, k, v, block_per_row=2, approx_mode="sparse",
+                                  return_selection=True)
+    chosen = np.zeros((nb, nb), bool)
+    chosen.reshape(-1)[sel[0, 0]] = True
+    for i in range(nb):
+        cols = np.nonzero(chosen[i])[0]
+        rows = slice(32 * i, 32 * i + 32)
+        if len(cols) == 0:
+            assert np.all(out[0, 0, rows] == 0)     # nothing selected: 0/0 -> 0
+            continue
+        vv = np.concatenate([v[0, 0, 32 * j:32 * j + 32] for j in cols])
+        assert np.all(out[0, 0, rows] <= vv.max(0) + 1e-12)
+        assert np.all(out[0, 0, rows] >= vv.min(0) - 1e-12)
+
+
+def test_masked_query_rows_are_zero_and_selection_skips_empty_blocks():
+    N, nb = 256, 8
+    q, k, v = rand_qkv(1, 1, N, seed=53)
+    mask = np.ones((1, N), np.uint8)
+    mask[0, 192:] = 0                       # blocks 6, 7 empty
+    mask[0, 5] = 0
+    out, sel = oracle.mra_forward(q, k, v, mask, block_per_row=4, return_selection=True)
+    assert np.all(out[0, 0, 192:] == 0) and np.all(out[0, 0, 5] == 0)
+    i, j = sel[0, 0] // nb, sel[0, 0] % nb
+    assert np.all(i < 6) and np.all(j < 6)   # 32 = K <= 36 valid pairs
+
+
+def test_selection_reading_on_named_workload_ties():
+    # The long sparse workload with priors (first 2, diagonal 3) has 884 prior
+    # cells for a budget of 512; the top of the order is always the priors.
+    w = workloads.iid("t", 1, 1, 4096, seed=3, scale=0.5, approx_mode="sparse",
+                      prior_first=2, prior_diag=3)
+    nb = 128
+    qh, cnt = oracle.pool_f32(w.q[0, 0])
+    kh, _ = oracle.pool_f32(w.k[0, 0])
+    S = oracle.lowres_logits_f32(qh, kh)
+    _, sc = oracle.scores_f32(S, cnt, 2, 3)
+    sel = oracle.select_top(sc, 512)
+    ii, jj = np.divmod(sel, nb)
+    prior = (np.abs(ii - jj) <= 1) | (ii < 2) | (jj < 2)
+    assert np.all(prior)
+    assert (sc > 2500).sum() == 884      # logit spread is far below the 5000 bias
