@@ -1,0 +1,202 @@
+"""MI355X-native MRA-2 multi-resolution approximate self-attention (forward).
+
+A thin binding over ``libmra.so`` (hand-written HIP kernels for gfx950 behind
+the C ABI in ``include/mra.h``).  This module only marshals arguments: torch
+supplies device memory and the current HIP stream; every step of the method
+runs in the library's kernels.  There is no CPU or PyTorch fallback: if the
+library is missing, importing the binding's entry points raises.
+
+Method: the page "A deep dive into the MRA model in Transformers"
+(深入解析 Transformers 中的 MRA 模型), steps 1-4 and the MraConfig section,
+whose parameter names the keyword arguments below keep.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["attention", "num_block", "workspace_size", "debug_stages", "debug_select",
+           "MraError", "library_path", "lib"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmra.so")
+_lib = None
+
+MODES = {"full": 0, "sparse": 1}
+DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+
+# Entry points declared in include/mra.h, with their ctypes signatures.
+_P, _I32, _I64, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+SIGNATURES = {
+    "mra_abi_version": ([], _I32),
+    "mra_status_string": ([_I32], ctypes.c_char_p),
+    "mra_num_block": ([_I32, _I32], _I64),
+    "mra_workspace_size": ([_P, _I32, _I32, ctypes.POINTER(_SZ)], ctypes.c_int),
+    "mra_attention_fwd": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P], ctypes.c_int),
+    "mra_debug_stages": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
+                          _P, _SZ, _P], ctypes.c_int),
+    "mra_debug_select": ([_P, _P, _P, _I32, _I32, _I32, _P, _P, _SZ, _P], ctypes.c_int),
+}
+
+
+class MraError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__("%s: status %d (%s)" % (what, status, _status_text(status)))
+        self.status = status
+
+
+class _Dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """Load libmra.so; raises when it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError("libmra.so is not built (run `python -m block_sparse_approximate_amd.build`"
+                              " or __graft_entry__.build()); there is no fallback path")
+        L = ctypes.CDLL(_LIB_PATH)
+        for name, (args, res) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def _status_text(status: int) -> str:
+    try:
+        return lib().mra_status_string(status).decode()
+    except Exception:  # pragma: no cover - library missing
+        return "?"
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise MraError(status, what)
+
+
+def num_block(seq_len: int, block_per_row: int) -> int:
+    return int(lib().mra_num_block(seq_len, block_per_row))
+
+
+def _dims(B, H, N, d, dtype_code) -> _Dims:
+    return _Dims(B, H, N, d, dtype_code)
+
+
+def workspace_size(batch, heads, seq_len, head_dim=64, dtype=torch.bfloat16, block_per_row=4,
+                   approx_mode="full") -> int:
+    n = _SZ(0)
+    dims = _dims(batch, heads, seq_len, head_dim, DTYPES.get(dtype, -1))
+    _check(lib().mra_workspace_size(ctypes.byref(dims), block_per_row, MODES.get(approx_mode, -1),
+                                    ctypes.byref(n)), "mra_workspace_size")
+    return n.value
+
+
+def _stream(t: torch.Tensor):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _check_inputs(q, k, v, mask):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError("%s must be a GPU tensor" % name)
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous [batch, heads, seq_len, head_dim] tensor" % name)
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share shape and dtype")
+    if q.dtype not in DTYPES:
+        raise ValueError("dtype must be float32 or bfloat16")
+    if mask is not None:
+        if mask.dtype == torch.bool:
+            raise ValueError("pass the mask as uint8 (1 = valid token)")
+        if (mask.dtype != torch.uint8 or mask.shape != (q.shape[0], q.shape[2]) or not mask.is_contiguous()
+                or mask.device != q.device):
+            raise ValueError("mask must be a contiguous uint8 [batch, seq_len] tensor on q's device")
+
+
+def attention(q, k, v, mask=None, block_per_row=4, approx_mode="full", initial_prior_first_n_blocks=0,
+              initial_prior_diagonal_n_blocks=0, out=None, workspace=None):
+    """MRA-2 forward on [batch, heads, seq_len, head_dim] tensors (bf16 or fp32).
+    mask: uint8 [batch, seq_len] (1 = valid) or None.  Returns `out`."""
+    _check_inputs(q, k, v, mask)
+    B, H, N, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    ws_bytes = workspace_size(B, H, N, d, q.dtype, block_per_row, approx_mode)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    dims = _dims(B, H, N, d, DTYPES[q.dtype])
+    st = lib().mra_attention_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), block_per_row,
+                                 MODES.get(approx_mode, -1), initial_prior_first_n_blocks,
+                                 initial_prior_diagonal_n_blocks, _ptr(out), _ptr(workspace),
+                                 workspace.numel(), _stream(q))
+    _check(st, "mra_attention_fwd")
+    return out
+
+
+def debug_stages(q, k, v, mask=None, block_per_row=4, approx_mode="full", initial_prior_first_n_blocks=0,
+                 initial_prior_diagonal_n_blocks=0):
+    """Steps 1-2 of the same kernels; returns a dict of device tensors:
+    qhat, khat, vhat (full mode), count, logits, rowmax, sel, error."""
+    _check_inputs(q, k, v, mask)
+    B, H, N, d = q.shape
+    nb = N // 32
+    K = num_block(N, block_per_row)
+    dev = q.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    r = {
+        "qhat": torch.empty(B, H, nb, d, **f32),
+        "khat": torch.empty(B, H, nb, d, **f32),
+        "vhat": torch.empty(B, H, nb, d, **f32) if approx_mode == "full" else None,
+        "count": torch.empty(B, nb, dtype=torch.int32, device=dev),
+        "logits": torch.empty(B, H, nb, nb, **f32),
+        "rowmax": torch.empty(B, H, nb, **f32),
+        "sel": torch.empty(B, H, max(K, 1), dtype=torch.int32, device=dev),
+        "error": torch.zeros(1, dtype=torch.int32, device=dev),
+    }
+    ws_bytes = workspace_size(B, H, N, d, q.dtype, block_per_row, approx_mode)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    dims = _dims(B, H, N, d, DTYPES[q.dtype])
+    st = lib().mra_debug_stages(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), block_per_row,
+                                MODES.get(approx_mode, -1), initial_prior_first_n_blocks,
+                                initial_prior_diagonal_n_blocks, _ptr(r["qhat"]), _ptr(r["khat"]),
+                                _ptr(r["vhat"]), _ptr(r["count"]), _ptr(r["logits"]), _ptr(r["rowmax"]),
+                                _ptr(r["sel"]), _ptr(r["error"]), _ptr(ws), ws_bytes, _stream(q))
+    _check(st, "mra_debug_stages")
+    r["sel"] = r["sel"][:, :, :K]
+    return r
+
+
+def debug_select(logits, count, batch, heads, block_per_row=4, initial_prior_first_n_blocks=0,
+                 initial_prior_diagonal_n_blocks=0):
+    """The step-2 selector alone on given fp32 logits [B, H, nb, nb] and
+    int32 counts [B, nb] (device tensors).  Returns sel [B, H, K] int32."""
+    nb = logits.shape[-1]
+    N = 32 * nb
+    K = num_block(N, block_per_row)
+    if logits.dtype != torch.float32 or not logits.is_contiguous() or logits.shape != (batch, heads, nb, nb):
+        raise ValueError("logits must be contiguous fp32 [B, H, nb, nb]")
+    if count.dtype != torch.int32 or not count.is_contiguous() or count.shape != (batch, nb):
+        raise ValueError("count must be contiguous int32 [B, nb]")
+    sel = torch.empty(batch, heads, max(K, 1), dtype=torch.int32, device=logits.device)
+    ws_bytes = workspace_size(batch, heads, N, 64, torch.bfloat16, block_per_row, "sparse")
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=logits.device)
+    dims = _dims(batch, heads, N, 64, 1)
+    st = lib().mra_debug_select(ctypes.byref(dims), _ptr(logits), _ptr(count), block_per_row,
+                                initial_prior_first_n_blocks, initial_prior_diagonal_n_blocks, _ptr(sel),
+                                _ptr(ws), ws_bytes, _stream(logits))
+    _check(st, "mra_debug_select")
+    return sel[:, :, :K]

@@ -1,0 +1,291 @@
+// mra_api.hip — host side of the C ABI declared in include/mra.h:
+// argument checks, workspace carve and the launch sequence on one stream.
+//
+//   pool            step 1 pooling, counts, mask words; clears the
+//                   selection histogram
+//   logits_select   step 1 logits + step 2 selection (CSR, bitmap, items)
+//   lowres          step 4 low-res attention on unselected blocks (full only)
+//   attn            step 3 block attention; finishes rows that fit one item
+//   merge           joins the partials of longer rows (and the low-res part)
+// Everything after the argument checks is asynchronous; nothing here waits.
+#include <string.h>
+
+#include "../../include/mra.h"
+#include "mra_common.h"
+
+#define MRA_API extern "C" __attribute__((visibility("default")))
+
+namespace mra {
+namespace {
+
+constexpr int32_t kAbiVersion = 1;
+constexpr int32_t kMaxSeqLen = 16384;
+
+size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool carve(const mra_dims& d, int32_t bpr, int32_t mode, Layout* L) {
+    L->B = d.batch; L->H = d.heads; L->N = d.seq_len; L->d = d.head_dim;
+    L->nb = d.seq_len / kBlock;
+    L->BH = d.batch * d.heads;
+    L->K = mra_num_block(d.seq_len, bpr);
+    if (L->K < 0) return false;
+    L->max_items = L->nb + (int32_t)((L->K + kChunk - 1) / kChunk);
+    const size_t BH = (size_t)L->BH, nb = (size_t)L->nb, dd = (size_t)d.head_dim;
+    const size_t words = (nb + 31) / 32;
+    size_t o = 256;  // first 256 bytes: device error word
+    auto take = [&](size_t bytes) { size_t at = o; o = up256(o + bytes); return at; };
+    L->qhat = take(BH * nb * dd * 4);
+    L->khat = take(BH * nb * dd * 4);
+    L->vhat = mode == MRA_APPROX_FULL ? take(BH * nb * dd * 4) : 0;
+    L->cnt = take((size_t)d.batch * nb * 4);
+    L->mbits = take((size_t)d.batch * nb * 4);
+    L->logits = take(BH * nb * nb * 4);
+    L->rowmax = take(BH * nb * 4);
+    L->hist = take(BH * kHistBins * 4);
+    L->done = take(BH * 4);
+    L->thresh = take(BH * 8);
+    L->row_ptr = take(BH * (nb + 1) * 4);
+    L->col = take(BH * (size_t)L->K * 4);
+    L->selbits = take(BH * nb * words * 4);
+    L->item_ptr = take(BH * (nb + 1) * 4);
+    L->items = take(BH * (size_t)L->max_items * 8);
+    L->n_items = take(BH * 4);
+    L->lo_o = mode == MRA_APPROX_FULL ? take(BH * nb * dd * 4) : 0;
+    L->lo_l = mode == MRA_APPROX_FULL ? take(BH * nb * 4) : 0;
+    L->part_o = take(BH * (size_t)L->max_items * kBlock * dd * 4);
+    L->part_ml = take(BH * (size_t)L->max_items * 2 * kBlock * 4);
+    L->total = o;
+    return true;
+}
+
+mra_status check_dims(const mra_dims* d) {
+    if (!d) return MRA_ERR_NULL;
+    if (d->batch < 1 || d->heads < 1) return MRA_ERR_SHAPE;
+    if (d->seq_len < kBlock || d->seq_len % kBlock != 0 || d->seq_len > kMaxSeqLen) return MRA_ERR_SEQ_LEN;
+    if (d->head_dim != kHeadDim) return MRA_ERR_HEAD_DIM;
+    if (d->dtype != MRA_F32 && d->dtype != MRA_BF16) return MRA_ERR_DTYPE;
+    if ((int64_t)d->batch * d->heads > (1 << 20)) return MRA_ERR_SHAPE;
+    return MRA_OK;
+}
+
+mra_status check_params(int32_t bpr, int32_t mode, int32_t pf, int32_t pd) {
+    if (mode != MRA_APPROX_FULL && mode != MRA_APPROX_SPARSE) return MRA_ERR_MODE;
+    if (bpr < 1) return MRA_ERR_BUDGET;
+    if (pf < 0 || pd < 0) return MRA_ERR_PRIOR;
+    return MRA_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
+
+Params make_params(const mra_dims& d, const Layout& L, int32_t mode, int32_t pf, int32_t pd, const void* q,
+                   const void* k, const void* v, const uint8_t* mask, void* out, void* ws) {
+    Params p;
+    memset(&p, 0, sizeof(p));
+    unsigned char* w = static_cast<unsigned char*>(ws);
+    p.B = L.B; p.H = L.H; p.N = L.N; p.d = L.d; p.nb = L.nb; p.BH = L.BH;
+    p.words = (L.nb + 31) / 32;
+    p.K = L.K;
+    p.mode = mode;
+    p.dtype = d.dtype;
+    p.prior_first = pf;
+    p.prior_diag = pd;
+    p.max_items = L.max_items;
+    p.q = q; p.k = k; p.v = v; p.mask = mask; p.out = out;
+    p.qhat = reinterpret_cast<float*>(w + L.qhat);
+    p.khat = reinterpret_cast<float*>(w + L.khat);
+    p.vhat = L.vhat ? reinterpret_cast<float*>(w + L.vhat) : nullptr;
+    p.cnt = reinterpret_cast<int32_t*>(w + L.cnt);
+    p.mbits = reinterpret_cast<uint32_t*>(w + L.mbits);
+    p.logits = reinterpret_cast<float*>(w + L.logits);
+    p.rowmax = reinterpret_cast<float*>(w + L.rowmax);
+    p.hist = reinterpret_cast<uint32_t*>(w + L.hist);
+    p.done = reinterpret_cast<uint32_t*>(w + L.done);
+    p.thresh = reinterpret_cast<uint64_t*>(w + L.thresh);
+    p.row_ptr = reinterpret_cast<int32_t*>(w + L.row_ptr);
+    p.col = reinterpret_cast<int32_t*>(w + L.col);
+    p.selbits = reinterpret_cast<uint32_t*>(w + L.selbits);
+    p.item_ptr = reinterpret_cast<int32_t*>(w + L.item_ptr);
+    p.items = reinterpret_cast<int2*>(w + L.items);
+    p.n_items = reinterpret_cast<int32_t*>(w + L.n_items);
+    p.lo_o = L.lo_o ? reinterpret_cast<float*>(w + L.lo_o) : nullptr;
+    p.lo_l = L.lo_l ? reinterpret_cast<float*>(w + L.lo_l) : nullptr;
+    p.part_o = reinterpret_cast<float*>(w + L.part_o);
+    p.part_ml = reinterpret_cast<float*>(w + L.part_ml);
+    p.error = reinterpret_cast<int32_t*>(w);
+    return p;
+}
+
+// Common checks of mra_attention_fwd and mra_debug_stages.
+mra_status check_call(const mra_dims* dims, const void* q, const void* k, const void* v, const uint8_t* mask,
+                      int32_t bpr, int32_t mode, int32_t pf, int32_t pd, const void* out, const void* ws,
+                      size_t ws_bytes, bool need_out, Layout* L) {
+    mra_status st = check_dims(dims);
+    if (st != MRA_OK) return st;
+    st = check_params(bpr, mode, pf, pd);
+    if (st != MRA_OK) return st;
+    if (!q || !k || !v || (need_out && !out)) return MRA_ERR_NULL;
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(mask) || (out && misaligned(out)))
+        return MRA_ERR_ALIGN;
+    if (!carve(*dims, bpr, mode, L)) return MRA_ERR_SEQ_LEN;
+    if (!ws || ws_bytes < L->total) return MRA_ERR_WORKSPACE;
+    if (((uintptr_t)ws & 255u) != 0) return MRA_ERR_ALIGN;
+    const size_t esz = dims->dtype == MRA_BF16 ? 2 : 4;
+    const size_t tb = (size_t)dims->batch * dims->heads * dims->seq_len * dims->head_dim * esz;
+    if (out && (overlaps(out, tb, q, tb) || overlaps(out, tb, k, tb) || overlaps(out, tb, v, tb) ||
+                overlaps(out, tb, mask, (size_t)dims->batch * dims->seq_len) || overlaps(out, tb, ws, ws_bytes)))
+        return MRA_ERR_ALIAS;
+    return MRA_OK;
+}
+
+__global__ void csr_to_flat_kernel(const int32_t* row_ptr, const int32_t* col, int nb, int64_t K, int BH,
+                                   int32_t* sel) {
+    const int x = blockIdx.x * blockDim.x + threadIdx.x;
+    if (x >= BH * nb) return;
+    const int bh = x / nb, i = x - bh * nb;
+    const int32_t* rp = row_ptr + (size_t)bh * (nb + 1);
+    for (int e = rp[i]; e < rp[i + 1]; e++) {
+        if (e >= 0 && e < K) sel[(size_t)bh * K + e] = i * nb + col[(size_t)bh * K + e];
+    }
+}
+
+}  // namespace
+}  // namespace mra
+
+using namespace mra;
+
+MRA_API int32_t mra_abi_version(void) { return kAbiVersion; }
+
+MRA_API const char* mra_status_string(int32_t s) {
+    switch (s) {
+        case MRA_OK: return "ok";
+        case MRA_ERR_NULL: return "a required pointer is NULL";
+        case MRA_ERR_SHAPE: return "batch/heads out of range";
+        case MRA_ERR_SEQ_LEN: return "seq_len must be a multiple of 32 in [32, 16384]";
+        case MRA_ERR_HEAD_DIM: return "head_dim must be 64";
+        case MRA_ERR_DTYPE: return "dtype must be MRA_F32 or MRA_BF16";
+        case MRA_ERR_MODE: return "approx_mode must be full (0) or sparse (1)";
+        case MRA_ERR_BUDGET: return "block_per_row must be >= 1";
+        case MRA_ERR_PRIOR: return "prior counts must be >= 0";
+        case MRA_ERR_ALIAS: return "out overlaps an input or the workspace";
+        case MRA_ERR_WORKSPACE: return "workspace missing or too small";
+        case MRA_ERR_HIP: return "a HIP launch failed";
+        case MRA_ERR_ALIGN: return "a pointer is not aligned (tensors 16 bytes, workspace 256 bytes)";
+        default: return "unknown status";
+    }
+}
+
+MRA_API int64_t mra_num_block(int32_t seq_len, int32_t block_per_row) {
+    if (seq_len < kBlock || seq_len % kBlock != 0 || block_per_row < 1) return -1;
+    const int64_t nb = seq_len / kBlock;
+    const int64_t k = nb * (int64_t)block_per_row, cap = nb * nb;
+    return k < cap ? k : cap;
+}
+
+MRA_API mra_status mra_workspace_size(const mra_dims* dims, int32_t block_per_row, int32_t approx_mode,
+                                      size_t* bytes) {
+    if (!bytes) return MRA_ERR_NULL;
+    mra_status st = check_dims(dims);
+    if (st != MRA_OK) return st;
+    st = check_params(block_per_row, approx_mode, 0, 0);
+    if (st != MRA_OK) return st;
+    Layout L;
+    if (!carve(*dims, block_per_row, approx_mode, &L)) return MRA_ERR_SEQ_LEN;
+    *bytes = L.total;
+    return MRA_OK;
+}
+
+static mra_status run_front(const Params& p, hipStream_t s) {
+    if (launch_pool(p, s) != hipSuccess) return MRA_ERR_HIP;
+    if (launch_logits_select(p, s) != hipSuccess) return MRA_ERR_HIP;
+    return MRA_OK;
+}
+
+MRA_API mra_status mra_attention_fwd(const mra_dims* dims, const void* q, const void* k, const void* v,
+                                     const uint8_t* mask, int32_t block_per_row, int32_t approx_mode,
+                                     int32_t prior_first, int32_t prior_diag, void* out, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+    Layout L;
+    mra_status st = check_call(dims, q, k, v, mask, block_per_row, approx_mode, prior_first, prior_diag, out,
+                               workspace, workspace_bytes, true, &L);
+    if (st != MRA_OK) return st;
+    const Params p = make_params(*dims, L, approx_mode, prior_first, prior_diag, q, k, v, mask, out, workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = run_front(p, s);
+    if (st != MRA_OK) return st;
+    if (approx_mode == MRA_APPROX_FULL && launch_lowres(p, s) != hipSuccess) return MRA_ERR_HIP;
+    if (launch_attn(p, s) != hipSuccess) return MRA_ERR_HIP;
+    if (launch_merge(p, s) != hipSuccess) return MRA_ERR_HIP;
+    return MRA_OK;
+}
+
+MRA_API mra_status mra_debug_stages(const mra_dims* dims, const void* q, const void* k, const void* v,
+                                    const uint8_t* mask, int32_t block_per_row, int32_t approx_mode,
+                                    int32_t prior_first, int32_t prior_diag, float* qhat, float* khat,
+                                    float* vhat, int32_t* count, float* logits, float* rowmax, int32_t* sel,
+                                    int32_t* error, void* workspace, size_t workspace_bytes, void* stream) {
+    Layout L;
+    mra_status st = check_call(dims, q, k, v, mask, block_per_row, approx_mode, prior_first, prior_diag,
+                               nullptr, workspace, workspace_bytes, false, &L);
+    if (st != MRA_OK) return st;
+    const Params p = make_params(*dims, L, approx_mode, prior_first, prior_diag, q, k, v, mask, nullptr,
+                                 workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = run_front(p, s);
+    if (st != MRA_OK) return st;
+    const size_t BH = (size_t)L.BH, nb = (size_t)L.nb, dd = (size_t)L.d;
+    hipError_t e = hipSuccess;
+    auto cp = [&](void* dst, const void* src, size_t bytes) {
+        if (dst && e == hipSuccess) e = hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s);
+    };
+    cp(qhat, p.qhat, BH * nb * dd * 4);
+    cp(khat, p.khat, BH * nb * dd * 4);
+    if (p.vhat) cp(vhat, p.vhat, BH * nb * dd * 4);
+    cp(count, p.cnt, (size_t)L.B * nb * 4);
+    cp(logits, p.logits, BH * nb * nb * 4);
+    cp(rowmax, p.rowmax, BH * nb * 4);
+    cp(error, p.error, 4);
+    if (e != hipSuccess) return MRA_ERR_HIP;
+    if (sel) {
+        const int total = L.BH * L.nb;
+        hipLaunchKernelGGL(csr_to_flat_kernel, dim3((total + 255) / 256), dim3(256), 0, s, p.row_ptr, p.col, L.nb,
+                           L.K, L.BH, sel);
+        if (hipGetLastError() != hipSuccess) return MRA_ERR_HIP;
+    }
+    return MRA_OK;
+}
+
+MRA_API mra_status mra_debug_select(const mra_dims* dims, const float* logits, const int32_t* count,
+                                    int32_t block_per_row, int32_t prior_first, int32_t prior_diag, int32_t* sel,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+    mra_status st = check_dims(dims);
+    if (st != MRA_OK) return st;
+    st = check_params(block_per_row, MRA_APPROX_SPARSE, prior_first, prior_diag);
+    if (st != MRA_OK) return st;
+    if (!logits || !count || !sel) return MRA_ERR_NULL;
+    Layout L;
+    if (!carve(*dims, block_per_row, MRA_APPROX_SPARSE, &L)) return MRA_ERR_SEQ_LEN;
+    if (!workspace || workspace_bytes < L.total) return MRA_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255u) != 0) return MRA_ERR_ALIGN;
+    Params p = make_params(*dims, L, MRA_APPROX_SPARSE, prior_first, prior_diag, nullptr, nullptr, nullptr,
+                           nullptr, nullptr, workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t BH = (size_t)L.BH, nb = (size_t)L.nb;
+    hipError_t e = hipMemcpyAsync(p.logits, logits, BH * nb * nb * 4, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(p.cnt, count, (size_t)L.B * nb * 4, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess) e = hipMemsetAsync(p.hist, 0, BH * kHistBins * 4, s);
+    if (e == hipSuccess) e = hipMemsetAsync(p.done, 0, BH * 4, s);
+    if (e == hipSuccess) e = hipMemsetAsync(p.error, 0, 4, s);
+    if (e != hipSuccess) return MRA_ERR_HIP;
+    if (launch_select_from_logits(p, s) != hipSuccess) return MRA_ERR_HIP;
+    const int total = L.BH * L.nb;
+    hipLaunchKernelGGL(csr_to_flat_kernel, dim3((total + 255) / 256), dim3(256), 0, s, p.row_ptr, p.col, L.nb, L.K,
+                       L.BH, sel);
+    if (hipGetLastError() != hipSuccess) return MRA_ERR_HIP;
+    return MRA_OK;
+}

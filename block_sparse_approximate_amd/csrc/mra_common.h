@@ -1,0 +1,116 @@
+// mra_common.h — types, constants and device helpers shared by the HIP
+// kernels of the MRA-2 forward pass (gfx950, wave64).
+//
+// Method: "A deep dive into the MRA model in Transformers" (cited [MRA]),
+// steps 1-4.  Everything here is device code or launch plumbing for this
+// library only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mra {
+
+constexpr int kBlock = 32;              // [MRA] engineering notes: block size 32
+constexpr int kHeadDim = 64;            // head dims this build accepts
+constexpr int kHistBits = 12;           // first radix digit of the selection key
+constexpr int kHistBins = 1 << kHistBits;
+constexpr float kPriorBias = 5000.0f;   // [MRA] step 2: 5e3 bias for forced blocks
+constexpr int kChunk = 8;               // max selected key blocks per attention work item
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Workspace carve, shared by the host dispatcher and the kernels.
+struct Layout {
+    int32_t B, H, N, d, nb, BH;
+    int64_t K;            // selection budget per (batch, head)
+    int32_t max_items;    // attention work items per head, upper bound
+    size_t qhat, khat, vhat, cnt, mbits, logits, rowmax, hist, done, thresh,
+        row_ptr, col, selbits, item_ptr, items, n_items, lo_o, lo_l, part_o, part_ml, total;
+};
+
+// Everything a kernel needs, passed by value.
+struct Params {
+    int32_t B, H, N, d, nb, BH, words;  // words = u32 words per selection-bitmap row
+    int64_t K;
+    int32_t mode;          // 0 full, 1 sparse
+    int32_t dtype;         // 0 fp32, 1 bf16
+    int32_t prior_first, prior_diag;
+    int32_t max_items;
+    const void* q;
+    const void* k;
+    const void* v;
+    const uint8_t* mask;   // [B, N] or null
+    void* out;
+    float* qhat;           // [BH, nb, d]
+    float* khat;
+    float* vhat;           // full mode only
+    int32_t* cnt;          // [B, nb] valid tokens per block
+    uint32_t* mbits;       // [B, nb] bit t = token t of the block is valid
+    float* logits;         // [BH, nb, nb]  tau * qhat_i . khat_j
+    float* rowmax;         // [BH, nb]      max over valid j of logits
+    uint32_t* hist;        // [BH, kHistBins]
+    uint32_t* done;        // [BH] workgroups finished per head (logits stage)
+    uint64_t* thresh;      // [BH] composite key of the last selected cell
+    int32_t* row_ptr;      // [BH, nb + 1]  CSR of the selection
+    int32_t* col;          // [BH, K]
+    uint32_t* selbits;     // [BH, nb, words]
+    int32_t* item_ptr;     // [BH, nb + 1]  first work item of each block row
+    int2* items;           // [BH, max_items] (block row, chunk)
+    int32_t* n_items;      // [BH]
+    float* lo_o;           // [BH, nb, d]   low-res numerator (shifted by rowmax)
+    float* lo_l;           // [BH, nb]      low-res denominator
+    float* part_o;         // [BH, max_items, 32, d] un-normalised high-res numerators
+    float* part_ml;        // [BH, max_items, 2, 32] running max (log2 units) and sum
+    int32_t* error;        // device error flag (0 = fine)
+};
+
+// Ordered key of an fp32 score: larger score -> larger unsigned key.
+__device__ __forceinline__ uint32_t float_key(float s) {
+    uint32_t u = __float_as_uint(s);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Step 2 score of cell (i, j) ([MRA] "第二步"): row-max-normalised low-res
+// logit plus 5000 per prior that covers the cell; -inf for empty blocks;
+// -0 folded to +0.  The fp32 operations and their order are fixed (this
+// translation unit is built with -ffp-contract=off).
+__device__ __forceinline__ float cell_score(float logit, float m, int i, int j, bool vi, bool vj,
+                                            int pf, int pd) {
+    if (!vi || !vj) return -__builtin_inff();
+    float s = logit - m;
+    int dist = i > j ? i - j : j - i;
+    if (pd > 0 && dist <= pd / 2) s = s + kPriorBias;
+    if (i < pf) s = s + kPriorBias;
+    if (j < pf) s = s + kPriorBias;
+    if (s == 0.0f) s = 0.0f;
+    return s;
+}
+
+// Composite key: score first, then the smaller flat index wins a tie.
+__device__ __forceinline__ uint64_t cell_key64(uint32_t key32, uint32_t flat) {
+    return ((uint64_t)key32 << 32) | (uint64_t)(0xFFFFFFFFu - flat);
+}
+
+__device__ __forceinline__ float bf16_to_float(uint16_t b) {
+    return __uint_as_float((uint32_t)b << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t float_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+}  // namespace mra
+
+// Host-side launchers (one per translation unit).
+namespace mra {
+hipError_t launch_pool(const Params& p, hipStream_t s);
+hipError_t launch_logits_select(const Params& p, hipStream_t s);
+hipError_t launch_select_from_logits(const Params& p, hipStream_t s);
+hipError_t launch_lowres(const Params& p, hipStream_t s);
+hipError_t launch_attn(const Params& p, hipStream_t s);
+hipError_t launch_merge(const Params& p, hipStream_t s);
+size_t logits_select_lds_bytes(int nb);
+}  // namespace mra

@@ -1,0 +1,141 @@
+/*
+ * mra.h — C ABI of the MI355X (gfx950) MRA-2 forward-pass library
+ * (libmra.so, built from block_sparse_approximate_amd/csrc).
+ *
+ * The method is MRA-2 multi-resolution approximate self-attention as
+ * described on the page "深入解析 Transformers 中的 MRA 模型" ("A deep dive
+ * into the MRA model in Transformers", cited [MRA]):
+ *   step 1 ("第一步")  average-pool Q and K (and V) over 32-token blocks and
+ *                      form the low-resolution block logits;
+ *   step 2 ("第二步")  pick the top num_block block pairs globally, with
+ *                      optional first-n and diagonal priors (a 5e3 bias);
+ *   step 3 ("第三步")  exact softmax attention on the selected 32x32 blocks;
+ *   step 4 ("第四步")  "full" mode merges it with low-resolution attention on
+ *                      the unselected blocks through a shared row maximum and
+ *                      normaliser; "sparse" mode keeps the high-res part only.
+ * Parameters and budget: section "MraConfig：四个专属参数" (block_per_row,
+ * approx_mode, initial_prior_first_n_blocks, initial_prior_diagonal_n_blocks,
+ * num_block = (N/32)*block_per_row capped at (N/32)^2).  N must be a
+ * multiple of 32 (engineering notes after step 4).  Attention is
+ * bidirectional (section "使用边界与结论").
+ *
+ * Readings of points the pages leave open: the logit scale is 1/sqrt(d);
+ * selection ranks the row-max-normalised low-res logits; ties at the k-th
+ * score go to the smaller flat index i*nb + j; the first-n prior adds 5000
+ * to rows i < n and again to columns j < n; the diagonal prior covers
+ * |i - j| <= floor(n/2); a low-res cell weighs cnt_j * exp(logit); an empty
+ * block scores -inf; padded query rows output 0; 0/0 gives 0.
+ *
+ * Conventions for every entry point:
+ *   - Tensors are row-major and contiguous.  q, k, v, out: [batch, heads,
+ *     seq_len, head_dim] in the dtype of `dims->dtype`; out has the same
+ *     dtype.  mask: [batch, seq_len] uint8, nonzero = valid token, or NULL
+ *     (every token valid).
+ *   - Pointers named device pointers are device memory owned by the caller;
+ *     q, k, v, out and mask must be 16-byte aligned; the library allocates
+ *     nothing and keeps no state between calls.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is queued
+ *     asynchronously on it; nothing synchronises.
+ *   - Arguments are checked on the host before anything is queued; on an
+ *     error nothing is written and the status says why.  MRA_ERR_HIP means a
+ *     launch failed; the outputs are then undefined.
+ *   - Calls that share a workspace must not overlap in time.
+ */
+#ifndef MRA_H
+#define MRA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MRA_OK = 0,
+    MRA_ERR_NULL = 1,       /* a required pointer is NULL */
+    MRA_ERR_SHAPE = 2,      /* batch or heads < 1, or the sizes overflow */
+    MRA_ERR_SEQ_LEN = 3,    /* seq_len not a multiple of 32, < 32 or > 16384 */
+    MRA_ERR_HEAD_DIM = 4,   /* head_dim other than 64 */
+    MRA_ERR_DTYPE = 5,      /* dtype not MRA_F32 or MRA_BF16 */
+    MRA_ERR_MODE = 6,       /* approx_mode not MRA_APPROX_FULL or MRA_APPROX_SPARSE */
+    MRA_ERR_BUDGET = 7,     /* block_per_row < 1 */
+    MRA_ERR_PRIOR = 8,      /* a prior count < 0 */
+    MRA_ERR_ALIAS = 9,      /* out overlaps an input or the workspace */
+    MRA_ERR_WORKSPACE = 10, /* workspace NULL or smaller than mra_workspace_size() */
+    MRA_ERR_HIP = 11,       /* a HIP call failed */
+    MRA_ERR_ALIGN = 12      /* a tensor pointer is not 16-byte aligned */
+} mra_status;
+
+typedef enum { MRA_F32 = 0, MRA_BF16 = 1 } mra_dtype;
+typedef enum { MRA_APPROX_FULL = 0, MRA_APPROX_SPARSE = 1 } mra_approx_mode;
+
+typedef struct {
+    int32_t batch;
+    int32_t heads;
+    int32_t seq_len;  /* N: multiple of 32, 32 <= N <= 16384 */
+    int32_t head_dim; /* d: 64 */
+    int32_t dtype;    /* mra_dtype */
+} mra_dims;
+
+/* Version of this ABI (changes when a signature or a layout changes). */
+int32_t mra_abi_version(void);
+
+/* Static text for a status code; never NULL. */
+const char* mra_status_string(int32_t status);
+
+/* Selection budget per (batch, head) ([MRA] "MraConfig" section):
+ * min((seq_len/32) * block_per_row, (seq_len/32)^2).  Returns -1 when
+ * seq_len is not a positive multiple of 32 or block_per_row < 1. */
+int64_t mra_num_block(int32_t seq_len, int32_t block_per_row);
+
+/* Bytes of device workspace mra_attention_fwd needs for these sizes.
+ * Host-only; *bytes is written on MRA_OK. */
+mra_status mra_workspace_size(const mra_dims* dims, int32_t block_per_row, int32_t approx_mode,
+                              size_t* bytes);
+
+/* The MRA-2 forward pass ([MRA] steps 1-4).
+ *   q, k, v      device, [B, H, N, d], dtype dims->dtype
+ *   mask         device, [B, N] uint8 (nonzero = valid), or NULL
+ *   block_per_row, approx_mode, prior_first, prior_diag: the four MraConfig
+ *                parameters (block_per_row >= 1, priors >= 0)
+ *   out          device, [B, H, N, d], dtype dims->dtype; written in full
+ *   workspace    device, at least mra_workspace_size() bytes, 256-byte
+ *                aligned; its contents need not be initialised
+ *   stream       hipStream_t or NULL */
+mra_status mra_attention_fwd(const mra_dims* dims, const void* q, const void* k, const void* v,
+                             const uint8_t* mask, int32_t block_per_row, int32_t approx_mode,
+                             int32_t prior_first, int32_t prior_diag, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Stage hook for parity tests: runs steps 1 and 2 of the same kernels and
+ * copies the intermediate results out (device buffers owned by the caller,
+ * any of them may be NULL to skip it):
+ *   qhat, khat, vhat  [B, H, N/32, d] fp32 pooled blocks (vhat: full mode only)
+ *   count             [B, N/32] int32 valid tokens per block
+ *   logits            [B, H, N/32, N/32] fp32 low-res logits, tau * qhat . khat
+ *   rowmax            [B, H, N/32] fp32 row max over non-empty key blocks
+ *   sel               [B, H, num_block] int32 selected flat indices i*nb + j,
+ *                     ascending
+ *   error             [1] int32 device error word (0 = consistent)
+ * The other arguments are as for mra_attention_fwd. */
+mra_status mra_debug_stages(const mra_dims* dims, const void* q, const void* k, const void* v,
+                            const uint8_t* mask, int32_t block_per_row, int32_t approx_mode,
+                            int32_t prior_first, int32_t prior_diag, float* qhat, float* khat,
+                            float* vhat, int32_t* count, float* logits, float* rowmax, int32_t* sel,
+                            int32_t* error, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stage hook: the step-2 selector alone on caller-given logits, so that its
+ * result can be compared with the oracle's on identical fp32 inputs.
+ *   logits  device [B, H, nb, nb] fp32, count device [B, nb] int32
+ *   sel     device [B, H, num_block] int32, ascending flat indices
+ * seq_len = 32 * nb comes from dims; q/k/v are not read. */
+mra_status mra_debug_select(const mra_dims* dims, const float* logits, const int32_t* count,
+                            int32_t block_per_row, int32_t prior_first, int32_t prior_diag,
+                            int32_t* sel, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MRA_H */

@@ -1,0 +1,116 @@
+"""CPU tests of the C ABI: the library loads, exports every entry point the
+header declares, and rejects bad arguments on the host before queueing any
+GPU work (so these calls never reach the HIP runtime)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_approximate_amd as mra
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mra.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mra_[a-z_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = mra.lib()
+    names = declared_functions()
+    assert len(names) == 7
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(mra.SIGNATURES)
+    assert L.mra_abi_version() == 1
+
+
+def test_status_strings():
+    for s in range(0, 13):
+        assert mra.lib().mra_status_string(s)
+    assert mra.lib().mra_status_string(99) == b"unknown status"
+
+
+@pytest.mark.parametrize("N,bpr", [(512, 4), (64, 4), (4096, 4), (16384, 8), (32, 1), (96, 100),
+                                   (48, 4), (0, 1), (512, 0), (-64, 2)])
+def test_num_block_matches_oracle(N, bpr):
+    assert mra.num_block(N, bpr) == oracle.num_block(N, bpr)
+
+
+def test_workspace_size_grows_and_validates():
+    small = mra.workspace_size(1, 2, 512)
+    big = mra.workspace_size(2, 12, 4096)
+    assert 0 < small < big
+    assert mra.workspace_size(2, 12, 4096, approx_mode="sparse") < big
+    with pytest.raises(mra.MraError) as e:
+        mra.workspace_size(1, 1, 100)
+    assert e.value.status == 3
+    with pytest.raises(mra.MraError) as e:
+        mra.workspace_size(1, 1, 512, head_dim=32)
+    assert e.value.status == 4
+    with pytest.raises(mra.MraError) as e:
+        mra.workspace_size(1, 1, 512, block_per_row=0)
+    assert e.value.status == 7
+    with pytest.raises(mra.MraError) as e:
+        mra.workspace_size(1, 1, 512, approx_mode="bogus")
+    assert e.value.status == 6
+    with pytest.raises(mra.MraError) as e:
+        mra.workspace_size(1, 1, 32768)
+    assert e.value.status == 3
+
+
+# Fake, aligned, non-null "device" addresses: every call below fails its
+# host-side checks, so no address is ever dereferenced.
+Q, K, V, O, W = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+
+
+def call(dims=(1, 2, 512, 64, 1), q=Q, k=K, v=V, mask=None, bpr=4, mode=0, pf=0, pd=0, out=O, ws=W,
+         ws_bytes=None):
+    d = mra._Dims(*dims)
+    if ws_bytes is None:
+        ws_bytes = 1 << 40 if ws else 0
+    return mra.lib().mra_attention_fwd(ctypes.byref(d), q, k, v, mask, bpr, mode, pf, pd, out, ws, ws_bytes,
+                                       None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(out=None), 1),
+    (dict(dims=(0, 2, 512, 64, 1)), 2), (dict(dims=(1, 0, 512, 64, 1)), 2),
+    (dict(dims=(1, 2, 500, 64, 1)), 3), (dict(dims=(1, 2, 0, 64, 1)), 3),
+    (dict(dims=(1, 2, 32768, 64, 1)), 3),
+    (dict(dims=(1, 2, 512, 128, 1)), 4), (dict(dims=(1, 2, 512, 64, 7)), 5),
+    (dict(mode=2), 6), (dict(mode=-1), 6), (dict(bpr=0), 7), (dict(pf=-1), 8), (dict(pd=-2), 8),
+    (dict(out=Q), 9), (dict(out=W), 9), (dict(out=Q + 4096), 9),
+    (dict(ws=None), 10), (dict(ws_bytes=1024), 10),
+    (dict(q=Q + 8), 12), (dict(mask=0x60000004), 12), (dict(ws=W + 16), 12),
+])
+def test_attention_fwd_rejects_bad_arguments(kw, status):
+    assert call(**kw) == status
+
+
+def test_null_dims_rejected():
+    L = mra.lib()
+    assert L.mra_attention_fwd(None, Q, K, V, None, 4, 0, 0, 0, O, W, 1 << 40, None) == 1
+    n = ctypes.c_size_t(0)
+    assert L.mra_workspace_size(None, 4, 0, ctypes.byref(n)) == 1
+
+
+def test_debug_select_rejects_bad_arguments():
+    L = mra.lib()
+    d = mra._Dims(1, 1, 512, 64, 1)
+    assert L.mra_debug_select(ctypes.byref(d), None, K, 4, 0, 0, O, W, 1 << 40, None) == 1
+    assert L.mra_debug_select(ctypes.byref(d), Q, K, 4, 0, 0, O, W, 16, None) == 10
+    assert L.mra_debug_select(ctypes.byref(d), Q, K, 0, 0, 0, O, W, 1 << 40, None) == 7
+    assert L.mra_debug_select(ctypes.byref(d), Q, K, 4, -1, 0, O, W, 1 << 40, None) == 8
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 64, 64)
+    with pytest.raises(ValueError):
+        mra.attention(q, q, q)
