@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark of the MRA-2 forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C4]
+
+A step is one call of the whole forward pass (pooling, low-res logits, top-k
+selection, block attention, low-res attention with the merge) on inputs already
+resident in HBM.  The default workload is the clustered N=4096 bf16 full-mode
+case (B=2, H=12, d=64, block_per_row=4), the one configuration at N=4096 that
+runs every stage.  W untimed warm-up steps, then exactly K timed steps
+bracketed by torch.cuda.synchronize(); rank 0 prints one JSON line.
+
+Besides tokens/s the line carries:
+  * per-kernel average durations, from HIP events recorded around each launch
+    on the library's stream (a second timed loop of K steps through
+    mra_attention_fwd_profiled);
+  * `roofline` for the kernel with the largest average duration: algorithmic
+    flops (block attention: 4*32*32*d per selected block) or algorithmic
+    bytes (the other kernels) per launch over its average duration;
+  * `traffic`: HBM bytes per launch of that kernel from rocprofv3 FETCH_SIZE /
+    WRITE_SIZE counters committed under profiles/, scaled by the same
+    counters' reading on a plain copy of known size; null when the kernel
+    source changed since the counters were taken;
+  * `cpu_baseline`: the CPU oracle on the host cores (the whole workload,
+    repeated for about 10 s).
+Only one GPU is used; --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3     # MI355X fp32 matrix
+METRIC = "MRA-2 fwd tokens/s and sparse-block MFMA % of peak, N=4096 bf16, 1 MI355X"
+KERNEL_SOURCES = {
+    "pool": "mra_pool.hip", "logits": "mra_select.hip", "select": "mra_select.hip",
+    "attn": "mra_attn.hip", "finish": "mra_finish.hip",
+}
+
+
+def kernel_hash(stage: str) -> str:
+    csrc = os.path.join(ROOT, "block_sparse_approximate_amd", "csrc")
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCES[stage], "mra_common.h"):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic(w, stage: str, sel_blocks: int) -> tuple[float, str]:
+    """(amount per launch, unit) for a stage: flops for the block attention,
+    bytes for the memory-bound stages.  Bytes are what the method must move:
+    every input read once and every output written once."""
+    B, H, N, d = w.B, w.H, w.N, w.d
+    BH, nb = B * H, N // 32
+    es = 2 if w.dtype == "bf16" else 4
+    full = w.approx_mode == "full"
+    ntens = 3 if full else 2
+    K = nb * w.block_per_row if nb * w.block_per_row < nb * nb else nb * nb
+    mask_b = 0 if w.mask is None else B * N
+    if stage == "attn":
+        return 4.0 * 32 * 32 * d * sel_blocks, "flop"
+    if stage == "pool":        # Q, K (V) in; pooled fp32 rows and block counts out
+        return ntens * BH * N * d * es + mask_b + ntens * BH * nb * d * 4 + 2 * B * nb * 4, "byte"
+    if stage == "logits":      # pooled Q, K in; nb x nb logits and row maxima out
+        return 2 * BH * nb * d * 4 + BH * nb * nb * 4 + BH * nb * 4, "byte"
+    if stage == "select":      # logits and row maxima in; K block indices out
+        return BH * nb * nb * 4 + BH * nb * 4 + BH * K * 4, "byte"
+    if full:                   # finish: low-res attention over the logits, merged into the output
+        return BH * nb * nb * 4 + BH * nb * d * 4 + 2 * BH * N * d * es, "byte"
+    return 0.0, "byte"         # sparse mode has no merge step in the method
+
+
+def selected_valid_blocks(w) -> int:
+    """Selected blocks whose query and key blocks both hold valid tokens (the
+    useful ones); every selected block when there is no mask."""
+    import numpy as np
+    nb = w.N // 32
+    K = min(nb * w.block_per_row, nb * nb)
+    if w.mask is None:
+        return w.B * w.H * K
+    cnt = w.mask.reshape(w.B, nb, 32).sum(-1)
+    valid = (cnt > 0).sum(-1)            # a fully valid-pair budget is min(K, valid^2)
+    return int(sum(w.H * min(K, int(v) * int(v)) for v in valid))
+
+
+def load_traffic(stage: str, workload: str):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        t = json.load(open(path))
+    except Exception:
+        return None
+    e = t.get(stage)
+    if not e or e.get("workload") != workload or e.get("source_hash") != kernel_hash(stage):
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(w, seconds: float = 10.0):
+    import oracle
+    threads = oracle.default_threads()
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        oracle.mra_forward(w.q, w.k, w.v, w.mask, block_per_row=w.block_per_row, approx_mode=w.approx_mode,
+                           prior_first=w.prior_first, prior_diag=w.prior_diag, threads=threads)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or runs >= 200:
+            break
+    return {"value": w.B * w.N * runs / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "the whole %s workload (%d heads), %d runs in %.1f s" % (w.name, w.B * w.H, runs, el)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="C4")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB fp32 copy (x * 1.0) 10 times, to calibrate HBM counters")
+    args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        a = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(10):
+            torch.mul(a, 1.0, out=b)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": a.numel() * 4, "bytes_written": b.numel() * 4,
+                          "launches": 10}))
+        return
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only (the MRA forward shards by (batch, head) with "
+              "no exchange between shards); --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_sparse_approximate_amd as mra
+    import workloads
+
+    w = workloads.get(args.config)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def to_dev(name):
+        x = w.raw(name)
+        if w.dtype == "bf16":
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x).to(dev)
+
+    q, k, v = to_dev("q"), to_dev("k"), to_dev("v")
+    mask = None if w.mask is None else torch.from_numpy(w.mask).to(dev)
+    out = torch.empty_like(q)
+    ws = torch.empty(mra.workspace_size(w.B, w.H, w.N, w.d, dt, w.block_per_row, w.approx_mode),
+                     dtype=torch.uint8, device=dev)
+    kw = dict(block_per_row=w.block_per_row, approx_mode=w.approx_mode,
+              initial_prior_first_n_blocks=w.prior_first, initial_prior_diagonal_n_blocks=w.prior_diag,
+              out=out, workspace=ws)
+
+    step, _ = mra.prepare(q, k, v, mask, **kw)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = wall * 1e3 / args.steps
+
+    # per-kernel durations: events around each launch, on the library's stream
+    stages = list(mra.STAGES)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(10)]
+    for e in ev:
+        e.record()
+    sums = {s: 0.0 for s in stages}
+    torch.cuda.synchronize()
+    tp0 = time.perf_counter()
+    for _ in range(args.steps):
+        mra.attention_profiled(q, k, v, ev, mask, **kw)
+        torch.cuda.synchronize()
+        for si, s in enumerate(stages):
+            sums[s] += ev[2 * si].elapsed_time(ev[2 * si + 1])
+    prof_wall = (time.perf_counter() - tp0) * 1e3 / args.steps
+    avg_ms = {s: sums[s] / args.steps for s in stages}
+
+    sel_blocks = selected_valid_blocks(w)
+    kernels = {}
+    for s, t in avg_ms.items():
+        amount, unit = algorithmic(w, s, sel_blocks)
+        rate = amount / (t * 1e-3)
+        if unit == "flop":
+            kernels[s] = {"avg_us": round(t * 1e3, 2), "tflops": round(rate / 1e12, 2),
+                          "mfma_frac": round(rate / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        else:
+            kernels[s] = {"avg_us": round(t * 1e3, 2), "gbs": round(rate / 1e9, 1),
+                          "hbm_frac": round(rate / 1e9 / PEAK_HBM_GBS, 4)}
+    dom = max(avg_ms, key=avg_ms.get)
+    amount, unit = algorithmic(w, dom, sel_blocks)
+    dom_s = avg_ms[dom] * 1e-3
+    if unit == "flop":
+        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(amount / dom_s / 1e12, 3), "peak": peak,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(amount / dom_s / 1e9, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = load_traffic(dom, w.name)
+
+    attn_flops = 4.0 * 32 * 32 * w.d * sel_blocks
+    tokens = w.B * w.N
+    rec = {
+        "metric": METRIC,
+        "value": round(tokens / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded, see workloads.py)",
+        "config": {"workload": w.name, "batch": w.B, "heads": w.H, "seq_len": w.N, "head_dim": w.d,
+                   "block_per_row": w.block_per_row, "approx_mode": w.approx_mode,
+                   "initial_prior_first_n_blocks": w.prior_first,
+                   "initial_prior_diagonal_n_blocks": w.prior_diag, "parallelism": "single GPU"},
+        "useful_tflops": round(attn_flops / (ms * 1e-3) / 1e12, 3),
+        "attn_mfma_frac": kernels["attn"]["mfma_frac"],
+        "kernels": kernels,
+        "profiled_ms_per_step": round(prof_wall, 5),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

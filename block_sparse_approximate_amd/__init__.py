@@ -17,7 +17,7 @@ import os
 
 import torch
 
-__all__ = ["attention", "num_block", "workspace_size", "debug_stages", "debug_select",
+__all__ = ["attention", "attention_profiled", "prepare", "num_block", "workspace_size", "debug_stages", "debug_select",
            "MraError", "library_path", "lib"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -35,6 +35,8 @@ SIGNATURES = {
     "mra_num_block": ([_I32, _I32], _I64),
     "mra_workspace_size": ([_P, _I32, _I32, ctypes.POINTER(_SZ)], ctypes.c_int),
     "mra_attention_fwd": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P], ctypes.c_int),
+    "mra_attention_fwd_profiled": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P, _P],
+                                   ctypes.c_int),
     "mra_debug_stages": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
                           _P, _SZ, _P], ctypes.c_int),
     "mra_debug_select": ([_P, _P, _P, _I32, _I32, _I32, _P, _P, _SZ, _P], ctypes.c_int),
@@ -144,6 +146,60 @@ def attention(q, k, v, mask=None, block_per_row=4, approx_mode="full", initial_p
                                  initial_prior_diagonal_n_blocks, _ptr(out), _ptr(workspace),
                                  workspace.numel(), _stream(q))
     _check(st, "mra_attention_fwd")
+    return out
+
+
+def prepare(q, k, v, mask=None, block_per_row=4, approx_mode="full", initial_prior_first_n_blocks=0,
+            initial_prior_diagonal_n_blocks=0, out=None, workspace=None):
+    """Check and marshal the arguments once; returns (call, out) where call()
+    queues one forward pass on the current stream through the C ABI.  The
+    tensors must stay alive and unchanged in shape while call is used."""
+    _check_inputs(q, k, v, mask)
+    B, H, N, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    ws_bytes = workspace_size(B, H, N, d, q.dtype, block_per_row, approx_mode)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    dims = _dims(B, H, N, d, DTYPES[q.dtype])
+    fn = lib().mra_attention_fwd
+    args = (ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), block_per_row, MODES.get(approx_mode, -1),
+            initial_prior_first_n_blocks, initial_prior_diagonal_n_blocks, _ptr(out), _ptr(workspace),
+            workspace.numel(), _stream(q))
+    keep = (dims, q, k, v, mask, out, workspace)
+
+    def call():
+        st = fn(*args)
+        if st != 0:
+            raise MraError(st, "mra_attention_fwd")
+        return keep[5]
+
+    return call, out
+
+
+STAGES = ("pool", "logits", "select", "attn", "finish")
+
+
+def attention_profiled(q, k, v, events, mask=None, block_per_row=4, approx_mode="full",
+                       initial_prior_first_n_blocks=0, initial_prior_diagonal_n_blocks=0, out=None,
+                       workspace=None):
+    """attention() plus HIP event records around each kernel launch.
+    events: 10 torch.cuda.Event(enable_timing=True) (already recorded once, so
+    that their handles exist), entry 2s / 2s+1 bracketing stage STAGES[s]."""
+    _check_inputs(q, k, v, mask)
+    B, H, N, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    ws_bytes = workspace_size(B, H, N, d, q.dtype, block_per_row, approx_mode)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    arr = (ctypes.c_void_p * 10)(*[e.cuda_event if e is not None else None for e in events])
+    dims = _dims(B, H, N, d, DTYPES[q.dtype])
+    st = lib().mra_attention_fwd_profiled(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(mask),
+                                          block_per_row, MODES.get(approx_mode, -1), initial_prior_first_n_blocks,
+                                          initial_prior_diagonal_n_blocks, _ptr(out), _ptr(workspace),
+                                          workspace.numel(), _stream(q), arr)
+    _check(st, "mra_attention_fwd_profiled")
     return out
 
 

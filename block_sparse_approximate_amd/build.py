@@ -28,7 +28,7 @@ UNITS = {
     "mra_pool": ["-ffp-contract=off"],
     "mra_select": ["-ffp-contract=off"],
     "mra_attn": [],
-    "mra_merge": [],
+    "mra_finish": [],
     "mra_api": [],
 }
 HEADERS = ["mra_common.h", os.path.join("..", "..", "include", "mra.h")]

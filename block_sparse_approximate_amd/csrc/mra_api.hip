@@ -1,12 +1,12 @@
 // mra_api.hip — host side of the C ABI declared in include/mra.h:
 // argument checks, workspace carve and the launch sequence on one stream.
 //
-//   pool            step 1 pooling, counts, mask words; clears the
-//                   selection histogram
-//   logits_select   step 1 logits + step 2 selection (CSR, bitmap, items)
-//   lowres          step 4 low-res attention on unselected blocks (full only)
-//   attn            step 3 block attention; finishes rows that fit one item
-//   merge           joins the partials of longer rows (and the low-res part)
+//   pool      step 1 pooling, counts, mask words; clears the selection
+//             histogram
+//   logits    step 1 low-res logits, row maxima, selection-key histogram
+//   select    step 2 top-K selection: bitmap, CSR, attention stream records
+//   attn      step 3 block attention; finishes rows that fit one segment
+//   finish    step 4 low-res attention (full mode) and merge of segments
 // Everything after the argument checks is asynchronous; nothing here waits.
 #include <string.h>
 
@@ -42,16 +42,15 @@ bool carve(const mra_dims& d, int32_t bpr, int32_t mode, Layout* L) {
     L->logits = take(BH * nb * nb * 4);
     L->rowmax = take(BH * nb * 4);
     L->hist = take(BH * kHistBins * 4);
-    L->done = take(BH * 4);
     L->thresh = take(BH * 8);
     L->row_ptr = take(BH * (nb + 1) * 4);
     L->col = take(BH * (size_t)L->K * 4);
     L->selbits = take(BH * nb * words * 4);
     L->item_ptr = take(BH * (nb + 1) * 4);
-    L->items = take(BH * (size_t)L->max_items * 8);
-    L->n_items = take(BH * 4);
-    L->lo_o = mode == MRA_APPROX_FULL ? take(BH * nb * dd * 4) : 0;
-    L->lo_l = mode == MRA_APPROX_FULL ? take(BH * nb * 4) : 0;
+    L->recs = take(BH * (size_t)L->K * sizeof(BlkRec));
+    L->merge_rows = take(BH * nb * 4);
+    L->n_merge = take(BH * 4);
+    L->side_ml = mode == MRA_APPROX_FULL ? take(BH * (size_t)d.seq_len * 8) : 0;
     L->part_o = take(BH * (size_t)L->max_items * kBlock * dd * 4);
     L->part_ml = take(BH * (size_t)L->max_items * 2 * kBlock * 4);
     L->total = o;
@@ -96,6 +95,7 @@ Params make_params(const mra_dims& d, const Layout& L, int32_t mode, int32_t pf,
     p.prior_first = pf;
     p.prior_diag = pd;
     p.max_items = L.max_items;
+    p.attn_wph = attn_grid_waves_per_head(L.BH, L.K);
     p.q = q; p.k = k; p.v = v; p.mask = mask; p.out = out;
     p.qhat = reinterpret_cast<float*>(w + L.qhat);
     p.khat = reinterpret_cast<float*>(w + L.khat);
@@ -105,16 +105,15 @@ Params make_params(const mra_dims& d, const Layout& L, int32_t mode, int32_t pf,
     p.logits = reinterpret_cast<float*>(w + L.logits);
     p.rowmax = reinterpret_cast<float*>(w + L.rowmax);
     p.hist = reinterpret_cast<uint32_t*>(w + L.hist);
-    p.done = reinterpret_cast<uint32_t*>(w + L.done);
     p.thresh = reinterpret_cast<uint64_t*>(w + L.thresh);
     p.row_ptr = reinterpret_cast<int32_t*>(w + L.row_ptr);
     p.col = reinterpret_cast<int32_t*>(w + L.col);
     p.selbits = reinterpret_cast<uint32_t*>(w + L.selbits);
     p.item_ptr = reinterpret_cast<int32_t*>(w + L.item_ptr);
-    p.items = reinterpret_cast<int2*>(w + L.items);
-    p.n_items = reinterpret_cast<int32_t*>(w + L.n_items);
-    p.lo_o = L.lo_o ? reinterpret_cast<float*>(w + L.lo_o) : nullptr;
-    p.lo_l = L.lo_l ? reinterpret_cast<float*>(w + L.lo_l) : nullptr;
+    p.recs = reinterpret_cast<BlkRec*>(w + L.recs);
+    p.merge_rows = reinterpret_cast<int32_t*>(w + L.merge_rows);
+    p.n_merge = reinterpret_cast<int32_t*>(w + L.n_merge);
+    p.side_ml = L.side_ml ? reinterpret_cast<float*>(w + L.side_ml) : nullptr;
     p.part_o = reinterpret_cast<float*>(w + L.part_o);
     p.part_ml = reinterpret_cast<float*>(w + L.part_ml);
     p.error = reinterpret_cast<int32_t*>(w);
@@ -202,26 +201,57 @@ MRA_API mra_status mra_workspace_size(const mra_dims* dims, int32_t block_per_ro
 
 static mra_status run_front(const Params& p, hipStream_t s) {
     if (launch_pool(p, s) != hipSuccess) return MRA_ERR_HIP;
-    if (launch_logits_select(p, s) != hipSuccess) return MRA_ERR_HIP;
+    if (launch_logits(p, s) != hipSuccess) return MRA_ERR_HIP;
+    if (launch_select(p, s) != hipSuccess) return MRA_ERR_HIP;
     return MRA_OK;
 }
 
-MRA_API mra_status mra_attention_fwd(const mra_dims* dims, const void* q, const void* k, const void* v,
-                                     const uint8_t* mask, int32_t block_per_row, int32_t approx_mode,
-                                     int32_t prior_first, int32_t prior_diag, void* out, void* workspace,
-                                     size_t workspace_bytes, void* stream) {
+// The launch sequence; ev (10 events or null) brackets each stage.
+static mra_status run_forward(const mra_dims* dims, const void* q, const void* k, const void* v,
+                              const uint8_t* mask, int32_t block_per_row, int32_t approx_mode, int32_t prior_first,
+                              int32_t prior_diag, void* out, void* workspace, size_t workspace_bytes, void* stream,
+                              void* const* ev) {
     Layout L;
     mra_status st = check_call(dims, q, k, v, mask, block_per_row, approx_mode, prior_first, prior_diag, out,
                                workspace, workspace_bytes, true, &L);
     if (st != MRA_OK) return st;
     const Params p = make_params(*dims, L, approx_mode, prior_first, prior_diag, q, k, v, mask, out, workspace);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    st = run_front(p, s);
-    if (st != MRA_OK) return st;
-    if (approx_mode == MRA_APPROX_FULL && launch_lowres(p, s) != hipSuccess) return MRA_ERR_HIP;
-    if (launch_attn(p, s) != hipSuccess) return MRA_ERR_HIP;
-    if (launch_merge(p, s) != hipSuccess) return MRA_ERR_HIP;
-    return MRA_OK;
+    auto mark = [&](int idx) {
+        return (ev && ev[idx]) ? hipEventRecord(static_cast<hipEvent_t>(ev[idx]), s) : hipSuccess;
+    };
+    hipError_t e = mark(0);
+    if (e == hipSuccess) e = launch_pool(p, s);
+    if (e == hipSuccess) e = mark(1);
+    if (e == hipSuccess) e = mark(2);
+    if (e == hipSuccess) e = launch_logits(p, s);
+    if (e == hipSuccess) e = mark(3);
+    if (e == hipSuccess) e = mark(4);
+    if (e == hipSuccess) e = launch_select(p, s);
+    if (e == hipSuccess) e = mark(5);
+    if (e == hipSuccess) e = mark(6);
+    if (e == hipSuccess) e = launch_attn(p, s);
+    if (e == hipSuccess) e = mark(7);
+    if (e == hipSuccess) e = mark(8);
+    if (e == hipSuccess) e = launch_finish(p, s);
+    if (e == hipSuccess) e = mark(9);
+    return e == hipSuccess ? MRA_OK : MRA_ERR_HIP;
+}
+
+MRA_API mra_status mra_attention_fwd(const mra_dims* dims, const void* q, const void* k, const void* v,
+                                     const uint8_t* mask, int32_t block_per_row, int32_t approx_mode,
+                                     int32_t prior_first, int32_t prior_diag, void* out, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+    return run_forward(dims, q, k, v, mask, block_per_row, approx_mode, prior_first, prior_diag, out, workspace,
+                       workspace_bytes, stream, nullptr);
+}
+
+MRA_API mra_status mra_attention_fwd_profiled(const mra_dims* dims, const void* q, const void* k, const void* v,
+                                              const uint8_t* mask, int32_t block_per_row, int32_t approx_mode,
+                                              int32_t prior_first, int32_t prior_diag, void* out, void* workspace,
+                                              size_t workspace_bytes, void* stream, void* const* events) {
+    return run_forward(dims, q, k, v, mask, block_per_row, approx_mode, prior_first, prior_diag, out, workspace,
+                       workspace_bytes, stream, events);
 }
 
 MRA_API mra_status mra_debug_stages(const mra_dims* dims, const void* q, const void* k, const void* v,
@@ -279,10 +309,10 @@ MRA_API mra_status mra_debug_select(const mra_dims* dims, const float* logits, c
     hipError_t e = hipMemcpyAsync(p.logits, logits, BH * nb * nb * 4, hipMemcpyDeviceToDevice, s);
     if (e == hipSuccess) e = hipMemcpyAsync(p.cnt, count, (size_t)L.B * nb * 4, hipMemcpyDeviceToDevice, s);
     if (e == hipSuccess) e = hipMemsetAsync(p.hist, 0, BH * kHistBins * 4, s);
-    if (e == hipSuccess) e = hipMemsetAsync(p.done, 0, BH * 4, s);
     if (e == hipSuccess) e = hipMemsetAsync(p.error, 0, 4, s);
     if (e != hipSuccess) return MRA_ERR_HIP;
-    if (launch_select_from_logits(p, s) != hipSuccess) return MRA_ERR_HIP;
+    if (launch_logits_given(p, s) != hipSuccess) return MRA_ERR_HIP;
+    if (launch_select(p, s) != hipSuccess) return MRA_ERR_HIP;
     const int total = L.BH * L.nb;
     hipLaunchKernelGGL(csr_to_flat_kernel, dim3((total + 255) / 256), dim3(256), 0, s, p.row_ptr, p.col, L.nb, L.K,
                        L.BH, sel);

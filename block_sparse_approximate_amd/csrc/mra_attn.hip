@@ -2,8 +2,16 @@
 // selected 32x32 blocks, i.e. what the pages' sampled dense matmul, row max,
 // sparse-dense matmul and reduce-sum do, in one pass with an online row max.
 //
-// Work item = (head, query block row i, chunk of at most kChunk selected key
-// blocks); one wave64 per item.  Per key block j of the chunk:
+// Work decomposition: the selector lists every selected block of a head in
+// CSR order (block row, then key block), each row cut into segments of at
+// most kChunk blocks.  W waves share a head: wave k takes the blocks
+// [k*K/W, (k+1)*K/W) of that list, moved to the next segment boundaries, so
+// every wave gets about the same number of blocks whatever the row lengths.
+// A wave streams through its blocks in batches: it issues the K, V and Q
+// loads of three blocks at once, then computes them, while the other wave on
+// its SIMD does the same half a batch out of step.
+//
+// Per key block j of a segment of query block row i:
 //   S^T = K_j Q_i^T           4 x MFMA 32x32x16 bf16 (fp32: 32 x 32x32x2 f32)
 //   online max / exp2 / sum   in registers: lane l holds query l%32 and 16 of
 //                             its 32 keys, so row reductions need one swap
@@ -15,13 +23,13 @@
 // accumulator layout of S^T is the B-operand layout of P^T up to a fixed
 // permutation of the key index, which V's LDS reads apply.
 //
-// A block row whose selection fits in one item is finished here: sparse
-// mode writes O / l; full mode merges with the low-resolution part of the
-// row ([MRA] "第四步") through the shared row maximum.  Longer rows write
-// un-normalised partials (O, running max, sum) that the merge kernel joins.
+// At the end of a segment that is a whole row the wave writes O/l (0 for
+// padded query tokens); in full mode it also keeps the row max and sum for
+// the low-resolution merge of the finish kernel.  Other segments write
+// un-normalised partials (O, running max, sum) that the finish kernel joins.
 //
 // Workgroups are placed XCD-aware: workgroup g runs on XCD g % 8, and all
-// items of head bh go to XCD bh % 8, so a head's K/V re-reads stay in one L2.
+// waves of head bh are on XCD bh % 8, so a head's K/V re-reads stay in one L2.
 #include "mra_common.h"
 
 namespace mra {
@@ -36,306 +44,348 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kVStrideB = 80;   // bf16 elements per staged V row (64 + 16 pad: no bank conflicts)
 constexpr int kVStrideF = 68;   // fp32 elements per staged V row
+constexpr int kWindow = 64;     // block records a wave holds (one per lane)
+constexpr int kMaxRun = kWindow - kChunk;   // blocks per wave before segment alignment
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+__device__ __forceinline__ int rl(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
 
 // key index held by accumulator register r of a 32x32 MFMA tile in lane l
 __device__ __forceinline__ int acc_row(int r, int lane) { return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); }
 
-template <int DT>
-struct Stage;
+__device__ __forceinline__ int info_pos(uint32_t x) { return (int)((x >> 20) & 15u); }
+__device__ __forceinline__ int info_len(uint32_t x) { return (int)((x >> 24) & 15u); }
+__device__ __forceinline__ bool info_whole(uint32_t x) { return (x >> 28) & 1u; }
+__device__ __forceinline__ int info_item(uint32_t x) { return (int)(x & 0xFFFFFu); }
 
-template <>
-struct Stage<1> {  // bf16
-    uint16_t v[32 * kVStrideB];
+template <int DT> struct Cfg;
+template <> struct Cfg<1> {                 // bf16: 16 bytes per lane per 8 elements
+    static constexpr int kBatch = 3;        // blocks whose loads are in flight together
+    static constexpr int kKV = 4;           // uint4 per lane for one K (or V) block
+    using Elem = uint16_t;
+    static constexpr int kStride = kVStrideB;
 };
-template <>
-struct Stage<0> {  // fp32
-    float v[32 * kVStrideF];
+template <> struct Cfg<0> {                 // fp32: twice the registers per block
+    static constexpr int kBatch = 1;
+    static constexpr int kKV = 8;
+    using Elem = float;
+    static constexpr int kStride = kVStrideF;
 };
 
 template <int DT>
-__global__ __launch_bounds__(kThreads) void attn_kernel(Params p, int wg_per_head) {
-    __shared__ __align__(16) Stage<DT> stage[kWaves];
-    const int g = blockIdx.x;
-    const int xcd = g & 7;
-    const int slot = g >> 3;
-    const int hm = slot / wg_per_head;
-    const int w = slot - hm * wg_per_head;
-    const int bh = xcd + 8 * hm;
-    if (bh >= p.BH) return;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int item = w * kWaves + wave;
-    if (item >= min(p.n_items[bh], p.max_items)) return;
+struct Slot {
+    uint4 k[Cfg<DT>::kKV];
+    uint4 v[Cfg<DT>::kKV];
+    uint4 q[Cfg<DT>::kKV];   // Q of the block's row (used when a segment starts)
+    uint32_t qm;             // and its mask word
+};
 
-    const int nb = p.nb;
-    const int2 it = p.items[(size_t)bh * p.max_items + item];
-    // indices read from memory are clamped so that no logic slip can address
-    // outside the tensors
-    const int i = min(max(it.x, 0), nb - 1), chunk = max(it.y, 0);
-    const int* rp = p.row_ptr + (size_t)bh * (nb + 1);
-    const int cbeg = rp[i] + chunk * kChunk;
-    const int nblk = max(0, min(min(kChunk, rp[i + 1] - cbeg), (int)p.K - cbeg));
-    const int* ip = p.item_ptr + (size_t)bh * (nb + 1);
-    const bool single = (ip[i + 1] - ip[i]) == 1;
-    const int b = bh / p.H;
-    const int jcol = lane < nblk ? min(max(p.col[(size_t)bh * p.K + cbeg + lane], 0), nb - 1) : 0;
-    const uint32_t* mb = p.mbits + (size_t)b * nb;
-    const float scale2 = (1.0f / __builtin_sqrtf((float)p.d)) * kLog2e;
-    const int n = lane & 31, h = lane >> 5;
+template <int DT>
+struct Wave {
+    // record window: lane t holds the record of block a + t
+    int wi, wj;
+    uint32_t wk, winfo;
+    int a;
+    int bh, b, nb, lane, n, h;
+    const typename Cfg<DT>::Elem* Qg;
+    const typename Cfg<DT>::Elem* Kg;
+    const typename Cfg<DT>::Elem* Vg;
+};
 
-    f32x16 o0, o1;
-#pragma unroll
-    for (int r = 0; r < 16; r++) { o0[r] = 0.f; o1[r] = 0.f; }
-    float mrun = -__builtin_inff(), lsum = 0.f;
-
-    const size_t head_off = (size_t)bh * p.N * kHeadDim;
+// Issue the loads of stream block e into a ring slot: K_j, V_j, and Q_i with
+// the mask word of row i.  Every step issues exactly these loads, with no
+// branch around them, so the compiler's wait counts stay exact and a slot's
+// data is waited for only when it is used.
+template <int DT>
+__device__ __forceinline__ void issue(const Params& p, const Wave<DT>& W, int e, Slot<DT>& s) {
+    const int we = e - W.a;
+    const int i = min(max(rl(W.wi, we), 0), W.nb - 1);
+    const int j = min(max(rl(W.wj, we), 0), W.nb - 1);
+    const int lane = W.lane, n = W.n, h = W.h;
     if constexpr (DT == 1) {
-        const uint16_t* Qg = static_cast<const uint16_t*>(p.q) + head_off + (size_t)i * kBlock * kHeadDim;
-        const uint16_t* Kg = static_cast<const uint16_t*>(p.k) + head_off;
-        const uint16_t* Vg = static_cast<const uint16_t*>(p.v) + head_off;
-        uint16_t* vs = stage[wave].v;
-        bf16x8 qb[4];
+        const uint16_t* Kb = W.Kg + (size_t)j * kBlock * kHeadDim;
+        const uint16_t* Vb = W.Vg + (size_t)j * kBlock * kHeadDim;
+        const uint16_t* Qb = W.Qg + (size_t)i * kBlock * kHeadDim;
 #pragma unroll
-        for (int kc = 0; kc < 4; kc++)
-            qb[kc] = as_bf16x8(*reinterpret_cast<const uint4*>(Qg + n * kHeadDim + 16 * kc + 8 * h));
-        // V tile loads: lane covers rows lane/8 + 8e, 16 bytes at column (lane%8)*8
-        const int vrow = lane >> 3, vcol = (lane & 7) * 8;
-        uint4 kn[4], vn[4];
-        if (nblk > 0) {
-            const int j = __shfl(jcol, 0, 64);
-            const uint16_t* Kb = Kg + (size_t)j * kBlock * kHeadDim;
-            const uint16_t* Vb = Vg + (size_t)j * kBlock * kHeadDim;
+        for (int kc = 0; kc < 4; kc++) s.k[kc] = *reinterpret_cast<const uint4*>(Kb + n * kHeadDim + 16 * kc + 8 * h);
 #pragma unroll
-            for (int kc = 0; kc < 4; kc++) kn[kc] = *reinterpret_cast<const uint4*>(Kb + n * kHeadDim + 16 * kc + 8 * h);
+        for (int x = 0; x < 4; x++)
+            s.v[x] = *reinterpret_cast<const uint4*>(Vb + ((lane >> 3) + 8 * x) * kHeadDim + (lane & 7) * 8);
 #pragma unroll
-            for (int e = 0; e < 4; e++) vn[e] = *reinterpret_cast<const uint4*>(Vb + (vrow + 8 * e) * kHeadDim + vcol);
-        }
-        for (int t = 0; t < nblk; t++) {
-            const int j = __shfl(jcol, t, 64);
-            uint4 kc_[4], vc_[4];
-#pragma unroll
-            for (int e = 0; e < 4; e++) { kc_[e] = kn[e]; vc_[e] = vn[e]; }
-            if (t + 1 < nblk) {  // prefetch the next block while this one computes
-                const int jn = __shfl(jcol, t + 1, 64);
-                const uint16_t* Kb = Kg + (size_t)jn * kBlock * kHeadDim;
-                const uint16_t* Vb = Vg + (size_t)jn * kBlock * kHeadDim;
-#pragma unroll
-                for (int kc = 0; kc < 4; kc++) kn[kc] = *reinterpret_cast<const uint4*>(Kb + n * kHeadDim + 16 * kc + 8 * h);
-#pragma unroll
-                for (int e = 0; e < 4; e++) vn[e] = *reinterpret_cast<const uint4*>(Vb + (vrow + 8 * e) * kHeadDim + vcol);
-            }
-            // S^T = K_j Q_i^T
-            f32x16 s;
-#pragma unroll
-            for (int r = 0; r < 16; r++) s[r] = 0.f;
-#pragma unroll
-            for (int kc = 0; kc < 4; kc++)
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kc_[kc]), qb[kc], s, 0, 0, 0);
-            // stage V_j in LDS (this wave's region only)
-#pragma unroll
-            for (int e = 0; e < 4; e++) *reinterpret_cast<uint4*>(vs + (vrow + 8 * e) * kVStrideB + vcol) = vc_[e];
-            // online softmax in log2 units
-            const uint32_t kb = mb[j];
-            float bm = -__builtin_inff();
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const float x = ((kb >> acc_row(r, lane)) & 1u) ? s[r] * scale2 : -__builtin_inff();
-                s[r] = x;
-                bm = fmaxf(bm, x);
-            }
-            bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-            const float mnew = fmaxf(mrun, bm);
-            const float muse = mnew == -__builtin_inff() ? 0.f : mnew;
-            const float alpha = fast_exp2(mrun - muse);
-            float ps = 0.f;
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                s[r] = fast_exp2(s[r] - muse);
-                ps += s[r];
-            }
-            lsum = lsum * alpha + ps;
-            mrun = mnew;
-#pragma unroll
-            for (int r = 0; r < 16; r++) { o0[r] *= alpha; o1[r] *= alpha; }
-            bf16x8 pb[2];
-#pragma unroll
-            for (int kc2 = 0; kc2 < 2; kc2++)
-#pragma unroll
-                for (int e = 0; e < 8; e++) pb[kc2][e] = static_cast<__bf16>(s[8 * kc2 + e]);
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            // O^T += V_j^T P^T ; A operand read transposed from LDS
-            const int g16 = lane >> 4, s16 = lane & 15;
-#pragma unroll
-            for (int kc2 = 0; kc2 < 2; kc2++) {
-#pragma unroll
-                for (int mt = 0; mt < 2; mt++) {
-                    const int col = 32 * mt + 16 * (g16 & 1) + 4 * (s16 & 3);
-                    const int row = 16 * kc2 + 4 * h + (s16 >> 2);
-                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4*)(vs + row * kVStrideB + col));
-                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4*)(vs + (row + 8) * kVStrideB + col));
-                    const short __attribute__((ext_vector_type(8))) a8 = {lo[0], lo[1], lo[2], lo[3],
-                                                                          hi[0], hi[1], hi[2], hi[3]};
-                    const bf16x8 a = __builtin_bit_cast(bf16x8, a8);
-                    if (mt == 0) o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kc2], o0, 0, 0, 0);
-                    else o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kc2], o1, 0, 0, 0);
-                }
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        }
+        for (int kc = 0; kc < 4; kc++) s.q[kc] = *reinterpret_cast<const uint4*>(Qb + n * kHeadDim + 16 * kc + 8 * h);
     } else {
-        const float* Qg = static_cast<const float*>(p.q) + head_off + (size_t)i * kBlock * kHeadDim;
-        const float* Kg = static_cast<const float*>(p.k) + head_off;
-        const float* Vg = static_cast<const float*>(p.v) + head_off;
-        float* vs = stage[wave].v;
-        float qf[32];
+        const float* Kb = W.Kg + (size_t)j * kBlock * kHeadDim;
+        const float* Vb = W.Vg + (size_t)j * kBlock * kHeadDim;
+        const float* Qb = W.Qg + (size_t)i * kBlock * kHeadDim;
 #pragma unroll
-        for (int c4 = 0; c4 < 8; c4++) {
-            const float4 x = *reinterpret_cast<const float4*>(Qg + n * kHeadDim + 32 * h + 4 * c4);
-            qf[4 * c4] = x.x; qf[4 * c4 + 1] = x.y; qf[4 * c4 + 2] = x.z; qf[4 * c4 + 3] = x.w;
-        }
-        const int vrow = lane >> 4, vcol = (lane & 15) * 4;
-        for (int t = 0; t < nblk; t++) {
-            const int j = __shfl(jcol, t, 64);
-            const float* Kb = Kg + (size_t)j * kBlock * kHeadDim;
-            const float* Vb = Vg + (size_t)j * kBlock * kHeadDim;
-            float kf[32];
+        for (int c4 = 0; c4 < 8; c4++) s.k[c4] = *reinterpret_cast<const uint4*>(Kb + n * kHeadDim + 32 * h + 4 * c4);
 #pragma unroll
-            for (int c4 = 0; c4 < 8; c4++) {
-                const float4 x = *reinterpret_cast<const float4*>(Kb + n * kHeadDim + 32 * h + 4 * c4);
-                kf[4 * c4] = x.x; kf[4 * c4 + 1] = x.y; kf[4 * c4 + 2] = x.z; kf[4 * c4 + 3] = x.w;
-            }
-            float4 vv[8];
+        for (int x = 0; x < 8; x++)
+            s.v[x] = *reinterpret_cast<const uint4*>(Vb + ((lane >> 4) + 4 * x) * kHeadDim + (lane & 15) * 4);
 #pragma unroll
-            for (int e = 0; e < 8; e++) vv[e] = *reinterpret_cast<const float4*>(Vb + (vrow + 4 * e) * kHeadDim + vcol);
-            f32x16 s;
-#pragma unroll
-            for (int r = 0; r < 16; r++) s[r] = 0.f;
-#pragma unroll
-            for (int kc = 0; kc < 32; kc++) s = __builtin_amdgcn_mfma_f32_32x32x2f32(kf[kc], qf[kc], s, 0, 0, 0);
-#pragma unroll
-            for (int e = 0; e < 8; e++) *reinterpret_cast<float4*>(vs + (vrow + 4 * e) * kVStrideF + vcol) = vv[e];
-            const uint32_t kb = mb[j];
-            float bm = -__builtin_inff();
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const float x = ((kb >> acc_row(r, lane)) & 1u) ? s[r] * scale2 : -__builtin_inff();
-                s[r] = x;
-                bm = fmaxf(bm, x);
-            }
-            bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-            const float mnew = fmaxf(mrun, bm);
-            const float muse = mnew == -__builtin_inff() ? 0.f : mnew;
-            const float alpha = fast_exp2(mrun - muse);
-            float ps = 0.f;
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                s[r] = fast_exp2(s[r] - muse);
-                ps += s[r];
-            }
-            lsum = lsum * alpha + ps;
-            mrun = mnew;
-#pragma unroll
-            for (int r = 0; r < 16; r++) { o0[r] *= alpha; o1[r] *= alpha; }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-            for (int kc = 0; kc < 16; kc++) {
-                const int key = (kc >> 2) * 8 + 4 * h + (kc & 3);
-                o0 = __builtin_amdgcn_mfma_f32_32x32x2f32(vs[key * kVStrideF + n], s[kc], o0, 0, 0, 0);
-                o1 = __builtin_amdgcn_mfma_f32_32x32x2f32(vs[key * kVStrideF + 32 + n], s[kc], o1, 0, 0, 0);
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        }
+        for (int c4 = 0; c4 < 8; c4++) s.q[c4] = *reinterpret_cast<const uint4*>(Qb + n * kHeadDim + 32 * h + 4 * c4);
     }
+    s.qm = p.mbits[(size_t)W.b * W.nb + i];
+}
 
-    const float ltot = lsum + __shfl_xor(lsum, 32, 64);
+template <int DT>
+struct Acc {
+    f32x16 o0, o1;
+    float mrun, lsum;
+};
+
+// Finish a segment: a whole row writes its output, otherwise a partial.
+template <int DT>
+__device__ __forceinline__ void finish_segment(const Params& p, const Wave<DT>& W, const Acc<DT>& A, int i,
+                                               uint32_t info, uint32_t qm) {
+    const int n = W.n, h = W.h;
+    const float ltot = A.lsum + __shfl_xor(A.lsum, 32, 64);
     const int tok = i * kBlock + n;
-    if (single) {
-        // finish the row: sparse O/l, or full-mode merge with the low-res part
-        const bool valid = (mb[i] >> n) & 1u;
-        float a = 0.f, bw = 0.f, den = 0.f;
-        const float* lo = nullptr;
-        if (p.mode == 0) {
-            const float mi2 = p.rowmax[(size_t)bh * nb + i] * kLog2e;
-            const float M2 = fmaxf(mrun, mi2);
-            if (M2 != -__builtin_inff()) {
-                a = fast_exp2(mrun - M2);
-                bw = fast_exp2(mi2 - M2);
-            }
-            const float ll = p.lo_l[(size_t)bh * nb + i];
-            den = ltot * a + ll * bw;
-            lo = p.lo_o + ((size_t)bh * nb + i) * kHeadDim;
-        } else {
-            a = 1.f;
-            den = ltot;
-        }
-        const float inv = (valid && den > 0.f) ? 1.0f / den : 0.f;
-        const size_t orow = ((size_t)bh * p.N + tok) * kHeadDim;
+    if (info_whole(info)) {
+        const bool valid = (qm >> n) & 1u;
+        const float inv = (valid && ltot > 0.f) ? 1.0f / ltot : 0.f;
+        const size_t orow = ((size_t)W.bh * p.N + tok) * kHeadDim;
 #pragma unroll
         for (int mt = 0; mt < 2; mt++) {
 #pragma unroll
             for (int gq = 0; gq < 4; gq++) {
                 const int d0 = 32 * mt + 8 * gq + 4 * h;
-                float vals[4];
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const float ov = mt == 0 ? o0[4 * gq + e] : o1[4 * gq + e];
-                    float num = ov * a;
-                    if (p.mode == 0) num += lo[d0 + e] * bw;
-                    vals[e] = num * inv;
-                }
+                const f32x16& oo = mt == 0 ? A.o0 : A.o1;
+                const float v0 = oo[4 * gq] * inv, v1 = oo[4 * gq + 1] * inv;
+                const float v2 = oo[4 * gq + 2] * inv, v3 = oo[4 * gq + 3] * inv;
                 if constexpr (DT == 1) {
                     uint2 pk;
-                    pk.x = (uint32_t)float_to_bf16(vals[0]) | ((uint32_t)float_to_bf16(vals[1]) << 16);
-                    pk.y = (uint32_t)float_to_bf16(vals[2]) | ((uint32_t)float_to_bf16(vals[3]) << 16);
+                    pk.x = (uint32_t)float_to_bf16(v0) | ((uint32_t)float_to_bf16(v1) << 16);
+                    pk.y = (uint32_t)float_to_bf16(v2) | ((uint32_t)float_to_bf16(v3) << 16);
                     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + orow + d0) = pk;
                 } else {
-                    *reinterpret_cast<float4*>(static_cast<float*>(p.out) + orow + d0) =
-                        make_float4(vals[0], vals[1], vals[2], vals[3]);
+                    *reinterpret_cast<float4*>(static_cast<float*>(p.out) + orow + d0) = make_float4(v0, v1, v2, v3);
                 }
             }
         }
+        if (p.mode == 0 && h == 0)
+            *reinterpret_cast<float2*>(p.side_ml + ((size_t)W.bh * p.N + tok) * 2) = make_float2(A.mrun, ltot);
     } else {
-        const size_t pidx = (size_t)bh * p.max_items + item;
+        const size_t pidx = (size_t)W.bh * p.max_items + min(info_item(info), p.max_items - 1);
         float* po = p.part_o + (pidx * kBlock + n) * kHeadDim;
 #pragma unroll
         for (int mt = 0; mt < 2; mt++)
 #pragma unroll
             for (int gq = 0; gq < 4; gq++) {
                 const int d0 = 32 * mt + 8 * gq + 4 * h;
-                const f32x16& oo = mt == 0 ? o0 : o1;
-                *reinterpret_cast<float4*>(po + d0) =
-                    make_float4(oo[4 * gq], oo[4 * gq + 1], oo[4 * gq + 2], oo[4 * gq + 3]);
+                const f32x16& oo = mt == 0 ? A.o0 : A.o1;
+                *reinterpret_cast<float4*>(po + d0) = make_float4(oo[4 * gq], oo[4 * gq + 1], oo[4 * gq + 2], oo[4 * gq + 3]);
             }
         if (h == 0) {
-            p.part_ml[pidx * 64 + n] = mrun;
+            p.part_ml[pidx * 64 + n] = A.mrun;
             p.part_ml[pidx * 64 + 32 + n] = ltot;
         }
     }
 }
 
+// One block of the stream: S^T, online softmax, O^T += V^T P^T.
+template <int DT>
+__device__ __forceinline__ void process(const Params& p, const Wave<DT>& W, int e, Slot<DT>& s, Acc<DT>& A,
+                                        typename Cfg<DT>::Elem* vs, float scale2) {
+    const int we = e - W.a;
+    const int i = min(max(rl(W.wi, we), 0), W.nb - 1);
+    const uint32_t kb = (uint32_t)rl((int)W.wk, we);
+    const uint32_t info = (uint32_t)rl((int)W.winfo, we);
+    const int lane = W.lane, n = W.n, h = W.h;
+    if (info_pos(info) == 0) {   // a segment starts
+#pragma unroll
+        for (int r = 0; r < 16; r++) { A.o0[r] = 0.f; A.o1[r] = 0.f; }
+        A.mrun = -__builtin_inff();
+        A.lsum = 0.f;
+    }
+    f32x16 S;
+#pragma unroll
+    for (int r = 0; r < 16; r++) S[r] = 0.f;
+    if constexpr (DT == 1) {
+        // stage V_j in LDS (this wave's region only)
+#pragma unroll
+        for (int x = 0; x < 4; x++)
+            *reinterpret_cast<uint4*>(vs + ((lane >> 3) + 8 * x) * kVStrideB + (lane & 7) * 8) = s.v[x];
+#pragma unroll
+        for (int kc = 0; kc < 4; kc++)
+            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(s.k[kc]), as_bf16x8(s.q[kc]), S, 0, 0, 0);
+    } else {
+#pragma unroll
+        for (int x = 0; x < 8; x++)
+            *reinterpret_cast<uint4*>(vs + ((lane >> 4) + 4 * x) * kVStrideF + (lane & 15) * 4) = s.v[x];
+#pragma unroll
+        for (int c4 = 0; c4 < 8; c4++) {
+            const float4 kf = __builtin_bit_cast(float4, s.k[c4]);
+            const float4 qf = __builtin_bit_cast(float4, s.q[c4]);
+            S = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.x, qf.x, S, 0, 0, 0);
+            S = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.y, qf.y, S, 0, 0, 0);
+            S = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.z, qf.z, S, 0, 0, 0);
+            S = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.w, qf.w, S, 0, 0, 0);
+        }
+    }
+    // online softmax in log2 units: max over the 32 keys of each query row
+    float bm = -__builtin_inff();
+    if (kb == 0xFFFFFFFFu) {
+#pragma unroll
+        for (int r = 0; r < 16; r++) bm = fmaxf(bm, S[r]);
+    } else {
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            S[r] = ((kb >> acc_row(r, lane)) & 1u) ? S[r] : -__builtin_inff();
+            bm = fmaxf(bm, S[r]);
+        }
+    }
+    bm = fmaxf(bm, __shfl_xor(bm, 32, 64)) * scale2;
+    const float mnew = fmaxf(A.mrun, bm);
+    const float muse = mnew == -__builtin_inff() ? 0.f : mnew;
+    const float alpha = fast_exp2(A.mrun - muse);
+    float ps = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+        S[r] = fast_exp2(__builtin_fmaf(S[r], scale2, -muse));
+        ps += S[r];
+    }
+    A.lsum = A.lsum * alpha + ps;
+    A.mrun = mnew;
+#pragma unroll
+    for (int r = 0; r < 16; r++) { A.o0[r] *= alpha; A.o1[r] *= alpha; }
+    // the LDS writes above precede these reads in the wave's in-order LDS queue
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if constexpr (DT == 1) {
+        bf16x8 pb[2];
+#pragma unroll
+        for (int kc2 = 0; kc2 < 2; kc2++)
+#pragma unroll
+            for (int x = 0; x < 8; x++) pb[kc2][x] = static_cast<__bf16>(S[8 * kc2 + x]);
+        // O^T += V_j^T P^T ; A operand read transposed from LDS
+        const int g16 = lane >> 4, s16 = lane & 15;
+#pragma unroll
+        for (int kc2 = 0; kc2 < 2; kc2++) {
+#pragma unroll
+            for (int mt = 0; mt < 2; mt++) {
+                const int col = 32 * mt + 16 * (g16 & 1) + 4 * (s16 & 3);
+                const int row = 16 * kc2 + 4 * h + (s16 >> 2);
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vs + row * kVStrideB + col));
+                const i16x4 hi =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vs + (row + 8) * kVStrideB + col));
+                const short __attribute__((ext_vector_type(8))) a8 = {lo[0], lo[1], lo[2], lo[3],
+                                                                      hi[0], hi[1], hi[2], hi[3]};
+                const bf16x8 av = __builtin_bit_cast(bf16x8, a8);
+                if (mt == 0) A.o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kc2], A.o0, 0, 0, 0);
+                else A.o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kc2], A.o1, 0, 0, 0);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int kc = 0; kc < 16; kc++) {
+            const int key = (kc >> 2) * 8 + 4 * h + (kc & 3);
+            A.o0 = __builtin_amdgcn_mfma_f32_32x32x2f32(vs[key * kVStrideF + n], S[kc], A.o0, 0, 0, 0);
+            A.o1 = __builtin_amdgcn_mfma_f32_32x32x2f32(vs[key * kVStrideF + 32 + n], S[kc], A.o1, 0, 0, 0);
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (info_pos(info) == info_len(info) - 1) finish_segment<DT>(p, W, A, i, info, s.qm);
+}
+
+template <int DT>
+struct StageBuf {
+    typename Cfg<DT>::Elem v[32 * Cfg<DT>::kStride];
+};
+
+template <int DT>
+__global__ __launch_bounds__(kThreads, 2) void attn_kernel(Params p) {
+    __shared__ __align__(16) StageBuf<DT> stage[kWaves];
+    const int xcd = blockIdx.x & 7;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wx = (blockIdx.x >> 3) * kWaves + wave;      // wave index within its XCD
+    const int WPH = p.attn_wph;
+    const int hm = wx / WPH, k = wx - hm * WPH;
+    const int bh = xcd + 8 * hm;
+    if (bh >= p.BH) return;
+
+    const int64_t K = p.K;
+    const int a = (int)((int64_t)k * K / WPH);
+    const int bnd = (int)((int64_t)(k + 1) * K / WPH);
+    const BlkRec* R = p.recs + (size_t)bh * K;
+    Wave<DT> W;
+    W.a = a;
+    W.bh = bh;
+    W.b = bh / p.H;
+    W.nb = p.nb;
+    W.lane = lane;
+    W.n = lane & 31;
+    W.h = lane >> 5;
+    {
+        int4 r = make_int4(0, 0, 0, 0);
+        if (a + lane < K) r = *reinterpret_cast<const int4*>(R + a + lane);
+        W.wi = r.x;
+        W.wj = r.y;
+        W.wk = (uint32_t)r.z;
+        W.winfo = (uint32_t)r.w;
+    }
+    const uint32_t info_b = bnd < K ? R[bnd].info : 0u;
+    // move both ends of [a, bnd) to segment starts
+    const uint32_t info_a = (uint32_t)rl((int)W.winfo, 0);
+    const int start = info_pos(info_a) == 0 ? a : a + info_len(info_a) - info_pos(info_a);
+    const int end = bnd >= K ? (int)K
+                             : (info_pos(info_b) == 0 ? bnd : bnd + info_len(info_b) - info_pos(info_b));
+    if (start >= end || end - a > kWindow) return;   // the window holds every block of the range
+
+    const size_t head_off = (size_t)bh * p.N * kHeadDim;
+    using E = typename Cfg<DT>::Elem;
+    W.Qg = static_cast<const E*>(p.q) + head_off;
+    W.Kg = static_cast<const E*>(p.k) + head_off;
+    W.Vg = static_cast<const E*>(p.v) + head_off;
+    E* vs = stage[wave].v;
+    const float scale2 = (1.0f / __builtin_sqrtf((float)p.d)) * kLog2e;
+
+    // Blocks go in batches: the loads of a whole batch are issued, then the
+    // batch is computed.  Past the end the last block is fetched again, so
+    // every batch issues the same loads and the wait counts stay exact; the
+    // second wave on the SIMD computes while this one waits.
+    constexpr int BATCH = Cfg<DT>::kBatch;
+    Acc<DT> A;
+    A.mrun = -__builtin_inff();
+    A.lsum = 0.f;
+    for (int e0 = start; e0 < end; e0 += BATCH) {
+        Slot<DT> sl[BATCH];
+#pragma unroll
+        for (int u = 0; u < BATCH; u++) issue<DT>(p, W, min(e0 + u, end - 1), sl[u]);
+        // keep the loads together: the scheduler must not sink them into the
+        // compute of the batch
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < BATCH; u++)
+            if (e0 + u < end) process<DT>(p, W, e0 + u, sl[u], A, vs, scale2);
+    }
+}
+
 }  // namespace
 
+int attn_grid_waves_per_head(int BH, int64_t K) {
+    const int heads_per_xcd = (BH + 7) / 8;
+    int64_t w = 256 / heads_per_xcd;                  // about 2048 waves on the chip
+    if (w < 1) w = 1;
+    const int64_t hi = (K + 1) / 2;                   // at least about two blocks a wave
+    if (w > hi) w = hi;
+    const int64_t lo = (K + kMaxRun - 1) / kMaxRun;    // keep each range inside one record window
+    if (w < lo) w = lo;
+    return (int)w;
+}
+
 hipError_t launch_attn(const Params& p, hipStream_t s) {
-    const int wg_per_head = (p.max_items + kWaves - 1) / kWaves;
-    const int head_slots = (p.BH + 7) / 8;
-    const int grid = 8 * head_slots * wg_per_head;
+    const int heads_per_xcd = (p.BH + 7) / 8;
+    const int64_t waves_per_xcd = (int64_t)heads_per_xcd * p.attn_wph;
+    const int64_t grid = 8 * ((waves_per_xcd + kWaves - 1) / kWaves);
     if (p.dtype == 1)
-        hipLaunchKernelGGL(attn_kernel<1>, dim3(grid), dim3(kThreads), 0, s, p, wg_per_head);
+        hipLaunchKernelGGL(attn_kernel<1>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
     else
-        hipLaunchKernelGGL(attn_kernel<0>, dim3(grid), dim3(kThreads), 0, s, p, wg_per_head);
+        hipLaunchKernelGGL(attn_kernel<0>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 

@@ -16,16 +16,35 @@ constexpr int kHeadDim = 64;            // head dims this build accepts
 constexpr int kHistBits = 12;           // first radix digit of the selection key
 constexpr int kHistBins = 1 << kHistBits;
 constexpr float kPriorBias = 5000.0f;   // [MRA] step 2: 5e3 bias for forced blocks
-constexpr int kChunk = 8;               // max selected key blocks per attention work item
+constexpr int kChunk = 8;               // max selected key blocks per segment of a row
 constexpr float kLog2e = 1.4426950408889634f;
+
+// One selected block, in the head's CSR order (block row ascending, then key
+// block ascending).  A block row's selection is cut into segments of at most
+// kChunk blocks; a segment is the unit whose partial softmax the attention
+// kernel produces.
+//   info bits  0..19  segment (item) index within the head
+//              20..23 position of the block within its segment
+//              24..27 segment length (1..kChunk)
+//              28     the segment is the whole row
+struct BlkRec {
+    int32_t i;        // query block row
+    int32_t j;        // key block
+    uint32_t kmask;   // valid-token mask word of key block j
+    uint32_t info;
+};
+
+__host__ __device__ constexpr uint32_t rec_info(int item, int pos, int len, bool whole) {
+    return (uint32_t)item | ((uint32_t)pos << 20) | ((uint32_t)len << 24) | (whole ? (1u << 28) : 0u);
+}
 
 // Workspace carve, shared by the host dispatcher and the kernels.
 struct Layout {
     int32_t B, H, N, d, nb, BH;
     int64_t K;            // selection budget per (batch, head)
-    int32_t max_items;    // attention work items per head, upper bound
-    size_t qhat, khat, vhat, cnt, mbits, logits, rowmax, hist, done, thresh,
-        row_ptr, col, selbits, item_ptr, items, n_items, lo_o, lo_l, part_o, part_ml, total;
+    int32_t max_items;    // segments per head, upper bound
+    size_t qhat, khat, vhat, cnt, mbits, logits, rowmax, hist, thresh, row_ptr, col, selbits, item_ptr, recs,
+        merge_rows, n_merge, side_ml, part_o, part_ml, total;
 };
 
 // Everything a kernel needs, passed by value.
@@ -49,19 +68,19 @@ struct Params {
     float* logits;         // [BH, nb, nb]  tau * qhat_i . khat_j
     float* rowmax;         // [BH, nb]      max over valid j of logits
     uint32_t* hist;        // [BH, kHistBins]
-    uint32_t* done;        // [BH] workgroups finished per head (logits stage)
     uint64_t* thresh;      // [BH] composite key of the last selected cell
     int32_t* row_ptr;      // [BH, nb + 1]  CSR of the selection
     int32_t* col;          // [BH, K]
     uint32_t* selbits;     // [BH, nb, words]
-    int32_t* item_ptr;     // [BH, nb + 1]  first work item of each block row
-    int2* items;           // [BH, max_items] (block row, chunk)
-    int32_t* n_items;      // [BH]
-    float* lo_o;           // [BH, nb, d]   low-res numerator (shifted by rowmax)
-    float* lo_l;           // [BH, nb]      low-res denominator
+    int32_t* item_ptr;     // [BH, nb + 1]  first segment of each block row
+    BlkRec* recs;          // [BH, K] selected blocks in CSR order
+    int32_t* merge_rows;   // [BH, nb] rows the final kernel must combine (0 or >1 segments)
+    int32_t* n_merge;      // [BH]
+    float* side_ml;        // [BH, N, 2] full mode: running max (log2) and sum of single-segment rows
     float* part_o;         // [BH, max_items, 32, d] un-normalised high-res numerators
     float* part_ml;        // [BH, max_items, 2, 32] running max (log2 units) and sum
     int32_t* error;        // device error flag (0 = fine)
+    int32_t attn_wph;      // attention stream: waves sharing one head's blocks
 };
 
 // Ordered key of an fp32 score: larger score -> larger unsigned key.
@@ -91,10 +110,6 @@ __device__ __forceinline__ uint64_t cell_key64(uint32_t key32, uint32_t flat) {
     return ((uint64_t)key32 << 32) | (uint64_t)(0xFFFFFFFFu - flat);
 }
 
-__device__ __forceinline__ float bf16_to_float(uint16_t b) {
-    return __uint_as_float((uint32_t)b << 16);
-}
-
 // fp32 -> bf16 bits, round to nearest even (finite inputs).
 __device__ __forceinline__ uint16_t float_to_bf16(float f) {
     uint32_t u = __float_as_uint(f);
@@ -107,10 +122,10 @@ __device__ __forceinline__ uint16_t float_to_bf16(float f) {
 // Host-side launchers (one per translation unit).
 namespace mra {
 hipError_t launch_pool(const Params& p, hipStream_t s);
-hipError_t launch_logits_select(const Params& p, hipStream_t s);
-hipError_t launch_select_from_logits(const Params& p, hipStream_t s);
-hipError_t launch_lowres(const Params& p, hipStream_t s);
+hipError_t launch_logits(const Params& p, hipStream_t s);
+hipError_t launch_logits_given(const Params& p, hipStream_t s);
+hipError_t launch_select(const Params& p, hipStream_t s);
 hipError_t launch_attn(const Params& p, hipStream_t s);
-hipError_t launch_merge(const Params& p, hipStream_t s);
-size_t logits_select_lds_bytes(int nb);
+hipError_t launch_finish(const Params& p, hipStream_t s);
+int attn_grid_waves_per_head(int BH, int64_t K);
 }  // namespace mra

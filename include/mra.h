@@ -108,6 +108,18 @@ mra_status mra_attention_fwd(const mra_dims* dims, const void* q, const void* k,
                              int32_t prior_first, int32_t prior_diag, void* out, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* Profiling variant of mra_attention_fwd: the same work, plus a
+ * hipEventRecord on `stream` before and after each kernel launch.
+ *   events  array of 10 hipEvent_t created by the caller (with timing);
+ *           entries 2s and 2s+1 bracket kernel s: 0 pooling, 1 low-res
+ *           logits, 2 top-k selection, 3 block attention, 4 low-res
+ *           attention and merge.  NULL entries are skipped.  The events stay
+ *           owned by the caller. */
+mra_status mra_attention_fwd_profiled(const mra_dims* dims, const void* q, const void* k, const void* v,
+                                      const uint8_t* mask, int32_t block_per_row, int32_t approx_mode,
+                                      int32_t prior_first, int32_t prior_diag, void* out, void* workspace,
+                                      size_t workspace_bytes, void* stream, void* const* events);
+
 /* Stage hook for parity tests: runs steps 1 and 2 of the same kernels and
  * copies the intermediate results out (device buffers owned by the caller,
  * any of them may be NULL to skip it):

@@ -20,6 +20,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "mra_oracle.c")
 _LIB = os.path.join(_HERE, "libmra_oracle.so")
+# A test that plants mistakes in copies of the oracle points this at a
+# mutated build; nothing else sets it.
+_LIB_OVERRIDE = os.environ.get("MRA_ORACLE_LIB")
 # -ffp-contract=off and no fast-math: the fp32 steps must be exactly the
 # operations written in the C source.
 CFLAGS = ["-O2", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
@@ -40,8 +43,11 @@ def build(force: bool = False) -> str:
 def lib():
     global _lib
     if _lib is None:
-        build()
-        L = ctypes.CDLL(_LIB)
+        if _LIB_OVERRIDE:
+            L = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            build()
+            L = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         i32, i64 = ctypes.c_int32, ctypes.c_int64
         L.oracle_num_block.argtypes = [i32, i32]
