@@ -70,13 +70,12 @@ def algorithmic(w, stage: str, sel_blocks: int) -> tuple[float, str]:
         return 4.0 * 32 * 32 * d * sel_blocks, "flop"
     if stage == "pool":        # Q, K (V) in; pooled fp32 rows and block counts out
         return ntens * BH * N * d * es + mask_b + ntens * BH * nb * d * 4 + 2 * B * nb * 4, "byte"
-    if stage == "logits":      # pooled Q, K in; nb x nb logits and row maxima out
-        return 2 * BH * nb * d * 4 + BH * nb * nb * 4 + BH * nb * 4, "byte"
+    if stage == "logits":      # pooled Q, K (V) in; logits, row maxima (low-res row sums) out
+        lowres = BH * nb * d * 4 + BH * nb * (d + 1) * 4 if full else 0
+        return 2 * BH * nb * d * 4 + BH * nb * nb * 4 + BH * nb * 4 + lowres, "byte"
     if stage == "select":      # logits and row maxima in; K block indices out
         return BH * nb * nb * 4 + BH * nb * 4 + BH * K * 4, "byte"
-    if full:                   # finish: low-res attention over the logits, merged into the output
-        return BH * nb * nb * 4 + BH * nb * d * 4 + 2 * BH * N * d * es, "byte"
-    return 0.0, "byte"         # sparse mode has no merge step in the method
+    return None, "byte"        # finish: only the rows split into several segments; no fixed volume
 
 
 def selected_valid_blocks(w) -> int:
@@ -204,6 +203,9 @@ def main():
     kernels = {}
     for s, t in avg_ms.items():
         amount, unit = algorithmic(w, s, sel_blocks)
+        if amount is None:
+            kernels[s] = {"avg_us": round(t * 1e3, 2)}
+            continue
         rate = amount / (t * 1e-3)
         if unit == "flop":
             kernels[s] = {"avg_us": round(t * 1e3, 2), "tflops": round(rate / 1e12, 2),
@@ -211,7 +213,7 @@ def main():
         else:
             kernels[s] = {"avg_us": round(t * 1e3, 2), "gbs": round(rate / 1e9, 1),
                           "hbm_frac": round(rate / 1e9 / PEAK_HBM_GBS, 4)}
-    dom = max(avg_ms, key=avg_ms.get)
+    dom = max((s for s in avg_ms if algorithmic(w, s, sel_blocks)[0] is not None), key=avg_ms.get)
     amount, unit = algorithmic(w, dom, sel_blocks)
     dom_s = avg_ms[dom] * 1e-3
     if unit == "flop":

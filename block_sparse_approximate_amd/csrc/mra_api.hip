@@ -40,6 +40,7 @@ bool carve(const mra_dims& d, int32_t bpr, int32_t mode, Layout* L) {
     L->cnt = take((size_t)d.batch * nb * 4);
     L->mbits = take((size_t)d.batch * nb * 4);
     L->logits = take(BH * nb * nb * 4);
+    L->keys = take(BH * nb * nb * 4);
     L->rowmax = take(BH * nb * 4);
     L->hist = take(BH * kHistBins * 4);
     L->thresh = take(BH * 8);
@@ -50,7 +51,8 @@ bool carve(const mra_dims& d, int32_t bpr, int32_t mode, Layout* L) {
     L->recs = take(BH * (size_t)L->K * sizeof(BlkRec));
     L->merge_rows = take(BH * nb * 4);
     L->n_merge = take(BH * 4);
-    L->side_ml = mode == MRA_APPROX_FULL ? take(BH * (size_t)d.seq_len * 8) : 0;
+    L->lo_all = mode == MRA_APPROX_FULL ? take(BH * nb * dd * 4) : 0;
+    L->ll_all = mode == MRA_APPROX_FULL ? take(BH * nb * 4) : 0;
     L->part_o = take(BH * (size_t)L->max_items * kBlock * dd * 4);
     L->part_ml = take(BH * (size_t)L->max_items * 2 * kBlock * 4);
     L->total = o;
@@ -103,6 +105,7 @@ Params make_params(const mra_dims& d, const Layout& L, int32_t mode, int32_t pf,
     p.cnt = reinterpret_cast<int32_t*>(w + L.cnt);
     p.mbits = reinterpret_cast<uint32_t*>(w + L.mbits);
     p.logits = reinterpret_cast<float*>(w + L.logits);
+    p.keys = reinterpret_cast<uint32_t*>(w + L.keys);
     p.rowmax = reinterpret_cast<float*>(w + L.rowmax);
     p.hist = reinterpret_cast<uint32_t*>(w + L.hist);
     p.thresh = reinterpret_cast<uint64_t*>(w + L.thresh);
@@ -113,7 +116,8 @@ Params make_params(const mra_dims& d, const Layout& L, int32_t mode, int32_t pf,
     p.recs = reinterpret_cast<BlkRec*>(w + L.recs);
     p.merge_rows = reinterpret_cast<int32_t*>(w + L.merge_rows);
     p.n_merge = reinterpret_cast<int32_t*>(w + L.n_merge);
-    p.side_ml = L.side_ml ? reinterpret_cast<float*>(w + L.side_ml) : nullptr;
+    p.lo_all = L.lo_all ? reinterpret_cast<float*>(w + L.lo_all) : nullptr;
+    p.ll_all = L.ll_all ? reinterpret_cast<float*>(w + L.ll_all) : nullptr;
     p.part_o = reinterpret_cast<float*>(w + L.part_o);
     p.part_ml = reinterpret_cast<float*>(w + L.part_ml);
     p.error = reinterpret_cast<int32_t*>(w);

@@ -23,10 +23,17 @@
 // accumulator layout of S^T is the B-operand layout of P^T up to a fixed
 // permutation of the key index, which V's LDS reads apply.
 //
-// At the end of a segment that is a whole row the wave writes O/l (0 for
-// padded query tokens); in full mode it also keeps the row max and sum for
-// the low-resolution merge of the finish kernel.  Other segments write
-// un-normalised partials (O, running max, sum) that the finish kernel joins.
+// At the end of a segment that is a whole row the wave writes the row's
+// output.  In sparse mode that is O/l (0 for padded query tokens).  In full
+// mode the wave also merges the low-resolution part ([MRA] "第四步"): the
+// logits kernel summed the low-res attention of the row over every key block
+// (lo_all, ll_all), and each record carries its cell's low-res weight w, so
+// the wave takes the selected blocks back out,
+//   lo = lo_all - sum_sel w vhat_j,   ll = ll_all - sum_sel w,
+// and writes (O 2^(m - M) + lo 2^(m_i - M)) / (l 2^(m - M) + ll 2^(m_i - M))
+// with M the larger of the high-res max m and the low-res row max m_i (both
+// in log2 units).  Other segments write un-normalised partials (O, running
+// max, sum) that the finish kernel joins.
 //
 // Workgroups are placed XCD-aware: workgroup g runs on XCD g % 8, and all
 // waves of head bh are on XCD bh % 8, so a head's K/V re-reads stay in one L2.
@@ -43,9 +50,12 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kVStrideB = 80;   // bf16 elements per staged V row (64 + 16 pad: no bank conflicts)
+constexpr int kKStrideB = 72;   // bf16 elements per staged Q row (144 bytes: 8 lanes' 16-byte reads hit 32 banks)
 constexpr int kVStrideF = 68;   // fp32 elements per staged V row
 constexpr int kWindow = 64;     // block records a wave holds (one per lane)
-constexpr int kMaxRun = kWindow - kChunk;   // blocks per wave before segment alignment
+// blocks per wave before segment alignment: an end moves up to kChunk - 1
+// blocks forward, a start up to kChunk / 2 back
+constexpr int kMaxRun = kWindow - kChunk - kChunk / 2;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
@@ -58,6 +68,15 @@ __device__ __forceinline__ int info_pos(uint32_t x) { return (int)((x >> 20) & 1
 __device__ __forceinline__ int info_len(uint32_t x) { return (int)((x >> 24) & 15u); }
 __device__ __forceinline__ bool info_whole(uint32_t x) { return (x >> 28) & 1u; }
 __device__ __forceinline__ int info_item(uint32_t x) { return (int)(x & 0xFFFFFu); }
+
+// The segment start nearest to stream block x (whose record info is given):
+// back to its segment's start when x is in the segment's first half, else
+// on to the next segment's start.  x >= K maps to K.
+__device__ __forceinline__ int nearest_segment_start(int x, uint32_t info, int64_t K) {
+    if (x >= K) return (int)K;
+    const int pos = info_pos(info), len = info_len(info);
+    return 2 * pos <= len ? x - pos : x - pos + len;
+}
 
 template <int DT> struct Cfg;
 template <> struct Cfg<1> {                 // bf16: 16 bytes per lane per 8 elements
@@ -77,15 +96,18 @@ template <int DT>
 struct Slot {
     uint4 k[Cfg<DT>::kKV];
     uint4 v[Cfg<DT>::kKV];
-    uint4 q[Cfg<DT>::kKV];   // Q of the block's row (used when a segment starts)
+    uint4 q[Cfg<DT>::kKV];   // Q of the block's row
     uint32_t qm;             // and its mask word
+    float vh;                // full mode: vhat_j[lane]
+    float lo;                // full mode: lo_all_i[lane]
 };
 
 template <int DT>
 struct Wave {
-    // record window: lane t holds the record of block a + t
-    int wi, wj;
-    uint32_t wk, winfo;
+    // record window: lane t holds the record of block a + t, and in full mode
+    // the low-res row max and weight sum of that block's row
+    uint32_t wij, wk, winfo;
+    float ww, wm, wll;
     int a;
     int bh, b, nb, lane, n, h;
     const typename Cfg<DT>::Elem* Qg;
@@ -93,27 +115,38 @@ struct Wave {
     const typename Cfg<DT>::Elem* Vg;
 };
 
-// Issue the loads of stream block e into a ring slot: K_j, V_j, and Q_i with
-// the mask word of row i.  Every step issues exactly these loads, with no
-// branch around them, so the compiler's wait counts stay exact and a slot's
-// data is waited for only when it is used.
-template <int DT>
+// Issue the loads of stream block e into a batch slot: K_j, V_j, Q_i when
+// the block starts a segment, the mask word of row i, and in full mode
+// vhat_j and lo_all_i at this lane's channel.
+__device__ __forceinline__ int rec_i(uint32_t ij) { return (int)(ij & 0xFFFFu); }
+__device__ __forceinline__ int rec_j(uint32_t ij) { return (int)(ij >> 16); }
+
+template <int DT, bool FULL>
 __device__ __forceinline__ void issue(const Params& p, const Wave<DT>& W, int e, Slot<DT>& s) {
     const int we = e - W.a;
-    const int i = min(max(rl(W.wi, we), 0), W.nb - 1);
-    const int j = min(max(rl(W.wj, we), 0), W.nb - 1);
+    const uint32_t ij = (uint32_t)rl((int)W.wij, we);
+    const int i = min(rec_i(ij), W.nb - 1);
+    const int j = min(rec_j(ij), W.nb - 1);
     const int lane = W.lane, n = W.n, h = W.h;
     if constexpr (DT == 1) {
         const uint16_t* Kb = W.Kg + (size_t)j * kBlock * kHeadDim;
         const uint16_t* Vb = W.Vg + (size_t)j * kBlock * kHeadDim;
         const uint16_t* Qb = W.Qg + (size_t)i * kBlock * kHeadDim;
+        const int off = (lane >> 3) * kHeadDim + (lane & 7) * 8;
+        // K_j straight into the MFMA operand layout: token n, channels 16 kc + 8 h .. +7
 #pragma unroll
         for (int kc = 0; kc < 4; kc++) s.k[kc] = *reinterpret_cast<const uint4*>(Kb + n * kHeadDim + 16 * kc + 8 * h);
 #pragma unroll
-        for (int x = 0; x < 4; x++)
-            s.v[x] = *reinterpret_cast<const uint4*>(Vb + ((lane >> 3) + 8 * x) * kHeadDim + (lane & 7) * 8);
+        for (int x = 0; x < 4; x++) s.v[x] = *reinterpret_cast<const uint4*>(Vb + off + 8 * x * kHeadDim);
+        // V_j and Q_i: whole 128-byte token rows per 8 lanes, so every load
+        // is 8 full cache lines; Q_i once per segment, by its first block
+        if (info_pos((uint32_t)rl((int)W.winfo, we)) == 0) {
 #pragma unroll
-        for (int kc = 0; kc < 4; kc++) s.q[kc] = *reinterpret_cast<const uint4*>(Qb + n * kHeadDim + 16 * kc + 8 * h);
+            for (int x = 0; x < 4; x++) s.q[x] = *reinterpret_cast<const uint4*>(Qb + off + 8 * x * kHeadDim);
+        } else {
+#pragma unroll
+            for (int x = 0; x < 4; x++) s.q[x] = make_uint4(0u, 0u, 0u, 0u);
+        }
     } else {
         const float* Kb = W.Kg + (size_t)j * kBlock * kHeadDim;
         const float* Vb = W.Vg + (size_t)j * kBlock * kHeadDim;
@@ -127,24 +160,45 @@ __device__ __forceinline__ void issue(const Params& p, const Wave<DT>& W, int e,
         for (int c4 = 0; c4 < 8; c4++) s.q[c4] = *reinterpret_cast<const uint4*>(Qb + n * kHeadDim + 32 * h + 4 * c4);
     }
     s.qm = p.mbits[(size_t)W.b * W.nb + i];
+    if constexpr (FULL) {
+        s.vh = p.vhat[((size_t)W.bh * W.nb + j) * kHeadDim + lane];
+        s.lo = p.lo_all[((size_t)W.bh * W.nb + i) * kHeadDim + lane];
+    }
 }
 
 template <int DT>
 struct Acc {
     f32x16 o0, o1;
     float mrun, lsum;
+    float corr;   // full mode: sum over the segment's blocks of w vhat_j[lane]
+    float sw;     // full mode: sum of their weights w
 };
 
 // Finish a segment: a whole row writes its output, otherwise a partial.
-template <int DT>
-__device__ __forceinline__ void finish_segment(const Params& p, const Wave<DT>& W, const Acc<DT>& A, int i,
-                                               uint32_t info, uint32_t qm) {
+template <int DT, bool FULL>
+__device__ __forceinline__ void finish_segment(const Params& p, const Wave<DT>& W, const Acc<DT>& A, int we,
+                                               int i, uint32_t info, const Slot<DT>& s, float* lo_lds) {
     const int n = W.n, h = W.h;
     const float ltot = A.lsum + __shfl_xor(A.lsum, 32, 64);
     const int tok = i * kBlock + n;
     if (info_whole(info)) {
-        const bool valid = (qm >> n) & 1u;
-        const float inv = (valid && ltot > 0.f) ? 1.0f / ltot : 0.f;
+        const bool valid = (s.qm >> n) & 1u;
+        float a = 1.f, bw = 0.f, den = ltot;
+        if constexpr (FULL) {
+            // low-res part of the row without the selected blocks, one channel per lane
+            lo_lds[W.lane] = s.lo - A.corr;
+            const float mi2 = __int_as_float(rl(__float_as_int(W.wm), we)) * kLog2e;
+            const float ll = fmaxf(__int_as_float(rl(__float_as_int(W.wll), we)) - A.sw, 0.f);
+            const float M = fmaxf(A.mrun, mi2);
+            a = M == -__builtin_inff() ? 0.f : fast_exp2(A.mrun - M);
+            bw = M == -__builtin_inff() ? 0.f : fast_exp2(mi2 - M);
+            den = ltot * a + ll * bw;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+        const float inv = (valid && den > 0.f) ? 1.0f / den : 0.f;
+        const float sa = a * inv, sb = bw * inv;
         const size_t orow = ((size_t)W.bh * p.N + tok) * kHeadDim;
 #pragma unroll
         for (int mt = 0; mt < 2; mt++) {
@@ -152,8 +206,15 @@ __device__ __forceinline__ void finish_segment(const Params& p, const Wave<DT>& 
             for (int gq = 0; gq < 4; gq++) {
                 const int d0 = 32 * mt + 8 * gq + 4 * h;
                 const f32x16& oo = mt == 0 ? A.o0 : A.o1;
-                const float v0 = oo[4 * gq] * inv, v1 = oo[4 * gq + 1] * inv;
-                const float v2 = oo[4 * gq + 2] * inv, v3 = oo[4 * gq + 3] * inv;
+                float v0 = oo[4 * gq] * sa, v1 = oo[4 * gq + 1] * sa;
+                float v2 = oo[4 * gq + 2] * sa, v3 = oo[4 * gq + 3] * sa;
+                if constexpr (FULL) {
+                    const float4 lo = *reinterpret_cast<const float4*>(lo_lds + d0);
+                    v0 = __builtin_fmaf(lo.x, sb, v0);
+                    v1 = __builtin_fmaf(lo.y, sb, v1);
+                    v2 = __builtin_fmaf(lo.z, sb, v2);
+                    v3 = __builtin_fmaf(lo.w, sb, v3);
+                }
                 if constexpr (DT == 1) {
                     uint2 pk;
                     pk.x = (uint32_t)float_to_bf16(v0) | ((uint32_t)float_to_bf16(v1) << 16);
@@ -164,8 +225,6 @@ __device__ __forceinline__ void finish_segment(const Params& p, const Wave<DT>& 
                 }
             }
         }
-        if (p.mode == 0 && h == 0)
-            *reinterpret_cast<float2*>(p.side_ml + ((size_t)W.bh * p.N + tok) * 2) = make_float2(A.mrun, ltot);
     } else {
         const size_t pidx = (size_t)W.bh * p.max_items + min(info_item(info), p.max_items - 1);
         float* po = p.part_o + (pidx * kBlock + n) * kHeadDim;
@@ -185,11 +244,11 @@ __device__ __forceinline__ void finish_segment(const Params& p, const Wave<DT>& 
 }
 
 // One block of the stream: S^T, online softmax, O^T += V^T P^T.
-template <int DT>
+template <int DT, bool FULL>
 __device__ __forceinline__ void process(const Params& p, const Wave<DT>& W, int e, Slot<DT>& s, Acc<DT>& A,
                                         typename Cfg<DT>::Elem* vs, float scale2) {
     const int we = e - W.a;
-    const int i = min(max(rl(W.wi, we), 0), W.nb - 1);
+    const int i = min(rec_i((uint32_t)rl((int)W.wij, we)), W.nb - 1);
     const uint32_t kb = (uint32_t)rl((int)W.wk, we);
     const uint32_t info = (uint32_t)rl((int)W.winfo, we);
     const int lane = W.lane, n = W.n, h = W.h;
@@ -198,18 +257,41 @@ __device__ __forceinline__ void process(const Params& p, const Wave<DT>& W, int 
         for (int r = 0; r < 16; r++) { A.o0[r] = 0.f; A.o1[r] = 0.f; }
         A.mrun = -__builtin_inff();
         A.lsum = 0.f;
+        if constexpr (FULL) {
+            A.corr = 0.f;
+            A.sw = 0.f;
+        }
+    }
+    if constexpr (FULL) {
+        const float w = __int_as_float(rl(__float_as_int(W.ww), we));
+        A.corr = __builtin_fmaf(w, s.vh, A.corr);
+        A.sw += w;
     }
     f32x16 S;
 #pragma unroll
     for (int r = 0; r < 16; r++) S[r] = 0.f;
     if constexpr (DT == 1) {
-        // stage V_j in LDS (this wave's region only)
+        // stage V_j (and Q_i when the segment starts) in this wave's LDS
+        // region; Q is read back one token row per lane (the MFMA operand
+        // layout: lane l holds token l % 32, channels 16 kc + 8 (l / 32))
+        uint16_t* qs = vs + kBlock * kVStrideB;
 #pragma unroll
         for (int x = 0; x < 4; x++)
             *reinterpret_cast<uint4*>(vs + ((lane >> 3) + 8 * x) * kVStrideB + (lane & 7) * 8) = s.v[x];
+        if (info_pos(info) == 0) {
 #pragma unroll
-        for (int kc = 0; kc < 4; kc++)
-            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(s.k[kc]), as_bf16x8(s.q[kc]), S, 0, 0, 0);
+            for (int x = 0; x < 4; x++)
+                *reinterpret_cast<uint4*>(qs + ((lane >> 3) + 8 * x) * kKStrideB + (lane & 7) * 8) = s.q[x];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int kc = 0; kc < 4; kc++) {
+            const uint4 ka = s.k[kc];
+            const uint4 qa = *reinterpret_cast<const uint4*>(qs + n * kKStrideB + 16 * kc + 8 * h);
+            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka), as_bf16x8(qa), S, 0, 0, 0);
+        }
     } else {
 #pragma unroll
         for (int x = 0; x < 8; x++)
@@ -289,15 +371,17 @@ __device__ __forceinline__ void process(const Params& p, const Wave<DT>& W, int 
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (info_pos(info) == info_len(info) - 1) finish_segment<DT>(p, W, A, i, info, s.qm);
+    if (info_pos(info) == info_len(info) - 1)
+        finish_segment<DT, FULL>(p, W, A, we, i, info, s, reinterpret_cast<float*>(vs));
 }
 
+// Per-wave LDS: V_j (read back transposed), and for bf16 also Q_i.
 template <int DT>
 struct StageBuf {
-    typename Cfg<DT>::Elem v[32 * Cfg<DT>::kStride];
+    typename Cfg<DT>::Elem v[32 * Cfg<DT>::kStride + (DT == 1 ? 32 * kKStrideB : 0)];
 };
 
-template <int DT>
+template <int DT, bool FULL>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(Params p) {
     __shared__ __align__(16) StageBuf<DT> stage[kWaves];
     const int xcd = blockIdx.x & 7;
@@ -311,9 +395,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(Params p) {
     const int64_t K = p.K;
     const int a = (int)((int64_t)k * K / WPH);
     const int bnd = (int)((int64_t)(k + 1) * K / WPH);
+    // the record window starts half a segment before a: the range's first
+    // block may move back that far
+    const int a0 = max(a - kChunk / 2, 0);
     const BlkRec* R = p.recs + (size_t)bh * K;
     Wave<DT> W;
-    W.a = a;
+    W.a = a0;
     W.bh = bh;
     W.b = bh / p.H;
     W.nb = p.nb;
@@ -322,19 +409,30 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(Params p) {
     W.h = lane >> 5;
     {
         int4 r = make_int4(0, 0, 0, 0);
-        if (a + lane < K) r = *reinterpret_cast<const int4*>(R + a + lane);
-        W.wi = r.x;
-        W.wj = r.y;
-        W.wk = (uint32_t)r.z;
+        if (a0 + lane < K) r = *reinterpret_cast<const int4*>(R + a0 + lane);
+        W.wij = (uint32_t)r.x;
+        W.wk = (uint32_t)r.y;
+        W.ww = __int_as_float(r.z);
         W.winfo = (uint32_t)r.w;
+        W.wm = 0.f;
+        W.wll = 0.f;
+        if (FULL && a0 + lane < K) {
+            const size_t row = (size_t)bh * p.nb + min(rec_i(W.wij), p.nb - 1);
+            W.wm = p.rowmax[row];
+            W.wll = p.ll_all[row];
+        }
     }
     const uint32_t info_b = bnd < K ? R[bnd].info : 0u;
-    // move both ends of [a, bnd) to segment starts
-    const uint32_t info_a = (uint32_t)rl((int)W.winfo, 0);
-    const int start = info_pos(info_a) == 0 ? a : a + info_len(info_a) - info_pos(info_a);
-    const int end = bnd >= K ? (int)K
-                             : (info_pos(info_b) == 0 ? bnd : bnd + info_len(info_b) - info_pos(info_b));
-    if (start >= end || end - a > kWindow) return;   // the window holds every block of the range
+    // Move both ends of [a, bnd) to the nearest segment start; the next
+    // wave's range starts where this one ends, since both round the same
+    // block index the same way.
+    const int start = nearest_segment_start(a, (uint32_t)rl((int)W.winfo, a - a0), K);
+    const int end = nearest_segment_start(bnd, info_b, K);
+    if (start >= end) return;
+    if (start < a0 || end - a0 > kWindow) {   // the window must hold every block of the range
+        if (lane == 0) atomicOr(reinterpret_cast<unsigned int*>(p.error), 4u);
+        return;
+    }
 
     const size_t head_off = (size_t)bh * p.N * kHeadDim;
     using E = typename Cfg<DT>::Elem;
@@ -355,13 +453,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(Params p) {
     for (int e0 = start; e0 < end; e0 += BATCH) {
         Slot<DT> sl[BATCH];
 #pragma unroll
-        for (int u = 0; u < BATCH; u++) issue<DT>(p, W, min(e0 + u, end - 1), sl[u]);
+        for (int u = 0; u < BATCH; u++) issue<DT, FULL>(p, W, min(e0 + u, end - 1), sl[u]);
         // keep the loads together: the scheduler must not sink them into the
         // compute of the batch
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < BATCH; u++)
-            if (e0 + u < end) process<DT>(p, W, e0 + u, sl[u], A, vs, scale2);
+            if (e0 + u < end) process<DT, FULL>(p, W, e0 + u, sl[u], A, vs, scale2);
     }
 }
 
@@ -382,10 +480,14 @@ hipError_t launch_attn(const Params& p, hipStream_t s) {
     const int heads_per_xcd = (p.BH + 7) / 8;
     const int64_t waves_per_xcd = (int64_t)heads_per_xcd * p.attn_wph;
     const int64_t grid = 8 * ((waves_per_xcd + kWaves - 1) / kWaves);
-    if (p.dtype == 1)
-        hipLaunchKernelGGL(attn_kernel<1>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
-    else
-        hipLaunchKernelGGL(attn_kernel<0>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+    const bool full = p.mode == 0;
+    if (p.dtype == 1) {
+        if (full) hipLaunchKernelGGL((attn_kernel<1, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL((attn_kernel<1, false>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+    } else {
+        if (full) hipLaunchKernelGGL((attn_kernel<0, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL((attn_kernel<0, false>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+    }
     return hipGetLastError();
 }
 

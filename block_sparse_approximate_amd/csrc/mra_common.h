@@ -23,17 +23,22 @@ constexpr float kLog2e = 1.4426950408889634f;
 // block ascending).  A block row's selection is cut into segments of at most
 // kChunk blocks; a segment is the unit whose partial softmax the attention
 // kernel produces.
-//   info bits  0..19  segment (item) index within the head
-//              20..23 position of the block within its segment
-//              24..27 segment length (1..kChunk)
-//              28     the segment is the whole row
+//   ij    query block row i (bits 0..15) and key block j (bits 16..31)
+//   kmask valid-token mask word of key block j
+//   w     full mode: the low-resolution weight cnt_j exp(S_ij - m_i) of the
+//         cell, which the low-res part must leave out; 0 in sparse mode
+//   info  bits  0..19  segment (item) index within the head
+//               20..23 position of the block within its segment
+//               24..27 segment length (1..kChunk)
+//               28     the segment is the whole row
 struct BlkRec {
-    int32_t i;        // query block row
-    int32_t j;        // key block
-    uint32_t kmask;   // valid-token mask word of key block j
+    uint32_t ij;
+    uint32_t kmask;
+    float w;
     uint32_t info;
 };
 
+__host__ __device__ constexpr uint32_t rec_ij(int i, int j) { return (uint32_t)i | ((uint32_t)j << 16); }
 __host__ __device__ constexpr uint32_t rec_info(int item, int pos, int len, bool whole) {
     return (uint32_t)item | ((uint32_t)pos << 20) | ((uint32_t)len << 24) | (whole ? (1u << 28) : 0u);
 }
@@ -43,8 +48,8 @@ struct Layout {
     int32_t B, H, N, d, nb, BH;
     int64_t K;            // selection budget per (batch, head)
     int32_t max_items;    // segments per head, upper bound
-    size_t qhat, khat, vhat, cnt, mbits, logits, rowmax, hist, thresh, row_ptr, col, selbits, item_ptr, recs,
-        merge_rows, n_merge, side_ml, part_o, part_ml, total;
+    size_t qhat, khat, vhat, cnt, mbits, logits, keys, rowmax, hist, thresh, row_ptr, col, selbits, item_ptr, recs,
+        merge_rows, n_merge, lo_all, ll_all, part_o, part_ml, total;
 };
 
 // Everything a kernel needs, passed by value.
@@ -66,6 +71,7 @@ struct Params {
     int32_t* cnt;          // [B, nb] valid tokens per block
     uint32_t* mbits;       // [B, nb] bit t = token t of the block is valid
     float* logits;         // [BH, nb, nb]  tau * qhat_i . khat_j
+    uint32_t* keys;        // [BH, nb, nb]  ordered key of each cell's selection score
     float* rowmax;         // [BH, nb]      max over valid j of logits
     uint32_t* hist;        // [BH, kHistBins]
     uint64_t* thresh;      // [BH] composite key of the last selected cell
@@ -76,7 +82,8 @@ struct Params {
     BlkRec* recs;          // [BH, K] selected blocks in CSR order
     int32_t* merge_rows;   // [BH, nb] rows the final kernel must combine (0 or >1 segments)
     int32_t* n_merge;      // [BH]
-    float* side_ml;        // [BH, N, 2] full mode: running max (log2) and sum of single-segment rows
+    float* lo_all;         // [BH, nb, d] full mode: sum over every key block j of w_ij vhat_j
+    float* ll_all;         // [BH, nb]    full mode: sum over every key block j of w_ij
     float* part_o;         // [BH, max_items, 32, d] un-normalised high-res numerators
     float* part_ml;        // [BH, max_items, 2, 32] running max (log2 units) and sum
     int32_t* error;        // device error flag (0 = fine)
@@ -108,6 +115,14 @@ __device__ __forceinline__ float cell_score(float logit, float m, int i, int j, 
 // Composite key: score first, then the smaller flat index wins a tie.
 __device__ __forceinline__ uint64_t cell_key64(uint32_t key32, uint32_t flat) {
     return ((uint64_t)key32 << 32) | (uint64_t)(0xFFFFFFFFu - flat);
+}
+
+// Low-resolution weight of cell (i, j) ([MRA] "第四步"): cnt_j exp(S_ij - m_i),
+// with m_i the row max of the low-res logits, 0 for an empty key block.
+// Every kernel that forms a weight uses this one expression, so a weight
+// added in one kernel and taken away in another cancels exactly.
+__device__ __forceinline__ float lowres_weight(float s, float m, int cnt) {
+    return cnt > 0 ? (float)cnt * __builtin_amdgcn_exp2f((s - m) * kLog2e) : 0.0f;
 }
 
 // fp32 -> bf16 bits, round to nearest even (finite inputs).

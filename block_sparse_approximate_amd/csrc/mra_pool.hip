@@ -8,7 +8,8 @@
 // an empty block pools to zeros.  Built with -ffp-contract=off.
 //
 // Mapping: a workgroup pools 8 consecutive blocks of one tensor and head,
-// which are one contiguous run of 256 token rows.  Every thread first issues
+// which are one contiguous run of 256 token rows; all workgroups of a head
+// run on the same XCD.  Every thread first issues
 // all of its 16-byte loads of that run (fully coalesced, one round trip),
 // stores them in LDS, and then each thread sums two channels of one block
 // over its 32 rows in token order.
@@ -36,12 +37,16 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(Params p, int ntens,
         if (gt == 0) *p.error = 0;
         for (int w = gt; w < zero_words; w += stride) p.hist[w] = 0u;
     }
-    const int g = blockIdx.x;
-    const int per_tensor = p.BH * groups_per_head;
-    const int tens = g / per_tensor;
-    const int rem = g - tens * per_tensor;
-    const int bh = rem / groups_per_head;
-    const int blk0 = (rem - bh * groups_per_head) * kPoolBlocks;
+    // workgroup g runs on XCD g % 8; every workgroup of head bh goes to XCD
+    // bh % 8, the XCD whose L2 the later stages of that head use
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int per_head = ntens * groups_per_head;
+    const int hm = slot / per_head;
+    const int rem = slot - hm * per_head;
+    const int tens = rem / groups_per_head;
+    const int bh = xcd + 8 * hm;
+    if (bh >= p.BH) return;
+    const int blk0 = (rem - tens * groups_per_head) * kPoolBlocks;
     const int nblk = min(kPoolBlocks, p.nb - blk0);
     const int b = bh / p.H;
     const int tid = threadIdx.x;
@@ -106,7 +111,7 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(Params p, int ntens,
 hipError_t launch_pool(const Params& p, hipStream_t s) {
     const int ntens = p.mode == 0 ? 3 : 2;
     const int groups_per_head = (p.nb + kPoolBlocks - 1) / kPoolBlocks;
-    const int grid = ntens * p.BH * groups_per_head;
+    const int grid = 8 * ((p.BH + 7) / 8) * ntens * groups_per_head;
     const int zero_words = p.BH * kHistBins;
     if (p.d != kHeadDim) return hipErrorInvalidValue;
     if (p.dtype == 1)

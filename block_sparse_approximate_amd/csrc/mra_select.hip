@@ -4,10 +4,14 @@
 // logits_kernel: workgroup (bh, t) computes the logits of 16 block rows of
 // head bh,  S_ij = fma-chain_c(qhat_i[c], khat_j[c]) * tau  (fp32, channels in
 // order from +0, the canonical order), the row maximum over non-empty key
-// blocks, the selection score of each cell and a 4096-bin histogram of the
-// top 12 bits of its ordered key, which it adds into the head's histogram.
+// blocks, the selection score of each cell, its ordered 32-bit key, and a
+// 4096-bin histogram of the top 12 key bits, which it adds into the head's
+// histogram.  In full mode it also sums the low-resolution attention of its
+// rows over every key block ("第四步"), selected or not.  All workgroups of a head run on one XCD, so the head's khat is
+// fetched from memory once and then served by that XCD's L2.
 //
-// select_kernel: one workgroup per head selects the top-K cells:
+// select_kernel: one workgroup of 1024 threads per head selects the top-K
+// cells:
 //   * the composite key of a cell is (ordered fp32 score, then the inverse
 //     flat index), so all keys differ and "the first K cells in (score
 //     descending, flat index ascending)" are exactly the K largest keys;
@@ -15,14 +19,16 @@
 //     first 12 bits, further 12-bit passes run only while that bin holds
 //     more than kCap cells; one pass then marks the cells above the bin as
 //     selected and copies the cells inside it into LDS, where 8-bit passes
-//     find the K-th largest key T;
+//     over those candidates find the K-th largest key T;
 //   * the selected set {key >= T} is written as a bitmap, as CSR (row_ptr,
 //     col ascending) and as the attention stream: one record per selected
-//     block, rows cut into segments of at most kChunk blocks.
-// The scores of a head are staged through LDS in tiles of 16384 cells (the
-// whole head up to N = 4096).  Every pass gives each thread a run of cells
-// and issues all of a thread's global loads before their first use, so a
-// pass costs about one memory round trip and no chain of LDS round trips.
+//     block, rows cut into segments of at most kChunk blocks; in full mode a
+//     record carries the low-res weight of its cell, which the attention
+//     kernel takes out of the row's low-res sum.
+// A thread holds 16 cell keys in registers (the whole head up to N = 4096;
+// longer heads are walked in tiles of 16384 cells with the next tile in
+// flight), and wave w's cells of a tile are 64 consecutive cells, so one
+// ballot is 64 consecutive bits of the selection.
 // The two kernels are separate launches: the kernel boundary is what makes
 // one workgroup's logits visible to another, with no device-wide fences.
 // The translation unit is built with -ffp-contract=off so that every fp32
@@ -32,13 +38,20 @@
 namespace mra {
 namespace {
 
-constexpr int kThreads = 512;
-constexpr int kWaves = kThreads / 64;
-constexpr int kRT = 16;        // block rows per logits workgroup
-constexpr int kCT = 128;       // key blocks per logits tile
-constexpr int kCap = 4096;     // selection candidates held in LDS
-constexpr int kTile = 16384;   // score cells staged in LDS at a time
-constexpr int kRun = kTile / kThreads;   // cells per thread and tile
+// logits kernel shape
+constexpr int kLgThreads = 512;
+constexpr int kLgWaves = kLgThreads / 64;
+constexpr int kRT = 2 * kLgWaves;   // block rows per logits workgroup (two per wave)
+constexpr int kCT = 128;            // key blocks per logits tile
+
+// select kernel shape
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kCells = 16;                         // cell keys per thread and tile
+constexpr int kTileCells = kSelThreads * kCells;   // 16384
+constexpr int kCap = 4096;                         // selection candidates held in LDS
+constexpr int kDigitBits = 8;                      // radix digit over the candidates
+constexpr int kDigitBins = 1 << kDigitBits;
 
 __host__ __device__ inline size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
 
@@ -60,62 +73,63 @@ __host__ __device__ inline LogitsLds logits_lds(int nb) {
     return L;
 }
 
-// Rows of scores staged in LDS at a time by the selector.
-__host__ __device__ inline int tile_rows(int nb) {
-    const int r = kTile / nb;
-    return r < 1 ? 1 : (r > nb ? nb : r);
-}
-
 struct SelectLds {
-    size_t tile, hist, cand, bitmap, rm, cntv, rc, ic, mbv, scan, small, total;
+    size_t hist, dig, cand, bitmap, rc, ic, mbv, rmv, stile, scan, small, total;
 };
 
-__host__ __device__ inline SelectLds select_lds(int nb) {
+// Full mode with the whole head in one tile stages the head's logits too,
+// for the low-res weights of the selected cells.
+__host__ __device__ inline bool stage_logits(int nb, int mode) {
+    return mode == 0 && (size_t)nb * nb <= (size_t)kTileCells;
+}
+
+__host__ __device__ inline SelectLds select_lds(int nb, int mode) {
     SelectLds L;
     const int words = (nb + 31) / 32;
     size_t o = 0;
-    L.tile = o; o = align16(o + (size_t)tile_rows(nb) * nb * 4);
+    L.stile = o; o = align16(o + (stage_logits(nb, mode) ? (size_t)nb * nb * 4 : 0));
+    L.rmv = o; o = align16(o + (size_t)nb * 4);
     L.hist = o; o = align16(o + kHistBins * 4);
+    L.dig = o; o = align16(o + 2 * kDigitBins * 4);
     L.cand = o; o = align16(o + (size_t)kCap * 8);
     L.bitmap = o; o = align16(o + (size_t)nb * words * 4);
-    L.rm = o; o = align16(o + (size_t)nb * 4);
-    L.cntv = o; o = align16(o + (size_t)nb * 4);
     L.rc = o; o = align16(o + (size_t)(nb + 1) * 4);
     L.ic = o; o = align16(o + (size_t)(nb + 1) * 4);
     L.mbv = o; o = align16(o + (size_t)nb * 4);
-    L.scan = o; o = align16(o + 64 * 4);
-    L.small = o; o = align16(o + 64 * 8);
+    L.scan = o; o = align16(o + (kSelWaves + 1) * 8);
+    L.small = o; o = align16(o + 32 * 4);
     L.total = o;
     return L;
 }
 
 // ---------------------------------------------------------------- helpers
-// Exclusive scan of one int per thread over the workgroup (kThreads).
-// Returns the exclusive prefix; *total gets the sum.  Uses scan[kWaves + 1].
-__device__ int block_excl_scan(int v, int* scan, int* total) {
+// Exclusive scan of one value per thread over the select workgroup.
+// Returns the exclusive prefix; *total gets the sum.  Uses scan[kSelWaves + 1].
+template <typename T>
+__device__ T block_excl_scan(T v, T* scan, T* total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int x = v;
+    T x = v;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-        int y = __shfl_up(x, off, 64);
+        const T y = __shfl_up(x, off, 64);
         if (lane >= off) x += y;
     }
     if (lane == 63) scan[wave] = x;
     __syncthreads();
     if (threadIdx.x < 64) {
-        const int t = threadIdx.x < kWaves ? scan[threadIdx.x] : 0;
-        int y = t;
+        const T t = threadIdx.x < kSelWaves ? scan[threadIdx.x] : T(0);
+        T y = t;
 #pragma unroll
-        for (int off = 1; off < kWaves; off <<= 1) {
-            int z = __shfl_up(y, off, 64);
+        for (int off = 1; off < kSelWaves; off <<= 1) {
+            const T z = __shfl_up(y, off, 64);
             if ((int)threadIdx.x >= off) y += z;
         }
-        if (threadIdx.x < kWaves) scan[threadIdx.x] = y - t;
-        if (threadIdx.x == kWaves - 1) scan[kWaves] = y;
+        if (threadIdx.x < kSelWaves) scan[threadIdx.x] = y - t;
+        if (threadIdx.x == kSelWaves - 1) scan[kSelWaves] = y;
     }
     __syncthreads();
-    const int ex = scan[wave] + x - v;
-    *total = scan[kWaves];
+    const T ex = scan[wave] + x - v;
+    *total = scan[kSelWaves];
     __syncthreads();
     return ex;
 }
@@ -124,26 +138,30 @@ struct BinPick {
     uint32_t bin, above, count;
 };
 
-// Find, in a histogram of kHistBins bins held in LDS, the bin where the
-// count taken from the top first reaches `need`.  Each thread owns 8 bins.
-__device__ BinPick pick_bin(const uint32_t* h, uint32_t need, int* scan, uint32_t* small) {
-    const int rt = kThreads - 1 - (int)threadIdx.x;   // reversed: the top bins come first
-    uint32_t local = 0;
+// In a histogram of kHistBins bins held in LDS, find the bin where the count
+// taken from the top first reaches `need`.  Each thread owns 4 bins; the
+// whole workgroup calls this.
+__device__ BinPick pick_bin(const uint32_t* h, uint32_t need, uint32_t* scan, uint32_t* small) {
+    constexpr int kPer = kHistBins / kSelThreads;
+    const int rt = kSelThreads - 1 - (int)threadIdx.x;   // reversed: the top bins come first
+    uint32_t c[kPer], local = 0;
 #pragma unroll
-    for (int e = 0; e < 8; e++) local += h[rt * 8 + e];
-    int tot;
-    const uint32_t above = (uint32_t)block_excl_scan((int)local, scan, &tot);
+    for (int e = 0; e < kPer; e++) {
+        c[e] = h[rt * kPer + e];
+        local += c[e];
+    }
+    uint32_t tot;
+    const uint32_t above = block_excl_scan<uint32_t>(local, scan, &tot);
     if (above < need && need <= above + local) {
         uint32_t acc = above;
-        for (int e = 7; e >= 0; e--) {
-            const uint32_t c = h[rt * 8 + e];
-            if (acc + c >= need) {
-                small[0] = (uint32_t)(rt * 8 + e);
+#pragma unroll
+        for (int e = kPer - 1; e >= 0; e--) {
+            if (acc < need && acc + c[e] >= need) {
+                small[0] = (uint32_t)(rt * kPer + e);
                 small[1] = acc;
-                small[2] = c;
-                break;
+                small[2] = c[e];
             }
-            acc += c;
+            acc += c[e];
         }
     }
     __syncthreads();
@@ -152,42 +170,166 @@ __device__ BinPick pick_bin(const uint32_t* h, uint32_t need, int* scan, uint32_
     return r;
 }
 
-__device__ __forceinline__ uint64_t tile_key(float logit, const float* rm, const int* cntv, int nb, int i, int j,
-                                            int pf, int pd) {
-    const float s = cell_score(logit, rm[i], i, j, cntv[i] > 0, cntv[j] > 0, pf, pd);
-    return cell_key64(float_key(s), (uint32_t)(i * nb + j));
-}
-
-// Global loads of a tile of scores into registers (all issued at once).
-__device__ __forceinline__ void fetch_tile(const float* __restrict__ S, int r0, int rows, int nb, float (&v)[kRun]) {
-    const int n = rows * nb;
-    const float* src = S + (size_t)r0 * nb;
+// The same over kDigitBins bins, by wave 0 alone (4 bins per lane); the
+// result goes to small[0..2] for the whole workgroup to read after a barrier.
+__device__ void pick_digit_wave(const uint32_t* h, uint32_t need, uint32_t* small) {
+    constexpr int kPer = kDigitBins / 64;
+    const int lane = threadIdx.x;
+    const int rt = 63 - lane;
+    uint32_t c[kPer], local = 0;
 #pragma unroll
-    for (int e = 0; e < kRun; e++) {
-        const int x = threadIdx.x + e * kThreads;
-        v[e] = x < n ? src[x] : 0.0f;
+    for (int e = 0; e < kPer; e++) {
+        c[e] = h[rt * kPer + e];
+        local += c[e];
+    }
+    uint32_t x = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    const uint32_t above = x - local;
+    if (above < need && need <= above + local) {
+        uint32_t acc = above;
+#pragma unroll
+        for (int e = kPer - 1; e >= 0; e--) {
+            if (acc < need && acc + c[e] >= need) {
+                small[0] = (uint32_t)(rt * kPer + e);
+                small[1] = acc;
+                small[2] = c[e];
+            }
+            acc += c[e];
+        }
     }
 }
 
-__device__ __forceinline__ void store_tile(int rows, int nb, const float (&v)[kRun], float* tile) {
-    const int n = rows * nb;
+// Cell keys of the tile at `base` into registers, every load issued at once;
+// register e holds cell base + threadIdx.x + e * kSelThreads.
+__device__ __forceinline__ void fetch_keys(const uint32_t* __restrict__ G, uint32_t base, uint32_t ncell,
+                                           uint32_t (&kv)[kCells]) {
 #pragma unroll
-    for (int e = 0; e < kRun; e++) {
-        const int x = threadIdx.x + e * kThreads;
-        if (x < n) tile[x] = v[e];
+    for (int e = 0; e < kCells; e++) {
+        const uint32_t x = base + threadIdx.x + e * kSelThreads;
+        kv[e] = x < ncell ? G[x] : 0u;
+    }
+}
+
+// Block row of flat cell x: x / nb by a multiply-high with one correction
+// step each way (x < 2^18 and nb <= 512 here).
+__device__ __forceinline__ uint32_t row_of(uint32_t x, uint32_t nb, uint32_t magic) {
+    uint32_t i = __umulhi(x, magic);
+    if (i * nb > x) i--;
+    if ((i + 1) * nb <= x) i++;
+    return i;
+}
+
+// The marking pass of the selector over every cell of a head, tile by tile:
+// a cell whose key prefix (the top pbits bits of the composite key) is above
+// `prefix` is selected for sure and goes into the bitmap; a cell whose prefix
+// equals it is a candidate and goes into the LDS list (one LDS atomic per wave
+// and four 64-cell groups).  kRows64: a block row holds a multiple of 64
+// cells, so a wave's 64 consecutive cells are two whole bitmap words and are
+// stored without atomics.  kNarrow: pbits <= 32, so the prefix is a prefix of
+// the 32-bit score key alone.
+template <bool kRows64, bool kNarrow>
+__device__ __forceinline__ void mark_cells(const uint32_t* __restrict__ G, uint32_t ncell, int ntiles, int nb,
+                                           int words, uint32_t magic, uint64_t prefix, int pbits,
+                                           uint32_t (&kv)[kCells], uint32_t* bitmap, uint64_t* cand,
+                                           uint32_t* small) {
+    const int lane = threadIdx.x & 63;
+    const uint64_t lt_mask = (1ull << lane) - 1ull;
+    const uint32_t wbase = (uint32_t)__builtin_amdgcn_readfirstlane((int)threadIdx.x - lane);
+    const uint32_t sh = kNarrow ? (uint32_t)(32 - pbits) : 0u;
+    const uint32_t p32 = (uint32_t)prefix;
+    for (int t = 0; t < ntiles; t++) {
+        const uint32_t base = (uint32_t)t * kTileCells;
+        uint32_t kn[kCells];
+        if (t + 1 < ntiles) fetch_keys(G, base + kTileCells, ncell, kn);   // next tile in flight
+#pragma unroll
+        for (int e0 = 0; e0 < kCells; e0 += 4) {
+            uint64_t mh[4];
+            bool hit[4];
+            uint32_t tot = 0;
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const int e = e0 + q;
+                const uint32_t x0 = base + wbase + (uint32_t)e * kSelThreads;   // the wave's first cell
+                const uint32_t x = x0 + lane;
+                const bool in = x < ncell;
+                bool sure;
+                if constexpr (kNarrow) {
+                    const uint32_t top = kv[e] >> sh;
+                    sure = in && top > p32;
+                    hit[q] = in && top == p32;
+                } else {
+                    const uint64_t top = cell_key64(kv[e], x) >> (64 - pbits);
+                    sure = in && top > prefix;
+                    hit[q] = in && top == prefix;
+                }
+                const uint64_t ms = __ballot(sure);
+                if constexpr (kRows64) {
+                    if (x0 < ncell) {
+                        const uint32_t i0 = row_of(x0, (uint32_t)nb, magic), j0 = x0 - i0 * (uint32_t)nb;
+                        if (lane == 0)
+                            *reinterpret_cast<uint2*>(bitmap + i0 * words + (j0 >> 5)) =
+                                make_uint2((uint32_t)ms, (uint32_t)(ms >> 32));
+                    }
+                } else if (sure) {
+                    const uint32_t i = row_of(x, (uint32_t)nb, magic), j = x - i * (uint32_t)nb;
+                    atomicOr(&bitmap[i * words + (j >> 5)], 1u << (j & 31));
+                }
+                mh[q] = __ballot(hit[q]);
+                tot += (uint32_t)__popcll(mh[q]);
+            }
+            if (tot) {
+                uint32_t at0 = 0;
+                if (lane == 0) at0 = atomicAdd(&small[8], tot);
+                at0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)at0);
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    if (hit[q]) {
+                        const uint32_t x = base + wbase + (uint32_t)(e0 + q) * kSelThreads + lane;
+                        const uint32_t at = at0 + (uint32_t)__popcll(mh[q] & lt_mask);
+                        if (at < (uint32_t)kCap) cand[at] = cell_key64(kv[e0 + q], x);
+                    }
+                    at0 += (uint32_t)__popcll(mh[q]);
+                }
+            }
+        }
+        if (t + 1 < ntiles) {
+#pragma unroll
+            for (int e = 0; e < kCells; e++) kv[e] = kn[e];
+        }
+    }
+}
+
+// A [kCT][kHeadDim] tile of vhat starting at key block j0 into registers:
+// float4 x = threadIdx.x + e * kLgThreads is block j0 + x / 16, channels
+// 4 * (x % 16) .. +3.
+__device__ __forceinline__ void fetch_vhat(const float* __restrict__ vh, int j0, int nb,
+                                           float4 (&vv)[kCT * (kHeadDim / 4) / kLgThreads]) {
+#pragma unroll
+    for (int e = 0; e < kCT * (kHeadDim / 4) / kLgThreads; e++) {
+        const int x = threadIdx.x + e * kLgThreads, j = j0 + (x >> 4);
+        vv[e] = j < nb ? *reinterpret_cast<const float4*>(vh + (size_t)j * kHeadDim + (x & 15) * 4)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 }
 
 // ---------------------------------------------------------------- logits
 // kGiven: the logits are already in p.logits (selector hook); skip their
-// computation and only form row maxima and the histogram.
+// computation and only form row maxima, keys and the histogram.
 template <bool kGiven>
-__global__ __launch_bounds__(kThreads) void logits_kernel(Params p) {
+__global__ __launch_bounds__(kLgThreads) void logits_kernel(Params p) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int nb = p.nb;
     const int tiles_per_head = (nb + kRT - 1) / kRT;
-    const int bh = blockIdx.x / tiles_per_head;
-    const int row0 = (blockIdx.x - bh * tiles_per_head) * kRT;
+    // workgroup g runs on XCD g % 8; head bh's tiles all go to XCD bh % 8
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int hm = slot / tiles_per_head;
+    const int bh = xcd + 8 * hm;
+    if (bh >= p.BH) return;
+    const int row0 = (slot - hm * tiles_per_head) * kRT;
     const int b = bh / p.H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float tau = (float)(1.0 / __builtin_sqrt((double)p.d));
@@ -203,10 +345,13 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(Params p) {
     const float* kh = p.khat + (size_t)bh * nb * kHeadDim;
 
     // every global load of the prologue first, then the LDS stores
-    constexpr int kKLoads = kCT * (kHeadDim / 4) / kThreads;   // float4s of one khat tile per thread
-    int cn = tid < nb ? p.cnt[b * nb + tid] : 0;               // nb <= 512 = kThreads
+    constexpr int kKLoads = kCT * (kHeadDim / 4) / kLgThreads;   // float4s of one khat tile per thread
+    int cn = tid < nb ? p.cnt[b * nb + tid] : 0;                 // nb <= 512 = kLgThreads
+    const bool lowres = !kGiven && p.mode == 0;
+    const float* vh = lowres ? p.vhat + (size_t)bh * nb * kHeadDim : nullptr;
     float4 qv = make_float4(0.f, 0.f, 0.f, 0.f);
-    float4 kv[kKLoads];
+    float4 kv[kKLoads], vv[kKLoads];
+    if (lowres) fetch_vhat(vh, 0, nb, vv);
     if (!kGiven) {
         if (tid < kRT * kHeadDim / 4) {
             const int r = tid / (kHeadDim / 4), c4 = (tid % (kHeadDim / 4)) * 4;
@@ -214,18 +359,18 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(Params p) {
         }
 #pragma unroll
         for (int e = 0; e < kKLoads; e++) {
-            const int x = tid + e * kThreads, jj = x % kCT, c4 = (x / kCT) * 4;
+            const int x = tid + e * kLgThreads, jj = x % kCT, c4 = (x / kCT) * 4;
             kv[e] = jj < nb ? *reinterpret_cast<const float4*>(kh + (size_t)jj * kHeadDim + c4)
                             : make_float4(0.f, 0.f, 0.f, 0.f);
         }
     } else {
-        for (int x = tid; x < kRT * nb; x += kThreads) {
+        for (int x = tid; x < kRT * nb; x += kLgThreads) {
             const int r = x / nb, j = x - r * nb;
             srow[x] = (row0 + r < nb) ? p.logits[((size_t)bh * nb + row0 + r) * nb + j] : 0.0f;
         }
     }
     if (tid < nb) cntv[tid] = cn;
-    for (int x = tid; x < kHistBins; x += kThreads) hist[x] = 0u;
+    for (int x = tid; x < kHistBins; x += kLgThreads) hist[x] = 0u;
     if (!kGiven && tid < kRT * kHeadDim / 4) {
         const int r = tid / (kHeadDim / 4), c4 = (tid % (kHeadDim / 4)) * 4;
         qT[(c4 + 0) * kRT + r] = qv.x;
@@ -239,7 +384,7 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(Params p) {
         // kT[c][jj] = khat[j0 + jj][c]
 #pragma unroll
         for (int e = 0; e < kKLoads; e++) {
-            const int x = tid + e * kThreads, jj = x % kCT, c4 = (x / kCT) * 4;
+            const int x = tid + e * kLgThreads, jj = x % kCT, c4 = (x / kCT) * 4;
             kT[(c4 + 0) * kCT + jj] = kv[e].x;
             kT[(c4 + 1) * kCT + jj] = kv[e].y;
             kT[(c4 + 2) * kCT + jj] = kv[e].z;
@@ -249,7 +394,7 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(Params p) {
         if (j0 + kCT < nb) {   // the next khat tile is in flight during this one
 #pragma unroll
             for (int e = 0; e < kKLoads; e++) {
-                const int x = tid + e * kThreads, jj = x % kCT, c4 = (x / kCT) * 4;
+                const int x = tid + e * kLgThreads, jj = x % kCT, c4 = (x / kCT) * 4;
                 kv[e] = j0 + kCT + jj < nb
                             ? *reinterpret_cast<const float4*>(kh + (size_t)(j0 + kCT + jj) * kHeadDim + c4)
                             : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -287,100 +432,161 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(Params p) {
         if (lane == 0) rmax[r] = m;
     }
     __syncthreads();
-    // scores -> histogram of the top 12 key bits; logits and maxima out
+    // scores -> keys and the histogram of their top 12 bits; logits and maxima out
     float* Sg = p.logits + (size_t)bh * nb * nb;
-    for (int x = tid; x < kRT * nb; x += kThreads) {
+    uint32_t* Kg = p.keys + (size_t)bh * nb * nb;
+    for (int x = tid; x < kRT * nb; x += kLgThreads) {
         const int r = x / nb, j = x - r * nb, i = row0 + r;
         if (i >= nb) continue;
         const float sv = srow[x];
         if (!kGiven) Sg[(size_t)i * nb + j] = sv;
         const float s = cell_score(sv, rmax[r], i, j, cntv[i] > 0, cntv[j] > 0, p.prior_first, p.prior_diag);
-        atomicAdd(&hist[float_key(s) >> (32 - kHistBits)], 1u);
+        const uint32_t key = float_key(s);
+        Kg[(size_t)i * nb + j] = key;
+        atomicAdd(&hist[key >> (32 - kHistBits)], 1u);
     }
-    for (int r = tid; r < kRT; r += kThreads)
+    for (int r = tid; r < kRT; r += kLgThreads)
         if (row0 + r < nb) p.rowmax[(size_t)bh * nb + row0 + r] = rmax[r];
     __syncthreads();
     uint32_t* gh = p.hist + (size_t)bh * kHistBins;
-    for (int x = tid; x < kHistBins; x += kThreads)
+    for (int x = tid; x < kHistBins; x += kLgThreads)
         if (hist[x]) atomicAdd(&gh[x], hist[x]);
+    if (!lowres) return;
+
+    // Full mode: the low-res sums of these rows over every key block,
+    //   lo_all_i = sum_j w_ij vhat_j,  ll_all_i = sum_j w_ij,
+    // from which the block attention takes away the selected blocks' terms.
+    // The weights replace the logits in LDS; vhat is staged in tiles of kCT
+    // key blocks with the next tile in flight.
+    for (int x = tid; x < kRT * nb; x += kLgThreads) {
+        const int r = x / nb, j = x - r * nb;
+        srow[x] = row0 + r < nb ? lowres_weight(srow[x], rmax[r], cntv[j]) : 0.f;
+    }
+    const int rr = tid >> 5, c2 = (tid & 31) * 2;   // row and channel pair of this thread
+    float* vt = kT;                                  // [kCT][kHeadDim] vhat tile
+    float acc0 = 0.f, acc1 = 0.f, lsum = 0.f;
+    for (int j0 = 0; j0 < nb; j0 += kCT) {
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < kKLoads; e++) {
+            const int x = tid + e * kLgThreads;
+            *reinterpret_cast<float4*>(vt + (x >> 4) * kHeadDim + (x & 15) * 4) = vv[e];
+        }
+        __syncthreads();
+        if (j0 + kCT < nb) fetch_vhat(vh, j0 + kCT, nb, vv);
+        const int jn = min(kCT, nb - j0);
+        const float* wr = srow + (size_t)rr * nb + j0;
+#pragma unroll 8
+        for (int jj = 0; jj < jn; jj++) {
+            const float w = wr[jj];
+            const float2 v = *reinterpret_cast<const float2*>(vt + jj * kHeadDim + c2);
+            acc0 = __builtin_fmaf(w, v.x, acc0);
+            acc1 = __builtin_fmaf(w, v.y, acc1);
+            lsum += w;
+        }
+    }
+    if (row0 + rr < nb) {
+        const size_t row = (size_t)bh * nb + row0 + rr;
+        *reinterpret_cast<float2*>(p.lo_all + row * kHeadDim + c2) = make_float2(acc0, acc1);
+        if (c2 == 0) p.ll_all[row] = lsum;
+    }
 }
 
 // ---------------------------------------------------------------- select
-__global__ __launch_bounds__(kThreads) void select_kernel(Params p) {
+__global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int nb = p.nb;
     const int bh = blockIdx.x;
     const int b = bh / p.H;
-    const int tid = threadIdx.x;
-    const SelectLds L = select_lds(nb);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const SelectLds L = select_lds(nb, p.mode);
+    const bool full = p.mode == 0;
+    const bool staged = stage_logits(nb, p.mode);
     const int words = p.words;
-    float* stile = reinterpret_cast<float*>(smem + L.tile);
     uint32_t* hist = reinterpret_cast<uint32_t*>(smem + L.hist);
+    uint32_t* dig = reinterpret_cast<uint32_t*>(smem + L.dig);
     uint64_t* cand = reinterpret_cast<uint64_t*>(smem + L.cand);
     uint32_t* bitmap = reinterpret_cast<uint32_t*>(smem + L.bitmap);
-    float* rm = reinterpret_cast<float*>(smem + L.rm);
-    int* cntv = reinterpret_cast<int*>(smem + L.cntv);
     int* rc = reinterpret_cast<int*>(smem + L.rc);
     int* ic = reinterpret_cast<int*>(smem + L.ic);
     uint32_t* mbv = reinterpret_cast<uint32_t*>(smem + L.mbv);
-    int* scan = reinterpret_cast<int*>(smem + L.scan);
+    float* rmv = reinterpret_cast<float*>(smem + L.rmv);
+    float* stile = reinterpret_cast<float*>(smem + L.stile);
+    uint32_t* scan32 = reinterpret_cast<uint32_t*>(smem + L.scan);
+    uint64_t* scan64 = reinterpret_cast<uint64_t*>(smem + L.scan);
     uint32_t* small = reinterpret_cast<uint32_t*>(smem + L.small);
-    const float* S = p.logits + (size_t)bh * nb * nb;
-    const int pf = p.prior_first, pd = p.prior_diag;
-    const int trows = tile_rows(nb);
-    const bool resident = trows >= nb;   // the whole head fits one tile: stage it once
+    const uint32_t ncell = (uint32_t)nb * (uint32_t)nb;
+    const int ntiles = (int)((ncell + kTileCells - 1) / kTileCells);
+    const uint32_t* G = p.keys + (size_t)bh * ncell;
+    const uint32_t magic = 0xFFFFFFFFu / (uint32_t)nb + 1u;
 
     // prologue: all global loads, then the LDS stores
+    uint32_t kv[kCells];
     {
-        uint32_t hv[kHistBins / kThreads];
+        constexpr int kPer = kHistBins / kSelThreads;
+        uint32_t hv[kPer];
 #pragma unroll
-        for (int e = 0; e < kHistBins / kThreads; e++) hv[e] = p.hist[(size_t)bh * kHistBins + tid + e * kThreads];
-        float tv[kRun];
-        if (resident) fetch_tile(S, 0, nb, nb, tv);
-        const int cn = tid < nb ? p.cnt[b * nb + tid] : 0;   // nb <= 512 = kThreads
-        const float rv = tid < nb ? p.rowmax[(size_t)bh * nb + tid] : 0.f;
-        const uint32_t mv = tid < nb ? p.mbits[b * nb + tid] : 0u;
+        for (int e = 0; e < kPer; e++) hv[e] = p.hist[(size_t)bh * kHistBins + tid + e * kSelThreads];
+        fetch_keys(G, 0, ncell, kv);
+        const float* Sg = p.logits + (size_t)bh * ncell;
+        float sv[kCells];
+        if (staged) {
+#pragma unroll
+            for (int e = 0; e < kCells; e++) {
+                const uint32_t x = tid + e * kSelThreads;
+                sv[e] = x < ncell ? Sg[x] : 0.f;
+            }
+        }
+        const uint32_t mv = tid < nb ? p.mbits[b * nb + tid] : 0u;   // nb <= 512 < kSelThreads
+        const float rv = (full && tid < nb) ? p.rowmax[(size_t)bh * nb + tid] : 0.f;
         if (tid < nb) {
-            cntv[tid] = cn;
-            rm[tid] = rv;
             mbv[tid] = mv;
+            rmv[tid] = rv;
+        }
+        if (staged) {
+#pragma unroll
+            for (int e = 0; e < kCells; e++) {
+                const uint32_t x = tid + e * kSelThreads;
+                if (x < ncell) stile[x] = sv[e];
+            }
         }
 #pragma unroll
-        for (int e = 0; e < kHistBins / kThreads; e++) hist[tid + e * kThreads] = hv[e];
-        for (int x = tid; x < nb * words; x += kThreads) bitmap[x] = 0u;
-        if (resident) store_tile(nb, nb, tv, stile);
+        for (int e = 0; e < kPer; e++) hist[tid + e * kSelThreads] = hv[e];
+        for (int x = tid; x < nb * words; x += kSelThreads) bitmap[x] = 0u;
+        if (tid < 2 * kDigitBins) dig[tid] = 0u;
+        if (tid == 0) small[8] = 0u;
     }
     __syncthreads();
 
     uint32_t need = (uint32_t)p.K;
-    BinPick bp = pick_bin(hist, need, scan, small);
+    BinPick bp = pick_bin(hist, need, scan32, small);
     need -= bp.above;
     uint64_t prefix = bp.bin;
     int pbits = kHistBits;
     uint32_t count = bp.count;
 
     // further 12-bit passes while the bin is too large for LDS (tie-heavy inputs)
+    bool tile0 = true;   // kv holds tile 0
     while (count > (uint32_t)kCap && pbits < 64) {
         const int db = (64 - pbits) < 12 ? (64 - pbits) : 12;
-        for (int x = tid; x < kHistBins; x += kThreads) hist[x] = 0u;
-        for (int r0 = 0; r0 < nb; r0 += trows) {
-            const int rows = min(trows, nb - r0);
-            if (!resident) {
-                float tv[kRun];
-                fetch_tile(S, r0, rows, nb, tv);
-                __syncthreads();
-                store_tile(rows, nb, tv, stile);
+        for (int x = tid; x < kHistBins; x += kSelThreads) hist[x] = 0u;
+        __syncthreads();
+        for (int t = 0; t < ntiles; t++) {
+            const uint32_t base = (uint32_t)t * kTileCells;
+            if (ntiles > 1) {
+                fetch_keys(G, base, ncell, kv);
+                tile0 = t == 0;
             }
-            __syncthreads();
-            for (int x = tid; x < rows * nb; x += kThreads) {
-                const int r = x / nb, j = x - r * nb, i = r0 + r;
-                const uint64_t k64 = tile_key(stile[x], rm, cntv, nb, i, j, pf, pd);
-                if ((k64 >> (64 - pbits)) == prefix)
+#pragma unroll
+            for (int e = 0; e < kCells; e++) {
+                const uint32_t x = base + tid + e * kSelThreads;
+                const uint64_t k64 = cell_key64(kv[e], x);
+                if (x < ncell && (k64 >> (64 - pbits)) == prefix)
                     atomicAdd(&hist[(uint32_t)((k64 >> (64 - pbits - db)) & ((1ull << db) - 1))], 1u);
             }
         }
         __syncthreads();
-        bp = pick_bin(hist, need, scan, small);
+        bp = pick_bin(hist, need, scan32, small);
         need -= bp.above;
         prefix = (prefix << db) | bp.bin;
         pbits += db;
@@ -388,171 +594,138 @@ __global__ __launch_bounds__(kThreads) void select_kernel(Params p) {
     }
 
     // One pass over the cells: cells above the bin are selected for sure
-    // (bitmap), cells inside it are appended to the LDS candidate list.  A
-    // wave takes 64 consecutive cells at a time, so its LDS reads are
-    // conflict-free and, when a row holds a multiple of 64 blocks, one ballot
-    // is two whole bitmap words.
-    if (tid == 0) small[8] = 0u;
+    // (bitmap), cells inside it are appended to the LDS candidate list.
+    if (!tile0) fetch_keys(G, 0, ncell, kv);
     const bool rows64 = (nb & 63) == 0;
-    const int lane = tid & 63;
-    for (int r0 = 0; r0 < nb; r0 += trows) {
-        const int rows = min(trows, nb - r0);
-        const int n = rows * nb;
-        if (!resident) {
-            float tv[kRun];
-            fetch_tile(S, r0, rows, nb, tv);
-            __syncthreads();
-            store_tile(rows, nb, tv, stile);
-        }
-        __syncthreads();
-        for (int x0 = tid - lane; x0 < n; x0 += kThreads) {
-            const int x = x0 + lane;
-            bool sure = false, hit = false;
-            uint64_t k64 = 0;
-            int i = 0, j = 0;
-            if (x < n) {
-                const int r = x / nb;
-                j = x - r * nb;
-                i = r0 + r;
-                k64 = tile_key(stile[x], rm, cntv, nb, i, j, pf, pd);
-                const uint64_t top = k64 >> (64 - pbits);
-                sure = top > prefix;
-                hit = top == prefix;
-            }
-            const uint64_t ms = __ballot(sure);
-            if (rows64) {
-                if (lane == 0) {
-                    const int i0 = r0 + x0 / nb, j0 = x0 - (x0 / nb) * nb;
-                    bitmap[i0 * words + (j0 >> 5)] = (uint32_t)ms;
-                    bitmap[i0 * words + (j0 >> 5) + 1] = (uint32_t)(ms >> 32);
-                }
-            } else if (sure) {
-                atomicOr(&bitmap[i * words + (j >> 5)], 1u << (j & 31));
-            }
-            const uint64_t mh = __ballot(hit);
-            if (mh) {
-                uint32_t base = 0;
-                if (lane == 0) base = atomicAdd(&small[8], (uint32_t)__popcll(mh));
-                base = __shfl(base, 0, 64);
-                if (hit) {
-                    const uint32_t at = base + (uint32_t)__popcll(mh & ((1ull << lane) - 1ull));
-                    if (at < (uint32_t)kCap) cand[at] = k64;
-                }
-            }
-        }
+    if (pbits <= 32) {
+        if (rows64) mark_cells<true, true>(G, ncell, ntiles, nb, words, magic, prefix, pbits, kv, bitmap, cand, small);
+        else mark_cells<false, true>(G, ncell, ntiles, nb, words, magic, prefix, pbits, kv, bitmap, cand, small);
+    } else {
+        if (rows64) mark_cells<true, false>(G, ncell, ntiles, nb, words, magic, prefix, pbits, kv, bitmap, cand, small);
+        else mark_cells<false, false>(G, ncell, ntiles, nb, words, magic, prefix, pbits, kv, bitmap, cand, small);
     }
     __syncthreads();
     const uint32_t ncand_all = small[8];
-    __syncthreads();
     const uint32_t ncand = ncand_all < (uint32_t)kCap ? ncand_all : (uint32_t)kCap;
     if (tid == 0 && ncand_all != count) atomicOr(reinterpret_cast<unsigned int*>(p.error), 1u);
 
-    // 8-bit passes over the candidates until the K-th largest key is pinned down
+    // 8-bit passes over the candidates until the K-th largest key is pinned
+    // down; the two digit histograms alternate, so a pass clears the other one
+    // and needs two barriers.
+    int buf = 0;
     while (pbits < 64) {
-        const int db = (64 - pbits) < 8 ? (64 - pbits) : 8;
-        for (int x = tid; x < kHistBins; x += kThreads) hist[x] = 0u;
-        __syncthreads();
-        for (uint32_t c = tid; c < ncand; c += kThreads) {
+        const int db = (64 - pbits) < kDigitBits ? (64 - pbits) : kDigitBits;
+        uint32_t* hc = dig + buf * kDigitBins;
+        for (uint32_t c = tid; c < ncand; c += kSelThreads) {
             const uint64_t k64 = cand[c];
             if ((k64 >> (64 - pbits)) == prefix)
-                atomicAdd(&hist[(uint32_t)((k64 >> (64 - pbits - db)) & ((1ull << db) - 1))], 1u);
+                atomicAdd(&hc[(uint32_t)((k64 >> (64 - pbits - db)) & ((1ull << db) - 1))], 1u);
         }
+        if (tid < kDigitBins) dig[(buf ^ 1) * kDigitBins + tid] = 0u;
         __syncthreads();
-        bp = pick_bin(hist, need, scan, small);
-        need -= bp.above;
-        prefix = (prefix << db) | bp.bin;
+        if (tid < 64) pick_digit_wave(hc, need, small + 16);
+        __syncthreads();
+        const uint32_t dbin = small[16], dabove = small[17], dcount = small[18];
+        need -= dabove;
+        prefix = (prefix << db) | dbin;
         pbits += db;
-        if (bp.count == 1u && pbits < 64) {
+        buf ^= 1;
+        if (dcount == 1u && pbits < 64) {
             // a single cell left: it is the threshold
-            for (uint32_t c = tid; c < ncand; c += kThreads) {
-                if ((cand[c] >> (64 - pbits)) == prefix) {
-                    small[10] = (uint32_t)(cand[c] >> 32);
-                    small[11] = (uint32_t)cand[c];
+            for (uint32_t c = tid; c < ncand; c += kSelThreads) {
+                const uint64_t k64 = cand[c];
+                if ((k64 >> (64 - pbits)) == prefix) {
+                    small[20] = (uint32_t)(k64 >> 32);
+                    small[21] = (uint32_t)k64;
                 }
             }
             __syncthreads();
-            prefix = ((uint64_t)small[10] << 32) | small[11];
+            prefix = ((uint64_t)small[20] << 32) | small[21];
             pbits = 64;
-            __syncthreads();
         }
     }
     const uint64_t T = prefix;
     if (tid == 0) p.thresh[bh] = T;
 
     // candidates at or above the threshold join the bitmap
-    for (uint32_t c = tid; c < ncand; c += kThreads) {
+    for (uint32_t c = tid; c < ncand; c += kSelThreads) {
         const uint64_t k64 = cand[c];
         if (k64 >= T) {
             const uint32_t f = 0xFFFFFFFFu - (uint32_t)k64;
-            const int i = (int)(f / (uint32_t)nb), j = (int)(f - (uint32_t)i * (uint32_t)nb);
-            if (i < nb) atomicOr(&bitmap[i * words + (j >> 5)], 1u << (j & 31));
+            const uint32_t i = row_of(f, (uint32_t)nb, magic), j = f - i * (uint32_t)nb;
+            if (i < (uint32_t)nb) atomicOr(&bitmap[i * words + (j >> 5)], 1u << (j & 31));
         }
     }
     __syncthreads();
 
-    // CSR row pointers and segment (item) pointers
+    // CSR row pointers, segment (item) pointers and the rows the final kernel
+    // combines, in one scan: one block row per thread (nb <= 512)
     int32_t* row_ptr = p.row_ptr + (size_t)bh * (nb + 1);
     int32_t* item_ptr = p.item_ptr + (size_t)bh * (nb + 1);
-    int row_base = 0, item_base = 0;
-    for (int i0 = 0; i0 < nb; i0 += kThreads) {
-        const int i = i0 + tid;
+    {
+        const int i = tid;
         int c = 0;
         if (i < nb)
             for (int w = 0; w < words; w++) c += __popc(bitmap[i * words + w]);
         const int it = (c + kChunk - 1) / kChunk;
-        int tc, ti;
-        const int ec = block_excl_scan(c, scan, &tc);
-        const int ei = block_excl_scan(it, scan, &ti);
+        const int mf = (i < nb && it != 1) ? 1 : 0;   // no selected block, or several segments
+        const uint64_t v = (uint64_t)c | ((uint64_t)it << 32) | ((uint64_t)mf << 48);
+        uint64_t tot;
+        const uint64_t ex = block_excl_scan<uint64_t>(v, scan64, &tot);
+        const int ec = (int)(uint32_t)ex, ei = (int)((ex >> 32) & 0xFFFFu), em = (int)(ex >> 48);
         if (i < nb) {
-            row_ptr[i] = row_base + ec;
-            item_ptr[i] = item_base + ei;
-            rc[i] = row_base + ec;
-            ic[i] = item_base + ei;
+            row_ptr[i] = ec;
+            item_ptr[i] = ei;
+            rc[i] = ec;
+            ic[i] = ei;
+            if (mf) p.merge_rows[(size_t)bh * nb + em] = i;
         }
-        row_base += tc;
-        item_base += ti;
-    }
-    if (tid == 0) {
-        row_ptr[nb] = row_base;
-        item_ptr[nb] = item_base;
-        rc[nb] = row_base;
-        ic[nb] = item_base;
-        small[12] = 0u;
-        if ((int64_t)row_base != p.K || item_base > p.max_items) atomicOr(reinterpret_cast<unsigned int*>(p.error), 2u);
+        if (tid == 0) {
+            const int tc = (int)(uint32_t)tot, ti = (int)((tot >> 32) & 0xFFFFu), tm = (int)(tot >> 48);
+            row_ptr[nb] = tc;
+            item_ptr[nb] = ti;
+            rc[nb] = tc;
+            ic[nb] = ti;
+            p.n_merge[bh] = tm;
+            if ((int64_t)tc != p.K || ti > p.max_items) atomicOr(reinterpret_cast<unsigned int*>(p.error), 2u);
+        }
     }
     __syncthreads();
 
-    // column lists and the attention stream records, one thread per row
+    // column lists and the attention stream records: one thread per (block
+    // row, bitmap word), which walks the set bits of its word; a cell's rank
+    // in its row counts the bits of the row's earlier words
     int32_t* col = p.col + (size_t)bh * p.K;
     BlkRec* recs = p.recs + (size_t)bh * p.K;
     uint32_t* gbits = p.selbits + (size_t)bh * nb * words;
-    for (int x = tid; x < nb * words; x += kThreads) gbits[x] = bitmap[x];
-    for (int i = tid; i < nb; i += kThreads) {
+    for (int x = tid; x < nb * words; x += kSelThreads) {
+        const int i = x / words, w = x - i * words;
+        uint32_t bits = bitmap[x];
+        gbits[x] = bits;
+        if (!bits) continue;
+        int r = 0;
+        for (int u = 0; u < w; u++) r += __popc(bitmap[i * words + u]);
         const int o = rc[i], n = rc[i + 1] - o, first = ic[i];
         const int nit = (n + kChunk - 1) / kChunk;
-        if (nit != 1) {   // no selected block, or several segments: the final kernel combines this row
-            const uint32_t at = atomicAdd(&small[12], 1u);
-            if (at < (uint32_t)nb) p.merge_rows[(size_t)bh * nb + at] = i;
-        }
-        int r = 0;
-        for (int w = 0; w < words && r < n; w++) {
-            uint32_t bits = bitmap[i * words + w];
-            while (bits) {
-                const int j = w * 32 + __builtin_ctz(bits);
-                bits &= bits - 1;
-                const int e = o + r;
-                if (e < p.K) {
-                    col[e] = j;
-                    const int sg = r / kChunk;
-                    const int len = min(kChunk, n - sg * kChunk);
-                    recs[e] = BlkRec{i, j, mbv[j], rec_info(first + sg, r - sg * kChunk, len, nit == 1)};
+        const float mi = rmv[i];
+        while (bits) {
+            const int j = w * 32 + __builtin_ctz(bits);
+            bits &= bits - 1;
+            const int e = o + r;
+            if (e < p.K) {
+                col[e] = j;
+                const int sg = r / kChunk;
+                const int len = min(kChunk, n - sg * kChunk);
+                float wt = 0.f;
+                if (full) {
+                    const float sij = staged ? stile[i * nb + j] : p.logits[((size_t)bh * nb + i) * nb + j];
+                    wt = lowres_weight(sij, mi, __popc(mbv[j]));
                 }
-                r++;
+                recs[e] = BlkRec{rec_ij(i, j), mbv[j], wt, rec_info(first + sg, r - sg * kChunk, len, nit == 1)};
             }
+            r++;
         }
     }
-    __syncthreads();
-    if (tid == 0) p.n_merge[bh] = (int32_t)min(small[12], (uint32_t)nb);
 }
 
 }  // namespace
@@ -563,8 +736,9 @@ static hipError_t launch_logits_t(const Params& p, hipStream_t s) {
     static const hipError_t a1 = hipFuncSetAttribute(reinterpret_cast<const void*>(&logits_kernel<kGiven>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (a1 != hipSuccess) return a1;
-    hipLaunchKernelGGL(logits_kernel<kGiven>, dim3(p.BH * tiles_per_head), dim3(kThreads), logits_lds(p.nb).total,
-                       s, p);
+    const int heads_per_xcd = (p.BH + 7) / 8;
+    hipLaunchKernelGGL(logits_kernel<kGiven>, dim3(8 * heads_per_xcd * tiles_per_head), dim3(kLgThreads),
+                       logits_lds(p.nb).total, s, p);
     return hipGetLastError();
 }
 
@@ -575,7 +749,7 @@ hipError_t launch_select(const Params& p, hipStream_t s) {
     static const hipError_t a2 = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (a2 != hipSuccess) return a2;
-    hipLaunchKernelGGL(select_kernel, dim3(p.BH), dim3(kThreads), select_lds(p.nb).total, s, p);
+    hipLaunchKernelGGL(select_kernel, dim3(p.BH), dim3(kSelThreads), select_lds(p.nb, p.mode).total, s, p);
     return hipGetLastError();
 }
 
