@@ -12,11 +12,14 @@ bracketed by torch.cuda.synchronize(); rank 0 prints one JSON line.
 
 Besides tokens/s the line carries:
   * per-kernel average durations, from HIP events recorded around each launch
-    on the library's stream (a second timed loop of K steps through
-    mra_attention_fwd_profiled);
-  * `roofline` for the kernel with the largest average duration: algorithmic
-    flops (block attention: 4*32*32*d per selected block) or algorithmic
-    bytes (the other kernels) per launch over its average duration;
+    on the library's stream (a second loop of K calls through
+    mra_attention_fwd_profiled, each call with its own events, one
+    synchronisation at the end);
+  * `roofline` for the kernel with the largest average duration: its
+    algorithmic bytes per launch (every input it needs read once, every
+    output written once) over its average duration, against HBM; for the
+    block attention, whose arithmetic intensity (4*32*32*d flop per selected
+    block) is far below the MFMA ridge, the MFMA rate is given beside it;
   * `traffic`: HBM bytes per launch of that kernel from rocprofv3 FETCH_SIZE /
     WRITE_SIZE counters committed under profiles/, scaled by the same
     counters' reading on a plain copy of known size; null when the kernel
@@ -66,8 +69,8 @@ def algorithmic(w, stage: str, sel_blocks: int) -> tuple[float, str]:
     ntens = 3 if full else 2
     K = nb * w.block_per_row if nb * w.block_per_row < nb * nb else nb * nb
     mask_b = 0 if w.mask is None else B * N
-    if stage == "attn":
-        return 4.0 * 32 * 32 * d * sel_blocks, "flop"
+    if stage == "attn":        # Q, K, V read once and O written once (its arithmetic intensity is far
+        return 4 * BH * N * d * es, "byte"   # below the MFMA ridge, so HBM is its roofline)
     if stage == "pool":        # Q, K (V) in; pooled fp32 rows and block counts out
         return ntens * BH * N * d * es + mask_b + ntens * BH * nb * d * 4 + 2 * B * nb * 4, "byte"
     if stage == "logits":      # pooled Q, K (V) in; logits, row maxima (low-res row sums) out
@@ -184,20 +187,20 @@ def main():
     ms = wall * 1e3 / args.steps
 
     # per-kernel durations: events around each launch, on the library's stream
+    # (each call gets its own events, so the stream is never drained between calls)
     stages = list(mra.STAGES)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(10)]
-    for e in ev:
-        e.record()
-    sums = {s: 0.0 for s in stages}
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(stages))] for _ in range(args.steps)]
+    for ev in evs:
+        for e in ev:
+            e.record()
     torch.cuda.synchronize()
     tp0 = time.perf_counter()
-    for _ in range(args.steps):
+    for ev in evs:
         mra.attention_profiled(q, k, v, ev, mask, **kw)
-        torch.cuda.synchronize()
-        for si, s in enumerate(stages):
-            sums[s] += ev[2 * si].elapsed_time(ev[2 * si + 1])
+    torch.cuda.synchronize()
     prof_wall = (time.perf_counter() - tp0) * 1e3 / args.steps
-    avg_ms = {s: sums[s] / args.steps for s in stages}
+    avg_ms = {s: sum(ev[2 * si].elapsed_time(ev[2 * si + 1]) for ev in evs) / args.steps
+              for si, s in enumerate(stages)}
 
     sel_blocks = selected_valid_blocks(w)
     kernels = {}
@@ -207,26 +210,25 @@ def main():
             kernels[s] = {"avg_us": round(t * 1e3, 2)}
             continue
         rate = amount / (t * 1e-3)
-        if unit == "flop":
-            kernels[s] = {"avg_us": round(t * 1e3, 2), "tflops": round(rate / 1e12, 2),
-                          "mfma_frac": round(rate / 1e12 / PEAK_BF16_TFLOPS, 4)}
-        else:
-            kernels[s] = {"avg_us": round(t * 1e3, 2), "gbs": round(rate / 1e9, 1),
-                          "hbm_frac": round(rate / 1e9 / PEAK_HBM_GBS, 4)}
+        kernels[s] = {"avg_us": round(t * 1e3, 2), "gbs": round(rate / 1e9, 1),
+                      "hbm_frac": round(rate / 1e9 / PEAK_HBM_GBS, 4)}
+    attn_flops = 4.0 * 32 * 32 * w.d * sel_blocks
+    mfma_peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    attn_tflops = attn_flops / (avg_ms["attn"] * 1e-3) / 1e12
+    kernels["attn"]["tflops"] = round(attn_tflops, 2)
+    kernels["attn"]["mfma_frac"] = round(attn_tflops / mfma_peak, 4)
     dom = max((s for s in avg_ms if algorithmic(w, s, sel_blocks)[0] is not None), key=avg_ms.get)
     amount, unit = algorithmic(w, dom, sel_blocks)
     dom_s = avg_ms[dom] * 1e-3
-    if unit == "flop":
-        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
-        roof = {"kernel": dom, "bound": "mfma", "achieved": round(amount / dom_s / 1e12, 3), "peak": peak,
-                "unit": "TFLOP/s"}
-    else:
-        roof = {"kernel": dom, "bound": "hbm", "achieved": round(amount / dom_s / 1e9, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s"}
+    roof = {"kernel": dom, "bound": "hbm", "achieved": round(amount / dom_s / 1e9, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = load_traffic(dom, w.name)
+    roof["algorithmic_bytes"] = int(amount)
+    if dom == "attn":
+        roof["mfma_tflops"] = kernels["attn"]["tflops"]
+        roof["mfma_frac"] = kernels["attn"]["mfma_frac"]
 
-    attn_flops = 4.0 * 32 * 32 * w.d * sel_blocks
     tokens = w.B * w.N
     rec = {
         "metric": METRIC,
