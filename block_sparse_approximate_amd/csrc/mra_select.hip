@@ -57,18 +57,25 @@ __host__ __device__ inline size_t align16(size_t x) { return (x + 15) & ~size_t(
 
 // ---------------------------------------------------------------- LDS plans
 struct LogitsLds {
-    size_t qT, kT, srow, cntv, hist, small, total;
+    size_t qT, kT, wl, hist, red, total;
 };
+
+constexpr int kMaxColTiles = 4;   // column tiles of kCT key blocks (N <= 16384)
+constexpr int kVtStride = 68;     // floats per staged vhat row (64 + 4 pad)
+
+// Rows of the low-res weight tile: nb + 4 floats (the pad spreads the rows
+// over the LDS banks for the MFMA operand reads).
+__host__ __device__ inline int wl_stride(int nb) { return nb + 4; }
 
 __host__ __device__ inline LogitsLds logits_lds(int nb) {
     LogitsLds L;
     size_t o = 0;
     L.qT = o; o = align16(o + 64 * kRT * 4);
-    L.kT = o; o = align16(o + 64 * kCT * 4);
-    L.srow = o; o = align16(o + (size_t)kRT * nb * 4);
-    L.cntv = o; o = align16(o + (size_t)nb * 4);
+    const size_t kt = 64 * kCT * 4, vt = (size_t)kCT * kVtStride * 4;   // khat tile, later the vhat tile
+    L.kT = o; o = align16(o + (kt > vt ? kt : vt));
+    L.wl = o; o = align16(o + (size_t)kRT * wl_stride(nb) * 4);
     L.hist = o; o = align16(o + kHistBins * 4);
-    L.small = o; o = align16(o + 64 * 4);
+    L.red = o; o = align16(o + 4 * 64 * 4 * 4);
     L.total = o;
     return L;
 }
@@ -207,10 +214,15 @@ __device__ void pick_digit_wave(const uint32_t* h, uint32_t need, uint32_t* smal
 // register e holds cell base + threadIdx.x + e * kSelThreads.
 __device__ __forceinline__ void fetch_keys(const uint32_t* __restrict__ G, uint32_t base, uint32_t ncell,
                                            uint32_t (&kv)[kCells]) {
+    if (base + kTileCells <= ncell) {   // a full tile: no per-cell guard
 #pragma unroll
-    for (int e = 0; e < kCells; e++) {
-        const uint32_t x = base + threadIdx.x + e * kSelThreads;
-        kv[e] = x < ncell ? G[x] : 0u;
+        for (int e = 0; e < kCells; e++) kv[e] = G[base + threadIdx.x + e * kSelThreads];
+    } else {
+#pragma unroll
+        for (int e = 0; e < kCells; e++) {
+            const uint32_t x = base + threadIdx.x + e * kSelThreads;
+            kv[e] = x < ncell ? G[x] : 0u;
+        }
     }
 }
 
@@ -316,7 +328,68 @@ __device__ __forceinline__ void fetch_vhat(const float* __restrict__ vh, int j0,
     }
 }
 
+// The khat tile of key blocks j0 .. j0 + kCT - 1 into registers: float4 x is
+// block j0 + x % kCT, channels 4 * (x / kCT) .. +3.
+__device__ __forceinline__ void fetch_khat(const float* __restrict__ kh, int j0, int nb,
+                                           float4 (&kv)[kCT * (kHeadDim / 4) / kLgThreads]) {
+#pragma unroll
+    for (int e = 0; e < kCT * (kHeadDim / 4) / kLgThreads; e++) {
+        const int x = threadIdx.x + e * kLgThreads, jj = x % kCT, c4 = (x / kCT) * 4;
+        kv[e] = j0 + jj < nb ? *reinterpret_cast<const float4*>(kh + (size_t)(j0 + jj) * kHeadDim + c4)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+// The marking pass for the common shape: one tile (kv holds every cell), a
+// multiple of 64 cells per block row, every cell of the tile present, and a
+// prefix of at most 32 bits.  Straight-line per 64-cell group: one shift,
+// two compares (their lane masks are the ballots), one bitmap store, and an
+// LDS atomic only for groups that hold candidates.
+__device__ __forceinline__ void mark_cells_fast(int nb, int words, uint32_t magic, uint32_t p32, int pbits,
+                                                const uint32_t (&kv)[kCells], uint32_t* bitmap, uint64_t* cand,
+                                                uint32_t* small) {
+    const int lane = threadIdx.x & 63;
+    const uint64_t lt_mask = (1ull << lane) - 1ull;
+    const uint32_t wbase = (uint32_t)__builtin_amdgcn_readfirstlane((int)threadIdx.x - lane);
+    const uint32_t sh = (uint32_t)(32 - pbits);
+#pragma unroll
+    for (int e = 0; e < kCells; e++) {
+        const uint32_t x0 = wbase + (uint32_t)e * kSelThreads;   // the wave's first cell (uniform)
+        const uint32_t top = kv[e] >> sh;
+        const uint64_t ms = __ballot(top > p32);
+        const uint64_t mh = __ballot(top == p32);
+        const uint32_t i0 = row_of(x0, (uint32_t)nb, magic), j0 = x0 - i0 * (uint32_t)nb;
+        if (lane == 0)
+            *reinterpret_cast<uint2*>(bitmap + i0 * words + (j0 >> 5)) = make_uint2((uint32_t)ms, (uint32_t)(ms >> 32));
+        if (mh) {
+            uint32_t at0 = 0;
+            if (lane == 0) at0 = atomicAdd(&small[8], (uint32_t)__popcll(mh));
+            at0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)at0);
+            if ((mh >> lane) & 1ull) {
+                const uint32_t at = at0 + (uint32_t)__popcll(mh & lt_mask);
+                if (at < (uint32_t)kCap) cand[at] = cell_key64(kv[e], x0 + lane);
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------- logits
+// Wave w owns block rows ra = row0 + 2w and rb = ra + 1 of the workgroup's 16;
+// lane l owns key blocks 128 t + 2l and 128 t + 2l + 1 of every column tile
+// t, so the row max, the scores, the keys and the low-res weights of a cell
+// never leave the registers of the lane that computed its logit.
 // kGiven: the logits are already in p.logits (selector hook); skip their
 // computation and only form row maxima, keys and the histogram.
 template <bool kGiven>
@@ -333,43 +406,50 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(Params p) {
     const int b = bh / p.H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float tau = (float)(1.0 / __builtin_sqrt((double)p.d));
+    const int ntile = (nb + kCT - 1) / kCT;
+    const int nbp = wl_stride(nb);
 
     const LogitsLds L = logits_lds(nb);
     float* qT = reinterpret_cast<float*>(smem + L.qT);
     float* kT = reinterpret_cast<float*>(smem + L.kT);
-    float* srow = reinterpret_cast<float*>(smem + L.srow);
-    int* cntv = reinterpret_cast<int*>(smem + L.cntv);
+    float* wl = reinterpret_cast<float*>(smem + L.wl);
     uint32_t* hist = reinterpret_cast<uint32_t*>(smem + L.hist);
-    float* rmax = reinterpret_cast<float*>(smem + L.small);
+    float* red = reinterpret_cast<float*>(smem + L.red);
     const float* qh = p.qhat + (size_t)bh * nb * kHeadDim;
     const float* kh = p.khat + (size_t)bh * nb * kHeadDim;
+    const bool lowres = !kGiven && p.mode == 0;
+    const float* vh = lowres ? p.vhat + (size_t)bh * nb * kHeadDim : nullptr;
+    const int* cnt = p.cnt + (size_t)b * nb;
+    const int ra = row0 + 2 * wave, rb = ra + 1;
 
     // every global load of the prologue first, then the LDS stores
     constexpr int kKLoads = kCT * (kHeadDim / 4) / kLgThreads;   // float4s of one khat tile per thread
-    int cn = tid < nb ? p.cnt[b * nb + tid] : 0;                 // nb <= 512 = kLgThreads
-    const bool lowres = !kGiven && p.mode == 0;
-    const float* vh = lowres ? p.vhat + (size_t)bh * nb * kHeadDim : nullptr;
     float4 qv = make_float4(0.f, 0.f, 0.f, 0.f);
     float4 kv[kKLoads], vv[kKLoads];
+    float sc[kMaxColTiles][4];   // logits of (ra, j), (ra, j + 1), (rb, j), (rb, j + 1), j = 128 t + 2 lane
+    int2 cj[kMaxColTiles];       // counts of key blocks j and j + 1
     if (lowres) fetch_vhat(vh, 0, nb, vv);
     if (!kGiven) {
         if (tid < kRT * kHeadDim / 4) {
             const int r = tid / (kHeadDim / 4), c4 = (tid % (kHeadDim / 4)) * 4;
             if (row0 + r < nb) qv = *reinterpret_cast<const float4*>(qh + (size_t)(row0 + r) * kHeadDim + c4);
         }
+        fetch_khat(kh, 0, nb, kv);
+    }
 #pragma unroll
-        for (int e = 0; e < kKLoads; e++) {
-            const int x = tid + e * kLgThreads, jj = x % kCT, c4 = (x / kCT) * 4;
-            kv[e] = jj < nb ? *reinterpret_cast<const float4*>(kh + (size_t)jj * kHeadDim + c4)
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-    } else {
-        for (int x = tid; x < kRT * nb; x += kLgThreads) {
-            const int r = x / nb, j = x - r * nb;
-            srow[x] = (row0 + r < nb) ? p.logits[((size_t)bh * nb + row0 + r) * nb + j] : 0.0f;
+    for (int t = 0; t < kMaxColTiles; t++) {
+        const int j = t * kCT + 2 * lane;
+        cj[t].x = (t < ntile && j < nb) ? cnt[j] : 0;
+        cj[t].y = (t < ntile && j + 1 < nb) ? cnt[j + 1] : 0;
+        if (kGiven) {
+            const float* S = p.logits + (size_t)bh * nb * nb;
+            sc[t][0] = (t < ntile && ra < nb && j < nb) ? S[(size_t)ra * nb + j] : 0.f;
+            sc[t][1] = (t < ntile && ra < nb && j + 1 < nb) ? S[(size_t)ra * nb + j + 1] : 0.f;
+            sc[t][2] = (t < ntile && rb < nb && j < nb) ? S[(size_t)rb * nb + j] : 0.f;
+            sc[t][3] = (t < ntile && rb < nb && j + 1 < nb) ? S[(size_t)rb * nb + j + 1] : 0.f;
         }
     }
-    if (tid < nb) cntv[tid] = cn;
+    const int cia = ra < nb ? cnt[ra] : 0, cib = rb < nb ? cnt[rb] : 0;
     for (int x = tid; x < kHistBins; x += kLgThreads) hist[x] = 0u;
     if (!kGiven && tid < kRT * kHeadDim / 4) {
         const int r = tid / (kHeadDim / 4), c4 = (tid % (kHeadDim / 4)) * 4;
@@ -378,117 +458,152 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(Params p) {
         qT[(c4 + 2) * kRT + r] = qv.z;
         qT[(c4 + 3) * kRT + r] = qv.w;
     }
-    const int r0 = 2 * wave;          // this wave's two block rows
-    for (int j0 = 0; j0 < (kGiven ? 0 : nb); j0 += kCT) {
-        __syncthreads();
-        // kT[c][jj] = khat[j0 + jj][c]
+    __syncthreads();
+
+    // logits, one column tile at a time: kT[c][jj] = khat[128 t + jj][c]
+    if (!kGiven) {
 #pragma unroll
-        for (int e = 0; e < kKLoads; e++) {
-            const int x = tid + e * kLgThreads, jj = x % kCT, c4 = (x / kCT) * 4;
-            kT[(c4 + 0) * kCT + jj] = kv[e].x;
-            kT[(c4 + 1) * kCT + jj] = kv[e].y;
-            kT[(c4 + 2) * kCT + jj] = kv[e].z;
-            kT[(c4 + 3) * kCT + jj] = kv[e].w;
-        }
-        __syncthreads();
-        if (j0 + kCT < nb) {   // the next khat tile is in flight during this one
+        for (int t = 0; t < kMaxColTiles; t++) {
+            if (t < ntile) {
+                if (t > 0) __syncthreads();
 #pragma unroll
-            for (int e = 0; e < kKLoads; e++) {
-                const int x = tid + e * kLgThreads, jj = x % kCT, c4 = (x / kCT) * 4;
-                kv[e] = j0 + kCT + jj < nb
-                            ? *reinterpret_cast<const float4*>(kh + (size_t)(j0 + kCT + jj) * kHeadDim + c4)
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
+                for (int e = 0; e < kKLoads; e++) {
+                    const int x = tid + e * kLgThreads, jj = x % kCT, c4 = (x / kCT) * 4;
+                    kT[(c4 + 0) * kCT + jj] = kv[e].x;
+                    kT[(c4 + 1) * kCT + jj] = kv[e].y;
+                    kT[(c4 + 2) * kCT + jj] = kv[e].z;
+                    kT[(c4 + 3) * kCT + jj] = kv[e].w;
+                }
+                __syncthreads();
+                if (t + 1 < ntile) fetch_khat(kh, (t + 1) * kCT, nb, kv);   // in flight during this tile
+                float a00 = 0.f, a01 = 0.f, a10 = 0.f, a11 = 0.f;
+#pragma unroll 8
+                for (int c = 0; c < kHeadDim; c++) {
+                    const float2 q2 = *reinterpret_cast<const float2*>(qT + c * kRT + 2 * wave);
+                    const float2 k2 = *reinterpret_cast<const float2*>(kT + c * kCT + 2 * lane);
+                    a00 = __builtin_fmaf(q2.x, k2.x, a00);
+                    a01 = __builtin_fmaf(q2.x, k2.y, a01);
+                    a10 = __builtin_fmaf(q2.y, k2.x, a10);
+                    a11 = __builtin_fmaf(q2.y, k2.y, a11);
+                }
+                sc[t][0] = a00 * tau;
+                sc[t][1] = a01 * tau;
+                sc[t][2] = a10 * tau;
+                sc[t][3] = a11 * tau;
             }
         }
-        float a00 = 0.f, a01 = 0.f, a10 = 0.f, a11 = 0.f;
-#pragma unroll 8
-        for (int c = 0; c < kHeadDim; c++) {
-            const float2 q2 = *reinterpret_cast<const float2*>(qT + c * kRT + r0);
-            const float2 k2 = *reinterpret_cast<const float2*>(kT + c * kCT + 2 * lane);
-            a00 = __builtin_fmaf(q2.x, k2.x, a00);
-            a01 = __builtin_fmaf(q2.x, k2.y, a01);
-            a10 = __builtin_fmaf(q2.y, k2.x, a10);
-            a11 = __builtin_fmaf(q2.y, k2.y, a11);
-        }
-        const int j = j0 + 2 * lane;
-        if (j < nb) {
-            srow[(size_t)r0 * nb + j] = a00 * tau;
-            srow[(size_t)(r0 + 1) * nb + j] = a10 * tau;
-        }
-        if (j + 1 < nb) {
-            srow[(size_t)r0 * nb + j + 1] = a01 * tau;
-            srow[(size_t)(r0 + 1) * nb + j + 1] = a11 * tau;
-        }
     }
-    __syncthreads();
+
     // row maxima over non-empty key blocks (exact: max does not round)
-    for (int rr = 0; rr < 2; rr++) {
-        const int r = r0 + rr;
-        float m = -__builtin_inff();
-        for (int j = lane; j < nb; j += 64)
-            if (cntv[j] > 0) m = fmaxf(m, srow[(size_t)r * nb + j]);
+    float ma = -__builtin_inff(), mb = -__builtin_inff();
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-        if (lane == 0) rmax[r] = m;
+    for (int t = 0; t < kMaxColTiles; t++) {
+        if (cj[t].x > 0) {
+            ma = fmaxf(ma, sc[t][0]);
+            mb = fmaxf(mb, sc[t][2]);
+        }
+        if (cj[t].y > 0) {
+            ma = fmaxf(ma, sc[t][1]);
+            mb = fmaxf(mb, sc[t][3]);
+        }
     }
-    __syncthreads();
-    // scores -> keys and the histogram of their top 12 bits; logits and maxima out
+    ma = wave_max(ma);
+    mb = wave_max(mb);
+
+    // scores -> keys and the histogram of their top 12 bits; logits, keys and
+    // maxima out
     float* Sg = p.logits + (size_t)bh * nb * nb;
     uint32_t* Kg = p.keys + (size_t)bh * nb * nb;
-    for (int x = tid; x < kRT * nb; x += kLgThreads) {
-        const int r = x / nb, j = x - r * nb, i = row0 + r;
-        if (i >= nb) continue;
-        const float sv = srow[x];
-        if (!kGiven) Sg[(size_t)i * nb + j] = sv;
-        const float s = cell_score(sv, rmax[r], i, j, cntv[i] > 0, cntv[j] > 0, p.prior_first, p.prior_diag);
-        const uint32_t key = float_key(s);
-        Kg[(size_t)i * nb + j] = key;
-        atomicAdd(&hist[key >> (32 - kHistBits)], 1u);
+    const int pf = p.prior_first, pd = p.prior_diag;
+#pragma unroll
+    for (int t = 0; t < kMaxColTiles; t++) {
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int i = q < 2 ? ra : rb, j = t * kCT + 2 * lane + (q & 1);
+            if (t < ntile && i < nb && j < nb) {
+                const float sv = sc[t][q];
+                if (!kGiven) Sg[(size_t)i * nb + j] = sv;
+                const int cjq = (q & 1) ? cj[t].y : cj[t].x;
+                const float s = cell_score(sv, q < 2 ? ma : mb, i, j, (q < 2 ? cia : cib) > 0, cjq > 0, pf, pd);
+                const uint32_t key = float_key(s);
+                Kg[(size_t)i * nb + j] = key;
+                atomicAdd(&hist[key >> (32 - kHistBits)], 1u);
+            }
+        }
     }
-    for (int r = tid; r < kRT; r += kLgThreads)
-        if (row0 + r < nb) p.rowmax[(size_t)bh * nb + row0 + r] = rmax[r];
+    if (lane == 0) {
+        if (ra < nb) p.rowmax[(size_t)bh * nb + ra] = ma;
+        if (rb < nb) p.rowmax[(size_t)bh * nb + rb] = mb;
+    }
+
+    // Full mode: the low-res weights of these rows into LDS, and their sums.
+    // The block attention later takes the selected cells back out of
+    //   lo_all_i = sum_j w_ij vhat_j,  ll_all_i = sum_j w_ij  (every key block).
+    if (lowres) {
+        float la = 0.f, lb = 0.f;
+#pragma unroll
+        for (int t = 0; t < kMaxColTiles; t++) {
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const int i = q < 2 ? ra : rb, j = t * kCT + 2 * lane + (q & 1);
+                if (t < ntile && j < nb) {
+                    const int cjq = (q & 1) ? cj[t].y : cj[t].x;
+                    const float w = i < nb ? lowres_weight(sc[t][q], q < 2 ? ma : mb, cjq) : 0.f;
+                    wl[(2 * wave + (q >> 1)) * nbp + j] = w;
+                    if (q < 2) la += w;
+                    else lb += w;
+                }
+            }
+        }
+        la = wave_sum(la);
+        lb = wave_sum(lb);
+        if (lane == 0) {
+            if (ra < nb) p.ll_all[(size_t)bh * nb + ra] = la;
+            if (rb < nb) p.ll_all[(size_t)bh * nb + rb] = lb;
+        }
+    }
     __syncthreads();
     uint32_t* gh = p.hist + (size_t)bh * kHistBins;
     for (int x = tid; x < kHistBins; x += kLgThreads)
         if (hist[x]) atomicAdd(&gh[x], hist[x]);
     if (!lowres) return;
 
-    // Full mode: the low-res sums of these rows over every key block,
-    //   lo_all_i = sum_j w_ij vhat_j,  ll_all_i = sum_j w_ij,
-    // from which the block attention takes away the selected blocks' terms.
-    // The weights replace the logits in LDS; vhat is staged in tiles of kCT
-    // key blocks with the next tile in flight.
-    for (int x = tid; x < kRT * nb; x += kLgThreads) {
-        const int r = x / nb, j = x - r * nb;
-        srow[x] = row0 + r < nb ? lowres_weight(srow[x], rmax[r], cntv[j]) : 0.f;
-    }
-    const int rr = tid >> 5, c2 = (tid & 31) * 2;   // row and channel pair of this thread
-    float* vt = kT;                                  // [kCT][kHeadDim] vhat tile
-    float acc0 = 0.f, acc1 = 0.f, lsum = 0.f;
+    // lo_all = W vhat on v_mfma_f32_16x16x4f32: wave w takes channels
+    // 16 (w % 4) .. +15 and one half of each key tile; A lane l holds
+    // W[l % 16][k = l / 16], B lane l holds vhat[k = l / 16][l % 16], and
+    // accumulator e of lane l is row 4 (l / 16) + e, channel l % 16.
+    const int ct = wave & 3, kh2 = wave >> 2;
+    float* vt = kT;   // [kCT][kVtStride] vhat tile
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int j0 = 0; j0 < nb; j0 += kCT) {
-        __syncthreads();
+        if (j0 > 0) __syncthreads();   // every wave is done with the previous tile
 #pragma unroll
         for (int e = 0; e < kKLoads; e++) {
             const int x = tid + e * kLgThreads;
-            *reinterpret_cast<float4*>(vt + (x >> 4) * kHeadDim + (x & 15) * 4) = vv[e];
+            *reinterpret_cast<float4*>(vt + (x >> 4) * kVtStride + (x & 15) * 4) = vv[e];
         }
         __syncthreads();
         if (j0 + kCT < nb) fetch_vhat(vh, j0 + kCT, nb, vv);
         const int jn = min(kCT, nb - j0);
-        const float* wr = srow + (size_t)rr * nb + j0;
-#pragma unroll 8
-        for (int jj = 0; jj < jn; jj++) {
-            const float w = wr[jj];
-            const float2 v = *reinterpret_cast<const float2*>(vt + jj * kHeadDim + c2);
-            acc0 = __builtin_fmaf(w, v.x, acc0);
-            acc1 = __builtin_fmaf(w, v.y, acc1);
-            lsum += w;
+#pragma unroll
+        for (int k4 = 0; k4 < kCT / 2; k4 += 4) {
+            const int k = kh2 * (kCT / 2) + k4 + (lane >> 4);
+            const bool ok = k < jn;
+            const float a = ok ? wl[(lane & 15) * nbp + j0 + k] : 0.f;
+            const float bv = ok ? vt[k * kVtStride + ct * 16 + (lane & 15)] : 0.f;
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, acc, 0, 0, 0);
         }
     }
-    if (row0 + rr < nb) {
-        const size_t row = (size_t)bh * nb + row0 + rr;
-        *reinterpret_cast<float2*>(p.lo_all + row * kHeadDim + c2) = make_float2(acc0, acc1);
-        if (c2 == 0) p.ll_all[row] = lsum;
+    if (kh2 == 1) *reinterpret_cast<f32x4*>(red + (ct * 64 + lane) * 4) = acc;
+    __syncthreads();
+    if (kh2 == 0) {
+        const f32x4 o = *reinterpret_cast<const f32x4*>(red + (ct * 64 + lane) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const int row = row0 + 4 * (lane >> 4) + e;
+            if (row < nb) p.lo_all[((size_t)bh * nb + row) * kHeadDim + ct * 16 + (lane & 15)] = acc[e] + o[e];
+        }
     }
 }
 
@@ -530,7 +645,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
         fetch_keys(G, 0, ncell, kv);
         const float* Sg = p.logits + (size_t)bh * ncell;
         float sv[kCells];
-        if (staged) {
+        if (staged && ncell == (uint32_t)kTileCells) {
+#pragma unroll
+            for (int e = 0; e < kCells; e++) sv[e] = Sg[tid + e * kSelThreads];
+        } else if (staged) {
 #pragma unroll
             for (int e = 0; e < kCells; e++) {
                 const uint32_t x = tid + e * kSelThreads;
@@ -597,7 +715,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
     // (bitmap), cells inside it are appended to the LDS candidate list.
     if (!tile0) fetch_keys(G, 0, ncell, kv);
     const bool rows64 = (nb & 63) == 0;
-    if (pbits <= 32) {
+    if (pbits <= 32 && rows64 && ncell == (uint32_t)kTileCells) {
+        mark_cells_fast(nb, words, magic, (uint32_t)prefix, pbits, kv, bitmap, cand, small);
+    } else if (pbits <= 32) {
         if (rows64) mark_cells<true, true>(G, ncell, ntiles, nb, words, magic, prefix, pbits, kv, bitmap, cand, small);
         else mark_cells<false, true>(G, ncell, ntiles, nb, words, magic, prefix, pbits, kv, bitmap, cand, small);
     } else {
