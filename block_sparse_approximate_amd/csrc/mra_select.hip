@@ -57,7 +57,7 @@ __host__ __device__ inline size_t align16(size_t x) { return (x + 15) & ~size_t(
 
 // ---------------------------------------------------------------- LDS plans
 struct LogitsLds {
-    size_t qT, kT, wl, hist, red, total;
+    size_t qT, kT, hist, total;
 };
 
 constexpr int kMaxColTiles = 4;   // column tiles of kCT key blocks (N <= 16384)
@@ -71,11 +71,9 @@ __host__ __device__ inline LogitsLds logits_lds(int nb) {
     LogitsLds L;
     size_t o = 0;
     L.qT = o; o = align16(o + 64 * kRT * 4);
-    const size_t kt = 64 * kCT * 4, vt = (size_t)kCT * kVtStride * 4;   // khat tile, later the vhat tile
+    const size_t kt = 64 * kCT * 4, vt = 0;   // khat tile
     L.kT = o; o = align16(o + (kt > vt ? kt : vt));
-    L.wl = o; o = align16(o + (size_t)kRT * wl_stride(nb) * 4);
     L.hist = o; o = align16(o + kHistBins * 4);
-    L.red = o; o = align16(o + 4 * 64 * 4 * 4);
     L.total = o;
     return L;
 }
@@ -113,7 +111,7 @@ __host__ __device__ inline SelectLds select_lds(int nb, int mode) {
 // Exclusive scan of one value per thread over the select workgroup.
 // Returns the exclusive prefix; *total gets the sum.  Uses scan[kSelWaves + 1].
 template <typename T>
-__device__ T block_excl_scan(T v, T* scan, T* total) {
+__device__ __forceinline__ T block_excl_scan(T v, T* scan, T* total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     T x = v;
 #pragma unroll
@@ -148,7 +146,7 @@ struct BinPick {
 // In a histogram of kHistBins bins held in LDS, find the bin where the count
 // taken from the top first reaches `need`.  Each thread owns 4 bins; the
 // whole workgroup calls this.
-__device__ BinPick pick_bin(const uint32_t* h, uint32_t need, uint32_t* scan, uint32_t* small) {
+__device__ __forceinline__ BinPick pick_bin(const uint32_t* h, uint32_t need, uint32_t* scan, uint32_t* small) {
     constexpr int kPer = kHistBins / kSelThreads;
     const int rt = kSelThreads - 1 - (int)threadIdx.x;   // reversed: the top bins come first
     uint32_t c[kPer], local = 0;
@@ -179,7 +177,7 @@ __device__ BinPick pick_bin(const uint32_t* h, uint32_t need, uint32_t* scan, ui
 
 // The same over kDigitBins bins, by wave 0 alone (4 bins per lane); the
 // result goes to small[0..2] for the whole workgroup to read after a barrier.
-__device__ void pick_digit_wave(const uint32_t* h, uint32_t need, uint32_t* small) {
+__device__ __forceinline__ void pick_digit_wave(const uint32_t* h, uint32_t need, uint32_t* small) {
     constexpr int kPer = kDigitBins / 64;
     const int lane = threadIdx.x;
     const int rt = 63 - lane;
@@ -407,28 +405,21 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(Params p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float tau = (float)(1.0 / __builtin_sqrt((double)p.d));
     const int ntile = (nb + kCT - 1) / kCT;
-    const int nbp = wl_stride(nb);
-
     const LogitsLds L = logits_lds(nb);
     float* qT = reinterpret_cast<float*>(smem + L.qT);
     float* kT = reinterpret_cast<float*>(smem + L.kT);
-    float* wl = reinterpret_cast<float*>(smem + L.wl);
     uint32_t* hist = reinterpret_cast<uint32_t*>(smem + L.hist);
-    float* red = reinterpret_cast<float*>(smem + L.red);
     const float* qh = p.qhat + (size_t)bh * nb * kHeadDim;
     const float* kh = p.khat + (size_t)bh * nb * kHeadDim;
-    const bool lowres = !kGiven && p.mode == 0;
-    const float* vh = lowres ? p.vhat + (size_t)bh * nb * kHeadDim : nullptr;
     const int* cnt = p.cnt + (size_t)b * nb;
     const int ra = row0 + 2 * wave, rb = ra + 1;
 
     // every global load of the prologue first, then the LDS stores
     constexpr int kKLoads = kCT * (kHeadDim / 4) / kLgThreads;   // float4s of one khat tile per thread
     float4 qv = make_float4(0.f, 0.f, 0.f, 0.f);
-    float4 kv[kKLoads], vv[kKLoads];
+    float4 kv[kKLoads];
     float sc[kMaxColTiles][4];   // logits of (ra, j), (ra, j + 1), (rb, j), (rb, j + 1), j = 128 t + 2 lane
     int2 cj[kMaxColTiles];       // counts of key blocks j and j + 1
-    if (lowres) fetch_vhat(vh, 0, nb, vv);
     if (!kGiven) {
         if (tid < kRT * kHeadDim / 4) {
             const int r = tid / (kHeadDim / 4), c4 = (tid % (kHeadDim / 4)) * 4;
@@ -536,72 +527,120 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(Params p) {
         if (rb < nb) p.rowmax[(size_t)bh * nb + rb] = mb;
     }
 
-    // Full mode: the low-res weights of these rows into LDS, and their sums.
-    // The block attention later takes the selected cells back out of
-    //   lo_all_i = sum_j w_ij vhat_j,  ll_all_i = sum_j w_ij  (every key block).
-    if (lowres) {
-        float la = 0.f, lb = 0.f;
-#pragma unroll
-        for (int t = 0; t < kMaxColTiles; t++) {
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                const int i = q < 2 ? ra : rb, j = t * kCT + 2 * lane + (q & 1);
-                if (t < ntile && j < nb) {
-                    const int cjq = (q & 1) ? cj[t].y : cj[t].x;
-                    const float w = i < nb ? lowres_weight(sc[t][q], q < 2 ? ma : mb, cjq) : 0.f;
-                    wl[(2 * wave + (q >> 1)) * nbp + j] = w;
-                    if (q < 2) la += w;
-                    else lb += w;
-                }
-            }
-        }
-        la = wave_sum(la);
-        lb = wave_sum(lb);
-        if (lane == 0) {
-            if (ra < nb) p.ll_all[(size_t)bh * nb + ra] = la;
-            if (rb < nb) p.ll_all[(size_t)bh * nb + rb] = lb;
-        }
-    }
     __syncthreads();
     uint32_t* gh = p.hist + (size_t)bh * kHistBins;
     for (int x = tid; x < kHistBins; x += kLgThreads)
         if (hist[x]) atomicAdd(&gh[x], hist[x]);
-    if (!lowres) return;
+}
 
-    // lo_all = W vhat on v_mfma_f32_16x16x4f32: wave w takes channels
-    // 16 (w % 4) .. +15 and one half of each key tile; A lane l holds
-    // W[l % 16][k = l / 16], B lane l holds vhat[k = l / 16][l % 16], and
-    // accumulator e of lane l is row 4 (l / 16) + e, channel l % 16.
-    const int ct = wave & 3, kh2 = wave >> 2;
-    float* vt = kT;   // [kCT][kVtStride] vhat tile
+// ---------------------------------------------------------------- low-res sums
+// Full mode, [MRA] "第四步": the low-resolution attention of 32 block rows of
+// head bh over every key block, selected or not,
+//   lo_all_i = sum_j w_ij vhat_j,  ll_all_i = sum_j w_ij,  w_ij = cnt_j exp(S_ij - m_i),
+// from which the block attention later takes the selected cells back out.
+// These workgroups ride in the selector's launch: they need only the logits
+// kernel's output, so they run on the CUs the per-head selectors leave idle.
+// The product runs on v_mfma_f32_16x16x4f32: wave w takes the 16-row tile
+// w / 8, the 16-channel tile (w / 2) % 4 and the key half w % 2 of each key
+// tile; A lane l holds W[l % 16][k = l / 16], B lane l holds
+// vhat[k = l / 16][l % 16], and accumulator e of lane l is row 4 (l / 16) + e,
+// channel l % 16.
+constexpr int kLoRows = 32;
+
+__host__ __device__ inline size_t lowres_lds(int nb) {
+    return align16((size_t)kLoRows * wl_stride(nb) * 4) + align16((size_t)kCT * kVtStride * 4) +
+           align16(2 * 8 * 64 * 4 * 4);
+}
+
+__device__ __forceinline__ void lowres_rows(const Params& p, int bh, int row0, unsigned char* smem) {
+    const int nb = p.nb, nbp = wl_stride(nb);
+    const int b = bh / p.H;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    float* wl = reinterpret_cast<float*>(smem);
+    float* vt = reinterpret_cast<float*>(smem + align16((size_t)kLoRows * nbp * 4));
+    float* red = vt + align16((size_t)kCT * kVtStride * 4) / 4;
+    const float* S = p.logits + (size_t)bh * nb * nb;
+    const float* vh = p.vhat + (size_t)bh * nb * kHeadDim;
+    const int* cnt = p.cnt + (size_t)b * nb;
+    constexpr int kVLoads = kCT * (kHeadDim / 4) / kSelThreads;   // float4s of one vhat tile per thread
+
+    // vhat tile 0 in flight first; the weights: wave w owns rows 2w, 2w + 1
+    float4 vv[kVLoads];
+#pragma unroll
+    for (int e = 0; e < kVLoads; e++) {
+        const int x = tid + e * kSelThreads, j = x >> 4;
+        vv[e] = j < nb ? *reinterpret_cast<const float4*>(vh + (size_t)j * kHeadDim + (x & 15) * 4)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    constexpr int kJ = kMaxColTiles * kCT / 64;   // key blocks per lane (nb <= 512)
+    const int ia = row0 + 2 * wave, ib = ia + 1;   // this wave's two rows
+    float sa[kJ], sb[kJ];
+    int cv[kJ];
+#pragma unroll
+    for (int t = 0; t < kJ; t++) {
+        const int j = lane + 64 * t;
+        cv[t] = j < nb ? cnt[j] : 0;
+        sa[t] = (ia < nb && j < nb) ? S[(size_t)ia * nb + j] : 0.f;
+        sb[t] = (ib < nb && j < nb) ? S[(size_t)ib * nb + j] : 0.f;
+    }
+    const float ma = ia < nb ? p.rowmax[(size_t)bh * nb + ia] : 0.f;
+    const float mb = ib < nb ? p.rowmax[(size_t)bh * nb + ib] : 0.f;
+    float la = 0.f, lb = 0.f;
+#pragma unroll
+    for (int t = 0; t < kJ; t++) {
+        const int j = lane + 64 * t;
+        if (j < nb) {
+            const float wa = ia < nb ? lowres_weight(sa[t], ma, cv[t]) : 0.f;
+            const float wb = ib < nb ? lowres_weight(sb[t], mb, cv[t]) : 0.f;
+            wl[(2 * wave) * nbp + j] = wa;
+            wl[(2 * wave + 1) * nbp + j] = wb;
+            la += wa;
+            lb += wb;
+        }
+    }
+    la = wave_sum(la);
+    lb = wave_sum(lb);
+    if (lane == 0) {
+        if (ia < nb) p.ll_all[(size_t)bh * nb + ia] = la;
+        if (ib < nb) p.ll_all[(size_t)bh * nb + ib] = lb;
+    }
+    const int rt = wave >> 3, ct = (wave >> 1) & 3, kh2 = wave & 1;
     typedef float f32x4 __attribute__((ext_vector_type(4)));
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int j0 = 0; j0 < nb; j0 += kCT) {
-        if (j0 > 0) __syncthreads();   // every wave is done with the previous tile
+        __syncthreads();   // the weights are in place; every wave is done with the previous tile
 #pragma unroll
-        for (int e = 0; e < kKLoads; e++) {
-            const int x = tid + e * kLgThreads;
+        for (int e = 0; e < kVLoads; e++) {
+            const int x = tid + e * kSelThreads;
             *reinterpret_cast<float4*>(vt + (x >> 4) * kVtStride + (x & 15) * 4) = vv[e];
         }
         __syncthreads();
-        if (j0 + kCT < nb) fetch_vhat(vh, j0 + kCT, nb, vv);
+        if (j0 + kCT < nb) {
+#pragma unroll
+            for (int e = 0; e < kVLoads; e++) {
+                const int x = tid + e * kSelThreads, j = j0 + kCT + (x >> 4);
+                vv[e] = j < nb ? *reinterpret_cast<const float4*>(vh + (size_t)j * kHeadDim + (x & 15) * 4)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
         const int jn = min(kCT, nb - j0);
 #pragma unroll
         for (int k4 = 0; k4 < kCT / 2; k4 += 4) {
             const int k = kh2 * (kCT / 2) + k4 + (lane >> 4);
             const bool ok = k < jn;
-            const float a = ok ? wl[(lane & 15) * nbp + j0 + k] : 0.f;
+            const float a = ok ? wl[(rt * 16 + (lane & 15)) * nbp + j0 + k] : 0.f;
             const float bv = ok ? vt[k * kVtStride + ct * 16 + (lane & 15)] : 0.f;
             acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, acc, 0, 0, 0);
         }
     }
-    if (kh2 == 1) *reinterpret_cast<f32x4*>(red + (ct * 64 + lane) * 4) = acc;
+    const int tile = rt * 4 + ct;   // 0..7
+    if (kh2 == 1) *reinterpret_cast<f32x4*>(red + (tile * 64 + lane) * 4) = acc;
     __syncthreads();
     if (kh2 == 0) {
-        const f32x4 o = *reinterpret_cast<const f32x4*>(red + (ct * 64 + lane) * 4);
+        const f32x4 o = *reinterpret_cast<const f32x4*>(red + (tile * 64 + lane) * 4);
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-            const int row = row0 + 4 * (lane >> 4) + e;
+            const int row = row0 + rt * 16 + 4 * (lane >> 4) + e;
             if (row < nb) p.lo_all[((size_t)bh * nb + row) * kHeadDim + ct * 16 + (lane & 15)] = acc[e] + o[e];
         }
     }
@@ -611,7 +650,20 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(Params p) {
 __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int nb = p.nb;
+    // workgroups [0, BH_pad) select, one per head (BH_pad = BH rounded up to
+    // a multiple of 8, so workgroup bh runs on XCD bh % 8); in full mode the
+    // rest sum the low-res attention of 32 rows each, placed on the XCD of
+    // their head
+    const int bh_pad = 8 * ((p.BH + 7) / 8);
+    if ((int)blockIdx.x >= bh_pad) {
+        const int g = blockIdx.x - bh_pad, xcd = g & 7, slot = g >> 3;
+        const int tiles = (nb + kLoRows - 1) / kLoRows;
+        const int hm = slot / tiles, lbh = xcd + 8 * hm;
+        if (lbh < p.BH) lowres_rows(p, lbh, (slot - hm * tiles) * kLoRows, smem);
+        return;
+    }
     const int bh = blockIdx.x;
+    if (bh >= p.BH) return;
     const int b = bh / p.H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const SelectLds L = select_lds(nb, p.mode);
@@ -869,7 +921,11 @@ hipError_t launch_select(const Params& p, hipStream_t s) {
     static const hipError_t a2 = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (a2 != hipSuccess) return a2;
-    hipLaunchKernelGGL(select_kernel, dim3(p.BH), dim3(kSelThreads), select_lds(p.nb, p.mode).total, s, p);
+    const int bh_pad = 8 * ((p.BH + 7) / 8);
+    const int lowres_wgs = p.mode == 0 ? bh_pad * ((p.nb + kLoRows - 1) / kLoRows) : 0;
+    size_t lds = select_lds(p.nb, p.mode).total;
+    if (p.mode == 0 && lowres_lds(p.nb) > lds) lds = lowres_lds(p.nb);
+    hipLaunchKernelGGL(select_kernel, dim3(bh_pad + lowres_wgs), dim3(kSelThreads), lds, s, p);
     return hipGetLastError();
 }
 
