@@ -55,6 +55,7 @@ bool carve(const mra_dims& d, int32_t bpr, int32_t mode, Layout* L) {
     L->ll_all = mode == MRA_APPROX_FULL ? take(BH * nb * 4) : 0;
     L->part_o = take(BH * (size_t)L->max_items * kBlock * dd * 4);
     L->part_ml = take(BH * (size_t)L->max_items * 2 * kBlock * 4);
+    L->part_corr = mode == MRA_APPROX_FULL ? take(BH * (size_t)L->max_items * kCorrStride * 4) : 0;
     L->total = o;
     return true;
 }
@@ -120,6 +121,7 @@ Params make_params(const mra_dims& d, const Layout& L, int32_t mode, int32_t pf,
     p.ll_all = L.ll_all ? reinterpret_cast<float*>(w + L.ll_all) : nullptr;
     p.part_o = reinterpret_cast<float*>(w + L.part_o);
     p.part_ml = reinterpret_cast<float*>(w + L.part_ml);
+    p.part_corr = L.part_corr ? reinterpret_cast<float*>(w + L.part_corr) : nullptr;
     p.error = reinterpret_cast<int32_t*>(w);
     return p;
 }

@@ -33,7 +33,8 @@
 // and writes (O 2^(m - M) + lo 2^(m_i - M)) / (l 2^(m - M) + ll 2^(m_i - M))
 // with M the larger of the high-res max m and the low-res row max m_i (both
 // in log2 units).  Other segments write un-normalised partials (O, running
-// max, sum) that the finish kernel joins.
+// max, sum, and in full mode the segment's sums of w vhat_j and of w) that
+// the finish kernel joins.
 //
 // Workgroups are placed XCD-aware: workgroup g runs on XCD g % 8, and all
 // waves of head bh are on XCD bh % 8, so a head's K/V re-reads stay in one L2.
@@ -239,6 +240,11 @@ __device__ __forceinline__ void finish_segment(const Params& p, const Wave<DT>& 
         if (h == 0) {
             p.part_ml[pidx * 64 + n] = A.mrun;
             p.part_ml[pidx * 64 + 32 + n] = ltot;
+        }
+        if constexpr (FULL) {   // the segment's share of the low-res correction
+            float* pc = p.part_corr + pidx * kCorrStride;
+            pc[W.lane] = A.corr;
+            if (W.lane == 0) pc[kHeadDim] = A.sw;
         }
     }
 }

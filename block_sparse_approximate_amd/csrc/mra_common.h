@@ -17,6 +17,7 @@ constexpr int kHistBits = 12;           // first radix digit of the selection ke
 constexpr int kHistBins = 1 << kHistBits;
 constexpr float kPriorBias = 5000.0f;   // [MRA] step 2: 5e3 bias for forced blocks
 constexpr int kChunk = 8;               // max selected key blocks per segment of a row
+constexpr int kCorrStride = 68;         // floats per segment's low-res correction: 64 channels, weight sum, pad
 constexpr float kLog2e = 1.4426950408889634f;
 
 // One selected block, in the head's CSR order (block row ascending, then key
@@ -49,7 +50,7 @@ struct Layout {
     int64_t K;            // selection budget per (batch, head)
     int32_t max_items;    // segments per head, upper bound
     size_t qhat, khat, vhat, cnt, mbits, logits, keys, rowmax, hist, thresh, row_ptr, col, selbits, item_ptr, recs,
-        merge_rows, n_merge, lo_all, ll_all, part_o, part_ml, total;
+        merge_rows, n_merge, lo_all, ll_all, part_o, part_ml, part_corr, total;
 };
 
 // Everything a kernel needs, passed by value.
@@ -86,6 +87,7 @@ struct Params {
     float* ll_all;         // [BH, nb]    full mode: sum over every key block j of w_ij
     float* part_o;         // [BH, max_items, 32, d] un-normalised high-res numerators
     float* part_ml;        // [BH, max_items, 2, 32] running max (log2 units) and sum
+    float* part_corr;      // [BH, max_items, kCorrStride] full mode: the segment's sum of w vhat_j, then of w
     int32_t* error;        // device error flag (0 = fine)
     int32_t attn_wph;      // attention stream: waves sharing one head's blocks
 };

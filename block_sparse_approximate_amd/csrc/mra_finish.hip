@@ -7,8 +7,8 @@
 //   * full mode: the row's low-resolution part without its selected blocks,
 //       lo = lo_all_i - sum_{j in sel(i)} w_ij vhat_j,
 //       ll = ll_all_i - sum_{j in sel(i)} w_ij,
-//     where lo_all, ll_all (every key block) come from the logits kernel and
-//     w_ij from the selection records;
+//     where lo_all, ll_all (every key block) come from the low-res sums and
+//     the two sums over sel(i) from the segments' partials;
 //   * the join, per query token t, with high-res maxima in log2 units and M
 //     the largest of the maxima involved:
 //       out_t = (sum_c O_c 2^(m_c - M) + lo 2^(m_i log2e - M))
@@ -27,42 +27,32 @@ constexpr int kBatch = 8;       // segments whose loads are in flight together
 constexpr int kRowSlots = 32;   // workgroups per head
 
 template <int DT>
-__device__ void merge_row(const Params& p, int bh, int i, float* lo, float (*red)[kHeadDim + 1], float* wsum) {
+__device__ void merge_row(const Params& p, int bh, int i, float* lo, float* ll_s) {
     const int nb = p.nb;
     const int b = bh / p.H;
     const int tid = threadIdx.x;
-    float mi2 = -__builtin_inff(), ll = 0.f;
-    if (p.mode == 0) {
-        const int* rp = p.row_ptr + (size_t)bh * (nb + 1);
-        const int o = rp[i], n = rp[i + 1] - o;
-        const BlkRec* R = p.recs + (size_t)bh * p.K + o;
-        const float* vh = p.vhat + (size_t)bh * nb * kHeadDim;
-        const int c = tid & 63, g = tid >> 6;
-        float acc = 0.f, sw = 0.f;
-        for (int e = g; e < n; e += 4) {
-            const BlkRec r = R[e];
-            const int j = min((int)(r.ij >> 16), nb - 1);
-            acc = __builtin_fmaf(r.w, vh[(size_t)j * kHeadDim + c], acc);
-            sw += r.w;
-        }
-        red[g][c] = acc;
-        if (c == 0) wsum[g] = sw;
-        __syncthreads();
-        const size_t row = (size_t)bh * nb + i;
-        if (tid < kHeadDim)
-            lo[tid] = p.lo_all[row * kHeadDim + tid] - ((red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]));
-        ll = fmaxf(p.ll_all[row] - ((wsum[0] + wsum[1]) + (wsum[2] + wsum[3])), 0.f);
-        mi2 = p.rowmax[row] * kLog2e;
-        __syncthreads();
-    }
-
     const int* ip = p.item_ptr + (size_t)bh * (nb + 1);
     const int first = max(ip[i], 0);
     const int nit = max(0, min(ip[i + 1] - first, p.max_items - first));
+    const size_t pbase = (size_t)bh * p.max_items + first;
+    float mi2 = -__builtin_inff(), ll = 0.f;
+    if (p.mode == 0) {
+        // the row's low-res part: lo_all minus the segments' corrections
+        const size_t row = (size_t)bh * nb + i;
+        if (tid < kHeadDim + 1) {
+            float c = 0.f;
+            for (int q = 0; q < nit; q++) c += p.part_corr[(pbase + q) * kCorrStride + tid];
+            if (tid < kHeadDim) lo[tid] = p.lo_all[row * kHeadDim + tid] - c;
+            else *ll_s = fmaxf(p.ll_all[row] - c, 0.f);
+        }
+        mi2 = p.rowmax[row] * kLog2e;
+        __syncthreads();
+        ll = *ll_s;
+    }
+
     const int t = tid >> 3;              // token within the block
     const int cg = (tid & 7) * 8;        // channels cg .. cg+7
     const bool valid = (p.mbits[(size_t)b * nb + i] >> t) & 1u;
-    const size_t pbase = (size_t)bh * p.max_items + first;
 
     float M2 = mi2;
     for (int c0 = 0; c0 < nit; c0 += kBatch) {
@@ -124,15 +114,14 @@ __device__ void merge_row(const Params& p, int bh, int i, float* lo, float (*red
 template <int DT>
 __global__ __launch_bounds__(kThreads) void finish_kernel(Params p) {
     __shared__ __align__(16) float lo[kHeadDim];
-    __shared__ float red[4][kHeadDim + 1];
-    __shared__ float wsum[4];
+    __shared__ float ll;
     const int nb = p.nb;
     const int bh = blockIdx.x / kRowSlots, slot = blockIdx.x - bh * kRowSlots;
     const int nm = min(p.n_merge[bh], nb);
     for (int s = slot; s < nm; s += kRowSlots) {
         const int i = min(max(p.merge_rows[(size_t)bh * nb + s], 0), nb - 1);
-        merge_row<DT>(p, bh, i, lo, red, wsum);
-        __syncthreads();   // lo, red and wsum are reused by the next row
+        merge_row<DT>(p, bh, i, lo, &ll);
+        __syncthreads();   // lo and ll are reused by the next row
     }
 }
 

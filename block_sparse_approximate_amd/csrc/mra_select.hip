@@ -687,16 +687,19 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
     const uint32_t* G = p.keys + (size_t)bh * ncell;
     const uint32_t magic = 0xFFFFFFFFu / (uint32_t)nb + 1u;
 
-    // prologue: all global loads, then the LDS stores
+    // prologue: every global load first; the histogram goes to LDS at once,
+    // the keys stay in registers, and the logits, row maxima and mask words
+    // (needed only for the records) go to LDS later, so that their latency
+    // hides behind the threshold search
     uint32_t kv[kCells];
-    {
-        constexpr int kPer = kHistBins / kSelThreads;
-        uint32_t hv[kPer];
+    float sv[kCells];
+    constexpr int kPer = kHistBins / kSelThreads;
+    uint32_t hv[kPer];
 #pragma unroll
-        for (int e = 0; e < kPer; e++) hv[e] = p.hist[(size_t)bh * kHistBins + tid + e * kSelThreads];
-        fetch_keys(G, 0, ncell, kv);
+    for (int e = 0; e < kPer; e++) hv[e] = p.hist[(size_t)bh * kHistBins + tid + e * kSelThreads];
+    fetch_keys(G, 0, ncell, kv);
+    {
         const float* Sg = p.logits + (size_t)bh * ncell;
-        float sv[kCells];
         if (staged && ncell == (uint32_t)kTileCells) {
 #pragma unroll
             for (int e = 0; e < kCells; e++) sv[e] = Sg[tid + e * kSelThreads];
@@ -707,25 +710,14 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
                 sv[e] = x < ncell ? Sg[x] : 0.f;
             }
         }
-        const uint32_t mv = tid < nb ? p.mbits[b * nb + tid] : 0u;   // nb <= 512 < kSelThreads
-        const float rv = (full && tid < nb) ? p.rowmax[(size_t)bh * nb + tid] : 0.f;
-        if (tid < nb) {
-            mbv[tid] = mv;
-            rmv[tid] = rv;
-        }
-        if (staged) {
-#pragma unroll
-            for (int e = 0; e < kCells; e++) {
-                const uint32_t x = tid + e * kSelThreads;
-                if (x < ncell) stile[x] = sv[e];
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < kPer; e++) hist[tid + e * kSelThreads] = hv[e];
-        for (int x = tid; x < nb * words; x += kSelThreads) bitmap[x] = 0u;
-        if (tid < 2 * kDigitBins) dig[tid] = 0u;
-        if (tid == 0) small[8] = 0u;
     }
+    const uint32_t mv = tid < nb ? p.mbits[b * nb + tid] : 0u;   // nb <= 512 < kSelThreads
+    const float rv = (full && tid < nb) ? p.rowmax[(size_t)bh * nb + tid] : 0.f;
+#pragma unroll
+    for (int e = 0; e < kPer; e++) hist[tid + e * kSelThreads] = hv[e];
+    for (int x = tid; x < nb * words; x += kSelThreads) bitmap[x] = 0u;
+    if (tid < 2 * kDigitBins) dig[tid] = 0u;
+    if (tid == 0) small[8] = 0u;
     __syncthreads();
 
     uint32_t need = (uint32_t)p.K;
@@ -829,6 +821,19 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
         }
     }
     __syncthreads();
+
+    // the records' inputs, loaded in the prologue (read after the scan's barriers)
+    if (tid < nb) {
+        mbv[tid] = mv;
+        rmv[tid] = rv;
+    }
+    if (staged) {
+#pragma unroll
+        for (int e = 0; e < kCells; e++) {
+            const uint32_t x = tid + e * kSelThreads;
+            if (x < ncell) stile[x] = sv[e];
+        }
+    }
 
     // CSR row pointers, segment (item) pointers and the rows the final kernel
     // combines, in one scan: one block row per thread (nb <= 512)
