@@ -49,7 +49,7 @@ bool carve(const mra_dims& d, int32_t bpr, int32_t mode, Layout* L) {
     L->selbits = take(BH * nb * words * 4);
     L->item_ptr = take(BH * (nb + 1) * 4);
     L->recs = take(BH * (size_t)L->K * sizeof(BlkRec));
-    L->merge_rows = take(BH * nb * 4);
+    L->merge_rows = take(BH * nb * 16);
     L->n_merge = take(BH * 4);
     L->lo_all = mode == MRA_APPROX_FULL ? take(BH * nb * dd * 4) : 0;
     L->ll_all = mode == MRA_APPROX_FULL ? take(BH * nb * 4) : 0;
@@ -115,7 +115,7 @@ Params make_params(const mra_dims& d, const Layout& L, int32_t mode, int32_t pf,
     p.selbits = reinterpret_cast<uint32_t*>(w + L.selbits);
     p.item_ptr = reinterpret_cast<int32_t*>(w + L.item_ptr);
     p.recs = reinterpret_cast<BlkRec*>(w + L.recs);
-    p.merge_rows = reinterpret_cast<int32_t*>(w + L.merge_rows);
+    p.merge_rows = reinterpret_cast<int4*>(w + L.merge_rows);
     p.n_merge = reinterpret_cast<int32_t*>(w + L.n_merge);
     p.lo_all = L.lo_all ? reinterpret_cast<float*>(w + L.lo_all) : nullptr;
     p.ll_all = L.ll_all ? reinterpret_cast<float*>(w + L.ll_all) : nullptr;

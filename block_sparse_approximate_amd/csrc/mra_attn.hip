@@ -65,10 +65,10 @@ __device__ __forceinline__ int rl(int x, int l) { return __builtin_amdgcn_readla
 // key index held by accumulator register r of a 32x32 MFMA tile in lane l
 __device__ __forceinline__ int acc_row(int r, int lane) { return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); }
 
-__device__ __forceinline__ int info_pos(uint32_t x) { return (int)((x >> 20) & 15u); }
-__device__ __forceinline__ int info_len(uint32_t x) { return (int)((x >> 24) & 15u); }
-__device__ __forceinline__ bool info_whole(uint32_t x) { return (x >> 28) & 1u; }
-__device__ __forceinline__ int info_item(uint32_t x) { return (int)(x & 0xFFFFFu); }
+__device__ __forceinline__ int info_pos(uint32_t x) { return (int)((x >> 18) & 63u); }
+__device__ __forceinline__ int info_len(uint32_t x) { return (int)((x >> 24) & 63u); }
+__device__ __forceinline__ bool info_whole(uint32_t x) { return (x >> 30) & 1u; }
+__device__ __forceinline__ int info_item(uint32_t x) { return (int)(x & 0x3FFFFu); }
 
 // The segment start nearest to stream block x (whose record info is given):
 // back to its segment's start when x is in the segment's first half, else

@@ -16,7 +16,7 @@ constexpr int kHeadDim = 64;            // head dims this build accepts
 constexpr int kHistBits = 12;           // first radix digit of the selection key
 constexpr int kHistBins = 1 << kHistBits;
 constexpr float kPriorBias = 5000.0f;   // [MRA] step 2: 5e3 bias for forced blocks
-constexpr int kChunk = 8;               // max selected key blocks per segment of a row
+constexpr int kChunk = 16;              // max selected key blocks per segment of a row
 constexpr int kCorrStride = 68;         // floats per segment's low-res correction: 64 channels, weight sum, pad
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -28,10 +28,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 //   kmask valid-token mask word of key block j
 //   w     full mode: the low-resolution weight cnt_j exp(S_ij - m_i) of the
 //         cell, which the low-res part must leave out; 0 in sparse mode
-//   info  bits  0..19  segment (item) index within the head
-//               20..23 position of the block within its segment
-//               24..27 segment length (1..kChunk)
-//               28     the segment is the whole row
+//   info  bits  0..17  segment (item) index within the head
+//               18..23 position of the block within its segment
+//               24..29 segment length (1..kChunk)
+//               30     the segment is the whole row
 struct BlkRec {
     uint32_t ij;
     uint32_t kmask;
@@ -41,7 +41,7 @@ struct BlkRec {
 
 __host__ __device__ constexpr uint32_t rec_ij(int i, int j) { return (uint32_t)i | ((uint32_t)j << 16); }
 __host__ __device__ constexpr uint32_t rec_info(int item, int pos, int len, bool whole) {
-    return (uint32_t)item | ((uint32_t)pos << 20) | ((uint32_t)len << 24) | (whole ? (1u << 28) : 0u);
+    return (uint32_t)item | ((uint32_t)pos << 18) | ((uint32_t)len << 24) | (whole ? (1u << 30) : 0u);
 }
 
 // Workspace carve, shared by the host dispatcher and the kernels.
@@ -81,7 +81,8 @@ struct Params {
     uint32_t* selbits;     // [BH, nb, words]
     int32_t* item_ptr;     // [BH, nb + 1]  first segment of each block row
     BlkRec* recs;          // [BH, K] selected blocks in CSR order
-    int32_t* merge_rows;   // [BH, nb] rows the final kernel must combine (0 or >1 segments)
+    int4* merge_rows;      // [BH, nb] rows the final kernel must combine (0 or >1 segments):
+                           //   (row, first segment, number of segments, 0)
     int32_t* n_merge;      // [BH]
     float* lo_all;         // [BH, nb, d] full mode: sum over every key block j of w_ij vhat_j
     float* ll_all;         // [BH, nb]    full mode: sum over every key block j of w_ij

@@ -3,7 +3,8 @@
 // selection was cut into several segments.  (A row that is one segment is
 // finished, low-res merge included, by the attention kernel.)
 //
-// For a listed block row i of head bh:
+// For a listed block row i of head bh (its descriptor: row, first segment,
+// number of segments):
 //   * full mode: the row's low-resolution part without its selected blocks,
 //       lo = lo_all_i - sum_{j in sel(i)} w_ij vhat_j,
 //       ll = ll_all_i - sum_{j in sel(i)} w_ij,
@@ -26,75 +27,84 @@ constexpr int kThreads = 256;
 constexpr int kBatch = 8;       // segments whose loads are in flight together
 constexpr int kRowSlots = 32;   // workgroups per head
 
+// One listed row, from its descriptor (row i, first segment, segments).
+// Every load the row needs is issued before the first wait; the segments are
+// joined in one pass with a running maximum.
 template <int DT>
-__device__ void merge_row(const Params& p, int bh, int i, float* lo, float* ll_s) {
+__device__ void merge_row(const Params& p, int bh, int4 dsc, float* lo, float* ll_s) {
     const int nb = p.nb;
     const int b = bh / p.H;
     const int tid = threadIdx.x;
-    const int* ip = p.item_ptr + (size_t)bh * (nb + 1);
-    const int first = max(ip[i], 0);
-    const int nit = max(0, min(ip[i + 1] - first, p.max_items - first));
+    const int i = min(max(dsc.x, 0), nb - 1);
+    const int first = max(dsc.y, 0);
+    const int nit = max(0, min(dsc.z, p.max_items - first));
     const size_t pbase = (size_t)bh * p.max_items + first;
-    float mi2 = -__builtin_inff(), ll = 0.f;
-    if (p.mode == 0) {
-        // the row's low-res part: lo_all minus the segments' corrections
-        const size_t row = (size_t)bh * nb + i;
-        if (tid < kHeadDim + 1) {
-            float c = 0.f;
-            for (int q = 0; q < nit; q++) c += p.part_corr[(pbase + q) * kCorrStride + tid];
-            if (tid < kHeadDim) lo[tid] = p.lo_all[row * kHeadDim + tid] - c;
-            else *ll_s = fmaxf(p.ll_all[row] - c, 0.f);
-        }
-        mi2 = p.rowmax[row] * kLog2e;
-        __syncthreads();
-        ll = *ll_s;
-    }
-
+    const size_t row = (size_t)bh * nb + i;
+    const bool full = p.mode == 0;
     const int t = tid >> 3;              // token within the block
     const int cg = (tid & 7) * 8;        // channels cg .. cg+7
-    const bool valid = (p.mbits[(size_t)b * nb + i] >> t) & 1u;
-
-    float M2 = mi2;
-    for (int c0 = 0; c0 < nit; c0 += kBatch) {
-        float mc[kBatch];
-#pragma unroll
-        for (int c = 0; c < kBatch; c++) mc[c] = c0 + c < nit ? p.part_ml[(pbase + c0 + c) * 64 + t] : -__builtin_inff();
-#pragma unroll
-        for (int c = 0; c < kBatch; c++) M2 = fmaxf(M2, mc[c]);
+    const uint32_t qm = p.mbits[(size_t)b * nb + i];
+    float lo_in = 0.f, mrow = 0.f;
+    if (full) {
+        if (tid <= kHeadDim) lo_in = tid < kHeadDim ? p.lo_all[row * kHeadDim + tid] : p.ll_all[row];
+        mrow = p.rowmax[row];
     }
+
+    // high-res segments: running max M (log2 units), numerator acc, denominator den
+    float M = -__builtin_inff(), den = 0.f, corr = 0.f;
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; e++) acc[e] = 0.f;
-    float den = 0.f;
-    if (M2 != -__builtin_inff()) {
-        for (int c0 = 0; c0 < nit; c0 += kBatch) {
-            float mc[kBatch], lc[kBatch];
-            float4 oa[kBatch], ob[kBatch];
+    for (int c0 = 0; c0 < nit; c0 += kBatch) {
+        float mc[kBatch], lc[kBatch], cc[kBatch];
+        float4 oa[kBatch], ob[kBatch];
+#pragma unroll
+        for (int c = 0; c < kBatch; c++) {
+            const bool ok = c0 + c < nit;
+            const size_t it = pbase + (ok ? c0 + c : 0);
+            mc[c] = ok ? p.part_ml[it * 64 + t] : -__builtin_inff();
+            lc[c] = ok ? p.part_ml[it * 64 + 32 + t] : 0.f;
+            cc[c] = (ok && full && tid <= kHeadDim) ? p.part_corr[it * kCorrStride + tid] : 0.f;
+            const float4* po = reinterpret_cast<const float4*>(p.part_o + (it * kBlock + t) * kHeadDim + cg);
+            oa[c] = ok ? po[0] : make_float4(0.f, 0.f, 0.f, 0.f);
+            ob[c] = ok ? po[1] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        float Mb = M;
+#pragma unroll
+        for (int c = 0; c < kBatch; c++) Mb = fmaxf(Mb, mc[c]);
+        if (Mb != -__builtin_inff()) {
+            const float s = M == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(M - Mb);
+            den *= s;
+#pragma unroll
+            for (int e = 0; e < 8; e++) acc[e] *= s;
 #pragma unroll
             for (int c = 0; c < kBatch; c++) {
-                const bool ok = c0 + c < nit;
-                const size_t it = pbase + c0 + c;
-                mc[c] = ok ? p.part_ml[it * 64 + t] : -__builtin_inff();
-                lc[c] = ok ? p.part_ml[it * 64 + 32 + t] : 0.f;
-                const float4* po = reinterpret_cast<const float4*>(p.part_o + (it * kBlock + t) * kHeadDim + cg);
-                oa[c] = ok ? po[0] : make_float4(0.f, 0.f, 0.f, 0.f);
-                ob[c] = ok ? po[1] : make_float4(0.f, 0.f, 0.f, 0.f);
-            }
-#pragma unroll
-            for (int c = 0; c < kBatch; c++) {
-                const float f = __builtin_amdgcn_exp2f(mc[c] - M2);
+                const float f = mc[c] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mc[c] - Mb);
                 den += lc[c] * f;
                 acc[0] += oa[c].x * f; acc[1] += oa[c].y * f; acc[2] += oa[c].z * f; acc[3] += oa[c].w * f;
                 acc[4] += ob[c].x * f; acc[5] += ob[c].y * f; acc[6] += ob[c].z * f; acc[7] += ob[c].w * f;
             }
+            M = Mb;
         }
-        if (p.mode == 0) {
-            const float f = __builtin_amdgcn_exp2f(mi2 - M2);
-            den += ll * f;
 #pragma unroll
-            for (int e = 0; e < 8; e++) acc[e] += lo[cg + e] * f;
+        for (int c = 0; c < kBatch; c++) corr += cc[c];
+    }
+    if (full) {
+        // the row's low-res part: lo_all minus the segments' corrections
+        if (tid < kHeadDim) lo[tid] = lo_in - corr;
+        else if (tid == kHeadDim) *ll_s = fmaxf(lo_in - corr, 0.f);
+        __syncthreads();
+        const float ll = *ll_s, mi2 = mrow * kLog2e;
+        const float Mf = fmaxf(M, mi2);
+        if (Mf != -__builtin_inff()) {
+            const float s = M == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(M - Mf);
+            const float f = __builtin_amdgcn_exp2f(mi2 - Mf);
+            den = den * s + ll * f;
+#pragma unroll
+            for (int e = 0; e < 8; e++) acc[e] = acc[e] * s + lo[cg + e] * f;
         }
     }
+    const bool valid = (qm >> t) & 1u;
     const float inv = (valid && den > 0.f) ? 1.0f / den : 0.f;
     const size_t orow = ((size_t)bh * p.N + (size_t)i * kBlock + t) * kHeadDim + cg;
     if constexpr (DT == 1) {
@@ -117,10 +127,12 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(Params p) {
     __shared__ float ll;
     const int nb = p.nb;
     const int bh = blockIdx.x / kRowSlots, slot = blockIdx.x - bh * kRowSlots;
+    // the descriptor of this workgroup's first row is loaded with the count
+    int4 dsc = slot < nb ? p.merge_rows[(size_t)bh * nb + slot] : make_int4(0, 0, 0, 0);
     const int nm = min(p.n_merge[bh], nb);
     for (int s = slot; s < nm; s += kRowSlots) {
-        const int i = min(max(p.merge_rows[(size_t)bh * nb + s], 0), nb - 1);
-        merge_row<DT>(p, bh, i, lo, &ll);
+        if (s != slot) dsc = p.merge_rows[(size_t)bh * nb + s];
+        merge_row<DT>(p, bh, dsc, lo, &ll);
         __syncthreads();   // lo and ll are reused by the next row
     }
 }

@@ -855,7 +855,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
             item_ptr[i] = ei;
             rc[i] = ec;
             ic[i] = ei;
-            if (mf) p.merge_rows[(size_t)bh * nb + em] = i;
+            if (mf) p.merge_rows[(size_t)bh * nb + em] = make_int4(i, ei, it, 0);
         }
         if (tid == 0) {
             const int tc = (int)(uint32_t)tot, ti = (int)((tot >> 32) & 0xFFFFu), tm = (int)(tot >> 48);
