@@ -8,7 +8,7 @@
 // [k*K/W, (k+1)*K/W) of that list, moved to the next segment boundaries, so
 // every wave gets about the same number of blocks whatever the row lengths.
 // A wave streams through its blocks in batches: it issues the K, V and Q
-// loads of three blocks at once, then computes them, while the other wave on
+// loads of two blocks at once, then computes them, while the other wave on
 // its SIMD does the same half a batch out of step.
 //
 // Per key block j of a segment of query block row i:
@@ -81,7 +81,7 @@ __device__ __forceinline__ int nearest_segment_start(int x, uint32_t info, int64
 
 template <int DT> struct Cfg;
 template <> struct Cfg<1> {                 // bf16: 16 bytes per lane per 8 elements
-    static constexpr int kBatch = 3;        // blocks whose loads are in flight together
+    static constexpr int kBatch = 2;        // blocks whose loads are in flight together (3 spills registers)
     static constexpr int kKV = 4;           // uint4 per lane for one K (or V) block
     using Elem = uint16_t;
     static constexpr int kStride = kVStrideB;
