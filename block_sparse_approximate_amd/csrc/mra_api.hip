@@ -56,6 +56,8 @@ bool carve(const mra_dims& d, int32_t bpr, int32_t mode, Layout* L) {
     L->part_o = take(BH * (size_t)L->max_items * kBlock * dd * 4);
     L->part_ml = take(BH * (size_t)L->max_items * 2 * kBlock * 4);
     L->part_corr = mode == MRA_APPROX_FULL ? take(BH * (size_t)L->max_items * kCorrStride * 4) : 0;
+    L->cand = take(BH * (size_t)kSelCap * 8);
+    L->ncand = take(BH * kCandStride * 4);
     L->total = o;
     return true;
 }
@@ -99,6 +101,7 @@ Params make_params(const mra_dims& d, const Layout& L, int32_t mode, int32_t pf,
     p.prior_diag = pd;
     p.max_items = L.max_items;
     p.attn_wph = attn_grid_waves_per_head(L.BH, L.K);
+    p.attn_seq = attn_heads_in_turn(L.BH, L.K) ? 1 : 0;
     p.q = q; p.k = k; p.v = v; p.mask = mask; p.out = out;
     p.qhat = reinterpret_cast<float*>(w + L.qhat);
     p.khat = reinterpret_cast<float*>(w + L.khat);
@@ -122,6 +125,8 @@ Params make_params(const mra_dims& d, const Layout& L, int32_t mode, int32_t pf,
     p.part_o = reinterpret_cast<float*>(w + L.part_o);
     p.part_ml = reinterpret_cast<float*>(w + L.part_ml);
     p.part_corr = L.part_corr ? reinterpret_cast<float*>(w + L.part_corr) : nullptr;
+    p.cand = reinterpret_cast<uint64_t*>(w + L.cand);
+    p.ncand = reinterpret_cast<uint32_t*>(w + L.ncand);
     p.error = reinterpret_cast<int32_t*>(w);
     return p;
 }
@@ -208,6 +213,7 @@ MRA_API mra_status mra_workspace_size(const mra_dims* dims, int32_t block_per_ro
 static mra_status run_front(const Params& p, hipStream_t s) {
     if (launch_pool(p, s) != hipSuccess) return MRA_ERR_HIP;
     if (launch_logits(p, s) != hipSuccess) return MRA_ERR_HIP;
+    if (launch_premark(p, s) != hipSuccess) return MRA_ERR_HIP;
     if (launch_select(p, s) != hipSuccess) return MRA_ERR_HIP;
     return MRA_OK;
 }
@@ -233,6 +239,7 @@ static mra_status run_forward(const mra_dims* dims, const void* q, const void* k
     if (e == hipSuccess) e = launch_logits(p, s);
     if (e == hipSuccess) e = mark(3);
     if (e == hipSuccess) e = mark(4);
+    if (e == hipSuccess) e = launch_premark(p, s);
     if (e == hipSuccess) e = launch_select(p, s);
     if (e == hipSuccess) e = mark(5);
     if (e == hipSuccess) e = mark(6);
@@ -315,9 +322,11 @@ MRA_API mra_status mra_debug_select(const mra_dims* dims, const float* logits, c
     hipError_t e = hipMemcpyAsync(p.logits, logits, BH * nb * nb * 4, hipMemcpyDeviceToDevice, s);
     if (e == hipSuccess) e = hipMemcpyAsync(p.cnt, count, (size_t)L.B * nb * 4, hipMemcpyDeviceToDevice, s);
     if (e == hipSuccess) e = hipMemsetAsync(p.hist, 0, BH * kHistBins * 4, s);
+    if (e == hipSuccess) e = hipMemsetAsync(p.ncand, 0, BH * kCandStride * 4, s);
     if (e == hipSuccess) e = hipMemsetAsync(p.error, 0, 4, s);
     if (e != hipSuccess) return MRA_ERR_HIP;
     if (launch_logits_given(p, s) != hipSuccess) return MRA_ERR_HIP;
+    if (launch_premark(p, s) != hipSuccess) return MRA_ERR_HIP;
     if (launch_select(p, s) != hipSuccess) return MRA_ERR_HIP;
     const int total = L.BH * L.nb;
     hipLaunchKernelGGL(csr_to_flat_kernel, dim3((total + 255) / 256), dim3(256), 0, s, p.row_ptr, p.col, L.nb, L.K,

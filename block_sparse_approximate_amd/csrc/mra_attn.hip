@@ -26,9 +26,10 @@
 // At the end of a segment that is a whole row the wave writes the row's
 // output.  In sparse mode that is O/l (0 for padded query tokens).  In full
 // mode the wave also merges the low-resolution part ([MRA] "第四步"): the
-// logits kernel summed the low-res attention of the row over every key block
-// (lo_all, ll_all), and each record carries its cell's low-res weight w, so
-// the wave takes the selected blocks back out,
+// low-res sums summed the low-res attention of the row over every key block
+// (lo_all, ll_all); the wave forms the low-res weight w of each of its cells
+// with the same expression from the same logit, row max and count, and takes
+// the selected blocks back out,
 //   lo = lo_all - sum_sel w vhat_j,   ll = ll_all - sum_sel w,
 // and writes (O 2^(m - M) + lo 2^(m_i - M)) / (l 2^(m - M) + ll 2^(m_i - M))
 // with M the larger of the high-res max m and the low-res row max m_i (both
@@ -38,6 +39,9 @@
 //
 // Workgroups are placed XCD-aware: workgroup g runs on XCD g % 8, and all
 // waves of head bh are on XCD bh % 8, so a head's K/V re-reads stay in one L2.
+// When a head has enough blocks for every wave of an XCD (long sequences),
+// the XCD's waves take its heads in turn rather than side by side, so that
+// L2 holds one head's K and V at a time.
 #include "mra_common.h"
 
 namespace mra {
@@ -54,6 +58,7 @@ constexpr int kVStrideB = 80;   // bf16 elements per staged V row (64 + 16 pad: 
 constexpr int kKStrideB = 72;   // bf16 elements per staged Q row (144 bytes: 8 lanes' 16-byte reads hit 32 banks)
 constexpr int kVStrideF = 68;   // fp32 elements per staged V row
 constexpr int kWindow = 64;     // block records a wave holds (one per lane)
+constexpr float kLazyMax = 8.0f;   // log2 headroom of the running max (probabilities <= 256)
 // blocks per wave before segment alignment: an end moves up to kChunk - 1
 // blocks forward, a start up to kChunk / 2 back
 constexpr int kMaxRun = kWindow - kChunk - kChunk / 2;
@@ -141,12 +146,10 @@ __device__ __forceinline__ void issue(const Params& p, const Wave<DT>& W, int e,
         for (int x = 0; x < 4; x++) s.v[x] = *reinterpret_cast<const uint4*>(Vb + off + 8 * x * kHeadDim);
         // V_j and Q_i: whole 128-byte token rows per 8 lanes, so every load
         // is 8 full cache lines; Q_i once per segment, by its first block
+        // (the other blocks leave s.q unset: only a segment's first block reads it)
         if (info_pos((uint32_t)rl((int)W.winfo, we)) == 0) {
 #pragma unroll
             for (int x = 0; x < 4; x++) s.q[x] = *reinterpret_cast<const uint4*>(Qb + off + 8 * x * kHeadDim);
-        } else {
-#pragma unroll
-            for (int x = 0; x < 4; x++) s.q[x] = make_uint4(0u, 0u, 0u, 0u);
         }
     } else {
         const float* Kb = W.Kg + (size_t)j * kBlock * kHeadDim;
@@ -258,11 +261,8 @@ __device__ __forceinline__ void process(const Params& p, const Wave<DT>& W, int 
     const uint32_t kb = (uint32_t)rl((int)W.wk, we);
     const uint32_t info = (uint32_t)rl((int)W.winfo, we);
     const int lane = W.lane, n = W.n, h = W.h;
-    if (info_pos(info) == 0) {   // a segment starts
-#pragma unroll
-        for (int r = 0; r < 16; r++) { A.o0[r] = 0.f; A.o1[r] = 0.f; }
+    if (info_pos(info) == 0) {   // a segment starts: alpha = 0 below clears O and l
         A.mrun = -__builtin_inff();
-        A.lsum = 0.f;
         if constexpr (FULL) {
             A.corr = 0.f;
             A.sw = 0.f;
@@ -325,7 +325,11 @@ __device__ __forceinline__ void process(const Params& p, const Wave<DT>& W, int 
         }
     }
     bm = fmaxf(bm, __shfl_xor(bm, 32, 64)) * scale2;
-    const float mnew = fmaxf(A.mrun, bm);
+    // The running max moves only when a block's max exceeds it by more than
+    // kLazyMax (log2 units), so most blocks keep alpha = 1 and skip the
+    // rescale of O; the probabilities then stay below 2^kLazyMax.  O and l are
+    // both relative to the max in use, so the result does not change.
+    const float mnew = bm > A.mrun + kLazyMax ? bm : A.mrun;
     const float muse = mnew == -__builtin_inff() ? 0.f : mnew;
     const float alpha = fast_exp2(A.mrun - muse);
     float ps = 0.f;
@@ -336,8 +340,10 @@ __device__ __forceinline__ void process(const Params& p, const Wave<DT>& W, int 
     }
     A.lsum = A.lsum * alpha + ps;
     A.mrun = mnew;
+    if (__ballot(alpha != 1.0f)) {
 #pragma unroll
-    for (int r = 0; r < 16; r++) { A.o0[r] *= alpha; A.o1[r] *= alpha; }
+        for (int r = 0; r < 16; r++) { A.o0[r] *= alpha; A.o1[r] *= alpha; }
+    }
     // the LDS writes above precede these reads in the wave's in-order LDS queue
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -387,17 +393,10 @@ struct StageBuf {
     typename Cfg<DT>::Elem v[32 * Cfg<DT>::kStride + (DT == 1 ? 32 * kKStrideB : 0)];
 };
 
+// Range k of the WPH ranges of head bh's record stream, by one wave.
 template <int DT, bool FULL>
-__global__ __launch_bounds__(kThreads, 2) void attn_kernel(Params p) {
-    __shared__ __align__(16) StageBuf<DT> stage[kWaves];
-    const int xcd = blockIdx.x & 7;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int wx = (blockIdx.x >> 3) * kWaves + wave;      // wave index within its XCD
-    const int WPH = p.attn_wph;
-    const int hm = wx / WPH, k = wx - hm * WPH;
-    const int bh = xcd + 8 * hm;
-    if (bh >= p.BH) return;
-
+__device__ __forceinline__ void run_range(const Params& p, int bh, int k, int WPH, int lane,
+                                          typename Cfg<DT>::Elem* vs) {
     const int64_t K = p.K;
     const int a = (int)((int64_t)k * K / WPH);
     const int bnd = (int)((int64_t)(k + 1) * K / WPH);
@@ -418,14 +417,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(Params p) {
         if (a0 + lane < K) r = *reinterpret_cast<const int4*>(R + a0 + lane);
         W.wij = (uint32_t)r.x;
         W.wk = (uint32_t)r.y;
-        W.ww = __int_as_float(r.z);
         W.winfo = (uint32_t)r.w;
+        W.ww = 0.f;
         W.wm = 0.f;
         W.wll = 0.f;
         if (FULL && a0 + lane < K) {
+            // the cell's low-res weight, formed as the low-res sums formed it
             const size_t row = (size_t)bh * p.nb + min(rec_i(W.wij), p.nb - 1);
+            const float sij = p.logits[row * p.nb + min(rec_j(W.wij), p.nb - 1)];
             W.wm = p.rowmax[row];
             W.wll = p.ll_all[row];
+            W.ww = lowres_weight(sij, W.wm, __popc(W.wk));
         }
     }
     const uint32_t info_b = bnd < K ? R[bnd].info : 0u;
@@ -445,7 +447,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(Params p) {
     W.Qg = static_cast<const E*>(p.q) + head_off;
     W.Kg = static_cast<const E*>(p.k) + head_off;
     W.Vg = static_cast<const E*>(p.v) + head_off;
-    E* vs = stage[wave].v;
     const float scale2 = (1.0f / __builtin_sqrtf((float)p.d)) * kLog2e;
 
     // Blocks go in batches: the loads of a whole batch are issued, then the
@@ -456,6 +457,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(Params p) {
     Acc<DT> A;
     A.mrun = -__builtin_inff();
     A.lsum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; r++) { A.o0[r] = 0.f; A.o1[r] = 0.f; }   // finite, so alpha = 0 clears them
     for (int e0 = start; e0 < end; e0 += BATCH) {
         Slot<DT> sl[BATCH];
 #pragma unroll
@@ -469,11 +472,39 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(Params p) {
     }
 }
 
+template <int DT, bool FULL>
+__global__ __launch_bounds__(kThreads, 2) void attn_kernel(Params p) {
+    __shared__ __align__(16) StageBuf<DT> stage[kWaves];
+    const int xcd = blockIdx.x & 7;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wx = (blockIdx.x >> 3) * kWaves + wave;      // wave index within its XCD
+    const int WPH = p.attn_wph;
+    if (p.attn_seq) {
+        // every wave of the XCD takes range wx of each of the XCD's heads in
+        // turn, so the XCD's L2 holds one head's K and V at a time
+        if (wx >= WPH) return;
+        for (int bh = xcd; bh < p.BH; bh += 8) run_range<DT, FULL>(p, bh, wx, WPH, lane, stage[wave].v);
+    } else {
+        const int hm = wx / WPH;
+        const int bh = xcd + 8 * hm;
+        if (bh < p.BH) run_range<DT, FULL>(p, bh, wx - hm * WPH, WPH, lane, stage[wave].v);
+    }
+}
+
 }  // namespace
+
+// Heads whose ranges would still hold at least this many blocks each when
+// every wave of an XCD shares one head are taken in turn.
+constexpr int64_t kTurnMinBlocks = 12;
+constexpr int kWavesPerXcd = 256;                     // about 2048 waves on the chip
+
+bool attn_heads_in_turn(int BH, int64_t K) {
+    return (BH + 7) / 8 >= 2 && K >= kTurnMinBlocks * kWavesPerXcd;
+}
 
 int attn_grid_waves_per_head(int BH, int64_t K) {
     const int heads_per_xcd = (BH + 7) / 8;
-    int64_t w = 256 / heads_per_xcd;                  // about 2048 waves on the chip
+    int64_t w = attn_heads_in_turn(BH, K) ? kWavesPerXcd : kWavesPerXcd / heads_per_xcd;
     if (w < 1) w = 1;
     const int64_t hi = (K + 1) / 2;                   // at least about two blocks a wave
     if (w > hi) w = hi;
@@ -484,7 +515,7 @@ int attn_grid_waves_per_head(int BH, int64_t K) {
 
 hipError_t launch_attn(const Params& p, hipStream_t s) {
     const int heads_per_xcd = (p.BH + 7) / 8;
-    const int64_t waves_per_xcd = (int64_t)heads_per_xcd * p.attn_wph;
+    const int64_t waves_per_xcd = p.attn_seq ? p.attn_wph : (int64_t)heads_per_xcd * p.attn_wph;
     const int64_t grid = 8 * ((waves_per_xcd + kWaves - 1) / kWaves);
     const bool full = p.mode == 0;
     if (p.dtype == 1) {

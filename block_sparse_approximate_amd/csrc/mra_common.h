@@ -18,6 +18,8 @@ constexpr int kHistBins = 1 << kHistBits;
 constexpr float kPriorBias = 5000.0f;   // [MRA] step 2: 5e3 bias for forced blocks
 constexpr int kChunk = 16;              // max selected key blocks per segment of a row
 constexpr int kCorrStride = 68;         // floats per segment's low-res correction: 64 channels, weight sum, pad
+constexpr int kSelCap = 4096;           // selection candidates one head's boundary bin may hold
+constexpr int kCandStride = 32;         // u32 per head's candidate counter: one 128-byte line each
 constexpr float kLog2e = 1.4426950408889634f;
 
 // One selected block, in the head's CSR order (block row ascending, then key
@@ -26,8 +28,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 // kernel produces.
 //   ij    query block row i (bits 0..15) and key block j (bits 16..31)
 //   kmask valid-token mask word of key block j
-//   w     full mode: the low-resolution weight cnt_j exp(S_ij - m_i) of the
-//         cell, which the low-res part must leave out; 0 in sparse mode
+//   rsv   0 (keeps a record 16 bytes, one load per lane)
 //   info  bits  0..17  segment (item) index within the head
 //               18..23 position of the block within its segment
 //               24..29 segment length (1..kChunk)
@@ -35,7 +36,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 struct BlkRec {
     uint32_t ij;
     uint32_t kmask;
-    float w;
+    uint32_t rsv;
     uint32_t info;
 };
 
@@ -50,7 +51,7 @@ struct Layout {
     int64_t K;            // selection budget per (batch, head)
     int32_t max_items;    // segments per head, upper bound
     size_t qhat, khat, vhat, cnt, mbits, logits, keys, rowmax, hist, thresh, row_ptr, col, selbits, item_ptr, recs,
-        merge_rows, n_merge, lo_all, ll_all, part_o, part_ml, part_corr, total;
+        merge_rows, n_merge, lo_all, ll_all, part_o, part_ml, part_corr, cand, ncand, total;
 };
 
 // Everything a kernel needs, passed by value.
@@ -89,8 +90,11 @@ struct Params {
     float* part_o;         // [BH, max_items, 32, d] un-normalised high-res numerators
     float* part_ml;        // [BH, max_items, 2, 32] running max (log2 units) and sum
     float* part_corr;      // [BH, max_items, kCorrStride] full mode: the segment's sum of w vhat_j, then of w
+    uint64_t* cand;        // [BH, kSelCap] boundary-bin cells found by the pre-marking pass
+    uint32_t* ncand;       // [BH, kCandStride] their number, in word 0 (cleared by the pooling kernel)
     int32_t* error;        // device error flag (0 = fine)
     int32_t attn_wph;      // attention stream: waves sharing one head's blocks
+    int32_t attn_seq;      // 1: those are all the waves of an XCD, which take the XCD's heads in turn
 };
 
 // Ordered key of an fp32 score: larger score -> larger unsigned key.
@@ -125,6 +129,7 @@ __device__ __forceinline__ uint64_t cell_key64(uint32_t key32, uint32_t flat) {
 // Every kernel that forms a weight uses this one expression, so a weight
 // added in one kernel and taken away in another cancels exactly.
 __device__ __forceinline__ float lowres_weight(float s, float m, int cnt) {
+#pragma clang fp contract(off)
     return cnt > 0 ? (float)cnt * __builtin_amdgcn_exp2f((s - m) * kLog2e) : 0.0f;
 }
 
@@ -142,8 +147,10 @@ namespace mra {
 hipError_t launch_pool(const Params& p, hipStream_t s);
 hipError_t launch_logits(const Params& p, hipStream_t s);
 hipError_t launch_logits_given(const Params& p, hipStream_t s);
+hipError_t launch_premark(const Params& p, hipStream_t s);
 hipError_t launch_select(const Params& p, hipStream_t s);
 hipError_t launch_attn(const Params& p, hipStream_t s);
 hipError_t launch_finish(const Params& p, hipStream_t s);
 int attn_grid_waves_per_head(int BH, int64_t K);
+bool attn_heads_in_turn(int BH, int64_t K);
 }  // namespace mra

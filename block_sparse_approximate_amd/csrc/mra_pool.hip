@@ -29,13 +29,14 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(Params p, int ntens,
     constexpr int kLoads = kPoolBlocks * kBlockBytes / 16 / kPoolThreads;
     __shared__ __align__(16) unsigned char tile[kPoolBlocks * kBlockBytes];
 
-    // Clear the selection histogram for the next stage (stream order makes
-    // this visible to it).
+    // Clear the selection histogram and candidate counts for the next stages
+    // (stream order makes this visible to them).
     {
         const int gt = blockIdx.x * kPoolThreads + threadIdx.x;
         const int stride = gridDim.x * kPoolThreads;
         if (gt == 0) *p.error = 0;
         for (int w = gt; w < zero_words; w += stride) p.hist[w] = 0u;
+        if (gt < p.BH) p.ncand[(size_t)gt * kCandStride] = 0u;
     }
     // workgroup g runs on XCD g % 8; every workgroup of head bh goes to XCD
     // bh % 8, the XCD whose L2 the later stages of that head use

@@ -22,15 +22,17 @@
 //     over those candidates find the K-th largest key T;
 //   * the selected set {key >= T} is written as a bitmap, as CSR (row_ptr,
 //     col ascending) and as the attention stream: one record per selected
-//     block, rows cut into segments of at most kChunk blocks; in full mode a
-//     record carries the low-res weight of its cell, which the attention
-//     kernel takes out of the row's low-res sum.
+//     block, rows cut into segments of at most kChunk blocks.
 // A thread holds 16 cell keys in registers (the whole head up to N = 4096;
 // longer heads are walked in tiles of 16384 cells with the next tile in
 // flight), and wave w's cells of a tile are 64 consecutive cells, so one
 // ballot is 64 consecutive bits of the selection.
-// The two kernels are separate launches: the kernel boundary is what makes
-// one workgroup's logits visible to another, with no device-wide fences.
+//
+// premark_kernel: for heads longer than one tile (with nb a multiple of 64)
+// the marking pass runs before the selector, one workgroup per tile, so the
+// selector only loads the bitmap of sure cells and the candidate list.
+// The kernels are separate launches: the kernel boundary is what makes one
+// workgroup's output visible to another, with no device-wide fences.
 // The translation unit is built with -ffp-contract=off so that every fp32
 // operation is the one written.
 #include "mra_common.h"
@@ -49,7 +51,7 @@ constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kCells = 16;                         // cell keys per thread and tile
 constexpr int kTileCells = kSelThreads * kCells;   // 16384
-constexpr int kCap = 4096;                         // selection candidates held in LDS
+constexpr int kCap = kSelCap;                      // selection candidates held in LDS
 constexpr int kDigitBits = 8;                      // radix digit over the candidates
 constexpr int kDigitBins = 1 << kDigitBits;
 
@@ -79,21 +81,19 @@ __host__ __device__ inline LogitsLds logits_lds(int nb) {
 }
 
 struct SelectLds {
-    size_t hist, dig, cand, bitmap, rc, ic, mbv, rmv, stile, scan, small, total;
+    size_t hist, dig, cand, bitmap, rc, ic, mbv, scan, small, total;
 };
 
-// Full mode with the whole head in one tile stages the head's logits too,
-// for the low-res weights of the selected cells.
-__host__ __device__ inline bool stage_logits(int nb, int mode) {
-    return mode == 0 && (size_t)nb * nb <= (size_t)kTileCells;
+// Heads of more than one tile of cells, with whole 64-cell groups per block
+// row, get their marking pass from premark_kernel.
+__host__ __device__ inline bool premarked(int nb) {
+    return (nb & 63) == 0 && (size_t)nb * nb > (size_t)kTileCells;
 }
 
-__host__ __device__ inline SelectLds select_lds(int nb, int mode) {
+__host__ __device__ inline SelectLds select_lds(int nb) {
     SelectLds L;
     const int words = (nb + 31) / 32;
     size_t o = 0;
-    L.stile = o; o = align16(o + (stage_logits(nb, mode) ? (size_t)nb * nb * 4 : 0));
-    L.rmv = o; o = align16(o + (size_t)nb * 4);
     L.hist = o; o = align16(o + kHistBins * 4);
     L.dig = o; o = align16(o + 2 * kDigitBins * 4);
     L.cand = o; o = align16(o + (size_t)kCap * 8);
@@ -646,6 +646,93 @@ __device__ __forceinline__ void lowres_rows(const Params& p, int bh, int row0, u
     }
 }
 
+// ---------------------------------------------------------------- premark
+// The selector's marking pass for long heads (premarked(nb)), one workgroup
+// per tile of kTileCells cells.  Every workgroup of a head makes the
+// selector's first bin pick on the head's histogram (the same pick in each),
+// then marks its tile: a cell whose top 12 key bits are above the bin is
+// selected for sure, and a wave's 64 consecutive cells are two whole words
+// of the head's selection bitmap, stored as they are; a cell inside the bin
+// is appended to the head's candidate list in memory (one atomic per
+// workgroup on the head's counter, which has a cache line of its own).
+// When the bin holds more than kCap cells the workgroups store nothing and
+// the selector walks the cells itself.
+__global__ __launch_bounds__(kSelThreads) void premark_kernel(Params p) {
+    __shared__ uint32_t hist[kHistBins];
+    __shared__ uint32_t scan32[kSelWaves + 1];
+    __shared__ uint32_t small[32];
+    __shared__ uint32_t wtot[kSelWaves + 1];
+    const int nb = p.nb, words = p.words;
+    const uint32_t ncell = (uint32_t)nb * (uint32_t)nb;
+    const int ntiles = (int)((ncell + kTileCells - 1) / kTileCells);
+    // workgroup g runs on XCD g % 8: the tiles of head bh go to XCD bh % 8
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int hm = slot / ntiles, t = slot - hm * ntiles;
+    const int bh = xcd + 8 * hm;
+    if (bh >= p.BH) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint32_t base = (uint32_t)t * kTileCells;
+    const uint32_t* G = p.keys + (size_t)bh * ncell;
+
+    constexpr int kPer = kHistBins / kSelThreads;
+    uint32_t hv[kPer], kv[kCells];
+#pragma unroll
+    for (int e = 0; e < kPer; e++) hv[e] = p.hist[(size_t)bh * kHistBins + tid + e * kSelThreads];
+    fetch_keys(G, base, ncell, kv);
+#pragma unroll
+    for (int e = 0; e < kPer; e++) hist[tid + e * kSelThreads] = hv[e];
+    __syncthreads();
+    const BinPick bp = pick_bin(hist, (uint32_t)p.K, scan32, small);
+    if (bp.count > (uint32_t)kCap) return;
+
+    const uint32_t p32 = bp.bin, sh = 32 - kHistBits;
+    const uint32_t magic = 0xFFFFFFFFu / (uint32_t)nb + 1u;
+    const uint32_t wbase = (uint32_t)__builtin_amdgcn_readfirstlane(tid - lane);
+    uint32_t* gbits = p.selbits + (size_t)bh * nb * words;
+    uint64_t mh[kCells];
+    uint32_t tot = 0;
+#pragma unroll
+    for (int e = 0; e < kCells; e++) {
+        const uint32_t x0 = base + wbase + (uint32_t)e * kSelThreads;   // the wave's first cell (uniform)
+        mh[e] = 0;
+        if (x0 < ncell) {   // ncell is a multiple of 64: the group is whole
+            const uint32_t top = kv[e] >> sh;
+            const uint64_t ms = __ballot(top > p32);
+            mh[e] = __ballot(top == p32);
+            const uint32_t i0 = row_of(x0, (uint32_t)nb, magic), j0 = x0 - i0 * (uint32_t)nb;
+            if (lane == 0)
+                *reinterpret_cast<uint2*>(gbits + i0 * words + (j0 >> 5)) = make_uint2((uint32_t)ms, (uint32_t)(ms >> 32));
+            tot += (uint32_t)__popcll(mh[e]);
+        }
+    }
+    // the workgroup's place in the candidate list: waves in order, one atomic
+    if (lane == 0) wtot[wave] = tot;
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t acc = 0;
+        for (int w = 0; w < kSelWaves; w++) {
+            const uint32_t c = wtot[w];
+            wtot[w] = acc;
+            acc += c;
+        }
+        wtot[kSelWaves] = acc ? atomicAdd(&p.ncand[(size_t)bh * kCandStride], acc) : 0u;
+    }
+    __syncthreads();
+    if (tot) {
+        uint32_t at0 = wtot[kSelWaves] + wtot[wave];
+        const uint64_t lt_mask = (1ull << lane) - 1ull;
+        uint64_t* gc = p.cand + (size_t)bh * kCap;
+#pragma unroll
+        for (int e = 0; e < kCells; e++) {
+            if ((mh[e] >> lane) & 1ull) {
+                const uint32_t at = at0 + (uint32_t)__popcll(mh[e] & lt_mask);
+                if (at < (uint32_t)kCap) gc[at] = cell_key64(kv[e], base + wbase + (uint32_t)e * kSelThreads + lane);
+            }
+            at0 += (uint32_t)__popcll(mh[e]);
+        }
+    }
+}
+
 // ---------------------------------------------------------------- select
 __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -666,9 +753,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
     if (bh >= p.BH) return;
     const int b = bh / p.H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const SelectLds L = select_lds(nb, p.mode);
-    const bool full = p.mode == 0;
-    const bool staged = stage_logits(nb, p.mode);
+    const SelectLds L = select_lds(nb);
     const int words = p.words;
     uint32_t* hist = reinterpret_cast<uint32_t*>(smem + L.hist);
     uint32_t* dig = reinterpret_cast<uint32_t*>(smem + L.dig);
@@ -677,8 +762,6 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
     int* rc = reinterpret_cast<int*>(smem + L.rc);
     int* ic = reinterpret_cast<int*>(smem + L.ic);
     uint32_t* mbv = reinterpret_cast<uint32_t*>(smem + L.mbv);
-    float* rmv = reinterpret_cast<float*>(smem + L.rmv);
-    float* stile = reinterpret_cast<float*>(smem + L.stile);
     uint32_t* scan32 = reinterpret_cast<uint32_t*>(smem + L.scan);
     uint64_t* scan64 = reinterpret_cast<uint64_t*>(smem + L.scan);
     uint32_t* small = reinterpret_cast<uint32_t*>(smem + L.small);
@@ -688,31 +771,18 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
     const uint32_t magic = 0xFFFFFFFFu / (uint32_t)nb + 1u;
 
     // prologue: every global load first; the histogram goes to LDS at once,
-    // the keys stay in registers, and the logits, row maxima and mask words
-    // (needed only for the records) go to LDS later, so that their latency
-    // hides behind the threshold search
+    // the keys stay in registers, and the mask words (needed only for the
+    // records) go to LDS later, so that their latency hides behind the
+    // threshold search.  With the pre-marking pass the keys are not needed.
+    const bool pre_ok = premarked(nb);
     uint32_t kv[kCells];
-    float sv[kCells];
     constexpr int kPer = kHistBins / kSelThreads;
     uint32_t hv[kPer];
 #pragma unroll
     for (int e = 0; e < kPer; e++) hv[e] = p.hist[(size_t)bh * kHistBins + tid + e * kSelThreads];
-    fetch_keys(G, 0, ncell, kv);
-    {
-        const float* Sg = p.logits + (size_t)bh * ncell;
-        if (staged && ncell == (uint32_t)kTileCells) {
-#pragma unroll
-            for (int e = 0; e < kCells; e++) sv[e] = Sg[tid + e * kSelThreads];
-        } else if (staged) {
-#pragma unroll
-            for (int e = 0; e < kCells; e++) {
-                const uint32_t x = tid + e * kSelThreads;
-                sv[e] = x < ncell ? Sg[x] : 0.f;
-            }
-        }
-    }
+    if (!pre_ok) fetch_keys(G, 0, ncell, kv);
+    const uint32_t npre = pre_ok ? p.ncand[(size_t)bh * kCandStride] : 0u;
     const uint32_t mv = tid < nb ? p.mbits[b * nb + tid] : 0u;   // nb <= 512 < kSelThreads
-    const float rv = (full && tid < nb) ? p.rowmax[(size_t)bh * nb + tid] : 0.f;
 #pragma unroll
     for (int e = 0; e < kPer; e++) hist[tid + e * kSelThreads] = hv[e];
     for (int x = tid; x < nb * words; x += kSelThreads) bitmap[x] = 0u;
@@ -726,9 +796,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
     uint64_t prefix = bp.bin;
     int pbits = kHistBits;
     uint32_t count = bp.count;
+    // the pre-marking kernel made the same bin pick and, when the bin fits
+    // the candidate list, did the marking pass
+    const bool pre = pre_ok && count <= (uint32_t)kCap;
 
     // further 12-bit passes while the bin is too large for LDS (tie-heavy inputs)
-    bool tile0 = true;   // kv holds tile 0
+    bool tile0 = !pre_ok;   // kv holds tile 0
     while (count > (uint32_t)kCap && pbits < 64) {
         const int db = (64 - pbits) < 12 ? (64 - pbits) : 12;
         for (int x = tid; x < kHistBins; x += kSelThreads) hist[x] = 0u;
@@ -757,16 +830,26 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
 
     // One pass over the cells: cells above the bin are selected for sure
     // (bitmap), cells inside it are appended to the LDS candidate list.
-    if (!tile0) fetch_keys(G, 0, ncell, kv);
+    // After the pre-marking pass both come from memory instead.
     const bool rows64 = (nb & 63) == 0;
-    if (pbits <= 32 && rows64 && ncell == (uint32_t)kTileCells) {
-        mark_cells_fast(nb, words, magic, (uint32_t)prefix, pbits, kv, bitmap, cand, small);
-    } else if (pbits <= 32) {
-        if (rows64) mark_cells<true, true>(G, ncell, ntiles, nb, words, magic, prefix, pbits, kv, bitmap, cand, small);
-        else mark_cells<false, true>(G, ncell, ntiles, nb, words, magic, prefix, pbits, kv, bitmap, cand, small);
+    if (pre) {
+        const uint32_t* gb = p.selbits + (size_t)bh * nb * words;
+        for (int x = tid; x < nb * words; x += kSelThreads) bitmap[x] = gb[x];
+        const uint32_t nc = npre < (uint32_t)kCap ? npre : (uint32_t)kCap;
+        const uint64_t* gc = p.cand + (size_t)bh * kCap;
+        for (uint32_t c = tid; c < nc; c += kSelThreads) cand[c] = gc[c];
+        if (tid == 0) small[8] = npre;
     } else {
-        if (rows64) mark_cells<true, false>(G, ncell, ntiles, nb, words, magic, prefix, pbits, kv, bitmap, cand, small);
-        else mark_cells<false, false>(G, ncell, ntiles, nb, words, magic, prefix, pbits, kv, bitmap, cand, small);
+        if (!tile0) fetch_keys(G, 0, ncell, kv);
+        if (pbits <= 32 && rows64 && ncell == (uint32_t)kTileCells) {
+            mark_cells_fast(nb, words, magic, (uint32_t)prefix, pbits, kv, bitmap, cand, small);
+        } else if (pbits <= 32) {
+            if (rows64) mark_cells<true, true>(G, ncell, ntiles, nb, words, magic, prefix, pbits, kv, bitmap, cand, small);
+            else mark_cells<false, true>(G, ncell, ntiles, nb, words, magic, prefix, pbits, kv, bitmap, cand, small);
+        } else {
+            if (rows64) mark_cells<true, false>(G, ncell, ntiles, nb, words, magic, prefix, pbits, kv, bitmap, cand, small);
+            else mark_cells<false, false>(G, ncell, ntiles, nb, words, magic, prefix, pbits, kv, bitmap, cand, small);
+        }
     }
     __syncthreads();
     const uint32_t ncand_all = small[8];
@@ -822,18 +905,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
     }
     __syncthreads();
 
-    // the records' inputs, loaded in the prologue (read after the scan's barriers)
-    if (tid < nb) {
-        mbv[tid] = mv;
-        rmv[tid] = rv;
-    }
-    if (staged) {
-#pragma unroll
-        for (int e = 0; e < kCells; e++) {
-            const uint32_t x = tid + e * kSelThreads;
-            if (x < ncell) stile[x] = sv[e];
-        }
-    }
+    // the records' input, loaded in the prologue (read after the scan's barriers)
+    if (tid < nb) mbv[tid] = mv;
 
     // CSR row pointers, segment (item) pointers and the rows the final kernel
     // combines, in one scan: one block row per thread (nb <= 512)
@@ -875,16 +948,31 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
     int32_t* col = p.col + (size_t)bh * p.K;
     BlkRec* recs = p.recs + (size_t)bh * p.K;
     uint32_t* gbits = p.selbits + (size_t)bh * nb * words;
-    for (int x = tid; x < nb * words; x += kSelThreads) {
+    const bool pow2w = (words & (words - 1)) == 0;   // then 64 % words == 0
+    for (int x0 = 0; x0 < nb * words; x0 += kSelThreads) {
+        const int x = x0 + tid;
+        const bool in = x < nb * words;
+        uint32_t bits = in ? bitmap[x] : 0u;
         const int i = x / words, w = x - i * words;
-        uint32_t bits = bitmap[x];
+        int r = 0;
+        if (pow2w) {
+            // a block row's words sit in `words` consecutive lanes: the rank
+            // of the word's first bit is a segmented scan along the row
+            const int c = __popc(bits);
+            int inc = c;
+            for (int off = 1; off < words; off <<= 1) {
+                const int y = __shfl_up(inc, off, 64);
+                if ((lane & (words - 1)) >= off) inc += y;
+            }
+            r = inc - c;
+        }
+        if (!in) continue;
         gbits[x] = bits;
         if (!bits) continue;
-        int r = 0;
-        for (int u = 0; u < w; u++) r += __popc(bitmap[i * words + u]);
+        if (!pow2w)
+            for (int u = 0; u < w; u++) r += __popc(bitmap[i * words + u]);
         const int o = rc[i], n = rc[i + 1] - o, first = ic[i];
         const int nit = (n + kChunk - 1) / kChunk;
-        const float mi = rmv[i];
         while (bits) {
             const int j = w * 32 + __builtin_ctz(bits);
             bits &= bits - 1;
@@ -893,12 +981,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
                 col[e] = j;
                 const int sg = r / kChunk;
                 const int len = min(kChunk, n - sg * kChunk);
-                float wt = 0.f;
-                if (full) {
-                    const float sij = staged ? stile[i * nb + j] : p.logits[((size_t)bh * nb + i) * nb + j];
-                    wt = lowres_weight(sij, mi, __popc(mbv[j]));
-                }
-                recs[e] = BlkRec{rec_ij(i, j), mbv[j], wt, rec_info(first + sg, r - sg * kChunk, len, nit == 1)};
+                recs[e] = BlkRec{rec_ij(i, j), mbv[j], 0u, rec_info(first + sg, r - sg * kChunk, len, nit == 1)};
             }
             r++;
         }
@@ -922,13 +1005,22 @@ static hipError_t launch_logits_t(const Params& p, hipStream_t s) {
 hipError_t launch_logits(const Params& p, hipStream_t s) { return launch_logits_t<false>(p, s); }
 hipError_t launch_logits_given(const Params& p, hipStream_t s) { return launch_logits_t<true>(p, s); }
 
+hipError_t launch_premark(const Params& p, hipStream_t s) {
+    if (!premarked(p.nb)) return hipSuccess;
+    const uint32_t ncell = (uint32_t)p.nb * (uint32_t)p.nb;
+    const int ntiles = (int)((ncell + kTileCells - 1) / kTileCells);
+    const int heads_per_xcd = (p.BH + 7) / 8;
+    hipLaunchKernelGGL(premark_kernel, dim3(8 * heads_per_xcd * ntiles), dim3(kSelThreads), 0, s, p);
+    return hipGetLastError();
+}
+
 hipError_t launch_select(const Params& p, hipStream_t s) {
     static const hipError_t a2 = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (a2 != hipSuccess) return a2;
     const int bh_pad = 8 * ((p.BH + 7) / 8);
     const int lowres_wgs = p.mode == 0 ? bh_pad * ((p.nb + kLoRows - 1) / kLoRows) : 0;
-    size_t lds = select_lds(p.nb, p.mode).total;
+    size_t lds = select_lds(p.nb).total;
     if (p.mode == 0 && lowres_lds(p.nb) > lds) lds = lowres_lds(p.nb);
     hipLaunchKernelGGL(select_kernel, dim3(bh_pad + lowres_wgs), dim3(kSelThreads), lds, s, p);
     return hipGetLastError();

@@ -156,7 +156,11 @@ def test_clustered_error_against_dense_shrinks_with_budget(mra):
 # ----------------------------------------------------------- selector alone --
 @pytest.mark.parametrize("nb,bpr,pf,pd,kind", [
     (16, 4, 0, 0, "normal"), (128, 4, 2, 3, "normal"), (128, 4, 0, 0, "equal"), (13, 2, 1, 2, "ints"),
-    (128, 4, 0, 0, "ints"), (1, 1, 0, 0, "normal"), (64, 64, 0, 0, "normal"), (512, 8, 0, 1, "ints")])
+    (128, 4, 0, 0, "ints"), (1, 1, 0, 0, "normal"), (64, 64, 0, 0, "normal"), (512, 8, 0, 1, "ints"),
+    # heads of several 16384-cell tiles: the marking pass runs one workgroup per tile
+    # (nb = 192: the last tile is partial; "coarse": many exact ties that still fit
+    # the candidate list), and nb = 161 walks its tiles in one workgroup
+    (192, 4, 1, 2, "normal"), (256, 3, 0, 0, "coarse"), (161, 2, 0, 0, "normal")])
 def test_selector_on_identical_logits(mra, nb, bpr, pf, pd, kind):
     print("case", nb, bpr, pf, pd, kind, flush=True)
     rng = np.random.default_rng(nb * 7 + bpr)
@@ -165,6 +169,8 @@ def test_selector_on_identical_logits(mra, nb, bpr, pf, pd, kind):
         S = np.zeros((B, H, nb, nb), np.float32)
     elif kind == "ints":
         S = rng.integers(-3, 3, (B, H, nb, nb)).astype(np.float32)
+    elif kind == "coarse":
+        S = (np.round(rng.standard_normal((B, H, nb, nb)) * 16.0) / 16.0).astype(np.float32)
     else:
         S = rng.standard_normal((B, H, nb, nb)).astype(np.float32)
     cnt = np.full((B, nb), 32, np.int32)
@@ -196,6 +202,10 @@ EDGE = [
     ("long-rows-full", dict(B=2, H=1, N=1024, block_per_row=2, prior_first=1)),
     ("long-rows-fp32", dict(B=1, H=1, N=1024, dtype="f32", block_per_row=3, prior_first=2,
                             approx_mode="sparse")),
+    ("tiles-nb192", dict(B=1, H=2, N=6144, block_per_row=3)),
+    ("tiles-nb161-sparse", dict(B=1, H=1, N=5152, block_per_row=2, approx_mode="sparse")),
+    # 9 heads: XCD 0 takes heads 0 and 8 in turn, the other XCDs one head each
+    ("heads-in-turn-bh9", dict(B=1, H=9, N=12288, block_per_row=8)),
     ("priors-over-budget", dict(B=1, H=2, N=2048, block_per_row=1, prior_first=3, prior_diag=5,
                                 approx_mode="sparse")),
 ]
