@@ -59,11 +59,13 @@ __host__ __device__ inline size_t align16(size_t x) { return (x + 15) & ~size_t(
 
 // ---------------------------------------------------------------- LDS plans
 struct LogitsLds {
-    size_t qT, kT, hist, total;
+    size_t qS, kS, hist, total;
 };
 
 constexpr int kMaxColTiles = 4;   // column tiles of kCT key blocks (N <= 16384)
 constexpr int kVtStride = 68;     // floats per staged vhat row (64 + 4 pad)
+constexpr int kHatStride = 68;    // floats per staged qhat / khat row: lane l's 16-byte reads of row l
+                                  // fall on banks 4l .. 4l + 3, distinct over each 16-lane phase
 
 // Rows of the low-res weight tile: nb + 4 floats (the pad spreads the rows
 // over the LDS banks for the MFMA operand reads).
@@ -72,9 +74,8 @@ __host__ __device__ inline int wl_stride(int nb) { return nb + 4; }
 __host__ __device__ inline LogitsLds logits_lds(int nb) {
     LogitsLds L;
     size_t o = 0;
-    L.qT = o; o = align16(o + 64 * kRT * 4);
-    const size_t kt = 64 * kCT * 4, vt = 0;   // khat tile
-    L.kT = o; o = align16(o + (kt > vt ? kt : vt));
+    L.qS = o; o = align16(o + (size_t)kRT * kHatStride * 4);   // qhat rows of the workgroup
+    L.kS = o; o = align16(o + (size_t)kCT * kHatStride * 4);   // khat rows of one column tile
     L.hist = o; o = align16(o + kHistBins * 4);
     L.total = o;
     return L;
@@ -327,12 +328,12 @@ __device__ __forceinline__ void fetch_vhat(const float* __restrict__ vh, int j0,
 }
 
 // The khat tile of key blocks j0 .. j0 + kCT - 1 into registers: float4 x is
-// block j0 + x % kCT, channels 4 * (x / kCT) .. +3.
+// block j0 + x / 16, channels 4 * (x % 16) .. +3 (16 lanes read one row).
 __device__ __forceinline__ void fetch_khat(const float* __restrict__ kh, int j0, int nb,
                                            float4 (&kv)[kCT * (kHeadDim / 4) / kLgThreads]) {
 #pragma unroll
     for (int e = 0; e < kCT * (kHeadDim / 4) / kLgThreads; e++) {
-        const int x = threadIdx.x + e * kLgThreads, jj = x % kCT, c4 = (x / kCT) * 4;
+        const int x = threadIdx.x + e * kLgThreads, jj = x >> 4, c4 = (x & 15) * 4;
         kv[e] = j0 + jj < nb ? *reinterpret_cast<const float4*>(kh + (size_t)(j0 + jj) * kHeadDim + c4)
                              : make_float4(0.f, 0.f, 0.f, 0.f);
     }
@@ -385,9 +386,12 @@ __device__ __forceinline__ void mark_cells_fast(int nb, int words, uint32_t magi
 
 // ---------------------------------------------------------------- logits
 // Wave w owns block rows ra = row0 + 2w and rb = ra + 1 of the workgroup's 16;
-// lane l owns key blocks 128 t + 2l and 128 t + 2l + 1 of every column tile
-// t, so the row max, the scores, the keys and the low-res weights of a cell
-// never leave the registers of the lane that computed its logit.
+// lane l owns key blocks 128 t + l and 128 t + 64 + l of every column tile
+// t, so the row max, the score and the key of a cell never leave the
+// registers of the lane that computed its logit.  The qhat rows and the khat
+// tile sit in LDS row-major; a lane reads 4 channels of each of its two key
+// blocks and of the two rows at once and does the 16 fmas they feed, each
+// cell's chain still going over the channels in order.
 // kGiven: the logits are already in p.logits (selector hook); skip their
 // computation and only form row maxima, keys and the histogram.
 template <bool kGiven>
@@ -406,8 +410,8 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(Params p) {
     const float tau = (float)(1.0 / __builtin_sqrt((double)p.d));
     const int ntile = (nb + kCT - 1) / kCT;
     const LogitsLds L = logits_lds(nb);
-    float* qT = reinterpret_cast<float*>(smem + L.qT);
-    float* kT = reinterpret_cast<float*>(smem + L.kT);
+    float* qS = reinterpret_cast<float*>(smem + L.qS);
+    float* kS = reinterpret_cast<float*>(smem + L.kS);
     uint32_t* hist = reinterpret_cast<uint32_t*>(smem + L.hist);
     const float* qh = p.qhat + (size_t)bh * nb * kHeadDim;
     const float* kh = p.khat + (size_t)bh * nb * kHeadDim;
@@ -418,8 +422,8 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(Params p) {
     constexpr int kKLoads = kCT * (kHeadDim / 4) / kLgThreads;   // float4s of one khat tile per thread
     float4 qv = make_float4(0.f, 0.f, 0.f, 0.f);
     float4 kv[kKLoads];
-    float sc[kMaxColTiles][4];   // logits of (ra, j), (ra, j + 1), (rb, j), (rb, j + 1), j = 128 t + 2 lane
-    int2 cj[kMaxColTiles];       // counts of key blocks j and j + 1
+    float sc[kMaxColTiles][4];   // logits of (ra, j), (ra, j + 64), (rb, j), (rb, j + 64), j = 128 t + lane
+    int2 cj[kMaxColTiles];       // counts of key blocks j and j + 64
     if (!kGiven) {
         if (tid < kRT * kHeadDim / 4) {
             const int r = tid / (kHeadDim / 4), c4 = (tid % (kHeadDim / 4)) * 4;
@@ -429,53 +433,65 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(Params p) {
     }
 #pragma unroll
     for (int t = 0; t < kMaxColTiles; t++) {
-        const int j = t * kCT + 2 * lane;
+        const int j = t * kCT + lane;
         cj[t].x = (t < ntile && j < nb) ? cnt[j] : 0;
-        cj[t].y = (t < ntile && j + 1 < nb) ? cnt[j + 1] : 0;
+        cj[t].y = (t < ntile && j + 64 < nb) ? cnt[j + 64] : 0;
         if (kGiven) {
             const float* S = p.logits + (size_t)bh * nb * nb;
             sc[t][0] = (t < ntile && ra < nb && j < nb) ? S[(size_t)ra * nb + j] : 0.f;
-            sc[t][1] = (t < ntile && ra < nb && j + 1 < nb) ? S[(size_t)ra * nb + j + 1] : 0.f;
+            sc[t][1] = (t < ntile && ra < nb && j + 64 < nb) ? S[(size_t)ra * nb + j + 64] : 0.f;
             sc[t][2] = (t < ntile && rb < nb && j < nb) ? S[(size_t)rb * nb + j] : 0.f;
-            sc[t][3] = (t < ntile && rb < nb && j + 1 < nb) ? S[(size_t)rb * nb + j + 1] : 0.f;
+            sc[t][3] = (t < ntile && rb < nb && j + 64 < nb) ? S[(size_t)rb * nb + j + 64] : 0.f;
         }
     }
     const int cia = ra < nb ? cnt[ra] : 0, cib = rb < nb ? cnt[rb] : 0;
     for (int x = tid; x < kHistBins; x += kLgThreads) hist[x] = 0u;
     if (!kGiven && tid < kRT * kHeadDim / 4) {
         const int r = tid / (kHeadDim / 4), c4 = (tid % (kHeadDim / 4)) * 4;
-        qT[(c4 + 0) * kRT + r] = qv.x;
-        qT[(c4 + 1) * kRT + r] = qv.y;
-        qT[(c4 + 2) * kRT + r] = qv.z;
-        qT[(c4 + 3) * kRT + r] = qv.w;
+        *reinterpret_cast<float4*>(qS + r * kHatStride + c4) = qv;
     }
     __syncthreads();
 
-    // logits, one column tile at a time: kT[c][jj] = khat[128 t + jj][c]
+    // logits, one column tile at a time: kS[jj][c] = khat[128 t + jj][c]
     if (!kGiven) {
+        const float* qa = qS + (2 * wave) * kHatStride;
+        const float* qb = qa + kHatStride;
+        const float* k0 = kS + lane * kHatStride;
+        const float* k1 = kS + (lane + 64) * kHatStride;
 #pragma unroll
         for (int t = 0; t < kMaxColTiles; t++) {
             if (t < ntile) {
                 if (t > 0) __syncthreads();
 #pragma unroll
                 for (int e = 0; e < kKLoads; e++) {
-                    const int x = tid + e * kLgThreads, jj = x % kCT, c4 = (x / kCT) * 4;
-                    kT[(c4 + 0) * kCT + jj] = kv[e].x;
-                    kT[(c4 + 1) * kCT + jj] = kv[e].y;
-                    kT[(c4 + 2) * kCT + jj] = kv[e].z;
-                    kT[(c4 + 3) * kCT + jj] = kv[e].w;
+                    const int x = tid + e * kLgThreads;
+                    *reinterpret_cast<float4*>(kS + (x >> 4) * kHatStride + (x & 15) * 4) = kv[e];
                 }
                 __syncthreads();
                 if (t + 1 < ntile) fetch_khat(kh, (t + 1) * kCT, nb, kv);   // in flight during this tile
                 float a00 = 0.f, a01 = 0.f, a10 = 0.f, a11 = 0.f;
-#pragma unroll 8
-                for (int c = 0; c < kHeadDim; c++) {
-                    const float2 q2 = *reinterpret_cast<const float2*>(qT + c * kRT + 2 * wave);
-                    const float2 k2 = *reinterpret_cast<const float2*>(kT + c * kCT + 2 * lane);
-                    a00 = __builtin_fmaf(q2.x, k2.x, a00);
-                    a01 = __builtin_fmaf(q2.x, k2.y, a01);
-                    a10 = __builtin_fmaf(q2.y, k2.x, a10);
-                    a11 = __builtin_fmaf(q2.y, k2.y, a11);
+#pragma unroll 4
+                for (int c = 0; c < kHeadDim; c += 4) {
+                    const float4 x0 = *reinterpret_cast<const float4*>(k0 + c);
+                    const float4 x1 = *reinterpret_cast<const float4*>(k1 + c);
+                    const float4 ya = *reinterpret_cast<const float4*>(qa + c);
+                    const float4 yb = *reinterpret_cast<const float4*>(qb + c);
+                    a00 = __builtin_fmaf(ya.x, x0.x, a00);
+                    a01 = __builtin_fmaf(ya.x, x1.x, a01);
+                    a10 = __builtin_fmaf(yb.x, x0.x, a10);
+                    a11 = __builtin_fmaf(yb.x, x1.x, a11);
+                    a00 = __builtin_fmaf(ya.y, x0.y, a00);
+                    a01 = __builtin_fmaf(ya.y, x1.y, a01);
+                    a10 = __builtin_fmaf(yb.y, x0.y, a10);
+                    a11 = __builtin_fmaf(yb.y, x1.y, a11);
+                    a00 = __builtin_fmaf(ya.z, x0.z, a00);
+                    a01 = __builtin_fmaf(ya.z, x1.z, a01);
+                    a10 = __builtin_fmaf(yb.z, x0.z, a10);
+                    a11 = __builtin_fmaf(yb.z, x1.z, a11);
+                    a00 = __builtin_fmaf(ya.w, x0.w, a00);
+                    a01 = __builtin_fmaf(ya.w, x1.w, a01);
+                    a10 = __builtin_fmaf(yb.w, x0.w, a10);
+                    a11 = __builtin_fmaf(yb.w, x1.w, a11);
                 }
                 sc[t][0] = a00 * tau;
                 sc[t][1] = a01 * tau;
@@ -510,7 +526,7 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(Params p) {
     for (int t = 0; t < kMaxColTiles; t++) {
 #pragma unroll
         for (int q = 0; q < 4; q++) {
-            const int i = q < 2 ? ra : rb, j = t * kCT + 2 * lane + (q & 1);
+            const int i = q < 2 ? ra : rb, j = t * kCT + lane + 64 * (q & 1);
             if (t < ntile && i < nb && j < nb) {
                 const float sv = sc[t][q];
                 if (!kGiven) Sg[(size_t)i * nb + j] = sv;
