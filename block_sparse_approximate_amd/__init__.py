@@ -18,6 +18,7 @@ import os
 import torch
 
 __all__ = ["attention", "attention_profiled", "prepare", "num_block", "workspace_size", "debug_stages", "debug_select",
+           "debug_replay",
            "MraError", "library_path", "lib"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -40,6 +41,7 @@ SIGNATURES = {
     "mra_debug_stages": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
                           _P, _SZ, _P], ctypes.c_int),
     "mra_debug_select": ([_P, _P, _P, _I32, _I32, _I32, _P, _P, _SZ, _P], ctypes.c_int),
+    "mra_debug_replay": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _SZ, _I32, _I32, _P], ctypes.c_int),
 }
 
 
@@ -200,6 +202,22 @@ def attention_profiled(q, k, v, events, mask=None, block_per_row=4, approx_mode=
                                           initial_prior_diagonal_n_blocks, _ptr(out), _ptr(workspace),
                                           workspace.numel(), _stream(q), arr)
     _check(st, "mra_attention_fwd_profiled")
+    return out
+
+
+def debug_replay(q, k, v, stage, count, mask=None, block_per_row=4, approx_mode="full",
+                 initial_prior_first_n_blocks=0, initial_prior_diagonal_n_blocks=0, out=None, workspace=None):
+    """Relaunch stage STAGES[stage] (3 attn or 4 finish only) `count` times on
+    the current stream, on a workspace and out that a forward call with the
+    same arguments has filled; for timing the kernel alone."""
+    _check_inputs(q, k, v, mask)
+    B, H, N, d = q.shape
+    dims = _dims(B, H, N, d, DTYPES[q.dtype])
+    st = lib().mra_debug_replay(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), block_per_row,
+                                MODES.get(approx_mode, -1), initial_prior_first_n_blocks,
+                                initial_prior_diagonal_n_blocks, _ptr(out), _ptr(workspace),
+                                0 if workspace is None else workspace.numel(), stage, count, _stream(q))
+    _check(st, "mra_debug_replay")
     return out
 
 

@@ -186,6 +186,7 @@ MRA_API const char* mra_status_string(int32_t s) {
         case MRA_ERR_WORKSPACE: return "workspace missing or too small";
         case MRA_ERR_HIP: return "a HIP launch failed";
         case MRA_ERR_ALIGN: return "a pointer is not aligned (tensors 16 bytes, workspace 256 bytes)";
+        case MRA_ERR_STAGE: return "stage cannot be replayed (3 and 4 only) or count < 1";
         default: return "unknown status";
     }
 }
@@ -265,6 +266,22 @@ MRA_API mra_status mra_attention_fwd_profiled(const mra_dims* dims, const void* 
                                               size_t workspace_bytes, void* stream, void* const* events) {
     return run_forward(dims, q, k, v, mask, block_per_row, approx_mode, prior_first, prior_diag, out, workspace,
                        workspace_bytes, stream, events);
+}
+
+MRA_API mra_status mra_debug_replay(const mra_dims* dims, const void* q, const void* k, const void* v,
+                                    const uint8_t* mask, int32_t block_per_row, int32_t approx_mode,
+                                    int32_t prior_first, int32_t prior_diag, void* out, void* workspace,
+                                    size_t workspace_bytes, int32_t stage, int32_t count, void* stream) {
+    Layout L;
+    mra_status st = check_call(dims, q, k, v, mask, block_per_row, approx_mode, prior_first, prior_diag, out,
+                               workspace, workspace_bytes, true, &L);
+    if (st != MRA_OK) return st;
+    if ((stage != 3 && stage != 4) || count < 1) return MRA_ERR_STAGE;
+    const Params p = make_params(*dims, L, approx_mode, prior_first, prior_diag, q, k, v, mask, out, workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int32_t c = 0; c < count; c++)
+        if ((stage == 3 ? launch_attn(p, s) : launch_finish(p, s)) != hipSuccess) return MRA_ERR_HIP;
+    return MRA_OK;
 }
 
 MRA_API mra_status mra_debug_stages(const mra_dims* dims, const void* q, const void* k, const void* v,

@@ -64,7 +64,8 @@ typedef enum {
     MRA_ERR_ALIAS = 9,      /* out overlaps an input or the workspace */
     MRA_ERR_WORKSPACE = 10, /* workspace NULL or smaller than mra_workspace_size() */
     MRA_ERR_HIP = 11,       /* a HIP call failed */
-    MRA_ERR_ALIGN = 12      /* a tensor pointer is not 16-byte aligned */
+    MRA_ERR_ALIGN = 12,     /* a tensor pointer is not 16-byte aligned */
+    MRA_ERR_STAGE = 13      /* mra_debug_replay: a stage other than 3 or 4, or count < 1 */
 } mra_status;
 
 typedef enum { MRA_F32 = 0, MRA_BF16 = 1 } mra_dtype;
@@ -145,6 +146,19 @@ mra_status mra_debug_stages(const mra_dims* dims, const void* q, const void* k, 
 mra_status mra_debug_select(const mra_dims* dims, const float* logits, const int32_t* count,
                             int32_t block_per_row, int32_t prior_first, int32_t prior_diag,
                             int32_t* sel, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Timing hook: relaunches one stage of the forward pass `count` times in a
+ * row on `stream`, on a workspace that a call of mra_attention_fwd with the
+ * same arguments has filled (stream order: after that call).  Only the two
+ * stages that read nothing they write are accepted: 3 (block attention) and
+ * 4 (join of cut rows with the low-res part); each relaunch rewrites the same
+ * output.  A pair of events around the call then times the kernel alone,
+ * with no event between its launches.  The arguments are checked as for
+ * mra_attention_fwd; MRA_ERR_STAGE for another stage or count < 1. */
+mra_status mra_debug_replay(const mra_dims* dims, const void* q, const void* k, const void* v,
+                            const uint8_t* mask, int32_t block_per_row, int32_t approx_mode,
+                            int32_t prior_first, int32_t prior_diag, void* out, void* workspace,
+                            size_t workspace_bytes, int32_t stage, int32_t count, void* stream);
 
 #ifdef __cplusplus
 }

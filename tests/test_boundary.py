@@ -23,7 +23,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     L = mra.lib()
     names = declared_functions()
-    assert len(names) == 8
+    assert len(names) == 9
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(mra.SIGNATURES)
@@ -31,7 +31,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for s in range(0, 13):
+    for s in range(0, 14):
         assert mra.lib().mra_status_string(s)
     assert mra.lib().mra_status_string(99) == b"unknown status"
 
@@ -107,6 +107,18 @@ def test_debug_select_rejects_bad_arguments():
     assert L.mra_debug_select(ctypes.byref(d), Q, K, 4, 0, 0, O, W, 16, None) == 10
     assert L.mra_debug_select(ctypes.byref(d), Q, K, 0, 0, 0, O, W, 1 << 40, None) == 7
     assert L.mra_debug_select(ctypes.byref(d), Q, K, 4, -1, 0, O, W, 1 << 40, None) == 8
+
+
+def test_debug_replay_rejects_bad_arguments():
+    L = mra.lib()
+    d = mra._Dims(1, 2, 512, 64, 1)
+    args = lambda stage, count, ws_bytes=1 << 40: (ctypes.byref(d), Q, K, V, None, 4, 0, 0, 0, O, W, ws_bytes,
+                                                   stage, count, None)
+    for stage in (0, 1, 2, 5, -1):
+        assert L.mra_debug_replay(*args(stage, 1)) == 13
+    assert L.mra_debug_replay(*args(3, 0)) == 13
+    assert L.mra_debug_replay(*args(3, 1, 16)) == 10
+    assert L.mra_debug_replay(ctypes.byref(d), Q, K, V, None, 4, 0, 0, 0, None, W, 1 << 40, 3, 1, None) == 1
 
 
 def test_binding_refuses_cpu_tensors():
