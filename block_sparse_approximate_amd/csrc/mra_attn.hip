@@ -12,7 +12,9 @@
 // its SIMD does the same half a batch out of step.
 //
 // Per key block j of a segment of query block row i:
-//   S^T = K_j Q_i^T           4 x MFMA 32x32x16 bf16 (fp32: 32 x 32x32x2 f32)
+//   S^T = K_j Q_i^T           4 x MFMA 32x32x16 bf16 (fp32: 32 x 32x32x2 f32);
+//                             bf16 K_j is loaded straight into LDS as whole
+//                             rows and read back in the operand layout
 //   online max / exp2 / sum   in registers: lane l holds query l%32 and 16 of
 //                             its 32 keys, so row reductions need one swap
 //                             with lane l^32
@@ -50,6 +52,10 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+// 16 bytes of a K, V or Q row.  A native vector, so copies are plain loads and
+// stores (HIP's uint4 struct is copied with memcpy, which can keep a batch's
+// register slots in scratch memory).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kWaves = 4;
@@ -64,7 +70,7 @@ constexpr float kLazyMax = 8.0f;   // log2 headroom of the running max (probabil
 constexpr int kMaxRun = kWindow - kChunk - kChunk / 2;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 __device__ __forceinline__ int rl(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
 
 // key index held by accumulator register r of a 32x32 MFMA tile in lane l
@@ -86,23 +92,49 @@ __device__ __forceinline__ int nearest_segment_start(int x, uint32_t info, int64
 
 template <int DT> struct Cfg;
 template <> struct Cfg<1> {                 // bf16: 16 bytes per lane per 8 elements
-    static constexpr int kBatch = 2;        // blocks whose loads are in flight together (3 spills registers)
-    static constexpr int kKV = 4;           // uint4 per lane for one K (or V) block
+    static constexpr int kBatch = 2;        // blocks whose loads are in flight together
+    static constexpr int kKV = 4;           // 16-byte pieces per lane for one V (or Q) block
+    static constexpr bool kKDirect = true;  // K goes straight from memory to LDS
     using Elem = uint16_t;
     static constexpr int kStride = kVStrideB;
 };
 template <> struct Cfg<0> {                 // fp32: twice the registers per block
     static constexpr int kBatch = 1;
     static constexpr int kKV = 8;
+    static constexpr bool kKDirect = false;
     using Elem = float;
     static constexpr int kStride = kVStrideF;
 };
 
+// bf16 K block in LDS: 32 token rows of 128 bytes, the 16-byte chunk c of row
+// r at position c ^ ((r / 2) mod 8) of the row.  The direct loads place the
+// chunks so (whole rows per 8 lanes, i.e. full cache lines), and the MFMA
+// operand reads (lane: one row, one chunk) then hit distinct banks in each
+// 16-lane phase.
+__device__ __forceinline__ int k_swz(int row, int chunk) { return row * kHeadDim + ((chunk ^ (row >> 1)) & 7) * 8; }
+
+// Per-wave LDS.  bf16: the K blocks of a batch (k_swz), V_j (read back
+// transposed) and Q_i; fp32: V_j.
+template <int DT> struct StageBuf;
+template <> struct StageBuf<1> {
+    uint16_t kring[Cfg<1>::kBatch][kBlock * kHeadDim];
+    uint16_t v[kBlock * kVStrideB];
+    uint16_t qs[kBlock * kKStrideB];
+};
+template <> struct StageBuf<0> {
+    float v[kBlock * kVStrideF];
+};
+
+// The attention kernel's dynamic LDS: kWaves StageBufs.  The direct loads
+// address it through this symbol, so that the compiler sees they write LDS
+// only (and can keep a batch's register slots in registers).
+extern __shared__ __align__(16) unsigned char attn_smem[];
+
 template <int DT>
 struct Slot {
-    uint4 k[Cfg<DT>::kKV];
-    uint4 v[Cfg<DT>::kKV];
-    uint4 q[Cfg<DT>::kKV];   // Q of the block's row
+    u32x4 k[Cfg<DT>::kKDirect ? 1 : Cfg<DT>::kKV];   // (unused when K goes straight to LDS)
+    u32x4 v[Cfg<DT>::kKV];
+    u32x4 q[Cfg<DT>::kKV];   // Q of the block's row
     uint32_t qm;             // and its mask word
     float vh;                // full mode: vhat_j[lane]
     float lo;                // full mode: lo_all_i[lane]
@@ -116,6 +148,7 @@ struct Wave {
     float ww, wm, wll;
     int a;
     int bh, b, nb, lane, n, h;
+    int wave;                // the wave's index in its workgroup (its StageBuf)
     const typename Cfg<DT>::Elem* Qg;
     const typename Cfg<DT>::Elem* Kg;
     const typename Cfg<DT>::Elem* Vg;
@@ -128,7 +161,8 @@ __device__ __forceinline__ int rec_i(uint32_t ij) { return (int)(ij & 0xFFFFu); 
 __device__ __forceinline__ int rec_j(uint32_t ij) { return (int)(ij >> 16); }
 
 template <int DT, bool FULL>
-__device__ __forceinline__ void issue(const Params& p, const Wave<DT>& W, int e, Slot<DT>& s) {
+__device__ __forceinline__ void issue(const Params& p, const Wave<DT>& W, int e, Slot<DT>& s, StageBuf<DT>& sb,
+                                      int u) {
     const int we = e - W.a;
     const uint32_t ij = (uint32_t)rl((int)W.wij, we);
     const int i = min(rec_i(ij), W.nb - 1);
@@ -139,29 +173,39 @@ __device__ __forceinline__ void issue(const Params& p, const Wave<DT>& W, int e,
         const uint16_t* Vb = W.Vg + (size_t)j * kBlock * kHeadDim;
         const uint16_t* Qb = W.Qg + (size_t)i * kBlock * kHeadDim;
         const int off = (lane >> 3) * kHeadDim + (lane & 7) * 8;
-        // K_j straight into the MFMA operand layout: token n, channels 16 kc + 8 h .. +7
+        // K_j straight into LDS slot u, 1 KiB (8 whole token rows) per load:
+        // lane l fetches the chunk that belongs at position l % 8 of row
+        // 8x + l / 8 (a load of every row's 32-byte operand piece instead
+        // would cost the address unit several times more)
+        typedef __attribute__((address_space(3))) void lds_void;
+        const size_t kbase = (size_t)W.wave * sizeof(StageBuf<1>) + offsetof(StageBuf<1>, kring) +
+                             (size_t)u * sizeof(sb.kring[0]);
 #pragma unroll
-        for (int kc = 0; kc < 4; kc++) s.k[kc] = *reinterpret_cast<const uint4*>(Kb + n * kHeadDim + 16 * kc + 8 * h);
+        for (int x = 0; x < 4; x++) {
+            const int r = 8 * x + (lane >> 3), c = ((lane & 7) ^ (r >> 1)) & 7;
+            __builtin_amdgcn_global_load_lds(Kb + r * kHeadDim + 8 * c, (lds_void*)(attn_smem + kbase + x * 1024), 16,
+                                             0, 0);
+        }
 #pragma unroll
-        for (int x = 0; x < 4; x++) s.v[x] = *reinterpret_cast<const uint4*>(Vb + off + 8 * x * kHeadDim);
+        for (int x = 0; x < 4; x++) s.v[x] = *reinterpret_cast<const u32x4*>(Vb + off + 8 * x * kHeadDim);
         // V_j and Q_i: whole 128-byte token rows per 8 lanes, so every load
         // is 8 full cache lines; Q_i once per segment, by its first block
         // (the other blocks leave s.q unset: only a segment's first block reads it)
         if (info_pos((uint32_t)rl((int)W.winfo, we)) == 0) {
 #pragma unroll
-            for (int x = 0; x < 4; x++) s.q[x] = *reinterpret_cast<const uint4*>(Qb + off + 8 * x * kHeadDim);
+            for (int x = 0; x < 4; x++) s.q[x] = *reinterpret_cast<const u32x4*>(Qb + off + 8 * x * kHeadDim);
         }
     } else {
         const float* Kb = W.Kg + (size_t)j * kBlock * kHeadDim;
         const float* Vb = W.Vg + (size_t)j * kBlock * kHeadDim;
         const float* Qb = W.Qg + (size_t)i * kBlock * kHeadDim;
 #pragma unroll
-        for (int c4 = 0; c4 < 8; c4++) s.k[c4] = *reinterpret_cast<const uint4*>(Kb + n * kHeadDim + 32 * h + 4 * c4);
+        for (int c4 = 0; c4 < 8; c4++) s.k[c4] = *reinterpret_cast<const u32x4*>(Kb + n * kHeadDim + 32 * h + 4 * c4);
 #pragma unroll
         for (int x = 0; x < 8; x++)
-            s.v[x] = *reinterpret_cast<const uint4*>(Vb + ((lane >> 4) + 4 * x) * kHeadDim + (lane & 15) * 4);
+            s.v[x] = *reinterpret_cast<const u32x4*>(Vb + ((lane >> 4) + 4 * x) * kHeadDim + (lane & 15) * 4);
 #pragma unroll
-        for (int c4 = 0; c4 < 8; c4++) s.q[c4] = *reinterpret_cast<const uint4*>(Qb + n * kHeadDim + 32 * h + 4 * c4);
+        for (int c4 = 0; c4 < 8; c4++) s.q[c4] = *reinterpret_cast<const u32x4*>(Qb + n * kHeadDim + 32 * h + 4 * c4);
     }
     s.qm = p.mbits[(size_t)W.b * W.nb + i];
     if constexpr (FULL) {
@@ -255,7 +299,8 @@ __device__ __forceinline__ void finish_segment(const Params& p, const Wave<DT>& 
 // One block of the stream: S^T, online softmax, O^T += V^T P^T.
 template <int DT, bool FULL>
 __device__ __forceinline__ void process(const Params& p, const Wave<DT>& W, int e, Slot<DT>& s, Acc<DT>& A,
-                                        typename Cfg<DT>::Elem* vs, float scale2) {
+                                        StageBuf<DT>& sb, int u, float scale2) {
+    auto* vs = sb.v;
     const int we = e - W.a;
     const int i = min(rec_i((uint32_t)rl((int)W.wij, we)), W.nb - 1);
     const uint32_t kb = (uint32_t)rl((int)W.wk, we);
@@ -278,30 +323,31 @@ __device__ __forceinline__ void process(const Params& p, const Wave<DT>& W, int 
     for (int r = 0; r < 16; r++) S[r] = 0.f;
     if constexpr (DT == 1) {
         // stage V_j (and Q_i when the segment starts) in this wave's LDS
-        // region; Q is read back one token row per lane (the MFMA operand
-        // layout: lane l holds token l % 32, channels 16 kc + 8 (l / 32))
-        uint16_t* qs = vs + kBlock * kVStrideB;
+        // region; K_j (already in slot u) and Q are read back one token row
+        // per lane (the MFMA operand layout: lane l holds token l % 32,
+        // channels 16 kc + 8 (l / 32))
+        uint16_t* qs = sb.qs;
 #pragma unroll
         for (int x = 0; x < 4; x++)
-            *reinterpret_cast<uint4*>(vs + ((lane >> 3) + 8 * x) * kVStrideB + (lane & 7) * 8) = s.v[x];
+            *reinterpret_cast<u32x4*>(vs + ((lane >> 3) + 8 * x) * kVStrideB + (lane & 7) * 8) = s.v[x];
         if (info_pos(info) == 0) {
 #pragma unroll
             for (int x = 0; x < 4; x++)
-                *reinterpret_cast<uint4*>(qs + ((lane >> 3) + 8 * x) * kKStrideB + (lane & 7) * 8) = s.q[x];
+                *reinterpret_cast<u32x4*>(qs + ((lane >> 3) + 8 * x) * kKStrideB + (lane & 7) * 8) = s.q[x];
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
         for (int kc = 0; kc < 4; kc++) {
-            const uint4 ka = s.k[kc];
-            const uint4 qa = *reinterpret_cast<const uint4*>(qs + n * kKStrideB + 16 * kc + 8 * h);
+            const u32x4 ka = *reinterpret_cast<const u32x4*>(sb.kring[u] + k_swz(n, 2 * kc + h));
+            const u32x4 qa = *reinterpret_cast<const u32x4*>(qs + n * kKStrideB + 16 * kc + 8 * h);
             S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka), as_bf16x8(qa), S, 0, 0, 0);
         }
     } else {
 #pragma unroll
         for (int x = 0; x < 8; x++)
-            *reinterpret_cast<uint4*>(vs + ((lane >> 4) + 4 * x) * kVStrideF + (lane & 15) * 4) = s.v[x];
+            *reinterpret_cast<u32x4*>(vs + ((lane >> 4) + 4 * x) * kVStrideF + (lane & 15) * 4) = s.v[x];
 #pragma unroll
         for (int c4 = 0; c4 < 8; c4++) {
             const float4 kf = __builtin_bit_cast(float4, s.k[c4]);
@@ -387,16 +433,11 @@ __device__ __forceinline__ void process(const Params& p, const Wave<DT>& W, int 
         finish_segment<DT, FULL>(p, W, A, we, i, info, s, reinterpret_cast<float*>(vs));
 }
 
-// Per-wave LDS: V_j (read back transposed), and for bf16 also Q_i.
-template <int DT>
-struct StageBuf {
-    typename Cfg<DT>::Elem v[32 * Cfg<DT>::kStride + (DT == 1 ? 32 * kKStrideB : 0)];
-};
 
 // Range k of the WPH ranges of head bh's record stream, by one wave.
 template <int DT, bool FULL>
-__device__ __forceinline__ void run_range(const Params& p, int bh, int k, int WPH, int lane,
-                                          typename Cfg<DT>::Elem* vs) {
+__device__ __forceinline__ void run_range(const Params& p, int bh, int k, int WPH, int lane, int wave,
+                                          StageBuf<DT>& sb) {
     const int64_t K = p.K;
     const int a = (int)((int64_t)k * K / WPH);
     const int bnd = (int)((int64_t)(k + 1) * K / WPH);
@@ -410,6 +451,7 @@ __device__ __forceinline__ void run_range(const Params& p, int bh, int k, int WP
     W.b = bh / p.H;
     W.nb = p.nb;
     W.lane = lane;
+    W.wave = wave;
     W.n = lane & 31;
     W.h = lane >> 5;
     {
@@ -462,19 +504,19 @@ __device__ __forceinline__ void run_range(const Params& p, int bh, int k, int WP
     for (int e0 = start; e0 < end; e0 += BATCH) {
         Slot<DT> sl[BATCH];
 #pragma unroll
-        for (int u = 0; u < BATCH; u++) issue<DT, FULL>(p, W, min(e0 + u, end - 1), sl[u]);
+        for (int u = 0; u < BATCH; u++) issue<DT, FULL>(p, W, min(e0 + u, end - 1), sl[u], sb, u);
         // keep the loads together: the scheduler must not sink them into the
         // compute of the batch
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < BATCH; u++)
-            if (e0 + u < end) process<DT, FULL>(p, W, e0 + u, sl[u], A, vs, scale2);
+            if (e0 + u < end) process<DT, FULL>(p, W, e0 + u, sl[u], A, sb, u, scale2);
     }
 }
 
 template <int DT, bool FULL>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(Params p) {
-    __shared__ __align__(16) StageBuf<DT> stage[kWaves];
+    StageBuf<DT>* stage = reinterpret_cast<StageBuf<DT>*>(attn_smem);   // one per wave
     const int xcd = blockIdx.x & 7;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int wx = (blockIdx.x >> 3) * kWaves + wave;      // wave index within its XCD
@@ -483,11 +525,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(Params p) {
         // every wave of the XCD takes range wx of each of the XCD's heads in
         // turn, so the XCD's L2 holds one head's K and V at a time
         if (wx >= WPH) return;
-        for (int bh = xcd; bh < p.BH; bh += 8) run_range<DT, FULL>(p, bh, wx, WPH, lane, stage[wave].v);
+        for (int bh = xcd; bh < p.BH; bh += 8) run_range<DT, FULL>(p, bh, wx, WPH, lane, wave, stage[wave]);
     } else {
         const int hm = wx / WPH;
         const int bh = xcd + 8 * hm;
-        if (bh < p.BH) run_range<DT, FULL>(p, bh, wx - hm * WPH, WPH, lane, stage[wave].v);
+        if (bh < p.BH) run_range<DT, FULL>(p, bh, wx - hm * WPH, WPH, lane, wave, stage[wave]);
     }
 }
 
@@ -513,19 +555,25 @@ int attn_grid_waves_per_head(int BH, int64_t K) {
     return (int)w;
 }
 
+// Launch one instantiation with kWaves stage buffers of dynamic LDS (bf16
+// needs more than the 64 KiB of static LDS); the size attribute is set once.
+template <int DT, bool FULL>
+static hipError_t launch_attn_t(const Params& p, unsigned grid, hipStream_t s) {
+    constexpr size_t kLds = kWaves * sizeof(StageBuf<DT>);
+    static const hipError_t a = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_kernel<DT, FULL>),
+                                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+    if (a != hipSuccess) return a;
+    hipLaunchKernelGGL((attn_kernel<DT, FULL>), dim3(grid), dim3(kThreads), kLds, s, p);
+    return hipGetLastError();
+}
+
 hipError_t launch_attn(const Params& p, hipStream_t s) {
     const int heads_per_xcd = (p.BH + 7) / 8;
     const int64_t waves_per_xcd = p.attn_seq ? p.attn_wph : (int64_t)heads_per_xcd * p.attn_wph;
-    const int64_t grid = 8 * ((waves_per_xcd + kWaves - 1) / kWaves);
+    const unsigned grid = (unsigned)(8 * ((waves_per_xcd + kWaves - 1) / kWaves));
     const bool full = p.mode == 0;
-    if (p.dtype == 1) {
-        if (full) hipLaunchKernelGGL((attn_kernel<1, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
-        else hipLaunchKernelGGL((attn_kernel<1, false>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
-    } else {
-        if (full) hipLaunchKernelGGL((attn_kernel<0, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
-        else hipLaunchKernelGGL((attn_kernel<0, false>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
-    }
-    return hipGetLastError();
+    if (p.dtype == 1) return full ? launch_attn_t<1, true>(p, grid, s) : launch_attn_t<1, false>(p, grid, s);
+    return full ? launch_attn_t<0, true>(p, grid, s) : launch_attn_t<0, false>(p, grid, s);
 }
 
 }  // namespace mra
