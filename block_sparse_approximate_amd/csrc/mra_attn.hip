@@ -135,9 +135,9 @@ struct Slot {
     u32x4 k[Cfg<DT>::kKDirect ? 1 : Cfg<DT>::kKV];   // (unused when K goes straight to LDS)
     u32x4 v[Cfg<DT>::kKV];
     u32x4 q[Cfg<DT>::kKV];   // Q of the block's row
-    uint32_t qm;             // and its mask word
+    uint32_t qm;             // and its mask word (segment's first block)
     float vh;                // full mode: vhat_j[lane]
-    float lo;                // full mode: lo_all_i[lane]
+    float lo;                // full mode: lo_all_i[lane] (segment's first block)
 };
 
 template <int DT>
@@ -154,9 +154,9 @@ struct Wave {
     const typename Cfg<DT>::Elem* Vg;
 };
 
-// Issue the loads of stream block e into a batch slot: K_j, V_j, Q_i when
-// the block starts a segment, the mask word of row i, and in full mode
-// vhat_j and lo_all_i at this lane's channel.
+// Issue the loads of stream block e into a batch slot: K_j, V_j, vhat_j at
+// this lane's channel (full mode), and when the block starts a segment Q_i,
+// the mask word of row i and lo_all_i at this lane's channel (full mode).
 __device__ __forceinline__ int rec_i(uint32_t ij) { return (int)(ij & 0xFFFFu); }
 __device__ __forceinline__ int rec_j(uint32_t ij) { return (int)(ij >> 16); }
 
@@ -207,11 +207,17 @@ __device__ __forceinline__ void issue(const Params& p, const Wave<DT>& W, int e,
 #pragma unroll
         for (int c4 = 0; c4 < 8; c4++) s.q[c4] = *reinterpret_cast<const u32x4*>(Qb + n * kHeadDim + 32 * h + 4 * c4);
     }
-    s.qm = p.mbits[(size_t)W.b * W.nb + i];
-    if constexpr (FULL) {
-        s.vh = p.vhat[((size_t)W.bh * W.nb + j) * kHeadDim + lane];
-        s.lo = p.lo_all[((size_t)W.bh * W.nb + i) * kHeadDim + lane];
+    // once per segment, by its first block: the row's mask word (uniform, so
+    // through the scalar cache) and in full mode lo_all_i; every block: vhat_j
+    typedef __attribute__((address_space(4))) const uint32_t const_u32;
+    if (info_pos((uint32_t)rl((int)W.winfo, we)) == 0) {
+        s.qm = *reinterpret_cast<const_u32*>((uintptr_t)(p.mbits + (size_t)W.b * W.nb + i));
+        if constexpr (FULL) s.lo = p.lo_all[((size_t)W.bh * W.nb + i) * kHeadDim + lane];
+    } else {
+        s.qm = 0u;
+        s.lo = 0.f;
     }
+    if constexpr (FULL) s.vh = p.vhat[((size_t)W.bh * W.nb + j) * kHeadDim + lane];
 }
 
 template <int DT>
@@ -220,6 +226,8 @@ struct Acc {
     float mrun, lsum;
     float corr;   // full mode: sum over the segment's blocks of w vhat_j[lane]
     float sw;     // full mode: sum of their weights w
+    float lo;     // full mode: lo_all_i[lane] of the segment's row
+    uint32_t qm;  // valid-token mask word of the segment's row
 };
 
 // Finish a segment: a whole row writes its output, otherwise a partial.
@@ -230,11 +238,11 @@ __device__ __forceinline__ void finish_segment(const Params& p, const Wave<DT>& 
     const float ltot = A.lsum + __shfl_xor(A.lsum, 32, 64);
     const int tok = i * kBlock + n;
     if (info_whole(info)) {
-        const bool valid = (s.qm >> n) & 1u;
+        const bool valid = (A.qm >> n) & 1u;
         float a = 1.f, bw = 0.f, den = ltot;
         if constexpr (FULL) {
             // low-res part of the row without the selected blocks, one channel per lane
-            lo_lds[W.lane] = s.lo - A.corr;
+            lo_lds[W.lane] = A.lo - A.corr;
             const float mi2 = __int_as_float(rl(__float_as_int(W.wm), we)) * kLog2e;
             const float ll = fmaxf(__int_as_float(rl(__float_as_int(W.wll), we)) - A.sw, 0.f);
             const float M = fmaxf(A.mrun, mi2);
@@ -308,9 +316,11 @@ __device__ __forceinline__ void process(const Params& p, const Wave<DT>& W, int 
     const int lane = W.lane, n = W.n, h = W.h;
     if (info_pos(info) == 0) {   // a segment starts: alpha = 0 below clears O and l
         A.mrun = -__builtin_inff();
+        A.qm = s.qm;
         if constexpr (FULL) {
             A.corr = 0.f;
             A.sw = 0.f;
+            A.lo = s.lo;
         }
     }
     if constexpr (FULL) {
