@@ -69,6 +69,8 @@ def lib():
         L.oracle_mra_fwd.restype = ctypes.c_int
         L.oracle_dense_fwd.argtypes = [i32, i32, i32, i32, P, P, P, P, P, i32]
         L.oracle_dense_fwd.restype = ctypes.c_int
+        L.oracle_mra_bwd.argtypes = [i32, i32, i32, i32, P, P, P, P, i32, i32, i32, i32, P, P, P, P, i32]
+        L.oracle_mra_bwd.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -178,6 +180,28 @@ def mra_forward(q, k, v, mask=None, block_per_row=4, approx_mode="full",
     if return_selection:
         return out, sel[:, :, :K]
     return out
+
+
+def mra_backward(q, k, v, dout, mask=None, block_per_row=4, approx_mode="full",
+                 prior_first=0, prior_diag=0, threads=None):
+    """Gradients of mra_forward's output with respect to q, k, v given
+    dout = dL/d out, with the selection held fixed ([MRA] step 3: the block
+    products' backward reuses the kernels on transposed indices).  All
+    [B, H, N, d]; returns (dq, dk, dv) fp64."""
+    q, k, v, g = _f32(q), _f32(k), _f32(v), _f32(dout)
+    B, H, N, d = q.shape
+    if num_block(N, block_per_row) < 0:
+        raise ValueError("invalid sequence length / block_per_row")
+    dq = np.zeros((B, H, N, d), np.float64)
+    dk = np.zeros_like(dq)
+    dv = np.zeros_like(dq)
+    m = _mask(mask)
+    rc = lib().oracle_mra_bwd(B, H, N, d, _p(q), _p(k), _p(v), _p(m), block_per_row, MODES[approx_mode],
+                              prior_first, prior_diag, _p(g), _p(dq), _p(dk), _p(dv),
+                              threads or default_threads())
+    if rc:
+        raise ValueError("oracle_mra_bwd failed: %d" % rc)
+    return dq, dk, dv
 
 
 def dense_forward(q, k, v, mask=None, threads=None):

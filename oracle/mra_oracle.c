@@ -1,5 +1,6 @@
 /*
- * mra_oracle.c — plain, slow CPU oracle for the MRA-2 forward pass.
+ * mra_oracle.c — plain, slow CPU oracle for the MRA-2 forward pass and its
+ * gradients.
  *
  * TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and the
  * cpu_baseline leg of bench.py may load this library.  The product path (the
@@ -419,6 +420,207 @@ static int oracle_dense_head(int32_t N, int32_t d, const float* q, const float* 
 }
 
 /* ------------------------------------------------------------------------ */
+/* Gradients of one (batch, head) unit of the forward pass above with respect
+ * to q, k and v, given dO = dL/d out.  [MRA] "第三步": the block products are
+ * autograd functions whose backward reuses the kernels on transposed block
+ * indices, so the selection (a top-k, step 2) is a constant of the backward
+ * pass; "第四步": in full mode the low-resolution branch is ordinary tensor
+ * code, so it is differentiated too, down through the block means.
+ *
+ * With the selection fixed, for a valid query token t of block row i:
+ *   out_t = (sum_u w_u v_u + sum_j W_j vhat_j) / (sum_u w_u + sum_j W_j),
+ *   w_u = e^{s_u}, s_u = tau q_t . k_u      (u: valid keys of selected blocks)
+ *   W_j = cnt_j e^{shat_ij}, shat_ij = tau qhat_i . khat_j
+ *                          (j: unselected non-empty blocks; full mode only)
+ * With Z the denominator, P_u = w_u / Z, Pi_j = W_j / Z, D_t = dO_t . out_t:
+ *   dv_u     += P_u dO_t                  dvhat_j  += Pi_j dO_t
+ *   ds_u      = P_u (dO_t . v_u - D_t)    dshat_ij  = Pi_j (dO_t . vhat_j - D_t)
+ *   dq_t     += tau ds_u k_u              dk_u     += tau ds_u q_t
+ *   dqhat_i  += tau dshat_ij khat_j       dkhat_j  += tau dshat_ij qhat_i
+ * and a block mean passes its gradient to each valid token of the block
+ * divided by the block's count.  Padded query rows (zero output) pass no
+ * gradient; empty blocks have zero means and no weight.
+ * dout: [N, d] fp32; dq, dk, dv: [N, d] fp64, overwritten. */
+static int oracle_mra_head_bwd(const head_args_t* a, const float* q, const float* k,
+                               const float* v, const uint8_t* mask, const float* dout,
+                               double* dq, double* dk, double* dv)
+{
+    const int32_t N = a->N, d = a->d, nb = N / MRA_BLOCK;
+    const int64_t K = oracle_num_block(N, a->block_per_row);
+    const double tau = 1.0 / sqrt((double)d);
+    const int full = a->mode == 0;
+    int rc = 0;
+
+    float* qh = (float*)malloc(sizeof(float) * (size_t)nb * d);
+    float* kh = (float*)malloc(sizeof(float) * (size_t)nb * d);
+    int32_t* cnt = (int32_t*)malloc(sizeof(int32_t) * (size_t)nb);
+    float* S = (float*)malloc(sizeof(float) * (size_t)nb * nb);
+    float* score = (float*)malloc(sizeof(float) * (size_t)nb * nb);
+    int32_t* sel = (int32_t*)malloc(sizeof(int32_t) * (size_t)(K > 0 ? K : 1));
+    uint8_t* chosen = (uint8_t*)calloc((size_t)nb * nb, 1);
+    double* qh64 = (double*)malloc(sizeof(double) * (size_t)nb * d);
+    double* kh64 = (double*)malloc(sizeof(double) * (size_t)nb * d);
+    double* vh64 = (double*)malloc(sizeof(double) * (size_t)nb * d);
+    double* dqh = (double*)calloc((size_t)nb * d, sizeof(double));
+    double* dkh = (double*)calloc((size_t)nb * d, sizeof(double));
+    double* dvh = (double*)calloc((size_t)nb * d, sizeof(double));
+    double* s_hi = (double*)malloc(sizeof(double) * (size_t)N);
+    double* s_lo = (double*)malloc(sizeof(double) * (size_t)nb);
+    double* o = (double*)malloc(sizeof(double) * (size_t)d);
+    if (!qh || !kh || !cnt || !S || !score || !sel || !chosen || !qh64 || !kh64 || !vh64 ||
+        !dqh || !dkh || !dvh || !s_hi || !s_lo || !o) {
+        rc = -2;
+        goto done;
+    }
+    memset(dq, 0, sizeof(double) * (size_t)N * d);
+    memset(dk, 0, sizeof(double) * (size_t)N * d);
+    memset(dv, 0, sizeof(double) * (size_t)N * d);
+
+    /* the forward's selection, made exactly as oracle_mra_head makes it */
+    oracle_pool_f32(N, d, q, mask, qh, cnt);
+    oracle_pool_f32(N, d, k, mask, kh, NULL);
+    oracle_lowres_logits_f32(nb, d, qh, kh, S);
+    oracle_scores_f32(nb, S, cnt, a->prior_first, a->prior_diag, NULL, score);
+    rc = oracle_select_top(nb, score, K, sel);
+    if (rc)
+        goto done;
+    for (int64_t r = 0; r < K; r++)
+        chosen[sel[r]] = 1;
+    oracle_pool_f64(N, d, q, mask, qh64);
+    oracle_pool_f64(N, d, k, mask, kh64);
+    oracle_pool_f64(N, d, v, mask, vh64);
+
+    for (int32_t i = 0; i < nb; i++) {
+        if (full)
+            for (int32_t j = 0; j < nb; j++) {
+                s_lo[j] = -INFINITY;
+                if (!chosen[(int64_t)i * nb + j] && cnt[j] > 0) {
+                    double dot = 0.0;
+                    for (int32_t c = 0; c < d; c++)
+                        dot += qh64[(int64_t)i * d + c] * kh64[(int64_t)j * d + c];
+                    s_lo[j] = tau * dot;
+                }
+            }
+        for (int32_t t = i * MRA_BLOCK; t < (i + 1) * MRA_BLOCK; t++) {
+            if (mask && !mask[t])
+                continue;
+            const float* g = dout + (int64_t)t * d;
+            double shift = -INFINITY;
+            for (int32_t j = 0; j < nb; j++) {
+                if (!chosen[(int64_t)i * nb + j])
+                    continue;
+                for (int32_t u = j * MRA_BLOCK; u < (j + 1) * MRA_BLOCK; u++) {
+                    s_hi[u] = -INFINITY;
+                    if (mask && !mask[u])
+                        continue;
+                    double dot = 0.0;
+                    for (int32_t c = 0; c < d; c++)
+                        dot += (double)q[(int64_t)t * d + c] * (double)k[(int64_t)u * d + c];
+                    s_hi[u] = tau * dot;
+                    if (s_hi[u] > shift)
+                        shift = s_hi[u];
+                }
+            }
+            if (full)
+                for (int32_t j = 0; j < nb; j++)
+                    if (s_lo[j] > shift)
+                        shift = s_lo[j];
+            if (shift == -INFINITY)
+                continue;
+            /* the forward quantities of token t: Z and out_t */
+            double Z = 0.0;
+            for (int32_t c = 0; c < d; c++)
+                o[c] = 0.0;
+            for (int32_t j = 0; j < nb; j++) {
+                if (!chosen[(int64_t)i * nb + j])
+                    continue;
+                for (int32_t u = j * MRA_BLOCK; u < (j + 1) * MRA_BLOCK; u++) {
+                    if (s_hi[u] == -INFINITY)
+                        continue;
+                    const double w = exp(s_hi[u] - shift);
+                    Z += w;
+                    for (int32_t c = 0; c < d; c++)
+                        o[c] += w * (double)v[(int64_t)u * d + c];
+                }
+            }
+            if (full)
+                for (int32_t j = 0; j < nb; j++) {
+                    if (s_lo[j] == -INFINITY)
+                        continue;
+                    const double w = (double)cnt[j] * exp(s_lo[j] - shift);
+                    Z += w;
+                    for (int32_t c = 0; c < d; c++)
+                        o[c] += w * vh64[(int64_t)j * d + c];
+                }
+            if (!(Z > 0.0))
+                continue;
+            double D = 0.0;
+            for (int32_t c = 0; c < d; c++) {
+                o[c] /= Z;
+                D += (double)g[c] * o[c];
+            }
+            /* high-resolution terms */
+            for (int32_t j = 0; j < nb; j++) {
+                if (!chosen[(int64_t)i * nb + j])
+                    continue;
+                for (int32_t u = j * MRA_BLOCK; u < (j + 1) * MRA_BLOCK; u++) {
+                    if (s_hi[u] == -INFINITY)
+                        continue;
+                    const double P = exp(s_hi[u] - shift) / Z;
+                    double dP = 0.0;
+                    for (int32_t c = 0; c < d; c++)
+                        dP += (double)g[c] * (double)v[(int64_t)u * d + c];
+                    const double ds = P * (dP - D);
+                    for (int32_t c = 0; c < d; c++) {
+                        dv[(int64_t)u * d + c] += P * (double)g[c];
+                        dq[(int64_t)t * d + c] += tau * ds * (double)k[(int64_t)u * d + c];
+                        dk[(int64_t)u * d + c] += tau * ds * (double)q[(int64_t)t * d + c];
+                    }
+                }
+            }
+            /* low-resolution terms (full mode), onto the block means */
+            if (full)
+                for (int32_t j = 0; j < nb; j++) {
+                    if (s_lo[j] == -INFINITY)
+                        continue;
+                    const double Pi = (double)cnt[j] * exp(s_lo[j] - shift) / Z;
+                    double dPi = 0.0;
+                    for (int32_t c = 0; c < d; c++)
+                        dPi += (double)g[c] * vh64[(int64_t)j * d + c];
+                    const double ds = Pi * (dPi - D);
+                    for (int32_t c = 0; c < d; c++) {
+                        dvh[(int64_t)j * d + c] += Pi * (double)g[c];
+                        dqh[(int64_t)i * d + c] += tau * ds * kh64[(int64_t)j * d + c];
+                        dkh[(int64_t)j * d + c] += tau * ds * qh64[(int64_t)i * d + c];
+                    }
+                }
+        }
+    }
+    /* a block mean's gradient goes to each valid token of the block / cnt */
+    if (full)
+        for (int32_t b = 0; b < nb; b++) {
+            if (cnt[b] <= 0)
+                continue;
+            const double inv = 1.0 / (double)cnt[b];
+            for (int32_t t = b * MRA_BLOCK; t < (b + 1) * MRA_BLOCK; t++) {
+                if (mask && !mask[t])
+                    continue;
+                for (int32_t c = 0; c < d; c++) {
+                    dq[(int64_t)t * d + c] += dqh[(int64_t)b * d + c] * inv;
+                    dk[(int64_t)t * d + c] += dkh[(int64_t)b * d + c] * inv;
+                    dv[(int64_t)t * d + c] += dvh[(int64_t)b * d + c] * inv;
+                }
+            }
+        }
+
+done:
+    free(qh); free(kh); free(cnt); free(S); free(score); free(sel); free(chosen);
+    free(qh64); free(kh64); free(vh64); free(dqh); free(dkh); free(dvh);
+    free(s_hi); free(s_lo); free(o);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Batched drivers: independent (batch, head) units spread over nthreads
  * POSIX threads.  Each unit is computed by exactly the code above; the
  * threads only decide which unit runs where. */
@@ -431,6 +633,9 @@ typedef struct {
     int32_t* sel;
     int64_t K;
     int dense;
+    int bwd;           /* gradients: dout in, dq / dk / dv out */
+    const float* dout;
+    double *dq, *dk, *dv;
     int next; /* shared unit counter */
     int rc;
 } job_t;
@@ -447,7 +652,10 @@ static void* worker(void* p)
         int64_t off = (int64_t)u * j->N * j->d;
         const uint8_t* m = j->mask ? j->mask + (int64_t)b * j->N : NULL;
         int rc;
-        if (j->dense)
+        if (j->bwd)
+            rc = oracle_mra_head_bwd(&j->ha, j->q + off, j->k + off, j->v + off, m, j->dout + off,
+                                     j->dq + off, j->dk + off, j->dv + off);
+        else if (j->dense)
             rc = oracle_dense_head(j->N, j->d, j->q + off, j->k + off, j->v + off, m,
                                    j->out + off);
         else
@@ -509,5 +717,28 @@ int oracle_dense_fwd(int32_t B, int32_t H, int32_t N, int32_t d, const float* q,
     j.B = B; j.H = H; j.N = N; j.d = d;
     j.q = q; j.k = k; j.v = v; j.mask = mask;
     j.out = out; j.dense = 1;
+    return run_jobs(&j, nthreads);
+}
+
+/* Gradients of the MRA-2 forward over [B, H, N, d] inputs with respect to
+ * q, k and v (oracle_mra_head_bwd), given dout = dL/d out.  Returns 0, or -1
+ * for invalid arguments, -2 when out of memory. */
+int oracle_mra_bwd(int32_t B, int32_t H, int32_t N, int32_t d, const float* q,
+                   const float* k, const float* v, const uint8_t* mask,
+                   int32_t block_per_row, int32_t mode, int32_t prior_first,
+                   int32_t prior_diag, const float* dout, double* dq, double* dk,
+                   double* dv, int32_t nthreads)
+{
+    int64_t K = oracle_num_block(N, block_per_row);
+    if (B < 1 || H < 1 || d < 1 || K < 0 || (mode != 0 && mode != 1) ||
+        prior_first < 0 || prior_diag < 0 || !q || !k || !v || !dout || !dq || !dk || !dv)
+        return -1;
+    job_t j;
+    memset(&j, 0, sizeof(j));
+    j.B = B; j.H = H; j.N = N; j.d = d;
+    j.q = q; j.k = k; j.v = v; j.mask = mask;
+    j.ha.N = N; j.ha.d = d; j.ha.block_per_row = block_per_row; j.ha.mode = mode;
+    j.ha.prior_first = prior_first; j.ha.prior_diag = prior_diag;
+    j.K = K; j.bwd = 1; j.dout = dout; j.dq = dq; j.dk = dk; j.dv = dv;
     return run_jobs(&j, nthreads);
 }

@@ -41,12 +41,22 @@ MUTANTS = {
                                                          "oracle_pool_f64(N, d, k, mask, vh64);"),
     "padded query rows not zeroed": ("if (mask && !mask[t])\n                continue; /* reading R12",
                                      "if (0)\n                continue; /* reading R12"),
+    "backward drops D_t": ("const double ds = P * (dP - D);", "const double ds = P * dP;"),
+    "backward drops tau on dk": ("dk[(int64_t)u * d + c] += tau * ds * (double)q[(int64_t)t * d + c];",
+                                 "dk[(int64_t)u * d + c] += ds * (double)q[(int64_t)t * d + c];"),
+    "backward skips the mean's 1/cnt": ("const double inv = 1.0 / (double)cnt[b];", "const double inv = 1.0;"),
+    "backward low-res query gradient uses qhat": (
+        "dqh[(int64_t)i * d + c] += tau * ds * kh64[(int64_t)j * d + c];",
+        "dqh[(int64_t)i * d + c] += tau * ds * qh64[(int64_t)i * d + c];"),
+    "backward drops the low-res value gradient": ("dvh[(int64_t)j * d + c] += Pi * (double)g[c];", ""),
 }
 
 
 def run_mutant(name, old, new, tmp):
     src = open(SRC).read()
-    assert src.count(old) == 1, "mutation anchor for %r not found exactly once" % name
+    # an expression the backward recomputes from the forward appears in both:
+    # the mistake is planted wherever it is written
+    assert src.count(old) >= 1, "mutation anchor for %r not found" % name
     path = os.path.join(tmp, "m%d.c" % abs(hash(name)))
     open(path, "w").write(src.replace(old, new))
     so = path[:-2] + ".so"

@@ -369,3 +369,105 @@ def test_selection_reading_on_named_workload_ties():
     prior = (np.abs(ii - jj) <= 1) | (ii < 2) | (jj < 2)
     assert np.all(prior)
     assert (sc > 2500).sum() == 884      # logit spread is far below the 5000 bias
+
+
+# ------------------------------------------------------------- gradients --
+# The oracle's backward (oracle_mra_bwd): gradients of the forward with the
+# selection held fixed ([MRA] step 3), through the low-res branch and the block
+# means in full mode ([MRA] step 4).
+def sdpa64_grads(q, k, v, dout, allowed=None):
+    """torch fp64 CPU autograd of softmax(q k^T / sqrt(d)) v against dout."""
+    tq, tk, tv = (torch.from_numpy(np.asarray(x, np.float64)).requires_grad_(True) for x in (q, k, v))
+    m = None if allowed is None else torch.from_numpy(allowed)
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=m)
+    out.backward(torch.from_numpy(np.asarray(dout, np.float64)))
+    return tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+def rand_dout(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape).astype(np.float32)
+
+
+@pytest.mark.parametrize("mode", ["full", "sparse"])
+def test_bwd_all_blocks_selected_equals_dense_autograd(mode):
+    N, bpr = 128, 4
+    q, k, v = rand_qkv(1, 2, N, seed=41)
+    g = rand_dout(q.shape, 42)
+    assert oracle.num_block(N, bpr) == (N // 32) ** 2
+    got = oracle.mra_backward(q, k, v, g, block_per_row=bpr, approx_mode=mode)
+    for a, b in zip(got, sdpa64_grads(q, k, v, g)):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-11)
+
+
+def test_bwd_all_pairs_selected_with_mask_equals_masked_dense_autograd():
+    N = 128
+    q, k, v = rand_qkv(2, 1, N, seed=43)
+    mask = np.ones((2, N), np.uint8)
+    mask[0, 100:] = 0
+    mask[1, ::5] = 0
+    g = rand_dout(q.shape, 44)
+    g[mask[:, None, :] == 0] = 0.0            # padded rows output 0: no gradient flows from them
+    allowed = np.broadcast_to(mask[:, None, None, :].astype(bool), (2, 1, N, N)).copy()
+    ref = sdpa64_grads(q, k, v, g, allowed)
+    for mode in ("full", "sparse"):
+        got = oracle.mra_backward(q, k, v, g, mask, block_per_row=4, approx_mode=mode)
+        for a, b in zip(got, ref):
+            np.testing.assert_allclose(a, b, rtol=0, atol=1e-11)
+
+
+def test_bwd_priors_only_sparse_equals_block_masked_dense_autograd():
+    N = 512
+    q, k, v = rand_qkv(1, 1, N, seed=45)
+    g = rand_dout(q.shape, 46)
+    got = oracle.mra_backward(q, k, v, g, block_per_row=7, approx_mode="sparse", prior_first=4)
+    blk = np.arange(N) // 32
+    allowed = (blk[:, None] < 4) | (blk[None, :] < 4)
+    assert oracle.num_block(N, 7) == int(allowed[::32, ::32].sum())
+    for a, b in zip(got, sdpa64_grads(q, k, v, g, allowed)):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-11)
+
+
+@pytest.mark.parametrize("mode", ["full", "sparse"])
+def test_bwd_value_gradients_sum_to_output_gradients(mode):
+    # every valid output row is a convex combination of values (and, in full
+    # mode, of block means whose weights each spread 1/cnt over cnt tokens),
+    # so the value gradients of one head sum to its rows' output gradients
+    N = 256
+    q, k, v = rand_qkv(2, 2, N, seed=47)
+    mask = np.ones((2, N), np.uint8)
+    mask[1, 150:] = 0
+    g = rand_dout(q.shape, 48)
+    _, _, dv = oracle.mra_backward(q, k, v, g, mask, block_per_row=2, approx_mode=mode)
+    want = (g.astype(np.float64) * mask[:, None, :, None]).sum(axis=2)
+    np.testing.assert_allclose(dv.sum(axis=2), want, rtol=0, atol=1e-10)
+
+
+@pytest.mark.parametrize("mode", ["full", "sparse"])
+def test_bwd_matches_central_differences(mode):
+    # loss = sum(out * g) with the fp64 forward oracle; central differences on
+    # sampled coordinates where the selection stays the same
+    B, H, N, d = 1, 1, 128, 8
+    rng = np.random.default_rng(49)
+    q, k, v = (rng.standard_normal((B, H, N, d)).astype(np.float32) for _ in range(3))
+    mask = np.ones((B, N), np.uint8)
+    mask[0, 120:] = 0                          # one partial block
+    g = rand_dout(q.shape, 50)
+    kw = dict(block_per_row=1, approx_mode=mode, prior_diag=1)
+    grads = oracle.mra_backward(q, k, v, g, mask, **kw)
+    _, sel0 = oracle.mra_forward(q, k, v, mask, return_selection=True, **kw)
+    checked = 0
+    for which in range(3):
+        for _ in range(10):
+            t, c = int(rng.integers(0, 120)), int(rng.integers(0, d))
+            vals = []
+            for sgn in (1, -1):
+                x = [q.copy(), k.copy(), v.copy()]
+                x[which][0, 0, t, c] = np.float32(x[which][0, 0, t, c] + sgn * np.float32(1e-3))
+                out, sel = oracle.mra_forward(*x, mask, return_selection=True, **kw)
+                vals.append((float((out * g).sum()), x[which][0, 0, t, c], np.array_equal(sel, sel0)))
+            if not (vals[0][2] and vals[1][2]):
+                continue
+            fd = (vals[0][0] - vals[1][0]) / (float(vals[0][1]) - float(vals[1][1]))
+            assert abs(fd - grads[which][0, 0, t, c]) <= 1e-5 * (1 + abs(fd)), (which, t, c, fd)
+            checked += 1
+    assert checked >= 24
