@@ -18,7 +18,7 @@ import os
 import torch
 
 __all__ = ["attention", "attention_profiled", "prepare", "num_block", "workspace_size", "debug_stages", "debug_select",
-           "debug_replay",
+           "debug_replay", "attention_backward",
            "MraError", "library_path", "lib"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -41,6 +41,8 @@ SIGNATURES = {
     "mra_debug_stages": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
                           _P, _SZ, _P], ctypes.c_int),
     "mra_debug_select": ([_P, _P, _P, _I32, _I32, _I32, _P, _P, _SZ, _P], ctypes.c_int),
+    "mra_attention_bwd": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P],
+                          ctypes.c_int),
     "mra_debug_replay": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _SZ, _I32, _I32, _P], ctypes.c_int),
 }
 
@@ -203,6 +205,30 @@ def attention_profiled(q, k, v, events, mask=None, block_per_row=4, approx_mode=
                                           workspace.numel(), _stream(q), arr)
     _check(st, "mra_attention_fwd_profiled")
     return out
+
+
+def attention_backward(q, k, v, out, dout, workspace, mask=None, block_per_row=4, approx_mode="sparse",
+                       initial_prior_first_n_blocks=0, initial_prior_diagonal_n_blocks=0, dq=None, dk=None,
+                       dv=None):
+    """Gradients (dq, dk, dv) of a forward call's output with respect to q, k,
+    v given dout.  `out` and `workspace` are that call's output and workspace
+    (the selection is read from it); the other arguments must be the ones it
+    was made with.  Sparse mode, bf16."""
+    _check_inputs(q, k, v, mask)
+    for t in (out, dout):
+        if not (t.is_cuda and t.dtype == q.dtype and t.shape == q.shape and t.is_contiguous()):
+            raise ValueError("out and dout must be contiguous device tensors shaped and typed like q")
+    B, H, N, d = q.shape
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    dims = _dims(B, H, N, d, DTYPES[q.dtype])
+    st = lib().mra_attention_bwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), block_per_row,
+                                 MODES.get(approx_mode, -1), initial_prior_first_n_blocks,
+                                 initial_prior_diagonal_n_blocks, _ptr(out), _ptr(dout), _ptr(dq), _ptr(dk),
+                                 _ptr(dv), _ptr(workspace), workspace.numel(), _stream(q))
+    _check(st, "mra_attention_bwd")
+    return dq, dk, dv
 
 
 def debug_replay(q, k, v, stage, count, mask=None, block_per_row=4, approx_mode="full",

@@ -29,6 +29,7 @@ UNITS = {
     "mra_select": ["-ffp-contract=off"],
     "mra_attn": [],
     "mra_finish": [],
+    "mra_bwd": [],
     "mra_api": [],
 }
 HEADERS = ["mra_common.h", os.path.join("..", "..", "include", "mra.h")]

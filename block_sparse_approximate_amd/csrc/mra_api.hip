@@ -58,6 +58,11 @@ bool carve(const mra_dims& d, int32_t bpr, int32_t mode, Layout* L) {
     L->part_corr = mode == MRA_APPROX_FULL ? take(BH * (size_t)L->max_items * kCorrStride * 4) : 0;
     L->cand = take(BH * (size_t)kSelCap * 8);
     L->ncand = take(BH * kCandStride * 4);
+    L->st_m = take(BH * (size_t)L->N * 4);
+    L->st_linv = take(BH * (size_t)L->N * 4);
+    L->st_d = take(BH * (size_t)L->N * 4);
+    L->ct_ptr = take(BH * (nb + 1) * 4);
+    L->ct_row = take(BH * (size_t)L->K * 4);
     L->total = o;
     return true;
 }
@@ -127,6 +132,11 @@ Params make_params(const mra_dims& d, const Layout& L, int32_t mode, int32_t pf,
     p.part_corr = L.part_corr ? reinterpret_cast<float*>(w + L.part_corr) : nullptr;
     p.cand = reinterpret_cast<uint64_t*>(w + L.cand);
     p.ncand = reinterpret_cast<uint32_t*>(w + L.ncand);
+    p.st_m = reinterpret_cast<float*>(w + L.st_m);
+    p.st_linv = reinterpret_cast<float*>(w + L.st_linv);
+    p.st_d = reinterpret_cast<float*>(w + L.st_d);
+    p.ct_ptr = reinterpret_cast<int32_t*>(w + L.ct_ptr);
+    p.ct_row = reinterpret_cast<int32_t*>(w + L.ct_row);
     p.error = reinterpret_cast<int32_t*>(w);
     return p;
 }
@@ -266,6 +276,39 @@ MRA_API mra_status mra_attention_fwd_profiled(const mra_dims* dims, const void* 
                                               size_t workspace_bytes, void* stream, void* const* events) {
     return run_forward(dims, q, k, v, mask, block_per_row, approx_mode, prior_first, prior_diag, out, workspace,
                        workspace_bytes, stream, events);
+}
+
+MRA_API mra_status mra_attention_bwd(const mra_dims* dims, const void* q, const void* k, const void* v,
+                                     const uint8_t* mask, int32_t block_per_row, int32_t approx_mode,
+                                     int32_t prior_first, int32_t prior_diag, const void* out, const void* dout,
+                                     void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+    Layout L;
+    mra_status st = check_call(dims, q, k, v, mask, block_per_row, approx_mode, prior_first, prior_diag, out,
+                               workspace, workspace_bytes, true, &L);
+    if (st != MRA_OK) return st;
+    if (approx_mode != MRA_APPROX_SPARSE) return MRA_ERR_MODE;
+    if (dims->dtype != MRA_BF16) return MRA_ERR_DTYPE;
+    if (!dout || !dq || !dk || !dv) return MRA_ERR_NULL;
+    if (misaligned(dout) || misaligned(dq) || misaligned(dk) || misaligned(dv)) return MRA_ERR_ALIGN;
+    const size_t tb = (size_t)dims->batch * dims->heads * dims->seq_len * dims->head_dim * 2;
+    const void* ins[] = {q, k, v, out, dout, workspace};
+    const size_t insz[] = {tb, tb, tb, tb, tb, workspace_bytes};
+    void* outs[] = {dq, dk, dv};
+    for (int a = 0; a < 3; a++) {
+        for (int c = 0; c < 6; c++)
+            if (overlaps(outs[a], tb, ins[c], insz[c])) return MRA_ERR_ALIAS;
+        for (int c = a + 1; c < 3; c++)
+            if (overlaps(outs[a], tb, outs[c], tb)) return MRA_ERR_ALIAS;
+    }
+    Params p = make_params(*dims, L, approx_mode, prior_first, prior_diag, q, k, v, mask, const_cast<void*>(out),
+                           workspace);
+    p.fout = out;
+    p.dout = dout;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    return launch_bwd(p, static_cast<hipStream_t>(stream)) == hipSuccess ? MRA_OK : MRA_ERR_HIP;
 }
 
 MRA_API mra_status mra_debug_replay(const mra_dims* dims, const void* q, const void* k, const void* v,

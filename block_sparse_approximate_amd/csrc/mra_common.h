@@ -51,7 +51,8 @@ struct Layout {
     int64_t K;            // selection budget per (batch, head)
     int32_t max_items;    // segments per head, upper bound
     size_t qhat, khat, vhat, cnt, mbits, logits, keys, rowmax, hist, thresh, row_ptr, col, selbits, item_ptr, recs,
-        merge_rows, n_merge, lo_all, ll_all, part_o, part_ml, part_corr, cand, ncand, total;
+        merge_rows, n_merge, lo_all, ll_all, part_o, part_ml, part_corr, cand, ncand, st_m, st_linv, st_d,
+        ct_ptr, ct_row, total;
 };
 
 // Everything a kernel needs, passed by value.
@@ -92,6 +93,17 @@ struct Params {
     float* part_corr;      // [BH, max_items, kCorrStride] full mode: the segment's sum of w vhat_j, then of w
     uint64_t* cand;        // [BH, kSelCap] boundary-bin cells found by the pre-marking pass
     uint32_t* ncand;       // [BH, kCandStride] their number, in word 0 (cleared by the pooling kernel)
+    // backward (mra_attention_bwd)
+    const void* fout;      // [B, H, N, d] the forward's output
+    const void* dout;      // [B, H, N, d] dL/d out
+    void* dq;              // [B, H, N, d] gradients out
+    void* dk;
+    void* dv;
+    float* st_m;           // [BH, N] per query token: max of its scaled logits (log2 units), 0 if none
+    float* st_linv;        // [BH, N] 1 / sum of 2^(s - m) over its keys; 0 for padded or keyless tokens
+    float* st_d;           // [BH, N] dO . O (0 where st_linv is 0)
+    int32_t* ct_ptr;       // [BH, nb + 1] per key block: start of its list in ct_row
+    int32_t* ct_row;       // [BH, K] query block rows that selected each key block, ascending
     int32_t* error;        // device error flag (0 = fine)
     int32_t attn_wph;      // attention stream: waves sharing one head's blocks
     int32_t attn_seq;      // 1: those are all the waves of an XCD, which take the XCD's heads in turn
@@ -151,6 +163,7 @@ hipError_t launch_premark(const Params& p, hipStream_t s);
 hipError_t launch_select(const Params& p, hipStream_t s);
 hipError_t launch_attn(const Params& p, hipStream_t s);
 hipError_t launch_finish(const Params& p, hipStream_t s);
+hipError_t launch_bwd(const Params& p, hipStream_t s);
 int attn_grid_waves_per_head(int BH, int64_t K);
 bool attn_heads_in_turn(int BH, int64_t K);
 }  // namespace mra

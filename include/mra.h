@@ -1,5 +1,5 @@
 /*
- * mra.h — C ABI of the MI355X (gfx950) MRA-2 forward-pass library
+ * mra.h — C ABI of the MI355X (gfx950) MRA-2 forward (and backward) library
  * (libmra.so, built from block_sparse_approximate_amd/csrc).
  *
  * The method is MRA-2 multi-resolution approximate self-attention as
@@ -146,6 +146,27 @@ mra_status mra_debug_stages(const mra_dims* dims, const void* q, const void* k, 
 mra_status mra_debug_select(const mra_dims* dims, const float* logits, const int32_t* count,
                             int32_t block_per_row, int32_t prior_first, int32_t prior_diag,
                             int32_t* sel, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Gradients of the forward pass with respect to q, k and v ([MRA] "第三步":
+ * the block products' backward reuses the kernels on transposed block
+ * indices, so the block selection is a constant of the backward pass).
+ *   q, k, v, mask, block_per_row, approx_mode, priors: as for the forward
+ *             call whose selection is used;
+ *   out       [B, H, N, d] that call's output;
+ *   dout      [B, H, N, d] dL/d out;
+ *   dq, dk, dv [B, H, N, d] gradients, written (in the dtype of dims);
+ *   workspace the workspace that forward call filled (it holds the
+ *             selection), unchanged since; the backward also writes per-token
+ *             row statistics and the transposed selection there.
+ * Must be queued after that forward call (stream order).  Supported: sparse
+ * mode (MRA_ERR_MODE otherwise), bf16 (MRA_ERR_DTYPE otherwise).  dq, dk, dv
+ * must be 16-byte aligned and overlap no input, each other or the
+ * workspace (MRA_ERR_ALIAS). */
+mra_status mra_attention_bwd(const mra_dims* dims, const void* q, const void* k, const void* v,
+                             const uint8_t* mask, int32_t block_per_row, int32_t approx_mode,
+                             int32_t prior_first, int32_t prior_diag, const void* out, const void* dout,
+                             void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 /* Timing hook: relaunches one stage of the forward pass `count` times in a
  * row on `stream`, on a workspace that a call of mra_attention_fwd with the

@@ -23,7 +23,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     L = mra.lib()
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 10
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(mra.SIGNATURES)

@@ -1,0 +1,125 @@
+"""GPU parity of the backward pass (mra_attention_bwd, through the C ABI)
+against the CPU oracle's gradients (oracle.mra_backward).
+
+The gradients run in bf16 operands with fp32 accumulation: the inputs, P and
+dS enter the products rounded to bf16 (relative error up to 2^-9 each), and
+D_t = dO_t . O_t uses the forward's bf16 output.  The bound is taken relative
+to each gradient tensor's scale: max |err| <= 2^-5 max |ref| and
+sum |err| / sum |ref| <= 2^-7 (a few bf16 roundings, with the cancellation in
+dP - D), written below as TOL_BWD.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL_BWD = dict(max_rel_to_scale=2.0 ** -5, mean_rel=2.0 ** -7)
+
+
+@pytest.fixture(scope="module")
+def mra():
+    import block_sparse_approximate_amd as m
+    m.lib()
+    return m
+
+
+def to_dev(x_bits):
+    return torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def bf16_round(x):
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16)
+
+
+def run_case(mra, w, seed=7):
+    q, k, v = to_dev(w.raw("q")), to_dev(w.raw("k")), to_dev(w.raw("v"))
+    mask = None if w.mask is None else torch.from_numpy(w.mask).cuda()
+    kw = dict(block_per_row=w.block_per_row, approx_mode="sparse", initial_prior_first_n_blocks=w.prior_first,
+              initial_prior_diagonal_n_blocks=w.prior_diag)
+    ws = torch.empty(mra.workspace_size(w.B, w.H, w.N, w.d, torch.bfloat16, w.block_per_row, "sparse"),
+                     dtype=torch.uint8, device="cuda")
+    out = mra.attention(q, k, v, mask, workspace=ws, **kw)
+    g16 = bf16_round(np.random.default_rng(seed).standard_normal(q.shape).astype(np.float32))
+    dq, dk, dv = mra.attention_backward(q, k, v, out, g16.cuda(), ws, mask, **kw)
+    torch.cuda.synchronize()
+    got = [t.float().cpu().numpy() for t in (dq, dk, dv)]
+    ref = oracle.mra_backward(w.q, w.k, w.v, g16.float().numpy(), w.mask, w.block_per_row, "sparse",
+                              w.prior_first, w.prior_diag)
+    return got, ref
+
+
+def check(name, got, ref):
+    for label, a, b in zip(("dq", "dk", "dv"), got, ref):
+        err = np.abs(a - b)
+        scale = float(np.abs(b).max())
+        rel = float(err.max()) / scale if scale > 0 else float(err.max())
+        mean_rel = float(err.sum() / np.abs(b).sum()) if scale > 0 else 0.0
+        print("  %s %s: max|err|/max|ref| %.3e  mean_rel %.3e  (max|ref| %.3e)" % (name, label, rel, mean_rel, scale),
+              flush=True)
+        assert np.isfinite(a).all(), label
+        if scale == 0:
+            assert err.max() == 0, label
+            continue
+        assert rel <= TOL_BWD["max_rel_to_scale"], (label, rel)
+        assert mean_rel <= TOL_BWD["mean_rel"], (label, mean_rel)
+
+
+def small(name, B, H, N, seed=0, mask=None, **kw):
+    return workloads.iid(name, B, H, N, dtype="bf16", seed=seed, scale=0.7, mask=mask, approx_mode="sparse", **kw)
+
+
+def ragged_mask(B, N, seed):
+    rng = np.random.default_rng(seed)
+    m = np.zeros((B, N), np.uint8)
+    for b in range(B):
+        m[b, : int(rng.integers(N // 2, N))] = 1
+    m[0, 5] = 0
+    return m
+
+
+CASES = [
+    ("one-block", dict(B=1, H=2, N=32)),
+    ("nb8-bpr2", dict(B=1, H=3, N=256, block_per_row=2)),
+    ("ragged-nb13-masked", dict(B=2, H=1, N=416, block_per_row=3, mask=ragged_mask(2, 416, 3))),
+    ("priors", dict(B=1, H=2, N=1024, block_per_row=3, prior_first=2, prior_diag=3)),
+    ("all-selected", dict(B=1, H=2, N=256, block_per_row=8)),
+    ("long-rows", dict(B=1, H=2, N=2048, block_per_row=2, prior_first=1)),
+]
+
+
+@pytest.mark.parametrize("name,kw", CASES, ids=[c[0] for c in CASES])
+def test_backward_matches_oracle(mra, name, kw):
+    w = small(name, **kw)
+    print("case", name, w, flush=True)
+    got, ref = run_case(mra, w)
+    check(name, got, ref)
+
+
+def test_backward_named_sparse_workload(mra):
+    w = workloads.get("C3")   # bf16, B=2, H=12, N=4096, sparse, priors
+    print("case", w, flush=True)
+    got, ref = run_case(mra, w)
+    check("C3", got, ref)
+
+
+def test_backward_all_selected_equals_dense_autograd(mra):
+    # every block selected: the gradients are those of dense attention
+    # (torch autograd in fp64 on the CPU, a library routine)
+    w = small("dense", B=1, H=2, N=256, block_per_row=8, seed=5)
+    got, _ = run_case(mra, w, seed=9)
+    g = bf16_round(np.random.default_rng(9).standard_normal((1, 2, 256, 64)).astype(np.float32)).double()
+    tq, tk, tv = (torch.from_numpy(np.asarray(x, np.float64)).requires_grad_(True) for x in (w.q, w.k, w.v))
+    torch.nn.functional.scaled_dot_product_attention(tq, tk, tv).backward(g)
+    check("dense", got, [t.grad.numpy() for t in (tq, tk, tv)])
+
+
+def test_backward_is_deterministic(mra):
+    w = small("det", B=1, H=2, N=1024, block_per_row=3, seed=4)
+    a, _ = run_case(mra, w)
+    b, _ = run_case(mra, w)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
