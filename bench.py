@@ -30,7 +30,13 @@ Besides tokens/s the line carries:
     counters' reading on a plain copy of known size; null when the kernel
     source changed since the counters were taken;
   * `cpu_baseline`: the CPU oracle on the host cores (the whole workload,
-    repeated for about 10 s).
+    repeated for about 10 s);
+  * `backward`: the gradient pass (mra_attention_bwd) on the sparse-mode
+    N=4096 workload C3, K timed calls between HIP events on the library's
+    stream after a forward call that left its selection in the workspace;
+    its algorithmic bytes (Q, K, V, O, dO read once, dQ, dK, dV written
+    once) and MFMA work (five 32x32x64 products per selected block: S, dP,
+    dS K, dS^T Q, P^T dO) over that time.
 Only one GPU is used; --gpus above 1 exits with a message.
 """
 from __future__ import annotations
@@ -128,6 +134,41 @@ def cpu_baseline(w, seconds: float = 10.0):
             "sample": "the whole %s workload (%d heads), %d runs in %.1f s" % (w.name, w.B * w.H, runs, el)}
 
 
+def bench_backward(mra, steps: int, warmup: int) -> dict:
+    import numpy as np
+    import torch
+
+    import workloads
+
+    w = workloads.get("C3")
+    to_dev = lambda n: torch.from_numpy(w.raw(n).view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v = to_dev("q"), to_dev("k"), to_dev("v")
+    kw = dict(block_per_row=w.block_per_row, approx_mode=w.approx_mode, initial_prior_first_n_blocks=w.prior_first,
+              initial_prior_diagonal_n_blocks=w.prior_diag)
+    ws = torch.empty(mra.workspace_size(w.B, w.H, w.N, w.d, torch.bfloat16, w.block_per_row, w.approx_mode),
+                     dtype=torch.uint8, device="cuda")
+    out = mra.attention(q, k, v, None, workspace=ws, **kw)
+    g = torch.from_numpy(np.random.default_rng(1).standard_normal(q.shape).astype(np.float32)).to(torch.bfloat16).cuda()
+    run, _ = mra.prepare_backward(q, k, v, out, g, ws, None, **kw)
+    for _ in range(warmup):
+        run()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    BH, K = w.B * w.H, mra.num_block(w.N, w.block_per_row)
+    nbytes = 8.0 * BH * w.N * w.d * 2
+    flops = 5.0 * 2 * 32 * 32 * w.d * BH * K
+    return {"workload": w.name, "ms_per_call": round(ms, 5), "tokens_per_s": round(w.B * w.N / (ms * 1e-3), 1),
+            "algorithmic_bytes": int(nbytes), "achieved_GBs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "mfma_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -135,6 +176,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="C4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB fp32 copy (x * 1.0) 10 times, to calibrate HBM counters")
     args = ap.parse_args()
@@ -273,6 +315,8 @@ def main():
         "profiled_ms_per_step": round(prof_wall, 5),
         "roofline": roof,
     }
+    if not args.no_backward:
+        rec["backward"] = bench_backward(mra, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(rec), flush=True)

@@ -41,8 +41,9 @@ SIGNATURES = {
     "mra_debug_stages": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
                           _P, _SZ, _P], ctypes.c_int),
     "mra_debug_select": ([_P, _P, _P, _I32, _I32, _I32, _P, _P, _SZ, _P], ctypes.c_int),
-    "mra_attention_bwd": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P],
-                          ctypes.c_int),
+    "mra_backward_workspace_size": ([_P, _I32, _I32, ctypes.POINTER(_SZ)], ctypes.c_int),
+    "mra_attention_bwd": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P, _SZ,
+                           _P], ctypes.c_int),
     "mra_debug_replay": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _SZ, _I32, _I32, _P], ctypes.c_int),
 }
 
@@ -104,6 +105,15 @@ def workspace_size(batch, heads, seq_len, head_dim=64, dtype=torch.bfloat16, blo
     dims = _dims(batch, heads, seq_len, head_dim, DTYPES.get(dtype, -1))
     _check(lib().mra_workspace_size(ctypes.byref(dims), block_per_row, MODES.get(approx_mode, -1),
                                     ctypes.byref(n)), "mra_workspace_size")
+    return n.value
+
+
+def backward_workspace_size(batch, heads, seq_len, head_dim=64, dtype=torch.bfloat16, block_per_row=4,
+                            approx_mode="sparse") -> int:
+    n = _SZ(0)
+    dims = _dims(batch, heads, seq_len, head_dim, DTYPES.get(dtype, -1))
+    _check(lib().mra_backward_workspace_size(ctypes.byref(dims), block_per_row, MODES.get(approx_mode, -1),
+                                             ctypes.byref(n)), "mra_backward_workspace_size")
     return n.value
 
 
@@ -207,13 +217,16 @@ def attention_profiled(q, k, v, events, mask=None, block_per_row=4, approx_mode=
     return out
 
 
-def attention_backward(q, k, v, out, dout, workspace, mask=None, block_per_row=4, approx_mode="sparse",
-                       initial_prior_first_n_blocks=0, initial_prior_diagonal_n_blocks=0, dq=None, dk=None,
-                       dv=None):
-    """Gradients (dq, dk, dv) of a forward call's output with respect to q, k,
-    v given dout.  `out` and `workspace` are that call's output and workspace
-    (the selection is read from it); the other arguments must be the ones it
-    was made with.  Sparse mode, bf16."""
+def prepare_backward(q, k, v, out, dout, workspace, mask=None, block_per_row=4, approx_mode="sparse",
+                     initial_prior_first_n_blocks=0, initial_prior_diagonal_n_blocks=0, dq=None, dk=None, dv=None,
+                     bwd_workspace=None):
+    """Check and marshal the arguments of attention_backward once; returns
+    (call, (dq, dk, dv)) where call() queues one backward pass on the current
+    stream through the C ABI.  `out` and `workspace` are a forward call's
+    output and workspace (the selection and softmax statistics are read from
+    it); the other arguments must be the ones it was made with.
+    `bwd_workspace` (uint8, backward_workspace_size bytes) is allocated when
+    not given.  Sparse mode, bf16."""
     _check_inputs(q, k, v, mask)
     for t in (out, dout):
         if not (t.is_cuda and t.dtype == q.dtype and t.shape == q.shape and t.is_contiguous()):
@@ -222,13 +235,39 @@ def attention_backward(q, k, v, out, dout, workspace, mask=None, block_per_row=4
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
+    for t in (dq, dk, dv):
+        if not (t.is_cuda and t.dtype == q.dtype and t.shape == q.shape and t.is_contiguous()):
+            raise ValueError("dq, dk and dv must be contiguous device tensors shaped and typed like q")
+    bw_bytes = backward_workspace_size(B, H, N, d, q.dtype, block_per_row, approx_mode)
+    if bwd_workspace is None or bwd_workspace.numel() < bw_bytes:
+        bwd_workspace = torch.empty(bw_bytes, dtype=torch.uint8, device=q.device)
     dims = _dims(B, H, N, d, DTYPES[q.dtype])
-    st = lib().mra_attention_bwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), block_per_row,
-                                 MODES.get(approx_mode, -1), initial_prior_first_n_blocks,
-                                 initial_prior_diagonal_n_blocks, _ptr(out), _ptr(dout), _ptr(dq), _ptr(dk),
-                                 _ptr(dv), _ptr(workspace), workspace.numel(), _stream(q))
-    _check(st, "mra_attention_bwd")
-    return dq, dk, dv
+    fn = lib().mra_attention_bwd
+    args = (ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), block_per_row, MODES.get(approx_mode, -1),
+            initial_prior_first_n_blocks, initial_prior_diagonal_n_blocks, _ptr(out), _ptr(dout), _ptr(dq),
+            _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _ptr(bwd_workspace), bwd_workspace.numel(),
+            _stream(q))
+    keep = (dims, q, k, v, mask, out, dout, dq, dk, dv, workspace, bwd_workspace)
+
+    def call():
+        st = fn(*args)
+        if st != 0:
+            raise MraError(st, "mra_attention_bwd")
+        return keep[7:10]
+
+    return call, (dq, dk, dv)
+
+
+def attention_backward(q, k, v, out, dout, workspace, mask=None, block_per_row=4, approx_mode="sparse",
+                       initial_prior_first_n_blocks=0, initial_prior_diagonal_n_blocks=0, dq=None, dk=None,
+                       dv=None, bwd_workspace=None):
+    """Gradients (dq, dk, dv) of a forward call's output with respect to q, k,
+    v given dout; arguments as for prepare_backward."""
+    call, grads = prepare_backward(q, k, v, out, dout, workspace, mask, block_per_row, approx_mode,
+                                   initial_prior_first_n_blocks, initial_prior_diagonal_n_blocks, dq, dk, dv,
+                                   bwd_workspace)
+    call()
+    return grads
 
 
 def debug_replay(q, k, v, stage, count, mask=None, block_per_row=4, approx_mode="full",

@@ -60,11 +60,34 @@ bool carve(const mra_dims& d, int32_t bpr, int32_t mode, Layout* L) {
     L->ncand = take(BH * kCandStride * 4);
     L->st_m = take(BH * (size_t)L->N * 4);
     L->st_linv = take(BH * (size_t)L->N * 4);
-    L->st_d = take(BH * (size_t)L->N * 4);
-    L->ct_ptr = take(BH * (nb + 1) * 4);
-    L->ct_row = take(BH * (size_t)L->K * 4);
     L->total = o;
     return true;
+}
+
+// The backward pass's own workspace (mra_attention_bwd).
+struct BwdLayout {
+    int32_t maxch;
+    size_t st_d, ct_ptr, ct_row, rch, cch, rmul, cmul, count, part_dq, part_dk, part_dv, total;
+};
+
+void carve_bwd(const Layout& L, BwdLayout* W) {
+    const size_t BH = (size_t)L.BH, nb = (size_t)L.nb;
+    W->maxch = bwd_max_chunks(L.nb, L.K);
+    const size_t slots = BH * (size_t)W->maxch, tile = (size_t)kBlock * L.d * 4;
+    size_t o = 0;
+    auto take = [&](size_t bytes) { size_t at = o; o = up256(o + bytes); return at; };
+    W->st_d = take(BH * (size_t)L.N * 4);
+    W->ct_ptr = take(BH * (nb + 1) * 4);
+    W->ct_row = take(BH * (size_t)L.K * 4);
+    W->rch = take(slots * 16);
+    W->cch = take(slots * 16);
+    W->rmul = take(BH * nb * 16);
+    W->cmul = take(BH * nb * 16);
+    W->count = take(BH * 16);
+    W->part_dq = take(slots * tile);
+    W->part_dk = take(slots * tile);
+    W->part_dv = take(slots * tile);
+    W->total = o;
 }
 
 mra_status check_dims(const mra_dims* d) {
@@ -134,9 +157,6 @@ Params make_params(const mra_dims& d, const Layout& L, int32_t mode, int32_t pf,
     p.ncand = reinterpret_cast<uint32_t*>(w + L.ncand);
     p.st_m = reinterpret_cast<float*>(w + L.st_m);
     p.st_linv = reinterpret_cast<float*>(w + L.st_linv);
-    p.st_d = reinterpret_cast<float*>(w + L.st_d);
-    p.ct_ptr = reinterpret_cast<int32_t*>(w + L.ct_ptr);
-    p.ct_row = reinterpret_cast<int32_t*>(w + L.ct_row);
     p.error = reinterpret_cast<int32_t*>(w);
     return p;
 }
@@ -278,11 +298,26 @@ MRA_API mra_status mra_attention_fwd_profiled(const mra_dims* dims, const void* 
                        workspace_bytes, stream, events);
 }
 
+MRA_API mra_status mra_backward_workspace_size(const mra_dims* dims, int32_t block_per_row, int32_t approx_mode,
+                                               size_t* bytes) {
+    if (!bytes) return MRA_ERR_NULL;
+    mra_status st = check_dims(dims);
+    if (st != MRA_OK) return st;
+    st = check_params(block_per_row, approx_mode, 0, 0);
+    if (st != MRA_OK) return st;
+    Layout L;
+    if (!carve(*dims, block_per_row, approx_mode, &L)) return MRA_ERR_SEQ_LEN;
+    BwdLayout W;
+    carve_bwd(L, &W);
+    *bytes = W.total;
+    return MRA_OK;
+}
+
 MRA_API mra_status mra_attention_bwd(const mra_dims* dims, const void* q, const void* k, const void* v,
                                      const uint8_t* mask, int32_t block_per_row, int32_t approx_mode,
                                      int32_t prior_first, int32_t prior_diag, const void* out, const void* dout,
                                      void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
-                                     void* stream) {
+                                     void* bwd_workspace, size_t bwd_workspace_bytes, void* stream) {
     Layout L;
     mra_status st = check_call(dims, q, k, v, mask, block_per_row, approx_mode, prior_first, prior_diag, out,
                                workspace, workspace_bytes, true, &L);
@@ -291,15 +326,20 @@ MRA_API mra_status mra_attention_bwd(const mra_dims* dims, const void* q, const 
     if (dims->dtype != MRA_BF16) return MRA_ERR_DTYPE;
     if (!dout || !dq || !dk || !dv) return MRA_ERR_NULL;
     if (misaligned(dout) || misaligned(dq) || misaligned(dk) || misaligned(dv)) return MRA_ERR_ALIGN;
+    BwdLayout W;
+    carve_bwd(L, &W);
+    if (!bwd_workspace || bwd_workspace_bytes < W.total) return MRA_ERR_WORKSPACE;
+    if (misaligned(bwd_workspace)) return MRA_ERR_ALIGN;
     const size_t tb = (size_t)dims->batch * dims->heads * dims->seq_len * dims->head_dim * 2;
     const void* ins[] = {q, k, v, out, dout, workspace};
     const size_t insz[] = {tb, tb, tb, tb, tb, workspace_bytes};
-    void* outs[] = {dq, dk, dv};
-    for (int a = 0; a < 3; a++) {
+    void* outs[] = {dq, dk, dv, bwd_workspace};
+    const size_t outsz[] = {tb, tb, tb, bwd_workspace_bytes};
+    for (int a = 0; a < 4; a++) {
         for (int c = 0; c < 6; c++)
-            if (overlaps(outs[a], tb, ins[c], insz[c])) return MRA_ERR_ALIAS;
-        for (int c = a + 1; c < 3; c++)
-            if (overlaps(outs[a], tb, outs[c], tb)) return MRA_ERR_ALIAS;
+            if (overlaps(outs[a], outsz[a], ins[c], insz[c])) return MRA_ERR_ALIAS;
+        for (int c = a + 1; c < 4; c++)
+            if (overlaps(outs[a], outsz[a], outs[c], outsz[c])) return MRA_ERR_ALIAS;
     }
     Params p = make_params(*dims, L, approx_mode, prior_first, prior_diag, q, k, v, mask, const_cast<void*>(out),
                            workspace);
@@ -308,6 +348,19 @@ MRA_API mra_status mra_attention_bwd(const mra_dims* dims, const void* q, const 
     p.dq = dq;
     p.dk = dk;
     p.dv = dv;
+    char* bw = static_cast<char*>(bwd_workspace);
+    p.st_d = reinterpret_cast<float*>(bw + W.st_d);
+    p.ct_ptr = reinterpret_cast<int32_t*>(bw + W.ct_ptr);
+    p.ct_row = reinterpret_cast<int32_t*>(bw + W.ct_row);
+    p.bwd_maxch = W.maxch;
+    p.bwd_rch = reinterpret_cast<int4*>(bw + W.rch);
+    p.bwd_cch = reinterpret_cast<int4*>(bw + W.cch);
+    p.bwd_rmul = reinterpret_cast<int4*>(bw + W.rmul);
+    p.bwd_cmul = reinterpret_cast<int4*>(bw + W.cmul);
+    p.bwd_count = reinterpret_cast<int4*>(bw + W.count);
+    p.bwd_part_dq = reinterpret_cast<float*>(bw + W.part_dq);
+    p.bwd_part_dk = reinterpret_cast<float*>(bw + W.part_dk);
+    p.bwd_part_dv = reinterpret_cast<float*>(bw + W.part_dv);
     return launch_bwd(p, static_cast<hipStream_t>(stream)) == hipSuccess ? MRA_OK : MRA_ERR_HIP;
 }
 

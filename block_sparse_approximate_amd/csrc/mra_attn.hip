@@ -240,6 +240,7 @@ __device__ __forceinline__ void finish_segment(const Params& p, const Wave<DT>& 
     if (info_whole(info)) {
         const bool valid = (A.qm >> n) & 1u;
         float a = 1.f, bw = 0.f, den = ltot;
+        float Mu = A.mrun;   // the max that den and the probabilities are relative to
         if constexpr (FULL) {
             // low-res part of the row without the selected blocks, one channel per lane
             lo_lds[W.lane] = A.lo - A.corr;
@@ -249,12 +250,18 @@ __device__ __forceinline__ void finish_segment(const Params& p, const Wave<DT>& 
             a = M == -__builtin_inff() ? 0.f : fast_exp2(A.mrun - M);
             bw = M == -__builtin_inff() ? 0.f : fast_exp2(mi2 - M);
             den = ltot * a + ll * bw;
+            Mu = M;
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
         const float inv = (valid && den > 0.f) ? 1.0f / den : 0.f;
         const float sa = a * inv, sb = bw * inv;
+        if (h == 0) {   // the token's softmax statistics, for the backward pass
+            const size_t st = (size_t)W.bh * p.N + tok;
+            p.st_m[st] = Mu == -__builtin_inff() ? 0.f : Mu;
+            p.st_linv[st] = inv;
+        }
         const size_t orow = ((size_t)W.bh * p.N + tok) * kHeadDim;
 #pragma unroll
         for (int mt = 0; mt < 2; mt++) {

@@ -11,19 +11,28 @@
 //   dS_u = P_u (dO_t . v_u - D_t),  dq_t = tau sum_u dS_u k_u,
 //   dk_u = tau sum_t dS_u q_t,      dv_u = sum_t P_u dO_t.
 //
-// Three kernels, in stream order after a forward call that left its
-// selection in the workspace:
-//   transpose_kernel  per head: the query-block rows that selected each key
-//                     block (column lists of the selection bitmap, ascending)
-//   dq_kernel         one wave per query block row i: pass 1 the row's max
-//                     m_t and sum l_t (stored, with D_t, for dkv_kernel);
-//                     pass 2 per selected block j:
-//                       S^T = K_j Q_i^T, dP^T = V_j dO_i^T   (lane = query)
-//                       dS^T = P^T (dP^T - D),  dQ^T += K_j^T dS^T
-//   dkv_kernel        one wave per key block column j, over the rows i that
-//                     selected it:
-//                       S = Q_i K_j^T, dP = dO_i V_j^T       (lane = key)
-//                       dV^T += dO_i^T P,  dK^T += Q_i^T dS
+// The forward left in its workspace the selection and each token's softmax
+// statistics (m_t in log2 units and 1 / l_t), so no statistics pass is
+// needed.  Four kernels, in stream order after that forward call:
+//   plan_kernel    per head: the query-block rows that selected each key
+//                  block (column lists of the selection bitmap, ascending),
+//                  and both lists cut into chunks of at most kChunkB blocks
+//                  (a row or column with none is one empty chunk)
+//   dq_kernel      one wave per row chunk (query block i, some of its
+//                  selected blocks j):
+//                    S^T = K_j Q_i^T, dP^T = V_j dO_i^T   (lane = query)
+//                    dS^T = P^T (dP^T - D),  dQ^T += K_j^T dS^T
+//                  and D_t, stored for dkv_kernel
+//   dkv_kernel     one wave per column chunk (key block j, some of the rows
+//                  i that selected it):
+//                    S = Q_i K_j^T, dP = dO_i V_j^T       (lane = key)
+//                    dV^T += dO_i^T P,  dK^T += Q_i^T dS
+//   reduce_kernel  rows and columns of several chunks: the chunks' fp32
+//                  partials summed in chunk order (the result does not
+//                  depend on scheduling); single-chunk rows and columns are
+//                  written directly by their wave
+// Chunks keep the work even: a prior makes some rows and columns hold every
+// block of the head.
 // Blocks are staged in the wave's LDS as 32 token rows; MFMA operands are
 // read one row per lane, and a transposed operand (X^T with the contraction
 // over the block's rows) with ds_read_b64_tr_b16 in the order of an
@@ -45,7 +54,8 @@ constexpr int kWaves = 2;             // per workgroup: 4 staged blocks per wave
 constexpr int kThreads = kWaves * 64;
 constexpr int kStr = 72;              // bf16 elements per staged token row (144 bytes)
 constexpr int kTile = kBlock * kStr;  // one staged block
-constexpr int kTrThreads = 512;       // transpose_kernel: one thread per key block (nb <= 512)
+constexpr int kTrThreads = 512;       // plan_kernel: one thread per block row / column (nb <= 512)
+constexpr int kChunkB = 8;            // selected blocks per backward work chunk
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 __device__ __forceinline__ float bf16_to_float(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
@@ -126,21 +136,11 @@ __device__ __forceinline__ void store_rows(uint16_t* g, const f32x16& a0, const 
         }
 }
 
-// ---------------------------------------------------------------- transpose
-__global__ __launch_bounds__(kTrThreads) void transpose_kernel(Params p) {
-    extern __shared__ __align__(16) uint32_t bits[];   // [nb, words]
-    __shared__ int wsum[kTrThreads / 64 + 1];
-    const int bh = blockIdx.x, nb = p.nb, words = p.words, tid = threadIdx.x;
-    const uint32_t* gb = p.selbits + (size_t)bh * nb * words;
-    for (int x = tid; x < nb * words; x += kTrThreads) bits[x] = gb[x];
-    __syncthreads();
-    const int j = tid;
-    int c = 0;
-    if (j < nb)
-        for (int i = 0; i < nb; i++) c += (bits[i * words + (j >> 5)] >> (j & 31)) & 1u;
-    // exclusive scan of the column counts over the workgroup
-    const int lane = tid & 63, wave = tid >> 6;
-    int x = c;
+// ---------------------------------------------------------------- plan
+// exclusive scan of one int per thread over the plan workgroup; *total gets the sum
+__device__ __forceinline__ int plan_scan(int v, int* wsum, int* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int x = v;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
         const int y = __shfl_up(x, off, 64);
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(kTrThreads) void transpose_kernel(Params p) {
     }
     if (lane == 63) wsum[wave] = x;
     __syncthreads();
-    if (tid == 0) {
+    if (threadIdx.x == 0) {
         int acc = 0;
         for (int w = 0; w < kTrThreads / 64; w++) {
             const int t = wsum[w];
@@ -158,38 +158,94 @@ __global__ __launch_bounds__(kTrThreads) void transpose_kernel(Params p) {
         wsum[kTrThreads / 64] = acc;
     }
     __syncthreads();
-    int pos = wsum[wave] + x - c;
-    int32_t* ptr = p.ct_ptr + (size_t)bh * (nb + 1);
-    int32_t* rows = p.ct_row + (size_t)bh * p.K;
-    if (j < nb) {
-        ptr[j] = pos;
+    const int ex = wsum[wave] + x - v;
+    *total = wsum[kTrThreads / 64];
+    __syncthreads();
+    return ex;
+}
+
+__global__ __launch_bounds__(kTrThreads) void plan_kernel(Params p) {
+    extern __shared__ __align__(16) uint32_t bits[];   // [nb, words]
+    __shared__ int wsum[kTrThreads / 64 + 1];
+    const int bh = blockIdx.x, nb = p.nb, words = p.words, x = threadIdx.x;
+    const int K = (int)p.K, maxch = p.bwd_maxch;
+    const uint32_t* gb = p.selbits + (size_t)bh * nb * words;
+    for (int t = x; t < nb * words; t += kTrThreads) bits[t] = gb[t];
+    __syncthreads();
+    const bool on = x < nb;
+    // thread x: block row x and key block column x
+    int ccount = 0;
+    if (on)
+        for (int i = 0; i < nb; i++) ccount += (bits[i * words + (x >> 5)] >> (x & 31)) & 1u;
+    const int32_t* rp = p.row_ptr + (size_t)bh * (nb + 1);
+    const int e0 = on ? min(max(rp[x], 0), K) : 0, e1 = on ? min(max(rp[x + 1], e0), K) : 0;
+    const int nr = on ? max(1, (e1 - e0 + kChunkB - 1) / kChunkB) : 0;
+    const int nc = on ? max(1, (ccount + kChunkB - 1) / kChunkB) : 0;
+    int tot_c, tot_r, tot_cc, tot_rm, tot_cm;
+    const int cpos = plan_scan(ccount, wsum, &tot_c);
+    const int rbase = plan_scan(nr, wsum, &tot_r);
+    const int cbase = plan_scan(nc, wsum, &tot_cc);
+    const int rm = plan_scan(nr > 1 ? 1 : 0, wsum, &tot_rm);
+    const int cm = plan_scan(nc > 1 ? 1 : 0, wsum, &tot_cm);
+    int32_t* cptr = p.ct_ptr + (size_t)bh * (nb + 1);
+    int32_t* crow = p.ct_row + (size_t)bh * K;
+    int4* rch = p.bwd_rch + (size_t)bh * maxch;
+    int4* cch = p.bwd_cch + (size_t)bh * maxch;
+    if (on) {
+        cptr[x] = cpos;
+        int pos = cpos;
         for (int i = 0; i < nb; i++)
-            if ((bits[i * words + (j >> 5)] >> (j & 31)) & 1u) {
-                if (pos < p.K) rows[pos] = i;
+            if ((bits[i * words + (x >> 5)] >> (x & 31)) & 1u) {
+                if (pos < K) crow[pos] = i;
                 pos++;
             }
+        for (int c = 0; c < nr && rbase + c < maxch; c++)
+            rch[rbase + c] = make_int4(x, e0 + c * kChunkB, min(e0 + (c + 1) * kChunkB, e1), nr > 1 ? rbase + c : -1);
+        const int c0 = cpos, c1 = min(cpos + ccount, K);
+        for (int c = 0; c < nc && cbase + c < maxch; c++)
+            cch[cbase + c] = make_int4(x, c0 + c * kChunkB, min(c0 + (c + 1) * kChunkB, c1), nc > 1 ? cbase + c : -1);
+        if (nr > 1) p.bwd_rmul[(size_t)bh * nb + rm] = make_int4(x, rbase, nr, 0);
+        if (nc > 1) p.bwd_cmul[(size_t)bh * nb + cm] = make_int4(x, cbase, nc, 0);
     }
-    if (tid == 0) {
-        ptr[nb] = wsum[kTrThreads / 64];
-        if ((int64_t)wsum[kTrThreads / 64] != p.K) atomicOr(reinterpret_cast<unsigned int*>(p.error), 8u);
+    if (x == 0) {
+        cptr[nb] = tot_c;
+        p.bwd_count[bh] = make_int4(min(tot_r, maxch), min(tot_cc, maxch), tot_rm, tot_cm);
+        if (tot_c != K || tot_r > maxch || tot_cc > maxch) atomicOr(reinterpret_cast<unsigned int*>(p.error), 8u);
     }
+}
+
+// A wave's 32 x 64 fp32 partial (channels 0..31 in a0, 32..63 in a1; lane l
+// holds token row l % 32) to a contiguous [32, 64] slot.
+__device__ __forceinline__ void store_part(float* g, const f32x16& a0, const f32x16& a1, int lane) {
+    const int n = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+        for (int gq = 0; gq < 4; gq++) {
+            const f32x16& a = mt == 0 ? a0 : a1;
+            *reinterpret_cast<float4*>(g + n * kHeadDim + 32 * mt + 8 * gq + 4 * h) =
+                make_float4(a[4 * gq], a[4 * gq + 1], a[4 * gq + 2], a[4 * gq + 3]);
+        }
 }
 
 // ---------------------------------------------------------------- dQ
 __global__ __launch_bounds__(kThreads) void dq_kernel(Params p) {
     __shared__ __align__(16) uint16_t lds[kWaves][4][kTile];   // per wave: Q_i, dO_i, K_j, V_j
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int nb = p.nb;
+    const int nb = p.nb, maxch = p.bwd_maxch;
     const int64_t g = (int64_t)blockIdx.x * kWaves + wave;
-    if (g >= (int64_t)p.BH * nb) return;
-    const int bh = (int)(g / nb), i = (int)(g - (int64_t)bh * nb), b = bh / p.H;
+    if (g >= (int64_t)p.BH * maxch) return;
+    const int bh = (int)(g / maxch), cid = (int)(g - (int64_t)bh * maxch);
+    if (cid >= p.bwd_count[bh].x) return;
+    const int4 dsc = p.bwd_rch[(size_t)bh * maxch + cid];
+    const int i = min(max(dsc.x, 0), nb - 1), b = bh / p.H;
+    const int e0 = max(dsc.y, 0), e1 = min(dsc.z, (int)p.K);
     const int n = lane & 31, h = lane >> 5;
     uint16_t* qs = lds[wave][0];
     uint16_t* dos = lds[wave][1];
     uint16_t* ks = lds[wave][2];
     uint16_t* vs = lds[wave][3];
     const size_t head = (size_t)bh * p.N * kHeadDim, rowoff = head + (size_t)i * kBlock * kHeadDim;
-    const uint16_t* Q = static_cast<const uint16_t*>(p.q) + head;
     const uint16_t* Kh = static_cast<const uint16_t*>(p.k) + head;
     const uint16_t* Vh = static_cast<const uint16_t*>(p.v) + head;
     const uint16_t* dO = static_cast<const uint16_t*>(p.dout) + rowoff;
@@ -197,7 +253,7 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(Params p) {
     const float tau = 1.0f / __builtin_sqrtf((float)p.d);
     const float scale2 = tau * kLog2e;
 
-    stage(qs, Q + (size_t)i * kBlock * kHeadDim, lane);
+    stage(qs, static_cast<const uint16_t*>(p.q) + rowoff, lane);
     stage(dos, dO, lane);
     // D_t = dO_t . O_t: lane (n, h) takes channels 32 h .. 32 h + 31 of token n
     float dpart = 0.f;
@@ -211,50 +267,14 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(Params p) {
             dpart += bf16_to_float(a[e] >> 16) * bf16_to_float(o[e] >> 16);
         }
     }
-    const float D = dpart + __shfl_xor(dpart, 32, 64);
-    const bool valid = (p.mbits[(size_t)b * nb + i] >> n) & 1u;
-    const int32_t* rp = p.row_ptr + (size_t)bh * (nb + 1);
-    const int e0 = max(rp[i], 0), e1 = min(rp[i + 1], (int)p.K);
+    const size_t t = (size_t)bh * p.N + (size_t)i * kBlock + n;
+    const float mu = p.st_m[t], linv = p.st_linv[t];
+    const bool qv = linv > 0.f;   // padded and keyless query tokens take no gradient
+    const float Dv = qv ? dpart + __shfl_xor(dpart, 32, 64) : 0.f;
+    if (h == 0) p.st_d[t] = Dv;   // every chunk of the row writes the same value
     const int32_t* cols = p.col + (size_t)bh * p.K;
     wave_sync_lds();
 
-    // pass 1: the row's max (log2 units) and sum over its selected valid keys
-    float m = -__builtin_inff(), lpart = 0.f;
-    for (int e = e0; e < e1; e++) {
-        const int j = min(max(cols[e], 0), nb - 1);
-        const uint32_t km = p.mbits[(size_t)b * nb + j];
-        stage(ks, Kh + (size_t)j * kBlock * kHeadDim, lane);
-        wave_sync_lds();
-        f32x16 S = mm4(zero16(), ks, qs, lane);   // S^T: lane = query, registers = keys
-        float bm = -__builtin_inff();
-#pragma unroll
-        for (int r = 0; r < 16; r++) {
-            S[r] = ((km >> acc_row(r, lane)) & 1u) ? S[r] * scale2 : -__builtin_inff();
-            bm = fmaxf(bm, S[r]);
-        }
-        bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-        const float mn = fmaxf(m, bm);
-        if (mn != -__builtin_inff()) {
-            float ps = 0.f;
-#pragma unroll
-            for (int r = 0; r < 16; r++) ps += __builtin_amdgcn_exp2f(S[r] - mn);
-            lpart = lpart * __builtin_amdgcn_exp2f(m - mn) + ps;
-            m = mn;
-        }
-        wave_sync_lds();
-    }
-    const float l = lpart + __shfl_xor(lpart, 32, 64);
-    const float mu = m == -__builtin_inff() ? 0.f : m;
-    const float linv = (valid && l > 0.f) ? 1.0f / l : 0.f;
-    const float Dv = linv > 0.f ? D : 0.f;
-    if (h == 0) {
-        const size_t t = (size_t)bh * p.N + (size_t)i * kBlock + n;
-        p.st_m[t] = mu;
-        p.st_linv[t] = linv;
-        p.st_d[t] = Dv;
-    }
-
-    // pass 2: dQ^T += K_j^T dS^T
     f32x16 dq0 = zero16(), dq1 = zero16();
     for (int e = e0; e < e1; e++) {
         const int j = min(max(cols[e], 0), nb - 1);
@@ -262,12 +282,12 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(Params p) {
         stage(ks, Kh + (size_t)j * kBlock * kHeadDim, lane);
         stage(vs, Vh + (size_t)j * kBlock * kHeadDim, lane);
         wave_sync_lds();
-        const f32x16 S = mm4(zero16(), ks, qs, lane);    // S^T
+        const f32x16 S = mm4(zero16(), ks, qs, lane);    // S^T: lane = query, registers = keys
         const f32x16 dP = mm4(zero16(), vs, dos, lane);  // dP^T
         f32x16 dS;
 #pragma unroll
         for (int r = 0; r < 16; r++) {
-            const float pv = ((km >> acc_row(r, lane)) & 1u) ? __builtin_amdgcn_exp2f(S[r] * scale2 - mu) * linv : 0.f;
+            const float pv = (qv && ((km >> acc_row(r, lane)) & 1u)) ? __builtin_amdgcn_exp2f(S[r] * scale2 - mu) * linv : 0.f;
             dS[r] = pv * (dP[r] - Dv);
         }
 #pragma unroll
@@ -278,7 +298,8 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(Params p) {
         }
         wave_sync_lds();
     }
-    store_rows(static_cast<uint16_t*>(p.dq) + rowoff, dq0, dq1, tau, lane);
+    if (dsc.w < 0) store_rows(static_cast<uint16_t*>(p.dq) + rowoff, dq0, dq1, tau, lane);
+    else store_part(p.bwd_part_dq + ((size_t)bh * maxch + min(dsc.w, maxch - 1)) * kBlock * kHeadDim, dq0, dq1, lane);
 }
 
 // ---------------------------------------------------------------- dK, dV
@@ -286,10 +307,14 @@ __global__ __launch_bounds__(kThreads) void dkv_kernel(Params p) {
     __shared__ __align__(16) uint16_t lds[kWaves][4][kTile];   // per wave: K_j, V_j, Q_i, dO_i
     __shared__ __align__(16) float st[kWaves][3][kBlock];      // per wave: m, 1/l, D of block i's tokens
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int nb = p.nb;
+    const int nb = p.nb, maxch = p.bwd_maxch;
     const int64_t g = (int64_t)blockIdx.x * kWaves + wave;
-    if (g >= (int64_t)p.BH * nb) return;
-    const int bh = (int)(g / nb), j = (int)(g - (int64_t)bh * nb), b = bh / p.H;
+    if (g >= (int64_t)p.BH * maxch) return;
+    const int bh = (int)(g / maxch), cid = (int)(g - (int64_t)bh * maxch);
+    if (cid >= p.bwd_count[bh].y) return;
+    const int4 dsc = p.bwd_cch[(size_t)bh * maxch + cid];
+    const int j = min(max(dsc.x, 0), nb - 1), b = bh / p.H;
+    const int c0 = max(dsc.y, 0), c1 = min(dsc.z, (int)p.K);
     const int n = lane & 31;
     uint16_t* ks = lds[wave][0];
     uint16_t* vs = lds[wave][1];
@@ -304,8 +329,6 @@ __global__ __launch_bounds__(kThreads) void dkv_kernel(Params p) {
     stage(ks, static_cast<const uint16_t*>(p.k) + coloff, lane);
     stage(vs, static_cast<const uint16_t*>(p.v) + coloff, lane);
     const bool kvalid = (p.mbits[(size_t)b * nb + j] >> n) & 1u;   // lane = key n
-    const int32_t* cp = p.ct_ptr + (size_t)bh * (nb + 1);
-    const int c0 = max(cp[j], 0), c1 = min(cp[j + 1], (int)p.K);
     const int32_t* rows = p.ct_row + (size_t)bh * p.K;
     const size_t sbase = (size_t)bh * p.N;
 
@@ -327,7 +350,8 @@ __global__ __launch_bounds__(kThreads) void dkv_kernel(Params p) {
 #pragma unroll
         for (int r = 0; r < 16; r++) {
             const int q = acc_row(r, lane);
-            const float pv = kvalid ? __builtin_amdgcn_exp2f(S[r] * scale2 - st[wave][0][q]) * st[wave][1][q] : 0.f;
+            const float li = st[wave][1][q];
+            const float pv = (kvalid && li > 0.f) ? __builtin_amdgcn_exp2f(S[r] * scale2 - st[wave][0][q]) * li : 0.f;
             P[r] = pv;
             dS[r] = pv * (dP[r] - st[wave][2][q]);
         }
@@ -341,24 +365,83 @@ __global__ __launch_bounds__(kThreads) void dkv_kernel(Params p) {
         }
         wave_sync_lds();
     }
-    store_rows(static_cast<uint16_t*>(p.dk) + coloff, dk0, dk1, tau, lane);
-    store_rows(static_cast<uint16_t*>(p.dv) + coloff, dv0, dv1, 1.0f, lane);
+    if (dsc.w < 0) {
+        store_rows(static_cast<uint16_t*>(p.dk) + coloff, dk0, dk1, tau, lane);
+        store_rows(static_cast<uint16_t*>(p.dv) + coloff, dv0, dv1, 1.0f, lane);
+    } else {
+        const size_t slot = ((size_t)bh * maxch + min(dsc.w, maxch - 1)) * kBlock * kHeadDim;
+        store_part(p.bwd_part_dk + slot, dk0, dk1, lane);
+        store_part(p.bwd_part_dv + slot, dv0, dv1, lane);
+    }
+}
+
+// ---------------------------------------------------------------- reduce
+// Workgroup (bh, x, side): the x-th row (side 0) or column (side 1) of head
+// bh that has several chunks.  Thread t sums token t / 8, channels
+// 8 (t % 8) .. +7 over the chunks in order and writes bf16.
+constexpr int kRedThreads = 256;
+
+__device__ __forceinline__ void reduce_one(const float* part, int first, int nch, float scale, uint16_t* dst,
+                                           size_t slot0, int tid) {
+    const int tok = tid >> 3, cg = (tid & 7) * 8;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) acc[e] = 0.f;
+    for (int c = 0; c < nch; c++) {
+        const float4* src = reinterpret_cast<const float4*>(part + (slot0 + first + c) * kBlock * kHeadDim +
+                                                            tok * kHeadDim + cg);
+        const float4 a = src[0], b2 = src[1];
+        acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+        acc[4] += b2.x; acc[5] += b2.y; acc[6] += b2.z; acc[7] += b2.w;
+    }
+    uint4 pk;
+    pk.x = (uint32_t)float_to_bf16(acc[0] * scale) | ((uint32_t)float_to_bf16(acc[1] * scale) << 16);
+    pk.y = (uint32_t)float_to_bf16(acc[2] * scale) | ((uint32_t)float_to_bf16(acc[3] * scale) << 16);
+    pk.z = (uint32_t)float_to_bf16(acc[4] * scale) | ((uint32_t)float_to_bf16(acc[5] * scale) << 16);
+    pk.w = (uint32_t)float_to_bf16(acc[6] * scale) | ((uint32_t)float_to_bf16(acc[7] * scale) << 16);
+    *reinterpret_cast<uint4*>(dst + tok * kHeadDim + cg) = pk;
+}
+
+__global__ __launch_bounds__(kRedThreads) void reduce_kernel(Params p) {
+    const int nb = p.nb, maxch = p.bwd_maxch;
+    const int side = blockIdx.x & 1;
+    const int64_t w = blockIdx.x >> 1;
+    const int bh = (int)(w / nb), x = (int)(w - (int64_t)bh * nb);
+    if (bh >= p.BH) return;
+    const int4 cnt = p.bwd_count[bh];
+    if (x >= (side == 0 ? cnt.z : cnt.w)) return;
+    const int4 m = (side == 0 ? p.bwd_rmul : p.bwd_cmul)[(size_t)bh * nb + x];
+    const int blk = min(max(m.x, 0), nb - 1);
+    const int first = max(m.y, 0), nch = max(0, min(m.z, maxch - first));
+    const float tau = 1.0f / __builtin_sqrtf((float)p.d);
+    const size_t off = ((size_t)bh * p.N + (size_t)blk * kBlock) * kHeadDim, slot0 = (size_t)bh * maxch;
+    if (side == 0) {
+        reduce_one(p.bwd_part_dq, first, nch, tau, static_cast<uint16_t*>(p.dq) + off, slot0, threadIdx.x);
+    } else {
+        reduce_one(p.bwd_part_dk, first, nch, tau, static_cast<uint16_t*>(p.dk) + off, slot0, threadIdx.x);
+        reduce_one(p.bwd_part_dv, first, nch, 1.0f, static_cast<uint16_t*>(p.dv) + off, slot0, threadIdx.x);
+    }
 }
 
 }  // namespace
 
+int bwd_max_chunks(int nb, int64_t K) { return nb + (int)((K + kChunkB - 1) / kChunkB); }
+
 hipError_t launch_bwd(const Params& p, hipStream_t s) {
     if (p.dtype != 1 || p.d != kHeadDim || p.nb > kTrThreads) return hipErrorInvalidValue;
-    const size_t tr_lds = (size_t)p.nb * p.words * 4;
-    hipLaunchKernelGGL(transpose_kernel, dim3(p.BH), dim3(kTrThreads), tr_lds, s, p);
+    const size_t plan_lds = (size_t)p.nb * p.words * 4;
+    hipLaunchKernelGGL(plan_kernel, dim3(p.BH), dim3(kTrThreads), plan_lds, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t waves = (int64_t)p.BH * p.nb;
+    const int64_t waves = (int64_t)p.BH * p.bwd_maxch;
     const unsigned grid = (unsigned)((waves + kWaves - 1) / kWaves);
     hipLaunchKernelGGL(dq_kernel, dim3(grid), dim3(kThreads), 0, s, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(dkv_kernel, dim3(grid), dim3(kThreads), 0, s, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)(2 * (int64_t)p.BH * p.nb)), dim3(kRedThreads), 0, s, p);
     return hipGetLastError();
 }
 

@@ -51,8 +51,7 @@ struct Layout {
     int64_t K;            // selection budget per (batch, head)
     int32_t max_items;    // segments per head, upper bound
     size_t qhat, khat, vhat, cnt, mbits, logits, keys, rowmax, hist, thresh, row_ptr, col, selbits, item_ptr, recs,
-        merge_rows, n_merge, lo_all, ll_all, part_o, part_ml, part_corr, cand, ncand, st_m, st_linv, st_d,
-        ct_ptr, ct_row, total;
+        merge_rows, n_merge, lo_all, ll_all, part_o, part_ml, part_corr, cand, ncand, st_m, st_linv, total;
 };
 
 // Everything a kernel needs, passed by value.
@@ -99,11 +98,22 @@ struct Params {
     void* dq;              // [B, H, N, d] gradients out
     void* dk;
     void* dv;
-    float* st_m;           // [BH, N] per query token: max of its scaled logits (log2 units), 0 if none
-    float* st_linv;        // [BH, N] 1 / sum of 2^(s - m) over its keys; 0 for padded or keyless tokens
+    float* st_m;           // [BH, N] per query token (forward): the max its softmax sum is relative
+                           //   to (log2 units), 0 if none
+    float* st_linv;        // [BH, N] (forward) 1 / that sum; 0 for padded or keyless tokens
+    // backward workspace
     float* st_d;           // [BH, N] dO . O (0 where st_linv is 0)
     int32_t* ct_ptr;       // [BH, nb + 1] per key block: start of its list in ct_row
     int32_t* ct_row;       // [BH, K] query block rows that selected each key block, ascending
+    int32_t bwd_maxch;     // chunk slots per head (one per chunk, rows and columns alike)
+    int4* bwd_rch;         // [BH, maxch] row chunks: (row i, first, end in col, partial slot or -1)
+    int4* bwd_cch;         // [BH, maxch] column chunks: (column j, first, end in ct_row, slot or -1)
+    int4* bwd_rmul;        // [BH, nb] rows of several chunks: (row, first chunk, chunks, 0)
+    int4* bwd_cmul;        // [BH, nb] columns of several chunks
+    int4* bwd_count;       // [BH] row chunks, column chunks, rows and columns of several chunks
+    float* bwd_part_dq;    // [BH, maxch, 32, d] fp32 partials of chunks of multi-chunk rows
+    float* bwd_part_dk;    // [BH, maxch, 32, d] and columns
+    float* bwd_part_dv;
     int32_t* error;        // device error flag (0 = fine)
     int32_t attn_wph;      // attention stream: waves sharing one head's blocks
     int32_t attn_seq;      // 1: those are all the waves of an XCD, which take the XCD's heads in turn
@@ -163,6 +173,7 @@ hipError_t launch_premark(const Params& p, hipStream_t s);
 hipError_t launch_select(const Params& p, hipStream_t s);
 hipError_t launch_attn(const Params& p, hipStream_t s);
 hipError_t launch_finish(const Params& p, hipStream_t s);
+int bwd_max_chunks(int nb, int64_t K);
 hipError_t launch_bwd(const Params& p, hipStream_t s);
 int attn_grid_waves_per_head(int BH, int64_t K);
 bool attn_heads_in_turn(int BH, int64_t K);

@@ -89,6 +89,7 @@ __device__ void merge_row(const Params& p, int bh, int4 dsc, float* lo, float* l
 #pragma unroll
         for (int c = 0; c < kBatch; c++) corr += cc[c];
     }
+    float Mu = M;   // the max that den and the probabilities are relative to
     if (full) {
         // the row's low-res part: lo_all minus the segments' corrections
         if (tid < kHeadDim) lo[tid] = lo_in - corr;
@@ -100,6 +101,7 @@ __device__ void merge_row(const Params& p, int bh, int4 dsc, float* lo, float* l
             const float s = M == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(M - Mf);
             const float f = __builtin_amdgcn_exp2f(mi2 - Mf);
             den = den * s + ll * f;
+            Mu = Mf;
 #pragma unroll
             for (int e = 0; e < 8; e++) acc[e] = acc[e] * s + lo[cg + e] * f;
         }
@@ -107,6 +109,11 @@ __device__ void merge_row(const Params& p, int bh, int4 dsc, float* lo, float* l
     const bool valid = (qm >> t) & 1u;
     const float inv = (valid && den > 0.f) ? 1.0f / den : 0.f;
     const size_t orow = ((size_t)bh * p.N + (size_t)i * kBlock + t) * kHeadDim + cg;
+    if ((tid & 7) == 0) {   // the token's softmax statistics, for the backward pass
+        const size_t st = (size_t)bh * p.N + (size_t)i * kBlock + t;
+        p.st_m[st] = Mu == -__builtin_inff() ? 0.f : Mu;
+        p.st_linv[st] = inv;
+    }
     if constexpr (DT == 1) {
         uint4 pk;
         pk.x = (uint32_t)float_to_bf16(acc[0] * inv) | ((uint32_t)float_to_bf16(acc[1] * inv) << 16);

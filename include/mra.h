@@ -147,6 +147,13 @@ mra_status mra_debug_select(const mra_dims* dims, const float* logits, const int
                             int32_t block_per_row, int32_t prior_first, int32_t prior_diag,
                             int32_t* sel, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of the backward pass's own workspace for these dimensions and
+ * selection parameters (mra_attention_bwd's bwd_workspace): the dO . O row
+ * terms, the transposed selection, the work chunks and fp32 partial
+ * gradients.  Status as for mra_workspace_size. */
+mra_status mra_backward_workspace_size(const mra_dims* dims, int32_t block_per_row, int32_t approx_mode,
+                                       size_t* bytes);
+
 /* Gradients of the forward pass with respect to q, k and v ([MRA] "第三步":
  * the block products' backward reuses the kernels on transposed block
  * indices, so the block selection is a constant of the backward pass).
@@ -155,18 +162,21 @@ mra_status mra_debug_select(const mra_dims* dims, const float* logits, const int
  *   out       [B, H, N, d] that call's output;
  *   dout      [B, H, N, d] dL/d out;
  *   dq, dk, dv [B, H, N, d] gradients, written (in the dtype of dims);
- *   workspace the workspace that forward call filled (it holds the
- *             selection), unchanged since; the backward also writes per-token
- *             row statistics and the transposed selection there.
+ *   workspace the workspace that forward call filled (its selection and
+ *             each token's softmax statistics), unchanged since; read only;
+ *   bwd_workspace  device scratch of mra_backward_workspace_size bytes
+ *             (16-byte aligned, caller-owned, no contents kept between
+ *             calls; MRA_ERR_WORKSPACE if smaller).
  * Must be queued after that forward call (stream order).  Supported: sparse
  * mode (MRA_ERR_MODE otherwise), bf16 (MRA_ERR_DTYPE otherwise).  dq, dk, dv
- * must be 16-byte aligned and overlap no input, each other or the
- * workspace (MRA_ERR_ALIAS). */
+ * and bwd_workspace must be 16-byte aligned and overlap no input or each
+ * other (MRA_ERR_ALIAS).  The result does not depend on scheduling: partial
+ * sums are added in a fixed order. */
 mra_status mra_attention_bwd(const mra_dims* dims, const void* q, const void* k, const void* v,
                              const uint8_t* mask, int32_t block_per_row, int32_t approx_mode,
                              int32_t prior_first, int32_t prior_diag, const void* out, const void* dout,
                              void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
-                             void* stream);
+                             void* bwd_workspace, size_t bwd_workspace_bytes, void* stream);
 
 /* Timing hook: relaunches one stage of the forward pass `count` times in a
  * row on `stream`, on a workspace that a call of mra_attention_fwd with the

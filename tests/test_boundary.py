@@ -23,7 +23,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     L = mra.lib()
     names = declared_functions()
-    assert len(names) == 10
+    assert len(names) == 11
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(mra.SIGNATURES)
@@ -119,6 +119,43 @@ def test_debug_replay_rejects_bad_arguments():
     assert L.mra_debug_replay(*args(3, 0)) == 13
     assert L.mra_debug_replay(*args(3, 1, 16)) == 10
     assert L.mra_debug_replay(ctypes.byref(d), Q, K, V, None, 4, 0, 0, 0, None, W, 1 << 40, 3, 1, None) == 1
+
+
+DO, DQ, DK, DV, BW = 0x70000000, 0x80000000, 0x90000000, 0xA0000000, 0xB0000000
+
+
+def call_bwd(dims=(1, 2, 512, 64, 1), mode=1, dout=DO, dq=DQ, dk=DK, dv=DV, bw=BW, bw_bytes=None, out=O,
+             ws=W):
+    d = mra._Dims(*dims)
+    ws_bytes = mra.workspace_size(1, 2, 512, approx_mode="full")   # enough for either mode
+    if bw_bytes is None:
+        bw_bytes = mra.backward_workspace_size(1, 2, 512)
+    return mra.lib().mra_attention_bwd(ctypes.byref(d), Q, K, V, None, 4, mode, 0, 0, out, dout, dq, dk, dv, ws,
+                                       ws_bytes, bw, bw_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(out=None), 1), (dict(dout=None), 1), (dict(dq=None), 1), (dict(dv=None), 1),
+    (dict(mode=0), 6), (dict(dims=(1, 2, 512, 64, 0)), 5), (dict(ws=None), 10),
+    (dict(bw=None), 10), (dict(bw_bytes=4096), 10),
+    (dict(dq=Q), 9), (dict(dk=O + 64), 9), (dict(dv=DQ), 9), (dict(dq=BW), 9), (dict(bw=DO), 9),
+    (dict(dq=DQ + 8), 12), (dict(bw=BW + 8), 12),
+])
+def test_attention_bwd_rejects_bad_arguments(kw, status):
+    assert call_bwd(**kw) == status
+
+
+def test_backward_workspace_size_grows_and_validates():
+    small = mra.backward_workspace_size(1, 2, 512)
+    big = mra.backward_workspace_size(2, 12, 4096)
+    assert 0 < small < big
+    assert mra.backward_workspace_size(2, 12, 4096, block_per_row=8) > big
+    with pytest.raises(mra.MraError) as e:
+        mra.backward_workspace_size(1, 1, 100)
+    assert e.value.status == 3
+    with pytest.raises(mra.MraError) as e:
+        mra.backward_workspace_size(1, 1, 512, block_per_row=0)
+    assert e.value.status == 7
 
 
 def test_binding_refuses_cpu_tensors():

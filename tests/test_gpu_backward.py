@@ -35,7 +35,7 @@ def bf16_round(x):
     return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16)
 
 
-def run_case(mra, w, seed=7):
+def run_case(mra, w, seed=7, bwd_workspace=None):
     q, k, v = to_dev(w.raw("q")), to_dev(w.raw("k")), to_dev(w.raw("v"))
     mask = None if w.mask is None else torch.from_numpy(w.mask).cuda()
     kw = dict(block_per_row=w.block_per_row, approx_mode="sparse", initial_prior_first_n_blocks=w.prior_first,
@@ -44,7 +44,7 @@ def run_case(mra, w, seed=7):
                      dtype=torch.uint8, device="cuda")
     out = mra.attention(q, k, v, mask, workspace=ws, **kw)
     g16 = bf16_round(np.random.default_rng(seed).standard_normal(q.shape).astype(np.float32))
-    dq, dk, dv = mra.attention_backward(q, k, v, out, g16.cuda(), ws, mask, **kw)
+    dq, dk, dv = mra.attention_backward(q, k, v, out, g16.cuda(), ws, mask, bwd_workspace=bwd_workspace, **kw)
     torch.cuda.synchronize()
     got = [t.float().cpu().numpy() for t in (dq, dk, dv)]
     ref = oracle.mra_backward(w.q, w.k, w.v, g16.float().numpy(), w.mask, w.block_per_row, "sparse",
@@ -123,3 +123,17 @@ def test_backward_is_deterministic(mra):
     b, _ = run_case(mra, w)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+def test_backward_reused_workspace_matches_fresh(mra):
+    # a backward workspace left over from a larger call holds stale chunk
+    # lists and partials; nothing of it may leak into the next call
+    big = small("big", B=1, H=2, N=2048, block_per_row=3, prior_first=2, seed=11)
+    little = small("little", B=1, H=3, N=512, block_per_row=2, prior_diag=3, seed=12)
+    bw = torch.empty(mra.backward_workspace_size(1, 2, 2048, block_per_row=3), dtype=torch.uint8, device="cuda")
+    run_case(mra, big, bwd_workspace=bw)
+    reused, ref = run_case(mra, little, bwd_workspace=bw)
+    fresh, _ = run_case(mra, little)
+    for x, y in zip(reused, fresh):
+        assert np.array_equal(x, y)
+    check("little", reused, ref)
