@@ -31,12 +31,14 @@ Besides tokens/s the line carries:
     source changed since the counters were taken;
   * `cpu_baseline`: the CPU oracle on the host cores (the whole workload,
     repeated for about 10 s);
-  * `backward`: the gradient pass (mra_attention_bwd) on the sparse-mode
-    N=4096 workload C3, K timed calls between HIP events on the library's
-    stream after a forward call that left its selection in the workspace;
-    its algorithmic bytes (Q, K, V, O, dO read once, dQ, dK, dV written
-    once) and MFMA work (five 32x32x64 products per selected block: S, dP,
-    dS K, dS^T Q, P^T dO) over that time.
+  * `backward`: the gradient pass (mra_attention_bwd) on the N=4096
+    workloads C3 (sparse mode, priors) and C4 (full mode, clustered), K timed
+    calls between HIP events on the library's stream after a forward call
+    that left its selection and statistics in the workspace; its algorithmic
+    bytes (Q, K, V, O, dO read once, dQ, dK, dV written once) and MFMA work
+    (five 32x32x64 products per selected block: S, dP, dS K, dS^T Q, P^T dO;
+    the low-res terms of full mode, 4 nb^2 d multiply-adds per head, are
+    left out) over that time.
 Only one GPU is used; --gpus above 1 exits with a message.
 """
 from __future__ import annotations
@@ -134,13 +136,13 @@ def cpu_baseline(w, seconds: float = 10.0):
             "sample": "the whole %s workload (%d heads), %d runs in %.1f s" % (w.name, w.B * w.H, runs, el)}
 
 
-def bench_backward(mra, steps: int, warmup: int) -> dict:
+def bench_backward(mra, steps: int, warmup: int, cfg: str) -> dict:
     import numpy as np
     import torch
 
     import workloads
 
-    w = workloads.get("C3")
+    w = workloads.get(cfg)
     to_dev = lambda n: torch.from_numpy(w.raw(n).view(np.int16)).view(torch.bfloat16).cuda()
     q, k, v = to_dev("q"), to_dev("k"), to_dev("v")
     kw = dict(block_per_row=w.block_per_row, approx_mode=w.approx_mode, initial_prior_first_n_blocks=w.prior_first,
@@ -316,7 +318,7 @@ def main():
         "roofline": roof,
     }
     if not args.no_backward:
-        rec["backward"] = bench_backward(mra, args.steps, args.warmup)
+        rec["backward"] = [bench_backward(mra, args.steps, args.warmup, cfg) for cfg in ("C3", "C4")]
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(rec), flush=True)

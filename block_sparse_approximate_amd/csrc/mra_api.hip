@@ -67,10 +67,11 @@ bool carve(const mra_dims& d, int32_t bpr, int32_t mode, Layout* L) {
 // The backward pass's own workspace (mra_attention_bwd).
 struct BwdLayout {
     int32_t maxch;
-    size_t st_d, ct_ptr, ct_row, rch, cch, rmul, cmul, count, part_dq, part_dk, part_dv, total;
+    size_t st_d, ct_ptr, ct_row, rch, cch, rmul, cmul, count, part_dq, part_dk, part_dv, g, c, et, wt, dqh, dkh,
+        dvh, total;
 };
 
-void carve_bwd(const Layout& L, BwdLayout* W) {
+void carve_bwd(const Layout& L, int32_t mode, BwdLayout* W) {
     const size_t BH = (size_t)L.BH, nb = (size_t)L.nb;
     W->maxch = bwd_max_chunks(L.nb, L.K);
     const size_t slots = BH * (size_t)W->maxch, tile = (size_t)kBlock * L.d * 4;
@@ -87,6 +88,15 @@ void carve_bwd(const Layout& L, BwdLayout* W) {
     W->part_dq = take(slots * tile);
     W->part_dk = take(slots * tile);
     W->part_dv = take(slots * tile);
+    const bool full = mode == MRA_APPROX_FULL;
+    const size_t blk = BH * nb * (size_t)L.d * 4, cell = BH * nb * nb * 4;
+    W->g = full ? take(blk) : 0;
+    W->c = full ? take(BH * nb * 4) : 0;
+    W->et = full ? take(cell) : 0;
+    W->wt = full ? take(cell) : 0;
+    W->dqh = full ? take(blk) : 0;
+    W->dkh = full ? take(blk) : 0;
+    W->dvh = full ? take(blk) : 0;
     W->total = o;
 }
 
@@ -308,7 +318,7 @@ MRA_API mra_status mra_backward_workspace_size(const mra_dims* dims, int32_t blo
     Layout L;
     if (!carve(*dims, block_per_row, approx_mode, &L)) return MRA_ERR_SEQ_LEN;
     BwdLayout W;
-    carve_bwd(L, &W);
+    carve_bwd(L, approx_mode, &W);
     *bytes = W.total;
     return MRA_OK;
 }
@@ -322,12 +332,11 @@ MRA_API mra_status mra_attention_bwd(const mra_dims* dims, const void* q, const 
     mra_status st = check_call(dims, q, k, v, mask, block_per_row, approx_mode, prior_first, prior_diag, out,
                                workspace, workspace_bytes, true, &L);
     if (st != MRA_OK) return st;
-    if (approx_mode != MRA_APPROX_SPARSE) return MRA_ERR_MODE;
     if (dims->dtype != MRA_BF16) return MRA_ERR_DTYPE;
     if (!dout || !dq || !dk || !dv) return MRA_ERR_NULL;
     if (misaligned(dout) || misaligned(dq) || misaligned(dk) || misaligned(dv)) return MRA_ERR_ALIGN;
     BwdLayout W;
-    carve_bwd(L, &W);
+    carve_bwd(L, approx_mode, &W);
     if (!bwd_workspace || bwd_workspace_bytes < W.total) return MRA_ERR_WORKSPACE;
     if (misaligned(bwd_workspace)) return MRA_ERR_ALIGN;
     const size_t tb = (size_t)dims->batch * dims->heads * dims->seq_len * dims->head_dim * 2;
@@ -361,6 +370,14 @@ MRA_API mra_status mra_attention_bwd(const mra_dims* dims, const void* q, const 
     p.bwd_part_dq = reinterpret_cast<float*>(bw + W.part_dq);
     p.bwd_part_dk = reinterpret_cast<float*>(bw + W.part_dk);
     p.bwd_part_dv = reinterpret_cast<float*>(bw + W.part_dv);
+    auto fl = [&](size_t off) { return off ? reinterpret_cast<float*>(bw + off) : nullptr; };
+    p.bwd_g = fl(W.g);
+    p.bwd_c = fl(W.c);
+    p.bwd_et = fl(W.et);
+    p.bwd_wt = fl(W.wt);
+    p.bwd_dqh = fl(W.dqh);
+    p.bwd_dkh = fl(W.dkh);
+    p.bwd_dvh = fl(W.dvh);
     return launch_bwd(p, static_cast<hipStream_t>(stream)) == hipSuccess ? MRA_OK : MRA_ERR_HIP;
 }
 

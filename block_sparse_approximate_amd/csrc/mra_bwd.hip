@@ -1,23 +1,38 @@
-// mra_bwd.hip — gradients of the sparse-mode forward with respect to q, k
-// and v ([MRA] "第三步": the block products are autograd functions whose
-// backward reuses the same kernels on transposed block indices, so the
-// selection of step 2 is a constant of the backward pass; in sparse mode the
-// output is the high-resolution part alone, [MRA] "第四步").
+// mra_bwd.hip — gradients of the forward with respect to q, k and v
+// ([MRA] "第三步": the block products are autograd functions whose backward
+// reuses the same kernels on transposed block indices, so the selection of
+// step 2 is a constant of the backward pass; [MRA] "第四步": in full mode the
+// low-resolution branch is ordinary tensor code and is differentiated too,
+// down through the block means).
 //
 // With the selection fixed, a valid query token t of block row i attends to
 // the valid keys u of its selected blocks:
 //   s_u = tau q_t . k_u,  P_u = 2^(s_u log2e - m_t) / l_t,  O_t = sum_u P_u v_u
-// and for dO = dL/dO, D_t = dO_t . O_t:
+// (+ the low-res part in full mode, included in m_t and l_t) and for
+// dO = dL/dO, D_t = dO_t . O_t:
 //   dS_u = P_u (dO_t . v_u - D_t),  dq_t = tau sum_u dS_u k_u,
 //   dk_u = tau sum_t dS_u q_t,      dv_u = sum_t P_u dO_t.
+// Full mode adds, for the unselected non-empty cells (i, j) with forward
+// weight w_ij = cnt_j 2^((S_ij - m_i) log2e), the low-res probability of
+// token t, w_ij a_t with a_t = 2^(m_i log2e - m_t) / l_t.  Summed over the
+// block's tokens this needs only
+//   g_i = sum_t a_t dO_t,  c_i = sum_t a_t D_t,
+//   e_ij = w_ij (g_i . vhat_j - c_i)       (gradient of the logit S_ij)
+//   dqhat_i = tau sum_j e_ij khat_j,  dkhat_j = tau sum_i e_ij qhat_i,
+//   dvhat_j = sum_i w_ij g_i,
+// and a block mean hands its gradient to each valid token of the block
+// divided by the block's count (added in the dq / dkv / reduce epilogues).
 //
 // The forward left in its workspace the selection and each token's softmax
 // statistics (m_t in log2 units and 1 / l_t), so no statistics pass is
-// needed.  Four kernels, in stream order after that forward call:
+// needed.  The kernels, in stream order after that forward call:
 //   plan_kernel    per head: the query-block rows that selected each key
 //                  block (column lists of the selection bitmap, ascending),
 //                  and both lists cut into chunks of at most kChunkB blocks
 //                  (a row or column with none is one empty chunk)
+//   lr_rows_kernel full mode: g_i, c_i, e_ij, w_ij and dqhat_i, one wave
+//                  per block row over key-block tiles staged in LDS
+//   lr_cols_kernel full mode: dkhat_j, dvhat_j, one wave per key block
 //   dq_kernel      one wave per row chunk (query block i, some of its
 //                  selected blocks j):
 //                    S^T = K_j Q_i^T, dP^T = V_j dO_i^T   (lane = query)
@@ -120,8 +135,10 @@ __device__ __forceinline__ f32x16 zero16() {
 }
 
 // A 32 x 64 result tile pair (channels 0..31 in a0, 32..63 in a1; lane l
-// holds token row l % 32) times `scale` to bf16 memory at g.
-__device__ __forceinline__ void store_rows(uint16_t* g, const f32x16& a0, const f32x16& a1, float scale, int lane) {
+// holds token row l % 32) times `scale`, plus add[channel] * aw when add is
+// given (a block mean's gradient share), to bf16 memory at g.
+__device__ __forceinline__ void store_rows(uint16_t* g, const f32x16& a0, const f32x16& a1, float scale, int lane,
+                                           const float* add = nullptr, float aw = 0.f) {
     const int n = lane & 31, h = lane >> 5;
 #pragma unroll
     for (int mt = 0; mt < 2; mt++)
@@ -129,11 +146,42 @@ __device__ __forceinline__ void store_rows(uint16_t* g, const f32x16& a0, const 
         for (int gq = 0; gq < 4; gq++) {
             const f32x16& a = mt == 0 ? a0 : a1;
             const int d0 = 32 * mt + 8 * gq + 4 * h;
+            float x[4];
+#pragma unroll
+            for (int e = 0; e < 4; e++) x[e] = a[4 * gq + e] * scale;
+            if (add) {
+                const float4 ad = *reinterpret_cast<const float4*>(add + d0);
+                x[0] += ad.x * aw; x[1] += ad.y * aw; x[2] += ad.z * aw; x[3] += ad.w * aw;
+            }
             uint2 pk;
-            pk.x = (uint32_t)float_to_bf16(a[4 * gq] * scale) | ((uint32_t)float_to_bf16(a[4 * gq + 1] * scale) << 16);
-            pk.y = (uint32_t)float_to_bf16(a[4 * gq + 2] * scale) | ((uint32_t)float_to_bf16(a[4 * gq + 3] * scale) << 16);
+            pk.x = (uint32_t)float_to_bf16(x[0]) | ((uint32_t)float_to_bf16(x[1]) << 16);
+            pk.y = (uint32_t)float_to_bf16(x[2]) | ((uint32_t)float_to_bf16(x[3]) << 16);
             *reinterpret_cast<uint2*>(g + n * kHeadDim + d0) = pk;
         }
+}
+
+// D_t = dO_t . O_t for token n = lane % 32 of a block (rows of 64 bf16
+// channels): lane (n, h) sums channels 32 h .. 32 h + 31, then the halves.
+__device__ __forceinline__ float row_dot(const uint16_t* dO, const uint16_t* O, int lane) {
+    const int n = lane & 31, h = lane >> 5;
+    float s = 0.f;
+#pragma unroll
+    for (int x = 0; x < 4; x++) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(dO + n * kHeadDim + 32 * h + 8 * x);
+        const u32x4 o = *reinterpret_cast<const u32x4*>(O + n * kHeadDim + 32 * h + 8 * x);
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            s += bf16_to_float(a[e] & 0xFFFFu) * bf16_to_float(o[e] & 0xFFFFu);
+            s += bf16_to_float(a[e] >> 16) * bf16_to_float(o[e] >> 16);
+        }
+    }
+    return s + __shfl_xor(s, 32, 64);
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
 }
 
 // ---------------------------------------------------------------- plan
@@ -228,6 +276,151 @@ __device__ __forceinline__ void store_part(float* g, const f32x16& a0, const f32
         }
 }
 
+// ---------------------------------------------------------------- low-res (full mode)
+constexpr int kLrWaves = 8;            // block rows (columns) per workgroup, one per wave
+constexpr int kLrThreads = kLrWaves * 64;
+constexpr int kLrTile = 64;            // key blocks (query blocks) per staged tile
+constexpr int kLrVStr = kHeadDim + 1;  // vhat tile stride: lane j reads row j without bank conflicts
+
+// Workgroup (bh, rows i0 .. i0 + 7), wave w takes row i = i0 + w:
+//   phase 1: a_t, D_t of the row's tokens; g_i (lane = channel), c_i
+//   phase 2: per tile of 64 key blocks (vhat, khat staged): lane = j forms
+//            w_ij (the forward's weight, 0 for selected or empty cells) and
+//            e_ij; then lane = channel adds e_ij khat_j to dqhat_i.  E and W
+//            go out transposed ([j][i], 8 consecutive rows per j).
+__global__ __launch_bounds__(kLrThreads) void lr_rows_kernel(Params p) {
+    __shared__ float vt[kLrTile][kLrVStr];
+    __shared__ __align__(16) float kt[kLrTile][kHeadDim];
+    __shared__ float gs[kLrWaves][kHeadDim];
+    __shared__ float es[kLrWaves][kLrTile];
+    __shared__ float ws[kLrWaves][kLrTile];
+    __shared__ float al[kLrWaves][kBlock];
+    const int nb = p.nb, groups = (nb + kLrWaves - 1) / kLrWaves;
+    const int bh = blockIdx.x / groups, i0 = (blockIdx.x - bh * groups) * kLrWaves;
+    if (bh >= p.BH) return;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int i = i0 + wave, b = bh / p.H;
+    const bool act = i < nb;
+    const float tau = 1.0f / __builtin_sqrtf((float)p.d);
+    const size_t hrow = (size_t)bh * nb + (act ? i : 0);
+    const float mi = p.rowmax[hrow];
+
+    float ci = 0.f;
+    if (act) {
+        const size_t rowoff = ((size_t)bh * p.N + (size_t)i * kBlock) * kHeadDim;
+        const uint16_t* dO = static_cast<const uint16_t*>(p.dout) + rowoff;
+        const int n = lane & 31, h = lane >> 5;
+        const float D = row_dot(dO, static_cast<const uint16_t*>(p.fout) + rowoff, lane);
+        const size_t t = (size_t)bh * p.N + (size_t)i * kBlock + n;
+        const float mu = p.st_m[t], linv = p.st_linv[t];
+        const float a = linv > 0.f ? __builtin_amdgcn_exp2f(mi * kLog2e - mu) * linv : 0.f;
+        if (h == 0) al[wave][n] = a;
+        ci = wave_sum(h == 0 ? a * D : 0.f);
+        wave_sync_lds();
+        float g = 0.f;
+#pragma unroll 8
+        for (int u = 0; u < kBlock; u++) g += al[wave][u] * bf16_to_float(dO[u * kHeadDim + lane]);
+        gs[wave][lane] = g;
+        p.bwd_g[hrow * kHeadDim + lane] = g;
+        if (lane == 0) p.bwd_c[hrow] = ci;
+    }
+
+    const float* S = p.logits + hrow * nb;
+    const uint32_t* sbits = p.selbits + hrow * p.words;
+    const int32_t* cnt = p.cnt + (size_t)b * nb;
+    const float* vh = p.vhat + (size_t)bh * nb * kHeadDim;
+    const float* kh = p.khat + (size_t)bh * nb * kHeadDim;
+    float dqh = 0.f;
+    for (int j0 = 0; j0 < nb; j0 += kLrTile) {
+        __syncthreads();   // every wave is done with the previous tile
+        for (int x = tid; x < kLrTile * (kHeadDim / 4); x += kLrThreads) {
+            const int r = x / (kHeadDim / 4), c4 = (x % (kHeadDim / 4)) * 4, j = j0 + r;
+            float4 vv = make_float4(0.f, 0.f, 0.f, 0.f), kk = vv;
+            if (j < nb) {
+                vv = *reinterpret_cast<const float4*>(vh + (size_t)j * kHeadDim + c4);
+                kk = *reinterpret_cast<const float4*>(kh + (size_t)j * kHeadDim + c4);
+            }
+            vt[r][c4] = vv.x; vt[r][c4 + 1] = vv.y; vt[r][c4 + 2] = vv.z; vt[r][c4 + 3] = vv.w;
+            *reinterpret_cast<float4*>(&kt[r][c4]) = kk;
+        }
+        __syncthreads();
+        if (act) {
+            const int j = j0 + lane;
+            float w = 0.f;
+            if (j < nb && !((sbits[j >> 5] >> (j & 31)) & 1u)) w = lowres_weight(S[j], mi, cnt[j]);
+            float T = 0.f;
+#pragma unroll 16
+            for (int c = 0; c < kHeadDim; c++) T += gs[wave][c] * vt[lane][c];
+            es[wave][lane] = w * (T - ci);
+            ws[wave][lane] = w;
+            wave_sync_lds();
+#pragma unroll 16
+            for (int u = 0; u < kLrTile; u++) dqh += es[wave][u] * kt[u][lane];
+        }
+        __syncthreads();   // the tile's e and w of every row
+        if (tid < 2 * kLrTile) {
+            const int u = tid & (kLrTile - 1), j = j0 + u;
+            if (j < nb) {
+                float* dst = (tid < kLrTile ? p.bwd_et : p.bwd_wt) + ((size_t)bh * nb + j) * nb + i0;
+                const float (*src)[kLrTile] = tid < kLrTile ? es : ws;
+                for (int r = 0; r < kLrWaves && i0 + r < nb; r++) dst[r] = src[r][u];
+            }
+        }
+    }
+    if (act) p.bwd_dqh[hrow * kHeadDim + lane] = tau * dqh;
+}
+
+// Workgroup (bh, key blocks j0 .. j0 + 7), wave w takes column j = j0 + w,
+// lane = channel: dvhat_j = sum_i w_ij g_i, dkhat_j = tau sum_i e_ij qhat_i
+// over tiles of 64 query blocks (g and qhat staged, shared by the waves).
+__global__ __launch_bounds__(kLrThreads) void lr_cols_kernel(Params p) {
+    __shared__ __align__(16) float gt[kLrTile][kHeadDim];
+    __shared__ __align__(16) float qt[kLrTile][kHeadDim];
+    __shared__ float es[kLrWaves][kLrTile];
+    __shared__ float ws[kLrWaves][kLrTile];
+    const int nb = p.nb, groups = (nb + kLrWaves - 1) / kLrWaves;
+    const int bh = blockIdx.x / groups, j0 = (blockIdx.x - bh * groups) * kLrWaves;
+    if (bh >= p.BH) return;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int j = j0 + wave;
+    const bool act = j < nb;
+    const float tau = 1.0f / __builtin_sqrtf((float)p.d);
+    const float* gh = p.bwd_g + (size_t)bh * nb * kHeadDim;
+    const float* qh = p.qhat + (size_t)bh * nb * kHeadDim;
+    const size_t col = ((size_t)bh * nb + (act ? j : 0)) * nb;
+    float dv = 0.f, dk = 0.f;
+    for (int r0 = 0; r0 < nb; r0 += kLrTile) {
+        __syncthreads();
+        for (int x = tid; x < kLrTile * (kHeadDim / 4); x += kLrThreads) {
+            const int r = x / (kHeadDim / 4), c4 = (x % (kHeadDim / 4)) * 4, i = r0 + r;
+            float4 gg = make_float4(0.f, 0.f, 0.f, 0.f), qq = gg;
+            if (i < nb) {
+                gg = *reinterpret_cast<const float4*>(gh + (size_t)i * kHeadDim + c4);
+                qq = *reinterpret_cast<const float4*>(qh + (size_t)i * kHeadDim + c4);
+            }
+            *reinterpret_cast<float4*>(&gt[r][c4]) = gg;
+            *reinterpret_cast<float4*>(&qt[r][c4]) = qq;
+        }
+        if (act) {
+            const int i = r0 + lane;
+            es[wave][lane] = i < nb ? p.bwd_et[col + i] : 0.f;
+            ws[wave][lane] = i < nb ? p.bwd_wt[col + i] : 0.f;
+        }
+        __syncthreads();
+        if (act) {
+#pragma unroll 16
+            for (int u = 0; u < kLrTile; u++) {
+                dv += ws[wave][u] * gt[u][lane];
+                dk += es[wave][u] * qt[u][lane];
+            }
+        }
+    }
+    if (act) {
+        p.bwd_dvh[col / nb * kHeadDim + lane] = dv;
+        p.bwd_dkh[col / nb * kHeadDim + lane] = tau * dk;
+    }
+}
+
 // ---------------------------------------------------------------- dQ
 __global__ __launch_bounds__(kThreads) void dq_kernel(Params p) {
     __shared__ __align__(16) uint16_t lds[kWaves][4][kTile];   // per wave: Q_i, dO_i, K_j, V_j
@@ -255,22 +448,11 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(Params p) {
 
     stage(qs, static_cast<const uint16_t*>(p.q) + rowoff, lane);
     stage(dos, dO, lane);
-    // D_t = dO_t . O_t: lane (n, h) takes channels 32 h .. 32 h + 31 of token n
-    float dpart = 0.f;
-#pragma unroll
-    for (int x = 0; x < 4; x++) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(dO + n * kHeadDim + 32 * h + 8 * x);
-        const u32x4 o = *reinterpret_cast<const u32x4*>(Of + n * kHeadDim + 32 * h + 8 * x);
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-            dpart += bf16_to_float(a[e] & 0xFFFFu) * bf16_to_float(o[e] & 0xFFFFu);
-            dpart += bf16_to_float(a[e] >> 16) * bf16_to_float(o[e] >> 16);
-        }
-    }
+    const float dfull = row_dot(dO, Of, lane);
     const size_t t = (size_t)bh * p.N + (size_t)i * kBlock + n;
     const float mu = p.st_m[t], linv = p.st_linv[t];
     const bool qv = linv > 0.f;   // padded and keyless query tokens take no gradient
-    const float Dv = qv ? dpart + __shfl_xor(dpart, 32, 64) : 0.f;
+    const float Dv = qv ? dfull : 0.f;
     if (h == 0) p.st_d[t] = Dv;   // every chunk of the row writes the same value
     const int32_t* cols = p.col + (size_t)bh * p.K;
     wave_sync_lds();
@@ -298,8 +480,15 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(Params p) {
         }
         wave_sync_lds();
     }
-    if (dsc.w < 0) store_rows(static_cast<uint16_t*>(p.dq) + rowoff, dq0, dq1, tau, lane);
-    else store_part(p.bwd_part_dq + ((size_t)bh * maxch + min(dsc.w, maxch - 1)) * kBlock * kHeadDim, dq0, dq1, lane);
+    if (dsc.w < 0) {
+        const float* add = nullptr;
+        float aw = 0.f;
+        if (p.mode == 0) {   // the token's share of dqhat_i
+            add = p.bwd_dqh + ((size_t)bh * nb + i) * kHeadDim;
+            aw = ((p.mbits[(size_t)b * nb + i] >> n) & 1u) ? 1.0f / (float)p.cnt[(size_t)b * nb + i] : 0.f;
+        }
+        store_rows(static_cast<uint16_t*>(p.dq) + rowoff, dq0, dq1, tau, lane, add, aw);
+    } else store_part(p.bwd_part_dq + ((size_t)bh * maxch + min(dsc.w, maxch - 1)) * kBlock * kHeadDim, dq0, dq1, lane);
 }
 
 // ---------------------------------------------------------------- dK, dV
@@ -366,8 +555,16 @@ __global__ __launch_bounds__(kThreads) void dkv_kernel(Params p) {
         wave_sync_lds();
     }
     if (dsc.w < 0) {
-        store_rows(static_cast<uint16_t*>(p.dk) + coloff, dk0, dk1, tau, lane);
-        store_rows(static_cast<uint16_t*>(p.dv) + coloff, dv0, dv1, 1.0f, lane);
+        const float* addk = nullptr;
+        const float* addv = nullptr;
+        float aw = 0.f;
+        if (p.mode == 0) {   // the key's share of dkhat_j, dvhat_j
+            addk = p.bwd_dkh + ((size_t)bh * nb + j) * kHeadDim;
+            addv = p.bwd_dvh + ((size_t)bh * nb + j) * kHeadDim;
+            aw = kvalid ? 1.0f / (float)p.cnt[(size_t)b * nb + j] : 0.f;
+        }
+        store_rows(static_cast<uint16_t*>(p.dk) + coloff, dk0, dk1, tau, lane, addk, aw);
+        store_rows(static_cast<uint16_t*>(p.dv) + coloff, dv0, dv1, 1.0f, lane, addv, aw);
     } else {
         const size_t slot = ((size_t)bh * maxch + min(dsc.w, maxch - 1)) * kBlock * kHeadDim;
         store_part(p.bwd_part_dk + slot, dk0, dk1, lane);
@@ -382,7 +579,7 @@ __global__ __launch_bounds__(kThreads) void dkv_kernel(Params p) {
 constexpr int kRedThreads = 256;
 
 __device__ __forceinline__ void reduce_one(const float* part, int first, int nch, float scale, uint16_t* dst,
-                                           size_t slot0, int tid) {
+                                           size_t slot0, int tid, const float* add, float aw) {
     const int tok = tid >> 3, cg = (tid & 7) * 8;
     float acc[8];
 #pragma unroll
@@ -394,11 +591,17 @@ __device__ __forceinline__ void reduce_one(const float* part, int first, int nch
         acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
         acc[4] += b2.x; acc[5] += b2.y; acc[6] += b2.z; acc[7] += b2.w;
     }
+#pragma unroll
+    for (int e = 0; e < 8; e++) acc[e] *= scale;
+    if (add) {
+#pragma unroll
+        for (int e = 0; e < 8; e++) acc[e] += add[cg + e] * aw;
+    }
     uint4 pk;
-    pk.x = (uint32_t)float_to_bf16(acc[0] * scale) | ((uint32_t)float_to_bf16(acc[1] * scale) << 16);
-    pk.y = (uint32_t)float_to_bf16(acc[2] * scale) | ((uint32_t)float_to_bf16(acc[3] * scale) << 16);
-    pk.z = (uint32_t)float_to_bf16(acc[4] * scale) | ((uint32_t)float_to_bf16(acc[5] * scale) << 16);
-    pk.w = (uint32_t)float_to_bf16(acc[6] * scale) | ((uint32_t)float_to_bf16(acc[7] * scale) << 16);
+    pk.x = (uint32_t)float_to_bf16(acc[0]) | ((uint32_t)float_to_bf16(acc[1]) << 16);
+    pk.y = (uint32_t)float_to_bf16(acc[2]) | ((uint32_t)float_to_bf16(acc[3]) << 16);
+    pk.z = (uint32_t)float_to_bf16(acc[4]) | ((uint32_t)float_to_bf16(acc[5]) << 16);
+    pk.w = (uint32_t)float_to_bf16(acc[6]) | ((uint32_t)float_to_bf16(acc[7]) << 16);
     *reinterpret_cast<uint4*>(dst + tok * kHeadDim + cg) = pk;
 }
 
@@ -415,11 +618,20 @@ __global__ __launch_bounds__(kRedThreads) void reduce_kernel(Params p) {
     const int first = max(m.y, 0), nch = max(0, min(m.z, maxch - first));
     const float tau = 1.0f / __builtin_sqrtf((float)p.d);
     const size_t off = ((size_t)bh * p.N + (size_t)blk * kBlock) * kHeadDim, slot0 = (size_t)bh * maxch;
+    // full mode: the token's share of its block mean's gradient
+    const int b = bh / p.H, tok = threadIdx.x >> 3;
+    const bool full = p.mode == 0;
+    const float aw = (full && ((p.mbits[(size_t)b * nb + blk] >> tok) & 1u)) ? 1.0f / (float)p.cnt[(size_t)b * nb + blk]
+                                                                              : 0.f;
+    const size_t hb = ((size_t)bh * nb + blk) * kHeadDim;
     if (side == 0) {
-        reduce_one(p.bwd_part_dq, first, nch, tau, static_cast<uint16_t*>(p.dq) + off, slot0, threadIdx.x);
+        reduce_one(p.bwd_part_dq, first, nch, tau, static_cast<uint16_t*>(p.dq) + off, slot0, threadIdx.x,
+                   full ? p.bwd_dqh + hb : nullptr, aw);
     } else {
-        reduce_one(p.bwd_part_dk, first, nch, tau, static_cast<uint16_t*>(p.dk) + off, slot0, threadIdx.x);
-        reduce_one(p.bwd_part_dv, first, nch, 1.0f, static_cast<uint16_t*>(p.dv) + off, slot0, threadIdx.x);
+        reduce_one(p.bwd_part_dk, first, nch, tau, static_cast<uint16_t*>(p.dk) + off, slot0, threadIdx.x,
+                   full ? p.bwd_dkh + hb : nullptr, aw);
+        reduce_one(p.bwd_part_dv, first, nch, 1.0f, static_cast<uint16_t*>(p.dv) + off, slot0, threadIdx.x,
+                   full ? p.bwd_dvh + hb : nullptr, aw);
     }
 }
 
@@ -429,10 +641,22 @@ int bwd_max_chunks(int nb, int64_t K) { return nb + (int)((K + kChunkB - 1) / kC
 
 hipError_t launch_bwd(const Params& p, hipStream_t s) {
     if (p.dtype != 1 || p.d != kHeadDim || p.nb > kTrThreads) return hipErrorInvalidValue;
+    if (p.mode == 0 && (!p.bwd_g || !p.bwd_c || !p.bwd_et || !p.bwd_wt || !p.bwd_dqh || !p.bwd_dkh || !p.bwd_dvh ||
+                        !p.vhat))
+        return hipErrorInvalidValue;
     const size_t plan_lds = (size_t)p.nb * p.words * 4;
     hipLaunchKernelGGL(plan_kernel, dim3(p.BH), dim3(kTrThreads), plan_lds, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (p.mode == 0) {
+        const unsigned lr_grid = (unsigned)((int64_t)p.BH * ((p.nb + kLrWaves - 1) / kLrWaves));
+        hipLaunchKernelGGL(lr_rows_kernel, dim3(lr_grid), dim3(kLrThreads), 0, s, p);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(lr_cols_kernel, dim3(lr_grid), dim3(kLrThreads), 0, s, p);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     const int64_t waves = (int64_t)p.BH * p.bwd_maxch;
     const unsigned grid = (unsigned)((waves + kWaves - 1) / kWaves);
     hipLaunchKernelGGL(dq_kernel, dim3(grid), dim3(kThreads), 0, s, p);

@@ -114,6 +114,14 @@ struct Params {
     float* bwd_part_dq;    // [BH, maxch, 32, d] fp32 partials of chunks of multi-chunk rows
     float* bwd_part_dk;    // [BH, maxch, 32, d] and columns
     float* bwd_part_dv;
+    // backward, full mode: the low-resolution branch through the block means
+    float* bwd_g;          // [BH, nb, d]  g_i = sum over block i's tokens of a_t dO_t
+    float* bwd_c;          // [BH, nb]     c_i = sum over block i's tokens of a_t D_t
+    float* bwd_et;         // [BH, nb, nb] E^T: e_ij = w_ij (g_i . vhat_j - c_i) at [j][i]
+    float* bwd_wt;         // [BH, nb, nb] W^T: w_ij of unselected cells (0 for selected) at [j][i]
+    float* bwd_dqh;        // [BH, nb, d]  gradients of the block means qhat, khat, vhat
+    float* bwd_dkh;
+    float* bwd_dvh;
     int32_t* error;        // device error flag (0 = fine)
     int32_t attn_wph;      // attention stream: waves sharing one head's blocks
     int32_t attn_seq;      // 1: those are all the waves of an XCD, which take the XCD's heads in turn

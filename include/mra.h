@@ -149,8 +149,9 @@ mra_status mra_debug_select(const mra_dims* dims, const float* logits, const int
 
 /* Bytes of the backward pass's own workspace for these dimensions and
  * selection parameters (mra_attention_bwd's bwd_workspace): the dO . O row
- * terms, the transposed selection, the work chunks and fp32 partial
- * gradients.  Status as for mra_workspace_size. */
+ * terms, the transposed selection, the work chunks, fp32 partial gradients
+ * and in full mode the low-resolution gradient terms (block-level vectors and
+ * two [nb, nb] fp32 matrices per head).  Status as for mra_workspace_size. */
 mra_status mra_backward_workspace_size(const mra_dims* dims, int32_t block_per_row, int32_t approx_mode,
                                        size_t* bytes);
 
@@ -167,11 +168,12 @@ mra_status mra_backward_workspace_size(const mra_dims* dims, int32_t block_per_r
  *   bwd_workspace  device scratch of mra_backward_workspace_size bytes
  *             (16-byte aligned, caller-owned, no contents kept between
  *             calls; MRA_ERR_WORKSPACE if smaller).
- * Must be queued after that forward call (stream order).  Supported: sparse
- * mode (MRA_ERR_MODE otherwise), bf16 (MRA_ERR_DTYPE otherwise).  dq, dk, dv
- * and bwd_workspace must be 16-byte aligned and overlap no input or each
- * other (MRA_ERR_ALIAS).  The result does not depend on scheduling: partial
- * sums are added in a fixed order. */
+ * Must be queued after that forward call (stream order).  Both modes; in
+ * full mode the low-resolution branch is differentiated too ([MRA] "第四步"),
+ * through the block means to every valid token of each block.  bf16 only
+ * (MRA_ERR_DTYPE otherwise).  dq, dk, dv and bwd_workspace must be 16-byte
+ * aligned and overlap no input or each other (MRA_ERR_ALIAS).  The result
+ * does not depend on scheduling: partial sums are added in a fixed order. */
 mra_status mra_attention_bwd(const mra_dims* dims, const void* q, const void* k, const void* v,
                              const uint8_t* mask, int32_t block_per_row, int32_t approx_mode,
                              int32_t prior_first, int32_t prior_diag, const void* out, const void* dout,

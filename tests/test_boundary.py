@@ -136,7 +136,7 @@ def call_bwd(dims=(1, 2, 512, 64, 1), mode=1, dout=DO, dq=DQ, dk=DK, dv=DV, bw=B
 
 @pytest.mark.parametrize("kw,status", [
     (dict(out=None), 1), (dict(dout=None), 1), (dict(dq=None), 1), (dict(dv=None), 1),
-    (dict(mode=0), 6), (dict(dims=(1, 2, 512, 64, 0)), 5), (dict(ws=None), 10),
+    (dict(mode=2), 6), (dict(mode=-1), 6), (dict(dims=(1, 2, 512, 64, 0)), 5), (dict(ws=None), 10),
     (dict(bw=None), 10), (dict(bw_bytes=4096), 10),
     (dict(dq=Q), 9), (dict(dk=O + 64), 9), (dict(dv=DQ), 9), (dict(dq=BW), 9), (dict(bw=DO), 9),
     (dict(dq=DQ + 8), 12), (dict(bw=BW + 8), 12),
@@ -150,6 +150,7 @@ def test_backward_workspace_size_grows_and_validates():
     big = mra.backward_workspace_size(2, 12, 4096)
     assert 0 < small < big
     assert mra.backward_workspace_size(2, 12, 4096, block_per_row=8) > big
+    assert mra.backward_workspace_size(2, 12, 4096, approx_mode="full") > big   # the low-res terms' buffers
     with pytest.raises(mra.MraError) as e:
         mra.backward_workspace_size(1, 1, 100)
     assert e.value.status == 3

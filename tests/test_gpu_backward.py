@@ -1,5 +1,6 @@
 """GPU parity of the backward pass (mra_attention_bwd, through the C ABI)
-against the CPU oracle's gradients (oracle.mra_backward).
+against the CPU oracle's gradients (oracle.mra_backward), in sparse and full
+mode.
 
 The gradients run in bf16 operands with fp32 accumulation: the inputs, P and
 dS enter the products rounded to bf16 (relative error up to 2^-9 each), and
@@ -38,16 +39,16 @@ def bf16_round(x):
 def run_case(mra, w, seed=7, bwd_workspace=None):
     q, k, v = to_dev(w.raw("q")), to_dev(w.raw("k")), to_dev(w.raw("v"))
     mask = None if w.mask is None else torch.from_numpy(w.mask).cuda()
-    kw = dict(block_per_row=w.block_per_row, approx_mode="sparse", initial_prior_first_n_blocks=w.prior_first,
+    kw = dict(block_per_row=w.block_per_row, approx_mode=w.approx_mode, initial_prior_first_n_blocks=w.prior_first,
               initial_prior_diagonal_n_blocks=w.prior_diag)
-    ws = torch.empty(mra.workspace_size(w.B, w.H, w.N, w.d, torch.bfloat16, w.block_per_row, "sparse"),
+    ws = torch.empty(mra.workspace_size(w.B, w.H, w.N, w.d, torch.bfloat16, w.block_per_row, w.approx_mode),
                      dtype=torch.uint8, device="cuda")
     out = mra.attention(q, k, v, mask, workspace=ws, **kw)
     g16 = bf16_round(np.random.default_rng(seed).standard_normal(q.shape).astype(np.float32))
     dq, dk, dv = mra.attention_backward(q, k, v, out, g16.cuda(), ws, mask, bwd_workspace=bwd_workspace, **kw)
     torch.cuda.synchronize()
     got = [t.float().cpu().numpy() for t in (dq, dk, dv)]
-    ref = oracle.mra_backward(w.q, w.k, w.v, g16.float().numpy(), w.mask, w.block_per_row, "sparse",
+    ref = oracle.mra_backward(w.q, w.k, w.v, g16.float().numpy(), w.mask, w.block_per_row, w.approx_mode,
                               w.prior_first, w.prior_diag)
     return got, ref
 
@@ -68,8 +69,8 @@ def check(name, got, ref):
         assert mean_rel <= TOL_BWD["mean_rel"], (label, mean_rel)
 
 
-def small(name, B, H, N, seed=0, mask=None, **kw):
-    return workloads.iid(name, B, H, N, dtype="bf16", seed=seed, scale=0.7, mask=mask, approx_mode="sparse", **kw)
+def small(name, B, H, N, seed=0, mask=None, mode="sparse", **kw):
+    return workloads.iid(name, B, H, N, dtype="bf16", seed=seed, scale=0.7, mask=mask, approx_mode=mode, **kw)
 
 
 def ragged_mask(B, N, seed):
@@ -91,19 +92,23 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("mode", ["sparse", "full"])
 @pytest.mark.parametrize("name,kw", CASES, ids=[c[0] for c in CASES])
-def test_backward_matches_oracle(mra, name, kw):
-    w = small(name, **kw)
-    print("case", name, w, flush=True)
+def test_backward_matches_oracle(mra, name, kw, mode):
+    w = small(name, mode=mode, **kw)
+    print("case", name, mode, w, flush=True)
     got, ref = run_case(mra, w)
     check(name, got, ref)
 
 
-def test_backward_named_sparse_workload(mra):
-    w = workloads.get("C3")   # bf16, B=2, H=12, N=4096, sparse, priors
+@pytest.mark.parametrize("cfg", ["C3", "C4", "C2"])
+def test_backward_named_workload(mra, cfg):
+    # C3: bf16 B=2 H=12 N=4096 sparse with priors; C4: the same shape in full
+    # mode on clustered inputs; C2: bf16 B=8 H=12 N=512 full mode, ragged mask
+    w = workloads.get(cfg)
     print("case", w, flush=True)
     got, ref = run_case(mra, w)
-    check("C3", got, ref)
+    check(cfg, got, ref)
 
 
 def test_backward_all_selected_equals_dense_autograd(mra):
@@ -117,20 +122,45 @@ def test_backward_all_selected_equals_dense_autograd(mra):
     check("dense", got, [t.grad.numpy() for t in (tq, tk, tv)])
 
 
-def test_backward_is_deterministic(mra):
-    w = small("det", B=1, H=2, N=1024, block_per_row=3, seed=4)
+@pytest.mark.parametrize("mode", ["sparse", "full"])
+def test_backward_is_deterministic(mra, mode):
+    w = small("det", B=1, H=2, N=1024, block_per_row=3, seed=4, prior_first=1, mode=mode)
     a, _ = run_case(mra, w)
     b, _ = run_case(mra, w)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
 
 
+def test_backward_full_block_constant_qk_matches_dense_along_blocks(mra):
+    # rows of q and k equal within each 32-token block: there the low-res
+    # branch is exact, so full mode coincides with dense attention on the
+    # subspace of block-constant q and k.  Derivatives along that subspace
+    # agree: dv everywhere (P is constant across a key block) and dq, dk
+    # summed over each block (the per-token parts off the subspace differ:
+    # a block mean spreads its gradient evenly).  Dense gradients: torch
+    # autograd in fp64 on the CPU.
+    rng = np.random.default_rng(21)
+    B, H, N, d = 1, 2, 256, 64
+    qb = np.repeat(rng.standard_normal((B, H, N // 32, d)).astype(np.float32) * 0.7, 32, axis=2)
+    kb = np.repeat(rng.standard_normal((B, H, N // 32, d)).astype(np.float32) * 0.7, 32, axis=2)
+    vv = rng.standard_normal((B, H, N, d)).astype(np.float32)
+    w = workloads.from_arrays("blockconst", qb, kb, vv, dtype="bf16", block_per_row=2, approx_mode="full")
+    got, _ = run_case(mra, w, seed=22)
+    g = bf16_round(np.random.default_rng(22).standard_normal((B, H, N, d)).astype(np.float32)).double()
+    tq, tk, tv = (torch.from_numpy(np.asarray(x, np.float64)).requires_grad_(True) for x in (w.q, w.k, w.v))
+    torch.nn.functional.scaled_dot_product_attention(tq, tk, tv).backward(g)
+    dense = [t.grad.numpy() for t in (tq, tk, tv)]
+    bsum = lambda x: x.reshape(B, H, N // 32, 32, d).sum(axis=3)
+    check("blockconst", [bsum(got[0]), bsum(got[1]), got[2]], [bsum(dense[0]), bsum(dense[1]), dense[2]])
+
+
 def test_backward_reused_workspace_matches_fresh(mra):
     # a backward workspace left over from a larger call holds stale chunk
     # lists and partials; nothing of it may leak into the next call
-    big = small("big", B=1, H=2, N=2048, block_per_row=3, prior_first=2, seed=11)
-    little = small("little", B=1, H=3, N=512, block_per_row=2, prior_diag=3, seed=12)
-    bw = torch.empty(mra.backward_workspace_size(1, 2, 2048, block_per_row=3), dtype=torch.uint8, device="cuda")
+    big = small("big", B=1, H=2, N=2048, block_per_row=3, prior_first=2, seed=11, mode="full")
+    little = small("little", B=1, H=3, N=512, block_per_row=2, prior_diag=3, seed=12, mode="full")
+    bw = torch.empty(mra.backward_workspace_size(1, 2, 2048, block_per_row=3, approx_mode="full"),
+                     dtype=torch.uint8, device="cuda")
     run_case(mra, big, bwd_workspace=bw)
     reused, ref = run_case(mra, little, bwd_workspace=bw)
     fresh, _ = run_case(mra, little)

@@ -81,6 +81,14 @@ def iid(name, B, H, N, d=64, dtype="bf16", scale=1.0, seed=0, block_per_row=4,
     return _finish(w, q, k, v)
 
 
+def from_arrays(name, q, k, v, dtype="bf16", block_per_row=4, approx_mode="full", prior_first=0, prior_diag=0,
+                mask=None) -> Workload:
+    """A workload from given [B, H, N, d] arrays (rounded to bf16 when dtype is bf16)."""
+    B, H, N, d = q.shape
+    w = Workload(name, B, H, N, d, dtype, block_per_row, approx_mode, prior_first, prior_diag, mask=mask)
+    return _finish(w, q, k, v)
+
+
 def c1() -> Workload:
     """fp32, B=1, H=2, N=512, d=64, N(0,1), no mask, bpr 4 (64 of 256), full."""
     return iid("C1-fp32-N512-full", 1, 2, 512, dtype="f32", scale=1.0, seed=1)
