@@ -179,6 +179,8 @@ def main():
     ap.add_argument("--config", default="C4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--only-backward", metavar="CFG", default=None,
+                    help="only time the backward pass on workload CFG (C3 or C4) and print its record")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB fp32 copy (x * 1.0) 10 times, to calibrate HBM counters")
     args = ap.parse_args()
@@ -202,6 +204,12 @@ def main():
 
     import block_sparse_approximate_amd as mra
     import workloads
+
+    if args.only_backward:
+        torch.cuda.set_device(torch.device("cuda:0"))
+        print(json.dumps({"backward": bench_backward(mra, args.steps, args.warmup, args.only_backward)}),
+              flush=True)
+        return
 
     w = workloads.get(args.config)
     dev = torch.device("cuda:0")
