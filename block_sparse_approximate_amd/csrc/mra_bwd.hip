@@ -87,12 +87,18 @@ __device__ __forceinline__ void wave_sync_lds() {
 // A 32 x 64 bf16 block (row-major in memory) into the wave's LDS: lane l
 // moves 16 bytes of token rows l / 8 + 8 x, channels 8 (l % 8) .. +7
 // (whole 128-byte rows per 8 lanes).
-__device__ __forceinline__ void stage(uint16_t* s, const uint16_t* g, int lane) {
-    u32x4 r[4];
+__device__ __forceinline__ void load_blk(u32x4 (&r)[4], const uint16_t* g, int lane) {
 #pragma unroll
     for (int x = 0; x < 4; x++) r[x] = *reinterpret_cast<const u32x4*>(g + ((lane >> 3) + 8 * x) * kHeadDim + (lane & 7) * 8);
+}
+__device__ __forceinline__ void store_blk(uint16_t* s, const u32x4 (&r)[4], int lane) {
 #pragma unroll
     for (int x = 0; x < 4; x++) *reinterpret_cast<u32x4*>(s + ((lane >> 3) + 8 * x) * kStr + (lane & 7) * 8) = r[x];
+}
+__device__ __forceinline__ void stage(uint16_t* s, const uint16_t* g, int lane) {
+    u32x4 r[4];
+    load_blk(r, g, lane);
+    store_blk(s, r, lane);
 }
 
 // MFMA operand piece kc of a staged block: row l % 32, channels 16 kc + 8 (l / 32) .. +7
@@ -178,6 +184,25 @@ __device__ __forceinline__ float row_dot(const uint16_t* dO, const uint16_t* O, 
     return s + __shfl_xor(s, 32, 64);
 }
 
+// Workgroup g runs on XCD g % 8.  With at least 8 heads, all workgroups of
+// head bh go to XCD bh % 8 (the XCD's heads one after another), so the
+// blocks a head re-reads stay in one L2; per_head = workgroups per head.
+__device__ __forceinline__ bool head_slot(int BH, int per_head, int* bh, int* idx) {
+    if (BH >= 8) {
+        const int xcd = blockIdx.x & 7, k = blockIdx.x >> 3, hl = k / per_head;
+        *bh = xcd + 8 * hl;
+        *idx = k - hl * per_head;
+    } else {
+        *bh = blockIdx.x / per_head;
+        *idx = blockIdx.x - *bh * per_head;
+    }
+    return *bh < BH;
+}
+
+inline unsigned head_grid(int BH, int per_head) {
+    return (unsigned)(BH >= 8 ? 8 * (int64_t)((BH + 7) / 8) * per_head : (int64_t)BH * per_head);
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
@@ -213,18 +238,31 @@ __device__ __forceinline__ int plan_scan(int v, int* wsum, int* total) {
 }
 
 __global__ __launch_bounds__(kTrThreads) void plan_kernel(Params p) {
-    extern __shared__ __align__(16) uint32_t bits[];   // [nb, words]
+    extern __shared__ __align__(16) uint32_t cbits[];   // [nb, words]: column j's bitmap over block rows,
+                                                        // then [nb] each column's list start
     __shared__ int wsum[kTrThreads / 64 + 1];
     const int bh = blockIdx.x, nb = p.nb, words = p.words, x = threadIdx.x;
     const int K = (int)p.K, maxch = p.bwd_maxch;
-    const uint32_t* gb = p.selbits + (size_t)bh * nb * words;
-    for (int t = x; t < nb * words; t += kTrThreads) bits[t] = gb[t];
+    const uint32_t* gb = p.selbits + (size_t)bh * nb * words;   // row i's bitmap over key blocks
+    // transpose the bitmap, one (column j, 32-row word wi) per item; the
+    // threads of a wave share wi and read the same row words
+    for (int it = x; it < nb * words; it += kTrThreads) {
+        const int wi = it / nb, j = it - wi * nb;
+        const int i0 = 32 * wi, rows = min(32, nb - i0);
+        uint32_t w[32];   // all 32 row words in flight at once
+#pragma unroll
+        for (int r = 0; r < 32; r++) w[r] = r < rows ? gb[(size_t)(i0 + r) * words + (j >> 5)] : 0u;
+        uint32_t m = 0;
+#pragma unroll
+        for (int r = 0; r < 32; r++) m |= ((w[r] >> (j & 31)) & 1u) << r;
+        cbits[j * words + wi] = m;
+    }
     __syncthreads();
     const bool on = x < nb;
     // thread x: block row x and key block column x
     int ccount = 0;
     if (on)
-        for (int i = 0; i < nb; i++) ccount += (bits[i * words + (x >> 5)] >> (x & 31)) & 1u;
+        for (int wi = 0; wi < words; wi++) ccount += __popc(cbits[x * words + wi]);
     const int32_t* rp = p.row_ptr + (size_t)bh * (nb + 1);
     const int e0 = on ? min(max(rp[x], 0), K) : 0, e1 = on ? min(max(rp[x + 1], e0), K) : 0;
     const int nr = on ? max(1, (e1 - e0 + kChunkB - 1) / kChunkB) : 0;
@@ -239,14 +277,10 @@ __global__ __launch_bounds__(kTrThreads) void plan_kernel(Params p) {
     int32_t* crow = p.ct_row + (size_t)bh * K;
     int4* rch = p.bwd_rch + (size_t)bh * maxch;
     int4* cch = p.bwd_cch + (size_t)bh * maxch;
+    int* cstart = reinterpret_cast<int*>(cbits + nb * words);
     if (on) {
         cptr[x] = cpos;
-        int pos = cpos;
-        for (int i = 0; i < nb; i++)
-            if ((bits[i * words + (x >> 5)] >> (x & 31)) & 1u) {
-                if (pos < K) crow[pos] = i;
-                pos++;
-            }
+        cstart[x] = cpos;
         for (int c = 0; c < nr && rbase + c < maxch; c++)
             rch[rbase + c] = make_int4(x, e0 + c * kChunkB, min(e0 + (c + 1) * kChunkB, e1), nr > 1 ? rbase + c : -1);
         const int c0 = cpos, c1 = min(cpos + ccount, K);
@@ -254,6 +288,21 @@ __global__ __launch_bounds__(kTrThreads) void plan_kernel(Params p) {
             cch[cbase + c] = make_int4(x, c0 + c * kChunkB, min(c0 + (c + 1) * kChunkB, c1), nc > 1 ? cbase + c : -1);
         if (nr > 1) p.bwd_rmul[(size_t)bh * nb + rm] = make_int4(x, rbase, nr, 0);
         if (nc > 1) p.bwd_cmul[(size_t)bh * nb + cm] = make_int4(x, cbase, nc, 0);
+    }
+    // column lists (ascending rows): item (j, wi) writes the rows of word wi
+    // at column j's start plus the bits of its earlier words
+    __syncthreads();
+    for (int it = x; it < nb * words; it += kTrThreads) {
+        const int wi = it / nb, j = it - wi * nb;
+        int pos = cstart[j];
+        for (int w2 = 0; w2 < wi; w2++) pos += __popc(cbits[j * words + w2]);
+        uint32_t m = cbits[j * words + wi];
+        while (m) {
+            const int r = __builtin_ctz(m);
+            m &= m - 1;
+            if (pos >= 0 && pos < K) crow[pos] = 32 * wi + r;
+            pos++;
+        }
     }
     if (x == 0) {
         cptr[nb] = tot_c;
@@ -296,8 +345,9 @@ __global__ __launch_bounds__(kLrThreads) void lr_rows_kernel(Params p) {
     __shared__ float ws[kLrWaves][kLrTile];
     __shared__ float al[kLrWaves][kBlock];
     const int nb = p.nb, groups = (nb + kLrWaves - 1) / kLrWaves;
-    const int bh = blockIdx.x / groups, i0 = (blockIdx.x - bh * groups) * kLrWaves;
-    if (bh >= p.BH) return;
+    int bh, grp;
+    if (!head_slot(p.BH, groups, &bh, &grp)) return;
+    const int i0 = grp * kLrWaves;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int i = i0 + wave, b = bh / p.H;
     const bool act = i < nb;
@@ -379,8 +429,9 @@ __global__ __launch_bounds__(kLrThreads) void lr_cols_kernel(Params p) {
     __shared__ float es[kLrWaves][kLrTile];
     __shared__ float ws[kLrWaves][kLrTile];
     const int nb = p.nb, groups = (nb + kLrWaves - 1) / kLrWaves;
-    const int bh = blockIdx.x / groups, j0 = (blockIdx.x - bh * groups) * kLrWaves;
-    if (bh >= p.BH) return;
+    int bh, grp;
+    if (!head_slot(p.BH, groups, &bh, &grp)) return;
+    const int j0 = grp * kLrWaves;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int j = j0 + wave;
     const bool act = j < nb;
@@ -426,9 +477,9 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(Params p) {
     __shared__ __align__(16) uint16_t lds[kWaves][4][kTile];   // per wave: Q_i, dO_i, K_j, V_j
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nb = p.nb, maxch = p.bwd_maxch;
-    const int64_t g = (int64_t)blockIdx.x * kWaves + wave;
-    if (g >= (int64_t)p.BH * maxch) return;
-    const int bh = (int)(g / maxch), cid = (int)(g - (int64_t)bh * maxch);
+    int bh, wg;
+    if (!head_slot(p.BH, (maxch + kWaves - 1) / kWaves, &bh, &wg)) return;
+    const int cid = wg * kWaves + wave;
     if (cid >= p.bwd_count[bh].x) return;
     const int4 dsc = p.bwd_rch[(size_t)bh * maxch + cid];
     const int i = min(max(dsc.x, 0), nb - 1), b = bh / p.H;
@@ -446,6 +497,18 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(Params p) {
     const float tau = 1.0f / __builtin_sqrtf((float)p.d);
     const float scale2 = tau * kLog2e;
 
+    // the next block's K and V rows and mask word travel in registers while
+    // the current block is computed; the first block's are issued before
+    // the row's own loads
+    const int32_t* cols = p.col + (size_t)bh * p.K;
+    u32x4 kr[4], vr[4];
+    uint32_t kmn = 0;
+    if (e0 < e1) {
+        const int j = min(max(cols[e0], 0), nb - 1);
+        load_blk(kr, Kh + (size_t)j * kBlock * kHeadDim, lane);
+        load_blk(vr, Vh + (size_t)j * kBlock * kHeadDim, lane);
+        kmn = p.mbits[(size_t)b * nb + j];
+    }
     stage(qs, static_cast<const uint16_t*>(p.q) + rowoff, lane);
     stage(dos, dO, lane);
     const float dfull = row_dot(dO, Of, lane);
@@ -454,15 +517,19 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(Params p) {
     const bool qv = linv > 0.f;   // padded and keyless query tokens take no gradient
     const float Dv = qv ? dfull : 0.f;
     if (h == 0) p.st_d[t] = Dv;   // every chunk of the row writes the same value
-    const int32_t* cols = p.col + (size_t)bh * p.K;
     wave_sync_lds();
 
     f32x16 dq0 = zero16(), dq1 = zero16();
     for (int e = e0; e < e1; e++) {
-        const int j = min(max(cols[e], 0), nb - 1);
-        const uint32_t km = p.mbits[(size_t)b * nb + j];
-        stage(ks, Kh + (size_t)j * kBlock * kHeadDim, lane);
-        stage(vs, Vh + (size_t)j * kBlock * kHeadDim, lane);
+        const uint32_t km = kmn;
+        store_blk(ks, kr, lane);
+        store_blk(vs, vr, lane);
+        if (e + 1 < e1) {
+            const int j = min(max(cols[e + 1], 0), nb - 1);
+            load_blk(kr, Kh + (size_t)j * kBlock * kHeadDim, lane);
+            load_blk(vr, Vh + (size_t)j * kBlock * kHeadDim, lane);
+            kmn = p.mbits[(size_t)b * nb + j];
+        }
         wave_sync_lds();
         const f32x16 S = mm4(zero16(), ks, qs, lane);    // S^T: lane = query, registers = keys
         const f32x16 dP = mm4(zero16(), vs, dos, lane);  // dP^T
@@ -497,9 +564,9 @@ __global__ __launch_bounds__(kThreads) void dkv_kernel(Params p) {
     __shared__ __align__(16) float st[kWaves][3][kBlock];      // per wave: m, 1/l, D of block i's tokens
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nb = p.nb, maxch = p.bwd_maxch;
-    const int64_t g = (int64_t)blockIdx.x * kWaves + wave;
-    if (g >= (int64_t)p.BH * maxch) return;
-    const int bh = (int)(g / maxch), cid = (int)(g - (int64_t)bh * maxch);
+    int bh, wg;
+    if (!head_slot(p.BH, (maxch + kWaves - 1) / kWaves, &bh, &wg)) return;
+    const int cid = wg * kWaves + wave;
     if (cid >= p.bwd_count[bh].y) return;
     const int4 dsc = p.bwd_cch[(size_t)bh * maxch + cid];
     const int j = min(max(dsc.x, 0), nb - 1), b = bh / p.H;
@@ -515,23 +582,37 @@ __global__ __launch_bounds__(kThreads) void dkv_kernel(Params p) {
     const float tau = 1.0f / __builtin_sqrtf((float)p.d);
     const float scale2 = tau * kLog2e;
 
+    const int32_t* rows = p.ct_row + (size_t)bh * p.K;
+    const size_t sbase = (size_t)bh * p.N;
+    // the next row block's Q and dO rows and statistics travel in registers
+    // while the current one is computed; the first one's are issued before
+    // the column's own loads
+    u32x4 qr[4], gr[4];
+    float sm = 0.f, sl = 0.f, sd = 0.f;
+    auto fetch = [&](int c) {
+        const int i = min(max(rows[c], 0), nb - 1);
+        load_blk(qr, Q + (size_t)i * kBlock * kHeadDim, lane);
+        load_blk(gr, dO + (size_t)i * kBlock * kHeadDim, lane);
+        const size_t t = sbase + (size_t)i * kBlock + (lane & 31);
+        sm = p.st_m[t];
+        sl = p.st_linv[t];
+        sd = p.st_d[t];
+    };
+    if (c0 < c1) fetch(c0);
     stage(ks, static_cast<const uint16_t*>(p.k) + coloff, lane);
     stage(vs, static_cast<const uint16_t*>(p.v) + coloff, lane);
     const bool kvalid = (p.mbits[(size_t)b * nb + j] >> n) & 1u;   // lane = key n
-    const int32_t* rows = p.ct_row + (size_t)bh * p.K;
-    const size_t sbase = (size_t)bh * p.N;
 
     f32x16 dk0 = zero16(), dk1 = zero16(), dv0 = zero16(), dv1 = zero16();
     for (int c = c0; c < c1; c++) {
-        const int i = min(max(rows[c], 0), nb - 1);
-        stage(qs, Q + (size_t)i * kBlock * kHeadDim, lane);
-        stage(dos, dO + (size_t)i * kBlock * kHeadDim, lane);
+        store_blk(qs, qr, lane);
+        store_blk(dos, gr, lane);
         if (lane < kBlock) {
-            const size_t t = sbase + (size_t)i * kBlock + lane;
-            st[wave][0][lane] = p.st_m[t];
-            st[wave][1][lane] = p.st_linv[t];
-            st[wave][2][lane] = p.st_d[t];
+            st[wave][0][lane] = sm;
+            st[wave][1][lane] = sl;
+            st[wave][2][lane] = sd;
         }
+        if (c + 1 < c1) fetch(c + 1);
         wave_sync_lds();
         const f32x16 S = mm4(zero16(), qs, ks, lane);    // S: lane = key, registers = queries
         const f32x16 dP = mm4(zero16(), dos, vs, lane);  // dP
@@ -584,12 +665,25 @@ __device__ __forceinline__ void reduce_one(const float* part, int first, int nch
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; e++) acc[e] = 0.f;
-    for (int c = 0; c < nch; c++) {
-        const float4* src = reinterpret_cast<const float4*>(part + (slot0 + first + c) * kBlock * kHeadDim +
-                                                            tok * kHeadDim + cg);
-        const float4 a = src[0], b2 = src[1];
-        acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
-        acc[4] += b2.x; acc[5] += b2.y; acc[6] += b2.z; acc[7] += b2.w;
+    const float* base = part + (slot0 + first) * kBlock * kHeadDim + tok * kHeadDim + cg;
+    constexpr int kBatch = 8;   // chunks loaded together; added in chunk order
+    for (int c0 = 0; c0 < nch; c0 += kBatch) {
+        float4 a[kBatch], b2[kBatch];
+#pragma unroll
+        for (int c = 0; c < kBatch; c++) {
+            if (c0 + c < nch) {
+                const float4* src = reinterpret_cast<const float4*>(base + (size_t)(c0 + c) * kBlock * kHeadDim);
+                a[c] = src[0];
+                b2[c] = src[1];
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < kBatch; c++) {
+            if (c0 + c < nch) {
+                acc[0] += a[c].x; acc[1] += a[c].y; acc[2] += a[c].z; acc[3] += a[c].w;
+                acc[4] += b2[c].x; acc[5] += b2[c].y; acc[6] += b2[c].z; acc[7] += b2[c].w;
+            }
+        }
     }
 #pragma unroll
     for (int e = 0; e < 8; e++) acc[e] *= scale;
@@ -605,14 +699,8 @@ __device__ __forceinline__ void reduce_one(const float* part, int first, int nch
     *reinterpret_cast<uint4*>(dst + tok * kHeadDim + cg) = pk;
 }
 
-__global__ __launch_bounds__(kRedThreads) void reduce_kernel(Params p) {
+__device__ void reduce_item(const Params& p, int bh, int x, int side) {
     const int nb = p.nb, maxch = p.bwd_maxch;
-    const int side = blockIdx.x & 1;
-    const int64_t w = blockIdx.x >> 1;
-    const int bh = (int)(w / nb), x = (int)(w - (int64_t)bh * nb);
-    if (bh >= p.BH) return;
-    const int4 cnt = p.bwd_count[bh];
-    if (x >= (side == 0 ? cnt.z : cnt.w)) return;
     const int4 m = (side == 0 ? p.bwd_rmul : p.bwd_cmul)[(size_t)bh * nb + x];
     const int blk = min(max(m.x, 0), nb - 1);
     const int first = max(m.y, 0), nch = max(0, min(m.z, maxch - first));
@@ -635,6 +723,21 @@ __global__ __launch_bounds__(kRedThreads) void reduce_kernel(Params p) {
     }
 }
 
+__global__ __launch_bounds__(kRedThreads) void reduce_kernel(Params p) {
+    const int nb = p.nb;
+    // items (x, bh, side), x slowest: the few rows and columns of several
+    // chunks are the first x of each head, so they spread over the workgroups
+    const int64_t items = 2 * (int64_t)p.BH * nb;
+    for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+        const int side = (int)(it & 1);
+        const int64_t w = it >> 1;
+        const int x = (int)(w / p.BH), bh = (int)(w - (int64_t)x * p.BH);
+        const int4 cnt = p.bwd_count[bh];
+        if (x >= (side == 0 ? cnt.z : cnt.w)) continue;
+        reduce_item(p, bh, x, side);
+    }
+}
+
 }  // namespace
 
 int bwd_max_chunks(int nb, int64_t K) { return nb + (int)((K + kChunkB - 1) / kChunkB); }
@@ -644,12 +747,12 @@ hipError_t launch_bwd(const Params& p, hipStream_t s) {
     if (p.mode == 0 && (!p.bwd_g || !p.bwd_c || !p.bwd_et || !p.bwd_wt || !p.bwd_dqh || !p.bwd_dkh || !p.bwd_dvh ||
                         !p.vhat))
         return hipErrorInvalidValue;
-    const size_t plan_lds = (size_t)p.nb * p.words * 4;
+    const size_t plan_lds = (size_t)p.nb * (p.words + 1) * 4;
     hipLaunchKernelGGL(plan_kernel, dim3(p.BH), dim3(kTrThreads), plan_lds, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (p.mode == 0) {
-        const unsigned lr_grid = (unsigned)((int64_t)p.BH * ((p.nb + kLrWaves - 1) / kLrWaves));
+        const unsigned lr_grid = head_grid(p.BH, (p.nb + kLrWaves - 1) / kLrWaves);
         hipLaunchKernelGGL(lr_rows_kernel, dim3(lr_grid), dim3(kLrThreads), 0, s, p);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -657,15 +760,15 @@ hipError_t launch_bwd(const Params& p, hipStream_t s) {
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const int64_t waves = (int64_t)p.BH * p.bwd_maxch;
-    const unsigned grid = (unsigned)((waves + kWaves - 1) / kWaves);
+    const unsigned grid = head_grid(p.BH, (p.bwd_maxch + kWaves - 1) / kWaves);
     hipLaunchKernelGGL(dq_kernel, dim3(grid), dim3(kThreads), 0, s, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(dkv_kernel, dim3(grid), dim3(kThreads), 0, s, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)(2 * (int64_t)p.BH * p.nb)), dim3(kRedThreads), 0, s, p);
+    const int64_t red_items = 2 * (int64_t)p.BH * p.nb;
+    hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)(red_items < 1024 ? red_items : 1024)), dim3(kRedThreads), 0, s, p);
     return hipGetLastError();
 }
 
