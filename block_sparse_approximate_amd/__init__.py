@@ -26,6 +26,8 @@ _LIB_PATH = os.path.join(_HERE, "libmra.so")
 _lib = None
 
 MODES = {"full": 0, "sparse": 1}
+# step 2's ranking: the row-max-normalised logits (default) or the raw logits
+RANKINGS = {"row_normalized": 0, "raw_logits": 1}
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 
 # Entry points declared in include/mra.h, with their ctypes signatures.
@@ -38,9 +40,10 @@ SIGNATURES = {
     "mra_attention_fwd": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P], ctypes.c_int),
     "mra_attention_fwd_profiled": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P, _P],
                                    ctypes.c_int),
-    "mra_debug_stages": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
-                          _P, _SZ, _P], ctypes.c_int),
-    "mra_debug_select": ([_P, _P, _P, _I32, _I32, _I32, _P, _P, _SZ, _P], ctypes.c_int),
+    "mra_attention_fwd_ex": ([_P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
+    "mra_debug_stages": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P,
+                          _P, _P, _SZ, _P], ctypes.c_int),
+    "mra_debug_select": ([_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P], ctypes.c_int),
     "mra_backward_workspace_size": ([_P, _I32, _I32, ctypes.POINTER(_SZ)], ctypes.c_int),
     "mra_attention_bwd": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P, _SZ,
                            _P], ctypes.c_int),
@@ -57,6 +60,12 @@ class MraError(RuntimeError):
 class _Dims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("seq_len", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class _Options(ctypes.Structure):
+    _fields_ = [("block_per_row", ctypes.c_int32), ("approx_mode", ctypes.c_int32),
+                ("prior_first", ctypes.c_int32), ("prior_diag", ctypes.c_int32),
+                ("score_ranking", ctypes.c_int32)]
 
 
 def library_path() -> str:
@@ -144,9 +153,11 @@ def _check_inputs(q, k, v, mask):
 
 
 def attention(q, k, v, mask=None, block_per_row=4, approx_mode="full", initial_prior_first_n_blocks=0,
-              initial_prior_diagonal_n_blocks=0, out=None, workspace=None):
+              initial_prior_diagonal_n_blocks=0, out=None, workspace=None, score_ranking="row_normalized"):
     """MRA-2 forward on [batch, heads, seq_len, head_dim] tensors (bf16 or fp32).
-    mask: uint8 [batch, seq_len] (1 = valid) or None.  Returns `out`."""
+    mask: uint8 [batch, seq_len] (1 = valid) or None.  score_ranking:
+    "row_normalized" (default) or "raw_logits", what step 2's top-k ranks.
+    Returns `out`."""
     _check_inputs(q, k, v, mask)
     B, H, N, d = q.shape
     if out is None:
@@ -155,11 +166,18 @@ def attention(q, k, v, mask=None, block_per_row=4, approx_mode="full", initial_p
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     dims = _dims(B, H, N, d, DTYPES[q.dtype])
-    st = lib().mra_attention_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), block_per_row,
-                                 MODES.get(approx_mode, -1), initial_prior_first_n_blocks,
-                                 initial_prior_diagonal_n_blocks, _ptr(out), _ptr(workspace),
-                                 workspace.numel(), _stream(q))
-    _check(st, "mra_attention_fwd")
+    if score_ranking == "row_normalized":
+        st = lib().mra_attention_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), block_per_row,
+                                     MODES.get(approx_mode, -1), initial_prior_first_n_blocks,
+                                     initial_prior_diagonal_n_blocks, _ptr(out), _ptr(workspace),
+                                     workspace.numel(), _stream(q))
+        _check(st, "mra_attention_fwd")
+        return out
+    opts = _Options(block_per_row, MODES.get(approx_mode, -1), initial_prior_first_n_blocks,
+                    initial_prior_diagonal_n_blocks, RANKINGS.get(score_ranking, -1))
+    st = lib().mra_attention_fwd_ex(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), ctypes.byref(opts),
+                                    _ptr(out), _ptr(workspace), workspace.numel(), _stream(q))
+    _check(st, "mra_attention_fwd_ex")
     return out
 
 
@@ -287,7 +305,7 @@ def debug_replay(q, k, v, stage, count, mask=None, block_per_row=4, approx_mode=
 
 
 def debug_stages(q, k, v, mask=None, block_per_row=4, approx_mode="full", initial_prior_first_n_blocks=0,
-                 initial_prior_diagonal_n_blocks=0):
+                 initial_prior_diagonal_n_blocks=0, score_ranking="row_normalized"):
     """Steps 1-2 of the same kernels; returns a dict of device tensors:
     qhat, khat, vhat (full mode), count, logits, rowmax, sel, error."""
     _check_inputs(q, k, v, mask)
@@ -311,7 +329,8 @@ def debug_stages(q, k, v, mask=None, block_per_row=4, approx_mode="full", initia
     dims = _dims(B, H, N, d, DTYPES[q.dtype])
     st = lib().mra_debug_stages(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), block_per_row,
                                 MODES.get(approx_mode, -1), initial_prior_first_n_blocks,
-                                initial_prior_diagonal_n_blocks, _ptr(r["qhat"]), _ptr(r["khat"]),
+                                initial_prior_diagonal_n_blocks, RANKINGS.get(score_ranking, -1),
+                                _ptr(r["qhat"]), _ptr(r["khat"]),
                                 _ptr(r["vhat"]), _ptr(r["count"]), _ptr(r["logits"]), _ptr(r["rowmax"]),
                                 _ptr(r["sel"]), _ptr(r["error"]), _ptr(ws), ws_bytes, _stream(q))
     _check(st, "mra_debug_stages")
@@ -320,7 +339,7 @@ def debug_stages(q, k, v, mask=None, block_per_row=4, approx_mode="full", initia
 
 
 def debug_select(logits, count, batch, heads, block_per_row=4, initial_prior_first_n_blocks=0,
-                 initial_prior_diagonal_n_blocks=0):
+                 initial_prior_diagonal_n_blocks=0, score_ranking="row_normalized"):
     """The step-2 selector alone on given fp32 logits [B, H, nb, nb] and
     int32 counts [B, nb] (device tensors).  Returns sel [B, H, K] int32."""
     nb = logits.shape[-1]
@@ -335,7 +354,7 @@ def debug_select(logits, count, batch, heads, block_per_row=4, initial_prior_fir
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=logits.device)
     dims = _dims(batch, heads, N, 64, 1)
     st = lib().mra_debug_select(ctypes.byref(dims), _ptr(logits), _ptr(count), block_per_row,
-                                initial_prior_first_n_blocks, initial_prior_diagonal_n_blocks, _ptr(sel),
-                                _ptr(ws), ws_bytes, _stream(logits))
+                                initial_prior_first_n_blocks, initial_prior_diagonal_n_blocks,
+                                RANKINGS.get(score_ranking, -1), _ptr(sel), _ptr(ws), ws_bytes, _stream(logits))
     _check(st, "mra_debug_select")
     return sel[:, :, :K]

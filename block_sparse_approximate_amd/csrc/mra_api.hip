@@ -18,7 +18,7 @@
 namespace mra {
 namespace {
 
-constexpr int32_t kAbiVersion = 1;
+constexpr int32_t kAbiVersion = 2;
 constexpr int32_t kMaxSeqLen = 16384;
 
 size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -126,7 +126,7 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
 
 Params make_params(const mra_dims& d, const Layout& L, int32_t mode, int32_t pf, int32_t pd, const void* q,
-                   const void* k, const void* v, const uint8_t* mask, void* out, void* ws) {
+                   const void* k, const void* v, const uint8_t* mask, void* out, void* ws, int32_t ranking = 0) {
     Params p;
     memset(&p, 0, sizeof(p));
     unsigned char* w = static_cast<unsigned char*>(ws);
@@ -137,6 +137,7 @@ Params make_params(const mra_dims& d, const Layout& L, int32_t mode, int32_t pf,
     p.dtype = d.dtype;
     p.prior_first = pf;
     p.prior_diag = pd;
+    p.rank_raw = ranking == MRA_RANK_RAW_LOGITS ? 1 : 0;
     p.max_items = L.max_items;
     p.attn_wph = attn_grid_waves_per_head(L.BH, L.K);
     p.attn_seq = attn_heads_in_turn(L.BH, L.K) ? 1 : 0;
@@ -263,12 +264,14 @@ static mra_status run_front(const Params& p, hipStream_t s) {
 static mra_status run_forward(const mra_dims* dims, const void* q, const void* k, const void* v,
                               const uint8_t* mask, int32_t block_per_row, int32_t approx_mode, int32_t prior_first,
                               int32_t prior_diag, void* out, void* workspace, size_t workspace_bytes, void* stream,
-                              void* const* ev) {
+                              void* const* ev, int32_t ranking = MRA_RANK_ROW_NORMALIZED) {
     Layout L;
     mra_status st = check_call(dims, q, k, v, mask, block_per_row, approx_mode, prior_first, prior_diag, out,
                                workspace, workspace_bytes, true, &L);
     if (st != MRA_OK) return st;
-    const Params p = make_params(*dims, L, approx_mode, prior_first, prior_diag, q, k, v, mask, out, workspace);
+    if (ranking != MRA_RANK_ROW_NORMALIZED && ranking != MRA_RANK_RAW_LOGITS) return MRA_ERR_MODE;
+    const Params p = make_params(*dims, L, approx_mode, prior_first, prior_diag, q, k, v, mask, out, workspace,
+                                 ranking);
     hipStream_t s = static_cast<hipStream_t>(stream);
     auto mark = [&](int idx) {
         return (ev && ev[idx]) ? hipEventRecord(static_cast<hipEvent_t>(ev[idx]), s) : hipSuccess;
@@ -298,6 +301,14 @@ MRA_API mra_status mra_attention_fwd(const mra_dims* dims, const void* q, const 
                                      size_t workspace_bytes, void* stream) {
     return run_forward(dims, q, k, v, mask, block_per_row, approx_mode, prior_first, prior_diag, out, workspace,
                        workspace_bytes, stream, nullptr);
+}
+
+MRA_API mra_status mra_attention_fwd_ex(const mra_dims* dims, const void* q, const void* k, const void* v,
+                                        const uint8_t* mask, const mra_options* opts, void* out, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+    if (!opts) return MRA_ERR_NULL;
+    return run_forward(dims, q, k, v, mask, opts->block_per_row, opts->approx_mode, opts->prior_first,
+                       opts->prior_diag, out, workspace, workspace_bytes, stream, nullptr, opts->score_ranking);
 }
 
 MRA_API mra_status mra_attention_fwd_profiled(const mra_dims* dims, const void* q, const void* k, const void* v,
@@ -399,15 +410,17 @@ MRA_API mra_status mra_debug_replay(const mra_dims* dims, const void* q, const v
 
 MRA_API mra_status mra_debug_stages(const mra_dims* dims, const void* q, const void* k, const void* v,
                                     const uint8_t* mask, int32_t block_per_row, int32_t approx_mode,
-                                    int32_t prior_first, int32_t prior_diag, float* qhat, float* khat,
-                                    float* vhat, int32_t* count, float* logits, float* rowmax, int32_t* sel,
-                                    int32_t* error, void* workspace, size_t workspace_bytes, void* stream) {
+                                    int32_t prior_first, int32_t prior_diag, int32_t score_ranking, float* qhat,
+                                    float* khat, float* vhat, int32_t* count, float* logits, float* rowmax,
+                                    int32_t* sel, int32_t* error, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
     Layout L;
     mra_status st = check_call(dims, q, k, v, mask, block_per_row, approx_mode, prior_first, prior_diag,
                                nullptr, workspace, workspace_bytes, false, &L);
     if (st != MRA_OK) return st;
+    if (score_ranking != MRA_RANK_ROW_NORMALIZED && score_ranking != MRA_RANK_RAW_LOGITS) return MRA_ERR_MODE;
     const Params p = make_params(*dims, L, approx_mode, prior_first, prior_diag, q, k, v, mask, nullptr,
-                                 workspace);
+                                 workspace, score_ranking);
     hipStream_t s = static_cast<hipStream_t>(stream);
     st = run_front(p, s);
     if (st != MRA_OK) return st;
@@ -434,19 +447,21 @@ MRA_API mra_status mra_debug_stages(const mra_dims* dims, const void* q, const v
 }
 
 MRA_API mra_status mra_debug_select(const mra_dims* dims, const float* logits, const int32_t* count,
-                                    int32_t block_per_row, int32_t prior_first, int32_t prior_diag, int32_t* sel,
-                                    void* workspace, size_t workspace_bytes, void* stream) {
+                                    int32_t block_per_row, int32_t prior_first, int32_t prior_diag,
+                                    int32_t score_ranking, int32_t* sel, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
     mra_status st = check_dims(dims);
     if (st != MRA_OK) return st;
     st = check_params(block_per_row, MRA_APPROX_SPARSE, prior_first, prior_diag);
     if (st != MRA_OK) return st;
+    if (score_ranking != MRA_RANK_ROW_NORMALIZED && score_ranking != MRA_RANK_RAW_LOGITS) return MRA_ERR_MODE;
     if (!logits || !count || !sel) return MRA_ERR_NULL;
     Layout L;
     if (!carve(*dims, block_per_row, MRA_APPROX_SPARSE, &L)) return MRA_ERR_SEQ_LEN;
     if (!workspace || workspace_bytes < L.total) return MRA_ERR_WORKSPACE;
     if (((uintptr_t)workspace & 255u) != 0) return MRA_ERR_ALIGN;
     Params p = make_params(*dims, L, MRA_APPROX_SPARSE, prior_first, prior_diag, nullptr, nullptr, nullptr,
-                           nullptr, nullptr, workspace);
+                           nullptr, nullptr, workspace, score_ranking);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const size_t BH = (size_t)L.BH, nb = (size_t)L.nb;
     hipError_t e = hipMemcpyAsync(p.logits, logits, BH * nb * nb * 4, hipMemcpyDeviceToDevice, s);

@@ -61,6 +61,7 @@ struct Params {
     int32_t mode;          // 0 full, 1 sparse
     int32_t dtype;         // 0 fp32, 1 bf16
     int32_t prior_first, prior_diag;
+    int32_t rank_raw;      // 1: step 2 ranks the raw low-res logits (no row max subtracted)
     int32_t max_items;
     const void* q;
     const void* k;
@@ -134,13 +135,14 @@ __device__ __forceinline__ uint32_t float_key(float s) {
 }
 
 // Step 2 score of cell (i, j) ([MRA] "第二步"): row-max-normalised low-res
-// logit plus 5000 per prior that covers the cell; -inf for empty blocks;
+// logit (raw: the logit itself) plus 5000 per prior that covers the cell;
+// -inf for empty blocks;
 // -0 folded to +0.  The fp32 operations and their order are fixed (this
 // translation unit is built with -ffp-contract=off).
 __device__ __forceinline__ float cell_score(float logit, float m, int i, int j, bool vi, bool vj,
-                                            int pf, int pd) {
+                                            int pf, int pd, bool raw) {
     if (!vi || !vj) return -__builtin_inff();
-    float s = logit - m;
+    float s = raw ? logit : logit - m;
     int dist = i > j ? i - j : j - i;
     if (pd > 0 && dist <= pd / 2) s = s + kPriorBias;
     if (i < pf) s = s + kPriorBias;

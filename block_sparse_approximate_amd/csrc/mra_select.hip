@@ -522,6 +522,7 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(Params p) {
     float* Sg = p.logits + (size_t)bh * nb * nb;
     uint32_t* Kg = p.keys + (size_t)bh * nb * nb;
     const int pf = p.prior_first, pd = p.prior_diag;
+    const bool raw = p.rank_raw != 0;
 #pragma unroll
     for (int t = 0; t < kMaxColTiles; t++) {
 #pragma unroll
@@ -531,7 +532,7 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(Params p) {
                 const float sv = sc[t][q];
                 if (!kGiven) Sg[(size_t)i * nb + j] = sv;
                 const int cjq = (q & 1) ? cj[t].y : cj[t].x;
-                const float s = cell_score(sv, q < 2 ? ma : mb, i, j, (q < 2 ? cia : cib) > 0, cjq > 0, pf, pd);
+                const float s = cell_score(sv, q < 2 ? ma : mb, i, j, (q < 2 ? cia : cib) > 0, cjq > 0, pf, pd, raw);
                 const uint32_t key = float_key(s);
                 Kg[(size_t)i * nb + j] = key;
                 atomicAdd(&hist[key >> (32 - kHistBits)], 1u);

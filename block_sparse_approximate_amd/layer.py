@@ -30,11 +30,13 @@ class MraAttentionFunction(torch.autograd.Function):
     through the block means ([MRA] 第四步)."""
 
     @staticmethod
-    def forward(ctx, q, k, v, mask, block_per_row, approx_mode, prior_first, prior_diag):
+    def forward(ctx, q, k, v, mask, block_per_row, approx_mode, prior_first, prior_diag,
+                score_ranking="row_normalized"):
         B, H, N, d = q.shape
         ws = torch.empty(workspace_size(B, H, N, d, q.dtype, block_per_row, approx_mode), dtype=torch.uint8,
                          device=q.device)
-        out = attention(q, k, v, mask, block_per_row, approx_mode, prior_first, prior_diag, workspace=ws)
+        out = attention(q, k, v, mask, block_per_row, approx_mode, prior_first, prior_diag, workspace=ws,
+                        score_ranking=score_ranking)
         ctx.save_for_backward(q, k, v, out, ws, mask if mask is not None else torch.empty(0, device=q.device))
         ctx.has_mask = mask is not None
         ctx.args = (block_per_row, approx_mode, prior_first, prior_diag)
@@ -51,26 +53,27 @@ class MraAttentionFunction(torch.autograd.Function):
         call, grads = prepare_backward(q, k, v, out, dout.contiguous(), ws, mask, block_per_row, approx_mode,
                                        prior_first, prior_diag, bwd_workspace=bw)
         call()
-        return grads[0], grads[1], grads[2], None, None, None, None, None
+        return grads[0], grads[1], grads[2], None, None, None, None, None, None
 
 
 def mra_attention(q, k, v, mask=None, block_per_row=4, approx_mode="full", initial_prior_first_n_blocks=0,
-                  initial_prior_diagonal_n_blocks=0):
+                  initial_prior_diagonal_n_blocks=0, score_ranking="row_normalized"):
     """Differentiable MRA-2 attention on contiguous [batch, heads, seq_len,
     64] device tensors; mask is uint8 [batch, seq_len] (1 = valid) or None."""
     return MraAttentionFunction.apply(q, k, v, mask, block_per_row, approx_mode, initial_prior_first_n_blocks,
-                                      initial_prior_diagonal_n_blocks)
+                                      initial_prior_diagonal_n_blocks, score_ranking)
 
 
 class MraSelfAttention(torch.nn.Module):
     """Query, key and value projections, head split, MRA-2 attention and head
     merge.  Parameters follow MraConfig ([MRA] MraConfig section):
     block_per_row, approx_mode, initial_prior_first_n_blocks,
-    initial_prior_diagonal_n_blocks.  head_dim = hidden_size / heads must be
-    64, the head size the kernels are built for."""
+    initial_prior_diagonal_n_blocks; score_ranking picks what step 2 ranks
+    ("row_normalized" or "raw_logits").  head_dim = hidden_size / heads must
+    be 64, the head size the kernels are built for."""
 
     def __init__(self, hidden_size=768, num_attention_heads=12, block_per_row=4, approx_mode="full",
-                 initial_prior_first_n_blocks=0, initial_prior_diagonal_n_blocks=0):
+                 initial_prior_first_n_blocks=0, initial_prior_diagonal_n_blocks=0, score_ranking="row_normalized"):
         super().__init__()
         if hidden_size % num_attention_heads != 0 or hidden_size // num_attention_heads != 64:
             raise ValueError("hidden_size / num_attention_heads must be 64")
@@ -83,6 +86,7 @@ class MraSelfAttention(torch.nn.Module):
         self.approx_mode = approx_mode
         self.prior_first = initial_prior_first_n_blocks
         self.prior_diag = initial_prior_diagonal_n_blocks
+        self.score_ranking = score_ranking
 
     def _heads(self, x, B, N):
         return x.view(B, N, self.num_attention_heads, self.head_dim).transpose(1, 2).contiguous()
@@ -105,7 +109,8 @@ class MraSelfAttention(torch.nn.Module):
         q = self._heads(self.query(x), B, Np)
         k = self._heads(self.key(x), B, Np)
         v = self._heads(self.value(x), B, Np)
-        ctx = mra_attention(q, k, v, mask, self.block_per_row, self.approx_mode, self.prior_first, self.prior_diag)
+        ctx = mra_attention(q, k, v, mask, self.block_per_row, self.approx_mode, self.prior_first, self.prior_diag,
+                            self.score_ranking)
         ctx = ctx.transpose(1, 2).reshape(B, Np, -1)
         return ctx[:, :N]
 

@@ -71,6 +71,23 @@ typedef enum {
 typedef enum { MRA_F32 = 0, MRA_BF16 = 1 } mra_dtype;
 typedef enum { MRA_APPROX_FULL = 0, MRA_APPROX_SPARSE = 1 } mra_approx_mode;
 
+/* What step 2's global top-k ranks ([MRA] "第二步": top-k on the low-res
+ * logits, each row's best blocks).  The default takes each cell's logit
+ * minus its row's maximum, so that every row's best block ranks first (the
+ * plainest reading of "each row" within one global top-k); the alternative
+ * ranks the raw logits themselves.  Priors and empty blocks apply to both. */
+typedef enum { MRA_RANK_ROW_NORMALIZED = 0, MRA_RANK_RAW_LOGITS = 1 } mra_score_ranking;
+
+/* The selection options of mra_attention_fwd_ex: the four MraConfig
+ * parameters and the ranking. */
+typedef struct {
+    int32_t block_per_row;
+    int32_t approx_mode;     /* mra_approx_mode */
+    int32_t prior_first;     /* initial_prior_first_n_blocks */
+    int32_t prior_diag;      /* initial_prior_diagonal_n_blocks */
+    int32_t score_ranking;   /* mra_score_ranking; MRA_ERR_MODE if neither */
+} mra_options;
+
 typedef struct {
     int32_t batch;
     int32_t heads;
@@ -109,6 +126,15 @@ mra_status mra_attention_fwd(const mra_dims* dims, const void* q, const void* k,
                              int32_t prior_first, int32_t prior_diag, void* out, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* mra_attention_fwd with its selection options in a struct (opts: host
+ * pointer, read during the call), which adds the choice of ranking;
+ * MRA_ERR_NULL when opts is NULL.  With MRA_RANK_ROW_NORMALIZED it is
+ * exactly mra_attention_fwd.  The backward pass reads the selection the
+ * forward made, so it needs no ranking of its own. */
+mra_status mra_attention_fwd_ex(const mra_dims* dims, const void* q, const void* k, const void* v,
+                                const uint8_t* mask, const mra_options* opts, void* out, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 /* Profiling variant of mra_attention_fwd: the same work, plus a
  * hipEventRecord on `stream` before and after each kernel launch.
  *   events  array of 10 hipEvent_t created by the caller (with timing);
@@ -131,10 +157,11 @@ mra_status mra_attention_fwd_profiled(const mra_dims* dims, const void* q, const
  *   sel               [B, H, num_block] int32 selected flat indices i*nb + j,
  *                     ascending
  *   error             [1] int32 device error word (0 = consistent)
- * The other arguments are as for mra_attention_fwd. */
+ * score_ranking as in mra_options; the other arguments are as for
+ * mra_attention_fwd. */
 mra_status mra_debug_stages(const mra_dims* dims, const void* q, const void* k, const void* v,
                             const uint8_t* mask, int32_t block_per_row, int32_t approx_mode,
-                            int32_t prior_first, int32_t prior_diag, float* qhat, float* khat,
+                            int32_t prior_first, int32_t prior_diag, int32_t score_ranking, float* qhat, float* khat,
                             float* vhat, int32_t* count, float* logits, float* rowmax, int32_t* sel,
                             int32_t* error, void* workspace, size_t workspace_bytes, void* stream);
 
@@ -145,7 +172,8 @@ mra_status mra_debug_stages(const mra_dims* dims, const void* q, const void* k, 
  * seq_len = 32 * nb comes from dims; q/k/v are not read. */
 mra_status mra_debug_select(const mra_dims* dims, const float* logits, const int32_t* count,
                             int32_t block_per_row, int32_t prior_first, int32_t prior_diag,
-                            int32_t* sel, void* workspace, size_t workspace_bytes, void* stream);
+                            int32_t score_ranking, int32_t* sel, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 /* Bytes of the backward pass's own workspace for these dimensions and
  * selection parameters (mra_attention_bwd's bwd_workspace): the dO . O row

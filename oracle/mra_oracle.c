@@ -144,9 +144,11 @@ void oracle_lowres_logits_f32(int32_t nb, int32_t d, const float* qhat,
  *            + 5000 if the diagonal prior is on and |i-j| <= floor(g/2)
  *            + 5000 if i < f   + 5000 if j < f                  (fp32 adds)
  *   score_ij = -inf if cnt_i == 0 or cnt_j == 0;  -0.0 becomes +0.0.
- * rowmax: [nb] (may be NULL), score: [nb, nb]. */
+ * ranking 1 takes the other reading of the step's "top-k on the low-res
+ * logits" (R2'): the raw logit S_ij in place of S_ij - rowmax_i, the rest
+ * unchanged.  rowmax: [nb] (may be NULL), score: [nb, nb]. */
 void oracle_scores_f32(int32_t nb, const float* S, const int32_t* cnt,
-                       int32_t prior_first, int32_t prior_diag,
+                       int32_t prior_first, int32_t prior_diag, int32_t ranking,
                        float* rowmax, float* score)
 {
     for (int32_t i = 0; i < nb; i++) {
@@ -161,7 +163,7 @@ void oracle_scores_f32(int32_t nb, const float* S, const int32_t* cnt,
             if (cnt[i] == 0 || cnt[j] == 0) {
                 s = -INFINITY;
             } else {
-                s = S[(int64_t)i * nb + j] - m;
+                s = ranking ? S[(int64_t)i * nb + j] : S[(int64_t)i * nb + j] - m;
                 int32_t dist = i > j ? i - j : j - i;
                 if (prior_diag > 0 && dist <= prior_diag / 2)
                     s = s + MRA_PRIOR_BIAS;
@@ -225,12 +227,12 @@ int oracle_select_top(int32_t nb, const float* score, int64_t K, int32_t* sel)
  * selector is compared against on identical logits). */
 int oracle_select_from_logits(int32_t nb, const float* S, const int32_t* cnt,
                               int64_t K, int32_t prior_first, int32_t prior_diag,
-                              int32_t* sel)
+                              int32_t ranking, int32_t* sel)
 {
     float* score = (float*)malloc(sizeof(float) * (size_t)nb * nb);
     if (!score)
         return -2;
-    oracle_scores_f32(nb, S, cnt, prior_first, prior_diag, NULL, score);
+    oracle_scores_f32(nb, S, cnt, prior_first, prior_diag, ranking, NULL, score);
     int rc = oracle_select_top(nb, score, K, sel);
     free(score);
     return rc;
@@ -241,7 +243,7 @@ int oracle_select_from_logits(int32_t nb, const float* S, const int32_t* cnt,
  * q,k,v: [N, d] fp32 values (bf16 inputs arrive widened exactly);
  * mask: [N] or NULL; out: [N, d] fp64; sel: [K] or NULL (ascending flat). */
 typedef struct {
-    int32_t N, d, block_per_row, mode, prior_first, prior_diag;
+    int32_t N, d, block_per_row, mode, prior_first, prior_diag, ranking;
 } head_args_t;
 
 static int oracle_mra_head(const head_args_t* a, const float* q, const float* k,
@@ -275,7 +277,7 @@ static int oracle_mra_head(const head_args_t* a, const float* q, const float* k,
     oracle_pool_f32(N, d, q, mask, qh, cnt);
     oracle_pool_f32(N, d, k, mask, kh, NULL);
     oracle_lowres_logits_f32(nb, d, qh, kh, S);
-    oracle_scores_f32(nb, S, cnt, a->prior_first, a->prior_diag, NULL, score);
+    oracle_scores_f32(nb, S, cnt, a->prior_first, a->prior_diag, a->ranking, NULL, score);
     rc = oracle_select_top(nb, score, K, sel);
     if (rc)
         goto done;
@@ -480,7 +482,7 @@ static int oracle_mra_head_bwd(const head_args_t* a, const float* q, const float
     oracle_pool_f32(N, d, q, mask, qh, cnt);
     oracle_pool_f32(N, d, k, mask, kh, NULL);
     oracle_lowres_logits_f32(nb, d, qh, kh, S);
-    oracle_scores_f32(nb, S, cnt, a->prior_first, a->prior_diag, NULL, score);
+    oracle_scores_f32(nb, S, cnt, a->prior_first, a->prior_diag, a->ranking, NULL, score);
     rc = oracle_select_top(nb, score, K, sel);
     if (rc)
         goto done;
@@ -689,18 +691,19 @@ static int run_jobs(job_t* j, int nthreads)
 int oracle_mra_fwd(int32_t B, int32_t H, int32_t N, int32_t d, const float* q,
                    const float* k, const float* v, const uint8_t* mask,
                    int32_t block_per_row, int32_t mode, int32_t prior_first,
-                   int32_t prior_diag, double* out, int32_t* sel, int32_t nthreads)
+                   int32_t prior_diag, int32_t ranking, double* out, int32_t* sel,
+                   int32_t nthreads)
 {
     int64_t K = oracle_num_block(N, block_per_row);
     if (B < 1 || H < 1 || d < 1 || K < 0 || (mode != 0 && mode != 1) ||
-        prior_first < 0 || prior_diag < 0 || !q || !k || !v || !out)
+        prior_first < 0 || prior_diag < 0 || (ranking != 0 && ranking != 1) || !q || !k || !v || !out)
         return -1;
     job_t j;
     memset(&j, 0, sizeof(j));
     j.B = B; j.H = H; j.N = N; j.d = d;
     j.q = q; j.k = k; j.v = v; j.mask = mask;
     j.ha.N = N; j.ha.d = d; j.ha.block_per_row = block_per_row; j.ha.mode = mode;
-    j.ha.prior_first = prior_first; j.ha.prior_diag = prior_diag;
+    j.ha.prior_first = prior_first; j.ha.prior_diag = prior_diag; j.ha.ranking = ranking;
     j.out = out; j.sel = sel; j.K = K; j.dense = 0;
     return run_jobs(&j, nthreads);
 }
@@ -726,19 +729,20 @@ int oracle_dense_fwd(int32_t B, int32_t H, int32_t N, int32_t d, const float* q,
 int oracle_mra_bwd(int32_t B, int32_t H, int32_t N, int32_t d, const float* q,
                    const float* k, const float* v, const uint8_t* mask,
                    int32_t block_per_row, int32_t mode, int32_t prior_first,
-                   int32_t prior_diag, const float* dout, double* dq, double* dk,
-                   double* dv, int32_t nthreads)
+                   int32_t prior_diag, int32_t ranking, const float* dout, double* dq,
+                   double* dk, double* dv, int32_t nthreads)
 {
     int64_t K = oracle_num_block(N, block_per_row);
     if (B < 1 || H < 1 || d < 1 || K < 0 || (mode != 0 && mode != 1) ||
-        prior_first < 0 || prior_diag < 0 || !q || !k || !v || !dout || !dq || !dk || !dv)
+        prior_first < 0 || prior_diag < 0 || (ranking != 0 && ranking != 1) || !q || !k || !v ||
+        !dout || !dq || !dk || !dv)
         return -1;
     job_t j;
     memset(&j, 0, sizeof(j));
     j.B = B; j.H = H; j.N = N; j.d = d;
     j.q = q; j.k = k; j.v = v; j.mask = mask;
     j.ha.N = N; j.ha.d = d; j.ha.block_per_row = block_per_row; j.ha.mode = mode;
-    j.ha.prior_first = prior_first; j.ha.prior_diag = prior_diag;
+    j.ha.prior_first = prior_first; j.ha.prior_diag = prior_diag; j.ha.ranking = ranking;
     j.K = K; j.bwd = 1; j.dout = dout; j.dq = dq; j.dk = dk; j.dv = dv;
     return run_jobs(&j, nthreads);
 }

@@ -23,11 +23,11 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     L = mra.lib()
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(mra.SIGNATURES)
-    assert L.mra_abi_version() == 1
+    assert L.mra_abi_version() == 2
 
 
 def test_status_strings():
@@ -93,6 +93,26 @@ def test_attention_fwd_rejects_bad_arguments(kw, status):
     assert call(**kw) == status
 
 
+def call_ex(opts=(4, 0, 0, 0, 1), **kw):
+    d = mra._Dims(*kw.get("dims", (1, 2, 512, 64, 1)))
+    o = None if opts is None else ctypes.byref(mra._Options(*opts))
+    return mra.lib().mra_attention_fwd_ex(ctypes.byref(d), Q, K, V, None, o, kw.get("out", O), W, 1 << 40, None)
+
+
+@pytest.mark.parametrize("opts,status", [
+    (None, 1), ((4, 0, 0, 0, 2), 6), ((4, 0, 0, 0, -1), 6), ((4, 3, 0, 0, 1), 6), ((0, 0, 0, 0, 1), 7),
+    ((4, 1, -1, 0, 1), 8),
+])
+def test_attention_fwd_ex_rejects_bad_options(opts, status):
+    assert call_ex(opts) == status
+
+
+def test_attention_fwd_ex_checks_like_fwd():
+    assert call_ex(out=None) == 1
+    assert call_ex(out=Q) == 9
+    assert call_ex(dims=(1, 2, 500, 64, 1)) == 3
+
+
 def test_null_dims_rejected():
     L = mra.lib()
     assert L.mra_attention_fwd(None, Q, K, V, None, 4, 0, 0, 0, O, W, 1 << 40, None) == 1
@@ -103,10 +123,11 @@ def test_null_dims_rejected():
 def test_debug_select_rejects_bad_arguments():
     L = mra.lib()
     d = mra._Dims(1, 1, 512, 64, 1)
-    assert L.mra_debug_select(ctypes.byref(d), None, K, 4, 0, 0, O, W, 1 << 40, None) == 1
-    assert L.mra_debug_select(ctypes.byref(d), Q, K, 4, 0, 0, O, W, 16, None) == 10
-    assert L.mra_debug_select(ctypes.byref(d), Q, K, 0, 0, 0, O, W, 1 << 40, None) == 7
-    assert L.mra_debug_select(ctypes.byref(d), Q, K, 4, -1, 0, O, W, 1 << 40, None) == 8
+    assert L.mra_debug_select(ctypes.byref(d), None, K, 4, 0, 0, 0, O, W, 1 << 40, None) == 1
+    assert L.mra_debug_select(ctypes.byref(d), Q, K, 4, 0, 0, 0, O, W, 16, None) == 10
+    assert L.mra_debug_select(ctypes.byref(d), Q, K, 0, 0, 0, 0, O, W, 1 << 40, None) == 7
+    assert L.mra_debug_select(ctypes.byref(d), Q, K, 4, -1, 0, 0, O, W, 1 << 40, None) == 8
+    assert L.mra_debug_select(ctypes.byref(d), Q, K, 4, 0, 0, 2, O, W, 1 << 40, None) == 6
 
 
 def test_debug_replay_rejects_bad_arguments():

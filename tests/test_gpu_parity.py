@@ -249,3 +249,52 @@ def test_run_to_run_bitwise_determinism(mra):
     b = mra.attention(q, k, v, **kw)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# ------------------------------------------- raw-logit ranking (reading R2') --
+@pytest.mark.parametrize("nb,bpr,pf,pd,kind", [
+    (16, 4, 0, 0, "normal"), (128, 4, 2, 3, "normal"), (128, 4, 0, 0, "ints"), (13, 2, 1, 2, "ints"),
+    (512, 8, 0, 1, "normal"), (192, 4, 1, 2, "normal")])
+def test_selector_raw_ranking_on_identical_logits(mra, nb, bpr, pf, pd, kind):
+    print("case raw", nb, bpr, pf, pd, kind, flush=True)
+    rng = np.random.default_rng(nb * 11 + bpr)
+    B, H = 2, 2
+    if kind == "ints":
+        S = rng.integers(-3, 3, (B, H, nb, nb)).astype(np.float32)
+    else:
+        S = rng.standard_normal((B, H, nb, nb)).astype(np.float32)
+    cnt = np.full((B, nb), 32, np.int32)
+    if nb > 4:
+        cnt[1, nb // 2] = 0
+    K = oracle.num_block(32 * nb, bpr)
+    got = mra.debug_select(torch.from_numpy(S).cuda(), torch.from_numpy(cnt).cuda(), B, H, bpr, pf, pd,
+                           score_ranking="raw_logits")
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    for b in range(B):
+        for h in range(H):
+            ref = oracle.select_from_logits(S[b, h], cnt[b], K, pf, pd, ranking="raw_logits")
+            assert np.array_equal(got[b, h], ref), (b, h)
+
+
+@pytest.mark.parametrize("cfg", ["C2", "C3", "C4"])
+def test_raw_ranking_selection_and_output(mra, cfg):
+    # under R2' many block rows get no selected block: full mode answers them
+    # from the low-res part alone, sparse mode with 0
+    w = workloads.get(cfg)
+    print("case raw", cfg, w, flush=True)
+    r = mra.debug_stages(dev(w, "q"), dev(w, "k"), dev(w, "v"), dev_mask(w), block_per_row=w.block_per_row,
+                         approx_mode=w.approx_mode, initial_prior_first_n_blocks=w.prior_first,
+                         initial_prior_diagonal_n_blocks=w.prior_diag, score_ranking="raw_logits")
+    torch.cuda.synchronize()
+    ref, sel = run_oracle(w, ranking="raw_logits")
+    assert int(r["error"][0].item()) == 0
+    assert np.array_equal(r["sel"].cpu().numpy(), sel)
+    nb = w.N // 32
+    rows_with_blocks = np.array([len(np.unique(s // nb)) for s in sel.reshape(-1, sel.shape[-1])])
+    print("  block rows with a selected block: mean %.1f of %d" % (rows_with_blocks.mean(), nb), flush=True)
+    got = run_gpu(mra, w, score_ranking="raw_logits")
+    assert_close(w, got, ref)
+    # the default ranking gives a different selection here
+    _, sel_default = run_oracle(w)
+    assert not np.array_equal(sel, sel_default)

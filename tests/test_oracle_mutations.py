@@ -21,7 +21,10 @@ SRC = os.path.join(ROOT, "oracle", "mra_oracle.c")
 MUTANTS = {
     "low-res weight drops cnt_j": ("double w = (double)cnt[j] * exp(s_lo[j] - shift);",
                                    "double w = exp(s_lo[j] - shift);"),
-    "ranks raw logits, not row-normalised": ("s = S[(int64_t)i * nb + j] - m;", "s = S[(int64_t)i * nb + j];"),
+    "ranks raw logits, not row-normalised": ("s = ranking ? S[(int64_t)i * nb + j] : S[(int64_t)i * nb + j] - m;",
+                                            "s = S[(int64_t)i * nb + j];"),
+    "raw-logit ranking ignored": ("s = ranking ? S[(int64_t)i * nb + j] : S[(int64_t)i * nb + j] - m;",
+                                  "s = S[(int64_t)i * nb + j] - m;"),
     "transposed low-res logits": ("acc = fmaf(qhat[(int64_t)i * d + c], khat[(int64_t)j * d + c], acc);",
                                   "acc = fmaf(qhat[(int64_t)j * d + c], khat[(int64_t)i * d + c], acc);"),
     "ties go to the larger flat index": ("return x->flat < y->flat ? -1 : (x->flat > y->flat ? 1 : 0);",

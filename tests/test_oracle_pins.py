@@ -174,6 +174,74 @@ def test_selection_one_per_row_is_row_argmax():
     assert np.array_equal(sel, np.arange(nb) * nb + S.argmax(1))
 
 
+# ------------------------------------------- raw-logit ranking (reading R2') --
+def test_raw_ranking_scores_are_the_logits_plus_priors():
+    # R2' ranks S_ij itself: no row max is subtracted; priors, empty blocks
+    # and the -0 fold behave as under R2
+    rng = np.random.default_rng(13)
+    nb = 12
+    S = rng.standard_normal((nb, nb)).astype(np.float32)
+    S[2, 5] = -0.0
+    cnt = np.full(nb, 32, np.int32)
+    cnt[7] = 0
+    _, sc = oracle.scores_f32(S, cnt, prior_first=2, prior_diag=3, ranking="raw_logits")
+    want = S.copy()
+    i, j = np.meshgrid(np.arange(nb), np.arange(nb), indexing="ij")
+    for m in ((np.abs(i - j) <= 1), (i < 2), (j < 2)):   # fp32 adds in the order diagonal, row, column
+        want = np.where(m, want + np.float32(5000.0), want).astype(np.float32)
+    want[7, :] = -np.inf
+    want[:, 7] = -np.inf
+    want[want == 0] = 0.0
+    assert np.array_equal(sc, want) and not np.signbit(sc[2, 5])
+
+
+def test_raw_ranking_selection_matches_lexsort():
+    rng = np.random.default_rng(14)
+    for nb, K in [(16, 64), (8, 8), (32, 96)]:
+        S = np.round(rng.standard_normal((nb, nb)) * 4).astype(np.float32) / 4   # ties
+        cnt = np.full(nb, 32, np.int32)
+        flat = np.arange(nb * nb)
+        ref = np.sort(np.lexsort((flat, -S.reshape(-1)))[:K])
+        assert np.array_equal(oracle.select_from_logits(S, cnt, K, ranking="raw_logits"), ref)
+
+
+def test_rankings_differ_on_rows_of_different_level():
+    # S_ij = 10 i + j / 100: under R2 every row's best cell scores 0, so bpr 1
+    # takes the last column; under R2' the K = nb largest logits are the
+    # whole last row
+    nb = 16
+    i, j = np.meshgrid(np.arange(nb), np.arange(nb), indexing="ij")
+    S = (10.0 * i + j / 100.0).astype(np.float32)
+    cnt = np.full(nb, 32, np.int32)
+    r2 = oracle.select_from_logits(S, cnt, nb)
+    r2p = oracle.select_from_logits(S, cnt, nb, ranking="raw_logits")
+    assert r2.tolist() == [r * nb + nb - 1 for r in range(nb)]
+    assert r2p.tolist() == [(nb - 1) * nb + c for c in range(nb)]
+
+
+def test_raw_ranking_sparse_forward_is_block_masked_dense():
+    # block-constant rows of q: the raw low-res logits are ordered by key
+    # block, the same in every row; with bpr 2 and no priors R2' takes whole
+    # key-block columns (the highest-logit ones), so sparse mode is dense
+    # attention masked to those columns
+    rng = np.random.default_rng(15)
+    N, nb, d = 256, 8, 64
+    k = rng.standard_normal((1, 1, N, d)).astype(np.float32)
+    qrow = rng.standard_normal(d).astype(np.float32)
+    q = np.broadcast_to(qrow, (1, 1, N, d)).copy()
+    v = rng.standard_normal((1, 1, N, d)).astype(np.float32)
+    out, sel = oracle.mra_forward(q, k, v, None, 2, "sparse", ranking="raw_logits", return_selection=True)
+    cells = sel[0, 0]
+    cols = sorted(set((cells % nb).tolist()))
+    assert len(cells) == 2 * nb and len(cols) == 2
+    assert all(((c // nb) * nb + cc) in set(cells.tolist()) for c in cells for cc in cols)
+    kh = k[0, 0].reshape(nb, 32, d).mean(1)
+    assert cols == sorted(np.argsort(-(kh @ qrow))[:2].tolist())
+    blk = np.arange(N) // 32
+    allowed = np.isin(blk, cols)[None, :].repeat(N, 0)
+    np.testing.assert_allclose(out, sdpa64(q, k, v, allowed), rtol=0, atol=1e-12)
+
+
 # -------------------------------------------------------- closed-form sets --
 @pytest.mark.parametrize("pf,pd,bpr,cells", [
     (0, 1, 1, lambda i, j: i == j),
