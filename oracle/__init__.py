@@ -71,6 +71,8 @@ def lib():
         L.oracle_dense_fwd.restype = ctypes.c_int
         L.oracle_mra_bwd.argtypes = [i32, i32, i32, i32, P, P, P, P, i32, i32, i32, i32, i32, P, P, P, P, i32]
         L.oracle_mra_bwd.restype = ctypes.c_int
+        L.oracle_bigbird_fwd.argtypes = [i32, i32, i32, i32, P, P, P, P, i32, i32, P, P, i32]
+        L.oracle_bigbird_fwd.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -217,4 +219,21 @@ def dense_forward(q, k, v, mask=None, threads=None):
                                 threads or default_threads())
     if rc:
         raise ValueError("oracle_dense_fwd failed: %d" % rc)
+    return out
+
+
+def bigbird_forward(q, k, v, rand, mask=None, block_size=64, threads=None):
+    """BigBird block-sparse attention ([BigBird]: 3-block window, the first
+    and last blocks global, r random key blocks per query block given in
+    rand [B, H, N / block_size, r]).  q, k, v: [B, H, N, d]; returns fp64."""
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    B, H, N, d = q.shape
+    rand = np.ascontiguousarray(rand, dtype=np.int32)
+    if rand.ndim != 4 or rand.shape[:3] != (B, H, N // block_size):
+        raise ValueError("rand must be [B, H, N / block_size, r]")
+    out = np.zeros((B, H, N, d), np.float64)
+    rc = lib().oracle_bigbird_fwd(B, H, N, d, _p(q), _p(k), _p(v), _p(_mask(mask)), block_size, rand.shape[3],
+                                  _p(rand), _p(out), threads or default_threads())
+    if rc:
+        raise ValueError("oracle_bigbird_fwd failed: %d" % rc)
     return out

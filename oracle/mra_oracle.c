@@ -18,7 +18,9 @@
  * multiple of 32) and "使用边界与结论" (bidirectional only).
  * The dense reference follows the textbook scaled-dot-product softmax
  * attention printed as "global MHRA" on the page "UniFormer ... MHRA"
- * (cited as [MHRA]).
+ * (cited as [MHRA]).  The block-sparse pattern of the last section follows
+ * the page "Transformers 中的 BigBird：面向超长序列的稀疏注意力模型完全指南"
+ * (cited as [BigBird]).
  *
  * Precision: selection is decided in fp32 in the fixed order written out
  * below (sequential sums and fused multiply-add chains, no reassociation);
@@ -623,6 +625,82 @@ done:
 }
 
 /* ------------------------------------------------------------------------ */
+/* BigBird block-sparse attention ([BigBird], the description of its three
+ * attention patterns, the usage notes and the BigBirdConfig table): the
+ * sequence is cut into nbb = N / bs blocks and query block I attends key
+ * block J when
+ *   I is a global block or J is a global block (the first and the last
+ *     block: two global blocks; reading B1),
+ *   |I - J| <= 1 (a window of three blocks, clipped at the ends; B2), or
+ *   J is one of row I's r random picks rand[I][0 .. r-1] (drawn outside and
+ *     passed in; a block is attended once however often it is named, and
+ *     picks outside [0, nbb) name nothing; B3).
+ * Each valid query token then takes exact softmax attention, scale
+ * 1/sqrt(d), over the valid keys of its attended blocks (B4); padded query
+ * rows and rows with no valid key output 0.  rand: [nbb, r]. */
+static int oracle_bigbird_head(int32_t N, int32_t d, int32_t bs, int32_t r, const int32_t* rand,
+                               const float* q, const float* k, const float* v, const uint8_t* mask,
+                               double* out)
+{
+    const int32_t nbb = N / bs;
+    const double tau = 1.0 / sqrt((double)d);
+    uint8_t* att = (uint8_t*)calloc((size_t)nbb * nbb, 1);
+    double* s = (double*)malloc(sizeof(double) * (size_t)N);
+    if (!att || !s) {
+        free(att);
+        free(s);
+        return -2;
+    }
+    for (int32_t I = 0; I < nbb; I++)
+        for (int32_t J = 0; J < nbb; J++) {
+            const int global = I == 0 || I == nbb - 1 || J == 0 || J == nbb - 1;
+            const int window = I - J <= 1 && J - I <= 1;
+            att[(int64_t)I * nbb + J] = (uint8_t)(global || window);
+        }
+    for (int32_t I = 0; I < nbb; I++)
+        for (int32_t x = 0; x < r; x++) {
+            const int32_t J = rand[(int64_t)I * r + x];
+            if (J >= 0 && J < nbb)
+                att[(int64_t)I * nbb + J] = 1;
+        }
+    for (int32_t t = 0; t < N; t++) {
+        double* o = out + (int64_t)t * d;
+        for (int32_t c = 0; c < d; c++)
+            o[c] = 0.0;
+        if (mask && !mask[t])
+            continue;
+        double shift = -INFINITY;
+        for (int32_t u = 0; u < N; u++) {
+            s[u] = -INFINITY;
+            if ((mask && !mask[u]) || !att[(int64_t)(t / bs) * nbb + u / bs])
+                continue;
+            double dot = 0.0;
+            for (int32_t c = 0; c < d; c++)
+                dot += (double)q[(int64_t)t * d + c] * (double)k[(int64_t)u * d + c];
+            s[u] = tau * dot;
+            if (s[u] > shift)
+                shift = s[u];
+        }
+        if (shift == -INFINITY)
+            continue;
+        double den = 0.0;
+        for (int32_t u = 0; u < N; u++) {
+            if (s[u] == -INFINITY)
+                continue;
+            const double w = exp(s[u] - shift);
+            den += w;
+            for (int32_t c = 0; c < d; c++)
+                o[c] += w * (double)v[(int64_t)u * d + c];
+        }
+        for (int32_t c = 0; c < d; c++)
+            o[c] /= den;
+    }
+    free(att);
+    free(s);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Batched drivers: independent (batch, head) units spread over nthreads
  * POSIX threads.  Each unit is computed by exactly the code above; the
  * threads only decide which unit runs where. */
@@ -636,6 +714,9 @@ typedef struct {
     int64_t K;
     int dense;
     int bwd;           /* gradients: dout in, dq / dk / dv out */
+    int bigbird;       /* BigBird pattern: block size bs, r picks per block row */
+    int32_t bs, r;
+    const int32_t* rand;
     const float* dout;
     double *dq, *dk, *dv;
     int next; /* shared unit counter */
@@ -654,7 +735,11 @@ static void* worker(void* p)
         int64_t off = (int64_t)u * j->N * j->d;
         const uint8_t* m = j->mask ? j->mask + (int64_t)b * j->N : NULL;
         int rc;
-        if (j->bwd)
+        if (j->bigbird)
+            rc = oracle_bigbird_head(j->N, j->d, j->bs, j->r,
+                                     j->rand + (int64_t)u * (j->N / j->bs) * j->r, j->q + off,
+                                     j->k + off, j->v + off, m, j->out + off);
+        else if (j->bwd)
             rc = oracle_mra_head_bwd(&j->ha, j->q + off, j->k + off, j->v + off, m, j->dout + off,
                                      j->dq + off, j->dk + off, j->dv + off);
         else if (j->dense)
@@ -744,5 +829,23 @@ int oracle_mra_bwd(int32_t B, int32_t H, int32_t N, int32_t d, const float* q,
     j.ha.N = N; j.ha.d = d; j.ha.block_per_row = block_per_row; j.ha.mode = mode;
     j.ha.prior_first = prior_first; j.ha.prior_diag = prior_diag; j.ha.ranking = ranking;
     j.K = K; j.bwd = 1; j.dout = dout; j.dq = dq; j.dk = dk; j.dv = dv;
+    return run_jobs(&j, nthreads);
+}
+
+/* BigBird block-sparse attention (oracle_bigbird_head) over [B, H, N, d]
+ * inputs; rand: [B, H, N / bs, r].  Returns 0, or -1 for invalid arguments
+ * (N not a positive multiple of bs, r < 0), -2 when out of memory. */
+int oracle_bigbird_fwd(int32_t B, int32_t H, int32_t N, int32_t d, const float* q,
+                       const float* k, const float* v, const uint8_t* mask, int32_t bs,
+                       int32_t r, const int32_t* rand, double* out, int32_t nthreads)
+{
+    if (B < 1 || H < 1 || d < 1 || bs < 1 || N < bs || N % bs != 0 || r < 0 ||
+        (r > 0 && !rand) || !q || !k || !v || !out)
+        return -1;
+    job_t j;
+    memset(&j, 0, sizeof(j));
+    j.B = B; j.H = H; j.N = N; j.d = d;
+    j.q = q; j.k = k; j.v = v; j.mask = mask;
+    j.out = out; j.bigbird = 1; j.bs = bs; j.r = r; j.rand = rand;
     return run_jobs(&j, nthreads);
 }

@@ -44,6 +44,10 @@ MUTANTS = {
                                                          "oracle_pool_f64(N, d, k, mask, vh64);"),
     "padded query rows not zeroed": ("if (mask && !mask[t])\n                continue; /* reading R12",
                                      "if (0)\n                continue; /* reading R12"),
+    "BigBird window of one block": ("const int window = I - J <= 1 && J - I <= 1;", "const int window = I == J;"),
+    "BigBird last block not global": ("const int global = I == 0 || I == nbb - 1 || J == 0 || J == nbb - 1;",
+                                      "const int global = I == 0 || J == 0;"),
+    "BigBird random picks ignored": ("                att[(int64_t)I * nbb + J] = 1;\n", "                (void)0;\n"),
     "backward drops D_t": ("const double ds = P * (dP - D);", "const double ds = P * dP;"),
     "backward drops tau on dk": ("dk[(int64_t)u * d + c] += tau * ds * (double)q[(int64_t)t * d + c];",
                                  "dk[(int64_t)u * d + c] += ds * (double)q[(int64_t)t * d + c];"),

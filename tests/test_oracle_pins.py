@@ -539,3 +539,84 @@ def test_bwd_matches_central_differences(mode):
             assert abs(fd - grads[which][0, 0, t, c]) <= 1e-5 * (1 + abs(fd)), (which, t, c, fd)
             checked += 1
     assert checked >= 24
+
+
+# ------------------------------------------------------- BigBird pattern ----
+def bigbird_allowed(N, bs, rand_bh):
+    """[N, N] bool from the pattern's three parts, built with numpy broadcasts."""
+    nbb = N // bs
+    I = np.arange(nbb)[:, None]
+    J = np.arange(nbb)[None, :]
+    blk = (np.abs(I - J) <= 1) | (I == 0) | (I == nbb - 1) | (J == 0) | (J == nbb - 1)
+    for i in range(nbb):
+        for x in rand_bh[i]:
+            if 0 <= x < nbb:
+                blk[i, x] = True
+    return np.repeat(np.repeat(blk, bs, 0), bs, 1)
+
+
+def test_bigbird_equals_block_masked_sdpa():
+    B, H, N, bs = 2, 2, 512, 64
+    q, k, v = rand_qkv(B, H, N, seed=61)
+    rand = workloads.bigbird_rand(B, H, N, bs, 2, seed=62)
+    mask = np.ones((B, N), np.uint8)
+    mask[1, 400:] = 0
+    got = oracle.bigbird_forward(q, k, v, rand, mask, bs)
+    for b in range(B):
+        for h in range(H):
+            allowed = bigbird_allowed(N, bs, rand[b, h]) & mask[b][None, :].astype(bool)
+            ref = sdpa64(q[b, h], k[b, h], v[b, h], allowed)
+            valid = mask[b].astype(bool)
+            np.testing.assert_allclose(got[b, h][valid], ref[valid], rtol=0, atol=1e-12)
+            assert np.all(got[b, h][~valid] == 0)
+
+
+def test_bigbird_short_sequence_is_dense():
+    # three blocks or fewer: the window and the two global blocks cover every pair
+    q, k, v = rand_qkv(1, 2, 192, seed=63)
+    got = oracle.bigbird_forward(q, k, v, np.full((1, 2, 3, 2), -1, np.int32), None, 64)
+    np.testing.assert_allclose(got, sdpa64(q, k, v), rtol=0, atol=1e-12)
+
+
+def test_bigbird_rows_see_only_their_blocks():
+    # a block row's output moves when an attended block's values change and
+    # stays bit-identical when a block outside its pattern changes
+    N, bs, nbb = 1024, 64, 16
+    q, k, v = rand_qkv(1, 1, N, seed=64)
+    rand = np.full((1, 1, nbb, 3), -1, np.int32)
+    rand[0, 0, 7] = [3, 12, 12]                     # a repeated pick names the block once
+    base = oracle.bigbird_forward(q, k, v, rand, None, bs)
+    rows = slice(7 * bs, 8 * bs)
+    for J, moves in [(3, True), (12, True), (6, True), (0, True), (15, True), (10, False), (4, False)]:
+        v2 = v.copy()
+        v2[0, 0, J * bs:(J + 1) * bs] += 1.0
+        out = oracle.bigbird_forward(q, k, v2, rand, None, bs)
+        assert (not np.array_equal(out[0, 0, rows], base[0, 0, rows])) == moves, J
+    # the global rows see every block
+    v2 = v.copy()
+    v2[0, 0, 5 * bs:6 * bs] += 1.0
+    out = oracle.bigbird_forward(q, k, v2, rand, None, bs)
+    assert not np.array_equal(out[0, 0, :bs], base[0, 0, :bs])
+    assert not np.array_equal(out[0, 0, -bs:], base[0, 0, -bs:])
+
+
+def test_bigbird_picks_outside_the_grid_name_nothing():
+    q, k, v = rand_qkv(1, 1, 512, seed=65)
+    none = oracle.bigbird_forward(q, k, v, np.full((1, 1, 8, 2), -1, np.int32), None, 64)
+    bad = np.full((1, 1, 8, 2), 8, np.int32)
+    bad[..., 1] = -5
+    assert np.array_equal(oracle.bigbird_forward(q, k, v, bad, None, 64), none)
+    # picks inside the window or on a global block change nothing either
+    inside = np.zeros((1, 1, 8, 2), np.int32)
+    inside[0, 0, :, 1] = np.clip(np.arange(8) + 1, 0, 7)
+    assert np.array_equal(oracle.bigbird_forward(q, k, v, inside, None, 64), none)
+
+
+def test_bigbird_generator_draws_outside_window_and_globals():
+    rand = workloads.bigbird_rand(2, 3, 4096, 64, 3, seed=66)
+    nbb = 64
+    for I in range(nbb):
+        picks = rand[:, :, I].reshape(-1, 3)
+        assert np.all(picks >= 1) and np.all(picks <= nbb - 2)
+        assert np.all(np.abs(picks - I) > 1)
+        assert all(len(set(p.tolist())) == 3 for p in picks)

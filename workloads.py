@@ -150,3 +150,39 @@ CONFIGS = {"C1": c1, "C2": c2, "C3": c3, "C4": c4, "C5": c5}
 
 def get(name: str) -> Workload:
     return CONFIGS[name]()
+
+
+def bigbird_rand(B, H, N, block_size=64, r=3, seed=0) -> np.ndarray:
+    """The random key blocks a BigBird layer draws for each query block
+    ([BigBird]: num_random_blocks per query block), drawn here and passed in
+    as an input: r distinct blocks outside the block's 3-block window and the
+    two global blocks (first and last), or -1 where fewer than r remain.
+    Returns int32 [B, H, N / block_size, r]."""
+    rng = np.random.default_rng(seed)
+    nbb = N // block_size
+    out = np.full((B, H, nbb, r), -1, np.int32)
+    for b in range(B):
+        for h in range(H):
+            for I in range(nbb):
+                cand = [J for J in range(1, nbb - 1) if abs(I - J) > 1]
+                if cand:
+                    pick = rng.choice(cand, size=min(r, len(cand)), replace=False)
+                    out[b, h, I, :len(pick)] = pick
+    return out
+
+
+@dataclass
+class BigBirdWorkload:
+    name: str
+    w: Workload                 # q, k, v, mask and dtype (block_per_row, approx_mode unused)
+    block_size: int
+    rand: np.ndarray = field(repr=False, default=None)   # int32 [B, H, N / block_size, r]
+
+
+def bigbird(name="BB-bf16-N4096-bs64-r3", B=2, H=12, N=4096, block_size=64, r=3, dtype="bf16", seed=6,
+            scale=0.5, mask=None) -> BigBirdWorkload:
+    """BigBird block-sparse workload: the page's defaults (block 64, three
+    random blocks) at the N = 4096 sequence length it is built for, iid
+    inputs of the same scale as the MRA workloads."""
+    w = iid(name, B, H, N, dtype=dtype, scale=scale, seed=seed, approx_mode="sparse", mask=mask)
+    return BigBirdWorkload(name, w, block_size, bigbird_rand(B, H, N, block_size, r, seed + 100))
