@@ -38,7 +38,12 @@ Besides tokens/s the line carries:
     bytes (Q, K, V, O, dO read once, dQ, dK, dV written once) and MFMA work
     (five 32x32x64 products per selected block: S, dP, dS K, dS^T Q, P^T dO;
     the low-res terms of full mode, 4 nb^2 d multiply-adds per head, are
-    left out) over that time.
+    left out) over that time;
+  * `bigbird`: BigBird block-sparse attention (mra_bigbird_fwd: the BigBird
+    page's window of three blocks, two global blocks and three random blocks
+    of 64 tokens) on B=2, H=12, N=4096 bf16, through the same attention
+    kernels; algorithmic bytes Q, K, V read and O written once, MFMA work
+    4 x 32 x 32 x 64 per attended 32-token cell.
 Only one GPU is used; --gpus above 1 exits with a message.
 """
 from __future__ import annotations
@@ -171,6 +176,54 @@ def bench_backward(mra, steps: int, warmup: int, cfg: str) -> dict:
             "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
+def bench_bigbird(mra, steps: int, warmup: int) -> dict:
+    """BigBird block-sparse attention (the BigBird page's pattern: window of
+    three blocks, first and last blocks global, three random blocks, block
+    64) on the N=4096 bf16 workload, through the same attention kernels."""
+    import numpy as np
+    import torch
+
+    import workloads
+
+    bb = workloads.bigbird()
+    w = bb.w
+    to_dev = lambda n: torch.from_numpy(w.raw(n).view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v = to_dev("q"), to_dev("k"), to_dev("v")
+    rand = torch.from_numpy(bb.rand).cuda()
+    run, out = mra.prepare_bigbird(q, k, v, rand, None, bb.block_size)
+    for _ in range(warmup):
+        run()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    # attended 32-token cells: f x f per attended pattern cell
+    nbb, f = w.N // bb.block_size, bb.block_size // 32
+    cells = 0
+    for b in range(w.B):
+        for h in range(w.H):
+            I = np.arange(nbb)[:, None]
+            J = np.arange(nbb)[None, :]
+            att = (np.abs(I - J) <= 1) | (I == 0) | (I == nbb - 1) | (J == 0) | (J == nbb - 1)
+            for i in range(nbb):
+                for x in bb.rand[b, h, i]:
+                    if 0 <= x < nbb:
+                        att[i, x] = True
+            cells += int(att.sum()) * f * f
+    nbytes = 4.0 * w.B * w.H * w.N * w.d * 2
+    flops = 4.0 * 32 * 32 * w.d * cells
+    return {"workload": w.name, "block_size": bb.block_size, "num_random_blocks": int(bb.rand.shape[3]),
+            "ms_per_call": round(ms, 5), "tokens_per_s": round(w.B * w.N / (ms * 1e-3), 1),
+            "attended_cells_32": cells, "algorithmic_bytes": int(nbytes),
+            "achieved_GBs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "mfma_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -179,6 +232,9 @@ def main():
     ap.add_argument("--config", default="C4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-bigbird", action="store_true")
+    ap.add_argument("--only-bigbird", action="store_true",
+                    help="only time BigBird block-sparse attention on its N=4096 workload")
     ap.add_argument("--only-backward", metavar="CFG", default=None,
                     help="only time the backward pass on workload CFG (C3 or C4) and print its record")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -205,6 +261,10 @@ def main():
     import block_sparse_approximate_amd as mra
     import workloads
 
+    if args.only_bigbird:
+        torch.cuda.set_device(torch.device("cuda:0"))
+        print(json.dumps({"bigbird": bench_bigbird(mra, args.steps, args.warmup)}), flush=True)
+        return
     if args.only_backward:
         torch.cuda.set_device(torch.device("cuda:0"))
         print(json.dumps({"backward": bench_backward(mra, args.steps, args.warmup, args.only_backward)}),
@@ -327,6 +387,8 @@ def main():
     }
     if not args.no_backward:
         rec["backward"] = [bench_backward(mra, args.steps, args.warmup, cfg) for cfg in ("C3", "C4")]
+    if not args.no_bigbird:
+        rec["bigbird"] = bench_bigbird(mra, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(rec), flush=True)

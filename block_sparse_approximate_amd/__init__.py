@@ -44,6 +44,8 @@ SIGNATURES = {
     "mra_debug_stages": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P,
                           _P, _P, _SZ, _P], ctypes.c_int),
     "mra_debug_select": ([_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P], ctypes.c_int),
+    "mra_bigbird_workspace_size": ([_P, _I32, _I32, ctypes.POINTER(_SZ)], ctypes.c_int),
+    "mra_bigbird_fwd": ([_P, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "mra_backward_workspace_size": ([_P, _I32, _I32, ctypes.POINTER(_SZ)], ctypes.c_int),
     "mra_attention_bwd": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P, _SZ,
                            _P], ctypes.c_int),
@@ -358,3 +360,50 @@ def debug_select(logits, count, batch, heads, block_per_row=4, initial_prior_fir
                                 RANKINGS.get(score_ranking, -1), _ptr(sel), _ptr(ws), ws_bytes, _stream(logits))
     _check(st, "mra_debug_select")
     return sel[:, :, :K]
+
+
+def bigbird_workspace_size(batch, heads, seq_len, head_dim=64, dtype=torch.bfloat16, block_size=64,
+                           num_random_blocks=3) -> int:
+    n = _SZ(0)
+    dims = _dims(batch, heads, seq_len, head_dim, DTYPES.get(dtype, -1))
+    _check(lib().mra_bigbird_workspace_size(ctypes.byref(dims), block_size, num_random_blocks, ctypes.byref(n)),
+           "mra_bigbird_workspace_size")
+    return n.value
+
+
+def prepare_bigbird(q, k, v, rand_blocks, mask=None, block_size=64, out=None, workspace=None):
+    """Check and marshal BigBird block-sparse attention once (mra_bigbird_fwd);
+    rand_blocks: int32 device tensor [B, H, seq_len / block_size, r] of the
+    random key blocks drawn per query block.  Returns (call, out)."""
+    _check_inputs(q, k, v, mask)
+    B, H, N, d = q.shape
+    if (not rand_blocks.is_cuda or rand_blocks.dtype != torch.int32 or rand_blocks.dim() != 4
+            or not rand_blocks.is_contiguous() or tuple(rand_blocks.shape[:3]) != (B, H, N // block_size)):
+        raise ValueError("rand_blocks must be a contiguous int32 device tensor [B, H, seq_len / block_size, r]")
+    r = rand_blocks.shape[3]
+    out = torch.empty_like(q) if out is None else out
+    ws_bytes = bigbird_workspace_size(B, H, N, d, q.dtype, block_size, r)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    dims = _dims(B, H, N, d, DTYPES[q.dtype])
+    fn = lib().mra_bigbird_fwd
+    args = (ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), block_size, r, _ptr(rand_blocks), _ptr(out),
+            _ptr(workspace), workspace.numel(), _stream(q))
+    keep = (dims, q, k, v, mask, rand_blocks, out, workspace)
+
+    def call():
+        st = fn(*args)
+        if st != 0:
+            raise MraError(st, "mra_bigbird_fwd")
+        return keep[6]
+
+    return call, out
+
+
+def bigbird_attention(q, k, v, rand_blocks, mask=None, block_size=64, out=None, workspace=None):
+    """BigBird block-sparse attention ([BigBird] pattern: window of three
+    blocks, first and last blocks global, the given random blocks) on
+    [batch, heads, seq_len, 64] tensors.  Returns `out`."""
+    call, out = prepare_bigbird(q, k, v, rand_blocks, mask, block_size, out, workspace)
+    call()
+    return out

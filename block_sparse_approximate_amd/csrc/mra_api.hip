@@ -10,6 +10,8 @@
 // Everything after the argument checks is asynchronous; nothing here waits.
 #include <string.h>
 
+#include <algorithm>
+
 #include "../../include/mra.h"
 #include "mra_common.h"
 
@@ -390,6 +392,72 @@ MRA_API mra_status mra_attention_bwd(const mra_dims* dims, const void* q, const 
     p.bwd_dkh = fl(W.dkh);
     p.bwd_dvh = fl(W.dvh);
     return launch_bwd(p, static_cast<hipStream_t>(stream)) == hipSuccess ? MRA_OK : MRA_ERR_HIP;
+}
+
+// ---------------------------------------------------------------- BigBird
+// Largest number of 32-token cells a BigBird pattern can select per head:
+// global rows attend every pattern block, the others at most 3 + 2 + r.
+static bool bigbird_budget(const mra_dims* d, int32_t block_size, int32_t r, int32_t* bpr) {
+    if (block_size < kBlock || block_size % kBlock != 0 || block_size > 4 * kBlock) return false;
+    if (d->seq_len % block_size != 0 || d->seq_len < block_size) return false;
+    const int64_t f = block_size / kBlock, nbb = d->seq_len / block_size, nb = d->seq_len / kBlock;
+    int64_t cells = 0;
+    for (int64_t I = 0; I < nbb; I++) {
+        const int64_t row = (I == 0 || I == nbb - 1) ? nbb : std::min<int64_t>(nbb, 5 + (int64_t)r);
+        cells += f * f * row;
+    }
+    cells = std::min<int64_t>(cells, nb * nb);
+    *bpr = (int32_t)((cells + nb - 1) / nb);   // mra_num_block(N, bpr) >= cells
+    return true;
+}
+
+static mra_status check_bigbird(const mra_dims* dims, int32_t block_size, int32_t r, int32_t* bpr) {
+    mra_status st = check_dims(dims);
+    if (st != MRA_OK) return st;
+    if (r < 1) return MRA_ERR_BUDGET;
+    if (!bigbird_budget(dims, block_size, r, bpr)) return MRA_ERR_SEQ_LEN;
+    return MRA_OK;
+}
+
+MRA_API mra_status mra_bigbird_workspace_size(const mra_dims* dims, int32_t block_size, int32_t num_random_blocks,
+                                              size_t* bytes) {
+    if (!bytes || !dims) return MRA_ERR_NULL;
+    int32_t bpr = 0;
+    const mra_status st = check_bigbird(dims, block_size, num_random_blocks, &bpr);
+    if (st != MRA_OK) return st;
+    Layout L;
+    if (!carve(*dims, bpr, MRA_APPROX_SPARSE, &L)) return MRA_ERR_SEQ_LEN;
+    *bytes = L.total;
+    return MRA_OK;
+}
+
+MRA_API mra_status mra_bigbird_fwd(const mra_dims* dims, const void* q, const void* k, const void* v,
+                                   const uint8_t* mask, int32_t block_size, int32_t num_random_blocks,
+                                   const int32_t* rand_blocks, void* out, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+    if (!dims) return MRA_ERR_NULL;
+    int32_t bpr = 0;
+    mra_status st = check_bigbird(dims, block_size, num_random_blocks, &bpr);
+    if (st != MRA_OK) return st;
+    Layout L;
+    st = check_call(dims, q, k, v, mask, bpr, MRA_APPROX_SPARSE, 0, 0, out, workspace, workspace_bytes, true, &L);
+    if (st != MRA_OK) return st;
+    if (!rand_blocks) return MRA_ERR_NULL;
+    if (((uintptr_t)rand_blocks & 3u) != 0) return MRA_ERR_ALIGN;
+    const size_t rbytes = (size_t)L.BH * (dims->seq_len / block_size) * num_random_blocks * 4;
+    if (overlaps(out, (size_t)L.BH * L.N * L.d * (dims->dtype == MRA_BF16 ? 2 : 4), rand_blocks, rbytes) ||
+        overlaps(workspace, workspace_bytes, rand_blocks, rbytes))
+        return MRA_ERR_ALIAS;
+    Params p = make_params(*dims, L, MRA_APPROX_SPARSE, 0, 0, q, k, v, mask, out, workspace);
+    p.attn_dyn = 1;
+    p.bb_f = block_size / kBlock;
+    p.bb_r = num_random_blocks;
+    p.bb_rand = rand_blocks;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (launch_bigbird_layout(p, s) != hipSuccess) return MRA_ERR_HIP;
+    if (launch_attn(p, s) != hipSuccess) return MRA_ERR_HIP;
+    if (launch_finish(p, s) != hipSuccess) return MRA_ERR_HIP;
+    return MRA_OK;
 }
 
 MRA_API mra_status mra_debug_replay(const mra_dims* dims, const void* q, const void* k, const void* v,

@@ -455,13 +455,15 @@ __device__ __forceinline__ void process(const Params& p, const Wave<DT>& W, int 
 template <int DT, bool FULL>
 __device__ __forceinline__ void run_range(const Params& p, int bh, int k, int WPH, int lane, int wave,
                                           StageBuf<DT>& sb) {
-    const int64_t K = p.K;
+    // the head's stream: K records (a static layout fills row_ptr[nb] of its
+    // capacity K)
+    const int64_t K = p.attn_dyn ? min((int64_t)p.row_ptr[(size_t)bh * (p.nb + 1) + p.nb], p.K) : p.K;
     const int a = (int)((int64_t)k * K / WPH);
     const int bnd = (int)((int64_t)(k + 1) * K / WPH);
     // the record window starts half a segment before a: the range's first
     // block may move back that far
     const int a0 = max(a - kChunk / 2, 0);
-    const BlkRec* R = p.recs + (size_t)bh * K;
+    const BlkRec* R = p.recs + (size_t)bh * p.K;
     Wave<DT> W;
     W.a = a0;
     W.bh = bh;

@@ -124,6 +124,10 @@ struct Params {
     float* bwd_dkh;
     float* bwd_dvh;
     int32_t* error;        // device error flag (0 = fine)
+    int32_t attn_dyn;      // 1: a head's stream holds row_ptr[nb] records (a static layout), not K
+    int32_t bb_f;          // BigBird layout: pattern block = bb_f blocks of 32 tokens
+    int32_t bb_r;          //   random picks per pattern row
+    const int32_t* bb_rand;  // [BH, N / (32 bb_f), bb_r]
     int32_t attn_wph;      // attention stream: waves sharing one head's blocks
     int32_t attn_seq;      // 1: those are all the waves of an XCD, which take the XCD's heads in turn
 };
@@ -183,6 +187,7 @@ hipError_t launch_premark(const Params& p, hipStream_t s);
 hipError_t launch_select(const Params& p, hipStream_t s);
 hipError_t launch_attn(const Params& p, hipStream_t s);
 hipError_t launch_finish(const Params& p, hipStream_t s);
+hipError_t launch_bigbird_layout(const Params& p, hipStream_t s);
 int bwd_max_chunks(int nb, int64_t K);
 hipError_t launch_bwd(const Params& p, hipStream_t s);
 int attn_grid_waves_per_head(int BH, int64_t K);

@@ -751,6 +751,100 @@ __global__ __launch_bounds__(kSelThreads) void premark_kernel(Params p) {
 }
 
 // ---------------------------------------------------------------- select
+// ---------------------------------------------------------------- stream
+// Head bh's selection, given as its bitmap in LDS (nb rows of `words`
+// words), into what the attention and join kernels read: the CSR (row_ptr,
+// col), the bitmap in memory, the segment pointers, the rows the join
+// kernel combines and one record per selected block.  mbv: the blocks' mask
+// words in LDS (written before the call; read after its barriers).  expect:
+// the number of selected cells the caller made (the error word's bit 2
+// flags another count), or -1 when the count is the layout's own (it must
+// stay within the stream's capacity p.K).  Called by a whole kSelThreads
+// workgroup.
+__device__ __forceinline__ void emit_stream(const Params& p, int bh, const uint32_t* bitmap, const uint32_t* mbv, int* rc,
+                            int* ic, uint64_t* scan64, int64_t expect) {
+    const int nb = p.nb, words = p.words;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // CSR row pointers, segment (item) pointers and the rows the final kernel
+    // combines, in one scan: one block row per thread (nb <= 512)
+    int32_t* row_ptr = p.row_ptr + (size_t)bh * (nb + 1);
+    int32_t* item_ptr = p.item_ptr + (size_t)bh * (nb + 1);
+    {
+        const int i = tid;
+        int c = 0;
+        if (i < nb)
+            for (int w = 0; w < words; w++) c += __popc(bitmap[i * words + w]);
+        const int it = (c + kChunk - 1) / kChunk;
+        const int mf = (i < nb && it != 1) ? 1 : 0;   // no selected block, or several segments
+        const uint64_t v = (uint64_t)c | ((uint64_t)it << 32) | ((uint64_t)mf << 48);
+        uint64_t tot;
+        const uint64_t ex = block_excl_scan<uint64_t>(v, scan64, &tot);
+        const int ec = (int)(uint32_t)ex, ei = (int)((ex >> 32) & 0xFFFFu), em = (int)(ex >> 48);
+        if (i < nb) {
+            row_ptr[i] = ec;
+            item_ptr[i] = ei;
+            rc[i] = ec;
+            ic[i] = ei;
+            if (mf) p.merge_rows[(size_t)bh * nb + em] = make_int4(i, ei, it, 0);
+        }
+        if (tid == 0) {
+            const int tc = (int)(uint32_t)tot, ti = (int)((tot >> 32) & 0xFFFFu), tm = (int)(tot >> 48);
+            row_ptr[nb] = tc;
+            item_ptr[nb] = ti;
+            rc[nb] = tc;
+            ic[nb] = ti;
+            p.n_merge[bh] = tm;
+            if ((expect >= 0 ? (int64_t)tc != expect : (int64_t)tc > p.K) || ti > p.max_items) atomicOr(reinterpret_cast<unsigned int*>(p.error), 2u);
+        }
+    }
+    __syncthreads();
+
+    // column lists and the attention stream records: one thread per (block
+    // row, bitmap word), which walks the set bits of its word; a cell's rank
+    // in its row counts the bits of the row's earlier words
+    int32_t* col = p.col + (size_t)bh * p.K;
+    BlkRec* recs = p.recs + (size_t)bh * p.K;
+    uint32_t* gbits = p.selbits + (size_t)bh * nb * words;
+    const bool pow2w = (words & (words - 1)) == 0;   // then 64 % words == 0
+    for (int x0 = 0; x0 < nb * words; x0 += kSelThreads) {
+        const int x = x0 + tid;
+        const bool in = x < nb * words;
+        uint32_t bits = in ? bitmap[x] : 0u;
+        const int i = x / words, w = x - i * words;
+        int r = 0;
+        if (pow2w) {
+            // a block row's words sit in `words` consecutive lanes: the rank
+            // of the word's first bit is a segmented scan along the row
+            const int c = __popc(bits);
+            int inc = c;
+            for (int off = 1; off < words; off <<= 1) {
+                const int y = __shfl_up(inc, off, 64);
+                if ((lane & (words - 1)) >= off) inc += y;
+            }
+            r = inc - c;
+        }
+        if (!in) continue;
+        gbits[x] = bits;
+        if (!bits) continue;
+        if (!pow2w)
+            for (int u = 0; u < w; u++) r += __popc(bitmap[i * words + u]);
+        const int o = rc[i], n = rc[i + 1] - o, first = ic[i];
+        const int nit = (n + kChunk - 1) / kChunk;
+        while (bits) {
+            const int j = w * 32 + __builtin_ctz(bits);
+            bits &= bits - 1;
+            const int e = o + r;
+            if (e < p.K) {
+                col[e] = j;
+                const int sg = r / kChunk;
+                const int len = min(kChunk, n - sg * kChunk);
+                recs[e] = BlkRec{rec_ij(i, j), mbv[j], 0u, rec_info(first + sg, r - sg * kChunk, len, nit == 1)};
+            }
+            r++;
+        }
+    }
+}
+
 __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int nb = p.nb;
@@ -924,85 +1018,77 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
 
     // the records' input, loaded in the prologue (read after the scan's barriers)
     if (tid < nb) mbv[tid] = mv;
+    emit_stream(p, bh, bitmap, mbv, rc, ic, scan64, p.K);
+}
 
-    // CSR row pointers, segment (item) pointers and the rows the final kernel
-    // combines, in one scan: one block row per thread (nb <= 512)
-    int32_t* row_ptr = p.row_ptr + (size_t)bh * (nb + 1);
-    int32_t* item_ptr = p.item_ptr + (size_t)bh * (nb + 1);
-    {
-        const int i = tid;
-        int c = 0;
-        if (i < nb)
-            for (int w = 0; w < words; w++) c += __popc(bitmap[i * words + w]);
-        const int it = (c + kChunk - 1) / kChunk;
-        const int mf = (i < nb && it != 1) ? 1 : 0;   // no selected block, or several segments
-        const uint64_t v = (uint64_t)c | ((uint64_t)it << 32) | ((uint64_t)mf << 48);
-        uint64_t tot;
-        const uint64_t ex = block_excl_scan<uint64_t>(v, scan64, &tot);
-        const int ec = (int)(uint32_t)ex, ei = (int)((ex >> 32) & 0xFFFFu), em = (int)(ex >> 48);
-        if (i < nb) {
-            row_ptr[i] = ec;
-            item_ptr[i] = ei;
-            rc[i] = ec;
-            ic[i] = ei;
-            if (mf) p.merge_rows[(size_t)bh * nb + em] = make_int4(i, ei, it, 0);
+// ---------------------------------------------------------------- BigBird layout
+// A static block-sparse pattern as a selection of 32-token blocks, for the
+// same attention and join kernels ([BigBird]: a window of three blocks, two
+// global blocks and num_random_blocks random blocks per query block).  With
+// pattern blocks of bs = 32 f tokens, nbb = N / bs, pattern row I attends
+// pattern block J when I or J is the first or last block, |I - J| <= 1, or J
+// is one of the row's given picks (picks outside [0, nbb) name nothing; a
+// block named twice is attended once); a pattern cell is f x f cells of
+// 32-token blocks.  One workgroup per head (on the head's XCD); it also
+// writes the blocks' mask words and counts, which pooling writes on the MRA
+// path.
+__global__ __launch_bounds__(kSelThreads) void bigbird_layout_kernel(Params p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int nb = p.nb, words = p.words;
+    const int bh = blockIdx.x;
+    if (bh >= p.BH) return;
+    const int b = bh / p.H, tid = threadIdx.x;
+    const SelectLds L = select_lds(nb);
+    uint32_t* bitmap = reinterpret_cast<uint32_t*>(smem + L.bitmap);
+    int* rc = reinterpret_cast<int*>(smem + L.rc);
+    int* ic = reinterpret_cast<int*>(smem + L.ic);
+    uint32_t* mbv = reinterpret_cast<uint32_t*>(smem + L.mbv);
+    uint64_t* scan64 = reinterpret_cast<uint64_t*>(smem + L.scan);
+    const int f = p.bb_f, nbb = nb / f, r = p.bb_r;
+    if (tid < nb) {
+        // block tid's mask word: bit t = token 32 tid + t is valid
+        uint32_t m = 0xFFFFFFFFu;
+        if (p.mask) {
+            const uint4* src = reinterpret_cast<const uint4*>(p.mask + (size_t)b * p.N + (size_t)tid * kBlock);
+            m = 0u;
+#pragma unroll
+            for (int x = 0; x < 2; x++) {
+                const uint4 u = src[x];
+                const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                for (int y = 0; y < 16; y++)
+                    if ((w4[y >> 2] >> (8 * (y & 3))) & 0xFFu) m |= 1u << (16 * x + y);
+            }
         }
-        if (tid == 0) {
-            const int tc = (int)(uint32_t)tot, ti = (int)((tot >> 32) & 0xFFFFu), tm = (int)(tot >> 48);
-            row_ptr[nb] = tc;
-            item_ptr[nb] = ti;
-            rc[nb] = tc;
-            ic[nb] = ti;
-            p.n_merge[bh] = tm;
-            if ((int64_t)tc != p.K || ti > p.max_items) atomicOr(reinterpret_cast<unsigned int*>(p.error), 2u);
+        mbv[tid] = m;
+        if (bh % p.H == 0) {
+            p.mbits[(size_t)b * nb + tid] = m;
+            p.cnt[(size_t)b * nb + tid] = __popc(m);
+        }
+        // row tid of the bitmap belongs to this thread alone
+        uint32_t* row = bitmap + (size_t)tid * words;
+        for (int w = 0; w < words; w++) row[w] = 0u;
+        const int I = tid / f;
+        auto attend = [&](int J) {
+            for (int c = 0; c < f; c++) {
+                const int j = f * J + c;
+                row[j >> 5] |= 1u << (j & 31);
+            }
+        };
+        if (I == 0 || I == nbb - 1) {
+            for (int w = 0; w < words; w++) row[w] = (w + 1) * 32 <= nb ? 0xFFFFFFFFu : (1u << (nb & 31)) - 1u;
+        } else {
+            attend(0);
+            attend(nbb - 1);
+            for (int J = I - 1; J <= I + 1; J++) attend(J);
+            const int32_t* picks = p.bb_rand + ((size_t)bh * nbb + I) * r;
+            for (int x = 0; x < r; x++) {
+                const int J = picks[x];
+                if (J >= 0 && J < nbb) attend(J);
+            }
         }
     }
-    __syncthreads();
-
-    // column lists and the attention stream records: one thread per (block
-    // row, bitmap word), which walks the set bits of its word; a cell's rank
-    // in its row counts the bits of the row's earlier words
-    int32_t* col = p.col + (size_t)bh * p.K;
-    BlkRec* recs = p.recs + (size_t)bh * p.K;
-    uint32_t* gbits = p.selbits + (size_t)bh * nb * words;
-    const bool pow2w = (words & (words - 1)) == 0;   // then 64 % words == 0
-    for (int x0 = 0; x0 < nb * words; x0 += kSelThreads) {
-        const int x = x0 + tid;
-        const bool in = x < nb * words;
-        uint32_t bits = in ? bitmap[x] : 0u;
-        const int i = x / words, w = x - i * words;
-        int r = 0;
-        if (pow2w) {
-            // a block row's words sit in `words` consecutive lanes: the rank
-            // of the word's first bit is a segmented scan along the row
-            const int c = __popc(bits);
-            int inc = c;
-            for (int off = 1; off < words; off <<= 1) {
-                const int y = __shfl_up(inc, off, 64);
-                if ((lane & (words - 1)) >= off) inc += y;
-            }
-            r = inc - c;
-        }
-        if (!in) continue;
-        gbits[x] = bits;
-        if (!bits) continue;
-        if (!pow2w)
-            for (int u = 0; u < w; u++) r += __popc(bitmap[i * words + u]);
-        const int o = rc[i], n = rc[i + 1] - o, first = ic[i];
-        const int nit = (n + kChunk - 1) / kChunk;
-        while (bits) {
-            const int j = w * 32 + __builtin_ctz(bits);
-            bits &= bits - 1;
-            const int e = o + r;
-            if (e < p.K) {
-                col[e] = j;
-                const int sg = r / kChunk;
-                const int len = min(kChunk, n - sg * kChunk);
-                recs[e] = BlkRec{rec_ij(i, j), mbv[j], 0u, rec_info(first + sg, r - sg * kChunk, len, nit == 1)};
-            }
-            r++;
-        }
-    }
+    emit_stream(p, bh, bitmap, mbv, rc, ic, scan64, -1);
 }
 
 }  // namespace
@@ -1043,4 +1129,14 @@ hipError_t launch_select(const Params& p, hipStream_t s) {
     return hipGetLastError();
 }
 
+}  // namespace mra
+
+namespace mra {
+hipError_t launch_bigbird_layout(const Params& p, hipStream_t s) {
+    static const hipError_t a = hipFuncSetAttribute(reinterpret_cast<const void*>(&bigbird_layout_kernel),
+                                                    hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (a != hipSuccess) return a;
+    hipLaunchKernelGGL(bigbird_layout_kernel, dim3(p.BH), dim3(kSelThreads), select_lds(p.nb).total, s, p);
+    return hipGetLastError();
+}
 }  // namespace mra

@@ -175,6 +175,32 @@ mra_status mra_debug_select(const mra_dims* dims, const float* logits, const int
                             int32_t score_ranking, int32_t* sel, void* workspace, size_t workspace_bytes,
                             void* stream);
 
+/* BigBird block-sparse attention through the same block-attention kernels
+ * (page "Transformers 中的 BigBird：面向超长序列的稀疏注意力模型完全指南",
+ * its description of the three attention patterns and the BigBirdConfig
+ * table).  The sequence is cut into nbb = seq_len / block_size pattern
+ * blocks; query block I attends key block J when I or J is the first or the
+ * last block (the two global blocks), when |I - J| <= 1 (the window of three
+ * blocks), or when J is one of row I's random picks; each valid query token
+ * then takes exact softmax attention (scale 1/sqrt(d)) over the valid keys of
+ * its attended blocks.  Padded query rows output 0.
+ *   block_size        32, 64 (the page's default) or 128; seq_len a
+ *                     multiple of it (MRA_ERR_SEQ_LEN otherwise)
+ *   num_random_blocks r >= 1 (the page: 0 is not supported; MRA_ERR_BUDGET)
+ *   rand_blocks       device int32 [B, H, nbb, r]: the random key blocks the
+ *                     layer drew for each query block (the caller draws them);
+ *                     values outside [0, nbb) name no block, a block named
+ *                     more than once or also in the window is attended once
+ *   the other arguments as for mra_attention_fwd; workspace of
+ *   mra_bigbird_workspace_size bytes.  No fallback to full attention for
+ *   short sequences: the pattern is applied as stated at every length. */
+mra_status mra_bigbird_workspace_size(const mra_dims* dims, int32_t block_size, int32_t num_random_blocks,
+                                      size_t* bytes);
+mra_status mra_bigbird_fwd(const mra_dims* dims, const void* q, const void* k, const void* v,
+                           const uint8_t* mask, int32_t block_size, int32_t num_random_blocks,
+                           const int32_t* rand_blocks, void* out, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
 /* Bytes of the backward pass's own workspace for these dimensions and
  * selection parameters (mra_attention_bwd's bwd_workspace): the dO . O row
  * terms, the transposed selection, the work chunks, fp32 partial gradients

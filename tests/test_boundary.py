@@ -23,7 +23,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     L = mra.lib()
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 14
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(mra.SIGNATURES)
@@ -185,3 +185,31 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 64, 64)
     with pytest.raises(ValueError):
         mra.attention(q, q, q)
+
+
+def test_bigbird_workspace_and_argument_checks():
+    assert mra.bigbird_workspace_size(2, 12, 4096) > 0
+    for kw, status in [(dict(seq_len=4000), 3), (dict(block_size=48), 3), (dict(block_size=256), 3),
+                       (dict(num_random_blocks=0), 7), (dict(seq_len=100), 3)]:
+        args = dict(batch=1, heads=2, seq_len=512, block_size=64, num_random_blocks=3)
+        args.update(kw)
+        with pytest.raises(mra.MraError) as e:
+            mra.bigbird_workspace_size(args["batch"], args["heads"], args["seq_len"], block_size=args["block_size"],
+                                       num_random_blocks=args["num_random_blocks"])
+        assert e.value.status == status, kw
+    L = mra.lib()
+    d = mra._Dims(1, 2, 512, 64, 1)
+    RB = 0xC0000000
+    ws = mra.bigbird_workspace_size(1, 2, 512)
+    call = lambda **kw: L.mra_bigbird_fwd(ctypes.byref(d), kw.get("q", Q), K, V, None, kw.get("bs", 64),
+                                          kw.get("r", 3), kw.get("rand", RB), kw.get("out", O), W,
+                                          kw.get("ws_bytes", ws), None)
+    assert call(rand=None) == 1
+    assert call(q=None) == 1
+    assert call(rand=RB + 2) == 12
+    assert call(rand=O) == 9
+    assert call(out=Q) == 9
+    assert call(ws_bytes=64) == 10
+    assert call(r=0) == 7
+    assert call(bs=96) == 3
+    assert L.mra_bigbird_fwd(None, Q, K, V, None, 64, 3, RB, O, W, ws, None) == 1
