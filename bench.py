@@ -43,7 +43,8 @@ Besides tokens/s the line carries:
     page's window of three blocks, two global blocks and three random blocks
     of 64 tokens) on B=2, H=12, N=4096 bf16, through the same attention
     kernels; algorithmic bytes Q, K, V read and O written once, MFMA work
-    4 x 32 x 32 x 64 per attended 32-token cell.
+    4 x 32 x 32 x 64 per attended 32-token cell; and its backward pass
+    (mra_bigbird_bwd) timed the same way.
 Only one GPU is used; --gpus above 1 exits with a message.
 """
 from __future__ import annotations
@@ -200,6 +201,25 @@ def bench_bigbird(mra, steps: int, warmup: int) -> dict:
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
+    # its backward pass (mra_bigbird_bwd) on the layout that forward left
+    g = torch.from_numpy(np.random.default_rng(2).standard_normal(q.shape).astype(np.float32)).to(torch.bfloat16)
+    g = g.cuda()
+    r = int(bb.rand.shape[3])
+    fws = torch.empty(mra.bigbird_workspace_size(w.B, w.H, w.N, w.d, torch.bfloat16, bb.block_size, r),
+                      dtype=torch.uint8, device="cuda")
+    out = mra.bigbird_attention(q, k, v, rand, None, bb.block_size, workspace=fws)
+    bws = torch.empty(mra.bigbird_backward_workspace_size(w.B, w.H, w.N, w.d, torch.bfloat16, bb.block_size, r),
+                      dtype=torch.uint8, device="cuda")
+    grads = [torch.empty_like(q) for _ in range(3)]
+    bwd = lambda: mra.bigbird_backward(q, k, v, out, g, fws, r, None, bb.block_size, *grads, bwd_workspace=bws)
+    for _ in range(warmup):
+        bwd()
+    e0.record()
+    for _ in range(steps):
+        bwd()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_bwd = e0.elapsed_time(e1) / steps
     # attended 32-token cells: f x f per attended pattern cell
     nbb, f = w.N // bb.block_size, bb.block_size // 32
     cells = 0
@@ -221,7 +241,9 @@ def bench_bigbird(mra, steps: int, warmup: int) -> dict:
             "achieved_GBs": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "mfma_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
-            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "backward_ms_per_call": round(ms_bwd, 5),
+            "backward_tokens_per_s": round(w.B * w.N / (ms_bwd * 1e-3), 1)}
 
 
 def main():

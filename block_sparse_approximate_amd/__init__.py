@@ -46,6 +46,8 @@ SIGNATURES = {
     "mra_debug_select": ([_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P], ctypes.c_int),
     "mra_bigbird_workspace_size": ([_P, _I32, _I32, ctypes.POINTER(_SZ)], ctypes.c_int),
     "mra_bigbird_fwd": ([_P, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _SZ, _P], ctypes.c_int),
+    "mra_bigbird_backward_workspace_size": ([_P, _I32, _I32, ctypes.POINTER(_SZ)], ctypes.c_int),
+    "mra_bigbird_bwd": ([_P, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P, _SZ, _P], ctypes.c_int),
     "mra_backward_workspace_size": ([_P, _I32, _I32, ctypes.POINTER(_SZ)], ctypes.c_int),
     "mra_attention_bwd": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P, _SZ,
                            _P], ctypes.c_int),
@@ -407,3 +409,37 @@ def bigbird_attention(q, k, v, rand_blocks, mask=None, block_size=64, out=None, 
     call, out = prepare_bigbird(q, k, v, rand_blocks, mask, block_size, out, workspace)
     call()
     return out
+
+
+def bigbird_backward_workspace_size(batch, heads, seq_len, head_dim=64, dtype=torch.bfloat16, block_size=64,
+                                    num_random_blocks=3) -> int:
+    n = _SZ(0)
+    dims = _dims(batch, heads, seq_len, head_dim, DTYPES.get(dtype, -1))
+    _check(lib().mra_bigbird_backward_workspace_size(ctypes.byref(dims), block_size, num_random_blocks,
+                                                     ctypes.byref(n)), "mra_bigbird_backward_workspace_size")
+    return n.value
+
+
+def bigbird_backward(q, k, v, out, dout, workspace, num_random_blocks, mask=None, block_size=64, dq=None,
+                     dk=None, dv=None, bwd_workspace=None):
+    """Gradients (dq, dk, dv) of a bigbird_attention call's output given
+    dout; `out` and `workspace` are that call's (its layout is read from the
+    workspace).  bf16."""
+    _check_inputs(q, k, v, mask)
+    for t in (out, dout):
+        if not (t.is_cuda and t.dtype == q.dtype and t.shape == q.shape and t.is_contiguous()):
+            raise ValueError("out and dout must be contiguous device tensors shaped and typed like q")
+    B, H, N, d = q.shape
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    bw_bytes = bigbird_backward_workspace_size(B, H, N, d, q.dtype, block_size, num_random_blocks)
+    if bwd_workspace is None or bwd_workspace.numel() < bw_bytes:
+        bwd_workspace = torch.empty(bw_bytes, dtype=torch.uint8, device=q.device)
+    dims = _dims(B, H, N, d, DTYPES[q.dtype])
+    st = lib().mra_bigbird_bwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), block_size,
+                               num_random_blocks, _ptr(out), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                               _ptr(workspace), workspace.numel(), _ptr(bwd_workspace), bwd_workspace.numel(),
+                               _stream(q))
+    _check(st, "mra_bigbird_bwd")
+    return dq, dk, dv

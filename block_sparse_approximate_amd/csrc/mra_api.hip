@@ -336,11 +336,12 @@ MRA_API mra_status mra_backward_workspace_size(const mra_dims* dims, int32_t blo
     return MRA_OK;
 }
 
-MRA_API mra_status mra_attention_bwd(const mra_dims* dims, const void* q, const void* k, const void* v,
-                                     const uint8_t* mask, int32_t block_per_row, int32_t approx_mode,
-                                     int32_t prior_first, int32_t prior_diag, const void* out, const void* dout,
-                                     void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
-                                     void* bwd_workspace, size_t bwd_workspace_bytes, void* stream) {
+// The backward pass on a forward call's workspace; dyn: the forward was a
+// static layout (mra_bigbird_fwd) whose stream length is its row_ptr[nb].
+static mra_status run_bwd(const mra_dims* dims, const void* q, const void* k, const void* v, const uint8_t* mask,
+                          int32_t block_per_row, int32_t approx_mode, int32_t prior_first, int32_t prior_diag,
+                          bool dyn, const void* out, const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                          size_t workspace_bytes, void* bwd_workspace, size_t bwd_workspace_bytes, void* stream) {
     Layout L;
     mra_status st = check_call(dims, q, k, v, mask, block_per_row, approx_mode, prior_first, prior_diag, out,
                                workspace, workspace_bytes, true, &L);
@@ -383,6 +384,7 @@ MRA_API mra_status mra_attention_bwd(const mra_dims* dims, const void* q, const 
     p.bwd_part_dq = reinterpret_cast<float*>(bw + W.part_dq);
     p.bwd_part_dk = reinterpret_cast<float*>(bw + W.part_dk);
     p.bwd_part_dv = reinterpret_cast<float*>(bw + W.part_dv);
+    p.attn_dyn = dyn ? 1 : 0;
     auto fl = [&](size_t off) { return off ? reinterpret_cast<float*>(bw + off) : nullptr; };
     p.bwd_g = fl(W.g);
     p.bwd_c = fl(W.c);
@@ -392,6 +394,15 @@ MRA_API mra_status mra_attention_bwd(const mra_dims* dims, const void* q, const 
     p.bwd_dkh = fl(W.dkh);
     p.bwd_dvh = fl(W.dvh);
     return launch_bwd(p, static_cast<hipStream_t>(stream)) == hipSuccess ? MRA_OK : MRA_ERR_HIP;
+}
+
+MRA_API mra_status mra_attention_bwd(const mra_dims* dims, const void* q, const void* k, const void* v,
+                                     const uint8_t* mask, int32_t block_per_row, int32_t approx_mode,
+                                     int32_t prior_first, int32_t prior_diag, const void* out, const void* dout,
+                                     void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                                     void* bwd_workspace, size_t bwd_workspace_bytes, void* stream) {
+    return run_bwd(dims, q, k, v, mask, block_per_row, approx_mode, prior_first, prior_diag, false, out, dout, dq,
+                   dk, dv, workspace, workspace_bytes, bwd_workspace, bwd_workspace_bytes, stream);
 }
 
 // ---------------------------------------------------------------- BigBird
@@ -458,6 +469,33 @@ MRA_API mra_status mra_bigbird_fwd(const mra_dims* dims, const void* q, const vo
     if (launch_attn(p, s) != hipSuccess) return MRA_ERR_HIP;
     if (launch_finish(p, s) != hipSuccess) return MRA_ERR_HIP;
     return MRA_OK;
+}
+
+MRA_API mra_status mra_bigbird_backward_workspace_size(const mra_dims* dims, int32_t block_size,
+                                                       int32_t num_random_blocks, size_t* bytes) {
+    if (!bytes || !dims) return MRA_ERR_NULL;
+    int32_t bpr = 0;
+    const mra_status st = check_bigbird(dims, block_size, num_random_blocks, &bpr);
+    if (st != MRA_OK) return st;
+    Layout L;
+    if (!carve(*dims, bpr, MRA_APPROX_SPARSE, &L)) return MRA_ERR_SEQ_LEN;
+    BwdLayout W;
+    carve_bwd(L, MRA_APPROX_SPARSE, &W);
+    *bytes = W.total;
+    return MRA_OK;
+}
+
+MRA_API mra_status mra_bigbird_bwd(const mra_dims* dims, const void* q, const void* k, const void* v,
+                                   const uint8_t* mask, int32_t block_size, int32_t num_random_blocks,
+                                   const void* out, const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                                   size_t workspace_bytes, void* bwd_workspace, size_t bwd_workspace_bytes,
+                                   void* stream) {
+    if (!dims) return MRA_ERR_NULL;
+    int32_t bpr = 0;
+    const mra_status st = check_bigbird(dims, block_size, num_random_blocks, &bpr);
+    if (st != MRA_OK) return st;
+    return run_bwd(dims, q, k, v, mask, bpr, MRA_APPROX_SPARSE, 0, 0, true, out, dout, dq, dk, dv, workspace,
+                   workspace_bytes, bwd_workspace, bwd_workspace_bytes, stream);
 }
 
 MRA_API mra_status mra_debug_replay(const mra_dims* dims, const void* q, const void* k, const void* v,

@@ -307,7 +307,9 @@ __global__ __launch_bounds__(kTrThreads) void plan_kernel(Params p) {
     if (x == 0) {
         cptr[nb] = tot_c;
         p.bwd_count[bh] = make_int4(min(tot_r, maxch), min(tot_cc, maxch), tot_rm, tot_cm);
-        if (tot_c != K || tot_r > maxch || tot_cc > maxch) atomicOr(reinterpret_cast<unsigned int*>(p.error), 8u);
+        // a static layout fills row_ptr[nb] of the stream's capacity K
+        const int want = p.attn_dyn ? min(rp[nb], K) : K;
+        if (tot_c != want || tot_r > maxch || tot_cc > maxch) atomicOr(reinterpret_cast<unsigned int*>(p.error), 8u);
     }
 }
 

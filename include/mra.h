@@ -201,6 +201,22 @@ mra_status mra_bigbird_fwd(const mra_dims* dims, const void* q, const void* k, c
                            const int32_t* rand_blocks, void* out, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/* Gradients of a mra_bigbird_fwd call's output with respect to q, k and v:
+ * the chunked backward of mra_attention_bwd (sparse mode) on the layout that
+ * call made (the pattern is a constant of the backward pass).
+ *   q, k, v, mask, block_size, num_random_blocks: as for that call (its
+ *   rand_blocks are not read again: the layout is in its workspace);
+ *   out, dout, dq, dk, dv, workspace, bwd_workspace: as for
+ *   mra_attention_bwd, with bwd_workspace of
+ *   mra_bigbird_backward_workspace_size bytes.  bf16 only. */
+mra_status mra_bigbird_backward_workspace_size(const mra_dims* dims, int32_t block_size,
+                                               int32_t num_random_blocks, size_t* bytes);
+mra_status mra_bigbird_bwd(const mra_dims* dims, const void* q, const void* k, const void* v,
+                           const uint8_t* mask, int32_t block_size, int32_t num_random_blocks,
+                           const void* out, const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                           size_t workspace_bytes, void* bwd_workspace, size_t bwd_workspace_bytes,
+                           void* stream);
+
 /* Bytes of the backward pass's own workspace for these dimensions and
  * selection parameters (mra_attention_bwd's bwd_workspace): the dO . O row
  * terms, the transposed selection, the work chunks, fp32 partial gradients

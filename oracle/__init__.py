@@ -73,6 +73,8 @@ def lib():
         L.oracle_mra_bwd.restype = ctypes.c_int
         L.oracle_bigbird_fwd.argtypes = [i32, i32, i32, i32, P, P, P, P, i32, i32, P, P, i32]
         L.oracle_bigbird_fwd.restype = ctypes.c_int
+        L.oracle_bigbird_bwd.argtypes = [i32, i32, i32, i32, P, P, P, P, i32, i32, P, P, P, P, P, i32]
+        L.oracle_bigbird_bwd.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -237,3 +239,19 @@ def bigbird_forward(q, k, v, rand, mask=None, block_size=64, threads=None):
     if rc:
         raise ValueError("oracle_bigbird_fwd failed: %d" % rc)
     return out
+
+
+def bigbird_backward(q, k, v, rand, dout, mask=None, block_size=64, threads=None):
+    """Gradients of bigbird_forward's output with respect to q, k, v given
+    dout = dL/d out (the pattern is a constant).  Returns (dq, dk, dv) fp64."""
+    q, k, v, g = _f32(q), _f32(k), _f32(v), _f32(dout)
+    B, H, N, d = q.shape
+    rand = np.ascontiguousarray(rand, dtype=np.int32)
+    if rand.ndim != 4 or rand.shape[:3] != (B, H, N // block_size):
+        raise ValueError("rand must be [B, H, N / block_size, r]")
+    dq, dk, dv = (np.zeros((B, H, N, d), np.float64) for _ in range(3))
+    rc = lib().oracle_bigbird_bwd(B, H, N, d, _p(q), _p(k), _p(v), _p(_mask(mask)), block_size, rand.shape[3],
+                                  _p(rand), _p(g), _p(dq), _p(dk), _p(dv), threads or default_threads())
+    if rc:
+        raise ValueError("oracle_bigbird_bwd failed: %d" % rc)
+    return dq, dk, dv

@@ -638,6 +638,23 @@ done:
  * Each valid query token then takes exact softmax attention, scale
  * 1/sqrt(d), over the valid keys of its attended blocks (B4); padded query
  * rows and rows with no valid key output 0.  rand: [nbb, r]. */
+/* The attended-block matrix att [nbb, nbb] of the pattern described below. */
+static void bigbird_pattern(int32_t nbb, int32_t r, const int32_t* rand, uint8_t* att)
+{
+    for (int32_t I = 0; I < nbb; I++)
+        for (int32_t J = 0; J < nbb; J++) {
+            const int global = I == 0 || I == nbb - 1 || J == 0 || J == nbb - 1;
+            const int window = I - J <= 1 && J - I <= 1;
+            att[(int64_t)I * nbb + J] = (uint8_t)(global || window);
+        }
+    for (int32_t I = 0; I < nbb; I++)
+        for (int32_t x = 0; x < r; x++) {
+            const int32_t J = rand[(int64_t)I * r + x];
+            if (J >= 0 && J < nbb)
+                att[(int64_t)I * nbb + J] = 1;
+        }
+}
+
 static int oracle_bigbird_head(int32_t N, int32_t d, int32_t bs, int32_t r, const int32_t* rand,
                                const float* q, const float* k, const float* v, const uint8_t* mask,
                                double* out)
@@ -651,18 +668,7 @@ static int oracle_bigbird_head(int32_t N, int32_t d, int32_t bs, int32_t r, cons
         free(s);
         return -2;
     }
-    for (int32_t I = 0; I < nbb; I++)
-        for (int32_t J = 0; J < nbb; J++) {
-            const int global = I == 0 || I == nbb - 1 || J == 0 || J == nbb - 1;
-            const int window = I - J <= 1 && J - I <= 1;
-            att[(int64_t)I * nbb + J] = (uint8_t)(global || window);
-        }
-    for (int32_t I = 0; I < nbb; I++)
-        for (int32_t x = 0; x < r; x++) {
-            const int32_t J = rand[(int64_t)I * r + x];
-            if (J >= 0 && J < nbb)
-                att[(int64_t)I * nbb + J] = 1;
-        }
+    bigbird_pattern(nbb, r, rand, att);
     for (int32_t t = 0; t < N; t++) {
         double* o = out + (int64_t)t * d;
         for (int32_t c = 0; c < d; c++)
@@ -697,6 +703,81 @@ static int oracle_bigbird_head(int32_t N, int32_t d, int32_t bs, int32_t r, cons
     }
     free(att);
     free(s);
+    return 0;
+}
+
+/* Gradients of oracle_bigbird_head's output with respect to q, k and v,
+ * given dO = dL/d out.  The pattern depends on block positions and the given
+ * picks only, so it is a constant; for a valid query token t and the valid
+ * keys u of its attended blocks, with P_u = e^{s_u} / Z and D_t = dO_t . out_t:
+ *   dS_u = P_u (dO_t . v_u - D_t),  dq_t += tau dS_u k_u,
+ *   dk_u += tau dS_u q_t,           dv_u += P_u dO_t.
+ * dout: [N, d] fp32; dq, dk, dv: [N, d] fp64, overwritten. */
+static int oracle_bigbird_head_bwd(int32_t N, int32_t d, int32_t bs, int32_t r, const int32_t* rand,
+                                   const float* q, const float* k, const float* v, const uint8_t* mask,
+                                   const float* dout, double* dq, double* dk, double* dv)
+{
+    const int32_t nbb = N / bs;
+    const double tau = 1.0 / sqrt((double)d);
+    uint8_t* att = (uint8_t*)calloc((size_t)nbb * nbb, 1);
+    double* s = (double*)malloc(sizeof(double) * (size_t)N);
+    double* o = (double*)malloc(sizeof(double) * (size_t)d);
+    if (!att || !s || !o) {
+        free(att); free(s); free(o);
+        return -2;
+    }
+    bigbird_pattern(nbb, r, rand, att);
+    memset(dq, 0, sizeof(double) * (size_t)N * d);
+    memset(dk, 0, sizeof(double) * (size_t)N * d);
+    memset(dv, 0, sizeof(double) * (size_t)N * d);
+    for (int32_t t = 0; t < N; t++) {
+        if (mask && !mask[t])
+            continue;
+        const float* g = dout + (int64_t)t * d;
+        double shift = -INFINITY;
+        for (int32_t u = 0; u < N; u++) {
+            s[u] = -INFINITY;
+            if ((mask && !mask[u]) || !att[(int64_t)(t / bs) * nbb + u / bs])
+                continue;
+            double dot = 0.0;
+            for (int32_t c = 0; c < d; c++)
+                dot += (double)q[(int64_t)t * d + c] * (double)k[(int64_t)u * d + c];
+            s[u] = tau * dot;
+            if (s[u] > shift)
+                shift = s[u];
+        }
+        if (shift == -INFINITY)
+            continue;
+        double Z = 0.0;
+        for (int32_t c = 0; c < d; c++)
+            o[c] = 0.0;
+        for (int32_t u = 0; u < N; u++) {
+            if (s[u] == -INFINITY)
+                continue;
+            const double w = exp(s[u] - shift);
+            Z += w;
+            for (int32_t c = 0; c < d; c++)
+                o[c] += w * (double)v[(int64_t)u * d + c];
+        }
+        double D = 0.0;
+        for (int32_t c = 0; c < d; c++)
+            D += (double)g[c] * (o[c] / Z);
+        for (int32_t u = 0; u < N; u++) {
+            if (s[u] == -INFINITY)
+                continue;
+            const double P = exp(s[u] - shift) / Z;
+            double dP = 0.0;
+            for (int32_t c = 0; c < d; c++)
+                dP += (double)g[c] * (double)v[(int64_t)u * d + c];
+            const double ds = P * (dP - D);
+            for (int32_t c = 0; c < d; c++) {
+                dv[(int64_t)u * d + c] += P * (double)g[c];
+                dq[(int64_t)t * d + c] += tau * ds * (double)k[(int64_t)u * d + c];
+                dk[(int64_t)u * d + c] += tau * ds * (double)q[(int64_t)t * d + c];
+            }
+        }
+    }
+    free(att); free(s); free(o);
     return 0;
 }
 
@@ -735,7 +816,12 @@ static void* worker(void* p)
         int64_t off = (int64_t)u * j->N * j->d;
         const uint8_t* m = j->mask ? j->mask + (int64_t)b * j->N : NULL;
         int rc;
-        if (j->bigbird)
+        if (j->bigbird && j->bwd)
+            rc = oracle_bigbird_head_bwd(j->N, j->d, j->bs, j->r,
+                                         j->rand + (int64_t)u * (j->N / j->bs) * j->r, j->q + off,
+                                         j->k + off, j->v + off, m, j->dout + off, j->dq + off,
+                                         j->dk + off, j->dv + off);
+        else if (j->bigbird)
             rc = oracle_bigbird_head(j->N, j->d, j->bs, j->r,
                                      j->rand + (int64_t)u * (j->N / j->bs) * j->r, j->q + off,
                                      j->k + off, j->v + off, m, j->out + off);
@@ -847,5 +933,24 @@ int oracle_bigbird_fwd(int32_t B, int32_t H, int32_t N, int32_t d, const float* 
     j.B = B; j.H = H; j.N = N; j.d = d;
     j.q = q; j.k = k; j.v = v; j.mask = mask;
     j.out = out; j.bigbird = 1; j.bs = bs; j.r = r; j.rand = rand;
+    return run_jobs(&j, nthreads);
+}
+
+/* Gradients of oracle_bigbird_fwd's output (oracle_bigbird_head_bwd) given
+ * dout; all [B, H, N, d], rand [B, H, N / bs, r]. */
+int oracle_bigbird_bwd(int32_t B, int32_t H, int32_t N, int32_t d, const float* q,
+                       const float* k, const float* v, const uint8_t* mask, int32_t bs,
+                       int32_t r, const int32_t* rand, const float* dout, double* dq, double* dk,
+                       double* dv, int32_t nthreads)
+{
+    if (B < 1 || H < 1 || d < 1 || bs < 1 || N < bs || N % bs != 0 || r < 0 ||
+        (r > 0 && !rand) || !q || !k || !v || !dout || !dq || !dk || !dv)
+        return -1;
+    job_t j;
+    memset(&j, 0, sizeof(j));
+    j.B = B; j.H = H; j.N = N; j.d = d;
+    j.q = q; j.k = k; j.v = v; j.mask = mask;
+    j.bigbird = 1; j.bs = bs; j.r = r; j.rand = rand;
+    j.bwd = 1; j.dout = dout; j.dq = dq; j.dk = dk; j.dv = dv;
     return run_jobs(&j, nthreads);
 }

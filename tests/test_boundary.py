@@ -23,7 +23,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     L = mra.lib()
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 16
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(mra.SIGNATURES)
@@ -213,3 +213,27 @@ def test_bigbird_workspace_and_argument_checks():
     assert call(r=0) == 7
     assert call(bs=96) == 3
     assert L.mra_bigbird_fwd(None, Q, K, V, None, 64, 3, RB, O, W, ws, None) == 1
+
+
+def test_bigbird_backward_checks():
+    assert mra.bigbird_backward_workspace_size(2, 12, 4096) > 0
+    with pytest.raises(mra.MraError) as e:
+        mra.bigbird_backward_workspace_size(1, 2, 512, num_random_blocks=0)
+    assert e.value.status == 7
+    L = mra.lib()
+    d = mra._Dims(1, 2, 512, 64, 1)
+    ws = mra.bigbird_workspace_size(1, 2, 512)
+    bw = mra.bigbird_backward_workspace_size(1, 2, 512)
+    DO2, DQ2, DK2, DV2, BW2 = 0x70000000, 0x80000000, 0x90000000, 0xA0000000, 0xB0000000
+    call = lambda **kw: L.mra_bigbird_bwd(ctypes.byref(d), Q, K, V, None, kw.get("bs", 64), kw.get("r", 3), O,
+                                          kw.get("dout", DO2), kw.get("dq", DQ2), DK2, DV2, W, ws,
+                                          kw.get("bw", BW2), kw.get("bw_bytes", bw), None)
+    assert call(dout=None) == 1
+    assert call(bw=None) == 10
+    assert call(bw_bytes=256) == 10
+    assert call(dq=Q) == 9
+    assert call(r=0) == 7
+    assert call(bs=96) == 3
+    d32 = mra._Dims(1, 2, 512, 64, 0)
+    assert L.mra_bigbird_bwd(ctypes.byref(d32), Q, K, V, None, 64, 3, O, DO2, DQ2, DK2, DV2, W, 1 << 30, BW2,
+                             1 << 30, None) == 5

@@ -109,3 +109,37 @@ def test_bigbird_matches_mra_sparse_on_the_same_cells(mra):
     out = mra.attention(dev(w, "q"), dev(w, "k"), dev(w, "v"), None, block_per_row=6, approx_mode="sparse")
     torch.cuda.synchronize()
     assert np.array_equal(out.float().cpu().numpy().astype(np.float64), got)
+
+
+
+TOL_BWD = dict(max_rel_to_scale=2.0 ** -5, mean_rel=2.0 ** -7)
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("bwd-named", dict()),
+    ("bwd-bs32-masked", dict(B=2, H=2, N=1024, block_size=32, r=2, mask=ragged_mask(2, 1024, 6))),
+    ("bwd-bs128", dict(B=1, H=2, N=2048, block_size=128, r=1)),
+])
+def test_bigbird_backward_matches_oracle(mra, name, kw):
+    bb = workloads.bigbird(name, seed=11, **kw) if kw else workloads.bigbird()
+    w = bb.w
+    print("case", bb, flush=True)
+    mask = None if w.mask is None else torch.from_numpy(w.mask).cuda()
+    q, k, v = dev(w, "q"), dev(w, "k"), dev(w, "v")
+    rand = torch.from_numpy(bb.rand).cuda()
+    ws = torch.zeros(mra.bigbird_workspace_size(w.B, w.H, w.N, w.d, torch.bfloat16, bb.block_size,
+                                                bb.rand.shape[3]), dtype=torch.uint8, device="cuda")
+    out = mra.bigbird_attention(q, k, v, rand, mask, bb.block_size, workspace=ws)
+    g16 = torch.from_numpy(np.random.default_rng(12).standard_normal(q.shape).astype(np.float32)).to(torch.bfloat16)
+    dq, dk, dv = mra.bigbird_backward(q, k, v, out, g16.cuda(), ws, bb.rand.shape[3], mask, bb.block_size)
+    torch.cuda.synchronize()
+    assert int(ws[:4].view(torch.int32).item()) == 0, "device error word"
+    ref = oracle.bigbird_backward(w.q, w.k, w.v, bb.rand, g16.float().numpy(), w.mask, bb.block_size)
+    for label, a, b in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        a = a.float().cpu().numpy()
+        err = np.abs(a - b)
+        rel = float(err.max()) / float(np.abs(b).max())
+        mean_rel = float(err.sum() / np.abs(b).sum())
+        print("  %s %s: max|err|/max|ref| %.3e  mean_rel %.3e" % (name, label, rel, mean_rel), flush=True)
+        assert np.isfinite(a).all()
+        assert rel <= TOL_BWD["max_rel_to_scale"] and mean_rel <= TOL_BWD["mean_rel"], (label, rel, mean_rel)

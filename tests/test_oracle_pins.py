@@ -620,3 +620,19 @@ def test_bigbird_generator_draws_outside_window_and_globals():
         assert np.all(picks >= 1) and np.all(picks <= nbb - 2)
         assert np.all(np.abs(picks - I) > 1)
         assert all(len(set(p.tolist())) == 3 for p in picks)
+
+
+def test_bigbird_gradients_equal_block_masked_autograd():
+    B, H, N, bs = 1, 2, 512, 64
+    q, k, v = rand_qkv(B, H, N, seed=67)
+    rand = workloads.bigbird_rand(B, H, N, bs, 2, seed=68)
+    mask = np.ones((B, N), np.uint8)
+    mask[0, 450:] = 0
+    g = rand_dout(q.shape, 69) * mask[:, None, :, None].astype(np.float32)   # padded rows output 0
+    got = oracle.bigbird_backward(q, k, v, rand, g, mask, bs)
+    for h in range(H):
+        allowed = bigbird_allowed(N, bs, rand[0, h]) & mask[0][None, :].astype(bool)
+        allowed[~mask[0].astype(bool)] = True   # padded query rows: any finite row (their dO is 0)
+        ref = sdpa64_grads(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], g[:, h:h + 1], allowed[None, None])
+        for a, b in zip(got, ref):
+            np.testing.assert_allclose(a[:, h:h + 1], b, rtol=0, atol=1e-11)
