@@ -1038,6 +1038,10 @@ __global__ __launch_bounds__(kSelThreads) void bigbird_layout_kernel(Params p) {
     const int bh = blockIdx.x;
     if (bh >= p.BH) return;
     const int b = bh / p.H, tid = threadIdx.x;
+    // the device error word starts clear (pooling clears it on the MRA path);
+    // this kernel cannot set a bit of its own, since the stream is sized for
+    // the pattern's largest count, so the attention kernel's bits stay exact
+    if (bh == 0 && tid == 0) *p.error = 0;
     const SelectLds L = select_lds(nb);
     uint32_t* bitmap = reinterpret_cast<uint32_t*>(smem + L.bitmap);
     int* rc = reinterpret_cast<int*>(smem + L.rc);

@@ -35,6 +35,7 @@ def run(mra, bb):
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     ws = torch.zeros(mra.bigbird_workspace_size(w.B, w.H, w.N, w.d, dt, bb.block_size, bb.rand.shape[3]),
                      dtype=torch.uint8, device="cuda")
+    ws[:4] = 0xFF                  # a stale error word: the call must clear it
     out = mra.bigbird_attention(dev(w, "q"), dev(w, "k"), dev(w, "v"), torch.from_numpy(bb.rand).cuda(), mask,
                                 bb.block_size, workspace=ws)
     torch.cuda.synchronize()
