@@ -248,7 +248,7 @@ def prepare_backward(q, k, v, out, dout, workspace, mask=None, block_per_row=4, 
     output and workspace (the selection and softmax statistics are read from
     it); the other arguments must be the ones it was made with.
     `bwd_workspace` (uint8, backward_workspace_size bytes) is allocated when
-    not given.  Sparse mode, bf16."""
+    not given.  Both modes, bf16 or fp32."""
     _check_inputs(q, k, v, mask)
     for t in (out, dout):
         if not (t.is_cuda and t.dtype == q.dtype and t.shape == q.shape and t.is_contiguous()):
@@ -424,7 +424,7 @@ def bigbird_backward(q, k, v, out, dout, workspace, num_random_blocks, mask=None
                      dk=None, dv=None, bwd_workspace=None):
     """Gradients (dq, dk, dv) of a bigbird_attention call's output given
     dout; `out` and `workspace` are that call's (its layout is read from the
-    workspace).  bf16."""
+    workspace).  bf16 or fp32."""
     _check_inputs(q, k, v, mask)
     for t in (out, dout):
         if not (t.is_cuda and t.dtype == q.dtype and t.shape == q.shape and t.is_contiguous()):

@@ -346,14 +346,14 @@ static mra_status run_bwd(const mra_dims* dims, const void* q, const void* k, co
     mra_status st = check_call(dims, q, k, v, mask, block_per_row, approx_mode, prior_first, prior_diag, out,
                                workspace, workspace_bytes, true, &L);
     if (st != MRA_OK) return st;
-    if (dims->dtype != MRA_BF16) return MRA_ERR_DTYPE;
     if (!dout || !dq || !dk || !dv) return MRA_ERR_NULL;
     if (misaligned(dout) || misaligned(dq) || misaligned(dk) || misaligned(dv)) return MRA_ERR_ALIGN;
     BwdLayout W;
     carve_bwd(L, approx_mode, &W);
     if (!bwd_workspace || bwd_workspace_bytes < W.total) return MRA_ERR_WORKSPACE;
     if (misaligned(bwd_workspace)) return MRA_ERR_ALIGN;
-    const size_t tb = (size_t)dims->batch * dims->heads * dims->seq_len * dims->head_dim * 2;
+    const size_t tb = (size_t)dims->batch * dims->heads * dims->seq_len * dims->head_dim *
+                      (dims->dtype == MRA_BF16 ? 2 : 4);
     const void* ins[] = {q, k, v, out, dout, workspace};
     const size_t insz[] = {tb, tb, tb, tb, tb, workspace_bytes};
     void* outs[] = {dq, dk, dv, bwd_workspace};

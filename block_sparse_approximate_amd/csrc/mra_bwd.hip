@@ -203,6 +203,19 @@ inline unsigned head_grid(int BH, int per_head) {
     return (unsigned)(BH >= 8 ? 8 * (int64_t)((BH + 7) / 8) * per_head : (int64_t)BH * per_head);
 }
 
+// D_t for fp32 rows: lane (n, h) sums channels 32 h .. 32 h + 31 of token n.
+__device__ __forceinline__ float row_dot32(const float* dO, const float* O, int lane) {
+    const int n = lane & 31, h = lane >> 5;
+    float s = 0.f;
+#pragma unroll
+    for (int x = 0; x < 8; x++) {
+        const float4 a = *reinterpret_cast<const float4*>(dO + n * kHeadDim + 32 * h + 4 * x);
+        const float4 o = *reinterpret_cast<const float4*>(O + n * kHeadDim + 32 * h + 4 * x);
+        s += a.x * o.x + a.y * o.y + a.z * o.z + a.w * o.w;
+    }
+    return s + __shfl_xor(s, 32, 64);
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
@@ -339,6 +352,7 @@ constexpr int kLrVStr = kHeadDim + 1;  // vhat tile stride: lane j reads row j w
 //            w_ij (the forward's weight, 0 for selected or empty cells) and
 //            e_ij; then lane = channel adds e_ij khat_j to dqhat_i.  E and W
 //            go out transposed ([j][i], 8 consecutive rows per j).
+template <int DT>
 __global__ __launch_bounds__(kLrThreads) void lr_rows_kernel(Params p) {
     __shared__ float vt[kLrTile][kLrVStr];
     __shared__ __align__(16) float kt[kLrTile][kHeadDim];
@@ -360,9 +374,14 @@ __global__ __launch_bounds__(kLrThreads) void lr_rows_kernel(Params p) {
     float ci = 0.f;
     if (act) {
         const size_t rowoff = ((size_t)bh * p.N + (size_t)i * kBlock) * kHeadDim;
-        const uint16_t* dO = static_cast<const uint16_t*>(p.dout) + rowoff;
         const int n = lane & 31, h = lane >> 5;
-        const float D = row_dot(dO, static_cast<const uint16_t*>(p.fout) + rowoff, lane);
+        float D;
+        if constexpr (DT == 1)
+            D = row_dot(static_cast<const uint16_t*>(p.dout) + rowoff, static_cast<const uint16_t*>(p.fout) + rowoff,
+                        lane);
+        else
+            D = row_dot32(static_cast<const float*>(p.dout) + rowoff, static_cast<const float*>(p.fout) + rowoff,
+                          lane);
         const size_t t = (size_t)bh * p.N + (size_t)i * kBlock + n;
         const float mu = p.st_m[t], linv = p.st_linv[t];
         const float a = linv > 0.f ? __builtin_amdgcn_exp2f(mi * kLog2e - mu) * linv : 0.f;
@@ -370,8 +389,15 @@ __global__ __launch_bounds__(kLrThreads) void lr_rows_kernel(Params p) {
         ci = wave_sum(h == 0 ? a * D : 0.f);
         wave_sync_lds();
         float g = 0.f;
+        if constexpr (DT == 1) {
+            const uint16_t* dO = static_cast<const uint16_t*>(p.dout) + rowoff;
 #pragma unroll 8
-        for (int u = 0; u < kBlock; u++) g += al[wave][u] * bf16_to_float(dO[u * kHeadDim + lane]);
+            for (int u = 0; u < kBlock; u++) g += al[wave][u] * bf16_to_float(dO[u * kHeadDim + lane]);
+        } else {
+            const float* dO = static_cast<const float*>(p.dout) + rowoff;
+#pragma unroll 8
+            for (int u = 0; u < kBlock; u++) g += al[wave][u] * dO[u * kHeadDim + lane];
+        }
         gs[wave][lane] = g;
         p.bwd_g[hrow * kHeadDim + lane] = g;
         if (lane == 0) p.bwd_c[hrow] = ci;
@@ -655,13 +681,216 @@ __global__ __launch_bounds__(kThreads) void dkv_kernel(Params p) {
     }
 }
 
+// ---------------------------------------------------------------- fp32 chunks
+// The same products on fp32 operands with v_mfma_f32_32x32x2f32 (32 token
+// rows of 64 channels per staged block, row stride kStr32 so that lanes
+// reading a column of different rows fall on different banks).  For a
+// product over the channels lane l takes row l % 32, channel 2 s + l / 32 at
+// step s, for A and B alike.  For a product over the block's tokens, the
+// accumulator of the previous product is the B operand: at step s lane l
+// gives its register s, the token acc_row(s, l), and the A operand is read
+// transposed from the staged block at that same token.
+constexpr int kStr32 = kHeadDim + 1;
+constexpr int kTile32 = kBlock * kStr32;
+
+__device__ __forceinline__ void load_blk32(float4 (&r)[8], const float* g, int lane) {
+#pragma unroll
+    for (int x = 0; x < 8; x++) r[x] = *reinterpret_cast<const float4*>(g + ((lane >> 4) + 4 * x) * kHeadDim + (lane & 15) * 4);
+}
+__device__ __forceinline__ void store_blk32(float* s, const float4 (&r)[8], int lane) {
+#pragma unroll
+    for (int x = 0; x < 8; x++) {
+        float* d = s + ((lane >> 4) + 4 * x) * kStr32 + (lane & 15) * 4;
+        d[0] = r[x].x; d[1] = r[x].y; d[2] = r[x].z; d[3] = r[x].w;
+    }
+}
+// C += A B^T over the 64 channels: A, B staged blocks (rows = the result's rows / columns)
+__device__ __forceinline__ f32x16 mm32(f32x16 c, const float* a, const float* b, int lane) {
+    const int n = lane & 31, h = lane >> 5;
+#pragma unroll 8
+    for (int st = 0; st < kHeadDim / 2; st++)
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[n * kStr32 + 2 * st + h], b[n * kStr32 + 2 * st + h], c, 0, 0, 0);
+    return c;
+}
+// C[channel][col] += sum_t X[t][32 mt + channel] acc[t][col] over the block's 32 tokens
+__device__ __forceinline__ f32x16 mm32_t(f32x16 c, const float* x, const f32x16& acc, int mt, int lane) {
+    const int m = lane & 31;
+#pragma unroll
+    for (int st = 0; st < 16; st++)
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(x[acc_row(st, lane) * kStr32 + 32 * mt + m], acc[st], c, 0, 0, 0);
+    return c;
+}
+// result tile pair (lane = token, registers = channels) times scale, plus add, to fp32 rows
+__device__ __forceinline__ void store_rows32(float* g, const f32x16& a0, const f32x16& a1, float scale, int lane,
+                                             const float* add, float aw) {
+    const int n = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+        for (int gq = 0; gq < 4; gq++) {
+            const f32x16& a = mt == 0 ? a0 : a1;
+            const int d0 = 32 * mt + 8 * gq + 4 * h;
+            float4 x = make_float4(a[4 * gq] * scale, a[4 * gq + 1] * scale, a[4 * gq + 2] * scale,
+                                   a[4 * gq + 3] * scale);
+            if (add) {
+                const float4 ad = *reinterpret_cast<const float4*>(add + d0);
+                x.x += ad.x * aw; x.y += ad.y * aw; x.z += ad.z * aw; x.w += ad.w * aw;
+            }
+            *reinterpret_cast<float4*>(g + n * kHeadDim + d0) = x;
+        }
+}
+
+__global__ __launch_bounds__(64) void dq32_kernel(Params p) {
+    __shared__ float lds[4][kTile32];   // Q_i, dO_i, K_j, V_j
+    const int lane = threadIdx.x & 63;
+    const int nb = p.nb, maxch = p.bwd_maxch;
+    int bh, cid;
+    if (!head_slot(p.BH, maxch, &bh, &cid)) return;
+    if (cid >= p.bwd_count[bh].x) return;
+    const int4 dsc = p.bwd_rch[(size_t)bh * maxch + cid];
+    const int i = min(max(dsc.x, 0), nb - 1), b = bh / p.H;
+    const int e0 = max(dsc.y, 0), e1 = min(dsc.z, (int)p.K);
+    const int n = lane & 31, h = lane >> 5;
+    float* qs = lds[0];
+    float* dos = lds[1];
+    float* ks = lds[2];
+    float* vs = lds[3];
+    const size_t head = (size_t)bh * p.N * kHeadDim, rowoff = head + (size_t)i * kBlock * kHeadDim;
+    const float* Kh = static_cast<const float*>(p.k) + head;
+    const float* Vh = static_cast<const float*>(p.v) + head;
+    const float* dO = static_cast<const float*>(p.dout) + rowoff;
+    const float tau = 1.0f / __builtin_sqrtf((float)p.d);
+    const float scale2 = tau * kLog2e;
+    const int32_t* cols = p.col + (size_t)bh * p.K;
+    float4 r[8];
+    load_blk32(r, static_cast<const float*>(p.q) + rowoff, lane);
+    store_blk32(qs, r, lane);
+    load_blk32(r, dO, lane);
+    store_blk32(dos, r, lane);
+    const float dfull = row_dot32(dO, static_cast<const float*>(p.fout) + rowoff, lane);
+    const size_t t = (size_t)bh * p.N + (size_t)i * kBlock + n;
+    const float mu = p.st_m[t], linv = p.st_linv[t];
+    const bool qv = linv > 0.f;
+    const float Dv = qv ? dfull : 0.f;
+    if (h == 0) p.st_d[t] = Dv;
+    f32x16 dq0 = zero16(), dq1 = zero16();
+    for (int e = e0; e < e1; e++) {
+        const int j = min(max(cols[e], 0), nb - 1);
+        const uint32_t km = p.mbits[(size_t)b * nb + j];
+        load_blk32(r, Kh + (size_t)j * kBlock * kHeadDim, lane);
+        store_blk32(ks, r, lane);
+        load_blk32(r, Vh + (size_t)j * kBlock * kHeadDim, lane);
+        store_blk32(vs, r, lane);
+        wave_sync_lds();
+        const f32x16 S = mm32(zero16(), ks, qs, lane);     // S^T: lane = query, registers = keys
+        const f32x16 dP = mm32(zero16(), vs, dos, lane);   // dP^T
+        f32x16 dS;
+#pragma unroll
+        for (int rr = 0; rr < 16; rr++) {
+            const float pv = (qv && ((km >> acc_row(rr, lane)) & 1u)) ? __builtin_amdgcn_exp2f(S[rr] * scale2 - mu) * linv : 0.f;
+            dS[rr] = pv * (dP[rr] - Dv);
+        }
+        dq0 = mm32_t(dq0, ks, dS, 0, lane);                 // dQ^T += K^T dS^T
+        dq1 = mm32_t(dq1, ks, dS, 1, lane);
+        wave_sync_lds();
+    }
+    if (dsc.w < 0) {
+        const float* add = nullptr;
+        float aw = 0.f;
+        if (p.mode == 0) {
+            add = p.bwd_dqh + ((size_t)bh * nb + i) * kHeadDim;
+            aw = ((p.mbits[(size_t)b * nb + i] >> n) & 1u) ? 1.0f / (float)p.cnt[(size_t)b * nb + i] : 0.f;
+        }
+        store_rows32(static_cast<float*>(p.dq) + rowoff, dq0, dq1, tau, lane, add, aw);
+    } else store_part(p.bwd_part_dq + ((size_t)bh * maxch + min(dsc.w, maxch - 1)) * kBlock * kHeadDim, dq0, dq1, lane);
+}
+
+__global__ __launch_bounds__(64) void dkv32_kernel(Params p) {
+    __shared__ float lds[4][kTile32];   // K_j, V_j, Q_i, dO_i
+    __shared__ float st[3][kBlock];     // m, 1/l, D of block i's tokens
+    const int lane = threadIdx.x & 63;
+    const int nb = p.nb, maxch = p.bwd_maxch;
+    int bh, cid;
+    if (!head_slot(p.BH, maxch, &bh, &cid)) return;
+    if (cid >= p.bwd_count[bh].y) return;
+    const int4 dsc = p.bwd_cch[(size_t)bh * maxch + cid];
+    const int j = min(max(dsc.x, 0), nb - 1), b = bh / p.H;
+    const int c0 = max(dsc.y, 0), c1 = min(dsc.z, (int)p.K);
+    const int n = lane & 31;
+    float* ks = lds[0];
+    float* vs = lds[1];
+    float* qs = lds[2];
+    float* dos = lds[3];
+    const size_t head = (size_t)bh * p.N * kHeadDim, coloff = head + (size_t)j * kBlock * kHeadDim;
+    const float* Q = static_cast<const float*>(p.q) + head;
+    const float* dO = static_cast<const float*>(p.dout) + head;
+    const float tau = 1.0f / __builtin_sqrtf((float)p.d);
+    const float scale2 = tau * kLog2e;
+    const int32_t* rows = p.ct_row + (size_t)bh * p.K;
+    const size_t sbase = (size_t)bh * p.N;
+    float4 r[8];
+    load_blk32(r, static_cast<const float*>(p.k) + coloff, lane);
+    store_blk32(ks, r, lane);
+    load_blk32(r, static_cast<const float*>(p.v) + coloff, lane);
+    store_blk32(vs, r, lane);
+    const bool kvalid = (p.mbits[(size_t)b * nb + j] >> n) & 1u;   // lane = key n
+    f32x16 dk0 = zero16(), dk1 = zero16(), dv0 = zero16(), dv1 = zero16();
+    for (int c = c0; c < c1; c++) {
+        const int i = min(max(rows[c], 0), nb - 1);
+        load_blk32(r, Q + (size_t)i * kBlock * kHeadDim, lane);
+        store_blk32(qs, r, lane);
+        load_blk32(r, dO + (size_t)i * kBlock * kHeadDim, lane);
+        store_blk32(dos, r, lane);
+        if (lane < kBlock) {
+            const size_t t = sbase + (size_t)i * kBlock + lane;
+            st[0][lane] = p.st_m[t];
+            st[1][lane] = p.st_linv[t];
+            st[2][lane] = p.st_d[t];
+        }
+        wave_sync_lds();
+        const f32x16 S = mm32(zero16(), qs, ks, lane);     // S: lane = key, registers = queries
+        const f32x16 dP = mm32(zero16(), dos, vs, lane);
+        f32x16 P, dS;
+#pragma unroll
+        for (int rr = 0; rr < 16; rr++) {
+            const int q = acc_row(rr, lane);
+            const float li = st[1][q];
+            const float pv = (kvalid && li > 0.f) ? __builtin_amdgcn_exp2f(S[rr] * scale2 - st[0][q]) * li : 0.f;
+            P[rr] = pv;
+            dS[rr] = pv * (dP[rr] - st[2][q]);
+        }
+        dv0 = mm32_t(dv0, dos, P, 0, lane);                 // dV^T += dO^T P
+        dv1 = mm32_t(dv1, dos, P, 1, lane);
+        dk0 = mm32_t(dk0, qs, dS, 0, lane);                 // dK^T += Q^T dS
+        dk1 = mm32_t(dk1, qs, dS, 1, lane);
+        wave_sync_lds();
+    }
+    if (dsc.w < 0) {
+        const float* addk = nullptr;
+        const float* addv = nullptr;
+        float aw = 0.f;
+        if (p.mode == 0) {
+            addk = p.bwd_dkh + ((size_t)bh * nb + j) * kHeadDim;
+            addv = p.bwd_dvh + ((size_t)bh * nb + j) * kHeadDim;
+            aw = kvalid ? 1.0f / (float)p.cnt[(size_t)b * nb + j] : 0.f;
+        }
+        store_rows32(static_cast<float*>(p.dk) + coloff, dk0, dk1, tau, lane, addk, aw);
+        store_rows32(static_cast<float*>(p.dv) + coloff, dv0, dv1, 1.0f, lane, addv, aw);
+    } else {
+        const size_t slot = ((size_t)bh * maxch + min(dsc.w, maxch - 1)) * kBlock * kHeadDim;
+        store_part(p.bwd_part_dk + slot, dk0, dk1, lane);
+        store_part(p.bwd_part_dv + slot, dv0, dv1, lane);
+    }
+}
+
 // ---------------------------------------------------------------- reduce
 // Workgroup (bh, x, side): the x-th row (side 0) or column (side 1) of head
 // bh that has several chunks.  Thread t sums token t / 8, channels
 // 8 (t % 8) .. +7 over the chunks in order and writes bf16.
 constexpr int kRedThreads = 256;
 
-__device__ __forceinline__ void reduce_one(const float* part, int first, int nch, float scale, uint16_t* dst,
+template <int DT>
+__device__ __forceinline__ void reduce_one(const float* part, int first, int nch, float scale, void* dst_v,
                                            size_t slot0, int tid, const float* add, float aw) {
     const int tok = tid >> 3, cg = (tid & 7) * 8;
     float acc[8];
@@ -693,15 +922,23 @@ __device__ __forceinline__ void reduce_one(const float* part, int first, int nch
 #pragma unroll
         for (int e = 0; e < 8; e++) acc[e] += add[cg + e] * aw;
     }
-    uint4 pk;
-    pk.x = (uint32_t)float_to_bf16(acc[0]) | ((uint32_t)float_to_bf16(acc[1]) << 16);
-    pk.y = (uint32_t)float_to_bf16(acc[2]) | ((uint32_t)float_to_bf16(acc[3]) << 16);
-    pk.z = (uint32_t)float_to_bf16(acc[4]) | ((uint32_t)float_to_bf16(acc[5]) << 16);
-    pk.w = (uint32_t)float_to_bf16(acc[6]) | ((uint32_t)float_to_bf16(acc[7]) << 16);
-    *reinterpret_cast<uint4*>(dst + tok * kHeadDim + cg) = pk;
+    if constexpr (DT == 1) {
+        uint4 pk;
+        pk.x = (uint32_t)float_to_bf16(acc[0]) | ((uint32_t)float_to_bf16(acc[1]) << 16);
+        pk.y = (uint32_t)float_to_bf16(acc[2]) | ((uint32_t)float_to_bf16(acc[3]) << 16);
+        pk.z = (uint32_t)float_to_bf16(acc[4]) | ((uint32_t)float_to_bf16(acc[5]) << 16);
+        pk.w = (uint32_t)float_to_bf16(acc[6]) | ((uint32_t)float_to_bf16(acc[7]) << 16);
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(dst_v) + tok * kHeadDim + cg) = pk;
+    } else {
+        float* dst = static_cast<float*>(dst_v) + tok * kHeadDim + cg;
+        *reinterpret_cast<float4*>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
 }
 
+template <int DT>
 __device__ void reduce_item(const Params& p, int bh, int x, int side) {
+    const size_t es = DT == 1 ? 2 : 4;
     const int nb = p.nb, maxch = p.bwd_maxch;
     const int4 m = (side == 0 ? p.bwd_rmul : p.bwd_cmul)[(size_t)bh * nb + x];
     const int blk = min(max(m.x, 0), nb - 1);
@@ -715,16 +952,17 @@ __device__ void reduce_item(const Params& p, int bh, int x, int side) {
                                                                               : 0.f;
     const size_t hb = ((size_t)bh * nb + blk) * kHeadDim;
     if (side == 0) {
-        reduce_one(p.bwd_part_dq, first, nch, tau, static_cast<uint16_t*>(p.dq) + off, slot0, threadIdx.x,
-                   full ? p.bwd_dqh + hb : nullptr, aw);
+        reduce_one<DT>(p.bwd_part_dq, first, nch, tau, static_cast<char*>(p.dq) + off * es, slot0, threadIdx.x,
+                       full ? p.bwd_dqh + hb : nullptr, aw);
     } else {
-        reduce_one(p.bwd_part_dk, first, nch, tau, static_cast<uint16_t*>(p.dk) + off, slot0, threadIdx.x,
-                   full ? p.bwd_dkh + hb : nullptr, aw);
-        reduce_one(p.bwd_part_dv, first, nch, 1.0f, static_cast<uint16_t*>(p.dv) + off, slot0, threadIdx.x,
-                   full ? p.bwd_dvh + hb : nullptr, aw);
+        reduce_one<DT>(p.bwd_part_dk, first, nch, tau, static_cast<char*>(p.dk) + off * es, slot0, threadIdx.x,
+                       full ? p.bwd_dkh + hb : nullptr, aw);
+        reduce_one<DT>(p.bwd_part_dv, first, nch, 1.0f, static_cast<char*>(p.dv) + off * es, slot0, threadIdx.x,
+                       full ? p.bwd_dvh + hb : nullptr, aw);
     }
 }
 
+template <int DT>
 __global__ __launch_bounds__(kRedThreads) void reduce_kernel(Params p) {
     const int nb = p.nb;
     // items (x, bh, side), x slowest: the few rows and columns of several
@@ -736,7 +974,7 @@ __global__ __launch_bounds__(kRedThreads) void reduce_kernel(Params p) {
         const int x = (int)(w / p.BH), bh = (int)(w - (int64_t)x * p.BH);
         const int4 cnt = p.bwd_count[bh];
         if (x >= (side == 0 ? cnt.z : cnt.w)) continue;
-        reduce_item(p, bh, x, side);
+        reduce_item<DT>(p, bh, x, side);
     }
 }
 
@@ -745,32 +983,44 @@ __global__ __launch_bounds__(kRedThreads) void reduce_kernel(Params p) {
 int bwd_max_chunks(int nb, int64_t K) { return nb + (int)((K + kChunkB - 1) / kChunkB); }
 
 hipError_t launch_bwd(const Params& p, hipStream_t s) {
-    if (p.dtype != 1 || p.d != kHeadDim || p.nb > kTrThreads) return hipErrorInvalidValue;
+    if ((p.dtype != 0 && p.dtype != 1) || p.d != kHeadDim || p.nb > kTrThreads) return hipErrorInvalidValue;
     if (p.mode == 0 && (!p.bwd_g || !p.bwd_c || !p.bwd_et || !p.bwd_wt || !p.bwd_dqh || !p.bwd_dkh || !p.bwd_dvh ||
                         !p.vhat))
         return hipErrorInvalidValue;
+    const bool bf = p.dtype == 1;
     const size_t plan_lds = (size_t)p.nb * (p.words + 1) * 4;
     hipLaunchKernelGGL(plan_kernel, dim3(p.BH), dim3(kTrThreads), plan_lds, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (p.mode == 0) {
         const unsigned lr_grid = head_grid(p.BH, (p.nb + kLrWaves - 1) / kLrWaves);
-        hipLaunchKernelGGL(lr_rows_kernel, dim3(lr_grid), dim3(kLrThreads), 0, s, p);
+        if (bf) hipLaunchKernelGGL(lr_rows_kernel<1>, dim3(lr_grid), dim3(kLrThreads), 0, s, p);
+        else hipLaunchKernelGGL(lr_rows_kernel<0>, dim3(lr_grid), dim3(kLrThreads), 0, s, p);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(lr_cols_kernel, dim3(lr_grid), dim3(kLrThreads), 0, s, p);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const unsigned grid = head_grid(p.BH, (p.bwd_maxch + kWaves - 1) / kWaves);
-    hipLaunchKernelGGL(dq_kernel, dim3(grid), dim3(kThreads), 0, s, p);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(dkv_kernel, dim3(grid), dim3(kThreads), 0, s, p);
+    if (bf) {
+        const unsigned grid = head_grid(p.BH, (p.bwd_maxch + kWaves - 1) / kWaves);
+        hipLaunchKernelGGL(dq_kernel, dim3(grid), dim3(kThreads), 0, s, p);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(dkv_kernel, dim3(grid), dim3(kThreads), 0, s, p);
+    } else {
+        const unsigned grid = head_grid(p.BH, p.bwd_maxch);   // one wave per workgroup
+        hipLaunchKernelGGL(dq32_kernel, dim3(grid), dim3(64), 0, s, p);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(dkv32_kernel, dim3(grid), dim3(64), 0, s, p);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t red_items = 2 * (int64_t)p.BH * p.nb;
-    hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)(red_items < 1024 ? red_items : 1024)), dim3(kRedThreads), 0, s, p);
+    const dim3 rg((unsigned)(red_items < 1024 ? red_items : 1024));
+    if (bf) hipLaunchKernelGGL(reduce_kernel<1>, rg, dim3(kRedThreads), 0, s, p);
+    else hipLaunchKernelGGL(reduce_kernel<0>, rg, dim3(kRedThreads), 0, s, p);
     return hipGetLastError();
 }
 

@@ -25,7 +25,7 @@ from . import attention, backward_workspace_size, prepare_backward, workspace_si
 
 class MraAttentionFunction(torch.autograd.Function):
     """out = MRA-2(q, k, v) on [batch, heads, seq_len, 64] tensors; its
-    backward is mra_attention_bwd (bf16), which takes the forward's selection
+    backward is mra_attention_bwd (bf16 or fp32), which takes the forward's selection
     as fixed ([MRA] 第三步) and in full mode differentiates the low-res branch
     through the block means ([MRA] 第四步)."""
 

@@ -208,7 +208,7 @@ mra_status mra_bigbird_fwd(const mra_dims* dims, const void* q, const void* k, c
  *   rand_blocks are not read again: the layout is in its workspace);
  *   out, dout, dq, dk, dv, workspace, bwd_workspace: as for
  *   mra_attention_bwd, with bwd_workspace of
- *   mra_bigbird_backward_workspace_size bytes.  bf16 only. */
+ *   mra_bigbird_backward_workspace_size bytes.  bf16 or fp32. */
 mra_status mra_bigbird_backward_workspace_size(const mra_dims* dims, int32_t block_size,
                                                int32_t num_random_blocks, size_t* bytes);
 mra_status mra_bigbird_bwd(const mra_dims* dims, const void* q, const void* k, const void* v,
@@ -240,10 +240,11 @@ mra_status mra_backward_workspace_size(const mra_dims* dims, int32_t block_per_r
  *             calls; MRA_ERR_WORKSPACE if smaller).
  * Must be queued after that forward call (stream order).  Both modes; in
  * full mode the low-resolution branch is differentiated too ([MRA] "第四步"),
- * through the block means to every valid token of each block.  bf16 only
- * (MRA_ERR_DTYPE otherwise).  dq, dk, dv and bwd_workspace must be 16-byte
- * aligned and overlap no input or each other (MRA_ERR_ALIAS).  The result
- * does not depend on scheduling: partial sums are added in a fixed order. */
+ * through the block means to every valid token of each block.  bf16 or fp32
+ * (the dtype of dims; fp32 runs its products on fp32 matrix instructions).
+ * dq, dk, dv and bwd_workspace must be 16-byte aligned and overlap no input
+ * or each other (MRA_ERR_ALIAS).  The result does not depend on scheduling:
+ * partial sums are added in a fixed order. */
 mra_status mra_attention_bwd(const mra_dims* dims, const void* q, const void* k, const void* v,
                              const uint8_t* mask, int32_t block_per_row, int32_t approx_mode,
                              int32_t prior_first, int32_t prior_diag, const void* out, const void* dout,

@@ -157,7 +157,7 @@ def call_bwd(dims=(1, 2, 512, 64, 1), mode=1, dout=DO, dq=DQ, dk=DK, dv=DV, bw=B
 
 @pytest.mark.parametrize("kw,status", [
     (dict(out=None), 1), (dict(dout=None), 1), (dict(dq=None), 1), (dict(dv=None), 1),
-    (dict(mode=2), 6), (dict(mode=-1), 6), (dict(dims=(1, 2, 512, 64, 0)), 5), (dict(ws=None), 10),
+    (dict(mode=2), 6), (dict(mode=-1), 6), (dict(dims=(1, 2, 512, 64, 7)), 5), (dict(ws=None), 10),
     (dict(bw=None), 10), (dict(bw_bytes=4096), 10),
     (dict(dq=Q), 9), (dict(dk=O + 64), 9), (dict(dv=DQ), 9), (dict(dq=BW), 9), (dict(bw=DO), 9),
     (dict(dq=DQ + 8), 12), (dict(bw=BW + 8), 12),
@@ -234,6 +234,6 @@ def test_bigbird_backward_checks():
     assert call(dq=Q) == 9
     assert call(r=0) == 7
     assert call(bs=96) == 3
-    d32 = mra._Dims(1, 2, 512, 64, 0)
-    assert L.mra_bigbird_bwd(ctypes.byref(d32), Q, K, V, None, 64, 3, O, DO2, DQ2, DK2, DV2, W, 1 << 30, BW2,
+    dbad = mra._Dims(1, 2, 512, 64, 7)
+    assert L.mra_bigbird_bwd(ctypes.byref(dbad), Q, K, V, None, 64, 3, O, DO2, DQ2, DK2, DV2, W, 1 << 30, BW2,
                              1 << 30, None) == 5
