@@ -63,7 +63,7 @@ class MraError(RuntimeError):
 
 class _Dims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("seq_len", ctypes.c_int32),
-                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32), ("scale_dim", ctypes.c_int32)]
 
 
 class _Options(ctypes.Structure):
@@ -108,8 +108,8 @@ def num_block(seq_len: int, block_per_row: int) -> int:
     return int(lib().mra_num_block(seq_len, block_per_row))
 
 
-def _dims(B, H, N, d, dtype_code) -> _Dims:
-    return _Dims(B, H, N, d, dtype_code)
+def _dims(B, H, N, d, dtype_code, scale_dim=0) -> _Dims:
+    return _Dims(B, H, N, d, dtype_code, scale_dim)
 
 
 def workspace_size(batch, heads, seq_len, head_dim=64, dtype=torch.bfloat16, block_per_row=4,
@@ -157,7 +157,7 @@ def _check_inputs(q, k, v, mask):
 
 
 def attention(q, k, v, mask=None, block_per_row=4, approx_mode="full", initial_prior_first_n_blocks=0,
-              initial_prior_diagonal_n_blocks=0, out=None, workspace=None, score_ranking="row_normalized"):
+              initial_prior_diagonal_n_blocks=0, out=None, workspace=None, score_ranking="row_normalized", scale_dim=0):
     """MRA-2 forward on [batch, heads, seq_len, head_dim] tensors (bf16 or fp32).
     mask: uint8 [batch, seq_len] (1 = valid) or None.  score_ranking:
     "row_normalized" (default) or "raw_logits", what step 2's top-k ranks.
@@ -169,7 +169,7 @@ def attention(q, k, v, mask=None, block_per_row=4, approx_mode="full", initial_p
     ws_bytes = workspace_size(B, H, N, d, q.dtype, block_per_row, approx_mode)
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-    dims = _dims(B, H, N, d, DTYPES[q.dtype])
+    dims = _dims(B, H, N, d, DTYPES[q.dtype], scale_dim)
     if score_ranking == "row_normalized":
         st = lib().mra_attention_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), block_per_row,
                                      MODES.get(approx_mode, -1), initial_prior_first_n_blocks,
@@ -186,7 +186,7 @@ def attention(q, k, v, mask=None, block_per_row=4, approx_mode="full", initial_p
 
 
 def prepare(q, k, v, mask=None, block_per_row=4, approx_mode="full", initial_prior_first_n_blocks=0,
-            initial_prior_diagonal_n_blocks=0, out=None, workspace=None):
+            initial_prior_diagonal_n_blocks=0, out=None, workspace=None, scale_dim=0):
     """Check and marshal the arguments once; returns (call, out) where call()
     queues one forward pass on the current stream through the C ABI.  The
     tensors must stay alive and unchanged in shape while call is used."""
@@ -197,7 +197,7 @@ def prepare(q, k, v, mask=None, block_per_row=4, approx_mode="full", initial_pri
     ws_bytes = workspace_size(B, H, N, d, q.dtype, block_per_row, approx_mode)
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-    dims = _dims(B, H, N, d, DTYPES[q.dtype])
+    dims = _dims(B, H, N, d, DTYPES[q.dtype], scale_dim)
     fn = lib().mra_attention_fwd
     args = (ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), block_per_row, MODES.get(approx_mode, -1),
             initial_prior_first_n_blocks, initial_prior_diagonal_n_blocks, _ptr(out), _ptr(workspace),
@@ -218,7 +218,7 @@ STAGES = ("pool", "logits", "select", "attn", "finish")
 
 def attention_profiled(q, k, v, events, mask=None, block_per_row=4, approx_mode="full",
                        initial_prior_first_n_blocks=0, initial_prior_diagonal_n_blocks=0, out=None,
-                       workspace=None):
+                       workspace=None, scale_dim=0):
     """attention() plus HIP event records around each kernel launch.
     events: 10 torch.cuda.Event(enable_timing=True) (already recorded once, so
     that their handles exist), entry 2s / 2s+1 bracketing stage STAGES[s]."""
@@ -230,7 +230,7 @@ def attention_profiled(q, k, v, events, mask=None, block_per_row=4, approx_mode=
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     arr = (ctypes.c_void_p * 10)(*[e.cuda_event if e is not None else None for e in events])
-    dims = _dims(B, H, N, d, DTYPES[q.dtype])
+    dims = _dims(B, H, N, d, DTYPES[q.dtype], scale_dim)
     st = lib().mra_attention_fwd_profiled(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(mask),
                                           block_per_row, MODES.get(approx_mode, -1), initial_prior_first_n_blocks,
                                           initial_prior_diagonal_n_blocks, _ptr(out), _ptr(workspace),
@@ -241,7 +241,7 @@ def attention_profiled(q, k, v, events, mask=None, block_per_row=4, approx_mode=
 
 def prepare_backward(q, k, v, out, dout, workspace, mask=None, block_per_row=4, approx_mode="sparse",
                      initial_prior_first_n_blocks=0, initial_prior_diagonal_n_blocks=0, dq=None, dk=None, dv=None,
-                     bwd_workspace=None):
+                     bwd_workspace=None, scale_dim=0):
     """Check and marshal the arguments of attention_backward once; returns
     (call, (dq, dk, dv)) where call() queues one backward pass on the current
     stream through the C ABI.  `out` and `workspace` are a forward call's
@@ -263,7 +263,7 @@ def prepare_backward(q, k, v, out, dout, workspace, mask=None, block_per_row=4, 
     bw_bytes = backward_workspace_size(B, H, N, d, q.dtype, block_per_row, approx_mode)
     if bwd_workspace is None or bwd_workspace.numel() < bw_bytes:
         bwd_workspace = torch.empty(bw_bytes, dtype=torch.uint8, device=q.device)
-    dims = _dims(B, H, N, d, DTYPES[q.dtype])
+    dims = _dims(B, H, N, d, DTYPES[q.dtype], scale_dim)
     fn = lib().mra_attention_bwd
     args = (ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), block_per_row, MODES.get(approx_mode, -1),
             initial_prior_first_n_blocks, initial_prior_diagonal_n_blocks, _ptr(out), _ptr(dout), _ptr(dq),
@@ -282,24 +282,24 @@ def prepare_backward(q, k, v, out, dout, workspace, mask=None, block_per_row=4, 
 
 def attention_backward(q, k, v, out, dout, workspace, mask=None, block_per_row=4, approx_mode="sparse",
                        initial_prior_first_n_blocks=0, initial_prior_diagonal_n_blocks=0, dq=None, dk=None,
-                       dv=None, bwd_workspace=None):
+                       dv=None, bwd_workspace=None, scale_dim=0):
     """Gradients (dq, dk, dv) of a forward call's output with respect to q, k,
     v given dout; arguments as for prepare_backward."""
     call, grads = prepare_backward(q, k, v, out, dout, workspace, mask, block_per_row, approx_mode,
                                    initial_prior_first_n_blocks, initial_prior_diagonal_n_blocks, dq, dk, dv,
-                                   bwd_workspace)
+                                   bwd_workspace, scale_dim)
     call()
     return grads
 
 
 def debug_replay(q, k, v, stage, count, mask=None, block_per_row=4, approx_mode="full",
-                 initial_prior_first_n_blocks=0, initial_prior_diagonal_n_blocks=0, out=None, workspace=None):
+                 initial_prior_first_n_blocks=0, initial_prior_diagonal_n_blocks=0, out=None, workspace=None, scale_dim=0):
     """Relaunch stage STAGES[stage] (3 attn or 4 finish only) `count` times on
     the current stream, on a workspace and out that a forward call with the
     same arguments has filled; for timing the kernel alone."""
     _check_inputs(q, k, v, mask)
     B, H, N, d = q.shape
-    dims = _dims(B, H, N, d, DTYPES[q.dtype])
+    dims = _dims(B, H, N, d, DTYPES[q.dtype], scale_dim)
     st = lib().mra_debug_replay(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), block_per_row,
                                 MODES.get(approx_mode, -1), initial_prior_first_n_blocks,
                                 initial_prior_diagonal_n_blocks, _ptr(out), _ptr(workspace),
@@ -309,7 +309,7 @@ def debug_replay(q, k, v, stage, count, mask=None, block_per_row=4, approx_mode=
 
 
 def debug_stages(q, k, v, mask=None, block_per_row=4, approx_mode="full", initial_prior_first_n_blocks=0,
-                 initial_prior_diagonal_n_blocks=0, score_ranking="row_normalized"):
+                 initial_prior_diagonal_n_blocks=0, score_ranking="row_normalized", scale_dim=0):
     """Steps 1-2 of the same kernels; returns a dict of device tensors:
     qhat, khat, vhat (full mode), count, logits, rowmax, sel, error."""
     _check_inputs(q, k, v, mask)
@@ -330,7 +330,7 @@ def debug_stages(q, k, v, mask=None, block_per_row=4, approx_mode="full", initia
     }
     ws_bytes = workspace_size(B, H, N, d, q.dtype, block_per_row, approx_mode)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    dims = _dims(B, H, N, d, DTYPES[q.dtype])
+    dims = _dims(B, H, N, d, DTYPES[q.dtype], scale_dim)
     st = lib().mra_debug_stages(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), block_per_row,
                                 MODES.get(approx_mode, -1), initial_prior_first_n_blocks,
                                 initial_prior_diagonal_n_blocks, RANKINGS.get(score_ranking, -1),
@@ -373,7 +373,7 @@ def bigbird_workspace_size(batch, heads, seq_len, head_dim=64, dtype=torch.bfloa
     return n.value
 
 
-def prepare_bigbird(q, k, v, rand_blocks, mask=None, block_size=64, out=None, workspace=None):
+def prepare_bigbird(q, k, v, rand_blocks, mask=None, block_size=64, out=None, workspace=None, scale_dim=0):
     """Check and marshal BigBird block-sparse attention once (mra_bigbird_fwd);
     rand_blocks: int32 device tensor [B, H, seq_len / block_size, r] of the
     random key blocks drawn per query block.  Returns (call, out)."""
@@ -387,7 +387,7 @@ def prepare_bigbird(q, k, v, rand_blocks, mask=None, block_size=64, out=None, wo
     ws_bytes = bigbird_workspace_size(B, H, N, d, q.dtype, block_size, r)
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-    dims = _dims(B, H, N, d, DTYPES[q.dtype])
+    dims = _dims(B, H, N, d, DTYPES[q.dtype], scale_dim)
     fn = lib().mra_bigbird_fwd
     args = (ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), block_size, r, _ptr(rand_blocks), _ptr(out),
             _ptr(workspace), workspace.numel(), _stream(q))
@@ -402,11 +402,11 @@ def prepare_bigbird(q, k, v, rand_blocks, mask=None, block_size=64, out=None, wo
     return call, out
 
 
-def bigbird_attention(q, k, v, rand_blocks, mask=None, block_size=64, out=None, workspace=None):
+def bigbird_attention(q, k, v, rand_blocks, mask=None, block_size=64, out=None, workspace=None, scale_dim=0):
     """BigBird block-sparse attention ([BigBird] pattern: window of three
     blocks, first and last blocks global, the given random blocks) on
     [batch, heads, seq_len, 64] tensors.  Returns `out`."""
-    call, out = prepare_bigbird(q, k, v, rand_blocks, mask, block_size, out, workspace)
+    call, out = prepare_bigbird(q, k, v, rand_blocks, mask, block_size, out, workspace, scale_dim)
     call()
     return out
 
@@ -421,7 +421,7 @@ def bigbird_backward_workspace_size(batch, heads, seq_len, head_dim=64, dtype=to
 
 
 def bigbird_backward(q, k, v, out, dout, workspace, num_random_blocks, mask=None, block_size=64, dq=None,
-                     dk=None, dv=None, bwd_workspace=None):
+                     dk=None, dv=None, bwd_workspace=None, scale_dim=0):
     """Gradients (dq, dk, dv) of a bigbird_attention call's output given
     dout; `out` and `workspace` are that call's (its layout is read from the
     workspace).  bf16 or fp32."""
@@ -436,7 +436,7 @@ def bigbird_backward(q, k, v, out, dout, workspace, num_random_blocks, mask=None
     bw_bytes = bigbird_backward_workspace_size(B, H, N, d, q.dtype, block_size, num_random_blocks)
     if bwd_workspace is None or bwd_workspace.numel() < bw_bytes:
         bwd_workspace = torch.empty(bw_bytes, dtype=torch.uint8, device=q.device)
-    dims = _dims(B, H, N, d, DTYPES[q.dtype])
+    dims = _dims(B, H, N, d, DTYPES[q.dtype], scale_dim)
     st = lib().mra_bigbird_bwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), block_size,
                                num_random_blocks, _ptr(out), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
                                _ptr(workspace), workspace.numel(), _ptr(bwd_workspace), bwd_workspace.numel(),

@@ -20,7 +20,7 @@
 namespace mra {
 namespace {
 
-constexpr int32_t kAbiVersion = 2;
+constexpr int32_t kAbiVersion = 3;
 constexpr int32_t kMaxSeqLen = 16384;
 
 size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -107,6 +107,7 @@ mra_status check_dims(const mra_dims* d) {
     if (d->batch < 1 || d->heads < 1) return MRA_ERR_SHAPE;
     if (d->seq_len < kBlock || d->seq_len % kBlock != 0 || d->seq_len > kMaxSeqLen) return MRA_ERR_SEQ_LEN;
     if (d->head_dim != kHeadDim) return MRA_ERR_HEAD_DIM;
+    if (d->scale_dim < 0 || d->scale_dim > d->head_dim) return MRA_ERR_HEAD_DIM;
     if (d->dtype != MRA_F32 && d->dtype != MRA_BF16) return MRA_ERR_DTYPE;
     if ((int64_t)d->batch * d->heads > (1 << 20)) return MRA_ERR_SHAPE;
     return MRA_OK;
@@ -133,6 +134,7 @@ Params make_params(const mra_dims& d, const Layout& L, int32_t mode, int32_t pf,
     memset(&p, 0, sizeof(p));
     unsigned char* w = static_cast<unsigned char*>(ws);
     p.B = L.B; p.H = L.H; p.N = L.N; p.d = L.d; p.nb = L.nb; p.BH = L.BH;
+    p.dscale = d.scale_dim > 0 ? d.scale_dim : d.head_dim;
     p.words = (L.nb + 31) / 32;
     p.K = L.K;
     p.mode = mode;
@@ -220,7 +222,7 @@ MRA_API const char* mra_status_string(int32_t s) {
         case MRA_ERR_NULL: return "a required pointer is NULL";
         case MRA_ERR_SHAPE: return "batch/heads out of range";
         case MRA_ERR_SEQ_LEN: return "seq_len must be a multiple of 32 in [32, 16384]";
-        case MRA_ERR_HEAD_DIM: return "head_dim must be 64";
+        case MRA_ERR_HEAD_DIM: return "head_dim must be 64 and scale_dim 0 or 1 .. head_dim";
         case MRA_ERR_DTYPE: return "dtype must be MRA_F32 or MRA_BF16";
         case MRA_ERR_MODE: return "approx_mode must be full (0) or sparse (1)";
         case MRA_ERR_BUDGET: return "block_per_row must be >= 1";

@@ -508,7 +508,7 @@ __device__ __forceinline__ void run_range(const Params& p, int bh, int k, int WP
     W.Qg = static_cast<const E*>(p.q) + head_off;
     W.Kg = static_cast<const E*>(p.k) + head_off;
     W.Vg = static_cast<const E*>(p.v) + head_off;
-    const float scale2 = (1.0f / __builtin_sqrtf((float)p.d)) * kLog2e;
+    const float scale2 = (1.0f / __builtin_sqrtf((float)p.dscale)) * kLog2e;
 
     // Blocks go in batches: the loads of a whole batch are issued, then the
     // batch is computed.  Past the end the last block is fetched again, so

@@ -367,7 +367,7 @@ __global__ __launch_bounds__(kLrThreads) void lr_rows_kernel(Params p) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int i = i0 + wave, b = bh / p.H;
     const bool act = i < nb;
-    const float tau = 1.0f / __builtin_sqrtf((float)p.d);
+    const float tau = 1.0f / __builtin_sqrtf((float)p.dscale);
     const size_t hrow = (size_t)bh * nb + (act ? i : 0);
     const float mi = p.rowmax[hrow];
 
@@ -463,7 +463,7 @@ __global__ __launch_bounds__(kLrThreads) void lr_cols_kernel(Params p) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int j = j0 + wave;
     const bool act = j < nb;
-    const float tau = 1.0f / __builtin_sqrtf((float)p.d);
+    const float tau = 1.0f / __builtin_sqrtf((float)p.dscale);
     const float* gh = p.bwd_g + (size_t)bh * nb * kHeadDim;
     const float* qh = p.qhat + (size_t)bh * nb * kHeadDim;
     const size_t col = ((size_t)bh * nb + (act ? j : 0)) * nb;
@@ -522,7 +522,7 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(Params p) {
     const uint16_t* Vh = static_cast<const uint16_t*>(p.v) + head;
     const uint16_t* dO = static_cast<const uint16_t*>(p.dout) + rowoff;
     const uint16_t* Of = static_cast<const uint16_t*>(p.fout) + rowoff;
-    const float tau = 1.0f / __builtin_sqrtf((float)p.d);
+    const float tau = 1.0f / __builtin_sqrtf((float)p.dscale);
     const float scale2 = tau * kLog2e;
 
     // the next block's K and V rows and mask word travel in registers while
@@ -607,7 +607,7 @@ __global__ __launch_bounds__(kThreads) void dkv_kernel(Params p) {
     const size_t head = (size_t)bh * p.N * kHeadDim, coloff = head + (size_t)j * kBlock * kHeadDim;
     const uint16_t* Q = static_cast<const uint16_t*>(p.q) + head;
     const uint16_t* dO = static_cast<const uint16_t*>(p.dout) + head;
-    const float tau = 1.0f / __builtin_sqrtf((float)p.d);
+    const float tau = 1.0f / __builtin_sqrtf((float)p.dscale);
     const float scale2 = tau * kLog2e;
 
     const int32_t* rows = p.ct_row + (size_t)bh * p.K;
@@ -759,7 +759,7 @@ __global__ __launch_bounds__(64) void dq32_kernel(Params p) {
     const float* Kh = static_cast<const float*>(p.k) + head;
     const float* Vh = static_cast<const float*>(p.v) + head;
     const float* dO = static_cast<const float*>(p.dout) + rowoff;
-    const float tau = 1.0f / __builtin_sqrtf((float)p.d);
+    const float tau = 1.0f / __builtin_sqrtf((float)p.dscale);
     const float scale2 = tau * kLog2e;
     const int32_t* cols = p.col + (size_t)bh * p.K;
     float4 r[8];
@@ -824,7 +824,7 @@ __global__ __launch_bounds__(64) void dkv32_kernel(Params p) {
     const size_t head = (size_t)bh * p.N * kHeadDim, coloff = head + (size_t)j * kBlock * kHeadDim;
     const float* Q = static_cast<const float*>(p.q) + head;
     const float* dO = static_cast<const float*>(p.dout) + head;
-    const float tau = 1.0f / __builtin_sqrtf((float)p.d);
+    const float tau = 1.0f / __builtin_sqrtf((float)p.dscale);
     const float scale2 = tau * kLog2e;
     const int32_t* rows = p.ct_row + (size_t)bh * p.K;
     const size_t sbase = (size_t)bh * p.N;
@@ -943,7 +943,7 @@ __device__ void reduce_item(const Params& p, int bh, int x, int side) {
     const int4 m = (side == 0 ? p.bwd_rmul : p.bwd_cmul)[(size_t)bh * nb + x];
     const int blk = min(max(m.x, 0), nb - 1);
     const int first = max(m.y, 0), nch = max(0, min(m.z, maxch - first));
-    const float tau = 1.0f / __builtin_sqrtf((float)p.d);
+    const float tau = 1.0f / __builtin_sqrtf((float)p.dscale);
     const size_t off = ((size_t)bh * p.N + (size_t)blk * kBlock) * kHeadDim, slot0 = (size_t)bh * maxch;
     // full mode: the token's share of its block mean's gradient
     const int b = bh / p.H, tok = threadIdx.x >> 3;

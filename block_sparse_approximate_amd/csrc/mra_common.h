@@ -57,6 +57,8 @@ struct Layout {
 // Everything a kernel needs, passed by value.
 struct Params {
     int32_t B, H, N, d, nb, BH, words;  // words = u32 words per selection-bitmap row
+    int32_t dscale;        // the head size the logit scale 1/sqrt(dscale) is taken from (d, or the
+                           //   logical size of zero-padded heads)
     int64_t K;
     int32_t mode;          // 0 full, 1 sparse
     int32_t dtype;         // 0 fp32, 1 bf16

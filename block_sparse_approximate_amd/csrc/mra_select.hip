@@ -407,7 +407,7 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(Params p) {
     const int row0 = (slot - hm * tiles_per_head) * kRT;
     const int b = bh / p.H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const float tau = (float)(1.0 / __builtin_sqrt((double)p.d));
+    const float tau = (float)(1.0 / __builtin_sqrt((double)p.dscale));
     const int ntile = (nb + kCT - 1) / kCT;
     const LogitsLds L = logits_lds(nb);
     float* qS = reinterpret_cast<float*>(smem + L.qS);

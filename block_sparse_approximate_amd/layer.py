@@ -31,37 +31,49 @@ class MraAttentionFunction(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, q, k, v, mask, block_per_row, approx_mode, prior_first, prior_diag,
-                score_ranking="row_normalized"):
+                score_ranking="row_normalized", scale_dim=0):
         B, H, N, d = q.shape
         ws = torch.empty(workspace_size(B, H, N, d, q.dtype, block_per_row, approx_mode), dtype=torch.uint8,
                          device=q.device)
         out = attention(q, k, v, mask, block_per_row, approx_mode, prior_first, prior_diag, workspace=ws,
-                        score_ranking=score_ranking)
+                        score_ranking=score_ranking, scale_dim=scale_dim)
         ctx.save_for_backward(q, k, v, out, ws, mask if mask is not None else torch.empty(0, device=q.device))
         ctx.has_mask = mask is not None
-        ctx.args = (block_per_row, approx_mode, prior_first, prior_diag)
+        ctx.args = (block_per_row, approx_mode, prior_first, prior_diag, scale_dim)
         return out
 
     @staticmethod
     def backward(ctx, dout):
         q, k, v, out, ws, mask = ctx.saved_tensors
         mask = mask if ctx.has_mask else None
-        block_per_row, approx_mode, prior_first, prior_diag = ctx.args
+        block_per_row, approx_mode, prior_first, prior_diag, scale_dim = ctx.args
         B, H, N, d = q.shape
         bw = torch.empty(backward_workspace_size(B, H, N, d, q.dtype, block_per_row, approx_mode),
                          dtype=torch.uint8, device=q.device)
         call, grads = prepare_backward(q, k, v, out, dout.contiguous(), ws, mask, block_per_row, approx_mode,
-                                       prior_first, prior_diag, bwd_workspace=bw)
+                                       prior_first, prior_diag, bwd_workspace=bw, scale_dim=scale_dim)
         call()
-        return grads[0], grads[1], grads[2], None, None, None, None, None, None
+        return grads[0], grads[1], grads[2], None, None, None, None, None, None, None
 
 
 def mra_attention(q, k, v, mask=None, block_per_row=4, approx_mode="full", initial_prior_first_n_blocks=0,
                   initial_prior_diagonal_n_blocks=0, score_ranking="row_normalized"):
-    """Differentiable MRA-2 attention on contiguous [batch, heads, seq_len,
-    64] device tensors; mask is uint8 [batch, seq_len] (1 = valid) or None."""
-    return MraAttentionFunction.apply(q, k, v, mask, block_per_row, approx_mode, initial_prior_first_n_blocks,
-                                      initial_prior_diagonal_n_blocks, score_ranking)
+    """Differentiable MRA-2 attention on [batch, heads, seq_len, d] device
+    tensors, d <= 64; mask is uint8 [batch, seq_len] (1 = valid) or None.
+    Heads narrower than 64 go to the kernels zero-padded to 64 channels with
+    the logit scale of their own size ([MRA] engineering notes: the model
+    pads small heads for the kernels; the zero channels change no sum), and
+    the output is cut back to d channels."""
+    d = q.shape[-1]
+    if d > 64:
+        raise ValueError("head_dim above 64 is not supported")
+    if d == 64:
+        return MraAttentionFunction.apply(q, k, v, mask, block_per_row, approx_mode, initial_prior_first_n_blocks,
+                                          initial_prior_diagonal_n_blocks, score_ranking, 0)
+    pad = lambda t: F.pad(t, (0, 64 - d)).contiguous()
+    out = MraAttentionFunction.apply(pad(q), pad(k), pad(v), mask, block_per_row, approx_mode,
+                                     initial_prior_first_n_blocks, initial_prior_diagonal_n_blocks, score_ranking, d)
+    return out[..., :d]
 
 
 class MraSelfAttention(torch.nn.Module):
@@ -69,14 +81,15 @@ class MraSelfAttention(torch.nn.Module):
     merge.  Parameters follow MraConfig ([MRA] MraConfig section):
     block_per_row, approx_mode, initial_prior_first_n_blocks,
     initial_prior_diagonal_n_blocks; score_ranking picks what step 2 ranks
-    ("row_normalized" or "raw_logits").  head_dim = hidden_size / heads must
-    be 64, the head size the kernels are built for."""
+    ("row_normalized" or "raw_logits").  head_dim = hidden_size / heads may
+    be at most 64 (the kernels' head size; narrower heads are zero-padded,
+    see mra_attention)."""
 
     def __init__(self, hidden_size=768, num_attention_heads=12, block_per_row=4, approx_mode="full",
                  initial_prior_first_n_blocks=0, initial_prior_diagonal_n_blocks=0, score_ranking="row_normalized"):
         super().__init__()
-        if hidden_size % num_attention_heads != 0 or hidden_size // num_attention_heads != 64:
-            raise ValueError("hidden_size / num_attention_heads must be 64")
+        if hidden_size % num_attention_heads != 0 or not 1 <= hidden_size // num_attention_heads <= 64:
+            raise ValueError("hidden_size / num_attention_heads must be a whole number from 1 to 64")
         self.num_attention_heads = num_attention_heads
         self.head_dim = hidden_size // num_attention_heads
         self.query = torch.nn.Linear(hidden_size, hidden_size)

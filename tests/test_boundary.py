@@ -27,7 +27,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(mra.SIGNATURES)
-    assert L.mra_abi_version() == 2
+    assert L.mra_abi_version() == 3
 
 
 def test_status_strings():
@@ -237,3 +237,11 @@ def test_bigbird_backward_checks():
     dbad = mra._Dims(1, 2, 512, 64, 7)
     assert L.mra_bigbird_bwd(ctypes.byref(dbad), Q, K, V, None, 64, 3, O, DO2, DQ2, DK2, DV2, W, 1 << 30, BW2,
                              1 << 30, None) == 5
+
+
+def test_scale_dim_checks():
+    for sd, status in [(-1, 4), (65, 4)]:
+        d = mra._Dims(1, 2, 512, 64, 1, sd)
+        assert mra.lib().mra_attention_fwd(ctypes.byref(d), Q, K, V, None, 4, 0, 0, 0, O, W, 1 << 40, None) == status
+    d = mra._Dims(1, 2, 512, 64, 1, 32)
+    assert mra.lib().mra_attention_fwd(ctypes.byref(d), Q, K, V, None, 4, 0, 0, 0, None, W, 1 << 40, None) == 1

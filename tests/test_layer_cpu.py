@@ -5,10 +5,14 @@ import torch
 from block_sparse_approximate_amd import layer
 
 
-def test_head_size_must_be_64():
+def test_head_size_at_most_64():
     with pytest.raises(ValueError):
-        layer.MraSelfAttention(hidden_size=256, num_attention_heads=8)
+        layer.MraSelfAttention(hidden_size=256, num_attention_heads=2)     # 128
+    with pytest.raises(ValueError):
+        layer.MraSelfAttention(hidden_size=250, num_attention_heads=4)     # not whole
     assert layer.MraSelfAttention(hidden_size=256, num_attention_heads=4).head_dim == 64
+    assert layer.MraSelfAttention(hidden_size=256, num_attention_heads=8).head_dim == 32
+    assert layer.MraSelfAttention(hidden_size=16, num_attention_heads=2).head_dim == 8
 
 
 def test_modules_refuse_cpu_inputs():
