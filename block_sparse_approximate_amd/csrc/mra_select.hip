@@ -354,8 +354,9 @@ __device__ __forceinline__ float wave_sum(float x) {
 // The marking pass for the common shape: one tile (kv holds every cell), a
 // multiple of 64 cells per block row, every cell of the tile present, and a
 // prefix of at most 32 bits.  Straight-line per 64-cell group: one shift,
-// two compares (their lane masks are the ballots), one bitmap store, and an
-// LDS atomic only for groups that hold candidates.
+// two compares (their lane masks are the ballots) and one bitmap store; the
+// wave's candidates then take their place in the list with one LDS atomic
+// (with many boundary cells, an atomic per group serialised the waves).
 __device__ __forceinline__ void mark_cells_fast(int nb, int words, uint32_t magic, uint32_t p32, int pbits,
                                                 const uint32_t (&kv)[kCells], uint32_t* bitmap, uint64_t* cand,
                                                 uint32_t* small) {
@@ -363,23 +364,32 @@ __device__ __forceinline__ void mark_cells_fast(int nb, int words, uint32_t magi
     const uint64_t lt_mask = (1ull << lane) - 1ull;
     const uint32_t wbase = (uint32_t)__builtin_amdgcn_readfirstlane((int)threadIdx.x - lane);
     const uint32_t sh = (uint32_t)(32 - pbits);
+    // sure cells straight into the bitmap; the wave's boundary cells are
+    // counted first and take their place in the list with one atomic
+    uint64_t mh[kCells];
+    uint32_t tot = 0;
 #pragma unroll
     for (int e = 0; e < kCells; e++) {
         const uint32_t x0 = wbase + (uint32_t)e * kSelThreads;   // the wave's first cell (uniform)
         const uint32_t top = kv[e] >> sh;
         const uint64_t ms = __ballot(top > p32);
-        const uint64_t mh = __ballot(top == p32);
+        mh[e] = __ballot(top == p32);
+        tot += (uint32_t)__popcll(mh[e]);
         const uint32_t i0 = row_of(x0, (uint32_t)nb, magic), j0 = x0 - i0 * (uint32_t)nb;
         if (lane == 0)
             *reinterpret_cast<uint2*>(bitmap + i0 * words + (j0 >> 5)) = make_uint2((uint32_t)ms, (uint32_t)(ms >> 32));
-        if (mh) {
-            uint32_t at0 = 0;
-            if (lane == 0) at0 = atomicAdd(&small[8], (uint32_t)__popcll(mh));
-            at0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)at0);
-            if ((mh >> lane) & 1ull) {
-                const uint32_t at = at0 + (uint32_t)__popcll(mh & lt_mask);
-                if (at < (uint32_t)kCap) cand[at] = cell_key64(kv[e], x0 + lane);
+    }
+    if (tot) {
+        uint32_t at0 = 0;
+        if (lane == 0) at0 = atomicAdd(&small[8], tot);
+        at0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)at0);
+#pragma unroll
+        for (int e = 0; e < kCells; e++) {
+            if ((mh[e] >> lane) & 1ull) {
+                const uint32_t at = at0 + (uint32_t)__popcll(mh[e] & lt_mask);
+                if (at < (uint32_t)kCap) cand[at] = cell_key64(kv[e], wbase + (uint32_t)e * kSelThreads + lane);
             }
+            at0 += (uint32_t)__popcll(mh[e]);
         }
     }
 }
