@@ -1,6 +1,8 @@
 /*
- * mra.h — C ABI of the MI355X (gfx950) MRA-2 forward (and backward) library
- * (libmra.so, built from block_sparse_approximate_amd/csrc).
+ * mra.h — C ABI of the MI355X (gfx950) MRA-2 attention library (libmra.so,
+ * built from block_sparse_approximate_amd/csrc): the forward pass, its
+ * backward pass, and BigBird's block-sparse pattern through the same block
+ * attention kernels.
  *
  * The method is MRA-2 multi-resolution approximate self-attention as
  * described on the page "深入解析 Transformers 中的 MRA 模型" ("A deep dive
@@ -55,14 +57,14 @@ typedef enum {
     MRA_OK = 0,
     MRA_ERR_NULL = 1,       /* a required pointer is NULL */
     MRA_ERR_SHAPE = 2,      /* batch or heads < 1, or the sizes overflow */
-    MRA_ERR_SEQ_LEN = 3,    /* seq_len not a multiple of 32, < 32 or > 16384 */
+    MRA_ERR_SEQ_LEN = 3,    /* seq_len not a multiple of 32, < 32 or > 16384 (BigBird: or of its block size) */
     MRA_ERR_HEAD_DIM = 4,   /* head_dim other than 64, or scale_dim outside 0 .. head_dim */
     MRA_ERR_DTYPE = 5,      /* dtype not MRA_F32 or MRA_BF16 */
     MRA_ERR_MODE = 6,       /* approx_mode not MRA_APPROX_FULL or MRA_APPROX_SPARSE */
-    MRA_ERR_BUDGET = 7,     /* block_per_row < 1 */
+    MRA_ERR_BUDGET = 7,     /* block_per_row < 1 (BigBird: num_random_blocks < 1) */
     MRA_ERR_PRIOR = 8,      /* a prior count < 0 */
-    MRA_ERR_ALIAS = 9,      /* out overlaps an input or the workspace */
-    MRA_ERR_WORKSPACE = 10, /* workspace NULL or smaller than mra_workspace_size() */
+    MRA_ERR_ALIAS = 9,      /* an output overlaps an input, another output or a workspace */
+    MRA_ERR_WORKSPACE = 10, /* a workspace NULL or smaller than its size query returns */
     MRA_ERR_HIP = 11,       /* a HIP call failed */
     MRA_ERR_ALIGN = 12,     /* a tensor pointer is not 16-byte aligned */
     MRA_ERR_STAGE = 13      /* mra_debug_replay: a stage other than 3 or 4, or count < 1 */
