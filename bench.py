@@ -44,7 +44,10 @@ Besides tokens/s the line carries:
     of 64 tokens) on B=2, H=12, N=4096 bf16, through the same attention
     kernels; algorithmic bytes Q, K, V read and O written once, MFMA work
     4 x 32 x 32 x 64 per attended 32-token cell; and its backward pass
-    (mra_bigbird_bwd) timed the same way.
+    (mra_bigbird_bwd) timed the same way;
+  * `head128`: the forward pass on 128-channel heads (B=2, H=12, N=4096,
+    bf16, full mode, i.i.d. N(0,1)*0.5 inputs), timed the same way, with the
+    same algorithmic bytes and MFMA work at d=128.
 Only one GPU is used; --gpus above 1 exits with a message.
 """
 from __future__ import annotations
@@ -246,6 +249,40 @@ def bench_bigbird(mra, steps: int, warmup: int) -> dict:
             "backward_tokens_per_s": round(w.B * w.N / (ms_bwd * 1e-3), 1)}
 
 
+def bench_head128(mra, steps: int, warmup: int) -> dict:
+    """The forward pass on 128-channel heads: bf16, B=2, H=12, N=4096,
+    Q/K/V i.i.d. N(0,1)*0.5, block_per_row=4, full mode."""
+    import numpy as np
+    import torch
+
+    import workloads
+
+    w = workloads.iid("D128-bf16-N4096-full", 2, 12, 4096, d=128, dtype="bf16", seed=128, scale=0.5,
+                      block_per_row=4, approx_mode="full")
+    to_dev = lambda n: torch.from_numpy(w.raw(n).view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v = to_dev("q"), to_dev("k"), to_dev("v")
+    kw = dict(block_per_row=w.block_per_row, approx_mode=w.approx_mode)
+    call, out = mra.prepare(q, k, v, None, **kw)
+    for _ in range(warmup):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    BH, K = w.B * w.H, mra.num_block(w.N, w.block_per_row)
+    nbytes = 4.0 * BH * w.N * w.d * 2          # Q, K, V read and O written once, bf16
+    flops = 4.0 * 32 * 32 * w.d * BH * K       # QK^T and PV on the selected blocks
+    return {"workload": w.name, "head_dim": w.d, "ms_per_call": round(ms, 5),
+            "tokens_per_s": round(w.B * w.N / (ms * 1e-3), 1), "algorithmic_bytes": int(nbytes),
+            "achieved_GBs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "mfma_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -255,6 +292,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-bigbird", action="store_true")
+    ap.add_argument("--no-head128", action="store_true")
+    ap.add_argument("--only-head128", action="store_true",
+                    help="only time the forward pass on 128-channel heads (N=4096 bf16 full mode)")
     ap.add_argument("--only-bigbird", action="store_true",
                     help="only time BigBird block-sparse attention on its N=4096 workload")
     ap.add_argument("--only-backward", metavar="CFG", default=None,
@@ -286,6 +326,10 @@ def main():
     if args.only_bigbird:
         torch.cuda.set_device(torch.device("cuda:0"))
         print(json.dumps({"bigbird": bench_bigbird(mra, args.steps, args.warmup)}), flush=True)
+        return
+    if args.only_head128:
+        torch.cuda.set_device(torch.device("cuda:0"))
+        print(json.dumps({"head128": bench_head128(mra, args.steps, args.warmup)}), flush=True)
         return
     if args.only_backward:
         torch.cuda.set_device(torch.device("cuda:0"))
@@ -411,6 +455,8 @@ def main():
         rec["backward"] = [bench_backward(mra, args.steps, args.warmup, cfg) for cfg in ("C3", "C4")]
     if not args.no_bigbird:
         rec["bigbird"] = bench_bigbird(mra, args.steps, args.warmup)
+    if not args.no_head128:
+        rec["head128"] = bench_head128(mra, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(rec), flush=True)

@@ -60,9 +60,10 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kVStrideB = 80;   // bf16 elements per staged V row (64 + 16 pad: no bank conflicts)
-constexpr int kKStrideB = 72;   // bf16 elements per staged Q row (144 bytes: 8 lanes' 16-byte reads hit 32 banks)
-constexpr int kVStrideF = 68;   // fp32 elements per staged V row
+// staged row strides for a head of hd channels (elements)
+__host__ __device__ constexpr int v_stride_b(int hd) { return hd + 16; }   // bf16 V: 16 pad, no bank conflicts
+__host__ __device__ constexpr int q_stride_b(int hd) { return hd + 8; }    // bf16 Q: row r's 16-byte reads start at bank group r
+__host__ __device__ constexpr int v_stride_f(int hd) { return hd + 4; }    // fp32 V
 constexpr int kWindow = 64;     // block records a wave holds (one per lane)
 constexpr float kLazyMax = 8.0f;   // log2 headroom of the running max (probabilities <= 256)
 // blocks per wave before segment alignment: an end moves up to kChunk - 1
@@ -90,39 +91,44 @@ __device__ __forceinline__ int nearest_segment_start(int x, uint32_t info, int64
     return 2 * pos <= len ? x - pos : x - pos + len;
 }
 
-template <int DT> struct Cfg;
-template <> struct Cfg<1> {                 // bf16: 16 bytes per lane per 8 elements
+// DT: 1 bf16, 0 fp32; HD: channels per head (64 or 128)
+template <int DT, int HD> struct Cfg;
+template <int HD> struct Cfg<1, HD> {       // bf16: 16 bytes per lane per 8 elements
     static constexpr int kBatch = 2;        // blocks whose loads are in flight together
-    static constexpr int kKV = 4;           // 16-byte pieces per lane for one V (or Q) block
+    static constexpr int kKV = HD / 16;     // 16-byte pieces per lane for one V (or Q) block
     static constexpr bool kKDirect = true;  // K goes straight from memory to LDS
     using Elem = uint16_t;
-    static constexpr int kStride = kVStrideB;
 };
-template <> struct Cfg<0> {                 // fp32: twice the registers per block
+template <int HD> struct Cfg<0, HD> {       // fp32: twice the registers per block
     static constexpr int kBatch = 1;
-    static constexpr int kKV = 8;
+    static constexpr int kKV = HD / 8;
     static constexpr bool kKDirect = false;
     using Elem = float;
-    static constexpr int kStride = kVStrideF;
 };
 
-// bf16 K block in LDS: 32 token rows of 128 bytes, the 16-byte chunk c of row
-// r at position c ^ ((r / 2) mod 8) of the row.  The direct loads place the
-// chunks so (whole rows per 8 lanes, i.e. full cache lines), and the MFMA
+// bf16 K block in LDS: 32 token rows of 2 HD bytes, the 16-byte chunk c of
+// row r at a swizzled position of the row: c ^ ((r / 2) mod 8) for 128-byte
+// rows, c ^ (r mod 16) for 256-byte ones.  The direct loads place the chunks
+// so (whole rows per HD / 8 lanes, i.e. full cache lines), and the MFMA
 // operand reads (lane: one row, one chunk) then hit distinct banks in each
 // 16-lane phase.
-__device__ __forceinline__ int k_swz(int row, int chunk) { return row * kHeadDim + ((chunk ^ (row >> 1)) & 7) * 8; }
+template <int HD>
+__device__ __forceinline__ int swz_key(int row) { return HD == 64 ? row >> 1 : row; }
+template <int HD>
+__device__ __forceinline__ int k_swz(int row, int chunk) {
+    return row * HD + ((chunk ^ swz_key<HD>(row)) & (HD / 8 - 1)) * 8;
+}
 
 // Per-wave LDS.  bf16: the K blocks of a batch (k_swz), V_j (read back
 // transposed) and Q_i; fp32: V_j.
-template <int DT> struct StageBuf;
-template <> struct StageBuf<1> {
-    uint16_t kring[Cfg<1>::kBatch][kBlock * kHeadDim];
-    uint16_t v[kBlock * kVStrideB];
-    uint16_t qs[kBlock * kKStrideB];
+template <int DT, int HD> struct StageBuf;
+template <int HD> struct StageBuf<1, HD> {
+    uint16_t kring[Cfg<1, HD>::kBatch][kBlock * HD];
+    uint16_t v[kBlock * v_stride_b(HD)];
+    uint16_t qs[kBlock * q_stride_b(HD)];
 };
-template <> struct StageBuf<0> {
-    float v[kBlock * kVStrideF];
+template <int HD> struct StageBuf<0, HD> {
+    float v[kBlock * v_stride_f(HD)];
 };
 
 // The attention kernel's dynamic LDS: kWaves StageBufs.  The direct loads
@@ -130,17 +136,19 @@ template <> struct StageBuf<0> {
 // only (and can keep a batch's register slots in registers).
 extern __shared__ __align__(16) unsigned char attn_smem[];
 
-template <int DT>
+// Full mode keeps one low-res value per channel in lanes: channel lane + 64 x,
+// x < HD / 64.
+template <int DT, int HD>
 struct Slot {
-    u32x4 k[Cfg<DT>::kKDirect ? 1 : Cfg<DT>::kKV];   // (unused when K goes straight to LDS)
-    u32x4 v[Cfg<DT>::kKV];
-    u32x4 q[Cfg<DT>::kKV];   // Q of the block's row
-    uint32_t qm;             // and its mask word (segment's first block)
-    float vh;                // full mode: vhat_j[lane]
-    float lo;                // full mode: lo_all_i[lane] (segment's first block)
+    u32x4 k[Cfg<DT, HD>::kKDirect ? 1 : Cfg<DT, HD>::kKV];   // (unused when K goes straight to LDS)
+    u32x4 v[Cfg<DT, HD>::kKV];
+    u32x4 q[Cfg<DT, HD>::kKV];   // Q of the block's row
+    uint32_t qm;                 // and its mask word (segment's first block)
+    float vh[HD / 64];           // full mode: vhat_j at this lane's channels
+    float lo[HD / 64];           // full mode: lo_all_i at this lane's channels (segment's first block)
 };
 
-template <int DT>
+template <int DT, int HD>
 struct Wave {
     // record window: lane t holds the record of block a + t, and in full mode
     // the low-res row max and weight sum of that block's row
@@ -149,9 +157,9 @@ struct Wave {
     int a;
     int bh, b, nb, lane, n, h;
     int wave;                // the wave's index in its workgroup (its StageBuf)
-    const typename Cfg<DT>::Elem* Qg;
-    const typename Cfg<DT>::Elem* Kg;
-    const typename Cfg<DT>::Elem* Vg;
+    const typename Cfg<DT, HD>::Elem* Qg;
+    const typename Cfg<DT, HD>::Elem* Kg;
+    const typename Cfg<DT, HD>::Elem* Vg;
 };
 
 // Issue the loads of stream block e into a batch slot: K_j, V_j, vhat_j at
@@ -160,80 +168,96 @@ struct Wave {
 __device__ __forceinline__ int rec_i(uint32_t ij) { return (int)(ij & 0xFFFFu); }
 __device__ __forceinline__ int rec_j(uint32_t ij) { return (int)(ij >> 16); }
 
-template <int DT, bool FULL>
-__device__ __forceinline__ void issue(const Params& p, const Wave<DT>& W, int e, Slot<DT>& s, StageBuf<DT>& sb,
-                                      int u) {
+template <int DT, int HD, bool FULL>
+__device__ __forceinline__ void issue(const Params& p, const Wave<DT, HD>& W, int e, Slot<DT, HD>& s,
+                                      StageBuf<DT, HD>& sb, int u) {
+    constexpr int kKV = Cfg<DT, HD>::kKV;
     const int we = e - W.a;
     const uint32_t ij = (uint32_t)rl((int)W.wij, we);
     const int i = min(rec_i(ij), W.nb - 1);
     const int j = min(rec_j(ij), W.nb - 1);
     const int lane = W.lane, n = W.n, h = W.h;
     if constexpr (DT == 1) {
-        const uint16_t* Kb = W.Kg + (size_t)j * kBlock * kHeadDim;
-        const uint16_t* Vb = W.Vg + (size_t)j * kBlock * kHeadDim;
-        const uint16_t* Qb = W.Qg + (size_t)i * kBlock * kHeadDim;
-        const int off = (lane >> 3) * kHeadDim + (lane & 7) * 8;
-        // K_j straight into LDS slot u, 1 KiB (8 whole token rows) per load:
-        // lane l fetches the chunk that belongs at position l % 8 of row
-        // 8x + l / 8 (a load of every row's 32-byte operand piece instead
-        // would cost the address unit several times more)
+        constexpr int kRowLanes = HD / 8;           // lanes per 2 HD-byte token row
+        constexpr int kRowsPerLoad = 64 / kRowLanes;
+        const uint16_t* Kb = W.Kg + (size_t)j * kBlock * HD;
+        const uint16_t* Vb = W.Vg + (size_t)j * kBlock * HD;
+        const uint16_t* Qb = W.Qg + (size_t)i * kBlock * HD;
+        const int off = (lane / kRowLanes) * HD + (lane % kRowLanes) * 8;
+        // K_j straight into LDS slot u, 1 KiB (whole token rows) per load:
+        // lane l fetches the chunk that belongs at its LDS position (a load
+        // of every row's 32-byte operand piece instead would cost the
+        // address unit several times more)
         typedef __attribute__((address_space(3))) void lds_void;
-        const size_t kbase = (size_t)W.wave * sizeof(StageBuf<1>) + offsetof(StageBuf<1>, kring) +
-                             (size_t)u * sizeof(sb.kring[0]);
+        using SB = StageBuf<1, HD>;
+        const size_t kbase = (size_t)W.wave * sizeof(SB) + offsetof(SB, kring) + (size_t)u * sizeof(sb.kring[0]);
 #pragma unroll
-        for (int x = 0; x < 4; x++) {
-            const int r = 8 * x + (lane >> 3), c = ((lane & 7) ^ (r >> 1)) & 7;
-            __builtin_amdgcn_global_load_lds(Kb + r * kHeadDim + 8 * c, (lds_void*)(attn_smem + kbase + x * 1024), 16,
-                                             0, 0);
+        for (int x = 0; x < kKV; x++) {
+            const int r = kRowsPerLoad * x + lane / kRowLanes, pos = lane % kRowLanes;
+            const int c = (pos ^ swz_key<HD>(r)) & (kRowLanes - 1);   // the chunk k_swz puts at pos
+            __builtin_amdgcn_global_load_lds(Kb + r * HD + 8 * c, (lds_void*)(attn_smem + kbase + x * 1024), 16, 0, 0);
         }
 #pragma unroll
-        for (int x = 0; x < 4; x++) s.v[x] = *reinterpret_cast<const u32x4*>(Vb + off + 8 * x * kHeadDim);
-        // V_j and Q_i: whole 128-byte token rows per 8 lanes, so every load
-        // is 8 full cache lines; Q_i once per segment, by its first block
-        // (the other blocks leave s.q unset: only a segment's first block reads it)
+        for (int x = 0; x < kKV; x++) s.v[x] = *reinterpret_cast<const u32x4*>(Vb + off + kRowsPerLoad * x * HD);
+        // V_j and Q_i: whole token rows per HD / 8 lanes, so every load is
+        // full cache lines; Q_i once per segment, by its first block (the
+        // other blocks leave s.q unset: only a segment's first block reads it)
         if (info_pos((uint32_t)rl((int)W.winfo, we)) == 0) {
 #pragma unroll
-            for (int x = 0; x < 4; x++) s.q[x] = *reinterpret_cast<const u32x4*>(Qb + off + 8 * x * kHeadDim);
+            for (int x = 0; x < kKV; x++) s.q[x] = *reinterpret_cast<const u32x4*>(Qb + off + kRowsPerLoad * x * HD);
         }
     } else {
-        const float* Kb = W.Kg + (size_t)j * kBlock * kHeadDim;
-        const float* Vb = W.Vg + (size_t)j * kBlock * kHeadDim;
-        const float* Qb = W.Qg + (size_t)i * kBlock * kHeadDim;
+        // lane l: token l % 32, channels HD / 2 * (l / 32) .. + HD / 2 - 1 of K and Q
+        const float* Kb = W.Kg + (size_t)j * kBlock * HD;
+        const float* Vb = W.Vg + (size_t)j * kBlock * HD;
+        const float* Qb = W.Qg + (size_t)i * kBlock * HD;
 #pragma unroll
-        for (int c4 = 0; c4 < 8; c4++) s.k[c4] = *reinterpret_cast<const u32x4*>(Kb + n * kHeadDim + 32 * h + 4 * c4);
+        for (int c4 = 0; c4 < kKV; c4++)
+            s.k[c4] = *reinterpret_cast<const u32x4*>(Kb + n * HD + (HD / 2) * h + 4 * c4);
+        constexpr int kRowLanes = HD / 4;           // lanes per fp32 token row
+        constexpr int kRowsPerLoad = 64 / kRowLanes;
 #pragma unroll
-        for (int x = 0; x < 8; x++)
-            s.v[x] = *reinterpret_cast<const u32x4*>(Vb + ((lane >> 4) + 4 * x) * kHeadDim + (lane & 15) * 4);
+        for (int x = 0; x < kKV; x++)
+            s.v[x] = *reinterpret_cast<const u32x4*>(Vb + (lane / kRowLanes + kRowsPerLoad * x) * HD +
+                                                      (lane % kRowLanes) * 4);
 #pragma unroll
-        for (int c4 = 0; c4 < 8; c4++) s.q[c4] = *reinterpret_cast<const u32x4*>(Qb + n * kHeadDim + 32 * h + 4 * c4);
+        for (int c4 = 0; c4 < kKV; c4++)
+            s.q[c4] = *reinterpret_cast<const u32x4*>(Qb + n * HD + (HD / 2) * h + 4 * c4);
     }
     // once per segment, by its first block: the row's mask word (uniform, so
     // through the scalar cache) and in full mode lo_all_i; every block: vhat_j
     typedef __attribute__((address_space(4))) const uint32_t const_u32;
     if (info_pos((uint32_t)rl((int)W.winfo, we)) == 0) {
         s.qm = *reinterpret_cast<const_u32*>((uintptr_t)(p.mbits + (size_t)W.b * W.nb + i));
-        if constexpr (FULL) s.lo = p.lo_all[((size_t)W.bh * W.nb + i) * kHeadDim + lane];
+        if constexpr (FULL) {
+#pragma unroll
+            for (int x = 0; x < HD / 64; x++) s.lo[x] = p.lo_all[((size_t)W.bh * W.nb + i) * HD + lane + 64 * x];
+        }
     } else {
         s.qm = 0u;
-        s.lo = 0.f;
+#pragma unroll
+        for (int x = 0; x < HD / 64; x++) s.lo[x] = 0.f;
     }
-    if constexpr (FULL) s.vh = p.vhat[((size_t)W.bh * W.nb + j) * kHeadDim + lane];
+    if constexpr (FULL) {
+#pragma unroll
+        for (int x = 0; x < HD / 64; x++) s.vh[x] = p.vhat[((size_t)W.bh * W.nb + j) * HD + lane + 64 * x];
+    }
 }
 
-template <int DT>
+template <int DT, int HD>
 struct Acc {
-    f32x16 o0, o1;
+    f32x16 o[HD / 32];    // O^T, 32 channels per tile
     float mrun, lsum;
-    float corr;   // full mode: sum over the segment's blocks of w vhat_j[lane]
-    float sw;     // full mode: sum of their weights w
-    float lo;     // full mode: lo_all_i[lane] of the segment's row
-    uint32_t qm;  // valid-token mask word of the segment's row
+    float corr[HD / 64];  // full mode: sum over the segment's blocks of w vhat_j at this lane's channels
+    float sw;             // full mode: sum of their weights w
+    float lo[HD / 64];    // full mode: lo_all_i at this lane's channels
+    uint32_t qm;          // valid-token mask word of the segment's row
 };
 
 // Finish a segment: a whole row writes its output, otherwise a partial.
-template <int DT, bool FULL>
-__device__ __forceinline__ void finish_segment(const Params& p, const Wave<DT>& W, const Acc<DT>& A, int we,
-                                               int i, uint32_t info, const Slot<DT>& s, float* lo_lds) {
+template <int DT, int HD, bool FULL>
+__device__ __forceinline__ void finish_segment(const Params& p, const Wave<DT, HD>& W, const Acc<DT, HD>& A, int we,
+                                               int i, uint32_t info, float* lo_lds) {
     const int n = W.n, h = W.h;
     const float ltot = A.lsum + __shfl_xor(A.lsum, 32, 64);
     const int tok = i * kBlock + n;
@@ -243,7 +267,8 @@ __device__ __forceinline__ void finish_segment(const Params& p, const Wave<DT>& 
         float Mu = A.mrun;   // the max that den and the probabilities are relative to
         if constexpr (FULL) {
             // low-res part of the row without the selected blocks, one channel per lane
-            lo_lds[W.lane] = A.lo - A.corr;
+#pragma unroll
+            for (int x = 0; x < HD / 64; x++) lo_lds[W.lane + 64 * x] = A.lo[x] - A.corr[x];
             const float mi2 = __int_as_float(rl(__float_as_int(W.wm), we)) * kLog2e;
             const float ll = fmaxf(__int_as_float(rl(__float_as_int(W.wll), we)) - A.sw, 0.f);
             const float M = fmaxf(A.mrun, mi2);
@@ -262,13 +287,13 @@ __device__ __forceinline__ void finish_segment(const Params& p, const Wave<DT>& 
             p.st_m[st] = Mu == -__builtin_inff() ? 0.f : Mu;
             p.st_linv[st] = inv;
         }
-        const size_t orow = ((size_t)W.bh * p.N + tok) * kHeadDim;
+        const size_t orow = ((size_t)W.bh * p.N + tok) * HD;
 #pragma unroll
-        for (int mt = 0; mt < 2; mt++) {
+        for (int mt = 0; mt < HD / 32; mt++) {
 #pragma unroll
             for (int gq = 0; gq < 4; gq++) {
                 const int d0 = 32 * mt + 8 * gq + 4 * h;
-                const f32x16& oo = mt == 0 ? A.o0 : A.o1;
+                const f32x16& oo = A.o[mt];
                 float v0 = oo[4 * gq] * sa, v1 = oo[4 * gq + 1] * sa;
                 float v2 = oo[4 * gq + 2] * sa, v3 = oo[4 * gq + 3] * sa;
                 if constexpr (FULL) {
@@ -290,13 +315,13 @@ __device__ __forceinline__ void finish_segment(const Params& p, const Wave<DT>& 
         }
     } else {
         const size_t pidx = (size_t)W.bh * p.max_items + min(info_item(info), p.max_items - 1);
-        float* po = p.part_o + (pidx * kBlock + n) * kHeadDim;
+        float* po = p.part_o + (pidx * kBlock + n) * HD;
 #pragma unroll
-        for (int mt = 0; mt < 2; mt++)
+        for (int mt = 0; mt < HD / 32; mt++)
 #pragma unroll
             for (int gq = 0; gq < 4; gq++) {
                 const int d0 = 32 * mt + 8 * gq + 4 * h;
-                const f32x16& oo = mt == 0 ? A.o0 : A.o1;
+                const f32x16& oo = A.o[mt];
                 *reinterpret_cast<float4*>(po + d0) = make_float4(oo[4 * gq], oo[4 * gq + 1], oo[4 * gq + 2], oo[4 * gq + 3]);
             }
         if (h == 0) {
@@ -304,17 +329,19 @@ __device__ __forceinline__ void finish_segment(const Params& p, const Wave<DT>& 
             p.part_ml[pidx * 64 + 32 + n] = ltot;
         }
         if constexpr (FULL) {   // the segment's share of the low-res correction
-            float* pc = p.part_corr + pidx * kCorrStride;
-            pc[W.lane] = A.corr;
-            if (W.lane == 0) pc[kHeadDim] = A.sw;
+            float* pc = p.part_corr + pidx * corr_stride(HD);
+#pragma unroll
+            for (int x = 0; x < HD / 64; x++) pc[W.lane + 64 * x] = A.corr[x];
+            if (W.lane == 0) pc[HD] = A.sw;
         }
     }
 }
 
 // One block of the stream: S^T, online softmax, O^T += V^T P^T.
-template <int DT, bool FULL>
-__device__ __forceinline__ void process(const Params& p, const Wave<DT>& W, int e, Slot<DT>& s, Acc<DT>& A,
-                                        StageBuf<DT>& sb, int u, float scale2) {
+template <int DT, int HD, bool FULL>
+__device__ __forceinline__ void process(const Params& p, const Wave<DT, HD>& W, int e, Slot<DT, HD>& s,
+                                        Acc<DT, HD>& A, StageBuf<DT, HD>& sb, int u, float scale2) {
+    constexpr int kKV = Cfg<DT, HD>::kKV;
     auto* vs = sb.v;
     const int we = e - W.a;
     const int i = min(rec_i((uint32_t)rl((int)W.wij, we)), W.nb - 1);
@@ -325,14 +352,18 @@ __device__ __forceinline__ void process(const Params& p, const Wave<DT>& W, int 
         A.mrun = -__builtin_inff();
         A.qm = s.qm;
         if constexpr (FULL) {
-            A.corr = 0.f;
+#pragma unroll
+            for (int x = 0; x < HD / 64; x++) {
+                A.corr[x] = 0.f;
+                A.lo[x] = s.lo[x];
+            }
             A.sw = 0.f;
-            A.lo = s.lo;
         }
     }
     if constexpr (FULL) {
         const float w = __int_as_float(rl(__float_as_int(W.ww), we));
-        A.corr = __builtin_fmaf(w, s.vh, A.corr);
+#pragma unroll
+        for (int x = 0; x < HD / 64; x++) A.corr[x] = __builtin_fmaf(w, s.vh[x], A.corr[x]);
         A.sw += w;
     }
     f32x16 S;
@@ -343,30 +374,36 @@ __device__ __forceinline__ void process(const Params& p, const Wave<DT>& W, int 
         // region; K_j (already in slot u) and Q are read back one token row
         // per lane (the MFMA operand layout: lane l holds token l % 32,
         // channels 16 kc + 8 (l / 32))
+        constexpr int kRowLanes = HD / 8, kRowsPerLoad = 64 / kRowLanes;
+        constexpr int VS = v_stride_b(HD), QS = q_stride_b(HD);
         uint16_t* qs = sb.qs;
+        const int r0 = lane / kRowLanes, c0 = (lane % kRowLanes) * 8;
 #pragma unroll
-        for (int x = 0; x < 4; x++)
-            *reinterpret_cast<u32x4*>(vs + ((lane >> 3) + 8 * x) * kVStrideB + (lane & 7) * 8) = s.v[x];
+        for (int x = 0; x < kKV; x++)
+            *reinterpret_cast<u32x4*>(vs + (r0 + kRowsPerLoad * x) * VS + c0) = s.v[x];
         if (info_pos(info) == 0) {
 #pragma unroll
-            for (int x = 0; x < 4; x++)
-                *reinterpret_cast<u32x4*>(qs + ((lane >> 3) + 8 * x) * kKStrideB + (lane & 7) * 8) = s.q[x];
+            for (int x = 0; x < kKV; x++)
+                *reinterpret_cast<u32x4*>(qs + (r0 + kRowsPerLoad * x) * QS + c0) = s.q[x];
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-        for (int kc = 0; kc < 4; kc++) {
-            const u32x4 ka = *reinterpret_cast<const u32x4*>(sb.kring[u] + k_swz(n, 2 * kc + h));
-            const u32x4 qa = *reinterpret_cast<const u32x4*>(qs + n * kKStrideB + 16 * kc + 8 * h);
+        for (int kc = 0; kc < HD / 16; kc++) {
+            const u32x4 ka = *reinterpret_cast<const u32x4*>(sb.kring[u] + k_swz<HD>(n, 2 * kc + h));
+            const u32x4 qa = *reinterpret_cast<const u32x4*>(qs + n * QS + 16 * kc + 8 * h);
             S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka), as_bf16x8(qa), S, 0, 0, 0);
         }
     } else {
+        constexpr int kRowLanes = HD / 4, kRowsPerLoad = 64 / kRowLanes;
+        constexpr int VS = v_stride_f(HD);
 #pragma unroll
-        for (int x = 0; x < 8; x++)
-            *reinterpret_cast<u32x4*>(vs + ((lane >> 4) + 4 * x) * kVStrideF + (lane & 15) * 4) = s.v[x];
+        for (int x = 0; x < kKV; x++)
+            *reinterpret_cast<u32x4*>(vs + (lane / kRowLanes + kRowsPerLoad * x) * VS + (lane % kRowLanes) * 4) =
+                s.v[x];
 #pragma unroll
-        for (int c4 = 0; c4 < 8; c4++) {
+        for (int c4 = 0; c4 < kKV; c4++) {
             const float4 kf = __builtin_bit_cast(float4, s.k[c4]);
             const float4 qf = __builtin_bit_cast(float4, s.q[c4]);
             S = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.x, qf.x, S, 0, 0, 0);
@@ -405,7 +442,9 @@ __device__ __forceinline__ void process(const Params& p, const Wave<DT>& W, int 
     A.mrun = mnew;
     if (__ballot(alpha != 1.0f)) {
 #pragma unroll
-        for (int r = 0; r < 16; r++) { A.o0[r] *= alpha; A.o1[r] *= alpha; }
+        for (int mt = 0; mt < HD / 32; mt++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) A.o[mt][r] *= alpha;
     }
     // the LDS writes above precede these reads in the wave's in-order LDS queue
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -422,39 +461,40 @@ __device__ __forceinline__ void process(const Params& p, const Wave<DT>& W, int 
 #pragma unroll
         for (int kc2 = 0; kc2 < 2; kc2++) {
 #pragma unroll
-            for (int mt = 0; mt < 2; mt++) {
+            for (int mt = 0; mt < HD / 32; mt++) {
+                constexpr int VS = v_stride_b(HD);
                 const int col = 32 * mt + 16 * (g16 & 1) + 4 * (s16 & 3);
                 const int row = 16 * kc2 + 4 * h + (s16 >> 2);
-                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vs + row * kVStrideB + col));
-                const i16x4 hi =
-                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vs + (row + 8) * kVStrideB + col));
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vs + row * VS + col));
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vs + (row + 8) * VS + col));
                 const short __attribute__((ext_vector_type(8))) a8 = {lo[0], lo[1], lo[2], lo[3],
                                                                       hi[0], hi[1], hi[2], hi[3]};
                 const bf16x8 av = __builtin_bit_cast(bf16x8, a8);
-                if (mt == 0) A.o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kc2], A.o0, 0, 0, 0);
-                else A.o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kc2], A.o1, 0, 0, 0);
+                A.o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kc2], A.o[mt], 0, 0, 0);
             }
         }
     } else {
+        constexpr int VS = v_stride_f(HD);
 #pragma unroll
         for (int kc = 0; kc < 16; kc++) {
             const int key = (kc >> 2) * 8 + 4 * h + (kc & 3);
-            A.o0 = __builtin_amdgcn_mfma_f32_32x32x2f32(vs[key * kVStrideF + n], S[kc], A.o0, 0, 0, 0);
-            A.o1 = __builtin_amdgcn_mfma_f32_32x32x2f32(vs[key * kVStrideF + 32 + n], S[kc], A.o1, 0, 0, 0);
+#pragma unroll
+            for (int mt = 0; mt < HD / 32; mt++)
+                A.o[mt] = __builtin_amdgcn_mfma_f32_32x32x2f32(vs[key * VS + 32 * mt + n], S[kc], A.o[mt], 0, 0, 0);
         }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     if (info_pos(info) == info_len(info) - 1)
-        finish_segment<DT, FULL>(p, W, A, we, i, info, s, reinterpret_cast<float*>(vs));
+        finish_segment<DT, HD, FULL>(p, W, A, we, i, info, reinterpret_cast<float*>(vs));
 }
 
 
 // Range k of the WPH ranges of head bh's record stream, by one wave.
-template <int DT, bool FULL>
+template <int DT, int HD, bool FULL>
 __device__ __forceinline__ void run_range(const Params& p, int bh, int k, int WPH, int lane, int wave,
-                                          StageBuf<DT>& sb) {
+                                          StageBuf<DT, HD>& sb) {
     // the head's stream: K records (a static layout fills row_ptr[nb] of its
     // capacity K)
     const int64_t K = p.attn_dyn ? min((int64_t)p.row_ptr[(size_t)bh * (p.nb + 1) + p.nb], p.K) : p.K;
@@ -464,7 +504,7 @@ __device__ __forceinline__ void run_range(const Params& p, int bh, int k, int WP
     // block may move back that far
     const int a0 = max(a - kChunk / 2, 0);
     const BlkRec* R = p.recs + (size_t)bh * p.K;
-    Wave<DT> W;
+    Wave<DT, HD> W;
     W.a = a0;
     W.bh = bh;
     W.b = bh / p.H;
@@ -503,8 +543,8 @@ __device__ __forceinline__ void run_range(const Params& p, int bh, int k, int WP
         return;
     }
 
-    const size_t head_off = (size_t)bh * p.N * kHeadDim;
-    using E = typename Cfg<DT>::Elem;
+    const size_t head_off = (size_t)bh * p.N * HD;
+    using E = typename Cfg<DT, HD>::Elem;
     W.Qg = static_cast<const E*>(p.q) + head_off;
     W.Kg = static_cast<const E*>(p.k) + head_off;
     W.Vg = static_cast<const E*>(p.v) + head_off;
@@ -514,28 +554,33 @@ __device__ __forceinline__ void run_range(const Params& p, int bh, int k, int WP
     // batch is computed.  Past the end the last block is fetched again, so
     // every batch issues the same loads and the wait counts stay exact; the
     // second wave on the SIMD computes while this one waits.
-    constexpr int BATCH = Cfg<DT>::kBatch;
-    Acc<DT> A;
+    constexpr int BATCH = Cfg<DT, HD>::kBatch;
+    Acc<DT, HD> A;
     A.mrun = -__builtin_inff();
     A.lsum = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; r++) { A.o0[r] = 0.f; A.o1[r] = 0.f; }   // finite, so alpha = 0 clears them
-    for (int e0 = start; e0 < end; e0 += BATCH) {
-        Slot<DT> sl[BATCH];
+    for (int mt = 0; mt < HD / 32; mt++)
 #pragma unroll
-        for (int u = 0; u < BATCH; u++) issue<DT, FULL>(p, W, min(e0 + u, end - 1), sl[u], sb, u);
+        for (int r = 0; r < 16; r++) A.o[mt][r] = 0.f;   // finite, so alpha = 0 clears them
+    for (int e0 = start; e0 < end; e0 += BATCH) {
+        Slot<DT, HD> sl[BATCH];
+#pragma unroll
+        for (int u = 0; u < BATCH; u++) issue<DT, HD, FULL>(p, W, min(e0 + u, end - 1), sl[u], sb, u);
         // keep the loads together: the scheduler must not sink them into the
         // compute of the batch
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < BATCH; u++)
-            if (e0 + u < end) process<DT, FULL>(p, W, e0 + u, sl[u], A, sb, u, scale2);
+            if (e0 + u < end) process<DT, HD, FULL>(p, W, e0 + u, sl[u], A, sb, u, scale2);
     }
 }
 
-template <int DT, bool FULL>
-__global__ __launch_bounds__(kThreads, 2) void attn_kernel(Params p) {
-    StageBuf<DT>* stage = reinterpret_cast<StageBuf<DT>*>(attn_smem);   // one per wave
+// Two workgroups per CU for 64-channel heads; one for 128-channel heads,
+// whose staged blocks fill the CU's LDS and whose accumulators need the
+// larger register budget.
+template <int DT, int HD, bool FULL>
+__global__ __launch_bounds__(kThreads, HD == 64 ? 2 : 1) void attn_kernel(Params p) {
+    StageBuf<DT, HD>* stage = reinterpret_cast<StageBuf<DT, HD>*>(attn_smem);   // one per wave
     const int xcd = blockIdx.x & 7;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int wx = (blockIdx.x >> 3) * kWaves + wave;      // wave index within its XCD
@@ -544,11 +589,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(Params p) {
         // every wave of the XCD takes range wx of each of the XCD's heads in
         // turn, so the XCD's L2 holds one head's K and V at a time
         if (wx >= WPH) return;
-        for (int bh = xcd; bh < p.BH; bh += 8) run_range<DT, FULL>(p, bh, wx, WPH, lane, wave, stage[wave]);
+        for (int bh = xcd; bh < p.BH; bh += 8) run_range<DT, HD, FULL>(p, bh, wx, WPH, lane, wave, stage[wave]);
     } else {
         const int hm = wx / WPH;
         const int bh = xcd + 8 * hm;
-        if (bh < p.BH) run_range<DT, FULL>(p, bh, wx - hm * WPH, WPH, lane, wave, stage[wave]);
+        if (bh < p.BH) run_range<DT, HD, FULL>(p, bh, wx - hm * WPH, WPH, lane, wave, stage[wave]);
     }
 }
 
@@ -576,23 +621,30 @@ int attn_grid_waves_per_head(int BH, int64_t K) {
 
 // Launch one instantiation with kWaves stage buffers of dynamic LDS (bf16
 // needs more than the 64 KiB of static LDS); the size attribute is set once.
-template <int DT, bool FULL>
+template <int DT, int HD, bool FULL>
 static hipError_t launch_attn_t(const Params& p, unsigned grid, hipStream_t s) {
-    constexpr size_t kLds = kWaves * sizeof(StageBuf<DT>);
-    static const hipError_t a = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_kernel<DT, FULL>),
+    constexpr size_t kLds = kWaves * sizeof(StageBuf<DT, HD>);
+    static const hipError_t a = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_kernel<DT, HD, FULL>),
                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
     if (a != hipSuccess) return a;
-    hipLaunchKernelGGL((attn_kernel<DT, FULL>), dim3(grid), dim3(kThreads), kLds, s, p);
+    hipLaunchKernelGGL((attn_kernel<DT, HD, FULL>), dim3(grid), dim3(kThreads), kLds, s, p);
     return hipGetLastError();
+}
+
+template <int HD>
+static hipError_t launch_attn_hd(const Params& p, unsigned grid, hipStream_t s) {
+    const bool full = p.mode == 0;
+    if (p.dtype == 1) return full ? launch_attn_t<1, HD, true>(p, grid, s) : launch_attn_t<1, HD, false>(p, grid, s);
+    return full ? launch_attn_t<0, HD, true>(p, grid, s) : launch_attn_t<0, HD, false>(p, grid, s);
 }
 
 hipError_t launch_attn(const Params& p, hipStream_t s) {
     const int heads_per_xcd = (p.BH + 7) / 8;
     const int64_t waves_per_xcd = p.attn_seq ? p.attn_wph : (int64_t)heads_per_xcd * p.attn_wph;
     const unsigned grid = (unsigned)(8 * ((waves_per_xcd + kWaves - 1) / kWaves));
-    const bool full = p.mode == 0;
-    if (p.dtype == 1) return full ? launch_attn_t<1, true>(p, grid, s) : launch_attn_t<1, false>(p, grid, s);
-    return full ? launch_attn_t<0, true>(p, grid, s) : launch_attn_t<0, false>(p, grid, s);
+    if (p.d == 64) return launch_attn_hd<64>(p, grid, s);
+    if (p.d == 128) return launch_attn_hd<128>(p, grid, s);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace mra

@@ -17,7 +17,9 @@ constexpr int kHistBits = 12;           // first radix digit of the selection ke
 constexpr int kHistBins = 1 << kHistBits;
 constexpr float kPriorBias = 5000.0f;   // [MRA] step 2: 5e3 bias for forced blocks
 constexpr int kChunk = 16;              // max selected key blocks per segment of a row
-constexpr int kCorrStride = 68;         // floats per segment's low-res correction: 64 channels, weight sum, pad
+constexpr int kMaxHeadDim = 128;        // widest head the forward kernels take
+// floats per segment's low-res correction: hd channels, weight sum, pad
+__host__ __device__ constexpr int corr_stride(int hd) { return hd + 4; }
 constexpr int kSelCap = 4096;           // selection candidates one head's boundary bin may hold
 constexpr int kCandStride = 32;         // u32 per head's candidate counter: one 128-byte line each
 constexpr float kLog2e = 1.4426950408889634f;
@@ -92,7 +94,7 @@ struct Params {
     float* ll_all;         // [BH, nb]    full mode: sum over every key block j of w_ij
     float* part_o;         // [BH, max_items, 32, d] un-normalised high-res numerators
     float* part_ml;        // [BH, max_items, 2, 32] running max (log2 units) and sum
-    float* part_corr;      // [BH, max_items, kCorrStride] full mode: the segment's sum of w vhat_j, then of w
+    float* part_corr;      // [BH, max_items, corr_stride(d)] full mode: the segment's sum of w vhat_j, then of w
     uint64_t* cand;        // [BH, kSelCap] boundary-bin cells found by the pre-marking pass
     uint32_t* ncand;       // [BH, kCandStride] their number, in word 0 (cleared by the pooling kernel)
     // backward (mra_attention_bwd)

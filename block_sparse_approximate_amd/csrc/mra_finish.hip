@@ -30,8 +30,10 @@ constexpr int kRowSlots = 32;   // workgroups per head
 // One listed row, from its descriptor (row i, first segment, segments).
 // Every load the row needs is issued before the first wait; the segments are
 // joined in one pass with a running maximum.
-template <int DT>
+template <int DT, int HD>
 __device__ void merge_row(const Params& p, int bh, int4 dsc, float* lo, float* ll_s) {
+    constexpr int kCh = HD / 8;          // channels per thread
+    constexpr int kF4 = kCh / 4;
     const int nb = p.nb;
     const int b = bh / p.H;
     const int tid = threadIdx.x;
@@ -42,32 +44,32 @@ __device__ void merge_row(const Params& p, int bh, int4 dsc, float* lo, float* l
     const size_t row = (size_t)bh * nb + i;
     const bool full = p.mode == 0;
     const int t = tid >> 3;              // token within the block
-    const int cg = (tid & 7) * 8;        // channels cg .. cg+7
+    const int cg = (tid & 7) * kCh;      // channels cg .. cg + kCh - 1
     const uint32_t qm = p.mbits[(size_t)b * nb + i];
     float lo_in = 0.f, mrow = 0.f;
     if (full) {
-        if (tid <= kHeadDim) lo_in = tid < kHeadDim ? p.lo_all[row * kHeadDim + tid] : p.ll_all[row];
+        if (tid <= HD) lo_in = tid < HD ? p.lo_all[row * HD + tid] : p.ll_all[row];
         mrow = p.rowmax[row];
     }
 
     // high-res segments: running max M (log2 units), numerator acc, denominator den
     float M = -__builtin_inff(), den = 0.f, corr = 0.f;
-    float acc[8];
+    float acc[kCh];
 #pragma unroll
-    for (int e = 0; e < 8; e++) acc[e] = 0.f;
+    for (int e = 0; e < kCh; e++) acc[e] = 0.f;
     for (int c0 = 0; c0 < nit; c0 += kBatch) {
         float mc[kBatch], lc[kBatch], cc[kBatch];
-        float4 oa[kBatch], ob[kBatch];
+        float4 oa[kBatch][kF4];
 #pragma unroll
         for (int c = 0; c < kBatch; c++) {
             const bool ok = c0 + c < nit;
             const size_t it = pbase + (ok ? c0 + c : 0);
             mc[c] = ok ? p.part_ml[it * 64 + t] : -__builtin_inff();
             lc[c] = ok ? p.part_ml[it * 64 + 32 + t] : 0.f;
-            cc[c] = (ok && full && tid <= kHeadDim) ? p.part_corr[it * kCorrStride + tid] : 0.f;
-            const float4* po = reinterpret_cast<const float4*>(p.part_o + (it * kBlock + t) * kHeadDim + cg);
-            oa[c] = ok ? po[0] : make_float4(0.f, 0.f, 0.f, 0.f);
-            ob[c] = ok ? po[1] : make_float4(0.f, 0.f, 0.f, 0.f);
+            cc[c] = (ok && full && tid <= HD) ? p.part_corr[it * corr_stride(HD) + tid] : 0.f;
+            const float4* po = reinterpret_cast<const float4*>(p.part_o + (it * kBlock + t) * HD + cg);
+#pragma unroll
+            for (int x = 0; x < kF4; x++) oa[c][x] = ok ? po[x] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
         float Mb = M;
 #pragma unroll
@@ -76,13 +78,18 @@ __device__ void merge_row(const Params& p, int bh, int4 dsc, float* lo, float* l
             const float s = M == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(M - Mb);
             den *= s;
 #pragma unroll
-            for (int e = 0; e < 8; e++) acc[e] *= s;
+            for (int e = 0; e < kCh; e++) acc[e] *= s;
 #pragma unroll
             for (int c = 0; c < kBatch; c++) {
                 const float f = mc[c] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mc[c] - Mb);
                 den += lc[c] * f;
-                acc[0] += oa[c].x * f; acc[1] += oa[c].y * f; acc[2] += oa[c].z * f; acc[3] += oa[c].w * f;
-                acc[4] += ob[c].x * f; acc[5] += ob[c].y * f; acc[6] += ob[c].z * f; acc[7] += ob[c].w * f;
+#pragma unroll
+                for (int x = 0; x < kF4; x++) {
+                    acc[4 * x] += oa[c][x].x * f;
+                    acc[4 * x + 1] += oa[c][x].y * f;
+                    acc[4 * x + 2] += oa[c][x].z * f;
+                    acc[4 * x + 3] += oa[c][x].w * f;
+                }
             }
             M = Mb;
         }
@@ -92,8 +99,8 @@ __device__ void merge_row(const Params& p, int bh, int4 dsc, float* lo, float* l
     float Mu = M;   // the max that den and the probabilities are relative to
     if (full) {
         // the row's low-res part: lo_all minus the segments' corrections
-        if (tid < kHeadDim) lo[tid] = lo_in - corr;
-        else if (tid == kHeadDim) *ll_s = fmaxf(lo_in - corr, 0.f);
+        if (tid < HD) lo[tid] = lo_in - corr;
+        else if (tid == HD) *ll_s = fmaxf(lo_in - corr, 0.f);
         __syncthreads();
         const float ll = *ll_s, mi2 = mrow * kLog2e;
         const float Mf = fmaxf(M, mi2);
@@ -103,34 +110,39 @@ __device__ void merge_row(const Params& p, int bh, int4 dsc, float* lo, float* l
             den = den * s + ll * f;
             Mu = Mf;
 #pragma unroll
-            for (int e = 0; e < 8; e++) acc[e] = acc[e] * s + lo[cg + e] * f;
+            for (int e = 0; e < kCh; e++) acc[e] = acc[e] * s + lo[cg + e] * f;
         }
     }
     const bool valid = (qm >> t) & 1u;
     const float inv = (valid && den > 0.f) ? 1.0f / den : 0.f;
-    const size_t orow = ((size_t)bh * p.N + (size_t)i * kBlock + t) * kHeadDim + cg;
+    const size_t orow = ((size_t)bh * p.N + (size_t)i * kBlock + t) * HD + cg;
     if ((tid & 7) == 0) {   // the token's softmax statistics, for the backward pass
         const size_t st = (size_t)bh * p.N + (size_t)i * kBlock + t;
         p.st_m[st] = Mu == -__builtin_inff() ? 0.f : Mu;
         p.st_linv[st] = inv;
     }
     if constexpr (DT == 1) {
-        uint4 pk;
-        pk.x = (uint32_t)float_to_bf16(acc[0] * inv) | ((uint32_t)float_to_bf16(acc[1] * inv) << 16);
-        pk.y = (uint32_t)float_to_bf16(acc[2] * inv) | ((uint32_t)float_to_bf16(acc[3] * inv) << 16);
-        pk.z = (uint32_t)float_to_bf16(acc[4] * inv) | ((uint32_t)float_to_bf16(acc[5] * inv) << 16);
-        pk.w = (uint32_t)float_to_bf16(acc[6] * inv) | ((uint32_t)float_to_bf16(acc[7] * inv) << 16);
-        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + orow) = pk;
+#pragma unroll
+        for (int x = 0; x < kCh / 8; x++) {
+            const float* a = acc + 8 * x;
+            uint4 pk;
+            pk.x = (uint32_t)float_to_bf16(a[0] * inv) | ((uint32_t)float_to_bf16(a[1] * inv) << 16);
+            pk.y = (uint32_t)float_to_bf16(a[2] * inv) | ((uint32_t)float_to_bf16(a[3] * inv) << 16);
+            pk.z = (uint32_t)float_to_bf16(a[4] * inv) | ((uint32_t)float_to_bf16(a[5] * inv) << 16);
+            pk.w = (uint32_t)float_to_bf16(a[6] * inv) | ((uint32_t)float_to_bf16(a[7] * inv) << 16);
+            reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + orow)[x] = pk;
+        }
     } else {
         float4* o = reinterpret_cast<float4*>(static_cast<float*>(p.out) + orow);
-        o[0] = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
-        o[1] = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+#pragma unroll
+        for (int x = 0; x < kF4; x++)
+            o[x] = make_float4(acc[4 * x] * inv, acc[4 * x + 1] * inv, acc[4 * x + 2] * inv, acc[4 * x + 3] * inv);
     }
 }
 
-template <int DT>
+template <int DT, int HD>
 __global__ __launch_bounds__(kThreads) void finish_kernel(Params p) {
-    __shared__ __align__(16) float lo[kHeadDim];
+    __shared__ __align__(16) float lo[HD];
     __shared__ float ll;
     const int nb = p.nb;
     const int bh = blockIdx.x / kRowSlots, slot = blockIdx.x - bh * kRowSlots;
@@ -139,20 +151,27 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(Params p) {
     const int nm = min(p.n_merge[bh], nb);
     for (int s = slot; s < nm; s += kRowSlots) {
         if (s != slot) dsc = p.merge_rows[(size_t)bh * nb + s];
-        merge_row<DT>(p, bh, dsc, lo, &ll);
+        merge_row<DT, HD>(p, bh, dsc, lo, &ll);
         __syncthreads();   // lo and ll are reused by the next row
     }
 }
 
 }  // namespace
 
-hipError_t launch_finish(const Params& p, hipStream_t s) {
+template <int HD>
+static hipError_t launch_finish_t(const Params& p, hipStream_t s) {
     const int grid = p.BH * kRowSlots;
     if (p.dtype == 1)
-        hipLaunchKernelGGL(finish_kernel<1>, dim3(grid), dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((finish_kernel<1, HD>), dim3(grid), dim3(kThreads), 0, s, p);
     else
-        hipLaunchKernelGGL(finish_kernel<0>, dim3(grid), dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((finish_kernel<0, HD>), dim3(grid), dim3(kThreads), 0, s, p);
     return hipGetLastError();
+}
+
+hipError_t launch_finish(const Params& p, hipStream_t s) {
+    if (p.d == 64) return launch_finish_t<64>(p, s);
+    if (p.d == 128) return launch_finish_t<128>(p, s);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace mra

@@ -7,25 +7,27 @@
 // order; the mean is that sum divided by (float)count, correctly rounded;
 // an empty block pools to zeros.  Built with -ffp-contract=off.
 //
-// Mapping: a workgroup pools 8 consecutive blocks of one tensor and head,
-// which are one contiguous run of 256 token rows; all workgroups of a head
-// run on the same XCD.  Every thread first issues
-// all of its 16-byte loads of that run (fully coalesced, one round trip),
-// stores them in LDS, and then each thread sums two channels of one block
-// over its 32 rows in token order.
+// Mapping: a workgroup pools 8 consecutive blocks (4 for 128-channel heads)
+// of one tensor and head, which are one contiguous run of token rows; all
+// workgroups of a head run on the same XCD.  Every thread first issues all
+// of its 16-byte loads of that run (fully coalesced, one round trip), stores
+// them in LDS, and then each thread sums two channels of one block over its
+// 32 rows in token order.
 #include "mra_common.h"
 
 namespace mra {
 namespace {
 
 constexpr int kPoolThreads = 256;
-constexpr int kPoolBlocks = 8;   // blocks per workgroup
+// blocks per workgroup: one thread per (block, channel pair)
+__host__ __device__ constexpr int pool_blocks(int hd) { return kPoolThreads / (hd / 2); }
 
-template <int DT>  // 0 = fp32, 1 = bf16
+template <int DT, int HD>  // DT: 0 = fp32, 1 = bf16; HD: channels per head
 __global__ __launch_bounds__(kPoolThreads) void pool_kernel(Params p, int ntens, int groups_per_head,
                                                             int zero_words) {
-    constexpr int kEs = DT == 1 ? 2 : 4;                   // bytes per element
-    constexpr int kBlockBytes = kBlock * kHeadDim * kEs;   // 4 KiB (bf16) or 8 KiB (fp32)
+    constexpr int kPoolBlocks = pool_blocks(HD);
+    constexpr int kEs = DT == 1 ? 2 : 4;              // bytes per element
+    constexpr int kBlockBytes = kBlock * HD * kEs;    // 4 to 16 KiB
     constexpr int kLoads = kPoolBlocks * kBlockBytes / 16 / kPoolThreads;
     __shared__ __align__(16) unsigned char tile[kPoolBlocks * kBlockBytes];
 
@@ -53,7 +55,7 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(Params p, int ntens,
     const int tid = threadIdx.x;
 
     const unsigned char* src = static_cast<const unsigned char*>(tens == 0 ? p.q : (tens == 1 ? p.k : p.v)) +
-                               ((size_t)bh * p.N + (size_t)blk0 * kBlock) * kHeadDim * kEs;
+                               ((size_t)bh * p.N + (size_t)blk0 * kBlock) * HD * kEs;
     uint4 v[kLoads];
 #pragma unroll
     for (int e = 0; e < kLoads; e++) {
@@ -64,7 +66,7 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(Params p, int ntens,
     for (int e = 0; e < kLoads; e++) *reinterpret_cast<uint4*>(tile + (tid + e * kPoolThreads) * 16) = v[e];
 
     // thread -> (block bk, channel pair cp)
-    const int bk = tid >> 5, cp = tid & 31;
+    const int bk = tid / (HD / 2), cp = tid % (HD / 2);
     const int blk = blk0 + bk;
     uint32_t bits = 0xFFFFFFFFu;
     if (p.mask && bk < nblk) {
@@ -88,11 +90,11 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(Params p, int ntens,
     for (int t = 0; t < kBlock; t++) {
         float x0, x1;
         if constexpr (DT == 1) {
-            const uint32_t w = *reinterpret_cast<const uint32_t*>(col + t * kHeadDim * kEs);
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(col + t * HD * kEs);
             x0 = __uint_as_float(w << 16);
             x1 = __uint_as_float(w & 0xFFFF0000u);
         } else {
-            const float2 w = *reinterpret_cast<const float2*>(col + t * kHeadDim * kEs);
+            const float2 w = *reinterpret_cast<const float2*>(col + t * HD * kEs);
             x0 = w.x;
             x1 = w.y;
         }
@@ -103,23 +105,31 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(Params p, int ntens,
     }
     const float fc = (float)count;
     float* dst = tens == 0 ? p.qhat : (tens == 1 ? p.khat : p.vhat);
-    *reinterpret_cast<float2*>(dst + ((size_t)bh * p.nb + blk) * kHeadDim + 2 * cp) =
+    *reinterpret_cast<float2*>(dst + ((size_t)bh * p.nb + blk) * HD + 2 * cp) =
         count > 0 ? make_float2(a0 / fc, a1 / fc) : make_float2(0.0f, 0.0f);
 }
 
 }  // namespace
 
-hipError_t launch_pool(const Params& p, hipStream_t s) {
+template <int HD>
+static hipError_t launch_pool_t(const Params& p, hipStream_t s) {
     const int ntens = p.mode == 0 ? 3 : 2;
-    const int groups_per_head = (p.nb + kPoolBlocks - 1) / kPoolBlocks;
+    const int groups_per_head = (p.nb + pool_blocks(HD) - 1) / pool_blocks(HD);
     const int grid = 8 * ((p.BH + 7) / 8) * ntens * groups_per_head;
     const int zero_words = p.BH * kHistBins;
-    if (p.d != kHeadDim) return hipErrorInvalidValue;
     if (p.dtype == 1)
-        hipLaunchKernelGGL(pool_kernel<1>, dim3(grid), dim3(kPoolThreads), 0, s, p, ntens, groups_per_head, zero_words);
+        hipLaunchKernelGGL((pool_kernel<1, HD>), dim3(grid), dim3(kPoolThreads), 0, s, p, ntens, groups_per_head,
+                           zero_words);
     else
-        hipLaunchKernelGGL(pool_kernel<0>, dim3(grid), dim3(kPoolThreads), 0, s, p, ntens, groups_per_head, zero_words);
+        hipLaunchKernelGGL((pool_kernel<0, HD>), dim3(grid), dim3(kPoolThreads), 0, s, p, ntens, groups_per_head,
+                           zero_words);
     return hipGetLastError();
+}
+
+hipError_t launch_pool(const Params& p, hipStream_t s) {
+    if (p.d == 64) return launch_pool_t<64>(p, s);
+    if (p.d == 128) return launch_pool_t<128>(p, s);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace mra

@@ -63,19 +63,20 @@ struct LogitsLds {
 };
 
 constexpr int kMaxColTiles = 4;   // column tiles of kCT key blocks (N <= 16384)
-constexpr int kVtStride = 68;     // floats per staged vhat row (64 + 4 pad)
-constexpr int kHatStride = 68;    // floats per staged qhat / khat row: lane l's 16-byte reads of row l
+// floats per staged qhat / khat / vhat row of a head of hd channels (4 floats
+// of pad: lane l's 16-byte reads of row l spread over the banks)
+__host__ __device__ constexpr int hat_stride(int hd) { return hd + 4; }
                                   // fall on banks 4l .. 4l + 3, distinct over each 16-lane phase
 
 // Rows of the low-res weight tile: nb + 4 floats (the pad spreads the rows
 // over the LDS banks for the MFMA operand reads).
 __host__ __device__ inline int wl_stride(int nb) { return nb + 4; }
 
-__host__ __device__ inline LogitsLds logits_lds(int nb) {
+__host__ __device__ inline LogitsLds logits_lds(int nb, int hd) {
     LogitsLds L;
     size_t o = 0;
-    L.qS = o; o = align16(o + (size_t)kRT * kHatStride * 4);   // qhat rows of the workgroup
-    L.kS = o; o = align16(o + (size_t)kCT * kHatStride * 4);   // khat rows of one column tile
+    L.qS = o; o = align16(o + (size_t)kRT * hat_stride(hd) * 4);   // qhat rows of the workgroup
+    L.kS = o; o = align16(o + (size_t)kCT * hat_stride(hd) * 4);   // khat rows of one column tile
     L.hist = o; o = align16(o + kHistBins * 4);
     L.total = o;
     return L;
@@ -314,27 +315,16 @@ __device__ __forceinline__ void mark_cells(const uint32_t* __restrict__ G, uint3
     }
 }
 
-// A [kCT][kHeadDim] tile of vhat starting at key block j0 into registers:
-// float4 x = threadIdx.x + e * kLgThreads is block j0 + x / 16, channels
-// 4 * (x % 16) .. +3.
-__device__ __forceinline__ void fetch_vhat(const float* __restrict__ vh, int j0, int nb,
-                                           float4 (&vv)[kCT * (kHeadDim / 4) / kLgThreads]) {
-#pragma unroll
-    for (int e = 0; e < kCT * (kHeadDim / 4) / kLgThreads; e++) {
-        const int x = threadIdx.x + e * kLgThreads, j = j0 + (x >> 4);
-        vv[e] = j < nb ? *reinterpret_cast<const float4*>(vh + (size_t)j * kHeadDim + (x & 15) * 4)
-                       : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-}
-
 // The khat tile of key blocks j0 .. j0 + kCT - 1 into registers: float4 x is
-// block j0 + x / 16, channels 4 * (x % 16) .. +3 (16 lanes read one row).
+// block j0 + x / (HD / 4), channels 4 * (x % (HD / 4)) .. +3 (HD / 4 lanes
+// read one row).
+template <int HD>
 __device__ __forceinline__ void fetch_khat(const float* __restrict__ kh, int j0, int nb,
-                                           float4 (&kv)[kCT * (kHeadDim / 4) / kLgThreads]) {
+                                           float4 (&kv)[kCT * (HD / 4) / kLgThreads]) {
 #pragma unroll
-    for (int e = 0; e < kCT * (kHeadDim / 4) / kLgThreads; e++) {
-        const int x = threadIdx.x + e * kLgThreads, jj = x >> 4, c4 = (x & 15) * 4;
-        kv[e] = j0 + jj < nb ? *reinterpret_cast<const float4*>(kh + (size_t)(j0 + jj) * kHeadDim + c4)
+    for (int e = 0; e < kCT * (HD / 4) / kLgThreads; e++) {
+        const int x = threadIdx.x + e * kLgThreads, jj = x / (HD / 4), c4 = (x % (HD / 4)) * 4;
+        kv[e] = j0 + jj < nb ? *reinterpret_cast<const float4*>(kh + (size_t)(j0 + jj) * HD + c4)
                              : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 }
@@ -404,8 +394,9 @@ __device__ __forceinline__ void mark_cells_fast(int nb, int words, uint32_t magi
 // cell's chain still going over the channels in order.
 // kGiven: the logits are already in p.logits (selector hook); skip their
 // computation and only form row maxima, keys and the histogram.
-template <bool kGiven>
+template <bool kGiven, int HD>
 __global__ __launch_bounds__(kLgThreads) void logits_kernel(Params p) {
+    constexpr int kHatStride = hat_stride(HD);
     extern __shared__ __align__(16) unsigned char smem[];
     const int nb = p.nb;
     const int tiles_per_head = (nb + kRT - 1) / kRT;
@@ -419,27 +410,27 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(Params p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float tau = (float)(1.0 / __builtin_sqrt((double)p.dscale));
     const int ntile = (nb + kCT - 1) / kCT;
-    const LogitsLds L = logits_lds(nb);
+    const LogitsLds L = logits_lds(nb, HD);
     float* qS = reinterpret_cast<float*>(smem + L.qS);
     float* kS = reinterpret_cast<float*>(smem + L.kS);
     uint32_t* hist = reinterpret_cast<uint32_t*>(smem + L.hist);
-    const float* qh = p.qhat + (size_t)bh * nb * kHeadDim;
-    const float* kh = p.khat + (size_t)bh * nb * kHeadDim;
+    const float* qh = p.qhat + (size_t)bh * nb * HD;
+    const float* kh = p.khat + (size_t)bh * nb * HD;
     const int* cnt = p.cnt + (size_t)b * nb;
     const int ra = row0 + 2 * wave, rb = ra + 1;
 
     // every global load of the prologue first, then the LDS stores
-    constexpr int kKLoads = kCT * (kHeadDim / 4) / kLgThreads;   // float4s of one khat tile per thread
+    constexpr int kKLoads = kCT * (HD / 4) / kLgThreads;   // float4s of one khat tile per thread
     float4 qv = make_float4(0.f, 0.f, 0.f, 0.f);
     float4 kv[kKLoads];
     float sc[kMaxColTiles][4];   // logits of (ra, j), (ra, j + 64), (rb, j), (rb, j + 64), j = 128 t + lane
     int2 cj[kMaxColTiles];       // counts of key blocks j and j + 64
     if (!kGiven) {
-        if (tid < kRT * kHeadDim / 4) {
-            const int r = tid / (kHeadDim / 4), c4 = (tid % (kHeadDim / 4)) * 4;
-            if (row0 + r < nb) qv = *reinterpret_cast<const float4*>(qh + (size_t)(row0 + r) * kHeadDim + c4);
+        if (tid < kRT * HD / 4) {
+            const int r = tid / (HD / 4), c4 = (tid % (HD / 4)) * 4;
+            if (row0 + r < nb) qv = *reinterpret_cast<const float4*>(qh + (size_t)(row0 + r) * HD + c4);
         }
-        fetch_khat(kh, 0, nb, kv);
+        fetch_khat<HD>(kh, 0, nb, kv);
     }
 #pragma unroll
     for (int t = 0; t < kMaxColTiles; t++) {
@@ -456,8 +447,8 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(Params p) {
     }
     const int cia = ra < nb ? cnt[ra] : 0, cib = rb < nb ? cnt[rb] : 0;
     for (int x = tid; x < kHistBins; x += kLgThreads) hist[x] = 0u;
-    if (!kGiven && tid < kRT * kHeadDim / 4) {
-        const int r = tid / (kHeadDim / 4), c4 = (tid % (kHeadDim / 4)) * 4;
+    if (!kGiven && tid < kRT * HD / 4) {
+        const int r = tid / (HD / 4), c4 = (tid % (HD / 4)) * 4;
         *reinterpret_cast<float4*>(qS + r * kHatStride + c4) = qv;
     }
     __syncthreads();
@@ -475,13 +466,13 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(Params p) {
 #pragma unroll
                 for (int e = 0; e < kKLoads; e++) {
                     const int x = tid + e * kLgThreads;
-                    *reinterpret_cast<float4*>(kS + (x >> 4) * kHatStride + (x & 15) * 4) = kv[e];
+                    *reinterpret_cast<float4*>(kS + (x / (HD / 4)) * kHatStride + (x % (HD / 4)) * 4) = kv[e];
                 }
                 __syncthreads();
-                if (t + 1 < ntile) fetch_khat(kh, (t + 1) * kCT, nb, kv);   // in flight during this tile
+                if (t + 1 < ntile) fetch_khat<HD>(kh, (t + 1) * kCT, nb, kv);   // in flight during this tile
                 float a00 = 0.f, a01 = 0.f, a10 = 0.f, a11 = 0.f;
 #pragma unroll 4
-                for (int c = 0; c < kHeadDim; c += 4) {
+                for (int c = 0; c < HD; c += 4) {
                     const float4 x0 = *reinterpret_cast<const float4*>(k0 + c);
                     const float4 x1 = *reinterpret_cast<const float4*>(k1 + c);
                     const float4 ya = *reinterpret_cast<const float4*>(qa + c);
@@ -573,30 +564,36 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(Params p) {
 // vhat[k = l / 16][l % 16], and accumulator e of lane l is row 4 (l / 16) + e,
 // channel l % 16.
 constexpr int kLoRows = 32;
+// key blocks per staged vhat tile: 128 for 64-channel heads, 64 for 128
+__host__ __device__ constexpr int lowres_keys(int hd) { return hd == 64 ? kCT : kCT / 2; }
 
-__host__ __device__ inline size_t lowres_lds(int nb) {
-    return align16((size_t)kLoRows * wl_stride(nb) * 4) + align16((size_t)kCT * kVtStride * 4) +
+__host__ __device__ inline size_t lowres_lds(int nb, int hd) {
+    return align16((size_t)kLoRows * wl_stride(nb) * 4) + align16((size_t)lowres_keys(hd) * hat_stride(hd) * 4) +
            align16(2 * 8 * 64 * 4 * 4);
 }
 
+template <int HD>
 __device__ __forceinline__ void lowres_rows(const Params& p, int bh, int row0, unsigned char* smem) {
+    constexpr int kVtStride = hat_stride(HD);
+    constexpr int kKT = lowres_keys(HD);     // key blocks per vhat tile
+    constexpr int kCTW = HD / 64;            // 16-channel tiles per wave
     const int nb = p.nb, nbp = wl_stride(nb);
     const int b = bh / p.H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     float* wl = reinterpret_cast<float*>(smem);
     float* vt = reinterpret_cast<float*>(smem + align16((size_t)kLoRows * nbp * 4));
-    float* red = vt + align16((size_t)kCT * kVtStride * 4) / 4;
+    float* red = vt + align16((size_t)kKT * kVtStride * 4) / 4;
     const float* S = p.logits + (size_t)bh * nb * nb;
-    const float* vh = p.vhat + (size_t)bh * nb * kHeadDim;
+    const float* vh = p.vhat + (size_t)bh * nb * HD;
     const int* cnt = p.cnt + (size_t)b * nb;
-    constexpr int kVLoads = kCT * (kHeadDim / 4) / kSelThreads;   // float4s of one vhat tile per thread
+    constexpr int kVLoads = kKT * (HD / 4) / kSelThreads;   // float4s of one vhat tile per thread
 
     // vhat tile 0 in flight first; the weights: wave w owns rows 2w, 2w + 1
     float4 vv[kVLoads];
 #pragma unroll
     for (int e = 0; e < kVLoads; e++) {
-        const int x = tid + e * kSelThreads, j = x >> 4;
-        vv[e] = j < nb ? *reinterpret_cast<const float4*>(vh + (size_t)j * kHeadDim + (x & 15) * 4)
+        const int x = tid + e * kSelThreads, j = x / (HD / 4);
+        vv[e] = j < nb ? *reinterpret_cast<const float4*>(vh + (size_t)j * HD + (x % (HD / 4)) * 4)
                        : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     constexpr int kJ = kMaxColTiles * kCT / 64;   // key blocks per lane (nb <= 512)
@@ -631,44 +628,59 @@ __device__ __forceinline__ void lowres_rows(const Params& p, int bh, int row0, u
         if (ia < nb) p.ll_all[(size_t)bh * nb + ia] = la;
         if (ib < nb) p.ll_all[(size_t)bh * nb + ib] = lb;
     }
+    // wave w: row tile w / 8, 16-channel tiles c = (w / 2) % 4 + 4 x (x < HD / 64),
+    // key half w % 2
     const int rt = wave >> 3, ct = (wave >> 1) & 3, kh2 = wave & 1;
     typedef float f32x4 __attribute__((ext_vector_type(4)));
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int j0 = 0; j0 < nb; j0 += kCT) {
+    f32x4 acc[kCTW];
+#pragma unroll
+    for (int x = 0; x < kCTW; x++) acc[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < nb; j0 += kKT) {
         __syncthreads();   // the weights are in place; every wave is done with the previous tile
 #pragma unroll
         for (int e = 0; e < kVLoads; e++) {
             const int x = tid + e * kSelThreads;
-            *reinterpret_cast<float4*>(vt + (x >> 4) * kVtStride + (x & 15) * 4) = vv[e];
+            *reinterpret_cast<float4*>(vt + (x / (HD / 4)) * kVtStride + (x % (HD / 4)) * 4) = vv[e];
         }
         __syncthreads();
-        if (j0 + kCT < nb) {
+        if (j0 + kKT < nb) {
 #pragma unroll
             for (int e = 0; e < kVLoads; e++) {
-                const int x = tid + e * kSelThreads, j = j0 + kCT + (x >> 4);
-                vv[e] = j < nb ? *reinterpret_cast<const float4*>(vh + (size_t)j * kHeadDim + (x & 15) * 4)
+                const int x = tid + e * kSelThreads, j = j0 + kKT + x / (HD / 4);
+                vv[e] = j < nb ? *reinterpret_cast<const float4*>(vh + (size_t)j * HD + (x % (HD / 4)) * 4)
                                : make_float4(0.f, 0.f, 0.f, 0.f);
             }
         }
-        const int jn = min(kCT, nb - j0);
+        const int jn = min(kKT, nb - j0);
 #pragma unroll
-        for (int k4 = 0; k4 < kCT / 2; k4 += 4) {
-            const int k = kh2 * (kCT / 2) + k4 + (lane >> 4);
+        for (int k4 = 0; k4 < kKT / 2; k4 += 4) {
+            const int k = kh2 * (kKT / 2) + k4 + (lane >> 4);
             const bool ok = k < jn;
             const float a = ok ? wl[(rt * 16 + (lane & 15)) * nbp + j0 + k] : 0.f;
-            const float bv = ok ? vt[k * kVtStride + ct * 16 + (lane & 15)] : 0.f;
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, acc, 0, 0, 0);
+#pragma unroll
+            for (int x = 0; x < kCTW; x++) {
+                const float bv = ok ? vt[k * kVtStride + (ct + 4 * x) * 16 + (lane & 15)] : 0.f;
+                acc[x] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, acc[x], 0, 0, 0);
+            }
         }
     }
-    const int tile = rt * 4 + ct;   // 0..7
-    if (kh2 == 1) *reinterpret_cast<f32x4*>(red + (tile * 64 + lane) * 4) = acc;
+#pragma unroll
+    for (int x = 0; x < kCTW; x++) {
+        const int tile = rt * 4 + ct + 8 * x;   // 0 .. 8 kCTW - 1
+        if (kh2 == 1) *reinterpret_cast<f32x4*>(red + (tile * 64 + lane) * 4) = acc[x];
+    }
     __syncthreads();
     if (kh2 == 0) {
-        const f32x4 o = *reinterpret_cast<const f32x4*>(red + (tile * 64 + lane) * 4);
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-            const int row = row0 + rt * 16 + 4 * (lane >> 4) + e;
-            if (row < nb) p.lo_all[((size_t)bh * nb + row) * kHeadDim + ct * 16 + (lane & 15)] = acc[e] + o[e];
+        for (int x = 0; x < kCTW; x++) {
+            const int tile = rt * 4 + ct + 8 * x;
+            const f32x4 o = *reinterpret_cast<const f32x4*>(red + (tile * 64 + lane) * 4);
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int row = row0 + rt * 16 + 4 * (lane >> 4) + e;
+                if (row < nb)
+                    p.lo_all[((size_t)bh * nb + row) * HD + (ct + 4 * x) * 16 + (lane & 15)] = acc[x][e] + o[e];
+            }
         }
     }
 }
@@ -867,7 +879,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
         const int g = blockIdx.x - bh_pad, xcd = g & 7, slot = g >> 3;
         const int tiles = (nb + kLoRows - 1) / kLoRows;
         const int hm = slot / tiles, lbh = xcd + 8 * hm;
-        if (lbh < p.BH) lowres_rows(p, lbh, (slot - hm * tiles) * kLoRows, smem);
+        if (lbh < p.BH) {
+            if (p.d == 128) lowres_rows<128>(p, lbh, (slot - hm * tiles) * kLoRows, smem);
+            else lowres_rows<64>(p, lbh, (slot - hm * tiles) * kLoRows, smem);
+        }
         return;
     }
     const int bh = blockIdx.x;
@@ -1107,20 +1122,24 @@ __global__ __launch_bounds__(kSelThreads) void bigbird_layout_kernel(Params p) {
 
 }  // namespace
 
-template <bool kGiven>
+template <bool kGiven, int HD>
 static hipError_t launch_logits_t(const Params& p, hipStream_t s) {
     const int tiles_per_head = (p.nb + kRT - 1) / kRT;
-    static const hipError_t a1 = hipFuncSetAttribute(reinterpret_cast<const void*>(&logits_kernel<kGiven>),
+    static const hipError_t a1 = hipFuncSetAttribute(reinterpret_cast<const void*>(&logits_kernel<kGiven, HD>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (a1 != hipSuccess) return a1;
     const int heads_per_xcd = (p.BH + 7) / 8;
-    hipLaunchKernelGGL(logits_kernel<kGiven>, dim3(8 * heads_per_xcd * tiles_per_head), dim3(kLgThreads),
-                       logits_lds(p.nb).total, s, p);
+    hipLaunchKernelGGL((logits_kernel<kGiven, HD>), dim3(8 * heads_per_xcd * tiles_per_head), dim3(kLgThreads),
+                       logits_lds(p.nb, HD).total, s, p);
     return hipGetLastError();
 }
 
-hipError_t launch_logits(const Params& p, hipStream_t s) { return launch_logits_t<false>(p, s); }
-hipError_t launch_logits_given(const Params& p, hipStream_t s) { return launch_logits_t<true>(p, s); }
+hipError_t launch_logits(const Params& p, hipStream_t s) {
+    return p.d == 128 ? launch_logits_t<false, 128>(p, s) : launch_logits_t<false, 64>(p, s);
+}
+hipError_t launch_logits_given(const Params& p, hipStream_t s) {
+    return p.d == 128 ? launch_logits_t<true, 128>(p, s) : launch_logits_t<true, 64>(p, s);
+}
 
 hipError_t launch_premark(const Params& p, hipStream_t s) {
     if (!premarked(p.nb)) return hipSuccess;
@@ -1138,7 +1157,7 @@ hipError_t launch_select(const Params& p, hipStream_t s) {
     const int bh_pad = 8 * ((p.BH + 7) / 8);
     const int lowres_wgs = p.mode == 0 ? bh_pad * ((p.nb + kLoRows - 1) / kLoRows) : 0;
     size_t lds = select_lds(p.nb).total;
-    if (p.mode == 0 && lowres_lds(p.nb) > lds) lds = lowres_lds(p.nb);
+    if (p.mode == 0 && lowres_lds(p.nb, p.d) > lds) lds = lowres_lds(p.nb, p.d);
     hipLaunchKernelGGL(select_kernel, dim3(bh_pad + lowres_wgs), dim3(kSelThreads), lds, s, p);
     return hipGetLastError();
 }

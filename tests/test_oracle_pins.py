@@ -375,6 +375,28 @@ def test_brute_force_materialisation(mode, bpr, pf, pd, masked):
         np.testing.assert_allclose(out[0, h], ref, rtol=0, atol=1e-12)
 
 
+# 128-channel heads: nothing in the oracle is tied to 64 channels
+@pytest.mark.parametrize("mode", ["full", "sparse"])
+def test_head128_all_blocks_selected_equals_dense(mode):
+    q, k, v = rand_qkv(1, 2, 256, d=128, seed=37)
+    out = oracle.mra_forward(q, k, v, block_per_row=8, approx_mode=mode)
+    np.testing.assert_allclose(out, sdpa64(q, k, v), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("mode,pf,pd,masked", [("full", 0, 1, True), ("sparse", 1, 3, False)])
+def test_head128_brute_force_materialisation(mode, pf, pd, masked):
+    N = 256
+    q, k, v = rand_qkv(1, 2, N, d=128, seed=43)
+    mask = None
+    if masked:
+        mask = (np.random.default_rng(6).random((1, N)) < 0.8).astype(np.uint8)
+    out, sel = oracle.mra_forward(q, k, v, mask, block_per_row=2, approx_mode=mode, prior_first=pf, prior_diag=pd,
+                                  return_selection=True)
+    for h in range(2):
+        ref = brute_force(q[0, h], k[0, h], v[0, h], None if mask is None else mask[0], sel[0, h], mode)
+        np.testing.assert_allclose(out[0, h], ref, rtol=0, atol=1e-12)
+
+
 # ------------------------------------------------------------- invariants ---
 @pytest.mark.parametrize("mode", ["full", "sparse"])
 def test_value_shift_and_scale_invariance(mode):
