@@ -45,6 +45,9 @@ class MraAttentionFunction(torch.autograd.Function):
     @staticmethod
     def backward(ctx, dout):
         q, k, v, out, ws, mask = ctx.saved_tensors
+        if q.shape[-1] != 64:
+            raise NotImplementedError("the backward kernels take heads of at most 64 channels; "
+                                      "heads of 65 to 128 channels run forward only")
         mask = mask if ctx.has_mask else None
         block_per_row, approx_mode, prior_first, prior_diag, scale_dim = ctx.args
         B, H, N, d = q.shape
@@ -58,19 +61,22 @@ class MraAttentionFunction(torch.autograd.Function):
 
 def mra_attention(q, k, v, mask=None, block_per_row=4, approx_mode="full", initial_prior_first_n_blocks=0,
                   initial_prior_diagonal_n_blocks=0, score_ranking="row_normalized"):
-    """Differentiable MRA-2 attention on [batch, heads, seq_len, d] device
-    tensors, d <= 64; mask is uint8 [batch, seq_len] (1 = valid) or None.
-    Heads narrower than 64 go to the kernels zero-padded to 64 channels with
-    the logit scale of their own size ([MRA] engineering notes: the model
-    pads small heads for the kernels; the zero channels change no sum), and
-    the output is cut back to d channels."""
+    """MRA-2 attention on [batch, heads, seq_len, d] device tensors, d <= 128;
+    mask is uint8 [batch, seq_len] (1 = valid) or None.  Differentiable for
+    d <= 64 (the backward kernels take 64 channels); heads of 65 to 128
+    channels run forward only.  Heads narrower than the kernels' 64 or 128
+    channels go to them zero-padded, with the logit scale of their own size
+    ([MRA] engineering notes: the model pads small heads for the kernels;
+    the zero channels change no sum), and the output is cut back to d
+    channels."""
     d = q.shape[-1]
-    if d > 64:
-        raise ValueError("head_dim above 64 is not supported")
-    if d == 64:
+    if d > 128:
+        raise ValueError("head_dim above 128 is not supported")
+    hd = 64 if d <= 64 else 128
+    if d == hd:
         return MraAttentionFunction.apply(q, k, v, mask, block_per_row, approx_mode, initial_prior_first_n_blocks,
                                           initial_prior_diagonal_n_blocks, score_ranking, 0)
-    pad = lambda t: F.pad(t, (0, 64 - d)).contiguous()
+    pad = lambda t: F.pad(t, (0, hd - d)).contiguous()
     out = MraAttentionFunction.apply(pad(q), pad(k), pad(v), mask, block_per_row, approx_mode,
                                      initial_prior_first_n_blocks, initial_prior_diagonal_n_blocks, score_ranking, d)
     return out[..., :d]
@@ -82,14 +88,13 @@ class MraSelfAttention(torch.nn.Module):
     block_per_row, approx_mode, initial_prior_first_n_blocks,
     initial_prior_diagonal_n_blocks; score_ranking picks what step 2 ranks
     ("row_normalized" or "raw_logits").  head_dim = hidden_size / heads may
-    be at most 64 (the kernels' head size; narrower heads are zero-padded,
-    see mra_attention)."""
+    be at most 128, and at most 64 for training (see mra_attention)."""
 
     def __init__(self, hidden_size=768, num_attention_heads=12, block_per_row=4, approx_mode="full",
                  initial_prior_first_n_blocks=0, initial_prior_diagonal_n_blocks=0, score_ranking="row_normalized"):
         super().__init__()
-        if hidden_size % num_attention_heads != 0 or not 1 <= hidden_size // num_attention_heads <= 64:
-            raise ValueError("hidden_size / num_attention_heads must be a whole number from 1 to 64")
+        if hidden_size % num_attention_heads != 0 or not 1 <= hidden_size // num_attention_heads <= 128:
+            raise ValueError("hidden_size / num_attention_heads must be a whole number from 1 to 128")
         self.num_attention_heads = num_attention_heads
         self.head_dim = hidden_size // num_attention_heads
         self.query = torch.nn.Linear(hidden_size, hidden_size)

@@ -57,6 +57,22 @@ def test_function_forward_and_gradients_match_oracle(layer, mode):
         close(name, t.grad.float().cpu().numpy(), r)
 
 
+@pytest.mark.parametrize("d", [96, 128])
+def test_wide_heads_forward_match_oracle_and_refuse_backward(layer, d):
+    # heads of 65 to 128 channels: zero-padded to the 128-channel kernels
+    # with their own logit scale; forward only
+    w = workloads.iid("wide-%d" % d, 1, 2, 512, d=d, dtype="bf16", seed=d, scale=0.7, block_per_row=3,
+                      approx_mode="full", prior_diag=1)
+    q, k, v = (bf16_dev(x).requires_grad_(True) for x in (w.q, w.k, w.v))
+    out = layer.mra_attention(q, k, v, None, w.block_per_row, "full", 0, w.prior_diag)
+    ref = oracle.mra_forward(w.q, w.k, w.v, None, w.block_per_row, "full", 0, w.prior_diag)
+    assert out.shape == q.shape
+    err = np.abs(out.detach().float().cpu().numpy() - ref)
+    assert err.max() <= 2e-2 and err.sum() / np.abs(ref).sum() <= 1e-2
+    with pytest.raises(NotImplementedError):
+        out.sum().backward()
+
+
 def test_self_attention_pads_to_a_block_multiple(layer):
     torch.manual_seed(0)
     B, N, hidden = 2, 100, 128

@@ -5,9 +5,11 @@ import torch
 from block_sparse_approximate_amd import layer
 
 
-def test_head_size_at_most_64():
+def test_head_size_at_most_128():
     with pytest.raises(ValueError):
-        layer.MraSelfAttention(hidden_size=256, num_attention_heads=2)     # 128
+        layer.MraSelfAttention(hidden_size=512, num_attention_heads=2)     # 256
+    assert layer.MraSelfAttention(hidden_size=256, num_attention_heads=2).head_dim == 128
+    assert layer.MraSelfAttention(hidden_size=288, num_attention_heads=3).head_dim == 96
     with pytest.raises(ValueError):
         layer.MraSelfAttention(hidden_size=250, num_attention_heads=4)     # not whole
     assert layer.MraSelfAttention(hidden_size=256, num_attention_heads=4).head_dim == 64
