@@ -47,7 +47,7 @@ Besides tokens/s the line carries:
     (mra_bigbird_bwd) timed the same way;
   * `head128`: the forward pass on 128-channel heads (B=2, H=12, N=4096,
     bf16, full mode, i.i.d. N(0,1)*0.5 inputs), timed the same way, with the
-    same algorithmic bytes and MFMA work at d=128.
+    same algorithmic bytes and MFMA work at d=128, and its backward pass.
 Only one GPU is used; --gpus above 1 exits with a message.
 """
 from __future__ import annotations
@@ -272,10 +272,26 @@ def bench_head128(mra, steps: int, warmup: int) -> dict:
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
+    # its backward pass on the selection that forward left
+    ws = torch.empty(mra.workspace_size(w.B, w.H, w.N, w.d, torch.bfloat16, w.block_per_row, w.approx_mode),
+                     dtype=torch.uint8, device="cuda")
+    out = mra.attention(q, k, v, None, workspace=ws, **kw)
+    g = torch.from_numpy(np.random.default_rng(3).standard_normal(q.shape).astype(np.float32)).to(torch.bfloat16)
+    run, _ = mra.prepare_backward(q, k, v, out, g.cuda(), ws, None, **kw)
+    for _ in range(warmup):
+        run()
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_bwd = e0.elapsed_time(e1) / steps
     BH, K = w.B * w.H, mra.num_block(w.N, w.block_per_row)
     nbytes = 4.0 * BH * w.N * w.d * 2          # Q, K, V read and O written once, bf16
     flops = 4.0 * 32 * 32 * w.d * BH * K       # QK^T and PV on the selected blocks
     return {"workload": w.name, "head_dim": w.d, "ms_per_call": round(ms, 5),
+            "backward_ms_per_call": round(ms_bwd, 5),
+            "backward_tokens_per_s": round(w.B * w.N / (ms_bwd * 1e-3), 1),
             "tokens_per_s": round(w.B * w.N / (ms * 1e-3), 1), "algorithmic_bytes": int(nbytes),
             "achieved_GBs": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),

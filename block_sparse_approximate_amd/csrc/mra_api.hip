@@ -222,7 +222,7 @@ MRA_API const char* mra_status_string(int32_t s) {
         case MRA_ERR_NULL: return "a required pointer is NULL";
         case MRA_ERR_SHAPE: return "batch/heads out of range";
         case MRA_ERR_SEQ_LEN: return "seq_len must be a multiple of 32 in [32, 16384]";
-        case MRA_ERR_HEAD_DIM: return "head_dim must be 64 or 128 (64 for the backward) and scale_dim 0 or 1 .. head_dim";
+        case MRA_ERR_HEAD_DIM: return "head_dim must be 64 or 128 and scale_dim 0 or 1 .. head_dim";
         case MRA_ERR_DTYPE: return "dtype must be MRA_F32 or MRA_BF16";
         case MRA_ERR_MODE: return "approx_mode must be full (0) or sparse (1)";
         case MRA_ERR_BUDGET: return "block_per_row must be >= 1";
@@ -328,7 +328,6 @@ MRA_API mra_status mra_backward_workspace_size(const mra_dims* dims, int32_t blo
     if (!bytes) return MRA_ERR_NULL;
     mra_status st = check_dims(dims);
     if (st != MRA_OK) return st;
-    if (dims->head_dim != kHeadDim) return MRA_ERR_HEAD_DIM;   // the backward kernels take 64 channels
     st = check_params(block_per_row, approx_mode, 0, 0);
     if (st != MRA_OK) return st;
     Layout L;
@@ -345,7 +344,6 @@ static mra_status run_bwd(const mra_dims* dims, const void* q, const void* k, co
                           int32_t block_per_row, int32_t approx_mode, int32_t prior_first, int32_t prior_diag,
                           bool dyn, const void* out, const void* dout, void* dq, void* dk, void* dv, void* workspace,
                           size_t workspace_bytes, void* bwd_workspace, size_t bwd_workspace_bytes, void* stream) {
-    if (dims && dims->head_dim != kHeadDim) return MRA_ERR_HEAD_DIM;   // the backward kernels take 64 channels
     Layout L;
     mra_status st = check_call(dims, q, k, v, mask, block_per_row, approx_mode, prior_first, prior_diag, out,
                                workspace, workspace_bytes, true, &L);
@@ -481,7 +479,6 @@ MRA_API mra_status mra_bigbird_backward_workspace_size(const mra_dims* dims, int
     int32_t bpr = 0;
     const mra_status st = check_bigbird(dims, block_size, num_random_blocks, &bpr);
     if (st != MRA_OK) return st;
-    if (dims->head_dim != kHeadDim) return MRA_ERR_HEAD_DIM;   // the backward kernels take 64 channels
     Layout L;
     if (!carve(*dims, bpr, MRA_APPROX_SPARSE, &L)) return MRA_ERR_SEQ_LEN;
     BwdLayout W;

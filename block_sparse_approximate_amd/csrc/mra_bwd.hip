@@ -65,17 +65,19 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int kWaves = 2;             // per workgroup: 4 staged blocks per wave fit static LDS
-constexpr int kThreads = kWaves * 64;
-constexpr int kStr = 72;              // bf16 elements per staged token row (144 bytes)
-constexpr int kTile = kBlock * kStr;  // one staged block
+// Head sizes HD = 64 or 128 (template parameter of every kernel below).
+// bf16 chunk kernels: 2 waves per workgroup for 64 channels, 1 for 128, so
+// that each wave's 4 staged blocks fit static LDS.
+__host__ __device__ constexpr int chunk_waves(int hd) { return hd == 64 ? 2 : 1; }
+__host__ __device__ constexpr int str_b(int hd) { return hd + 8; }          // bf16 per staged token row
+__host__ __device__ constexpr int tile_b(int hd) { return kBlock * str_b(hd); }
 constexpr int kTrThreads = 512;       // plan_kernel: one thread per block row / column (nb <= 512)
 constexpr int kChunkB = 8;            // selected blocks per backward work chunk
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 __device__ __forceinline__ float bf16_to_float(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
-// row index (within the 32 x 32 tile) held by accumulator register r in lane l
+// key index held by accumulator register r of a 32x32 MFMA tile in lane l
 __device__ __forceinline__ int acc_row(int r, int lane) { return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); }
 
 __device__ __forceinline__ void wave_sync_lds() {
@@ -84,37 +86,46 @@ __device__ __forceinline__ void wave_sync_lds() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// A 32 x 64 bf16 block (row-major in memory) into the wave's LDS: lane l
-// moves 16 bytes of token rows l / 8 + 8 x, channels 8 (l % 8) .. +7
-// (whole 128-byte rows per 8 lanes).
-__device__ __forceinline__ void load_blk(u32x4 (&r)[4], const uint16_t* g, int lane) {
+// A 32 x HD bf16 block (row-major in memory) into the wave's LDS: lane l
+// moves 16 bytes of token rows l / (HD / 8) + (512 / HD) x, channels
+// 8 (l % (HD / 8)) .. +7 (whole token rows per HD / 8 lanes).
+template <int HD>
+__device__ __forceinline__ void load_blk(u32x4 (&r)[HD / 16], const uint16_t* g, int lane) {
+    constexpr int kRowLanes = HD / 8, kRows = 64 / kRowLanes;
 #pragma unroll
-    for (int x = 0; x < 4; x++) r[x] = *reinterpret_cast<const u32x4*>(g + ((lane >> 3) + 8 * x) * kHeadDim + (lane & 7) * 8);
+    for (int x = 0; x < HD / 16; x++)
+        r[x] = *reinterpret_cast<const u32x4*>(g + (lane / kRowLanes + kRows * x) * HD + (lane % kRowLanes) * 8);
 }
-__device__ __forceinline__ void store_blk(uint16_t* s, const u32x4 (&r)[4], int lane) {
+template <int HD>
+__device__ __forceinline__ void store_blk(uint16_t* s, const u32x4 (&r)[HD / 16], int lane) {
+    constexpr int kRowLanes = HD / 8, kRows = 64 / kRowLanes;
 #pragma unroll
-    for (int x = 0; x < 4; x++) *reinterpret_cast<u32x4*>(s + ((lane >> 3) + 8 * x) * kStr + (lane & 7) * 8) = r[x];
+    for (int x = 0; x < HD / 16; x++)
+        *reinterpret_cast<u32x4*>(s + (lane / kRowLanes + kRows * x) * str_b(HD) + (lane % kRowLanes) * 8) = r[x];
 }
+template <int HD>
 __device__ __forceinline__ void stage(uint16_t* s, const uint16_t* g, int lane) {
-    u32x4 r[4];
-    load_blk(r, g, lane);
-    store_blk(s, r, lane);
+    u32x4 r[HD / 16];
+    load_blk<HD>(r, g, lane);
+    store_blk<HD>(s, r, lane);
 }
 
 // MFMA operand piece kc of a staged block: row l % 32, channels 16 kc + 8 (l / 32) .. +7
+template <int HD>
 __device__ __forceinline__ bf16x8 op(const uint16_t* s, int lane, int kc) {
-    return as_bf16x8(*reinterpret_cast<const u32x4*>(s + (lane & 31) * kStr + 16 * kc + 8 * (lane >> 5)));
+    return as_bf16x8(*reinterpret_cast<const u32x4*>(s + (lane & 31) * str_b(HD) + 16 * kc + 8 * (lane >> 5)));
 }
 
 // A operand of X^T for rows (channels) 32 mt .. 32 mt + 31, contracting over
 // the staged block's rows in the order that accumulator registers
 // 8 kc2 .. 8 kc2 + 7 of lane l hold them (acc_row).
+template <int HD>
 __device__ __forceinline__ bf16x8 op_t(const uint16_t* s, int lane, int kc2, int mt) {
     const int g16 = lane >> 4, s16 = lane & 15, h = lane >> 5;
     const int col = 32 * mt + 16 * (g16 & 1) + 4 * (s16 & 3);
     const int row = 16 * kc2 + 4 * h + (s16 >> 2);
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(s + row * kStr + col));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(s + (row + 8) * kStr + col));
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(s + row * str_b(HD) + col));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(s + (row + 8) * str_b(HD) + col));
     const i16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8, a8);
 }
@@ -127,9 +138,12 @@ __device__ __forceinline__ bf16x8 acc_op(const f32x16& a, int kc2) {
     return b;
 }
 
-__device__ __forceinline__ f32x16 mm4(f32x16 c, const uint16_t* a, const uint16_t* b, int lane) {
+// C += A B^T over the HD channels of two staged blocks
+template <int HD>
+__device__ __forceinline__ f32x16 mmk(f32x16 c, const uint16_t* a, const uint16_t* b, int lane) {
 #pragma unroll
-    for (int kc = 0; kc < 4; kc++) c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op(a, lane, kc), op(b, lane, kc), c, 0, 0, 0);
+    for (int kc = 0; kc < HD / 16; kc++)
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op<HD>(a, lane, kc), op<HD>(b, lane, kc), c, 0, 0, 0);
     return c;
 }
 
@@ -140,21 +154,21 @@ __device__ __forceinline__ f32x16 zero16() {
     return z;
 }
 
-// A 32 x 64 result tile pair (channels 0..31 in a0, 32..63 in a1; lane l
-// holds token row l % 32) times `scale`, plus add[channel] * aw when add is
-// given (a block mean's gradient share), to bf16 memory at g.
-__device__ __forceinline__ void store_rows(uint16_t* g, const f32x16& a0, const f32x16& a1, float scale, int lane,
+// A 32 x HD result (tile mt holds channels 32 mt .. 32 mt + 31; lane l holds
+// token row l % 32) times `scale`, plus add[channel] * aw when add is given
+// (a block mean's gradient share), to bf16 memory at g.
+template <int HD>
+__device__ __forceinline__ void store_rows(uint16_t* g, const f32x16 (&a)[HD / 32], float scale, int lane,
                                            const float* add = nullptr, float aw = 0.f) {
     const int n = lane & 31, h = lane >> 5;
 #pragma unroll
-    for (int mt = 0; mt < 2; mt++)
+    for (int mt = 0; mt < HD / 32; mt++)
 #pragma unroll
         for (int gq = 0; gq < 4; gq++) {
-            const f32x16& a = mt == 0 ? a0 : a1;
             const int d0 = 32 * mt + 8 * gq + 4 * h;
             float x[4];
 #pragma unroll
-            for (int e = 0; e < 4; e++) x[e] = a[4 * gq + e] * scale;
+            for (int e = 0; e < 4; e++) x[e] = a[mt][4 * gq + e] * scale;
             if (add) {
                 const float4 ad = *reinterpret_cast<const float4*>(add + d0);
                 x[0] += ad.x * aw; x[1] += ad.y * aw; x[2] += ad.z * aw; x[3] += ad.w * aw;
@@ -162,19 +176,20 @@ __device__ __forceinline__ void store_rows(uint16_t* g, const f32x16& a0, const 
             uint2 pk;
             pk.x = (uint32_t)float_to_bf16(x[0]) | ((uint32_t)float_to_bf16(x[1]) << 16);
             pk.y = (uint32_t)float_to_bf16(x[2]) | ((uint32_t)float_to_bf16(x[3]) << 16);
-            *reinterpret_cast<uint2*>(g + n * kHeadDim + d0) = pk;
+            *reinterpret_cast<uint2*>(g + n * HD + d0) = pk;
         }
 }
 
-// D_t = dO_t . O_t for token n = lane % 32 of a block (rows of 64 bf16
-// channels): lane (n, h) sums channels 32 h .. 32 h + 31, then the halves.
+// D_t = dO_t . O_t for token n = lane % 32 of a block (rows of HD bf16
+// channels): lane (n, h) sums channels HD / 2 h .. + HD / 2 - 1, then the halves.
+template <int HD>
 __device__ __forceinline__ float row_dot(const uint16_t* dO, const uint16_t* O, int lane) {
     const int n = lane & 31, h = lane >> 5;
     float s = 0.f;
 #pragma unroll
-    for (int x = 0; x < 4; x++) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(dO + n * kHeadDim + 32 * h + 8 * x);
-        const u32x4 o = *reinterpret_cast<const u32x4*>(O + n * kHeadDim + 32 * h + 8 * x);
+    for (int x = 0; x < HD / 16; x++) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(dO + n * HD + (HD / 2) * h + 8 * x);
+        const u32x4 o = *reinterpret_cast<const u32x4*>(O + n * HD + (HD / 2) * h + 8 * x);
 #pragma unroll
         for (int e = 0; e < 4; e++) {
             s += bf16_to_float(a[e] & 0xFFFFu) * bf16_to_float(o[e] & 0xFFFFu);
@@ -203,14 +218,15 @@ inline unsigned head_grid(int BH, int per_head) {
     return (unsigned)(BH >= 8 ? 8 * (int64_t)((BH + 7) / 8) * per_head : (int64_t)BH * per_head);
 }
 
-// D_t for fp32 rows: lane (n, h) sums channels 32 h .. 32 h + 31 of token n.
+// D_t for fp32 rows: lane (n, h) sums channels HD / 2 h .. + HD / 2 - 1 of token n.
+template <int HD>
 __device__ __forceinline__ float row_dot32(const float* dO, const float* O, int lane) {
     const int n = lane & 31, h = lane >> 5;
     float s = 0.f;
 #pragma unroll
-    for (int x = 0; x < 8; x++) {
-        const float4 a = *reinterpret_cast<const float4*>(dO + n * kHeadDim + 32 * h + 4 * x);
-        const float4 o = *reinterpret_cast<const float4*>(O + n * kHeadDim + 32 * h + 4 * x);
+    for (int x = 0; x < HD / 8; x++) {
+        const float4 a = *reinterpret_cast<const float4*>(dO + n * HD + (HD / 2) * h + 4 * x);
+        const float4 o = *reinterpret_cast<const float4*>(O + n * HD + (HD / 2) * h + 4 * x);
         s += a.x * o.x + a.y * o.y + a.z * o.z + a.w * o.w;
     }
     return s + __shfl_xor(s, 32, 64);
@@ -326,37 +342,39 @@ __global__ __launch_bounds__(kTrThreads) void plan_kernel(Params p) {
     }
 }
 
-// A wave's 32 x 64 fp32 partial (channels 0..31 in a0, 32..63 in a1; lane l
-// holds token row l % 32) to a contiguous [32, 64] slot.
-__device__ __forceinline__ void store_part(float* g, const f32x16& a0, const f32x16& a1, int lane) {
+// A wave's 32 x HD fp32 partial (tile mt: channels 32 mt .. 32 mt + 31; lane
+// l holds token row l % 32) to a contiguous [32, HD] slot.
+template <int HD>
+__device__ __forceinline__ void store_part(float* g, const f32x16 (&a)[HD / 32], int lane) {
     const int n = lane & 31, h = lane >> 5;
 #pragma unroll
-    for (int mt = 0; mt < 2; mt++)
+    for (int mt = 0; mt < HD / 32; mt++)
 #pragma unroll
-        for (int gq = 0; gq < 4; gq++) {
-            const f32x16& a = mt == 0 ? a0 : a1;
-            *reinterpret_cast<float4*>(g + n * kHeadDim + 32 * mt + 8 * gq + 4 * h) =
-                make_float4(a[4 * gq], a[4 * gq + 1], a[4 * gq + 2], a[4 * gq + 3]);
-        }
+        for (int gq = 0; gq < 4; gq++)
+            *reinterpret_cast<float4*>(g + n * HD + 32 * mt + 8 * gq + 4 * h) =
+                make_float4(a[mt][4 * gq], a[mt][4 * gq + 1], a[mt][4 * gq + 2], a[mt][4 * gq + 3]);
 }
 
 // ---------------------------------------------------------------- low-res (full mode)
 constexpr int kLrWaves = 8;            // block rows (columns) per workgroup, one per wave
 constexpr int kLrThreads = kLrWaves * 64;
-constexpr int kLrTile = 64;            // key blocks (query blocks) per staged tile
-constexpr int kLrVStr = kHeadDim + 1;  // vhat tile stride: lane j reads row j without bank conflicts
+// key blocks (query blocks) per staged tile: 64 for 64-channel heads, 32 for
+// 128 (the tiles then still fit static LDS)
+__host__ __device__ constexpr int lr_tile(int hd) { return hd == 64 ? 64 : 32; }
 
 // Workgroup (bh, rows i0 .. i0 + 7), wave w takes row i = i0 + w:
-//   phase 1: a_t, D_t of the row's tokens; g_i (lane = channel), c_i
-//   phase 2: per tile of 64 key blocks (vhat, khat staged): lane = j forms
-//            w_ij (the forward's weight, 0 for selected or empty cells) and
-//            e_ij; then lane = channel adds e_ij khat_j to dqhat_i.  E and W
-//            go out transposed ([j][i], 8 consecutive rows per j).
-template <int DT>
+//   phase 1: a_t, D_t of the row's tokens; g_i (lane = channel, and channel
+//            + 64 for 128-channel heads), c_i
+//   phase 2: per tile of kLrTile key blocks (vhat, khat staged): lane = j
+//            forms w_ij (the forward's weight, 0 for selected or empty cells)
+//            and e_ij; then lane = channel adds e_ij khat_j to dqhat_i.  E and
+//            W go out transposed ([j][i], 8 consecutive rows per j).
+template <int DT, int HD>
 __global__ __launch_bounds__(kLrThreads) void lr_rows_kernel(Params p) {
-    __shared__ float vt[kLrTile][kLrVStr];
-    __shared__ __align__(16) float kt[kLrTile][kHeadDim];
-    __shared__ float gs[kLrWaves][kHeadDim];
+    constexpr int kLrTile = lr_tile(HD), kCx = HD / 64;   // channels per lane
+    __shared__ float vt[kLrTile][HD + 1];   // stride HD + 1: lane j reads row j without bank conflicts
+    __shared__ __align__(16) float kt[kLrTile][HD];
+    __shared__ float gs[kLrWaves][HD];
     __shared__ float es[kLrWaves][kLrTile];
     __shared__ float ws[kLrWaves][kLrTile];
     __shared__ float al[kLrWaves][kBlock];
@@ -373,67 +391,77 @@ __global__ __launch_bounds__(kLrThreads) void lr_rows_kernel(Params p) {
 
     float ci = 0.f;
     if (act) {
-        const size_t rowoff = ((size_t)bh * p.N + (size_t)i * kBlock) * kHeadDim;
+        const size_t rowoff = ((size_t)bh * p.N + (size_t)i * kBlock) * HD;
         const int n = lane & 31, h = lane >> 5;
         float D;
         if constexpr (DT == 1)
-            D = row_dot(static_cast<const uint16_t*>(p.dout) + rowoff, static_cast<const uint16_t*>(p.fout) + rowoff,
-                        lane);
+            D = row_dot<HD>(static_cast<const uint16_t*>(p.dout) + rowoff,
+                            static_cast<const uint16_t*>(p.fout) + rowoff, lane);
         else
-            D = row_dot32(static_cast<const float*>(p.dout) + rowoff, static_cast<const float*>(p.fout) + rowoff,
-                          lane);
+            D = row_dot32<HD>(static_cast<const float*>(p.dout) + rowoff, static_cast<const float*>(p.fout) + rowoff,
+                              lane);
         const size_t t = (size_t)bh * p.N + (size_t)i * kBlock + n;
         const float mu = p.st_m[t], linv = p.st_linv[t];
         const float a = linv > 0.f ? __builtin_amdgcn_exp2f(mi * kLog2e - mu) * linv : 0.f;
         if (h == 0) al[wave][n] = a;
         ci = wave_sum(h == 0 ? a * D : 0.f);
         wave_sync_lds();
-        float g = 0.f;
-        if constexpr (DT == 1) {
-            const uint16_t* dO = static_cast<const uint16_t*>(p.dout) + rowoff;
+#pragma unroll
+        for (int x = 0; x < kCx; x++) {
+            const int c = lane + 64 * x;
+            float g = 0.f;
+            if constexpr (DT == 1) {
+                const uint16_t* dO = static_cast<const uint16_t*>(p.dout) + rowoff;
 #pragma unroll 8
-            for (int u = 0; u < kBlock; u++) g += al[wave][u] * bf16_to_float(dO[u * kHeadDim + lane]);
-        } else {
-            const float* dO = static_cast<const float*>(p.dout) + rowoff;
+                for (int u = 0; u < kBlock; u++) g += al[wave][u] * bf16_to_float(dO[u * HD + c]);
+            } else {
+                const float* dO = static_cast<const float*>(p.dout) + rowoff;
 #pragma unroll 8
-            for (int u = 0; u < kBlock; u++) g += al[wave][u] * dO[u * kHeadDim + lane];
+                for (int u = 0; u < kBlock; u++) g += al[wave][u] * dO[u * HD + c];
+            }
+            gs[wave][c] = g;
+            p.bwd_g[hrow * HD + c] = g;
         }
-        gs[wave][lane] = g;
-        p.bwd_g[hrow * kHeadDim + lane] = g;
         if (lane == 0) p.bwd_c[hrow] = ci;
     }
 
     const float* S = p.logits + hrow * nb;
     const uint32_t* sbits = p.selbits + hrow * p.words;
     const int32_t* cnt = p.cnt + (size_t)b * nb;
-    const float* vh = p.vhat + (size_t)bh * nb * kHeadDim;
-    const float* kh = p.khat + (size_t)bh * nb * kHeadDim;
-    float dqh = 0.f;
+    const float* vh = p.vhat + (size_t)bh * nb * HD;
+    const float* kh = p.khat + (size_t)bh * nb * HD;
+    float dqh[kCx];
+#pragma unroll
+    for (int x = 0; x < kCx; x++) dqh[x] = 0.f;
     for (int j0 = 0; j0 < nb; j0 += kLrTile) {
         __syncthreads();   // every wave is done with the previous tile
-        for (int x = tid; x < kLrTile * (kHeadDim / 4); x += kLrThreads) {
-            const int r = x / (kHeadDim / 4), c4 = (x % (kHeadDim / 4)) * 4, j = j0 + r;
+        for (int x = tid; x < kLrTile * (HD / 4); x += kLrThreads) {
+            const int r = x / (HD / 4), c4 = (x % (HD / 4)) * 4, j = j0 + r;
             float4 vv = make_float4(0.f, 0.f, 0.f, 0.f), kk = vv;
             if (j < nb) {
-                vv = *reinterpret_cast<const float4*>(vh + (size_t)j * kHeadDim + c4);
-                kk = *reinterpret_cast<const float4*>(kh + (size_t)j * kHeadDim + c4);
+                vv = *reinterpret_cast<const float4*>(vh + (size_t)j * HD + c4);
+                kk = *reinterpret_cast<const float4*>(kh + (size_t)j * HD + c4);
             }
             vt[r][c4] = vv.x; vt[r][c4 + 1] = vv.y; vt[r][c4 + 2] = vv.z; vt[r][c4 + 3] = vv.w;
             *reinterpret_cast<float4*>(&kt[r][c4]) = kk;
         }
         __syncthreads();
         if (act) {
-            const int j = j0 + lane;
-            float w = 0.f;
-            if (j < nb && !((sbits[j >> 5] >> (j & 31)) & 1u)) w = lowres_weight(S[j], mi, cnt[j]);
-            float T = 0.f;
+            if (lane < kLrTile) {
+                const int j = j0 + lane;
+                float w = 0.f;
+                if (j < nb && !((sbits[j >> 5] >> (j & 31)) & 1u)) w = lowres_weight(S[j], mi, cnt[j]);
+                float T = 0.f;
 #pragma unroll 16
-            for (int c = 0; c < kHeadDim; c++) T += gs[wave][c] * vt[lane][c];
-            es[wave][lane] = w * (T - ci);
-            ws[wave][lane] = w;
+                for (int c = 0; c < HD; c++) T += gs[wave][c] * vt[lane][c];
+                es[wave][lane] = w * (T - ci);
+                ws[wave][lane] = w;
+            }
             wave_sync_lds();
+#pragma unroll
+            for (int x = 0; x < kCx; x++)
 #pragma unroll 16
-            for (int u = 0; u < kLrTile; u++) dqh += es[wave][u] * kt[u][lane];
+                for (int u = 0; u < kLrTile; u++) dqh[x] += es[wave][u] * kt[u][lane + 64 * x];
         }
         __syncthreads();   // the tile's e and w of every row
         if (tid < 2 * kLrTile) {
@@ -445,15 +473,21 @@ __global__ __launch_bounds__(kLrThreads) void lr_rows_kernel(Params p) {
             }
         }
     }
-    if (act) p.bwd_dqh[hrow * kHeadDim + lane] = tau * dqh;
+    if (act) {
+#pragma unroll
+        for (int x = 0; x < kCx; x++) p.bwd_dqh[hrow * HD + lane + 64 * x] = tau * dqh[x];
+    }
 }
 
 // Workgroup (bh, key blocks j0 .. j0 + 7), wave w takes column j = j0 + w,
-// lane = channel: dvhat_j = sum_i w_ij g_i, dkhat_j = tau sum_i e_ij qhat_i
-// over tiles of 64 query blocks (g and qhat staged, shared by the waves).
+// lane = channel (and channel + 64): dvhat_j = sum_i w_ij g_i,
+// dkhat_j = tau sum_i e_ij qhat_i over tiles of kLrTile query blocks (g and
+// qhat staged, shared by the waves).
+template <int HD>
 __global__ __launch_bounds__(kLrThreads) void lr_cols_kernel(Params p) {
-    __shared__ __align__(16) float gt[kLrTile][kHeadDim];
-    __shared__ __align__(16) float qt[kLrTile][kHeadDim];
+    constexpr int kLrTile = lr_tile(HD), kCx = HD / 64;
+    __shared__ __align__(16) float gt[kLrTile][HD];
+    __shared__ __align__(16) float qt[kLrTile][HD];
     __shared__ float es[kLrWaves][kLrTile];
     __shared__ float ws[kLrWaves][kLrTile];
     const int nb = p.nb, groups = (nb + kLrWaves - 1) / kLrWaves;
@@ -464,45 +498,54 @@ __global__ __launch_bounds__(kLrThreads) void lr_cols_kernel(Params p) {
     const int j = j0 + wave;
     const bool act = j < nb;
     const float tau = 1.0f / __builtin_sqrtf((float)p.dscale);
-    const float* gh = p.bwd_g + (size_t)bh * nb * kHeadDim;
-    const float* qh = p.qhat + (size_t)bh * nb * kHeadDim;
+    const float* gh = p.bwd_g + (size_t)bh * nb * HD;
+    const float* qh = p.qhat + (size_t)bh * nb * HD;
     const size_t col = ((size_t)bh * nb + (act ? j : 0)) * nb;
-    float dv = 0.f, dk = 0.f;
+    float dv[kCx], dk[kCx];
+#pragma unroll
+    for (int x = 0; x < kCx; x++) dv[x] = dk[x] = 0.f;
     for (int r0 = 0; r0 < nb; r0 += kLrTile) {
         __syncthreads();
-        for (int x = tid; x < kLrTile * (kHeadDim / 4); x += kLrThreads) {
-            const int r = x / (kHeadDim / 4), c4 = (x % (kHeadDim / 4)) * 4, i = r0 + r;
+        for (int x = tid; x < kLrTile * (HD / 4); x += kLrThreads) {
+            const int r = x / (HD / 4), c4 = (x % (HD / 4)) * 4, i = r0 + r;
             float4 gg = make_float4(0.f, 0.f, 0.f, 0.f), qq = gg;
             if (i < nb) {
-                gg = *reinterpret_cast<const float4*>(gh + (size_t)i * kHeadDim + c4);
-                qq = *reinterpret_cast<const float4*>(qh + (size_t)i * kHeadDim + c4);
+                gg = *reinterpret_cast<const float4*>(gh + (size_t)i * HD + c4);
+                qq = *reinterpret_cast<const float4*>(qh + (size_t)i * HD + c4);
             }
             *reinterpret_cast<float4*>(&gt[r][c4]) = gg;
             *reinterpret_cast<float4*>(&qt[r][c4]) = qq;
         }
-        if (act) {
+        if (act && lane < kLrTile) {
             const int i = r0 + lane;
             es[wave][lane] = i < nb ? p.bwd_et[col + i] : 0.f;
             ws[wave][lane] = i < nb ? p.bwd_wt[col + i] : 0.f;
         }
         __syncthreads();
         if (act) {
+#pragma unroll
+            for (int x = 0; x < kCx; x++)
 #pragma unroll 16
-            for (int u = 0; u < kLrTile; u++) {
-                dv += ws[wave][u] * gt[u][lane];
-                dk += es[wave][u] * qt[u][lane];
-            }
+                for (int u = 0; u < kLrTile; u++) {
+                    dv[x] += ws[wave][u] * gt[u][lane + 64 * x];
+                    dk[x] += es[wave][u] * qt[u][lane + 64 * x];
+                }
         }
     }
     if (act) {
-        p.bwd_dvh[col / nb * kHeadDim + lane] = dv;
-        p.bwd_dkh[col / nb * kHeadDim + lane] = tau * dk;
+#pragma unroll
+        for (int x = 0; x < kCx; x++) {
+            p.bwd_dvh[col / nb * HD + lane + 64 * x] = dv[x];
+            p.bwd_dkh[col / nb * HD + lane + 64 * x] = tau * dk[x];
+        }
     }
 }
 
 // ---------------------------------------------------------------- dQ
-__global__ __launch_bounds__(kThreads) void dq_kernel(Params p) {
-    __shared__ __align__(16) uint16_t lds[kWaves][4][kTile];   // per wave: Q_i, dO_i, K_j, V_j
+template <int HD>
+__global__ __launch_bounds__(64 * chunk_waves(HD)) void dq_kernel(Params p) {
+    constexpr int kWaves = chunk_waves(HD), kKV = HD / 16, kMT = HD / 32;
+    __shared__ __align__(16) uint16_t lds[kWaves][4][tile_b(HD)];   // per wave: Q_i, dO_i, K_j, V_j
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nb = p.nb, maxch = p.bwd_maxch;
     int bh, wg;
@@ -517,7 +560,7 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(Params p) {
     uint16_t* dos = lds[wave][1];
     uint16_t* ks = lds[wave][2];
     uint16_t* vs = lds[wave][3];
-    const size_t head = (size_t)bh * p.N * kHeadDim, rowoff = head + (size_t)i * kBlock * kHeadDim;
+    const size_t head = (size_t)bh * p.N * HD, rowoff = head + (size_t)i * kBlock * HD;
     const uint16_t* Kh = static_cast<const uint16_t*>(p.k) + head;
     const uint16_t* Vh = static_cast<const uint16_t*>(p.v) + head;
     const uint16_t* dO = static_cast<const uint16_t*>(p.dout) + rowoff;
@@ -529,17 +572,17 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(Params p) {
     // the current block is computed; the first block's are issued before
     // the row's own loads
     const int32_t* cols = p.col + (size_t)bh * p.K;
-    u32x4 kr[4], vr[4];
+    u32x4 kr[kKV], vr[kKV];
     uint32_t kmn = 0;
     if (e0 < e1) {
         const int j = min(max(cols[e0], 0), nb - 1);
-        load_blk(kr, Kh + (size_t)j * kBlock * kHeadDim, lane);
-        load_blk(vr, Vh + (size_t)j * kBlock * kHeadDim, lane);
+        load_blk<HD>(kr, Kh + (size_t)j * kBlock * HD, lane);
+        load_blk<HD>(vr, Vh + (size_t)j * kBlock * HD, lane);
         kmn = p.mbits[(size_t)b * nb + j];
     }
-    stage(qs, static_cast<const uint16_t*>(p.q) + rowoff, lane);
-    stage(dos, dO, lane);
-    const float dfull = row_dot(dO, Of, lane);
+    stage<HD>(qs, static_cast<const uint16_t*>(p.q) + rowoff, lane);
+    stage<HD>(dos, dO, lane);
+    const float dfull = row_dot<HD>(dO, Of, lane);
     const size_t t = (size_t)bh * p.N + (size_t)i * kBlock + n;
     const float mu = p.st_m[t], linv = p.st_linv[t];
     const bool qv = linv > 0.f;   // padded and keyless query tokens take no gradient
@@ -547,20 +590,22 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(Params p) {
     if (h == 0) p.st_d[t] = Dv;   // every chunk of the row writes the same value
     wave_sync_lds();
 
-    f32x16 dq0 = zero16(), dq1 = zero16();
+    f32x16 dq[kMT];
+#pragma unroll
+    for (int mt = 0; mt < kMT; mt++) dq[mt] = zero16();
     for (int e = e0; e < e1; e++) {
         const uint32_t km = kmn;
-        store_blk(ks, kr, lane);
-        store_blk(vs, vr, lane);
+        store_blk<HD>(ks, kr, lane);
+        store_blk<HD>(vs, vr, lane);
         if (e + 1 < e1) {
             const int j = min(max(cols[e + 1], 0), nb - 1);
-            load_blk(kr, Kh + (size_t)j * kBlock * kHeadDim, lane);
-            load_blk(vr, Vh + (size_t)j * kBlock * kHeadDim, lane);
+            load_blk<HD>(kr, Kh + (size_t)j * kBlock * HD, lane);
+            load_blk<HD>(vr, Vh + (size_t)j * kBlock * HD, lane);
             kmn = p.mbits[(size_t)b * nb + j];
         }
         wave_sync_lds();
-        const f32x16 S = mm4(zero16(), ks, qs, lane);    // S^T: lane = query, registers = keys
-        const f32x16 dP = mm4(zero16(), vs, dos, lane);  // dP^T
+        const f32x16 S = mmk<HD>(zero16(), ks, qs, lane);    // S^T: lane = query, registers = keys
+        const f32x16 dP = mmk<HD>(zero16(), vs, dos, lane);  // dP^T
         f32x16 dS;
 #pragma unroll
         for (int r = 0; r < 16; r++) {
@@ -570,8 +615,9 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(Params p) {
 #pragma unroll
         for (int kc2 = 0; kc2 < 2; kc2++) {
             const bf16x8 bs = acc_op(dS, kc2);
-            dq0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op_t(ks, lane, kc2, 0), bs, dq0, 0, 0, 0);
-            dq1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op_t(ks, lane, kc2, 1), bs, dq1, 0, 0, 0);
+#pragma unroll
+            for (int mt = 0; mt < kMT; mt++)
+                dq[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op_t<HD>(ks, lane, kc2, mt), bs, dq[mt], 0, 0, 0);
         }
         wave_sync_lds();
     }
@@ -579,16 +625,18 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(Params p) {
         const float* add = nullptr;
         float aw = 0.f;
         if (p.mode == 0) {   // the token's share of dqhat_i
-            add = p.bwd_dqh + ((size_t)bh * nb + i) * kHeadDim;
+            add = p.bwd_dqh + ((size_t)bh * nb + i) * HD;
             aw = ((p.mbits[(size_t)b * nb + i] >> n) & 1u) ? 1.0f / (float)p.cnt[(size_t)b * nb + i] : 0.f;
         }
-        store_rows(static_cast<uint16_t*>(p.dq) + rowoff, dq0, dq1, tau, lane, add, aw);
-    } else store_part(p.bwd_part_dq + ((size_t)bh * maxch + min(dsc.w, maxch - 1)) * kBlock * kHeadDim, dq0, dq1, lane);
+        store_rows<HD>(static_cast<uint16_t*>(p.dq) + rowoff, dq, tau, lane, add, aw);
+    } else store_part<HD>(p.bwd_part_dq + ((size_t)bh * maxch + min(dsc.w, maxch - 1)) * kBlock * HD, dq, lane);
 }
 
 // ---------------------------------------------------------------- dK, dV
-__global__ __launch_bounds__(kThreads) void dkv_kernel(Params p) {
-    __shared__ __align__(16) uint16_t lds[kWaves][4][kTile];   // per wave: K_j, V_j, Q_i, dO_i
+template <int HD>
+__global__ __launch_bounds__(64 * chunk_waves(HD)) void dkv_kernel(Params p) {
+    constexpr int kWaves = chunk_waves(HD), kKV = HD / 16, kMT = HD / 32;
+    __shared__ __align__(16) uint16_t lds[kWaves][4][tile_b(HD)];   // per wave: K_j, V_j, Q_i, dO_i
     __shared__ __align__(16) float st[kWaves][3][kBlock];      // per wave: m, 1/l, D of block i's tokens
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nb = p.nb, maxch = p.bwd_maxch;
@@ -604,7 +652,7 @@ __global__ __launch_bounds__(kThreads) void dkv_kernel(Params p) {
     uint16_t* vs = lds[wave][1];
     uint16_t* qs = lds[wave][2];
     uint16_t* dos = lds[wave][3];
-    const size_t head = (size_t)bh * p.N * kHeadDim, coloff = head + (size_t)j * kBlock * kHeadDim;
+    const size_t head = (size_t)bh * p.N * HD, coloff = head + (size_t)j * kBlock * HD;
     const uint16_t* Q = static_cast<const uint16_t*>(p.q) + head;
     const uint16_t* dO = static_cast<const uint16_t*>(p.dout) + head;
     const float tau = 1.0f / __builtin_sqrtf((float)p.dscale);
@@ -615,26 +663,28 @@ __global__ __launch_bounds__(kThreads) void dkv_kernel(Params p) {
     // the next row block's Q and dO rows and statistics travel in registers
     // while the current one is computed; the first one's are issued before
     // the column's own loads
-    u32x4 qr[4], gr[4];
+    u32x4 qr[kKV], gr[kKV];
     float sm = 0.f, sl = 0.f, sd = 0.f;
     auto fetch = [&](int c) {
         const int i = min(max(rows[c], 0), nb - 1);
-        load_blk(qr, Q + (size_t)i * kBlock * kHeadDim, lane);
-        load_blk(gr, dO + (size_t)i * kBlock * kHeadDim, lane);
+        load_blk<HD>(qr, Q + (size_t)i * kBlock * HD, lane);
+        load_blk<HD>(gr, dO + (size_t)i * kBlock * HD, lane);
         const size_t t = sbase + (size_t)i * kBlock + (lane & 31);
         sm = p.st_m[t];
         sl = p.st_linv[t];
         sd = p.st_d[t];
     };
     if (c0 < c1) fetch(c0);
-    stage(ks, static_cast<const uint16_t*>(p.k) + coloff, lane);
-    stage(vs, static_cast<const uint16_t*>(p.v) + coloff, lane);
+    stage<HD>(ks, static_cast<const uint16_t*>(p.k) + coloff, lane);
+    stage<HD>(vs, static_cast<const uint16_t*>(p.v) + coloff, lane);
     const bool kvalid = (p.mbits[(size_t)b * nb + j] >> n) & 1u;   // lane = key n
 
-    f32x16 dk0 = zero16(), dk1 = zero16(), dv0 = zero16(), dv1 = zero16();
+    f32x16 dk[kMT], dv[kMT];
+#pragma unroll
+    for (int mt = 0; mt < kMT; mt++) dk[mt] = dv[mt] = zero16();
     for (int c = c0; c < c1; c++) {
-        store_blk(qs, qr, lane);
-        store_blk(dos, gr, lane);
+        store_blk<HD>(qs, qr, lane);
+        store_blk<HD>(dos, gr, lane);
         if (lane < kBlock) {
             st[wave][0][lane] = sm;
             st[wave][1][lane] = sl;
@@ -642,8 +692,8 @@ __global__ __launch_bounds__(kThreads) void dkv_kernel(Params p) {
         }
         if (c + 1 < c1) fetch(c + 1);
         wave_sync_lds();
-        const f32x16 S = mm4(zero16(), qs, ks, lane);    // S: lane = key, registers = queries
-        const f32x16 dP = mm4(zero16(), dos, vs, lane);  // dP
+        const f32x16 S = mmk<HD>(zero16(), qs, ks, lane);    // S: lane = key, registers = queries
+        const f32x16 dP = mmk<HD>(zero16(), dos, vs, lane);  // dP
         f32x16 P, dS;
 #pragma unroll
         for (int r = 0; r < 16; r++) {
@@ -656,10 +706,11 @@ __global__ __launch_bounds__(kThreads) void dkv_kernel(Params p) {
 #pragma unroll
         for (int kc2 = 0; kc2 < 2; kc2++) {
             const bf16x8 bp = acc_op(P, kc2), bs = acc_op(dS, kc2);
-            dv0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op_t(dos, lane, kc2, 0), bp, dv0, 0, 0, 0);
-            dv1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op_t(dos, lane, kc2, 1), bp, dv1, 0, 0, 0);
-            dk0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op_t(qs, lane, kc2, 0), bs, dk0, 0, 0, 0);
-            dk1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op_t(qs, lane, kc2, 1), bs, dk1, 0, 0, 0);
+#pragma unroll
+            for (int mt = 0; mt < kMT; mt++) {
+                dv[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op_t<HD>(dos, lane, kc2, mt), bp, dv[mt], 0, 0, 0);
+                dk[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op_t<HD>(qs, lane, kc2, mt), bs, dk[mt], 0, 0, 0);
+            }
         }
         wave_sync_lds();
     }
@@ -668,80 +719,94 @@ __global__ __launch_bounds__(kThreads) void dkv_kernel(Params p) {
         const float* addv = nullptr;
         float aw = 0.f;
         if (p.mode == 0) {   // the key's share of dkhat_j, dvhat_j
-            addk = p.bwd_dkh + ((size_t)bh * nb + j) * kHeadDim;
-            addv = p.bwd_dvh + ((size_t)bh * nb + j) * kHeadDim;
+            addk = p.bwd_dkh + ((size_t)bh * nb + j) * HD;
+            addv = p.bwd_dvh + ((size_t)bh * nb + j) * HD;
             aw = kvalid ? 1.0f / (float)p.cnt[(size_t)b * nb + j] : 0.f;
         }
-        store_rows(static_cast<uint16_t*>(p.dk) + coloff, dk0, dk1, tau, lane, addk, aw);
-        store_rows(static_cast<uint16_t*>(p.dv) + coloff, dv0, dv1, 1.0f, lane, addv, aw);
+        store_rows<HD>(static_cast<uint16_t*>(p.dk) + coloff, dk, tau, lane, addk, aw);
+        store_rows<HD>(static_cast<uint16_t*>(p.dv) + coloff, dv, 1.0f, lane, addv, aw);
     } else {
-        const size_t slot = ((size_t)bh * maxch + min(dsc.w, maxch - 1)) * kBlock * kHeadDim;
-        store_part(p.bwd_part_dk + slot, dk0, dk1, lane);
-        store_part(p.bwd_part_dv + slot, dv0, dv1, lane);
+        const size_t slot = ((size_t)bh * maxch + min(dsc.w, maxch - 1)) * kBlock * HD;
+        store_part<HD>(p.bwd_part_dk + slot, dk, lane);
+        store_part<HD>(p.bwd_part_dv + slot, dv, lane);
     }
 }
 
 // ---------------------------------------------------------------- fp32 chunks
 // The same products on fp32 operands with v_mfma_f32_32x32x2f32 (32 token
-// rows of 64 channels per staged block, row stride kStr32 so that lanes
-// reading a column of different rows fall on different banks).  For a
+// rows of HD channels per staged block, row stride HD + 1 so that lanes
+// reading a column of different rows fall on different banks; the staged
+// blocks of 128-channel heads exceed static LDS, so these kernels take
+// dynamic LDS).  For a
 // product over the channels lane l takes row l % 32, channel 2 s + l / 32 at
 // step s, for A and B alike.  For a product over the block's tokens, the
 // accumulator of the previous product is the B operand: at step s lane l
 // gives its register s, the token acc_row(s, l), and the A operand is read
 // transposed from the staged block at that same token.
-constexpr int kStr32 = kHeadDim + 1;
-constexpr int kTile32 = kBlock * kStr32;
+__host__ __device__ constexpr int str32(int hd) { return hd + 1; }   // fp32 per staged token row
+__host__ __device__ constexpr int tile32(int hd) { return kBlock * str32(hd); }
+// LDS of the fp32 chunk kernels: 4 staged blocks, then (dkv) 3 x 32 statistics
+__host__ __device__ constexpr size_t lds32_bytes(int hd) { return (4 * (size_t)tile32(hd) + 3 * kBlock) * 4; }
 
-__device__ __forceinline__ void load_blk32(float4 (&r)[8], const float* g, int lane) {
+template <int HD>
+__device__ __forceinline__ void load_blk32(float4 (&r)[HD / 8], const float* g, int lane) {
+    constexpr int kRowLanes = HD / 4, kRows = 64 / kRowLanes;
 #pragma unroll
-    for (int x = 0; x < 8; x++) r[x] = *reinterpret_cast<const float4*>(g + ((lane >> 4) + 4 * x) * kHeadDim + (lane & 15) * 4);
+    for (int x = 0; x < HD / 8; x++)
+        r[x] = *reinterpret_cast<const float4*>(g + (lane / kRowLanes + kRows * x) * HD + (lane % kRowLanes) * 4);
 }
-__device__ __forceinline__ void store_blk32(float* s, const float4 (&r)[8], int lane) {
+template <int HD>
+__device__ __forceinline__ void store_blk32(float* s, const float4 (&r)[HD / 8], int lane) {
+    constexpr int kRowLanes = HD / 4, kRows = 64 / kRowLanes;
 #pragma unroll
-    for (int x = 0; x < 8; x++) {
-        float* d = s + ((lane >> 4) + 4 * x) * kStr32 + (lane & 15) * 4;
+    for (int x = 0; x < HD / 8; x++) {
+        float* d = s + (lane / kRowLanes + kRows * x) * str32(HD) + (lane % kRowLanes) * 4;
         d[0] = r[x].x; d[1] = r[x].y; d[2] = r[x].z; d[3] = r[x].w;
     }
 }
-// C += A B^T over the 64 channels: A, B staged blocks (rows = the result's rows / columns)
+// C += A B^T over the HD channels: A, B staged blocks (rows = the result's rows / columns)
+template <int HD>
 __device__ __forceinline__ f32x16 mm32(f32x16 c, const float* a, const float* b, int lane) {
     const int n = lane & 31, h = lane >> 5;
 #pragma unroll 8
-    for (int st = 0; st < kHeadDim / 2; st++)
-        c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[n * kStr32 + 2 * st + h], b[n * kStr32 + 2 * st + h], c, 0, 0, 0);
+    for (int st = 0; st < HD / 2; st++)
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[n * str32(HD) + 2 * st + h], b[n * str32(HD) + 2 * st + h], c, 0,
+                                                 0, 0);
     return c;
 }
 // C[channel][col] += sum_t X[t][32 mt + channel] acc[t][col] over the block's 32 tokens
+template <int HD>
 __device__ __forceinline__ f32x16 mm32_t(f32x16 c, const float* x, const f32x16& acc, int mt, int lane) {
     const int m = lane & 31;
 #pragma unroll
     for (int st = 0; st < 16; st++)
-        c = __builtin_amdgcn_mfma_f32_32x32x2f32(x[acc_row(st, lane) * kStr32 + 32 * mt + m], acc[st], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(x[acc_row(st, lane) * str32(HD) + 32 * mt + m], acc[st], c, 0, 0, 0);
     return c;
 }
-// result tile pair (lane = token, registers = channels) times scale, plus add, to fp32 rows
-__device__ __forceinline__ void store_rows32(float* g, const f32x16& a0, const f32x16& a1, float scale, int lane,
+// result tiles (lane = token, registers = channels) times scale, plus add, to fp32 rows
+template <int HD>
+__device__ __forceinline__ void store_rows32(float* g, const f32x16 (&a)[HD / 32], float scale, int lane,
                                              const float* add, float aw) {
     const int n = lane & 31, h = lane >> 5;
 #pragma unroll
-    for (int mt = 0; mt < 2; mt++)
+    for (int mt = 0; mt < HD / 32; mt++)
 #pragma unroll
         for (int gq = 0; gq < 4; gq++) {
-            const f32x16& a = mt == 0 ? a0 : a1;
             const int d0 = 32 * mt + 8 * gq + 4 * h;
-            float4 x = make_float4(a[4 * gq] * scale, a[4 * gq + 1] * scale, a[4 * gq + 2] * scale,
-                                   a[4 * gq + 3] * scale);
+            float4 x = make_float4(a[mt][4 * gq] * scale, a[mt][4 * gq + 1] * scale, a[mt][4 * gq + 2] * scale,
+                                   a[mt][4 * gq + 3] * scale);
             if (add) {
                 const float4 ad = *reinterpret_cast<const float4*>(add + d0);
                 x.x += ad.x * aw; x.y += ad.y * aw; x.z += ad.z * aw; x.w += ad.w * aw;
             }
-            *reinterpret_cast<float4*>(g + n * kHeadDim + d0) = x;
+            *reinterpret_cast<float4*>(g + n * HD + d0) = x;
         }
 }
 
+template <int HD>
 __global__ __launch_bounds__(64) void dq32_kernel(Params p) {
-    __shared__ float lds[4][kTile32];   // Q_i, dO_i, K_j, V_j
+    extern __shared__ __align__(16) float lds32[];   // Q_i, dO_i, K_j, V_j: lds32_bytes(HD)
+    constexpr int kMT = HD / 32;
     const int lane = threadIdx.x & 63;
     const int nb = p.nb, maxch = p.bwd_maxch;
     int bh, cid;
@@ -751,63 +816,68 @@ __global__ __launch_bounds__(64) void dq32_kernel(Params p) {
     const int i = min(max(dsc.x, 0), nb - 1), b = bh / p.H;
     const int e0 = max(dsc.y, 0), e1 = min(dsc.z, (int)p.K);
     const int n = lane & 31, h = lane >> 5;
-    float* qs = lds[0];
-    float* dos = lds[1];
-    float* ks = lds[2];
-    float* vs = lds[3];
-    const size_t head = (size_t)bh * p.N * kHeadDim, rowoff = head + (size_t)i * kBlock * kHeadDim;
+    float* qs = lds32;
+    float* dos = lds32 + tile32(HD);
+    float* ks = lds32 + 2 * tile32(HD);
+    float* vs = lds32 + 3 * tile32(HD);
+    const size_t head = (size_t)bh * p.N * HD, rowoff = head + (size_t)i * kBlock * HD;
     const float* Kh = static_cast<const float*>(p.k) + head;
     const float* Vh = static_cast<const float*>(p.v) + head;
     const float* dO = static_cast<const float*>(p.dout) + rowoff;
     const float tau = 1.0f / __builtin_sqrtf((float)p.dscale);
     const float scale2 = tau * kLog2e;
     const int32_t* cols = p.col + (size_t)bh * p.K;
-    float4 r[8];
-    load_blk32(r, static_cast<const float*>(p.q) + rowoff, lane);
-    store_blk32(qs, r, lane);
-    load_blk32(r, dO, lane);
-    store_blk32(dos, r, lane);
-    const float dfull = row_dot32(dO, static_cast<const float*>(p.fout) + rowoff, lane);
+    float4 r[HD / 8];
+    load_blk32<HD>(r, static_cast<const float*>(p.q) + rowoff, lane);
+    store_blk32<HD>(qs, r, lane);
+    load_blk32<HD>(r, dO, lane);
+    store_blk32<HD>(dos, r, lane);
+    const float dfull = row_dot32<HD>(dO, static_cast<const float*>(p.fout) + rowoff, lane);
     const size_t t = (size_t)bh * p.N + (size_t)i * kBlock + n;
     const float mu = p.st_m[t], linv = p.st_linv[t];
     const bool qv = linv > 0.f;
     const float Dv = qv ? dfull : 0.f;
     if (h == 0) p.st_d[t] = Dv;
-    f32x16 dq0 = zero16(), dq1 = zero16();
+    f32x16 dq[kMT];
+#pragma unroll
+    for (int mt = 0; mt < kMT; mt++) dq[mt] = zero16();
     for (int e = e0; e < e1; e++) {
         const int j = min(max(cols[e], 0), nb - 1);
         const uint32_t km = p.mbits[(size_t)b * nb + j];
-        load_blk32(r, Kh + (size_t)j * kBlock * kHeadDim, lane);
-        store_blk32(ks, r, lane);
-        load_blk32(r, Vh + (size_t)j * kBlock * kHeadDim, lane);
-        store_blk32(vs, r, lane);
+        load_blk32<HD>(r, Kh + (size_t)j * kBlock * HD, lane);
+        store_blk32<HD>(ks, r, lane);
+        load_blk32<HD>(r, Vh + (size_t)j * kBlock * HD, lane);
+        store_blk32<HD>(vs, r, lane);
         wave_sync_lds();
-        const f32x16 S = mm32(zero16(), ks, qs, lane);     // S^T: lane = query, registers = keys
-        const f32x16 dP = mm32(zero16(), vs, dos, lane);   // dP^T
+        const f32x16 S = mm32<HD>(zero16(), ks, qs, lane);     // S^T: lane = query, registers = keys
+        const f32x16 dP = mm32<HD>(zero16(), vs, dos, lane);   // dP^T
         f32x16 dS;
 #pragma unroll
         for (int rr = 0; rr < 16; rr++) {
             const float pv = (qv && ((km >> acc_row(rr, lane)) & 1u)) ? __builtin_amdgcn_exp2f(S[rr] * scale2 - mu) * linv : 0.f;
             dS[rr] = pv * (dP[rr] - Dv);
         }
-        dq0 = mm32_t(dq0, ks, dS, 0, lane);                 // dQ^T += K^T dS^T
-        dq1 = mm32_t(dq1, ks, dS, 1, lane);
+#pragma unroll
+        for (int mt = 0; mt < kMT; mt++) dq[mt] = mm32_t<HD>(dq[mt], ks, dS, mt, lane);   // dQ^T += K^T dS^T
         wave_sync_lds();
     }
     if (dsc.w < 0) {
         const float* add = nullptr;
         float aw = 0.f;
         if (p.mode == 0) {
-            add = p.bwd_dqh + ((size_t)bh * nb + i) * kHeadDim;
+            add = p.bwd_dqh + ((size_t)bh * nb + i) * HD;
             aw = ((p.mbits[(size_t)b * nb + i] >> n) & 1u) ? 1.0f / (float)p.cnt[(size_t)b * nb + i] : 0.f;
         }
-        store_rows32(static_cast<float*>(p.dq) + rowoff, dq0, dq1, tau, lane, add, aw);
-    } else store_part(p.bwd_part_dq + ((size_t)bh * maxch + min(dsc.w, maxch - 1)) * kBlock * kHeadDim, dq0, dq1, lane);
+        store_rows32<HD>(static_cast<float*>(p.dq) + rowoff, dq, tau, lane, add, aw);
+    } else store_part<HD>(p.bwd_part_dq + ((size_t)bh * maxch + min(dsc.w, maxch - 1)) * kBlock * HD, dq, lane);
 }
 
+template <int HD>
 __global__ __launch_bounds__(64) void dkv32_kernel(Params p) {
-    __shared__ float lds[4][kTile32];   // K_j, V_j, Q_i, dO_i
-    __shared__ float st[3][kBlock];     // m, 1/l, D of block i's tokens
+    // K_j, V_j, Q_i, dO_i, then m, 1/l, D of block i's tokens: lds32_bytes(HD)
+    extern __shared__ __align__(16) float lds32[];
+    constexpr int kMT = HD / 32;
+    float (*st)[kBlock] = reinterpret_cast<float (*)[kBlock]>(lds32 + 4 * tile32(HD));
     const int lane = threadIdx.x & 63;
     const int nb = p.nb, maxch = p.bwd_maxch;
     int bh, cid;
@@ -817,30 +887,32 @@ __global__ __launch_bounds__(64) void dkv32_kernel(Params p) {
     const int j = min(max(dsc.x, 0), nb - 1), b = bh / p.H;
     const int c0 = max(dsc.y, 0), c1 = min(dsc.z, (int)p.K);
     const int n = lane & 31;
-    float* ks = lds[0];
-    float* vs = lds[1];
-    float* qs = lds[2];
-    float* dos = lds[3];
-    const size_t head = (size_t)bh * p.N * kHeadDim, coloff = head + (size_t)j * kBlock * kHeadDim;
+    float* ks = lds32;
+    float* vs = lds32 + tile32(HD);
+    float* qs = lds32 + 2 * tile32(HD);
+    float* dos = lds32 + 3 * tile32(HD);
+    const size_t head = (size_t)bh * p.N * HD, coloff = head + (size_t)j * kBlock * HD;
     const float* Q = static_cast<const float*>(p.q) + head;
     const float* dO = static_cast<const float*>(p.dout) + head;
     const float tau = 1.0f / __builtin_sqrtf((float)p.dscale);
     const float scale2 = tau * kLog2e;
     const int32_t* rows = p.ct_row + (size_t)bh * p.K;
     const size_t sbase = (size_t)bh * p.N;
-    float4 r[8];
-    load_blk32(r, static_cast<const float*>(p.k) + coloff, lane);
-    store_blk32(ks, r, lane);
-    load_blk32(r, static_cast<const float*>(p.v) + coloff, lane);
-    store_blk32(vs, r, lane);
+    float4 r[HD / 8];
+    load_blk32<HD>(r, static_cast<const float*>(p.k) + coloff, lane);
+    store_blk32<HD>(ks, r, lane);
+    load_blk32<HD>(r, static_cast<const float*>(p.v) + coloff, lane);
+    store_blk32<HD>(vs, r, lane);
     const bool kvalid = (p.mbits[(size_t)b * nb + j] >> n) & 1u;   // lane = key n
-    f32x16 dk0 = zero16(), dk1 = zero16(), dv0 = zero16(), dv1 = zero16();
+    f32x16 dk[kMT], dv[kMT];
+#pragma unroll
+    for (int mt = 0; mt < kMT; mt++) dk[mt] = dv[mt] = zero16();
     for (int c = c0; c < c1; c++) {
         const int i = min(max(rows[c], 0), nb - 1);
-        load_blk32(r, Q + (size_t)i * kBlock * kHeadDim, lane);
-        store_blk32(qs, r, lane);
-        load_blk32(r, dO + (size_t)i * kBlock * kHeadDim, lane);
-        store_blk32(dos, r, lane);
+        load_blk32<HD>(r, Q + (size_t)i * kBlock * HD, lane);
+        store_blk32<HD>(qs, r, lane);
+        load_blk32<HD>(r, dO + (size_t)i * kBlock * HD, lane);
+        store_blk32<HD>(dos, r, lane);
         if (lane < kBlock) {
             const size_t t = sbase + (size_t)i * kBlock + lane;
             st[0][lane] = p.st_m[t];
@@ -848,8 +920,8 @@ __global__ __launch_bounds__(64) void dkv32_kernel(Params p) {
             st[2][lane] = p.st_d[t];
         }
         wave_sync_lds();
-        const f32x16 S = mm32(zero16(), qs, ks, lane);     // S: lane = key, registers = queries
-        const f32x16 dP = mm32(zero16(), dos, vs, lane);
+        const f32x16 S = mm32<HD>(zero16(), qs, ks, lane);     // S: lane = key, registers = queries
+        const f32x16 dP = mm32<HD>(zero16(), dos, vs, lane);
         f32x16 P, dS;
 #pragma unroll
         for (int rr = 0; rr < 16; rr++) {
@@ -859,10 +931,11 @@ __global__ __launch_bounds__(64) void dkv32_kernel(Params p) {
             P[rr] = pv;
             dS[rr] = pv * (dP[rr] - st[2][q]);
         }
-        dv0 = mm32_t(dv0, dos, P, 0, lane);                 // dV^T += dO^T P
-        dv1 = mm32_t(dv1, dos, P, 1, lane);
-        dk0 = mm32_t(dk0, qs, dS, 0, lane);                 // dK^T += Q^T dS
-        dk1 = mm32_t(dk1, qs, dS, 1, lane);
+#pragma unroll
+        for (int mt = 0; mt < kMT; mt++) {
+            dv[mt] = mm32_t<HD>(dv[mt], dos, P, mt, lane);     // dV^T += dO^T P
+            dk[mt] = mm32_t<HD>(dk[mt], qs, dS, mt, lane);     // dK^T += Q^T dS
+        }
         wave_sync_lds();
     }
     if (dsc.w < 0) {
@@ -870,73 +943,83 @@ __global__ __launch_bounds__(64) void dkv32_kernel(Params p) {
         const float* addv = nullptr;
         float aw = 0.f;
         if (p.mode == 0) {
-            addk = p.bwd_dkh + ((size_t)bh * nb + j) * kHeadDim;
-            addv = p.bwd_dvh + ((size_t)bh * nb + j) * kHeadDim;
+            addk = p.bwd_dkh + ((size_t)bh * nb + j) * HD;
+            addv = p.bwd_dvh + ((size_t)bh * nb + j) * HD;
             aw = kvalid ? 1.0f / (float)p.cnt[(size_t)b * nb + j] : 0.f;
         }
-        store_rows32(static_cast<float*>(p.dk) + coloff, dk0, dk1, tau, lane, addk, aw);
-        store_rows32(static_cast<float*>(p.dv) + coloff, dv0, dv1, 1.0f, lane, addv, aw);
+        store_rows32<HD>(static_cast<float*>(p.dk) + coloff, dk, tau, lane, addk, aw);
+        store_rows32<HD>(static_cast<float*>(p.dv) + coloff, dv, 1.0f, lane, addv, aw);
     } else {
-        const size_t slot = ((size_t)bh * maxch + min(dsc.w, maxch - 1)) * kBlock * kHeadDim;
-        store_part(p.bwd_part_dk + slot, dk0, dk1, lane);
-        store_part(p.bwd_part_dv + slot, dv0, dv1, lane);
+        const size_t slot = ((size_t)bh * maxch + min(dsc.w, maxch - 1)) * kBlock * HD;
+        store_part<HD>(p.bwd_part_dk + slot, dk, lane);
+        store_part<HD>(p.bwd_part_dv + slot, dv, lane);
     }
 }
 
 // ---------------------------------------------------------------- reduce
 // Workgroup (bh, x, side): the x-th row (side 0) or column (side 1) of head
 // bh that has several chunks.  Thread t sums token t / 8, channels
-// 8 (t % 8) .. +7 over the chunks in order and writes bf16.
+// HD / 8 (t % 8) .. + HD / 8 - 1 over the chunks in order and writes them.
 constexpr int kRedThreads = 256;
 
-template <int DT>
+template <int DT, int HD>
 __device__ __forceinline__ void reduce_one(const float* part, int first, int nch, float scale, void* dst_v,
                                            size_t slot0, int tid, const float* add, float aw) {
-    const int tok = tid >> 3, cg = (tid & 7) * 8;
-    float acc[8];
+    constexpr int kCh = HD / 8, kF4 = kCh / 4;
+    const int tok = tid >> 3, cg = (tid & 7) * kCh;
+    float acc[kCh];
 #pragma unroll
-    for (int e = 0; e < 8; e++) acc[e] = 0.f;
-    const float* base = part + (slot0 + first) * kBlock * kHeadDim + tok * kHeadDim + cg;
+    for (int e = 0; e < kCh; e++) acc[e] = 0.f;
+    const float* base = part + (slot0 + first) * kBlock * HD + tok * HD + cg;
     constexpr int kBatch = 8;   // chunks loaded together; added in chunk order
     for (int c0 = 0; c0 < nch; c0 += kBatch) {
-        float4 a[kBatch], b2[kBatch];
+        float4 a[kBatch][kF4];
 #pragma unroll
         for (int c = 0; c < kBatch; c++) {
             if (c0 + c < nch) {
-                const float4* src = reinterpret_cast<const float4*>(base + (size_t)(c0 + c) * kBlock * kHeadDim);
-                a[c] = src[0];
-                b2[c] = src[1];
+                const float4* src = reinterpret_cast<const float4*>(base + (size_t)(c0 + c) * kBlock * HD);
+#pragma unroll
+                for (int x = 0; x < kF4; x++) a[c][x] = src[x];
             }
         }
 #pragma unroll
         for (int c = 0; c < kBatch; c++) {
             if (c0 + c < nch) {
-                acc[0] += a[c].x; acc[1] += a[c].y; acc[2] += a[c].z; acc[3] += a[c].w;
-                acc[4] += b2[c].x; acc[5] += b2[c].y; acc[6] += b2[c].z; acc[7] += b2[c].w;
+#pragma unroll
+                for (int x = 0; x < kF4; x++) {
+                    acc[4 * x] += a[c][x].x;
+                    acc[4 * x + 1] += a[c][x].y;
+                    acc[4 * x + 2] += a[c][x].z;
+                    acc[4 * x + 3] += a[c][x].w;
+                }
             }
         }
     }
 #pragma unroll
-    for (int e = 0; e < 8; e++) acc[e] *= scale;
+    for (int e = 0; e < kCh; e++) acc[e] *= scale;
     if (add) {
 #pragma unroll
-        for (int e = 0; e < 8; e++) acc[e] += add[cg + e] * aw;
+        for (int e = 0; e < kCh; e++) acc[e] += add[cg + e] * aw;
     }
     if constexpr (DT == 1) {
-        uint4 pk;
-        pk.x = (uint32_t)float_to_bf16(acc[0]) | ((uint32_t)float_to_bf16(acc[1]) << 16);
-        pk.y = (uint32_t)float_to_bf16(acc[2]) | ((uint32_t)float_to_bf16(acc[3]) << 16);
-        pk.z = (uint32_t)float_to_bf16(acc[4]) | ((uint32_t)float_to_bf16(acc[5]) << 16);
-        pk.w = (uint32_t)float_to_bf16(acc[6]) | ((uint32_t)float_to_bf16(acc[7]) << 16);
-        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(dst_v) + tok * kHeadDim + cg) = pk;
+#pragma unroll
+        for (int x = 0; x < kCh / 8; x++) {
+            const float* v = acc + 8 * x;
+            uint4 pk;
+            pk.x = (uint32_t)float_to_bf16(v[0]) | ((uint32_t)float_to_bf16(v[1]) << 16);
+            pk.y = (uint32_t)float_to_bf16(v[2]) | ((uint32_t)float_to_bf16(v[3]) << 16);
+            pk.z = (uint32_t)float_to_bf16(v[4]) | ((uint32_t)float_to_bf16(v[5]) << 16);
+            pk.w = (uint32_t)float_to_bf16(v[6]) | ((uint32_t)float_to_bf16(v[7]) << 16);
+            reinterpret_cast<uint4*>(static_cast<uint16_t*>(dst_v) + tok * HD + cg)[x] = pk;
+        }
     } else {
-        float* dst = static_cast<float*>(dst_v) + tok * kHeadDim + cg;
-        *reinterpret_cast<float4*>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+        float4* dst = reinterpret_cast<float4*>(static_cast<float*>(dst_v) + tok * HD + cg);
+#pragma unroll
+        for (int x = 0; x < kF4; x++) dst[x] = make_float4(acc[4 * x], acc[4 * x + 1], acc[4 * x + 2], acc[4 * x + 3]);
     }
 }
 
-template <int DT>
+template <int DT, int HD>
 __device__ void reduce_item(const Params& p, int bh, int x, int side) {
     const size_t es = DT == 1 ? 2 : 4;
     const int nb = p.nb, maxch = p.bwd_maxch;
@@ -944,25 +1027,25 @@ __device__ void reduce_item(const Params& p, int bh, int x, int side) {
     const int blk = min(max(m.x, 0), nb - 1);
     const int first = max(m.y, 0), nch = max(0, min(m.z, maxch - first));
     const float tau = 1.0f / __builtin_sqrtf((float)p.dscale);
-    const size_t off = ((size_t)bh * p.N + (size_t)blk * kBlock) * kHeadDim, slot0 = (size_t)bh * maxch;
+    const size_t off = ((size_t)bh * p.N + (size_t)blk * kBlock) * HD, slot0 = (size_t)bh * maxch;
     // full mode: the token's share of its block mean's gradient
     const int b = bh / p.H, tok = threadIdx.x >> 3;
     const bool full = p.mode == 0;
     const float aw = (full && ((p.mbits[(size_t)b * nb + blk] >> tok) & 1u)) ? 1.0f / (float)p.cnt[(size_t)b * nb + blk]
                                                                               : 0.f;
-    const size_t hb = ((size_t)bh * nb + blk) * kHeadDim;
+    const size_t hb = ((size_t)bh * nb + blk) * HD;
     if (side == 0) {
-        reduce_one<DT>(p.bwd_part_dq, first, nch, tau, static_cast<char*>(p.dq) + off * es, slot0, threadIdx.x,
+        reduce_one<DT, HD>(p.bwd_part_dq, first, nch, tau, static_cast<char*>(p.dq) + off * es, slot0, threadIdx.x,
                        full ? p.bwd_dqh + hb : nullptr, aw);
     } else {
-        reduce_one<DT>(p.bwd_part_dk, first, nch, tau, static_cast<char*>(p.dk) + off * es, slot0, threadIdx.x,
+        reduce_one<DT, HD>(p.bwd_part_dk, first, nch, tau, static_cast<char*>(p.dk) + off * es, slot0, threadIdx.x,
                        full ? p.bwd_dkh + hb : nullptr, aw);
-        reduce_one<DT>(p.bwd_part_dv, first, nch, 1.0f, static_cast<char*>(p.dv) + off * es, slot0, threadIdx.x,
+        reduce_one<DT, HD>(p.bwd_part_dv, first, nch, 1.0f, static_cast<char*>(p.dv) + off * es, slot0, threadIdx.x,
                        full ? p.bwd_dvh + hb : nullptr, aw);
     }
 }
 
-template <int DT>
+template <int DT, int HD>
 __global__ __launch_bounds__(kRedThreads) void reduce_kernel(Params p) {
     const int nb = p.nb;
     // items (x, bh, side), x slowest: the few rows and columns of several
@@ -974,7 +1057,7 @@ __global__ __launch_bounds__(kRedThreads) void reduce_kernel(Params p) {
         const int x = (int)(w / p.BH), bh = (int)(w - (int64_t)x * p.BH);
         const int4 cnt = p.bwd_count[bh];
         if (x >= (side == 0 ? cnt.z : cnt.w)) continue;
-        reduce_item<DT>(p, bh, x, side);
+        reduce_item<DT, HD>(p, bh, x, side);
     }
 }
 
@@ -982,11 +1065,8 @@ __global__ __launch_bounds__(kRedThreads) void reduce_kernel(Params p) {
 
 int bwd_max_chunks(int nb, int64_t K) { return nb + (int)((K + kChunkB - 1) / kChunkB); }
 
-hipError_t launch_bwd(const Params& p, hipStream_t s) {
-    if ((p.dtype != 0 && p.dtype != 1) || p.d != kHeadDim || p.nb > kTrThreads) return hipErrorInvalidValue;
-    if (p.mode == 0 && (!p.bwd_g || !p.bwd_c || !p.bwd_et || !p.bwd_wt || !p.bwd_dqh || !p.bwd_dkh || !p.bwd_dvh ||
-                        !p.vhat))
-        return hipErrorInvalidValue;
+template <int HD>
+static hipError_t launch_bwd_t(const Params& p, hipStream_t s) {
     const bool bf = p.dtype == 1;
     const size_t plan_lds = (size_t)p.nb * (p.words + 1) * 4;
     hipLaunchKernelGGL(plan_kernel, dim3(p.BH), dim3(kTrThreads), plan_lds, s, p);
@@ -994,34 +1074,52 @@ hipError_t launch_bwd(const Params& p, hipStream_t s) {
     if (e != hipSuccess) return e;
     if (p.mode == 0) {
         const unsigned lr_grid = head_grid(p.BH, (p.nb + kLrWaves - 1) / kLrWaves);
-        if (bf) hipLaunchKernelGGL(lr_rows_kernel<1>, dim3(lr_grid), dim3(kLrThreads), 0, s, p);
-        else hipLaunchKernelGGL(lr_rows_kernel<0>, dim3(lr_grid), dim3(kLrThreads), 0, s, p);
+        if (bf) hipLaunchKernelGGL((lr_rows_kernel<1, HD>), dim3(lr_grid), dim3(kLrThreads), 0, s, p);
+        else hipLaunchKernelGGL((lr_rows_kernel<0, HD>), dim3(lr_grid), dim3(kLrThreads), 0, s, p);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(lr_cols_kernel, dim3(lr_grid), dim3(kLrThreads), 0, s, p);
+        hipLaunchKernelGGL(lr_cols_kernel<HD>, dim3(lr_grid), dim3(kLrThreads), 0, s, p);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (bf) {
-        const unsigned grid = head_grid(p.BH, (p.bwd_maxch + kWaves - 1) / kWaves);
-        hipLaunchKernelGGL(dq_kernel, dim3(grid), dim3(kThreads), 0, s, p);
+        constexpr int kW = chunk_waves(HD);
+        const unsigned grid = head_grid(p.BH, (p.bwd_maxch + kW - 1) / kW);
+        hipLaunchKernelGGL(dq_kernel<HD>, dim3(grid), dim3(64 * kW), 0, s, p);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(dkv_kernel, dim3(grid), dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL(dkv_kernel<HD>, dim3(grid), dim3(64 * kW), 0, s, p);
     } else {
+        constexpr size_t kLds = lds32_bytes(HD);
+        static const hipError_t a1 = hipFuncSetAttribute(reinterpret_cast<const void*>(&dq32_kernel<HD>),
+                                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+        static const hipError_t a2 = hipFuncSetAttribute(reinterpret_cast<const void*>(&dkv32_kernel<HD>),
+                                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+        if (a1 != hipSuccess) return a1;
+        if (a2 != hipSuccess) return a2;
         const unsigned grid = head_grid(p.BH, p.bwd_maxch);   // one wave per workgroup
-        hipLaunchKernelGGL(dq32_kernel, dim3(grid), dim3(64), 0, s, p);
+        hipLaunchKernelGGL(dq32_kernel<HD>, dim3(grid), dim3(64), kLds, s, p);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(dkv32_kernel, dim3(grid), dim3(64), 0, s, p);
+        hipLaunchKernelGGL(dkv32_kernel<HD>, dim3(grid), dim3(64), kLds, s, p);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t red_items = 2 * (int64_t)p.BH * p.nb;
     const dim3 rg((unsigned)(red_items < 1024 ? red_items : 1024));
-    if (bf) hipLaunchKernelGGL(reduce_kernel<1>, rg, dim3(kRedThreads), 0, s, p);
-    else hipLaunchKernelGGL(reduce_kernel<0>, rg, dim3(kRedThreads), 0, s, p);
+    if (bf) hipLaunchKernelGGL((reduce_kernel<1, HD>), rg, dim3(kRedThreads), 0, s, p);
+    else hipLaunchKernelGGL((reduce_kernel<0, HD>), rg, dim3(kRedThreads), 0, s, p);
     return hipGetLastError();
+}
+
+hipError_t launch_bwd(const Params& p, hipStream_t s) {
+    if ((p.dtype != 0 && p.dtype != 1) || p.nb > kTrThreads) return hipErrorInvalidValue;
+    if (p.mode == 0 && (!p.bwd_g || !p.bwd_c || !p.bwd_et || !p.bwd_wt || !p.bwd_dqh || !p.bwd_dkh || !p.bwd_dvh ||
+                        !p.vhat))
+        return hipErrorInvalidValue;
+    if (p.d == 64) return launch_bwd_t<64>(p, s);
+    if (p.d == 128) return launch_bwd_t<128>(p, s);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace mra

@@ -24,7 +24,7 @@ from . import attention, backward_workspace_size, prepare_backward, workspace_si
 
 
 class MraAttentionFunction(torch.autograd.Function):
-    """out = MRA-2(q, k, v) on [batch, heads, seq_len, 64] tensors; its
+    """out = MRA-2(q, k, v) on [batch, heads, seq_len, 64 or 128] tensors; its
     backward is mra_attention_bwd (bf16 or fp32), which takes the forward's selection
     as fixed ([MRA] 第三步) and in full mode differentiates the low-res branch
     through the block means ([MRA] 第四步)."""
@@ -45,9 +45,6 @@ class MraAttentionFunction(torch.autograd.Function):
     @staticmethod
     def backward(ctx, dout):
         q, k, v, out, ws, mask = ctx.saved_tensors
-        if q.shape[-1] != 64:
-            raise NotImplementedError("the backward kernels take heads of at most 64 channels; "
-                                      "heads of 65 to 128 channels run forward only")
         mask = mask if ctx.has_mask else None
         block_per_row, approx_mode, prior_first, prior_diag, scale_dim = ctx.args
         B, H, N, d = q.shape
@@ -61,14 +58,12 @@ class MraAttentionFunction(torch.autograd.Function):
 
 def mra_attention(q, k, v, mask=None, block_per_row=4, approx_mode="full", initial_prior_first_n_blocks=0,
                   initial_prior_diagonal_n_blocks=0, score_ranking="row_normalized"):
-    """MRA-2 attention on [batch, heads, seq_len, d] device tensors, d <= 128;
-    mask is uint8 [batch, seq_len] (1 = valid) or None.  Differentiable for
-    d <= 64 (the backward kernels take 64 channels); heads of 65 to 128
-    channels run forward only.  Heads narrower than the kernels' 64 or 128
-    channels go to them zero-padded, with the logit scale of their own size
-    ([MRA] engineering notes: the model pads small heads for the kernels;
-    the zero channels change no sum), and the output is cut back to d
-    channels."""
+    """Differentiable MRA-2 attention on [batch, heads, seq_len, d] device
+    tensors, d <= 128; mask is uint8 [batch, seq_len] (1 = valid) or None.
+    Heads narrower than the kernels' 64 or 128 channels go to them
+    zero-padded, with the logit scale of their own size ([MRA] engineering
+    notes: the model pads small heads for the kernels; the zero channels
+    change no sum), and the output is cut back to d channels."""
     d = q.shape[-1]
     if d > 128:
         raise ValueError("head_dim above 128 is not supported")
@@ -88,7 +83,7 @@ class MraSelfAttention(torch.nn.Module):
     block_per_row, approx_mode, initial_prior_first_n_blocks,
     initial_prior_diagonal_n_blocks; score_ranking picks what step 2 ranks
     ("row_normalized" or "raw_logits").  head_dim = hidden_size / heads may
-    be at most 128, and at most 64 for training (see mra_attention)."""
+    be at most 128 (see mra_attention)."""
 
     def __init__(self, hidden_size=768, num_attention_heads=12, block_per_row=4, approx_mode="full",
                  initial_prior_first_n_blocks=0, initial_prior_diagonal_n_blocks=0, score_ranking="row_normalized"):

@@ -58,8 +58,7 @@ typedef enum {
     MRA_ERR_NULL = 1,       /* a required pointer is NULL */
     MRA_ERR_SHAPE = 2,      /* batch or heads < 1, or the sizes overflow */
     MRA_ERR_SEQ_LEN = 3,    /* seq_len not a multiple of 32, < 32 or > 16384 (BigBird: or of its block size) */
-    MRA_ERR_HEAD_DIM = 4,   /* head_dim other than 64 or 128 (the backward entry points: other than
-                               64), or scale_dim outside 0 .. head_dim */
+    MRA_ERR_HEAD_DIM = 4,   /* head_dim other than 64 or 128, or scale_dim outside 0 .. head_dim */
     MRA_ERR_DTYPE = 5,      /* dtype not MRA_F32 or MRA_BF16 */
     MRA_ERR_MODE = 6,       /* approx_mode not MRA_APPROX_FULL or MRA_APPROX_SPARSE */
     MRA_ERR_BUDGET = 7,     /* block_per_row < 1 (BigBird: num_random_blocks < 1) */
@@ -95,7 +94,7 @@ typedef struct {
     int32_t batch;
     int32_t heads;
     int32_t seq_len;  /* N: multiple of 32, 32 <= N <= 16384 */
-    int32_t head_dim; /* d: 64, or 128 for the forward entry points */
+    int32_t head_dim; /* d: 64 or 128 */
     int32_t dtype;    /* mra_dtype */
     int32_t scale_dim; /* 0, or the logical head size (1 .. head_dim) of heads zero-padded to head_dim:
                           the logit scale is 1/sqrt(scale_dim).  Zero channels add exact zeros to

@@ -8,8 +8,8 @@ against the CPU oracle at the same head size.
   mean-relative over valid query rows; padded query rows exactly 0.
 Cases cover both modes and dtypes, ragged masks, priors, a fully masked
 sequence, the one-block sequence and the N = 4096 and 16384 shapes of the
-named workloads.  The backward pass takes 64-channel heads only; its entry
-points reject 128 before any GPU work (tests/test_boundary.py).
+named workloads.  The backward pass at 128 channels is checked against the
+oracle's gradients with the bounds of tests/test_gpu_backward.py.
 """
 import numpy as np
 import pytest
@@ -17,6 +17,7 @@ import torch
 
 import oracle
 import workloads
+from test_gpu_backward import TOL_BWD, TOL_BWD32, check, run_case
 
 pytestmark = pytest.mark.gpu
 
@@ -175,3 +176,53 @@ def test_head128_matches_padded_head64_path(mra):
     assert torch.equal(s64["logits"], s128["logits"])
     assert torch.all(o128[..., 64:] == 0)
     assert (o128[..., :64].float() - o64.float()).abs().max().item() <= 2e-2
+
+
+BWD_CASES = [
+    # name, B, H, N, dtype, mode, bpr, prior_first, prior_diag, masked
+    ("bf16-sparse-priors", 1, 3, 1024, "bf16", "sparse", 3, 1, 3, False),
+    ("bf16-full-mask", 2, 2, 1024, "bf16", "full", 4, 0, 1, True),
+    ("f32-sparse-mask", 1, 2, 512, "f32", "sparse", 3, 0, 3, True),
+    ("f32-full", 1, 2, 512, "f32", "full", 4, 1, 0, False),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_head128_backward(mra, case):
+    name, B, H, N, dtype, mode, bpr, pf, pd, masked = case
+    w = workloads.iid("d128-bwd-" + name, B, H, N, d=128, dtype=dtype, seed=N + 7 * bpr, scale=0.7,
+                      block_per_row=bpr, approx_mode=mode, prior_first=pf, prior_diag=pd,
+                      mask=ragged_mask(B, N, 4) if masked else None)
+    print("case", w, flush=True)
+    got, ref = run_case(mra, w)
+    check(w.name, got, ref, TOL_BWD if dtype == "bf16" else TOL_BWD32)
+
+
+@pytest.mark.parametrize("mode,pf,pd", [("sparse", 2, 3), ("full", 0, 0)])
+def test_head128_backward_n4096(mra, mode, pf, pd):
+    w = workloads.iid("d128-bwd-N4096-" + mode, 1, 4, 4096, d=128, dtype="bf16", seed=77, scale=0.5,
+                      block_per_row=4, approx_mode=mode, prior_first=pf, prior_diag=pd)
+    print("case", w, flush=True)
+    got, ref = run_case(mra, w)
+    check(w.name, got, ref)
+
+
+def test_head128_bigbird_forward_and_backward(mra):
+    bb = workloads.bigbird("d128-BB-bs64-r2", B=1, H=2, N=2048, block_size=64, r=2, seed=13, d=128,
+                           mask=ragged_mask(1, 2048, 8))
+    w = bb.w
+    print("case", bb, flush=True)
+    mask = torch.from_numpy(w.mask).cuda()
+    q, k, v = dev(w, "q"), dev(w, "k"), dev(w, "v")
+    r = bb.rand.shape[3]
+    ws = torch.zeros(mra.bigbird_workspace_size(w.B, w.H, w.N, w.d, torch.bfloat16, bb.block_size, r),
+                     dtype=torch.uint8, device="cuda")
+    out = mra.bigbird_attention(q, k, v, torch.from_numpy(bb.rand).cuda(), mask, bb.block_size, workspace=ws)
+    g16 = torch.from_numpy(np.random.default_rng(14).standard_normal(q.shape).astype(np.float32)).to(torch.bfloat16)
+    grads = mra.bigbird_backward(q, k, v, out, g16.cuda(), ws, r, mask, bb.block_size)
+    torch.cuda.synchronize()
+    assert int(ws[:4].view(torch.int32).item()) == 0, "device error word"
+    assert_close(w, out.float().cpu().numpy().astype(np.float64),
+                 oracle.bigbird_forward(w.q, w.k, w.v, bb.rand, w.mask, bb.block_size))
+    ref = oracle.bigbird_backward(w.q, w.k, w.v, bb.rand, g16.float().numpy(), w.mask, bb.block_size)
+    check(w.name, [t.float().cpu().numpy() for t in grads], ref)

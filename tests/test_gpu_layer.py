@@ -58,9 +58,9 @@ def test_function_forward_and_gradients_match_oracle(layer, mode):
 
 
 @pytest.mark.parametrize("d", [96, 128])
-def test_wide_heads_forward_match_oracle_and_refuse_backward(layer, d):
+def test_wide_heads_match_oracle(layer, d):
     # heads of 65 to 128 channels: zero-padded to the 128-channel kernels
-    # with their own logit scale; forward only
+    # with their own logit scale, forward and gradients
     w = workloads.iid("wide-%d" % d, 1, 2, 512, d=d, dtype="bf16", seed=d, scale=0.7, block_per_row=3,
                       approx_mode="full", prior_diag=1)
     q, k, v = (bf16_dev(x).requires_grad_(True) for x in (w.q, w.k, w.v))
@@ -69,8 +69,13 @@ def test_wide_heads_forward_match_oracle_and_refuse_backward(layer, d):
     assert out.shape == q.shape
     err = np.abs(out.detach().float().cpu().numpy() - ref)
     assert err.max() <= 2e-2 and err.sum() / np.abs(ref).sum() <= 1e-2
-    with pytest.raises(NotImplementedError):
-        out.sum().backward()
+    g = np.random.default_rng(d + 1).standard_normal(q.shape).astype(np.float32)
+    g16 = torch.from_numpy(g).to(torch.bfloat16)
+    out.backward(g16.cuda())
+    refg = oracle.mra_backward(w.q, w.k, w.v, g16.float().numpy(), None, w.block_per_row, "full", 0, w.prior_diag)
+    for name, t, r in zip(("dq", "dk", "dv"), (q, k, v), refg):
+        assert t.grad.shape == t.shape
+        close(name, t.grad.float().cpu().numpy(), r)
 
 
 def test_self_attention_pads_to_a_block_multiple(layer):

@@ -180,9 +180,9 @@ class BigBirdWorkload:
 
 
 def bigbird(name="BB-bf16-N4096-bs64-r3", B=2, H=12, N=4096, block_size=64, r=3, dtype="bf16", seed=6,
-            scale=0.5, mask=None) -> BigBirdWorkload:
+            scale=0.5, mask=None, d=64) -> BigBirdWorkload:
     """BigBird block-sparse workload: the page's defaults (block 64, three
     random blocks) at the N = 4096 sequence length it is built for, iid
     inputs of the same scale as the MRA workloads."""
-    w = iid(name, B, H, N, dtype=dtype, scale=scale, seed=seed, approx_mode="sparse", mask=mask)
+    w = iid(name, B, H, N, d=d, dtype=dtype, scale=scale, seed=seed, approx_mode="sparse", mask=mask)
     return BigBirdWorkload(name, w, block_size, bigbird_rand(B, H, N, block_size, r, seed + 100))
