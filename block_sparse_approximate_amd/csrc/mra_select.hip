@@ -786,7 +786,7 @@ __global__ __launch_bounds__(kSelThreads) void premark_kernel(Params p) {
 __device__ __forceinline__ void emit_stream(const Params& p, int bh, const uint32_t* bitmap, const uint32_t* mbv, int* rc,
                             int* ic, uint64_t* scan64, int64_t expect) {
     const int nb = p.nb, words = p.words;
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x;
     // CSR row pointers, segment (item) pointers and the rows the final kernel
     // combines, in one scan: one block row per thread (nb <= 512)
     int32_t* row_ptr = p.row_ptr + (size_t)bh * (nb + 1);
@@ -821,49 +821,53 @@ __device__ __forceinline__ void emit_stream(const Params& p, int bh, const uint3
     }
     __syncthreads();
 
-    // column lists and the attention stream records: one thread per (block
-    // row, bitmap word), which walks the set bits of its word; a cell's rank
-    // in its row counts the bits of the row's earlier words
+    // the bitmap in memory
+    uint32_t* gbits = p.selbits + (size_t)bh * nb * words;
+    for (int x = tid; x < nb * words; x += kSelThreads) gbits[x] = bitmap[x];
+    // column lists and the attention stream records: one thread per selected
+    // cell e (CSR order).  Its block row is the last row whose start is at
+    // most e; its key block is the bit of rank e - start among the set bits
+    // of that row's bitmap.
     int32_t* col = p.col + (size_t)bh * p.K;
     BlkRec* recs = p.recs + (size_t)bh * p.K;
-    uint32_t* gbits = p.selbits + (size_t)bh * nb * words;
-    const bool pow2w = (words & (words - 1)) == 0;   // then 64 % words == 0
-    for (int x0 = 0; x0 < nb * words; x0 += kSelThreads) {
-        const int x = x0 + tid;
-        const bool in = x < nb * words;
-        uint32_t bits = in ? bitmap[x] : 0u;
-        const int i = x / words, w = x - i * words;
-        int r = 0;
-        if (pow2w) {
-            // a block row's words sit in `words` consecutive lanes: the rank
-            // of the word's first bit is a segmented scan along the row
-            const int c = __popc(bits);
-            int inc = c;
-            for (int off = 1; off < words; off <<= 1) {
-                const int y = __shfl_up(inc, off, 64);
-                if ((lane & (words - 1)) >= off) inc += y;
-            }
-            r = inc - c;
+    const int tcap = (int)min((int64_t)rc[nb], p.K);
+    for (int e = tid; e < tcap; e += kSelThreads) {
+        int lo = 0, hi = nb - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (rc[mid] <= e) lo = mid;
+            else hi = mid - 1;
         }
-        if (!in) continue;
-        gbits[x] = bits;
-        if (!bits) continue;
-        if (!pow2w)
-            for (int u = 0; u < w; u++) r += __popc(bitmap[i * words + u]);
-        const int o = rc[i], n = rc[i + 1] - o, first = ic[i];
-        const int nit = (n + kChunk - 1) / kChunk;
-        while (bits) {
-            const int j = w * 32 + __builtin_ctz(bits);
-            bits &= bits - 1;
-            const int e = o + r;
-            if (e < p.K) {
-                col[e] = j;
-                const int sg = r / kChunk;
-                const int len = min(kChunk, n - sg * kChunk);
-                recs[e] = BlkRec{rec_ij(i, j), mbv[j], 0u, rec_info(first + sg, r - sg * kChunk, len, nit == 1)};
-            }
-            r++;
+        const int i = lo, o = rc[i], n = rc[i + 1] - o, rank = e - o;
+        // the word that holds the cell, then the bit: halve the word five
+        // times, keeping the half that holds the remaining rank
+        const uint32_t* row = bitmap + i * words;
+        int r = rank, w = 0;
+        uint32_t bits = row[0];
+        int c = __popc(bits);
+        while (r >= c && w + 1 < words) {
+            r -= c;
+            bits = row[++w];
+            c = __popc(bits);
         }
+        int pos = 0;
+#pragma unroll
+        for (int half = 16; half > 0; half >>= 1) {
+            const uint32_t low = bits & ((1u << half) - 1u);
+            const int cl = __popc(low);
+            if (r >= cl) {
+                r -= cl;
+                bits >>= half;
+                pos += half;
+            } else {
+                bits = low;
+            }
+        }
+        const int j = w * 32 + pos;
+        col[e] = j;
+        const int nit = (n + kChunk - 1) / kChunk, sg = rank / kChunk;
+        const int len = min(kChunk, n - sg * kChunk);
+        recs[e] = BlkRec{rec_ij(i, j), mbv[j], 0u, rec_info(ic[i] + sg, rank - sg * kChunk, len, nit == 1)};
     }
 }
 
