@@ -25,7 +25,15 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kBatch = 8;       // segments whose loads are in flight together
-constexpr int kRowSlots = 32;   // workgroups per head
+// Workgroups per head: about kGridTarget in all (many small heads share few
+// rows to join each; a few long heads can have hundreds), 4 to 32 per head,
+// and never more than the head's block rows.
+constexpr int kGridTarget = 512;
+__host__ __device__ inline int row_slots(int nb, int BH) {
+    int s = kGridTarget / BH;
+    s = s < 4 ? 4 : (s > 32 ? 32 : s);
+    return nb < s ? nb : s;
+}
 
 // One listed row, from its descriptor (row i, first segment, segments).
 // Every load the row needs is issued before the first wait; the segments are
@@ -145,11 +153,12 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(Params p) {
     __shared__ __align__(16) float lo[HD];
     __shared__ float ll;
     const int nb = p.nb;
-    const int bh = blockIdx.x / kRowSlots, slot = blockIdx.x - bh * kRowSlots;
+    const int slots = row_slots(nb, p.BH);
+    const int bh = blockIdx.x / slots, slot = blockIdx.x - bh * slots;
     // the descriptor of this workgroup's first row is loaded with the count
     int4 dsc = slot < nb ? p.merge_rows[(size_t)bh * nb + slot] : make_int4(0, 0, 0, 0);
     const int nm = min(p.n_merge[bh], nb);
-    for (int s = slot; s < nm; s += kRowSlots) {
+    for (int s = slot; s < nm; s += slots) {
         if (s != slot) dsc = p.merge_rows[(size_t)bh * nb + s];
         merge_row<DT, HD>(p, bh, dsc, lo, &ll);
         __syncthreads();   // lo and ll are reused by the next row
@@ -160,7 +169,7 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(Params p) {
 
 template <int HD>
 static hipError_t launch_finish_t(const Params& p, hipStream_t s) {
-    const int grid = p.BH * kRowSlots;
+    const int grid = p.BH * row_slots(p.nb, p.BH);
     if (p.dtype == 1)
         hipLaunchKernelGGL((finish_kernel<1, HD>), dim3(grid), dim3(kThreads), 0, s, p);
     else
