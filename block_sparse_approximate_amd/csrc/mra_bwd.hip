@@ -239,28 +239,29 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // ---------------------------------------------------------------- plan
-// exclusive scan of one int per thread over the plan workgroup; *total gets the sum
-__device__ __forceinline__ int plan_scan(int v, int* wsum, int* total) {
+// exclusive scan of one value per thread over the plan workgroup; *total gets the sum
+template <typename T>
+__device__ __forceinline__ T plan_scan(T v, T* wsum, T* total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int x = v;
+    T x = v;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off, 64);
+        const T y = __shfl_up(x, off, 64);
         if (lane >= off) x += y;
     }
     if (lane == 63) wsum[wave] = x;
     __syncthreads();
     if (threadIdx.x == 0) {
-        int acc = 0;
+        T acc = 0;
         for (int w = 0; w < kTrThreads / 64; w++) {
-            const int t = wsum[w];
+            const T t = wsum[w];
             wsum[w] = acc;
             acc += t;
         }
         wsum[kTrThreads / 64] = acc;
     }
     __syncthreads();
-    const int ex = wsum[wave] + x - v;
+    const T ex = wsum[wave] + x - v;
     *total = wsum[kTrThreads / 64];
     __syncthreads();
     return ex;
@@ -269,7 +270,7 @@ __device__ __forceinline__ int plan_scan(int v, int* wsum, int* total) {
 __global__ __launch_bounds__(kTrThreads) void plan_kernel(Params p) {
     extern __shared__ __align__(16) uint32_t cbits[];   // [nb, words]: column j's bitmap over block rows,
                                                         // then [nb] each column's list start
-    __shared__ int wsum[kTrThreads / 64 + 1];
+    __shared__ uint64_t wsum[kTrThreads / 64 + 1];
     const int bh = blockIdx.x, nb = p.nb, words = p.words, x = threadIdx.x;
     const int K = (int)p.K, maxch = p.bwd_maxch;
     const uint32_t* gb = p.selbits + (size_t)bh * nb * words;   // row i's bitmap over key blocks
@@ -296,12 +297,17 @@ __global__ __launch_bounds__(kTrThreads) void plan_kernel(Params p) {
     const int e0 = on ? min(max(rp[x], 0), K) : 0, e1 = on ? min(max(rp[x + 1], e0), K) : 0;
     const int nr = on ? max(1, (e1 - e0 + kChunkB - 1) / kChunkB) : 0;
     const int nc = on ? max(1, (ccount + kChunkB - 1) / kChunkB) : 0;
-    int tot_c, tot_r, tot_cc, tot_rm, tot_cm;
-    const int cpos = plan_scan(ccount, wsum, &tot_c);
-    const int rbase = plan_scan(nr, wsum, &tot_r);
-    const int cbase = plan_scan(nc, wsum, &tot_cc);
-    const int rm = plan_scan(nr > 1 ? 1 : 0, wsum, &tot_rm);
-    const int cm = plan_scan(nc > 1 ? 1 : 0, wsum, &tot_cm);
+    // two scans of packed fields: column counts, row chunks and column chunks
+    // (21 bits each: totals stay below K + nb + K / kChunkB < 2^21), then
+    // the rows and columns of several chunks (16 bits each, totals <= nb)
+    constexpr uint64_t kM21 = (1u << 21) - 1;
+    uint64_t t1, t2;
+    const uint64_t s1 = plan_scan<uint64_t>((uint64_t)ccount | ((uint64_t)nr << 21) | ((uint64_t)nc << 42), wsum, &t1);
+    const uint64_t s2 = plan_scan<uint64_t>((uint64_t)(nr > 1 ? 1 : 0) | ((uint64_t)(nc > 1 ? 1 : 0) << 16), wsum, &t2);
+    const int cpos = (int)(s1 & kM21), rbase = (int)((s1 >> 21) & kM21), cbase = (int)(s1 >> 42);
+    const int tot_c = (int)(t1 & kM21), tot_r = (int)((t1 >> 21) & kM21), tot_cc = (int)(t1 >> 42);
+    const int rm = (int)(s2 & 0xFFFFu), cm = (int)(s2 >> 16);
+    const int tot_rm = (int)(t2 & 0xFFFFu), tot_cm = (int)(t2 >> 16);
     int32_t* cptr = p.ct_ptr + (size_t)bh * (nb + 1);
     int32_t* crow = p.ct_row + (size_t)bh * K;
     int4* rch = p.bwd_rch + (size_t)bh * maxch;
@@ -318,20 +324,41 @@ __global__ __launch_bounds__(kTrThreads) void plan_kernel(Params p) {
         if (nr > 1) p.bwd_rmul[(size_t)bh * nb + rm] = make_int4(x, rbase, nr, 0);
         if (nc > 1) p.bwd_cmul[(size_t)bh * nb + cm] = make_int4(x, cbase, nc, 0);
     }
-    // column lists (ascending rows): item (j, wi) writes the rows of word wi
-    // at column j's start plus the bits of its earlier words
+    // column lists (ascending rows), one thread per selected cell c in
+    // column order: its column is the last whose list starts at or before
+    // c, its row the bit of rank c - start among the column's set bits
     __syncthreads();
-    for (int it = x; it < nb * words; it += kTrThreads) {
-        const int wi = it / nb, j = it - wi * nb;
-        int pos = cstart[j];
-        for (int w2 = 0; w2 < wi; w2++) pos += __popc(cbits[j * words + w2]);
-        uint32_t m = cbits[j * words + wi];
-        while (m) {
-            const int r = __builtin_ctz(m);
-            m &= m - 1;
-            if (pos >= 0 && pos < K) crow[pos] = 32 * wi + r;
-            pos++;
+    const int ncell = min(tot_c, K);
+    for (int c = x; c < ncell; c += kTrThreads) {
+        int lo = 0, hi = nb - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (cstart[mid] <= c) lo = mid;
+            else hi = mid - 1;
         }
+        const uint32_t* cw = cbits + lo * words;
+        int r = c - cstart[lo], wi = 0;
+        uint32_t bits = cw[0];
+        int cn = __popc(bits);
+        while (r >= cn && wi + 1 < words) {
+            r -= cn;
+            bits = cw[++wi];
+            cn = __popc(bits);
+        }
+        int pos = 0;
+#pragma unroll
+        for (int half = 16; half > 0; half >>= 1) {
+            const uint32_t low = bits & ((1u << half) - 1u);
+            const int cl = __popc(low);
+            if (r >= cl) {
+                r -= cl;
+                bits >>= half;
+                pos += half;
+            } else {
+                bits = low;
+            }
+        }
+        crow[c] = 32 * wi + pos;
     }
     if (x == 0) {
         cptr[nb] = tot_c;
