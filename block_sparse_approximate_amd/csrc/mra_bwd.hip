@@ -385,9 +385,15 @@ __device__ __forceinline__ void store_part(float* g, const f32x16 (&a)[HD / 32],
 // ---------------------------------------------------------------- low-res (full mode)
 constexpr int kLrWaves = 8;            // block rows (columns) per workgroup, one per wave
 constexpr int kLrThreads = kLrWaves * 64;
-// key blocks (query blocks) per staged tile: 64 for 64-channel heads, 32 for
-// 128 (the tiles then still fit static LDS)
-__host__ __device__ constexpr int lr_tile(int hd) { return hd == 64 ? 64 : 32; }
+constexpr int kLrTile = 64;            // key blocks (query blocks) per staged tile
+// dynamic LDS of the low-res kernels (128-channel tiles exceed static LDS)
+__host__ __device__ constexpr size_t lr_rows_lds(int hd) {
+    return ((size_t)kLrTile * (hd + 1) + (size_t)kLrTile * hd + (size_t)kLrWaves * hd + 2 * kLrWaves * kLrTile +
+            kLrWaves * kBlock) * 4;
+}
+__host__ __device__ constexpr size_t lr_cols_lds(int hd) {
+    return (2 * (size_t)kLrTile * hd + 2 * kLrWaves * kLrTile) * 4;
+}
 
 // Workgroup (bh, rows i0 .. i0 + 7), wave w takes row i = i0 + w:
 //   phase 1: a_t, D_t of the row's tokens; g_i (lane = channel, and channel
@@ -398,13 +404,16 @@ __host__ __device__ constexpr int lr_tile(int hd) { return hd == 64 ? 64 : 32; }
 //            W go out transposed ([j][i], 8 consecutive rows per j).
 template <int DT, int HD>
 __global__ __launch_bounds__(kLrThreads) void lr_rows_kernel(Params p) {
-    constexpr int kLrTile = lr_tile(HD), kCx = HD / 64;   // channels per lane
-    __shared__ float vt[kLrTile][HD + 1];   // stride HD + 1: lane j reads row j without bank conflicts
-    __shared__ __align__(16) float kt[kLrTile][HD];
-    __shared__ float gs[kLrWaves][HD];
-    __shared__ float es[kLrWaves][kLrTile];
-    __shared__ float ws[kLrWaves][kLrTile];
-    __shared__ float al[kLrWaves][kBlock];
+    constexpr int kCx = HD / 64;   // channels per lane
+    // kt [kLrTile][HD] first (16-byte stores), then vt [kLrTile][HD + 1] (stride HD + 1: lane j reads row j
+    // without bank conflicts), gs [kLrWaves][HD], es and ws [kLrWaves][kLrTile], al [kLrWaves][kBlock]
+    extern __shared__ __align__(16) float lrs[];
+    float (*kt)[HD] = reinterpret_cast<float (*)[HD]>(lrs);
+    float (*vt)[HD + 1] = reinterpret_cast<float (*)[HD + 1]>(lrs + kLrTile * HD);
+    float (*gs)[HD] = reinterpret_cast<float (*)[HD]>(lrs + kLrTile * HD + kLrTile * (HD + 1));
+    float (*es)[kLrTile] = reinterpret_cast<float (*)[kLrTile]>(lrs + kLrTile * HD + kLrTile * (HD + 1) + kLrWaves * HD);
+    float (*ws)[kLrTile] = es + kLrWaves;
+    float (*al)[kBlock] = reinterpret_cast<float (*)[kBlock]>(ws + kLrWaves);
     const int nb = p.nb, groups = (nb + kLrWaves - 1) / kLrWaves;
     int bh, grp;
     if (!head_slot(p.BH, groups, &bh, &grp)) return;
@@ -512,11 +521,13 @@ __global__ __launch_bounds__(kLrThreads) void lr_rows_kernel(Params p) {
 // qhat staged, shared by the waves).
 template <int HD>
 __global__ __launch_bounds__(kLrThreads) void lr_cols_kernel(Params p) {
-    constexpr int kLrTile = lr_tile(HD), kCx = HD / 64;
-    __shared__ __align__(16) float gt[kLrTile][HD];
-    __shared__ __align__(16) float qt[kLrTile][HD];
-    __shared__ float es[kLrWaves][kLrTile];
-    __shared__ float ws[kLrWaves][kLrTile];
+    constexpr int kCx = HD / 64;
+    // gt, qt [kLrTile][HD], then es, ws [kLrWaves][kLrTile]
+    extern __shared__ __align__(16) float lrs[];
+    float (*gt)[HD] = reinterpret_cast<float (*)[HD]>(lrs);
+    float (*qt)[HD] = gt + kLrTile;
+    float (*es)[kLrTile] = reinterpret_cast<float (*)[kLrTile]>(lrs + 2 * kLrTile * HD);
+    float (*ws)[kLrTile] = es + kLrWaves;
     const int nb = p.nb, groups = (nb + kLrWaves - 1) / kLrWaves;
     int bh, grp;
     if (!head_slot(p.BH, groups, &bh, &grp)) return;
@@ -1101,11 +1112,21 @@ static hipError_t launch_bwd_t(const Params& p, hipStream_t s) {
     if (e != hipSuccess) return e;
     if (p.mode == 0) {
         const unsigned lr_grid = head_grid(p.BH, (p.nb + kLrWaves - 1) / kLrWaves);
-        if (bf) hipLaunchKernelGGL((lr_rows_kernel<1, HD>), dim3(lr_grid), dim3(kLrThreads), 0, s, p);
-        else hipLaunchKernelGGL((lr_rows_kernel<0, HD>), dim3(lr_grid), dim3(kLrThreads), 0, s, p);
+        constexpr size_t kRowsLds = lr_rows_lds(HD), kColsLds = lr_cols_lds(HD);
+        static const hipError_t a1 = hipFuncSetAttribute(reinterpret_cast<const void*>(&lr_rows_kernel<1, HD>),
+                                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kRowsLds);
+        static const hipError_t a2 = hipFuncSetAttribute(reinterpret_cast<const void*>(&lr_rows_kernel<0, HD>),
+                                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kRowsLds);
+        static const hipError_t a3 = hipFuncSetAttribute(reinterpret_cast<const void*>(&lr_cols_kernel<HD>),
+                                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kColsLds);
+        if (a1 != hipSuccess) return a1;
+        if (a2 != hipSuccess) return a2;
+        if (a3 != hipSuccess) return a3;
+        if (bf) hipLaunchKernelGGL((lr_rows_kernel<1, HD>), dim3(lr_grid), dim3(kLrThreads), kRowsLds, s, p);
+        else hipLaunchKernelGGL((lr_rows_kernel<0, HD>), dim3(lr_grid), dim3(kLrThreads), kRowsLds, s, p);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(lr_cols_kernel<HD>, dim3(lr_grid), dim3(kLrThreads), 0, s, p);
+        hipLaunchKernelGGL(lr_cols_kernel<HD>, dim3(lr_grid), dim3(kLrThreads), kColsLds, s, p);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
