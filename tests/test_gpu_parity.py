@@ -208,6 +208,12 @@ EDGE = [
     ("heads-in-turn-bh9", dict(B=1, H=9, N=12288, block_per_row=8)),
     ("priors-over-budget", dict(B=1, H=2, N=2048, block_per_row=1, prior_first=3, prior_diag=5,
                                 approx_mode="sparse")),
+    # many heads: the join kernel takes 4 workgroups per head (2 where a head has 2 block rows), each
+    # joining several rows; half the sequences are padded, so many rows have no selected block
+    ("many-heads-bh512-masked", dict(B=32, H=16, N=256, block_per_row=2, prior_first=1,
+                                     mask=np.repeat(np.arange(256)[None, :] < np.array([[256], [96]]), 16,
+                                                    axis=0).astype(np.uint8))),
+    ("many-heads-bh1024-nb2", dict(B=64, H=16, N=64, block_per_row=1, approx_mode="sparse")),
 ]
 
 
