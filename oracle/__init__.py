@@ -102,6 +102,14 @@ MODES = {"full": 0, "sparse": 1}
 # how step 2 ranks the cells: "row_normalized" S_ij - rowmax_i (reading R2,
 # the default) or "raw_logits" S_ij (reading R2')
 RANKINGS = {"row_normalized": 0, "raw_logits": 1}
+# width of the diagonal prior band for even n: |i - j| <= n // 2 ("symmetric", n + 1 wide)
+# or exactly n wide, offsets -((n - 1) // 2) .. n // 2 ("exact")
+BANDS = {"symmetric": 0, "exact": 2}
+
+
+def _variant(ranking, band):
+    return RANKINGS[ranking] | BANDS[band]
+
 
 
 def num_block(seq_len: int, block_per_row: int) -> int:
@@ -136,13 +144,14 @@ def lowres_logits_f32(qhat, khat):
     return S
 
 
-def scores_f32(S, cnt, prior_first=0, prior_diag=0, ranking="row_normalized"):
+def scores_f32(S, cnt, prior_first=0, prior_diag=0, ranking="row_normalized", band="symmetric"):
     S = _f32(S)
     cnt = np.ascontiguousarray(cnt, dtype=np.int32)
     nb = S.shape[0]
     rowmax = np.zeros(nb, np.float32)
     score = np.zeros((nb, nb), np.float32)
-    lib().oracle_scores_f32(nb, _p(S), _p(cnt), prior_first, prior_diag, RANKINGS[ranking], _p(rowmax), _p(score))
+    lib().oracle_scores_f32(nb, _p(S), _p(cnt), prior_first, prior_diag, _variant(ranking, band), _p(rowmax),
+                            _p(score))
     return rowmax, score
 
 
@@ -156,20 +165,21 @@ def select_top(score, K):
     return sel[:K]
 
 
-def select_from_logits(S, cnt, K, prior_first=0, prior_diag=0, ranking="row_normalized"):
+def select_from_logits(S, cnt, K, prior_first=0, prior_diag=0, ranking="row_normalized", band="symmetric"):
     S = _f32(S)
     cnt = np.ascontiguousarray(cnt, dtype=np.int32)
     nb = S.shape[0]
     sel = np.zeros(max(K, 1), np.int32)
-    rc = lib().oracle_select_from_logits(nb, _p(S), _p(cnt), K, prior_first, prior_diag, RANKINGS[ranking],
-                                         _p(sel))
+    rc = lib().oracle_select_from_logits(nb, _p(S), _p(cnt), K, prior_first, prior_diag,
+                                         _variant(ranking, band), _p(sel))
     if rc:
         raise ValueError("oracle_select_from_logits failed: %d" % rc)
     return sel[:K]
 
 
 def mra_forward(q, k, v, mask=None, block_per_row=4, approx_mode="full",
-                prior_first=0, prior_diag=0, threads=None, return_selection=False, ranking="row_normalized"):
+                prior_first=0, prior_diag=0, threads=None, return_selection=False, ranking="row_normalized",
+                band="symmetric"):
     """q, k, v: [B, H, N, d] (fp32 values; bf16 inputs widened exactly).
     mask: [B, N] or None.  Returns out [B, H, N, d] fp64 (and sel [B, H, K])."""
     q, k, v = _f32(q), _f32(k), _f32(v)
@@ -181,7 +191,7 @@ def mra_forward(q, k, v, mask=None, block_per_row=4, approx_mode="full",
     sel = np.zeros((B, H, max(K, 1)), np.int32) if return_selection else None
     m = _mask(mask)
     rc = lib().oracle_mra_fwd(B, H, N, d, _p(q), _p(k), _p(v), _p(m), block_per_row,
-                              MODES[approx_mode], prior_first, prior_diag, RANKINGS[ranking], _p(out), _p(sel),
+                              MODES[approx_mode], prior_first, prior_diag, _variant(ranking, band), _p(out), _p(sel),
                               threads or default_threads())
     if rc:
         raise ValueError("oracle_mra_fwd failed: %d" % rc)
@@ -191,7 +201,7 @@ def mra_forward(q, k, v, mask=None, block_per_row=4, approx_mode="full",
 
 
 def mra_backward(q, k, v, dout, mask=None, block_per_row=4, approx_mode="full",
-                 prior_first=0, prior_diag=0, threads=None, ranking="row_normalized"):
+                 prior_first=0, prior_diag=0, threads=None, ranking="row_normalized", band="symmetric"):
     """Gradients of mra_forward's output with respect to q, k, v given
     dout = dL/d out, with the selection held fixed ([MRA] step 3: the block
     products' backward reuses the kernels on transposed indices).  All
@@ -205,7 +215,7 @@ def mra_backward(q, k, v, dout, mask=None, block_per_row=4, approx_mode="full",
     dv = np.zeros_like(dq)
     m = _mask(mask)
     rc = lib().oracle_mra_bwd(B, H, N, d, _p(q), _p(k), _p(v), _p(m), block_per_row, MODES[approx_mode],
-                              prior_first, prior_diag, RANKINGS[ranking], _p(g), _p(dq), _p(dk), _p(dv),
+                              prior_first, prior_diag, _variant(ranking, band), _p(g), _p(dq), _p(dk), _p(dv),
                               threads or default_threads())
     if rc:
         raise ValueError("oracle_mra_bwd failed: %d" % rc)

@@ -38,7 +38,10 @@
  *   R5  ties at the k-th score go to the smaller flat index i*nb + j.
  *   R6  first-n prior: +5000 for rows i < n and +5000 for columns j < n
  *       (additive).
- *   R7  diagonal prior: +5000 where |i - j| <= floor(n/2).
+ *   R7  diagonal prior: +5000 where |i - j| <= floor(n/2).  For even n
+ *       that band is n + 1 blocks wide; the other reading (R7', variant
+ *       bit 1) keeps it exactly n wide, offsets j - i from
+ *       -floor((n-1)/2) to +floor(n/2).
  *   R8  the low-resolution branch covers exactly the unselected blocks.
  *   R9  a low-res cell stands for cnt_j keys, so its weight is
  *       cnt_j * exp(S_ij).
@@ -144,13 +147,19 @@ void oracle_lowres_logits_f32(int32_t nb, int32_t d, const float* qhat,
  *   rowmax_i = max over key blocks j with cnt_j > 0 of S_ij (-inf if none);
  *   score_ij = S_ij - rowmax_i                                      (fp32)
  *            + 5000 if the diagonal prior is on and |i-j| <= floor(g/2)
+ *                   (bit 1 of variant: -floor((g-1)/2) <= j-i <= floor(g/2))
  *            + 5000 if i < f   + 5000 if j < f                  (fp32 adds)
  *   score_ij = -inf if cnt_i == 0 or cnt_j == 0;  -0.0 becomes +0.0.
- * ranking 1 takes the other reading of the step's "top-k on the low-res
- * logits" (R2'): the raw logit S_ij in place of S_ij - rowmax_i, the rest
- * unchanged.  rowmax: [nb] (may be NULL), score: [nb, nb]. */
+ * variant is a bit set of the readings the step leaves open:
+ *   bit 0 (R2')  rank the raw logit S_ij in place of S_ij - rowmax_i ("top-k
+ *                on the low-res logits" taken literally), the rest unchanged;
+ *   bit 1 (R7')  the diagonal band is exactly g blocks wide, centred on the
+ *                main diagonal: offsets j - i in [-floor((g-1)/2), floor(g/2)]
+ *                (the same band as R7 for odd g; for even g it leans one
+ *                block to the right of the diagonal).
+ * rowmax: [nb] (may be NULL), score: [nb, nb]. */
 void oracle_scores_f32(int32_t nb, const float* S, const int32_t* cnt,
-                       int32_t prior_first, int32_t prior_diag, int32_t ranking,
+                       int32_t prior_first, int32_t prior_diag, int32_t variant,
                        float* rowmax, float* score)
 {
     for (int32_t i = 0; i < nb; i++) {
@@ -165,9 +174,11 @@ void oracle_scores_f32(int32_t nb, const float* S, const int32_t* cnt,
             if (cnt[i] == 0 || cnt[j] == 0) {
                 s = -INFINITY;
             } else {
-                s = ranking ? S[(int64_t)i * nb + j] : S[(int64_t)i * nb + j] - m;
+                s = (variant & 1) ? S[(int64_t)i * nb + j] : S[(int64_t)i * nb + j] - m;
                 int32_t dist = i > j ? i - j : j - i;
-                if (prior_diag > 0 && dist <= prior_diag / 2)
+                int32_t in_band = (variant & 2) ? (j - i >= -((prior_diag - 1) / 2) && j - i <= prior_diag / 2)
+                                                : dist <= prior_diag / 2;
+                if (prior_diag > 0 && in_band)
                     s = s + MRA_PRIOR_BIAS;
                 if (i < prior_first)
                     s = s + MRA_PRIOR_BIAS;
@@ -229,12 +240,12 @@ int oracle_select_top(int32_t nb, const float* score, int64_t K, int32_t* sel)
  * selector is compared against on identical logits). */
 int oracle_select_from_logits(int32_t nb, const float* S, const int32_t* cnt,
                               int64_t K, int32_t prior_first, int32_t prior_diag,
-                              int32_t ranking, int32_t* sel)
+                              int32_t variant, int32_t* sel)
 {
     float* score = (float*)malloc(sizeof(float) * (size_t)nb * nb);
     if (!score)
         return -2;
-    oracle_scores_f32(nb, S, cnt, prior_first, prior_diag, ranking, NULL, score);
+    oracle_scores_f32(nb, S, cnt, prior_first, prior_diag, variant, NULL, score);
     int rc = oracle_select_top(nb, score, K, sel);
     free(score);
     return rc;
@@ -245,7 +256,7 @@ int oracle_select_from_logits(int32_t nb, const float* S, const int32_t* cnt,
  * q,k,v: [N, d] fp32 values (bf16 inputs arrive widened exactly);
  * mask: [N] or NULL; out: [N, d] fp64; sel: [K] or NULL (ascending flat). */
 typedef struct {
-    int32_t N, d, block_per_row, mode, prior_first, prior_diag, ranking;
+    int32_t N, d, block_per_row, mode, prior_first, prior_diag, variant;
 } head_args_t;
 
 static int oracle_mra_head(const head_args_t* a, const float* q, const float* k,
@@ -279,7 +290,7 @@ static int oracle_mra_head(const head_args_t* a, const float* q, const float* k,
     oracle_pool_f32(N, d, q, mask, qh, cnt);
     oracle_pool_f32(N, d, k, mask, kh, NULL);
     oracle_lowres_logits_f32(nb, d, qh, kh, S);
-    oracle_scores_f32(nb, S, cnt, a->prior_first, a->prior_diag, a->ranking, NULL, score);
+    oracle_scores_f32(nb, S, cnt, a->prior_first, a->prior_diag, a->variant, NULL, score);
     rc = oracle_select_top(nb, score, K, sel);
     if (rc)
         goto done;
@@ -484,7 +495,7 @@ static int oracle_mra_head_bwd(const head_args_t* a, const float* q, const float
     oracle_pool_f32(N, d, q, mask, qh, cnt);
     oracle_pool_f32(N, d, k, mask, kh, NULL);
     oracle_lowres_logits_f32(nb, d, qh, kh, S);
-    oracle_scores_f32(nb, S, cnt, a->prior_first, a->prior_diag, a->ranking, NULL, score);
+    oracle_scores_f32(nb, S, cnt, a->prior_first, a->prior_diag, a->variant, NULL, score);
     rc = oracle_select_top(nb, score, K, sel);
     if (rc)
         goto done;
@@ -862,19 +873,19 @@ static int run_jobs(job_t* j, int nthreads)
 int oracle_mra_fwd(int32_t B, int32_t H, int32_t N, int32_t d, const float* q,
                    const float* k, const float* v, const uint8_t* mask,
                    int32_t block_per_row, int32_t mode, int32_t prior_first,
-                   int32_t prior_diag, int32_t ranking, double* out, int32_t* sel,
+                   int32_t prior_diag, int32_t variant, double* out, int32_t* sel,
                    int32_t nthreads)
 {
     int64_t K = oracle_num_block(N, block_per_row);
     if (B < 1 || H < 1 || d < 1 || K < 0 || (mode != 0 && mode != 1) ||
-        prior_first < 0 || prior_diag < 0 || (ranking != 0 && ranking != 1) || !q || !k || !v || !out)
+        prior_first < 0 || prior_diag < 0 || (variant & ~3) != 0 || !q || !k || !v || !out)
         return -1;
     job_t j;
     memset(&j, 0, sizeof(j));
     j.B = B; j.H = H; j.N = N; j.d = d;
     j.q = q; j.k = k; j.v = v; j.mask = mask;
     j.ha.N = N; j.ha.d = d; j.ha.block_per_row = block_per_row; j.ha.mode = mode;
-    j.ha.prior_first = prior_first; j.ha.prior_diag = prior_diag; j.ha.ranking = ranking;
+    j.ha.prior_first = prior_first; j.ha.prior_diag = prior_diag; j.ha.variant = variant;
     j.out = out; j.sel = sel; j.K = K; j.dense = 0;
     return run_jobs(&j, nthreads);
 }
@@ -900,12 +911,12 @@ int oracle_dense_fwd(int32_t B, int32_t H, int32_t N, int32_t d, const float* q,
 int oracle_mra_bwd(int32_t B, int32_t H, int32_t N, int32_t d, const float* q,
                    const float* k, const float* v, const uint8_t* mask,
                    int32_t block_per_row, int32_t mode, int32_t prior_first,
-                   int32_t prior_diag, int32_t ranking, const float* dout, double* dq,
+                   int32_t prior_diag, int32_t variant, const float* dout, double* dq,
                    double* dk, double* dv, int32_t nthreads)
 {
     int64_t K = oracle_num_block(N, block_per_row);
     if (B < 1 || H < 1 || d < 1 || K < 0 || (mode != 0 && mode != 1) ||
-        prior_first < 0 || prior_diag < 0 || (ranking != 0 && ranking != 1) || !q || !k || !v ||
+        prior_first < 0 || prior_diag < 0 || (variant & ~3) != 0 || !q || !k || !v ||
         !dout || !dq || !dk || !dv)
         return -1;
     job_t j;
@@ -913,7 +924,7 @@ int oracle_mra_bwd(int32_t B, int32_t H, int32_t N, int32_t d, const float* q,
     j.B = B; j.H = H; j.N = N; j.d = d;
     j.q = q; j.k = k; j.v = v; j.mask = mask;
     j.ha.N = N; j.ha.d = d; j.ha.block_per_row = block_per_row; j.ha.mode = mode;
-    j.ha.prior_first = prior_first; j.ha.prior_diag = prior_diag; j.ha.ranking = ranking;
+    j.ha.prior_first = prior_first; j.ha.prior_diag = prior_diag; j.ha.variant = variant;
     j.K = K; j.bwd = 1; j.dout = dout; j.dq = dq; j.dk = dk; j.dv = dv;
     return run_jobs(&j, nthreads);
 }

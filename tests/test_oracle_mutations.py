@@ -21,15 +21,18 @@ SRC = os.path.join(ROOT, "oracle", "mra_oracle.c")
 MUTANTS = {
     "low-res weight drops cnt_j": ("double w = (double)cnt[j] * exp(s_lo[j] - shift);",
                                    "double w = exp(s_lo[j] - shift);"),
-    "ranks raw logits, not row-normalised": ("s = ranking ? S[(int64_t)i * nb + j] : S[(int64_t)i * nb + j] - m;",
+    "ranks raw logits, not row-normalised": ("s = (variant & 1) ? S[(int64_t)i * nb + j] : S[(int64_t)i * nb + j] - m;",
                                             "s = S[(int64_t)i * nb + j];"),
-    "raw-logit ranking ignored": ("s = ranking ? S[(int64_t)i * nb + j] : S[(int64_t)i * nb + j] - m;",
+    "raw-logit ranking ignored": ("s = (variant & 1) ? S[(int64_t)i * nb + j] : S[(int64_t)i * nb + j] - m;",
                                   "s = S[(int64_t)i * nb + j] - m;"),
     "transposed low-res logits": ("acc = fmaf(qhat[(int64_t)i * d + c], khat[(int64_t)j * d + c], acc);",
                                   "acc = fmaf(qhat[(int64_t)j * d + c], khat[(int64_t)i * d + c], acc);"),
     "ties go to the larger flat index": ("return x->flat < y->flat ? -1 : (x->flat > y->flat ? 1 : 0);",
                                          "return x->flat > y->flat ? -1 : (x->flat < y->flat ? 1 : 0);"),
-    "diagonal band too wide": ("dist <= prior_diag / 2", "dist < prior_diag"),
+    "diagonal band too wide": (": dist <= prior_diag / 2", ": dist < prior_diag"),
+    "exact-width band leans left": ("(j - i >= -((prior_diag - 1) / 2) && j - i <= prior_diag / 2)",
+                                    "(j - i >= -(prior_diag / 2) && j - i <= (prior_diag - 1) / 2)"),
+    "exact-width band option ignored": ("int32_t in_band = (variant & 2) ?", "int32_t in_band = 0 ?"),
     "first-n prior on rows only": ("if (j < prior_first)\n                    s = s + MRA_PRIOR_BIAS;", ""),
     "masked keys not skipped": ("s_hi[u] = -INFINITY;\n                    if (mask && !mask[u])\n"
                                 "                        continue;", "s_hi[u] = -INFINITY;"),

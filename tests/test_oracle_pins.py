@@ -146,6 +146,40 @@ def test_diagonal_band_width(g, half):
     assert np.array_equal(sc == 5000.0, band) and np.all(sc[~band] == 0.0)
 
 
+@pytest.mark.parametrize("g,lo,hi", [(1, 0, 0), (2, 0, 1), (3, -1, 1), (4, -1, 2), (5, -2, 2), (6, -2, 3)])
+def test_diagonal_band_exact_width(g, lo, hi):
+    # reading R7': the band is exactly g blocks wide, offsets j - i in
+    # [-floor((g-1)/2), floor(g/2)]; an interior block row holds g band cells
+    nb = 11
+    S = np.zeros((nb, nb), np.float32)
+    cnt = np.full(nb, 32, np.int32)
+    _, sc = oracle.scores_f32(S, cnt, prior_diag=g, band="exact")
+    off = np.subtract.outer(np.arange(nb), np.arange(nb)) * -1   # off[i, j] = j - i
+    band = (off >= lo) & (off <= hi)
+    assert np.array_equal(sc == 5000.0, band) and np.all(sc[~band] == 0.0)
+    assert all(int((sc[i] == 5000.0).sum()) == g for i in range(3, nb - 3))
+    if g % 2 == 1:   # odd widths: both readings give the same band
+        _, sym = oracle.scores_f32(S, cnt, prior_diag=g)
+        assert np.array_equal(sym, sc)
+
+
+@pytest.mark.parametrize("band,g,bpr", [("exact", 2, 2), ("exact", 4, 4), ("symmetric", 2, 3),
+                                        ("symmetric", 4, 5)])
+def test_band_prior_sets_closed_form(band, g, bpr):
+    # equal logits: the budget takes every band cell (+5000) and fills the
+    # rest with the smallest flat indices outside the band
+    nb = 16
+    cells = [(i, j) for i in range(nb) for j in range(nb)
+             if (-((g - 1) // 2) <= j - i <= g // 2 if band == "exact" else abs(i - j) <= g // 2)]
+    K = nb * bpr
+    assert len(cells) <= K
+    inside = sorted(i * nb + j for i, j in cells)
+    outside = [f for f in range(nb * nb) if f not in set(inside)][: K - len(cells)]
+    sel = oracle.select_from_logits(np.zeros((nb, nb), np.float32), np.full(nb, 32, np.int32), K,
+                                    prior_diag=g, band=band)
+    assert sel.tolist() == sorted(inside + outside)
+
+
 # ---------------------------------------------------------------- selection -
 def test_selection_matches_lexsort_with_ties():
     rng = np.random.default_rng(11)
