@@ -158,7 +158,7 @@ def bench_backward(mra, steps: int, warmup: int, cfg: str) -> dict:
               initial_prior_diagonal_n_blocks=w.prior_diag)
     ws = torch.empty(mra.workspace_size(w.B, w.H, w.N, w.d, torch.bfloat16, w.block_per_row, w.approx_mode),
                      dtype=torch.uint8, device="cuda")
-    out = mra.attention(q, k, v, None, workspace=ws, **kw)
+    out = mra.attention(q, k, v, None, workspace=ws, save_stats=True, **kw)
     g = torch.from_numpy(np.random.default_rng(1).standard_normal(q.shape).astype(np.float32)).to(torch.bfloat16).cuda()
     run, _ = mra.prepare_backward(q, k, v, out, g, ws, None, **kw)
     for _ in range(warmup):
@@ -275,7 +275,7 @@ def bench_head128(mra, steps: int, warmup: int) -> dict:
     # its backward pass on the selection that forward left
     ws = torch.empty(mra.workspace_size(w.B, w.H, w.N, w.d, torch.bfloat16, w.block_per_row, w.approx_mode),
                      dtype=torch.uint8, device="cuda")
-    out = mra.attention(q, k, v, None, workspace=ws, **kw)
+    out = mra.attention(q, k, v, None, workspace=ws, save_stats=True, **kw)
     g = torch.from_numpy(np.random.default_rng(3).standard_normal(q.shape).astype(np.float32)).to(torch.bfloat16)
     run, _ = mra.prepare_backward(q, k, v, out, g.cuda(), ws, None, **kw)
     for _ in range(warmup):

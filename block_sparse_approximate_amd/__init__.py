@@ -18,7 +18,7 @@ import os
 import torch
 
 __all__ = ["attention", "attention_profiled", "prepare", "num_block", "workspace_size", "debug_stages", "debug_select",
-           "debug_replay", "attention_backward",
+           "debug_replay", "attention_backward", "workspace_error", "MraDeviceError",
            "MraError", "library_path", "lib"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -28,6 +28,16 @@ _lib = None
 MODES = {"full": 0, "sparse": 1}
 # step 2's ranking: the row-max-normalised logits (default) or the raw logits
 RANKINGS = {"row_normalized": 0, "raw_logits": 1}
+# width of the diagonal prior band for even n: |i - j| <= n // 2 ("symmetric")
+# or exactly n blocks, offsets -((n - 1) // 2) .. n // 2 ("exact")
+BANDS = {"symmetric": 0, "exact": 1}
+# bits of a workspace's device error word (include/mra.h MRA_DEVERR_*)
+DEVICE_ERRORS = {1: "selector candidate list", 2: "selection or segment count", 4: "attention record window",
+                 8: "backward plan", 16: "forward kept no softmax statistics"}
+# When set (environment MRA_CHECK_DEVICE_ERRORS=1, or assigned), every forward
+# and backward call waits for its stream and raises MraDeviceError if a
+# kernel flagged an inconsistency.  Off by default: the check synchronises.
+CHECK_DEVICE_ERRORS = os.environ.get("MRA_CHECK_DEVICE_ERRORS", "0") == "1"
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 
 # Entry points declared in include/mra.h, with their ctypes signatures.
@@ -41,9 +51,10 @@ SIGNATURES = {
     "mra_attention_fwd_profiled": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P, _P],
                                    ctypes.c_int),
     "mra_attention_fwd_ex": ([_P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
-    "mra_debug_stages": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P,
+    "mra_debug_stages": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P,
                           _P, _P, _SZ, _P], ctypes.c_int),
-    "mra_debug_select": ([_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P], ctypes.c_int),
+    "mra_debug_select": ([_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P], ctypes.c_int),
+    "mra_workspace_error": ([_P, _SZ, _P, ctypes.POINTER(ctypes.c_uint32)], ctypes.c_int),
     "mra_bigbird_workspace_size": ([_P, _I32, _I32, ctypes.POINTER(_SZ)], ctypes.c_int),
     "mra_bigbird_fwd": ([_P, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "mra_bigbird_backward_workspace_size": ([_P, _I32, _I32, ctypes.POINTER(_SZ)], ctypes.c_int),
@@ -61,6 +72,16 @@ class MraError(RuntimeError):
         self.status = status
 
 
+class MraDeviceError(RuntimeError):
+    """A kernel flagged an inconsistency in its bookkeeping: the call's
+    outputs are undefined.  `word` holds the device error word's bits."""
+
+    def __init__(self, word: int, what: str):
+        names = [n for b, n in DEVICE_ERRORS.items() if word & b]
+        super().__init__("%s: device error word 0x%x (%s)" % (what, word, ", ".join(names) or "?"))
+        self.word = word
+
+
 class _Dims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("seq_len", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32), ("scale_dim", ctypes.c_int32)]
@@ -69,7 +90,8 @@ class _Dims(ctypes.Structure):
 class _Options(ctypes.Structure):
     _fields_ = [("block_per_row", ctypes.c_int32), ("approx_mode", ctypes.c_int32),
                 ("prior_first", ctypes.c_int32), ("prior_diag", ctypes.c_int32),
-                ("score_ranking", ctypes.c_int32)]
+                ("score_ranking", ctypes.c_int32), ("diag_band", ctypes.c_int32),
+                ("save_stats", ctypes.c_int32)]
 
 
 def library_path() -> str:
@@ -102,6 +124,23 @@ def _status_text(status: int) -> str:
 def _check(status: int, what: str):
     if status != 0:
         raise MraError(status, what)
+
+
+def workspace_error(workspace: torch.Tensor) -> int:
+    """The device error word of a forward call's workspace (and of the
+    backward passes that read it), after the current stream has finished its
+    queued work; 0 when every kernel's bookkeeping added up."""
+    word = ctypes.c_uint32(0)
+    _check(lib().mra_workspace_error(_ptr(workspace), workspace.numel(), _stream(workspace), ctypes.byref(word)),
+           "mra_workspace_error")
+    return int(word.value)
+
+
+def _check_device(workspace: torch.Tensor, what: str):
+    if CHECK_DEVICE_ERRORS:
+        word = workspace_error(workspace)
+        if word:
+            raise MraDeviceError(word, what)
 
 
 def num_block(seq_len: int, block_per_row: int) -> int:
@@ -157,11 +196,14 @@ def _check_inputs(q, k, v, mask):
 
 
 def attention(q, k, v, mask=None, block_per_row=4, approx_mode="full", initial_prior_first_n_blocks=0,
-              initial_prior_diagonal_n_blocks=0, out=None, workspace=None, score_ranking="row_normalized", scale_dim=0):
+              initial_prior_diagonal_n_blocks=0, out=None, workspace=None, score_ranking="row_normalized", scale_dim=0,
+              diag_band="symmetric", save_stats=False):
     """MRA-2 forward on [batch, heads, seq_len, head_dim] tensors (bf16 or fp32).
     mask: uint8 [batch, seq_len] (1 = valid) or None.  score_ranking:
     "row_normalized" (default) or "raw_logits", what step 2's top-k ranks.
-    Returns `out`."""
+    diag_band: "symmetric" (default, |i - j| <= n // 2) or "exact" (a band of
+    exactly n blocks).  save_stats: keep each token's softmax statistics in
+    the workspace for attention_backward.  Returns `out`."""
     _check_inputs(q, k, v, mask)
     B, H, N, d = q.shape
     if out is None:
@@ -170,18 +212,20 @@ def attention(q, k, v, mask=None, block_per_row=4, approx_mode="full", initial_p
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     dims = _dims(B, H, N, d, DTYPES[q.dtype], scale_dim)
-    if score_ranking == "row_normalized":
+    if score_ranking == "row_normalized" and diag_band == "symmetric" and not save_stats:
         st = lib().mra_attention_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), block_per_row,
                                      MODES.get(approx_mode, -1), initial_prior_first_n_blocks,
                                      initial_prior_diagonal_n_blocks, _ptr(out), _ptr(workspace),
                                      workspace.numel(), _stream(q))
         _check(st, "mra_attention_fwd")
-        return out
-    opts = _Options(block_per_row, MODES.get(approx_mode, -1), initial_prior_first_n_blocks,
-                    initial_prior_diagonal_n_blocks, RANKINGS.get(score_ranking, -1))
-    st = lib().mra_attention_fwd_ex(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), ctypes.byref(opts),
-                                    _ptr(out), _ptr(workspace), workspace.numel(), _stream(q))
-    _check(st, "mra_attention_fwd_ex")
+    else:
+        opts = _Options(block_per_row, MODES.get(approx_mode, -1), initial_prior_first_n_blocks,
+                        initial_prior_diagonal_n_blocks, RANKINGS.get(score_ranking, -1), BANDS.get(diag_band, -1),
+                        1 if save_stats else 0)
+        st = lib().mra_attention_fwd_ex(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(mask),
+                                        ctypes.byref(opts), _ptr(out), _ptr(workspace), workspace.numel(), _stream(q))
+        _check(st, "mra_attention_fwd_ex")
+    _check_device(workspace, "mra_attention_fwd")
     return out
 
 
@@ -208,6 +252,7 @@ def prepare(q, k, v, mask=None, block_per_row=4, approx_mode="full", initial_pri
         st = fn(*args)
         if st != 0:
             raise MraError(st, "mra_attention_fwd")
+        _check_device(workspace, "mra_attention_fwd")
         return keep[5]
 
     return call, out
@@ -275,6 +320,7 @@ def prepare_backward(q, k, v, out, dout, workspace, mask=None, block_per_row=4, 
         st = fn(*args)
         if st != 0:
             raise MraError(st, "mra_attention_bwd")
+        _check_device(workspace, "mra_attention_bwd")
         return keep[7:10]
 
     return call, (dq, dk, dv)
@@ -309,7 +355,8 @@ def debug_replay(q, k, v, stage, count, mask=None, block_per_row=4, approx_mode=
 
 
 def debug_stages(q, k, v, mask=None, block_per_row=4, approx_mode="full", initial_prior_first_n_blocks=0,
-                 initial_prior_diagonal_n_blocks=0, score_ranking="row_normalized", scale_dim=0):
+                 initial_prior_diagonal_n_blocks=0, score_ranking="row_normalized", scale_dim=0,
+                 diag_band="symmetric"):
     """Steps 1-2 of the same kernels; returns a dict of device tensors:
     qhat, khat, vhat (full mode), count, logits, rowmax, sel, error."""
     _check_inputs(q, k, v, mask)
@@ -334,7 +381,7 @@ def debug_stages(q, k, v, mask=None, block_per_row=4, approx_mode="full", initia
     st = lib().mra_debug_stages(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), block_per_row,
                                 MODES.get(approx_mode, -1), initial_prior_first_n_blocks,
                                 initial_prior_diagonal_n_blocks, RANKINGS.get(score_ranking, -1),
-                                _ptr(r["qhat"]), _ptr(r["khat"]),
+                                BANDS.get(diag_band, -1), _ptr(r["qhat"]), _ptr(r["khat"]),
                                 _ptr(r["vhat"]), _ptr(r["count"]), _ptr(r["logits"]), _ptr(r["rowmax"]),
                                 _ptr(r["sel"]), _ptr(r["error"]), _ptr(ws), ws_bytes, _stream(q))
     _check(st, "mra_debug_stages")
@@ -343,7 +390,7 @@ def debug_stages(q, k, v, mask=None, block_per_row=4, approx_mode="full", initia
 
 
 def debug_select(logits, count, batch, heads, block_per_row=4, initial_prior_first_n_blocks=0,
-                 initial_prior_diagonal_n_blocks=0, score_ranking="row_normalized"):
+                 initial_prior_diagonal_n_blocks=0, score_ranking="row_normalized", diag_band="symmetric"):
     """The step-2 selector alone on given fp32 logits [B, H, nb, nb] and
     int32 counts [B, nb] (device tensors).  Returns sel [B, H, K] int32."""
     nb = logits.shape[-1]
@@ -359,7 +406,8 @@ def debug_select(logits, count, batch, heads, block_per_row=4, initial_prior_fir
     dims = _dims(batch, heads, N, 64, 1)
     st = lib().mra_debug_select(ctypes.byref(dims), _ptr(logits), _ptr(count), block_per_row,
                                 initial_prior_first_n_blocks, initial_prior_diagonal_n_blocks,
-                                RANKINGS.get(score_ranking, -1), _ptr(sel), _ptr(ws), ws_bytes, _stream(logits))
+                                RANKINGS.get(score_ranking, -1), BANDS.get(diag_band, -1), _ptr(sel), _ptr(ws),
+                                ws_bytes, _stream(logits))
     _check(st, "mra_debug_select")
     return sel[:, :, :K]
 
@@ -397,6 +445,7 @@ def prepare_bigbird(q, k, v, rand_blocks, mask=None, block_size=64, out=None, wo
         st = fn(*args)
         if st != 0:
             raise MraError(st, "mra_bigbird_fwd")
+        _check_device(workspace, "mra_bigbird_fwd")
         return keep[6]
 
     return call, out
@@ -442,4 +491,5 @@ def bigbird_backward(q, k, v, out, dout, workspace, num_random_blocks, mask=None
                                _ptr(workspace), workspace.numel(), _ptr(bwd_workspace), bwd_workspace.numel(),
                                _stream(q))
     _check(st, "mra_bigbird_bwd")
+    _check_device(workspace, "mra_bigbird_bwd")
     return dq, dk, dv

@@ -20,7 +20,7 @@
 namespace mra {
 namespace {
 
-constexpr int32_t kAbiVersion = 3;
+constexpr int32_t kAbiVersion = 4;
 constexpr int32_t kMaxSeqLen = 16384;
 
 size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -129,7 +129,8 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
 
 Params make_params(const mra_dims& d, const Layout& L, int32_t mode, int32_t pf, int32_t pd, const void* q,
-                   const void* k, const void* v, const uint8_t* mask, void* out, void* ws, int32_t ranking = 0) {
+                   const void* k, const void* v, const uint8_t* mask, void* out, void* ws, int32_t ranking = 0,
+                   int32_t band = MRA_BAND_SYMMETRIC, int32_t save_stats = 0) {
     Params p;
     memset(&p, 0, sizeof(p));
     unsigned char* w = static_cast<unsigned char*>(ws);
@@ -142,6 +143,8 @@ Params make_params(const mra_dims& d, const Layout& L, int32_t mode, int32_t pf,
     p.prior_first = pf;
     p.prior_diag = pd;
     p.rank_raw = ranking == MRA_RANK_RAW_LOGITS ? 1 : 0;
+    p.band_exact = band == MRA_BAND_EXACT ? 1 : 0;
+    p.save_stats = save_stats ? 1 : 0;
     p.max_items = L.max_items;
     p.attn_wph = attn_grid_waves_per_head(L.BH, L.K);
     p.attn_seq = attn_heads_in_turn(L.BH, L.K) ? 1 : 0;
@@ -192,8 +195,13 @@ mra_status check_call(const mra_dims* dims, const void* q, const void* k, const 
     if (((uintptr_t)ws & 255u) != 0) return MRA_ERR_ALIGN;
     const size_t esz = dims->dtype == MRA_BF16 ? 2 : 4;
     const size_t tb = (size_t)dims->batch * dims->heads * dims->seq_len * dims->head_dim * esz;
+    const size_t mb = (size_t)dims->batch * dims->seq_len;
     if (out && (overlaps(out, tb, q, tb) || overlaps(out, tb, k, tb) || overlaps(out, tb, v, tb) ||
-                overlaps(out, tb, mask, (size_t)dims->batch * dims->seq_len) || overlaps(out, tb, ws, ws_bytes)))
+                overlaps(out, tb, mask, mb) || overlaps(out, tb, ws, ws_bytes)))
+        return MRA_ERR_ALIAS;
+    // the kernels write the workspace while the inputs are still being read
+    if (overlaps(ws, ws_bytes, q, tb) || overlaps(ws, ws_bytes, k, tb) || overlaps(ws, ws_bytes, v, tb) ||
+        overlaps(ws, ws_bytes, mask, mb))
         return MRA_ERR_ALIAS;
     return MRA_OK;
 }
@@ -264,18 +272,23 @@ static mra_status run_front(const Params& p, hipStream_t s) {
     return MRA_OK;
 }
 
+static bool bad_ranking(int32_t r) { return r != MRA_RANK_ROW_NORMALIZED && r != MRA_RANK_RAW_LOGITS; }
+static bool bad_band(int32_t b) { return b != MRA_BAND_SYMMETRIC && b != MRA_BAND_EXACT; }
+
 // The launch sequence; ev (10 events or null) brackets each stage.
 static mra_status run_forward(const mra_dims* dims, const void* q, const void* k, const void* v,
                               const uint8_t* mask, int32_t block_per_row, int32_t approx_mode, int32_t prior_first,
                               int32_t prior_diag, void* out, void* workspace, size_t workspace_bytes, void* stream,
-                              void* const* ev, int32_t ranking = MRA_RANK_ROW_NORMALIZED) {
+                              void* const* ev, int32_t ranking = MRA_RANK_ROW_NORMALIZED,
+                              int32_t band = MRA_BAND_SYMMETRIC, int32_t save_stats = 0) {
     Layout L;
     mra_status st = check_call(dims, q, k, v, mask, block_per_row, approx_mode, prior_first, prior_diag, out,
                                workspace, workspace_bytes, true, &L);
     if (st != MRA_OK) return st;
-    if (ranking != MRA_RANK_ROW_NORMALIZED && ranking != MRA_RANK_RAW_LOGITS) return MRA_ERR_MODE;
+    if (bad_ranking(ranking)) return MRA_ERR_MODE;
+    if (bad_band(band)) return MRA_ERR_PRIOR;
     const Params p = make_params(*dims, L, approx_mode, prior_first, prior_diag, q, k, v, mask, out, workspace,
-                                 ranking);
+                                 ranking, band, save_stats);
     hipStream_t s = static_cast<hipStream_t>(stream);
     auto mark = [&](int idx) {
         return (ev && ev[idx]) ? hipEventRecord(static_cast<hipEvent_t>(ev[idx]), s) : hipSuccess;
@@ -312,7 +325,8 @@ MRA_API mra_status mra_attention_fwd_ex(const mra_dims* dims, const void* q, con
                                         size_t workspace_bytes, void* stream) {
     if (!opts) return MRA_ERR_NULL;
     return run_forward(dims, q, k, v, mask, opts->block_per_row, opts->approx_mode, opts->prior_first,
-                       opts->prior_diag, out, workspace, workspace_bytes, stream, nullptr, opts->score_ranking);
+                       opts->prior_diag, out, workspace, workspace_bytes, stream, nullptr, opts->score_ranking,
+                       opts->diag_band, opts->save_stats);
 }
 
 MRA_API mra_status mra_attention_fwd_profiled(const mra_dims* dims, const void* q, const void* k, const void* v,
@@ -356,12 +370,12 @@ static mra_status run_bwd(const mra_dims* dims, const void* q, const void* k, co
     if (misaligned(bwd_workspace)) return MRA_ERR_ALIGN;
     const size_t tb = (size_t)dims->batch * dims->heads * dims->seq_len * dims->head_dim *
                       (dims->dtype == MRA_BF16 ? 2 : 4);
-    const void* ins[] = {q, k, v, out, dout, workspace};
-    const size_t insz[] = {tb, tb, tb, tb, tb, workspace_bytes};
+    const void* ins[] = {q, k, v, out, dout, workspace, mask};
+    const size_t insz[] = {tb, tb, tb, tb, tb, workspace_bytes, (size_t)dims->batch * dims->seq_len};
     void* outs[] = {dq, dk, dv, bwd_workspace};
     const size_t outsz[] = {tb, tb, tb, bwd_workspace_bytes};
     for (int a = 0; a < 4; a++) {
-        for (int c = 0; c < 6; c++)
+        for (int c = 0; c < 7; c++)
             if (overlaps(outs[a], outsz[a], ins[c], insz[c])) return MRA_ERR_ALIAS;
         for (int c = a + 1; c < 4; c++)
             if (overlaps(outs[a], outsz[a], outs[c], outsz[c])) return MRA_ERR_ALIAS;
@@ -461,7 +475,9 @@ MRA_API mra_status mra_bigbird_fwd(const mra_dims* dims, const void* q, const vo
     if (overlaps(out, (size_t)L.BH * L.N * L.d * (dims->dtype == MRA_BF16 ? 2 : 4), rand_blocks, rbytes) ||
         overlaps(workspace, workspace_bytes, rand_blocks, rbytes))
         return MRA_ERR_ALIAS;
-    Params p = make_params(*dims, L, MRA_APPROX_SPARSE, 0, 0, q, k, v, mask, out, workspace);
+    // the backward pass of a BigBird call reads its statistics: always kept
+    Params p = make_params(*dims, L, MRA_APPROX_SPARSE, 0, 0, q, k, v, mask, out, workspace, MRA_RANK_ROW_NORMALIZED,
+                           MRA_BAND_SYMMETRIC, 1);
     p.attn_dyn = 1;
     p.bb_f = block_size / kBlock;
     p.bb_r = num_random_blocks;
@@ -500,6 +516,18 @@ MRA_API mra_status mra_bigbird_bwd(const mra_dims* dims, const void* q, const vo
                    workspace_bytes, bwd_workspace, bwd_workspace_bytes, stream);
 }
 
+MRA_API mra_status mra_workspace_error(const void* workspace, size_t workspace_bytes, void* stream,
+                                       uint32_t* error) {
+    if (!workspace || !error) return MRA_ERR_NULL;
+    if (workspace_bytes < 256) return MRA_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (hipStreamSynchronize(s) != hipSuccess) return MRA_ERR_HIP;
+    uint32_t word = 0;
+    if (hipMemcpy(&word, workspace, 4, hipMemcpyDeviceToHost) != hipSuccess) return MRA_ERR_HIP;
+    *error = word;
+    return MRA_OK;
+}
+
 MRA_API mra_status mra_debug_replay(const mra_dims* dims, const void* q, const void* k, const void* v,
                                     const uint8_t* mask, int32_t block_per_row, int32_t approx_mode,
                                     int32_t prior_first, int32_t prior_diag, void* out, void* workspace,
@@ -518,17 +546,18 @@ MRA_API mra_status mra_debug_replay(const mra_dims* dims, const void* q, const v
 
 MRA_API mra_status mra_debug_stages(const mra_dims* dims, const void* q, const void* k, const void* v,
                                     const uint8_t* mask, int32_t block_per_row, int32_t approx_mode,
-                                    int32_t prior_first, int32_t prior_diag, int32_t score_ranking, float* qhat,
-                                    float* khat, float* vhat, int32_t* count, float* logits, float* rowmax,
-                                    int32_t* sel, int32_t* error, void* workspace, size_t workspace_bytes,
-                                    void* stream) {
+                                    int32_t prior_first, int32_t prior_diag, int32_t score_ranking,
+                                    int32_t diag_band, float* qhat, float* khat, float* vhat, int32_t* count,
+                                    float* logits, float* rowmax, int32_t* sel, int32_t* error, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
     Layout L;
     mra_status st = check_call(dims, q, k, v, mask, block_per_row, approx_mode, prior_first, prior_diag,
                                nullptr, workspace, workspace_bytes, false, &L);
     if (st != MRA_OK) return st;
-    if (score_ranking != MRA_RANK_ROW_NORMALIZED && score_ranking != MRA_RANK_RAW_LOGITS) return MRA_ERR_MODE;
+    if (bad_ranking(score_ranking)) return MRA_ERR_MODE;
+    if (bad_band(diag_band)) return MRA_ERR_PRIOR;
     const Params p = make_params(*dims, L, approx_mode, prior_first, prior_diag, q, k, v, mask, nullptr,
-                                 workspace, score_ranking);
+                                 workspace, score_ranking, diag_band);
     hipStream_t s = static_cast<hipStream_t>(stream);
     st = run_front(p, s);
     if (st != MRA_OK) return st;
@@ -556,20 +585,21 @@ MRA_API mra_status mra_debug_stages(const mra_dims* dims, const void* q, const v
 
 MRA_API mra_status mra_debug_select(const mra_dims* dims, const float* logits, const int32_t* count,
                                     int32_t block_per_row, int32_t prior_first, int32_t prior_diag,
-                                    int32_t score_ranking, int32_t* sel, void* workspace, size_t workspace_bytes,
-                                    void* stream) {
+                                    int32_t score_ranking, int32_t diag_band, int32_t* sel, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
     mra_status st = check_dims(dims);
     if (st != MRA_OK) return st;
     st = check_params(block_per_row, MRA_APPROX_SPARSE, prior_first, prior_diag);
     if (st != MRA_OK) return st;
-    if (score_ranking != MRA_RANK_ROW_NORMALIZED && score_ranking != MRA_RANK_RAW_LOGITS) return MRA_ERR_MODE;
+    if (bad_ranking(score_ranking)) return MRA_ERR_MODE;
+    if (bad_band(diag_band)) return MRA_ERR_PRIOR;
     if (!logits || !count || !sel) return MRA_ERR_NULL;
     Layout L;
     if (!carve(*dims, block_per_row, MRA_APPROX_SPARSE, &L)) return MRA_ERR_SEQ_LEN;
     if (!workspace || workspace_bytes < L.total) return MRA_ERR_WORKSPACE;
     if (((uintptr_t)workspace & 255u) != 0) return MRA_ERR_ALIGN;
     Params p = make_params(*dims, L, MRA_APPROX_SPARSE, prior_first, prior_diag, nullptr, nullptr, nullptr,
-                           nullptr, nullptr, workspace, score_ranking);
+                           nullptr, nullptr, workspace, score_ranking, diag_band);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const size_t BH = (size_t)L.BH, nb = (size_t)L.nb;
     hipError_t e = hipMemcpyAsync(p.logits, logits, BH * nb * nb * 4, hipMemcpyDeviceToDevice, s);

@@ -282,7 +282,7 @@ __device__ __forceinline__ void finish_segment(const Params& p, const Wave<DT, H
         }
         const float inv = (valid && den > 0.f) ? 1.0f / den : 0.f;
         const float sa = a * inv, sb = bw * inv;
-        if (h == 0) {   // the token's softmax statistics, for the backward pass
+        if (h == 0 && p.save_stats) {   // the token's softmax statistics, for the backward pass
             const size_t st = (size_t)W.bh * p.N + tok;
             p.st_m[st] = Mu == -__builtin_inff() ? 0.f : Mu;
             p.st_linv[st] = inv;

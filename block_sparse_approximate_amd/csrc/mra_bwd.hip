@@ -366,6 +366,8 @@ __global__ __launch_bounds__(kTrThreads) void plan_kernel(Params p) {
         // a static layout fills row_ptr[nb] of the stream's capacity K
         const int want = p.attn_dyn ? min(rp[nb], K) : K;
         if (tot_c != want || tot_r > maxch || tot_cc > maxch) atomicOr(reinterpret_cast<unsigned int*>(p.error), 8u);
+        // the forward must have kept each token's softmax statistics
+        if (p.error[1] != 1) atomicOr(reinterpret_cast<unsigned int*>(p.error), 16u);
     }
 }
 

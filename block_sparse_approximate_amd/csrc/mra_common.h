@@ -66,6 +66,8 @@ struct Params {
     int32_t dtype;         // 0 fp32, 1 bf16
     int32_t prior_first, prior_diag;
     int32_t rank_raw;      // 1: step 2 ranks the raw low-res logits (no row max subtracted)
+    int32_t band_exact;    // 1: the diagonal prior band is exactly prior_diag blocks wide
+    int32_t save_stats;    // 1: store each token's softmax statistics (st_m, st_linv) for the backward
     int32_t max_items;
     const void* q;
     const void* k;
@@ -127,7 +129,8 @@ struct Params {
     float* bwd_dqh;        // [BH, nb, d]  gradients of the block means qhat, khat, vhat
     float* bwd_dkh;
     float* bwd_dvh;
-    int32_t* error;        // device error flag (0 = fine)
+    int32_t* error;        // device error word (0 = fine; bits MRA_DEVERR_*), then at error[1] the
+                           //   forward's save_stats (the backward checks it)
     int32_t attn_dyn;      // 1: a head's stream holds row_ptr[nb] records (a static layout), not K
     int32_t bb_f;          // BigBird layout: pattern block = bb_f blocks of 32 tokens
     int32_t bb_r;          //   random picks per pattern row
@@ -145,14 +148,17 @@ __device__ __forceinline__ uint32_t float_key(float s) {
 // Step 2 score of cell (i, j) ([MRA] "第二步"): row-max-normalised low-res
 // logit (raw: the logit itself) plus 5000 per prior that covers the cell;
 // -inf for empty blocks;
-// -0 folded to +0.  The fp32 operations and their order are fixed (this
-// translation unit is built with -ffp-contract=off).
+// -0 folded to +0.  The diagonal band of pd blocks is |i - j| <= pd / 2, or
+// with `exact` exactly pd blocks wide: -(pd - 1) / 2 <= j - i <= pd / 2.
+// The fp32 operations and their order are fixed (this translation unit is
+// built with -ffp-contract=off).
 __device__ __forceinline__ float cell_score(float logit, float m, int i, int j, bool vi, bool vj,
-                                            int pf, int pd, bool raw) {
+                                            int pf, int pd, bool raw, bool exact) {
     if (!vi || !vj) return -__builtin_inff();
     float s = raw ? logit : logit - m;
-    int dist = i > j ? i - j : j - i;
-    if (pd > 0 && dist <= pd / 2) s = s + kPriorBias;
+    const int dist = i > j ? i - j : j - i;
+    const bool band = exact ? (j - i >= -((pd - 1) / 2) && j - i <= pd / 2) : dist <= pd / 2;
+    if (pd > 0 && band) s = s + kPriorBias;
     if (i < pf) s = s + kPriorBias;
     if (j < pf) s = s + kPriorBias;
     if (s == 0.0f) s = 0.0f;

@@ -124,7 +124,7 @@ __device__ void merge_row(const Params& p, int bh, int4 dsc, float* lo, float* l
     const bool valid = (qm >> t) & 1u;
     const float inv = (valid && den > 0.f) ? 1.0f / den : 0.f;
     const size_t orow = ((size_t)bh * p.N + (size_t)i * kBlock + t) * HD + cg;
-    if ((tid & 7) == 0) {   // the token's softmax statistics, for the backward pass
+    if ((tid & 7) == 0 && p.save_stats) {   // the token's softmax statistics, for the backward pass
         const size_t st = (size_t)bh * p.N + (size_t)i * kBlock + t;
         p.st_m[st] = Mu == -__builtin_inff() ? 0.f : Mu;
         p.st_linv[st] = inv;

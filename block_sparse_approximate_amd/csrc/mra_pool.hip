@@ -24,7 +24,7 @@ __host__ __device__ constexpr int pool_blocks(int hd) { return kPoolThreads / (h
 
 template <int DT, int HD>  // DT: 0 = fp32, 1 = bf16; HD: channels per head
 __global__ __launch_bounds__(kPoolThreads) void pool_kernel(Params p, int ntens, int groups_per_head,
-                                                            int zero_words) {
+                                                            size_t zero_words) {
     constexpr int kPoolBlocks = pool_blocks(HD);
     constexpr int kEs = DT == 1 ? 2 : 4;              // bytes per element
     constexpr int kBlockBytes = kBlock * HD * kEs;    // 4 to 16 KiB
@@ -34,10 +34,13 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(Params p, int ntens,
     // Clear the selection histogram and candidate counts for the next stages
     // (stream order makes this visible to them).
     {
-        const int gt = blockIdx.x * kPoolThreads + threadIdx.x;
-        const int stride = gridDim.x * kPoolThreads;
-        if (gt == 0) *p.error = 0;
-        for (int w = gt; w < zero_words; w += stride) p.hist[w] = 0u;
+        const size_t gt = (size_t)blockIdx.x * kPoolThreads + threadIdx.x;
+        const size_t stride = (size_t)gridDim.x * kPoolThreads;
+        if (gt == 0) {
+            p.error[0] = 0;
+            p.error[1] = p.save_stats;   // the backward checks that the statistics were kept
+        }
+        for (size_t w = gt; w < zero_words; w += stride) p.hist[w] = 0u;
         if (gt < p.BH) p.ncand[(size_t)gt * kCandStride] = 0u;
     }
     // workgroup g runs on XCD g % 8; every workgroup of head bh goes to XCD
@@ -116,7 +119,7 @@ static hipError_t launch_pool_t(const Params& p, hipStream_t s) {
     const int ntens = p.mode == 0 ? 3 : 2;
     const int groups_per_head = (p.nb + pool_blocks(HD) - 1) / pool_blocks(HD);
     const int grid = 8 * ((p.BH + 7) / 8) * ntens * groups_per_head;
-    const int zero_words = p.BH * kHistBins;
+    const size_t zero_words = (size_t)p.BH * kHistBins;
     if (p.dtype == 1)
         hipLaunchKernelGGL((pool_kernel<1, HD>), dim3(grid), dim3(kPoolThreads), 0, s, p, ntens, groups_per_head,
                            zero_words);

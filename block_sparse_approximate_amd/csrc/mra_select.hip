@@ -523,7 +523,7 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(Params p) {
     float* Sg = p.logits + (size_t)bh * nb * nb;
     uint32_t* Kg = p.keys + (size_t)bh * nb * nb;
     const int pf = p.prior_first, pd = p.prior_diag;
-    const bool raw = p.rank_raw != 0;
+    const bool raw = p.rank_raw != 0, exact = p.band_exact != 0;
 #pragma unroll
     for (int t = 0; t < kMaxColTiles; t++) {
 #pragma unroll
@@ -533,7 +533,8 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(Params p) {
                 const float sv = sc[t][q];
                 if (!kGiven) Sg[(size_t)i * nb + j] = sv;
                 const int cjq = (q & 1) ? cj[t].y : cj[t].x;
-                const float s = cell_score(sv, q < 2 ? ma : mb, i, j, (q < 2 ? cia : cib) > 0, cjq > 0, pf, pd, raw);
+                const float s = cell_score(sv, q < 2 ? ma : mb, i, j, (q < 2 ? cia : cib) > 0, cjq > 0, pf, pd, raw,
+                                           exact);
                 const uint32_t key = float_key(s);
                 Kg[(size_t)i * nb + j] = key;
                 atomicAdd(&hist[key >> (32 - kHistBits)], 1u);
@@ -1070,7 +1071,10 @@ __global__ __launch_bounds__(kSelThreads) void bigbird_layout_kernel(Params p) {
     // the device error word starts clear (pooling clears it on the MRA path);
     // this kernel cannot set a bit of its own, since the stream is sized for
     // the pattern's largest count, so the attention kernel's bits stay exact
-    if (bh == 0 && tid == 0) *p.error = 0;
+    if (bh == 0 && tid == 0) {
+        p.error[0] = 0;
+        p.error[1] = p.save_stats;
+    }
     const SelectLds L = select_lds(nb);
     uint32_t* bitmap = reinterpret_cast<uint32_t*>(smem + L.bitmap);
     int* rc = reinterpret_cast<int*>(smem + L.rc);

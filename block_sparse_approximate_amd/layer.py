@@ -36,7 +36,7 @@ class MraAttentionFunction(torch.autograd.Function):
         ws = torch.empty(workspace_size(B, H, N, d, q.dtype, block_per_row, approx_mode), dtype=torch.uint8,
                          device=q.device)
         out = attention(q, k, v, mask, block_per_row, approx_mode, prior_first, prior_diag, workspace=ws,
-                        score_ranking=score_ranking, scale_dim=scale_dim)
+                        score_ranking=score_ranking, scale_dim=scale_dim, save_stats=True)
         ctx.save_for_backward(q, k, v, out, ws, mask if mask is not None else torch.empty(0, device=q.device))
         ctx.has_mask = mask is not None
         ctx.args = (block_per_row, approx_mode, prior_first, prior_diag, scale_dim)

@@ -25,7 +25,8 @@
  * selection ranks the row-max-normalised low-res logits; ties at the k-th
  * score go to the smaller flat index i*nb + j; the first-n prior adds 5000
  * to rows i < n and again to columns j < n; the diagonal prior covers
- * |i - j| <= floor(n/2); a low-res cell weighs cnt_j * exp(logit); an empty
+ * |i - j| <= floor(n/2) (or, as an option, a band exactly n blocks wide);
+ * a low-res cell weighs cnt_j * exp(logit); an empty
  * block scores -inf; padded query rows output 0; 0/0 gives 0.
  *
  * Conventions for every entry point:
@@ -62,13 +63,39 @@ typedef enum {
     MRA_ERR_DTYPE = 5,      /* dtype not MRA_F32 or MRA_BF16 */
     MRA_ERR_MODE = 6,       /* approx_mode not MRA_APPROX_FULL or MRA_APPROX_SPARSE */
     MRA_ERR_BUDGET = 7,     /* block_per_row < 1 (BigBird: num_random_blocks < 1) */
-    MRA_ERR_PRIOR = 8,      /* a prior count < 0 */
+    MRA_ERR_PRIOR = 8,      /* a prior count < 0, or an unknown diagonal band reading */
     MRA_ERR_ALIAS = 9,      /* an output overlaps an input, another output or a workspace */
     MRA_ERR_WORKSPACE = 10, /* a workspace NULL or smaller than its size query returns */
     MRA_ERR_HIP = 11,       /* a HIP call failed */
     MRA_ERR_ALIGN = 12,     /* a tensor pointer is not 16-byte aligned */
     MRA_ERR_STAGE = 13      /* mra_debug_replay: a stage other than 3 or 4, or count < 1 */
 } mra_status;
+
+/* Bits of a workspace's device error word (mra_workspace_error).  The
+ * kernels check their own bookkeeping as they run and set a bit when it does
+ * not add up; every bit means the call's outputs are undefined.
+ *   MRA_DEVERR_CANDIDATES  selector: the boundary bin's candidate list does
+ *                          not hold the bin's count (selection undefined)
+ *   MRA_DEVERR_STREAM      selector or layout: the selection does not hold
+ *                          num_block cells (BigBird: more than its capacity),
+ *                          or a head needs more segments than the workspace
+ *                          holds (selection and output undefined)
+ *   MRA_DEVERR_WINDOW      block attention: a wave's share of a head's blocks
+ *                          does not fit its record window; that wave wrote
+ *                          none of its rows (output undefined)
+ *   MRA_DEVERR_BWD_PLAN    backward: the transposed selection or the chunk
+ *                          plan does not match the forward's selection
+ *                          (gradients undefined)
+ *   MRA_DEVERR_NO_STATS    backward: the forward call did not save the
+ *                          softmax statistics (mra_options.save_stats = 0;
+ *                          gradients undefined) */
+enum {
+    MRA_DEVERR_CANDIDATES = 1,
+    MRA_DEVERR_STREAM = 2,
+    MRA_DEVERR_WINDOW = 4,
+    MRA_DEVERR_BWD_PLAN = 8,
+    MRA_DEVERR_NO_STATS = 16
+};
 
 typedef enum { MRA_F32 = 0, MRA_BF16 = 1 } mra_dtype;
 typedef enum { MRA_APPROX_FULL = 0, MRA_APPROX_SPARSE = 1 } mra_approx_mode;
@@ -80,14 +107,29 @@ typedef enum { MRA_APPROX_FULL = 0, MRA_APPROX_SPARSE = 1 } mra_approx_mode;
  * ranks the raw logits themselves.  Priors and empty blocks apply to both. */
 typedef enum { MRA_RANK_ROW_NORMALIZED = 0, MRA_RANK_RAW_LOGITS = 1 } mra_score_ranking;
 
+/* Width of the diagonal prior band of initial_prior_diagonal_n_blocks = n
+ * ([MRA] "第二步": a band of blocks centred on the main diagonal).  For odd n
+ * both readings are the band |i - j| <= (n - 1) / 2.  For even n a band
+ * centred on the diagonal cannot be exactly n blocks wide and symmetric:
+ *   MRA_BAND_SYMMETRIC  |i - j| <= floor(n / 2), n + 1 blocks wide (default);
+ *   MRA_BAND_EXACT      exactly n blocks wide, offsets j - i from
+ *                       -floor((n - 1) / 2) to +floor(n / 2). */
+typedef enum { MRA_BAND_SYMMETRIC = 0, MRA_BAND_EXACT = 1 } mra_diag_band;
+
 /* The selection options of mra_attention_fwd_ex: the four MraConfig
- * parameters and the ranking. */
+ * parameters, the ranking, the band reading, and whether to keep what the
+ * backward pass needs. */
 typedef struct {
     int32_t block_per_row;
     int32_t approx_mode;     /* mra_approx_mode */
     int32_t prior_first;     /* initial_prior_first_n_blocks */
     int32_t prior_diag;      /* initial_prior_diagonal_n_blocks */
     int32_t score_ranking;   /* mra_score_ranking; MRA_ERR_MODE if neither */
+    int32_t diag_band;       /* mra_diag_band; MRA_ERR_PRIOR if neither */
+    int32_t save_stats;      /* 1: also store each token's softmax maximum and
+                                1/normaliser in the workspace, for
+                                mra_attention_bwd; 0: inference only (the
+                                backward then flags MRA_DEVERR_NO_STATS) */
 } mra_options;
 
 typedef struct {
@@ -127,18 +169,25 @@ mra_status mra_workspace_size(const mra_dims* dims, int32_t block_per_row, int32
  *                parameters (block_per_row >= 1, priors >= 0)
  *   out          device, [B, H, N, d], dtype dims->dtype; written in full
  *   workspace    device, at least mra_workspace_size() bytes, 256-byte
- *                aligned; its contents need not be initialised
- *   stream       hipStream_t or NULL */
+ *                aligned, overlapping no input or output (MRA_ERR_ALIAS);
+ *                its contents need not be initialised
+ *   stream       hipStream_t or NULL
+ * The default options of mra_attention_fwd_ex: row-normalised ranking, the
+ * symmetric band, and no softmax statistics kept (inference); a forward
+ * call whose output is to be differentiated goes through
+ * mra_attention_fwd_ex with save_stats = 1. */
 mra_status mra_attention_fwd(const mra_dims* dims, const void* q, const void* k, const void* v,
                              const uint8_t* mask, int32_t block_per_row, int32_t approx_mode,
                              int32_t prior_first, int32_t prior_diag, void* out, void* workspace,
                              size_t workspace_bytes, void* stream);
 
-/* mra_attention_fwd with its selection options in a struct (opts: host
- * pointer, read during the call), which adds the choice of ranking;
- * MRA_ERR_NULL when opts is NULL.  With MRA_RANK_ROW_NORMALIZED it is
- * exactly mra_attention_fwd.  The backward pass reads the selection the
- * forward made, so it needs no ranking of its own. */
+/* mra_attention_fwd with its options in a struct (opts: host pointer, read
+ * during the call), which adds the choice of ranking and band reading and
+ * the softmax statistics for the backward pass; MRA_ERR_NULL when opts is
+ * NULL.  With score_ranking = MRA_RANK_ROW_NORMALIZED, diag_band =
+ * MRA_BAND_SYMMETRIC and save_stats = 0 it is exactly mra_attention_fwd.
+ * The backward pass reads the selection the forward made, so it needs no
+ * ranking or band of its own. */
 mra_status mra_attention_fwd_ex(const mra_dims* dims, const void* q, const void* k, const void* v,
                                 const uint8_t* mask, const mra_options* opts, void* out, void* workspace,
                                 size_t workspace_bytes, void* stream);
@@ -165,11 +214,12 @@ mra_status mra_attention_fwd_profiled(const mra_dims* dims, const void* q, const
  *   sel               [B, H, num_block] int32 selected flat indices i*nb + j,
  *                     ascending
  *   error             [1] int32 device error word (0 = consistent)
- * score_ranking as in mra_options; the other arguments are as for
- * mra_attention_fwd. */
+ * score_ranking and diag_band as in mra_options; the other arguments are as
+ * for mra_attention_fwd. */
 mra_status mra_debug_stages(const mra_dims* dims, const void* q, const void* k, const void* v,
                             const uint8_t* mask, int32_t block_per_row, int32_t approx_mode,
-                            int32_t prior_first, int32_t prior_diag, int32_t score_ranking, float* qhat, float* khat,
+                            int32_t prior_first, int32_t prior_diag, int32_t score_ranking,
+                            int32_t diag_band, float* qhat, float* khat,
                             float* vhat, int32_t* count, float* logits, float* rowmax, int32_t* sel,
                             int32_t* error, void* workspace, size_t workspace_bytes, void* stream);
 
@@ -177,11 +227,12 @@ mra_status mra_debug_stages(const mra_dims* dims, const void* q, const void* k, 
  * result can be compared with the oracle's on identical fp32 inputs.
  *   logits  device [B, H, nb, nb] fp32, count device [B, nb] int32
  *   sel     device [B, H, num_block] int32, ascending flat indices
- * seq_len = 32 * nb comes from dims; q/k/v are not read. */
+ * seq_len = 32 * nb comes from dims; q/k/v are not read; score_ranking and
+ * diag_band as in mra_options. */
 mra_status mra_debug_select(const mra_dims* dims, const float* logits, const int32_t* count,
                             int32_t block_per_row, int32_t prior_first, int32_t prior_diag,
-                            int32_t score_ranking, int32_t* sel, void* workspace, size_t workspace_bytes,
-                            void* stream);
+                            int32_t score_ranking, int32_t diag_band, int32_t* sel, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /* BigBird block-sparse attention through the same block-attention kernels
  * (page "Transformers 中的 BigBird：面向超长序列的稀疏注意力模型完全指南",
@@ -242,7 +293,9 @@ mra_status mra_backward_workspace_size(const mra_dims* dims, int32_t block_per_r
  *   dout      [B, H, N, d] dL/d out;
  *   dq, dk, dv [B, H, N, d] gradients, written (in the dtype of dims);
  *   workspace the workspace that forward call filled (its selection and
- *             each token's softmax statistics), unchanged since; read only;
+ *             each token's softmax statistics, so a forward call made with
+ *             save_stats = 1), unchanged since; read only except for its
+ *             device error word, where the backward's own checks add bits;
  *   bwd_workspace  device scratch of mra_backward_workspace_size bytes
  *             (16-byte aligned, caller-owned, no contents kept between
  *             calls; MRA_ERR_WORKSPACE if smaller).
@@ -258,6 +311,17 @@ mra_status mra_attention_bwd(const mra_dims* dims, const void* q, const void* k,
                              int32_t prior_first, int32_t prior_diag, const void* out, const void* dout,
                              void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                              void* bwd_workspace, size_t bwd_workspace_bytes, void* stream);
+
+/* The device error word of a workspace (a forward call's; the backward
+ * passes that read it add their bits there too): waits for `stream` to
+ * finish its queued work, then copies the word to *error (host pointer).
+ * 0 means every kernel's bookkeeping added up; any MRA_DEVERR_ bit means the
+ * outputs of the call that set it are undefined.  The word is cleared by
+ * the next forward call on the workspace.  MRA_ERR_NULL / MRA_ERR_WORKSPACE
+ * for a missing pointer or a workspace smaller than 256 bytes,
+ * MRA_ERR_HIP if the wait or the copy fails. */
+mra_status mra_workspace_error(const void* workspace, size_t workspace_bytes, void* stream,
+                               uint32_t* error);
 
 /* Timing hook: relaunches one stage of the forward pass `count` times in a
  * row on `stream`, on a workspace that a call of mra_attention_fwd with the

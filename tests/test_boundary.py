@@ -23,11 +23,11 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     L = mra.lib()
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(mra.SIGNATURES)
-    assert L.mra_abi_version() == 3
+    assert L.mra_abi_version() == 4
 
 
 def test_status_strings():
@@ -96,6 +96,8 @@ def call(dims=(1, 2, 512, 64, 1), q=Q, k=K, v=V, mask=None, bpr=4, mode=0, pf=0,
     (dict(out=Q), 9), (dict(out=W), 9), (dict(out=Q + 4096), 9),
     (dict(ws=None), 10), (dict(ws_bytes=1024), 10),
     (dict(q=Q + 8), 12), (dict(mask=0x60000004), 12), (dict(ws=W + 16), 12),
+    # the workspace is written while the inputs are read: it may overlap none of them
+    (dict(ws=Q - 256), 9), (dict(ws=V + 4096, ws_bytes=1 << 20), 9), (dict(mask=W + 4096), 9),
 ])
 def test_attention_fwd_rejects_bad_arguments(kw, status):
     assert call(**kw) == status
@@ -109,7 +111,7 @@ def call_ex(opts=(4, 0, 0, 0, 1), **kw):
 
 @pytest.mark.parametrize("opts,status", [
     (None, 1), ((4, 0, 0, 0, 2), 6), ((4, 0, 0, 0, -1), 6), ((4, 3, 0, 0, 1), 6), ((0, 0, 0, 0, 1), 7),
-    ((4, 1, -1, 0, 1), 8),
+    ((4, 1, -1, 0, 1), 8), ((4, 0, 0, 2, 0, 2, 0), 8), ((4, 0, 0, 2, 0, -1, 1), 8),
 ])
 def test_attention_fwd_ex_rejects_bad_options(opts, status):
     assert call_ex(opts) == status
@@ -131,11 +133,12 @@ def test_null_dims_rejected():
 def test_debug_select_rejects_bad_arguments():
     L = mra.lib()
     d = mra._Dims(1, 1, 512, 64, 1)
-    assert L.mra_debug_select(ctypes.byref(d), None, K, 4, 0, 0, 0, O, W, 1 << 40, None) == 1
-    assert L.mra_debug_select(ctypes.byref(d), Q, K, 4, 0, 0, 0, O, W, 16, None) == 10
-    assert L.mra_debug_select(ctypes.byref(d), Q, K, 0, 0, 0, 0, O, W, 1 << 40, None) == 7
-    assert L.mra_debug_select(ctypes.byref(d), Q, K, 4, -1, 0, 0, O, W, 1 << 40, None) == 8
-    assert L.mra_debug_select(ctypes.byref(d), Q, K, 4, 0, 0, 2, O, W, 1 << 40, None) == 6
+    assert L.mra_debug_select(ctypes.byref(d), None, K, 4, 0, 0, 0, 0, O, W, 1 << 40, None) == 1
+    assert L.mra_debug_select(ctypes.byref(d), Q, K, 4, 0, 0, 0, 0, O, W, 16, None) == 10
+    assert L.mra_debug_select(ctypes.byref(d), Q, K, 0, 0, 0, 0, 0, O, W, 1 << 40, None) == 7
+    assert L.mra_debug_select(ctypes.byref(d), Q, K, 4, -1, 0, 0, 0, O, W, 1 << 40, None) == 8
+    assert L.mra_debug_select(ctypes.byref(d), Q, K, 4, 0, 0, 2, 0, O, W, 1 << 40, None) == 6
+    assert L.mra_debug_select(ctypes.byref(d), Q, K, 4, 0, 2, 0, 3, O, W, 1 << 40, None) == 8
 
 
 def test_debug_replay_rejects_bad_arguments():
@@ -153,13 +156,16 @@ def test_debug_replay_rejects_bad_arguments():
 DO, DQ, DK, DV, BW = 0x70000000, 0x80000000, 0x90000000, 0xA0000000, 0xB0000000
 
 
+MK = 0x60000000
+
+
 def call_bwd(dims=(1, 2, 512, 64, 1), mode=1, dout=DO, dq=DQ, dk=DK, dv=DV, bw=BW, bw_bytes=None, out=O,
-             ws=W):
+             ws=W, mask=None):
     d = mra._Dims(*dims)
     ws_bytes = mra.workspace_size(1, 2, 512, approx_mode="full")   # enough for either mode
     if bw_bytes is None:
         bw_bytes = mra.backward_workspace_size(1, 2, 512)
-    return mra.lib().mra_attention_bwd(ctypes.byref(d), Q, K, V, None, 4, mode, 0, 0, out, dout, dq, dk, dv, ws,
+    return mra.lib().mra_attention_bwd(ctypes.byref(d), Q, K, V, mask, 4, mode, 0, 0, out, dout, dq, dk, dv, ws,
                                        ws_bytes, bw, bw_bytes, None)
 
 
@@ -170,6 +176,8 @@ def call_bwd(dims=(1, 2, 512, 64, 1), mode=1, dout=DO, dq=DQ, dk=DK, dv=DV, bw=B
     (dict(bw=None), 10), (dict(bw_bytes=4096), 10),
     (dict(dq=Q), 9), (dict(dk=O + 64), 9), (dict(dv=DQ), 9), (dict(dq=BW), 9), (dict(bw=DO), 9),
     (dict(dq=DQ + 8), 12), (dict(bw=BW + 8), 12),
+    # no output of the backward may overlap the mask it reads
+    (dict(mask=MK, dq=MK - 1024), 9), (dict(mask=MK, bw=MK - 256), 9), (dict(mask=DV + 64), 9),
 ])
 def test_attention_bwd_rejects_bad_arguments(kw, status):
     assert call_bwd(**kw) == status
@@ -254,3 +262,31 @@ def test_scale_dim_checks():
         assert mra.lib().mra_attention_fwd(ctypes.byref(d), Q, K, V, None, 4, 0, 0, 0, O, W, 1 << 40, None) == status
     d = mra._Dims(1, 2, 512, 64, 1, 32)
     assert mra.lib().mra_attention_fwd(ctypes.byref(d), Q, K, V, None, 4, 0, 0, 0, None, W, 1 << 40, None) == 1
+
+
+def test_workspace_error_checks_arguments():
+    # host-side checks only: none of these reaches the HIP runtime
+    L = mra.lib()
+    word = ctypes.c_uint32(7)
+    assert L.mra_workspace_error(None, 1 << 20, None, ctypes.byref(word)) == 1
+    assert L.mra_workspace_error(W, 1 << 20, None, None) == 1
+    assert L.mra_workspace_error(W, 128, None, ctypes.byref(word)) == 10
+    assert word.value == 7
+
+
+def test_device_error_bits_are_named():
+    # every bit the header documents has a name in the binding
+    text = open(HEADER).read()
+    bits = {int(v) for v in re.findall(r"MRA_DEVERR_[A-Z_]+ = (\d+)", text)}
+    assert bits == set(mra.DEVICE_ERRORS) == {1, 2, 4, 8, 16}
+
+
+def test_head_count_cap():
+    # batch * heads up to 2^20 pass the host checks (the kernels index the
+    # per-head histograms, BH * 4096 words, in 64 bits); more is rejected
+    n = ctypes.c_size_t(0)
+    d = mra._Dims(1 << 10, 1 << 10, 32, 64, 1)
+    assert mra.lib().mra_workspace_size(ctypes.byref(d), 1, 0, ctypes.byref(n)) == 0
+    assert n.value > (1 << 20) * 4096 * 4
+    d = mra._Dims(1 << 10, (1 << 10) + 1, 32, 64, 1)
+    assert mra.lib().mra_workspace_size(ctypes.byref(d), 1, 0, ctypes.byref(n)) == 2

@@ -56,7 +56,7 @@ def run_case(mra, w, seed=7, bwd_workspace=None):
               initial_prior_diagonal_n_blocks=w.prior_diag)
     ws = torch.empty(mra.workspace_size(w.B, w.H, w.N, w.d, dt, w.block_per_row, w.approx_mode),
                      dtype=torch.uint8, device="cuda")
-    out = mra.attention(q, k, v, mask, workspace=ws, **kw)
+    out = mra.attention(q, k, v, mask, workspace=ws, save_stats=True, **kw)
     g = np.random.default_rng(seed).standard_normal(q.shape).astype(np.float32)
     g = bf16_round(g) if dt == torch.bfloat16 else torch.from_numpy(g)
     dq, dk, dv = mra.attention_backward(q, k, v, out, g.to(dt).cuda(), ws, mask, bwd_workspace=bwd_workspace, **kw)

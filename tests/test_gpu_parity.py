@@ -304,3 +304,90 @@ def test_raw_ranking_selection_and_output(mra, cfg):
     # the default ranking gives a different selection here
     _, sel_default = run_oracle(w)
     assert not np.array_equal(sel, sel_default)
+
+
+# ------------------------------------ exactly n-wide diagonal band (R7') --
+@pytest.mark.parametrize("nb,bpr,pf,pd,kind", [
+    (16, 3, 0, 2, "equal"), (16, 4, 0, 4, "normal"), (128, 4, 0, 2, "normal"), (128, 4, 2, 4, "ints"),
+    (13, 2, 1, 6, "ints"), (192, 4, 0, 2, "normal"), (512, 8, 0, 4, "normal"), (128, 4, 0, 3, "normal")])
+def test_selector_exact_band_on_identical_logits(mra, nb, bpr, pf, pd, kind):
+    print("case band", nb, bpr, pf, pd, kind, flush=True)
+    rng = np.random.default_rng(nb * 13 + pd)
+    B, H = 2, 2
+    if kind == "equal":
+        S = np.zeros((B, H, nb, nb), np.float32)
+    elif kind == "ints":
+        S = rng.integers(-3, 3, (B, H, nb, nb)).astype(np.float32)
+    else:
+        S = rng.standard_normal((B, H, nb, nb)).astype(np.float32)
+    cnt = np.full((B, nb), 32, np.int32)
+    if nb > 4:
+        cnt[1, nb // 3] = 0
+    K = oracle.num_block(32 * nb, bpr)
+    got = mra.debug_select(torch.from_numpy(S).cuda(), torch.from_numpy(cnt).cuda(), B, H, bpr, pf, pd,
+                           diag_band="exact")
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    for b in range(B):
+        for h in range(H):
+            ref = oracle.select_from_logits(S[b, h], cnt[b], K, pf, pd, band="exact")
+            assert np.array_equal(got[b, h], ref), (b, h)
+    if pd % 2 == 0 and kind == "equal":
+        sym = oracle.select_from_logits(S[0, 0], cnt[0], K, pf, pd)
+        assert not np.array_equal(got[0, 0], sym)   # the two readings differ for even n
+
+
+@pytest.mark.parametrize("mode", ["sparse", "full"])
+def test_exact_band_end_to_end(mra, mode):
+    # N = 4096 with a diagonal prior of 4 blocks: selections bit-exact, output in tolerance
+    w = workloads.iid("band-exact-" + mode, 2, 4, 4096, dtype="bf16", seed=41, scale=0.5, block_per_row=4,
+                      approx_mode=mode, prior_first=1, prior_diag=4)
+    print("case band", w, flush=True)
+    r = mra.debug_stages(dev(w, "q"), dev(w, "k"), dev(w, "v"), None, block_per_row=4, approx_mode=mode,
+                         initial_prior_first_n_blocks=1, initial_prior_diagonal_n_blocks=4, diag_band="exact")
+    torch.cuda.synchronize()
+    ref, sel = run_oracle(w, band="exact")
+    assert int(r["error"][0].item()) == 0
+    assert np.array_equal(r["sel"].cpu().numpy(), sel)
+    got = run_gpu(mra, w, diag_band="exact")
+    assert_close(w, got, ref)
+    _, sel_sym = run_oracle(w)
+    assert not np.array_equal(sel, sel_sym)
+
+
+# ------------------------------------------------------ device error word --
+@pytest.mark.parametrize("cfg", NAMED)
+def test_named_workloads_leave_error_word_clear(mra, cfg):
+    # every kernel's bookkeeping adds up on the named workloads, forward and
+    # (bf16) backward
+    w = workloads.get(cfg)
+    q, k, v, mask = dev(w, "q"), dev(w, "k"), dev(w, "v"), dev_mask(w)
+    kw = dict(block_per_row=w.block_per_row, approx_mode=w.approx_mode,
+              initial_prior_first_n_blocks=w.prior_first, initial_prior_diagonal_n_blocks=w.prior_diag)
+    ws = torch.empty(mra.workspace_size(w.B, w.H, w.N, w.d, q.dtype, w.block_per_row, w.approx_mode),
+                     dtype=torch.uint8, device="cuda")
+    out = mra.attention(q, k, v, mask, workspace=ws, save_stats=True, **kw)
+    assert mra.workspace_error(ws) == 0
+    g = torch.ones_like(q)
+    mra.attention_backward(q, k, v, out, g, ws, mask, **kw)
+    assert mra.workspace_error(ws) == 0
+
+
+def test_backward_without_saved_statistics_is_flagged(mra):
+    # a forward call made for inference keeps no softmax statistics; the
+    # backward's plan kernel notices and sets MRA_DEVERR_NO_STATS
+    w = small("no-stats", 1, 2, 512, block_per_row=2)
+    q, k, v = dev(w, "q"), dev(w, "k"), dev(w, "v")
+    ws = torch.empty(mra.workspace_size(1, 2, 512, 64, q.dtype, 2, "full"), dtype=torch.uint8, device="cuda")
+    out = mra.attention(q, k, v, None, block_per_row=2, workspace=ws)
+    assert mra.workspace_error(ws) == 0
+    saved = mra.CHECK_DEVICE_ERRORS
+    mra.CHECK_DEVICE_ERRORS = False
+    try:
+        mra.attention_backward(q, k, v, out, torch.ones_like(q), ws, None, block_per_row=2, approx_mode="full")
+    finally:
+        mra.CHECK_DEVICE_ERRORS = saved
+    assert mra.workspace_error(ws) == 16
+    # the next forward call clears the word
+    mra.attention(q, k, v, None, block_per_row=2, workspace=ws, save_stats=True)
+    assert mra.workspace_error(ws) == 0

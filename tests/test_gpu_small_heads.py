@@ -73,7 +73,7 @@ def test_small_heads_backward(mra, dtype, mode):
     dt = q.dtype
     ws = torch.empty(mra.workspace_size(w.B, w.H, w.N, 64, dt, w.block_per_row, mode), dtype=torch.uint8,
                      device="cuda")
-    out = mra.attention(q, k, v, None, workspace=ws, **kw)
+    out = mra.attention(q, k, v, None, workspace=ws, save_stats=True, **kw)
     g = np.zeros(q.shape, np.float32)
     g[..., :d] = np.random.default_rng(4).standard_normal(w.q.shape).astype(np.float32)
     gt = torch.from_numpy(g).to(dt)
