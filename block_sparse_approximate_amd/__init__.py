@@ -55,6 +55,7 @@ SIGNATURES = {
                           _P, _P, _SZ, _P], ctypes.c_int),
     "mra_debug_select": ([_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P], ctypes.c_int),
     "mra_workspace_error": ([_P, _SZ, _P, ctypes.POINTER(ctypes.c_uint32)], ctypes.c_int),
+    "mra_attention_fwd_noalloc": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P], ctypes.c_int),
     "mra_bigbird_workspace_size": ([_P, _I32, _I32, ctypes.POINTER(_SZ)], ctypes.c_int),
     "mra_bigbird_fwd": ([_P, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "mra_bigbird_backward_workspace_size": ([_P, _I32, _I32, ctypes.POINTER(_SZ)], ctypes.c_int),
@@ -226,6 +227,23 @@ def attention(q, k, v, mask=None, block_per_row=4, approx_mode="full", initial_p
                                         ctypes.byref(opts), _ptr(out), _ptr(workspace), workspace.numel(), _stream(q))
         _check(st, "mra_attention_fwd_ex")
     _check_device(workspace, "mra_attention_fwd")
+    return out
+
+
+def attention_noalloc(q, k, v, mask=None, block_per_row=4, approx_mode="full", initial_prior_first_n_blocks=0,
+                      initial_prior_diagonal_n_blocks=0, out=None, scale_dim=0):
+    """attention() through mra_attention_fwd_noalloc: the library's own fixed
+    device scratch (48 MiB per GPU) serves as the workspace, so the library
+    allocates nothing; calls on one GPU must not overlap.  Returns `out`."""
+    _check_inputs(q, k, v, mask)
+    B, H, N, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    dims = _dims(B, H, N, d, DTYPES[q.dtype], scale_dim)
+    st = lib().mra_attention_fwd_noalloc(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(mask), block_per_row,
+                                         MODES.get(approx_mode, -1), initial_prior_first_n_blocks,
+                                         initial_prior_diagonal_n_blocks, _ptr(out), _stream(q))
+    _check(st, "mra_attention_fwd_noalloc")
     return out
 
 

@@ -11,6 +11,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/mra.h"
 #include "mra_common.h"
@@ -240,6 +241,7 @@ MRA_API const char* mra_status_string(int32_t s) {
         case MRA_ERR_HIP: return "a HIP launch failed";
         case MRA_ERR_ALIGN: return "a pointer is not aligned (tensors 16 bytes, workspace 256 bytes)";
         case MRA_ERR_STAGE: return "stage cannot be replayed (3 and 4 only) or count < 1";
+        case MRA_ERR_SCRATCH: return "the sizes need more workspace than the allocation-free entry point holds";
         default: return "unknown status";
     }
 }
@@ -514,6 +516,48 @@ MRA_API mra_status mra_bigbird_bwd(const mra_dims* dims, const void* q, const vo
     if (st != MRA_OK) return st;
     return run_bwd(dims, q, k, v, mask, bpr, MRA_APPROX_SPARSE, 0, 0, true, out, dout, dq, dk, dv, workspace,
                    workspace_bytes, bwd_workspace, bwd_workspace_bytes, stream);
+}
+
+// ------------------------------------------------------ allocation-free forward
+// A fixed device array serves as the workspace of mra_attention_fwd_noalloc.
+// Host code never uses the array's name as an address: each device's copy is
+// looked up once with hipGetSymbolAddress (with that device current) and
+// only that pointer is passed to kernels.
+constexpr size_t kScratchBytes = size_t(48) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+static void* g_scratch_ptr[kMaxDevices];
+static hipError_t g_scratch_err[kMaxDevices];
+static std::once_flag g_scratch_once[kMaxDevices];
+
+// This device's copy of the scratch array (null when the lookup failed).
+static void* scratch_for_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* ptr = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? ptr : nullptr;
+    });
+    return g_scratch_ptr[dev];
+}
+
+MRA_API mra_status mra_attention_fwd_noalloc(const mra_dims* dims, const void* q, const void* k, const void* v,
+                                             const uint8_t* mask, int32_t block_per_row, int32_t approx_mode,
+                                             int32_t prior_first, int32_t prior_diag, void* out, void* stream) {
+    // sizes first, so that an oversized call is refused before anything else
+    mra_status st = check_dims(dims);
+    if (st != MRA_OK) return st;
+    st = check_params(block_per_row, approx_mode, prior_first, prior_diag);
+    if (st != MRA_OK) return st;
+    Layout L;
+    if (!carve(*dims, block_per_row, approx_mode, &L)) return MRA_ERR_SEQ_LEN;
+    if (L.total > kScratchBytes) return MRA_ERR_SCRATCH;
+    void* ws = scratch_for_current_device();
+    if (!ws) return MRA_ERR_HIP;
+    return run_forward(dims, q, k, v, mask, block_per_row, approx_mode, prior_first, prior_diag, out, ws,
+                       kScratchBytes, stream, nullptr);
 }
 
 MRA_API mra_status mra_workspace_error(const void* workspace, size_t workspace_bytes, void* stream,

@@ -68,7 +68,8 @@ typedef enum {
     MRA_ERR_WORKSPACE = 10, /* a workspace NULL or smaller than its size query returns */
     MRA_ERR_HIP = 11,       /* a HIP call failed */
     MRA_ERR_ALIGN = 12,     /* a tensor pointer is not 16-byte aligned */
-    MRA_ERR_STAGE = 13      /* mra_debug_replay: a stage other than 3 or 4, or count < 1 */
+    MRA_ERR_STAGE = 13,     /* mra_debug_replay: a stage other than 3 or 4, or count < 1 */
+    MRA_ERR_SCRATCH = 14    /* mra_attention_fwd_noalloc: the sizes need more than its 48 MiB scratch */
 } mra_status;
 
 /* Bits of a workspace's device error word (mra_workspace_error).  The
@@ -180,6 +181,21 @@ mra_status mra_attention_fwd(const mra_dims* dims, const void* q, const void* k,
                              const uint8_t* mask, int32_t block_per_row, int32_t approx_mode,
                              int32_t prior_first, int32_t prior_diag, void* out, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/* mra_attention_fwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels, with no workspace argument.  The workspace
+ * is a fixed 48 MiB device array inside the library, one copy per GPU, held
+ * until the process ends; the call allocates nothing.  Sizes whose
+ * mra_workspace_size exceeds 48 MiB return MRA_ERR_SCRATCH (B=2, H=12,
+ * N=4096 full mode needs 40.2 MiB).  Every call on one GPU shares that GPU's
+ * array, so calls that overlap in time on one GPU (other streams, other
+ * threads) race and must be serialised by the caller; each call clears what
+ * it needs cleared.  Its device error word is not exposed.  Other arguments
+ * and errors as for mra_attention_fwd. */
+mra_status mra_attention_fwd_noalloc(const mra_dims* dims, const void* q, const void* k, const void* v,
+                                     const uint8_t* mask, int32_t block_per_row, int32_t approx_mode,
+                                     int32_t prior_first, int32_t prior_diag, void* out, void* stream);
 
 /* mra_attention_fwd with its options in a struct (opts: host pointer, read
  * during the call), which adds the choice of ranking and band reading and

@@ -23,7 +23,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     L = mra.lib()
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 18
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(mra.SIGNATURES)
@@ -31,7 +31,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for s in range(0, 14):
+    for s in range(0, 15):
         assert mra.lib().mra_status_string(s)
     assert mra.lib().mra_status_string(99) == b"unknown status"
 
