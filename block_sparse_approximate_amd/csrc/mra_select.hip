@@ -109,6 +109,34 @@ __host__ __device__ inline SelectLds select_lds(int nb) {
     return L;
 }
 
+// Heads of one tile whose block rows hold whole 64-cell groups (nb = 64 or
+// 128) are selected by kTileRows-row workgroups (select_rows below).
+constexpr int kTileRows = 32;
+__host__ __device__ inline bool row_tiled(int nb) { return nb == 64 || nb == 128; }
+
+struct TileLds {
+    size_t hist, dig, cand, bitmap, rc, ic, mbv, wcnt, few, rank, small, total;
+};
+
+__host__ __device__ inline TileLds tile_lds(int nb) {
+    TileLds L;
+    const int words = (nb + 31) / 32;
+    size_t o = 0;
+    L.hist = o; o = align16(o + kHistBins * 4);
+    L.dig = o; o = align16(o + 2 * kDigitBins * 4);
+    L.cand = o; o = align16(o + (size_t)kCap * 8);
+    L.bitmap = o; o = align16(o + (size_t)kTileRows * words * 4);   // the workgroup's own rows
+    L.rc = o; o = align16(o + (size_t)(nb + 1) * 4);
+    L.ic = o; o = align16(o + (size_t)(nb + 1) * 4);
+    L.mbv = o; o = align16(o + (size_t)nb * 4);
+    L.wcnt = o; o = align16(o + (size_t)kCells * kSelWaves * 4);
+    L.few = o; o = align16(o + 64 * 8);
+    L.rank = o; o = align16(o + 64 * 4);
+    L.small = o; o = align16(o + 32 * 4);
+    L.total = o;
+    return L;
+}
+
 // ---------------------------------------------------------------- helpers
 // Exclusive scan of one value per thread over the select workgroup.
 // Returns the exclusive prefix; *total gets the sum.  Uses scan[kSelWaves + 1].
@@ -872,6 +900,400 @@ __device__ __forceinline__ void emit_stream(const Params& p, int bh, const uint3
     }
 }
 
+// Inclusive scan over the 64 lanes of a wave by DPP: shifts within rows of
+// 16 lanes, then each row's total broadcast to the rows after it.
+__device__ __forceinline__ uint32_t wave_scan_incl(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);   // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);   // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);   // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);   // row_shr:8
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    return x;
+}
+
+// The bin pick of pick_bin by wave 0 alone, so that the other waves wait at
+// one barrier instead of a workgroup scan's three: lane l sums bins
+// (63 - l) * 64 .. + 63 (read as 16-byte pieces), a wave scan finds the lane
+// whose range holds the need-th cell from the top, and a second scan over
+// that lane's 64 bins, one per lane, finds the bin.  The whole workgroup
+// calls this.
+__device__ __forceinline__ BinPick pick_bin_wave(const uint32_t* h, uint32_t need, uint32_t* small) {
+    constexpr int kPer = kHistBins / 64;
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        const uint4* hv = reinterpret_cast<const uint4*>(h + (63 - lane) * kPer);
+        uint32_t local = 0;
+#pragma unroll
+        for (int e = 0; e < kPer / 4; e++) {
+            const uint4 c = hv[e];
+            local += c.x + c.y + c.z + c.w;
+        }
+        const uint32_t above = wave_scan_incl(local) - local;
+        const uint64_t hit = __ballot(above < need && need <= above + local);
+        if (hit) {
+            const int src = __builtin_ctzll(hit);
+            const uint32_t sabove = (uint32_t)__builtin_amdgcn_readlane((int)above, src);
+            const int bin = (63 - src) * kPer + (kPer - 1 - lane);   // lane 0: that range's top bin
+            const uint32_t c = h[bin];
+            const uint32_t ab = sabove + wave_scan_incl(c) - c;
+            if (ab < need && need <= ab + c) {
+                small[0] = (uint32_t)bin;
+                small[1] = ab;
+                small[2] = c;
+            }
+        }
+    }
+    __syncthreads();
+    BinPick r{small[0], small[1], small[2]};
+    return r;
+}
+
+// Position of the n-th (1-based) set bit of m.
+__device__ __forceinline__ int nth_set_bit(uint64_t m, uint32_t n) {
+    int pos = 0;
+#pragma unroll
+    for (int half = 32; half > 0; half >>= 1) {
+        const uint64_t low = m & ((1ull << half) - 1ull);
+        const uint32_t c = (uint32_t)__popcll(low);
+        if (n > c) {
+            n -= c;
+            m >>= half;
+            pos += half;
+        } else {
+            m = low;
+        }
+    }
+    return pos;
+}
+
+constexpr int kRankSet = 64;   // candidates few enough to be ranked pairwise
+
+// The threshold key T: the need-th largest of the candidates whose top pbits
+// key bits are `prefix`.  While more than kRankSet of them remain, digit
+// passes narrow the prefix (every thread adds its candidates to a 256-bin
+// histogram, wave 0 picks the digit); then the remaining ones, at most
+// kRankSet, are gathered and ranked pairwise by the whole workgroup (all
+// keys differ, since each holds its flat index), and T is the one of rank
+// need - 1.  The whole workgroup calls this; every thread gets T.
+__device__ __forceinline__ uint64_t threshold_key(const uint64_t* cand, uint32_t ncand, uint64_t prefix, int pbits,
+                                                  uint32_t need, uint32_t count, uint32_t* dig, uint64_t* few,
+                                                  uint32_t* rank, uint32_t* small) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    auto matches = [&](uint64_t k64) { return pbits == 64 ? k64 == prefix : (k64 >> (64 - pbits)) == prefix; };
+    while (count > (uint32_t)kRankSet && pbits < 64) {
+        const int db = (64 - pbits) < kDigitBits ? (64 - pbits) : kDigitBits;
+        if (tid < kDigitBins) dig[tid] = 0u;
+        __syncthreads();
+        for (uint32_t c = tid; c < ncand; c += kSelThreads) {
+            const uint64_t k64 = cand[c];
+            if (matches(k64)) atomicAdd(&dig[(uint32_t)((k64 >> (64 - pbits - db)) & ((1ull << db) - 1))], 1u);
+        }
+        __syncthreads();
+        if (tid < 64) {
+            // lane l: bins 4 (63 - l) + 3 .. 4 (63 - l), from the top
+            const uint4 c4 = reinterpret_cast<const uint4*>(dig)[63 - lane];
+            const uint32_t cb[4] = {c4.w, c4.z, c4.y, c4.x};
+            const uint32_t local = c4.x + c4.y + c4.z + c4.w;
+            uint32_t acc = wave_scan_incl(local) - local;
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                if (acc < need && need <= acc + cb[q]) {
+                    small[16] = (uint32_t)(4 * (63 - lane) + 3 - q);
+                    small[17] = acc;
+                    small[18] = cb[q];
+                }
+                acc += cb[q];
+            }
+        }
+        __syncthreads();
+        need -= small[17];
+        prefix = (prefix << db) | small[16];
+        pbits += db;
+        count = small[18];
+    }
+    // gather the remaining candidates (at most kRankSet) and rank them
+    if (tid == 0) small[24] = 0u;
+    if (tid < kRankSet) rank[tid] = 0u;
+    __syncthreads();
+    for (uint32_t c0 = 0; c0 < ncand; c0 += kSelThreads) {
+        const uint32_t c = c0 + tid;
+        const bool hit = c < ncand && matches(cand[c]);
+        const uint64_t m = __ballot(hit);
+        if (m) {
+            uint32_t at = 0;
+            if (lane == 0) at = atomicAdd(&small[24], (uint32_t)__popcll(m));
+            at = (uint32_t)__builtin_amdgcn_readfirstlane((int)at) + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
+            if (hit && at < (uint32_t)kRankSet) few[at] = cand[c];
+        }
+    }
+    __syncthreads();
+    const uint32_t nf = small[24] < (uint32_t)kRankSet ? small[24] : (uint32_t)kRankSet;
+    {
+        // thread (j, l): does few[j] outrank few[l]?  four j per thread
+        const uint32_t l = (uint32_t)tid & 63u;
+        uint32_t r = 0;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const uint32_t j = ((uint32_t)tid >> 6) + 16u * q;
+            if (j < nf && l < nf && few[j] > few[l]) r++;
+        }
+        if (r) atomicAdd(&rank[l], r);
+    }
+    __syncthreads();
+    if (tid < 64) {
+        const bool is_t = (uint32_t)tid < nf && rank[tid] == need - 1u;
+        const uint64_t m = __ballot(is_t);
+        if (tid == 0) {
+            const uint64_t T = m ? few[__builtin_ctzll(m)] : (pbits == 64 ? prefix : prefix << (64 - pbits));
+            small[20] = (uint32_t)(T >> 32);
+            small[21] = (uint32_t)T;
+        }
+    }
+    __syncthreads();
+    return ((uint64_t)small[20] << 32) | small[21];
+}
+
+// ---------------------------------------------------------------- select by row tiles
+// One-tile heads whose block rows hold whole 64-cell groups (nb = 64 or 128,
+// N = 2048 or 4096) are selected by nb / kTileRows workgroups per head, all
+// on the head's XCD.  Every workgroup of a head makes the same decisions for
+// the whole head from the same inputs (the head's histogram and every cell
+// key, read from the head's L2): the threshold bin, the candidates, the
+// threshold key T and the selected count of every 64-cell group.  It then
+// writes only its own rows' share of the output: their bitmap words, row and
+// segment pointers, join-list entries and records.  No workgroup waits for
+// another.
+__device__ __forceinline__ void select_rows(const Params& p, int bh, int t, unsigned char* smem) {
+    const int nb = p.nb, words = p.words;
+    const int b = bh / p.H;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row0 = t * kTileRows;
+    const int lnb = nb == 128 ? 7 : 6;   // log2(nb)
+    const TileLds L = tile_lds(nb);
+    uint32_t* hist = reinterpret_cast<uint32_t*>(smem + L.hist);
+    uint32_t* dig = reinterpret_cast<uint32_t*>(smem + L.dig);
+    uint64_t* cand = reinterpret_cast<uint64_t*>(smem + L.cand);
+    uint32_t* bitmap = reinterpret_cast<uint32_t*>(smem + L.bitmap);
+    int* rc = reinterpret_cast<int*>(smem + L.rc);
+    int* ic = reinterpret_cast<int*>(smem + L.ic);
+    uint32_t* mbv = reinterpret_cast<uint32_t*>(smem + L.mbv);
+    uint32_t* gcnt = reinterpret_cast<uint32_t*>(smem + L.wcnt);   // per 64-cell group g = e * kSelWaves + wave
+    uint64_t* few = reinterpret_cast<uint64_t*>(smem + L.few);
+    uint32_t* rank = reinterpret_cast<uint32_t*>(smem + L.rank);
+    uint32_t* small = reinterpret_cast<uint32_t*>(smem + L.small);
+    const uint32_t ncell = (uint32_t)nb * (uint32_t)nb;
+    const uint32_t* G = p.keys + (size_t)bh * ncell;
+
+    // prologue: every global load first
+    constexpr int kPer = kHistBins / kSelThreads;
+    uint32_t hv[kPer], kv[kCells];
+#pragma unroll
+    for (int e = 0; e < kPer; e++) hv[e] = p.hist[(size_t)bh * kHistBins + tid + e * kSelThreads];
+    fetch_keys(G, 0, ncell, kv);
+    const uint32_t mv = tid < nb ? p.mbits[b * nb + tid] : 0u;
+#pragma unroll
+    for (int e = 0; e < kPer; e++) hist[tid + e * kSelThreads] = hv[e];
+    if (tid < kTileRows * words) bitmap[tid] = 0u;
+    if (tid < nb) mbv[tid] = mv;
+    if (tid == 0) small[8] = 0u;
+    __syncthreads();
+
+    uint32_t need = (uint32_t)p.K;
+    BinPick bp = pick_bin_wave(hist, need, small);
+    need -= bp.above;
+    uint64_t prefix = bp.bin;
+    int pbits = kHistBits;
+    uint32_t count = bp.count;
+    // further 12-bit passes while the bin is too large for LDS (tie-heavy inputs)
+    while (count > (uint32_t)kCap && pbits < 64) {
+        __syncthreads();   // every thread has read small[0..2]
+        const int db = (64 - pbits) < 12 ? (64 - pbits) : 12;
+        for (int x = tid; x < kHistBins; x += kSelThreads) hist[x] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < kCells; e++) {
+            const uint32_t x = tid + e * kSelThreads;
+            const uint64_t k64 = cell_key64(kv[e], x);
+            if (x < ncell && (k64 >> (64 - pbits)) == prefix)
+                atomicAdd(&hist[(uint32_t)((k64 >> (64 - pbits - db)) & ((1ull << db) - 1))], 1u);
+        }
+        __syncthreads();
+        bp = pick_bin_wave(hist, need, small);
+        need -= bp.above;
+        prefix = (prefix << db) | bp.bin;
+        pbits += db;
+        count = bp.count;
+    }
+
+    // One pass over every cell of the head, 64-cell groups: cells above the
+    // bin are selected for sure (their count per group, and this workgroup's
+    // rows' bitmap words); cells inside it are candidates, placed in the list
+    // with one LDS atomic per wave.  Most groups hold no cell at or above the
+    // bin and cost one compare.
+    const uint32_t wbase = (uint32_t)__builtin_amdgcn_readfirstlane(tid - lane);
+    const uint64_t lt_mask = (1ull << lane) - 1ull;
+    {
+        uint64_t mh[kCells];
+        uint32_t mys = 0, tot = 0;
+        const uint32_t sh = pbits <= 32 ? (uint32_t)(32 - pbits) : 0u;
+#pragma unroll
+        for (int e = 0; e < kCells; e++) {
+            const uint32_t x0 = (uint32_t)e * kSelThreads + wbase;
+            mh[e] = 0;
+            if (x0 < ncell) {
+                bool sure, hit;
+                if (pbits <= 32) {
+                    const uint32_t top = kv[e] >> sh;
+                    sure = top > (uint32_t)prefix;
+                    hit = top == (uint32_t)prefix;
+                } else {
+                    const uint64_t top = cell_key64(kv[e], x0 + lane) >> (64 - pbits);
+                    sure = top > prefix;
+                    hit = top == prefix;
+                }
+                if (__ballot(sure || hit)) {
+                    const uint64_t ms = __ballot(sure);
+                    mh[e] = __ballot(hit);
+                    tot += (uint32_t)__popcll(mh[e]);
+                    if (lane == e) mys = (uint32_t)__popcll(ms);
+                    const uint32_t i0 = x0 >> lnb;
+                    if (lane == 0 && i0 - (uint32_t)row0 < (uint32_t)kTileRows)
+                        *reinterpret_cast<uint2*>(bitmap + (i0 - row0) * words + ((x0 & (uint32_t)(nb - 1)) >> 5)) =
+                            make_uint2((uint32_t)ms, (uint32_t)(ms >> 32));
+                }
+            }
+        }
+        if (lane < kCells) gcnt[lane * kSelWaves + wave] = mys;
+        if (tot) {
+            uint32_t at = 0;
+            if (lane == 0) at = atomicAdd(&small[8], tot);
+            at = (uint32_t)__builtin_amdgcn_readfirstlane((int)at);
+#pragma unroll
+            for (int e = 0; e < kCells; e++) {
+                if (mh[e]) {
+                    if ((mh[e] >> lane) & 1ull) {
+                        const uint32_t pos = at + (uint32_t)__popcll(mh[e] & lt_mask);
+                        if (pos < (uint32_t)kCap) cand[pos] = cell_key64(kv[e], (uint32_t)e * kSelThreads + wbase + lane);
+                    }
+                    at += (uint32_t)__popcll(mh[e]);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    const uint32_t ncand_all = small[8];
+    const uint32_t ncand = ncand_all < (uint32_t)kCap ? ncand_all : (uint32_t)kCap;
+    if (tid == 0 && ncand_all != count) atomicOr(reinterpret_cast<unsigned int*>(p.error), 1u);
+
+    const uint64_t T = threshold_key(cand, ncand, prefix, pbits, need, count, dig, few, rank, small);
+    if (tid == 0 && t == 0) p.thresh[bh] = T;
+
+    // candidates at or above the threshold: their groups' counts, and this
+    // workgroup's rows' bitmap
+    for (uint32_t c = tid; c < ncand; c += kSelThreads) {
+        const uint64_t k64 = cand[c];
+        if (k64 >= T) {
+            const uint32_t f = 0xFFFFFFFFu - (uint32_t)k64;
+            if (f < ncell) {
+                atomicAdd(&gcnt[f >> 6], 1u);
+                const uint32_t i = f >> lnb, j = f & (uint32_t)(nb - 1);
+                if (i - (uint32_t)row0 < (uint32_t)kTileRows)
+                    atomicOr(&bitmap[(i - row0) * words + (j >> 5)], 1u << (j & 31));
+            }
+        }
+    }
+    __syncthreads();
+
+    // every row's CSR and segment pointers and join flag from one scan by
+    // wave 0, rows 2 lane and 2 lane + 1 (a row is nb / 64 consecutive
+    // groups; the same in every workgroup of the head); this workgroup
+    // writes its rows'
+    int32_t* row_ptr = p.row_ptr + (size_t)bh * (nb + 1);
+    int32_t* item_ptr = p.item_ptr + (size_t)bh * (nb + 1);
+    if (tid < 64) {
+        const int gpr = nb >> 6;   // groups per row
+        int cc[2], itc[2], mfc[2];
+#pragma unroll
+        for (int q = 0; q < 2; q++) {
+            const int i = 2 * tid + q;
+            int c = 0;
+            if (i < nb) {
+                c = (int)gcnt[i * gpr];
+                if (gpr == 2) c += (int)gcnt[i * gpr + 1];
+            }
+            cc[q] = c;
+            itc[q] = (c + kChunk - 1) / kChunk;
+            mfc[q] = (i < nb && itc[q] != 1) ? 1 : 0;   // no selected block, or several segments
+        }
+        // counts in bits 0..19 and join flags in 20..31 of one word; segments in another
+        const uint32_t va = (uint32_t)(cc[0] + cc[1]) | ((uint32_t)(mfc[0] + mfc[1]) << 20);
+        const uint32_t vi = (uint32_t)(itc[0] + itc[1]);
+        const uint32_t xa = wave_scan_incl(va), xi = wave_scan_incl(vi);
+        int ec = (int)((xa - va) & 0xFFFFFu), em = (int)((xa - va) >> 20), ei = (int)(xi - vi);
+#pragma unroll
+        for (int q = 0; q < 2; q++) {
+            const int i = 2 * tid + q;
+            if (i < nb) {
+                rc[i] = ec;
+                ic[i] = ei;
+                if ((uint32_t)(i - row0) < (uint32_t)kTileRows) {
+                    row_ptr[i] = ec;
+                    item_ptr[i] = ei;
+                    if (mfc[q]) p.merge_rows[(size_t)bh * nb + em] = make_int4(i, ei, itc[q], 0);
+                }
+            }
+            ec += cc[q];
+            ei += itc[q];
+            em += mfc[q];
+        }
+        if (tid == 63) {
+            const int tc = (int)(xa & 0xFFFFFu), tm = (int)(xa >> 20), ti = (int)xi;
+            rc[nb] = tc;
+            ic[nb] = ti;
+            if (row0 + kTileRows == nb) {
+                row_ptr[nb] = tc;
+                item_ptr[nb] = ti;
+                p.n_merge[bh] = tm;
+            }
+            if ((int64_t)tc != p.K || ti > p.max_items) atomicOr(reinterpret_cast<unsigned int*>(p.error), 2u);
+        }
+    }
+    __syncthreads();
+
+    // this workgroup's rows of the bitmap in memory; its cells' columns and
+    // records, one thread per selected cell (row by binary search over the
+    // row pointers, key block as the bit of the cell's rank in its row)
+    uint32_t* gbits = p.selbits + ((size_t)bh * nb + row0) * words;
+    if (tid < kTileRows * words) gbits[tid] = bitmap[tid];
+    int32_t* col = p.col + (size_t)bh * p.K;
+    BlkRec* recs = p.recs + (size_t)bh * p.K;
+    const int e_end = (int)min((int64_t)rc[row0 + kTileRows], p.K);
+    for (int e = rc[row0] + tid; e < e_end; e += kSelThreads) {
+        int lo = row0, hi = row0 + kTileRows - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (rc[mid] <= e) lo = mid;
+            else hi = mid - 1;
+        }
+        const int i = lo, o = rc[i], n = rc[i + 1] - o, rank_in_row = e - o;
+        const uint32_t* row = bitmap + (i - row0) * words;
+        int r = rank_in_row, w = 0;
+        uint32_t bits = row[0];
+        int c = __popc(bits);
+        while (r >= c && w + 1 < words) {
+            r -= c;
+            bits = row[++w];
+            c = __popc(bits);
+        }
+        const int j = w * 32 + nth_set_bit(bits, (uint32_t)r + 1u);
+        col[e] = j;
+        const int nit = (n + kChunk - 1) / kChunk, sg = rank_in_row / kChunk;
+        const int len = min(kChunk, n - sg * kChunk);
+        recs[e] = BlkRec{rec_ij(i, j), mbv[j], 0u, rec_info(ic[i] + sg, rank_in_row - sg * kChunk, len, nit == 1)};
+    }
+}
+
 __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int nb = p.nb;
@@ -880,14 +1302,23 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
     // rest sum the low-res attention of 32 rows each, placed on the XCD of
     // their head
     const int bh_pad = 8 * ((p.BH + 7) / 8);
-    if ((int)blockIdx.x >= bh_pad) {
-        const int g = blockIdx.x - bh_pad, xcd = g & 7, slot = g >> 3;
+    const int tiles = row_tiled(nb) ? nb / kTileRows : 1;   // selecting workgroups per head
+    if ((int)blockIdx.x >= bh_pad * tiles) {
+        const int g = blockIdx.x - bh_pad * tiles, xcd = g & 7, slot = g >> 3;
         const int tiles = (nb + kLoRows - 1) / kLoRows;
         const int hm = slot / tiles, lbh = xcd + 8 * hm;
         if (lbh < p.BH) {
             if (p.d == 128) lowres_rows<128>(p, lbh, (slot - hm * tiles) * kLoRows, smem);
             else lowres_rows<64>(p, lbh, (slot - hm * tiles) * kLoRows, smem);
         }
+        return;
+    }
+    if (row_tiled(nb)) {
+        // workgroup g runs on XCD g % 8: the row tiles of head bh go to XCD bh % 8
+        const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+        const int hm = slot / tiles, t = slot - hm * tiles;
+        const int tbh = xcd + 8 * hm;
+        if (tbh < p.BH) select_rows(p, tbh, t, smem);
         return;
     }
     const int bh = blockIdx.x;
@@ -1164,9 +1595,10 @@ hipError_t launch_select(const Params& p, hipStream_t s) {
     if (a2 != hipSuccess) return a2;
     const int bh_pad = 8 * ((p.BH + 7) / 8);
     const int lowres_wgs = p.mode == 0 ? bh_pad * ((p.nb + kLoRows - 1) / kLoRows) : 0;
-    size_t lds = select_lds(p.nb).total;
+    const int sel_wgs = row_tiled(p.nb) ? bh_pad * (p.nb / kTileRows) : bh_pad;
+    size_t lds = row_tiled(p.nb) ? tile_lds(p.nb).total : select_lds(p.nb).total;
     if (p.mode == 0 && lowres_lds(p.nb, p.d) > lds) lds = lowres_lds(p.nb, p.d);
-    hipLaunchKernelGGL(select_kernel, dim3(bh_pad + lowres_wgs), dim3(kSelThreads), lds, s, p);
+    hipLaunchKernelGGL(select_kernel, dim3(sel_wgs + lowres_wgs), dim3(kSelThreads), lds, s, p);
     return hipGetLastError();
 }
 

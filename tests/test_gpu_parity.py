@@ -160,7 +160,11 @@ def test_clustered_error_against_dense_shrinks_with_budget(mra):
     # heads of several 16384-cell tiles: the marking pass runs one workgroup per tile
     # (nb = 192: the last tile is partial; "coarse": many exact ties that still fit
     # the candidate list), and nb = 161 walks its tiles in one workgroup
-    (192, 4, 1, 2, "normal"), (256, 3, 0, 0, "coarse"), (161, 2, 0, 0, "normal")])
+    (192, 4, 1, 2, "normal"), (256, 3, 0, 0, "coarse"), (161, 2, 0, 0, "normal"),
+    # nb = 64 and 128 are selected by 16-row workgroups that each settle the whole head:
+    # exact ties at the threshold ("coarse", "ints", priors) settle by flat order
+    (64, 4, 1, 2, "normal"), (64, 3, 0, 0, "coarse"), (64, 1, 0, 0, "equal"), (128, 4, 0, 0, "coarse"),
+    (128, 2, 2, 3, "ints"), (128, 6, 0, 4, "equal"), (128, 1, 5, 0, "coarse")])
 def test_selector_on_identical_logits(mra, nb, bpr, pf, pd, kind):
     print("case", nb, bpr, pf, pd, kind, flush=True)
     rng = np.random.default_rng(nb * 7 + bpr)
