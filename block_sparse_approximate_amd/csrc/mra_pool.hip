@@ -7,29 +7,40 @@
 // order; the mean is that sum divided by (float)count, correctly rounded;
 // an empty block pools to zeros.  Built with -ffp-contract=off.
 //
-// Mapping: a workgroup pools 8 consecutive blocks (4 for 128-channel heads)
-// of one tensor and head, which are one contiguous run of token rows; all
-// workgroups of a head run on the same XCD.  Every thread first issues all
-// of its 16-byte loads of that run (fully coalesced, one round trip), stores
-// them in LDS, and then each thread sums two channels of one block over its
-// 32 rows in token order.
+// Mapping: a workgroup of kPoolThreads threads pools kPoolThreads / (d / 2)
+// consecutive blocks of one tensor and head (one thread per block and
+// channel pair), which are one contiguous run of token rows; all workgroups
+// of a head run on the same XCD.  Every thread first issues all of its
+// 16-byte loads of that run (fully coalesced, one round trip), stores them in
+// LDS, and then each thread sums two channels of one block over its 32 rows
+// in token order.  (Workgroups of 1024 threads and 128 KiB of staging were
+// measured slower at N = 4096 with three tensors: one workgroup per CU left
+// part of the grid for a second round.)
 #include "mra_common.h"
 
 namespace mra {
 namespace {
 
-constexpr int kPoolThreads = 256;
-// blocks per workgroup: one thread per (block, channel pair)
-__host__ __device__ constexpr int pool_blocks(int hd) { return kPoolThreads / (hd / 2); }
+constexpr int kPoolMaxThreads = 256;
+constexpr int kPoolTileBytes = 64 * 1024;    // LDS staging per workgroup, at most
+// blocks per workgroup (one thread per block and channel pair): as many as
+// fill the staging tile, up to kPoolMaxThreads threads
+__host__ __device__ constexpr int pool_blocks(int dt, int hd) {
+    return (kPoolTileBytes / (kBlock * hd * (dt == 1 ? 2 : 4))) * (hd / 2) > kPoolMaxThreads
+               ? kPoolMaxThreads / (hd / 2)
+               : kPoolTileBytes / (kBlock * hd * (dt == 1 ? 2 : 4));
+}
+__host__ __device__ constexpr int pool_threads(int dt, int hd) { return pool_blocks(dt, hd) * (hd / 2); }
 
 template <int DT, int HD>  // DT: 0 = fp32, 1 = bf16; HD: channels per head
-__global__ __launch_bounds__(kPoolThreads) void pool_kernel(Params p, int ntens, int groups_per_head,
-                                                            size_t zero_words) {
-    constexpr int kPoolBlocks = pool_blocks(HD);
+__global__ __launch_bounds__(kPoolMaxThreads) void pool_kernel(Params p, int ntens, int groups_per_head,
+                                                               size_t zero_words) {
+    constexpr int kPoolThreads = pool_threads(DT, HD);
+    constexpr int kPoolBlocks = pool_blocks(DT, HD);
     constexpr int kEs = DT == 1 ? 2 : 4;              // bytes per element
     constexpr int kBlockBytes = kBlock * HD * kEs;    // 4 to 16 KiB
     constexpr int kLoads = kPoolBlocks * kBlockBytes / 16 / kPoolThreads;
-    __shared__ __align__(16) unsigned char tile[kPoolBlocks * kBlockBytes];
+    extern __shared__ __align__(16) unsigned char tile[];   // kPoolBlocks * kBlockBytes
 
     // Clear the selection histogram and candidate counts for the next stages
     // (stream order makes this visible to them).
@@ -114,19 +125,26 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(Params p, int ntens,
 
 }  // namespace
 
+template <int DT, int HD>
+static hipError_t launch_pool_dt(const Params& p, hipStream_t s, int ntens, int groups_per_head, size_t zero_words) {
+    constexpr size_t kLds = (size_t)pool_blocks(DT, HD) * kBlock * HD * (DT == 1 ? 2 : 4);
+    static const hipError_t a = hipFuncSetAttribute(reinterpret_cast<const void*>(&pool_kernel<DT, HD>),
+                                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+    if (a != hipSuccess) return a;
+    const int grid = 8 * ((p.BH + 7) / 8) * ntens * groups_per_head;
+    hipLaunchKernelGGL((pool_kernel<DT, HD>), dim3(grid), dim3(pool_threads(DT, HD)), kLds, s, p, ntens,
+                       groups_per_head, zero_words);
+    return hipGetLastError();
+}
+
 template <int HD>
 static hipError_t launch_pool_t(const Params& p, hipStream_t s) {
     const int ntens = p.mode == 0 ? 3 : 2;
-    const int groups_per_head = (p.nb + pool_blocks(HD) - 1) / pool_blocks(HD);
-    const int grid = 8 * ((p.BH + 7) / 8) * ntens * groups_per_head;
+    const int pb = p.dtype == 1 ? pool_blocks(1, HD) : pool_blocks(0, HD);
+    const int groups_per_head = (p.nb + pb - 1) / pb;
     const size_t zero_words = (size_t)p.BH * kHistBins;
-    if (p.dtype == 1)
-        hipLaunchKernelGGL((pool_kernel<1, HD>), dim3(grid), dim3(kPoolThreads), 0, s, p, ntens, groups_per_head,
-                           zero_words);
-    else
-        hipLaunchKernelGGL((pool_kernel<0, HD>), dim3(grid), dim3(kPoolThreads), 0, s, p, ntens, groups_per_head,
-                           zero_words);
-    return hipGetLastError();
+    return p.dtype == 1 ? launch_pool_dt<1, HD>(p, s, ntens, groups_per_head, zero_words)
+                        : launch_pool_dt<0, HD>(p, s, ntens, groups_per_head, zero_words);
 }
 
 hipError_t launch_pool(const Params& p, hipStream_t s) {

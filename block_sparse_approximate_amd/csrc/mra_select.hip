@@ -138,27 +138,59 @@ __host__ __device__ inline TileLds tile_lds(int nb) {
 }
 
 // ---------------------------------------------------------------- helpers
+// Inclusive scan over the 64 lanes of a wave by DPP: shifts within rows of
+// 16 lanes, then each row's total broadcast to the rows after it.
+__device__ __forceinline__ uint32_t wave_scan_incl(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);   // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);   // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);   // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);   // row_shr:8
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    return x;
+}
+
+// The same for 64-bit values whose 32-bit halves never carry into each other
+// (packed counts): each half is scanned on its own.
+__device__ __forceinline__ uint64_t wave_scan_incl(uint64_t x) {
+    const uint32_t lo = wave_scan_incl((uint32_t)x), hi = wave_scan_incl((uint32_t)(x >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Max and sum over the 64 lanes of a wave by DPP (the result in every lane).
+// The max is exact in any order; the sum's order is fixed by the lane layout.
+__device__ __forceinline__ float wave_max(float x) {
+    const int ninf = __builtin_bit_cast(int, -__builtin_inff());
+    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(ninf, __builtin_bit_cast(int, x), 0x111, 0xF, 0xF, false)));
+    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(ninf, __builtin_bit_cast(int, x), 0x112, 0xF, 0xF, false)));
+    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(ninf, __builtin_bit_cast(int, x), 0x114, 0xF, 0xF, false)));
+    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(ninf, __builtin_bit_cast(int, x), 0x118, 0xF, 0xF, false)));
+    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(ninf, __builtin_bit_cast(int, x), 0x142, 0xA, 0xF, false)));
+    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(ninf, __builtin_bit_cast(int, x), 0x143, 0xC, 0xF, false)));
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x111, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x112, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x114, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x118, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x142, 0xA, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x143, 0xC, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+
 // Exclusive scan of one value per thread over the select workgroup.
 // Returns the exclusive prefix; *total gets the sum.  Uses scan[kSelWaves + 1].
 template <typename T>
 __device__ __forceinline__ T block_excl_scan(T v, T* scan, T* total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    T x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const T y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
+    const T x = wave_scan_incl(v);
     if (lane == 63) scan[wave] = x;
     __syncthreads();
     if (threadIdx.x < 64) {
         const T t = threadIdx.x < kSelWaves ? scan[threadIdx.x] : T(0);
-        T y = t;
-#pragma unroll
-        for (int off = 1; off < kSelWaves; off <<= 1) {
-            const T z = __shfl_up(y, off, 64);
-            if ((int)threadIdx.x >= off) y += z;
-        }
+        const T y = wave_scan_incl(t);
         if (threadIdx.x < kSelWaves) scan[threadIdx.x] = y - t;
         if (threadIdx.x == kSelWaves - 1) scan[kSelWaves] = y;
     }
@@ -217,13 +249,7 @@ __device__ __forceinline__ void pick_digit_wave(const uint32_t* h, uint32_t need
         c[e] = h[rt * kPer + e];
         local += c[e];
     }
-    uint32_t x = local;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
-    const uint32_t above = x - local;
+    const uint32_t above = wave_scan_incl(local) - local;
     if (above < need && need <= above + local) {
         uint32_t acc = above;
 #pragma unroll
@@ -357,17 +383,6 @@ __device__ __forceinline__ void fetch_khat(const float* __restrict__ kh, int j0,
     }
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
-    return x;
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-    return x;
-}
 
 // The marking pass for the common shape: one tile (kv holds every cell), a
 // multiple of 64 cells per block row, every cell of the tile present, and a
@@ -898,18 +913,6 @@ __device__ __forceinline__ void emit_stream(const Params& p, int bh, const uint3
         const int len = min(kChunk, n - sg * kChunk);
         recs[e] = BlkRec{rec_ij(i, j), mbv[j], 0u, rec_info(ic[i] + sg, rank - sg * kChunk, len, nit == 1)};
     }
-}
-
-// Inclusive scan over the 64 lanes of a wave by DPP: shifts within rows of
-// 16 lanes, then each row's total broadcast to the rows after it.
-__device__ __forceinline__ uint32_t wave_scan_incl(uint32_t x) {
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);   // row_shr:1
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);   // row_shr:2
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);   // row_shr:4
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);   // row_shr:8
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
-    return x;
 }
 
 // The bin pick of pick_bin by wave 0 alone, so that the other waves wait at
