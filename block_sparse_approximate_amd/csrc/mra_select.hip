@@ -1057,6 +1057,66 @@ __device__ __forceinline__ uint64_t threshold_key(const uint64_t* cand, uint32_t
     return ((uint64_t)small[20] << 32) | small[21];
 }
 
+// The marking pass of select_rows over every cell of a one-tile head (kv:
+// the thread's cell keys, cell tid + e * kSelThreads in kv[e]; a wave's 64
+// consecutive cells, group g = e * kSelWaves + wave, lie in one block row).
+// Cells whose key prefix is above `prefix` are selected for sure: their
+// count goes to gcnt[g], and the workgroup's own rows (row0 .. + kTileRows)
+// get their bitmap words.  Cells whose prefix equals it are candidates: each
+// wave places its own with one LDS atomic on small[8].  kNarrow: the prefix
+// has at most 32 bits (a prefix of the score key alone).
+template <bool kNarrow>
+__device__ __forceinline__ void mark_groups(const uint32_t (&kv)[kCells], uint32_t ncell, int lnb, int nb, int words,
+                                            int row0, uint64_t prefix, int pbits, uint32_t* gcnt, uint32_t* bitmap,
+                                            uint64_t* cand, uint32_t* small) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t wbase = (uint32_t)__builtin_amdgcn_readfirstlane((int)threadIdx.x - lane);
+    const uint64_t lt_mask = (1ull << lane) - 1ull;
+    const uint32_t sh = kNarrow ? (uint32_t)(32 - pbits) : 0u, p32 = (uint32_t)prefix;
+    // the groups of the workgroup's rows: e in [e_own, e_own + kTileRows * nb / kSelThreads)
+    const uint32_t own_lo = (uint32_t)row0 << lnb, own_hi = own_lo + ((uint32_t)kTileRows << lnb);
+    uint64_t mh[kCells];
+    uint32_t mys = 0, tot = 0;
+#pragma unroll
+    for (int e = 0; e < kCells; e++) {
+        const uint32_t x0 = (uint32_t)e * kSelThreads + wbase;
+        uint64_t ms = 0, mhe = 0;
+        if (x0 < ncell) {
+            if constexpr (kNarrow) {
+                const uint32_t top = kv[e] >> sh;
+                ms = __ballot(top > p32);
+                mhe = __ballot(top == p32);
+            } else {
+                const uint64_t top = cell_key64(kv[e], x0 + lane) >> (64 - pbits);
+                ms = __ballot(top > prefix);
+                mhe = __ballot(top == prefix);
+            }
+            if (x0 - own_lo < own_hi - own_lo && lane == 0)
+                *reinterpret_cast<uint2*>(bitmap + ((x0 - own_lo) >> lnb) * words + ((x0 & (uint32_t)(nb - 1)) >> 5)) =
+                    make_uint2((uint32_t)ms, (uint32_t)(ms >> 32));
+        }
+        mh[e] = mhe;
+        tot += (uint32_t)__popcll(mhe);
+        mys = lane == e ? (uint32_t)__popcll(ms) : mys;
+    }
+    if (lane < kCells) gcnt[lane * kSelWaves + wave] = mys;
+    if (tot) {
+        uint32_t at = 0;
+        if (lane == 0) at = atomicAdd(&small[8], tot);
+        at = (uint32_t)__builtin_amdgcn_readfirstlane((int)at);
+#pragma unroll
+        for (int e = 0; e < kCells; e++) {
+            if (mh[e]) {
+                if ((mh[e] >> lane) & 1ull) {
+                    const uint32_t pos = at + (uint32_t)__popcll(mh[e] & lt_mask);
+                    if (pos < (uint32_t)kCap) cand[pos] = cell_key64(kv[e], (uint32_t)e * kSelThreads + wbase + lane);
+                }
+                at += (uint32_t)__popcll(mh[e]);
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------- select by row tiles
 // One-tile heads whose block rows hold whole 64-cell groups (nb = 64 or 128,
 // N = 2048 or 4096) are selected by nb / kTileRows workgroups per head, all
@@ -1132,58 +1192,12 @@ __device__ __forceinline__ void select_rows(const Params& p, int bh, int t, unsi
     // One pass over every cell of the head, 64-cell groups: cells above the
     // bin are selected for sure (their count per group, and this workgroup's
     // rows' bitmap words); cells inside it are candidates, placed in the list
-    // with one LDS atomic per wave.  Most groups hold no cell at or above the
-    // bin and cost one compare.
+    // with one LDS atomic per wave.
     const uint32_t wbase = (uint32_t)__builtin_amdgcn_readfirstlane(tid - lane);
-    const uint64_t lt_mask = (1ull << lane) - 1ull;
-    {
-        uint64_t mh[kCells];
-        uint32_t mys = 0, tot = 0;
-        const uint32_t sh = pbits <= 32 ? (uint32_t)(32 - pbits) : 0u;
-#pragma unroll
-        for (int e = 0; e < kCells; e++) {
-            const uint32_t x0 = (uint32_t)e * kSelThreads + wbase;
-            mh[e] = 0;
-            if (x0 < ncell) {
-                bool sure, hit;
-                if (pbits <= 32) {
-                    const uint32_t top = kv[e] >> sh;
-                    sure = top > (uint32_t)prefix;
-                    hit = top == (uint32_t)prefix;
-                } else {
-                    const uint64_t top = cell_key64(kv[e], x0 + lane) >> (64 - pbits);
-                    sure = top > prefix;
-                    hit = top == prefix;
-                }
-                if (__ballot(sure || hit)) {
-                    const uint64_t ms = __ballot(sure);
-                    mh[e] = __ballot(hit);
-                    tot += (uint32_t)__popcll(mh[e]);
-                    if (lane == e) mys = (uint32_t)__popcll(ms);
-                    const uint32_t i0 = x0 >> lnb;
-                    if (lane == 0 && i0 - (uint32_t)row0 < (uint32_t)kTileRows)
-                        *reinterpret_cast<uint2*>(bitmap + (i0 - row0) * words + ((x0 & (uint32_t)(nb - 1)) >> 5)) =
-                            make_uint2((uint32_t)ms, (uint32_t)(ms >> 32));
-                }
-            }
-        }
-        if (lane < kCells) gcnt[lane * kSelWaves + wave] = mys;
-        if (tot) {
-            uint32_t at = 0;
-            if (lane == 0) at = atomicAdd(&small[8], tot);
-            at = (uint32_t)__builtin_amdgcn_readfirstlane((int)at);
-#pragma unroll
-            for (int e = 0; e < kCells; e++) {
-                if (mh[e]) {
-                    if ((mh[e] >> lane) & 1ull) {
-                        const uint32_t pos = at + (uint32_t)__popcll(mh[e] & lt_mask);
-                        if (pos < (uint32_t)kCap) cand[pos] = cell_key64(kv[e], (uint32_t)e * kSelThreads + wbase + lane);
-                    }
-                    at += (uint32_t)__popcll(mh[e]);
-                }
-            }
-        }
-    }
+    if (pbits <= 32)
+        mark_groups<true>(kv, ncell, lnb, nb, words, row0, prefix, pbits, gcnt, bitmap, cand, small);
+    else
+        mark_groups<false>(kv, ncell, lnb, nb, words, row0, prefix, pbits, gcnt, bitmap, cand, small);
     __syncthreads();
     const uint32_t ncand_all = small[8];
     const uint32_t ncand = ncand_all < (uint32_t)kCap ? ncand_all : (uint32_t)kCap;
