@@ -47,8 +47,22 @@ Besides tokens/s the line carries:
     (mra_bigbird_bwd) timed the same way;
   * `head128`: the forward pass on 128-channel heads (B=2, H=12, N=4096,
     bf16, full mode, i.i.d. N(0,1)*0.5 inputs), timed the same way, with the
-    same algorithmic bytes and MFMA work at d=128, and its backward pass.
-Only one GPU is used; --gpus above 1 exits with a message.
+    same algorithmic bytes and MFMA work at d=128, and its backward pass;
+  * `regimes`: for the three N >= 4096 workloads (C3 sparse with priors, C4
+    full clustered, C5 N=16384), per-call durations of --calls calls (200 by
+    default), each call between its own pair of HIP events: median, p10 and
+    p90 in two regimes.  "warm": calls back to back, so inputs and workspace
+    stay in the 256 MB last-level cache (MALL).  "cold": before each call
+    (outside its events) a 1 GiB buffer is rewritten by a fill kernel, more
+    than the MALL and the L2s hold, so the call starts from HBM;
+  * `attn_cold`: the block attention kernel alone after the same 1 GiB write
+    (a relaunch on the filled workspace), median of --calls launches, with
+    its algorithmic HBM rate;
+  * `copy_bandwidth`: a measured device-to-device copy of 1 GiB (bytes read
+    plus bytes written over the median duration of 20 copies), the practical
+    HBM ceiling the roofline fractions are also given against.
+The headline `value` stays the wall-clock rate of the K timed steps.  Only
+one GPU is used; --gpus above 1 exits with a message.
 """
 from __future__ import annotations
 
@@ -116,6 +130,103 @@ def selected_valid_blocks(w) -> int:
     return int(sum(w.H * min(K, int(v) * int(v)) for v in valid))
 
 
+SCRUB_BYTES = 1 << 30   # more than the 256 MB MALL plus the L2s
+
+
+def percentiles(ts):
+    import numpy as np
+    a = np.asarray(ts, np.float64)
+    return {"median_us": round(float(np.median(a)), 2), "p10_us": round(float(np.percentile(a, 10)), 2),
+            "p90_us": round(float(np.percentile(a, 90)), 2), "mean_us": round(float(a.mean()), 2),
+            "calls": int(a.size)}
+
+
+def time_each(call, n, scrub=None):
+    """Durations (us) of n calls of `call`, each between its own pair of HIP
+    events on the current stream.  With `scrub` (a device buffer), a fill
+    kernel rewrites it before each call, outside the call's events."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i, (a, b) in enumerate(evs):
+        if scrub is not None:
+            scrub.fill_(i % 251 + 1)
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) * 1e3 for a, b in evs]
+
+
+def copy_bandwidth():
+    """Bytes read plus bytes written per second of a 1 GiB device-to-device
+    copy (median of 20)."""
+    import torch
+    a = torch.full((SCRUB_BYTES,), 7, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    ts = time_each(lambda: b.copy_(a), 20)
+    import numpy as np
+    med = float(np.median(ts)) * 1e-6
+    del a, b
+    return {"bytes_moved": 2 * SCRUB_BYTES, "median_us": round(med * 1e6, 1),
+            "GBs": round(2 * SCRUB_BYTES / med / 1e9, 1), "kind": "torch copy_ of 1 GiB, device to device"}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def bench_regimes(mra, cfgs, calls: int, copy_gbs: float) -> dict:
+    """Warm and cold per-call durations of the forward pass on the named
+    workloads, and for the block attention alone after the cold write."""
+    import numpy as np
+    import torch
+
+    import workloads
+
+    scrub = torch.empty(SCRUB_BYTES, dtype=torch.uint8, device="cuda")
+    res = {}
+    attn_cold = {}
+    for cfg in cfgs:
+        w = workloads.get(cfg)
+        q, k, v = (torch.from_numpy(w.raw(n).view(np.int16)).view(torch.bfloat16).cuda() for n in ("q", "k", "v"))
+        mask = None if w.mask is None else torch.from_numpy(w.mask).cuda()
+        kw = dict(block_per_row=w.block_per_row, approx_mode=w.approx_mode,
+                  initial_prior_first_n_blocks=w.prior_first, initial_prior_diagonal_n_blocks=w.prior_diag)
+        out = torch.empty_like(q)
+        ws = torch.empty(mra.workspace_size(w.B, w.H, w.N, w.d, q.dtype, w.block_per_row, w.approx_mode),
+                         dtype=torch.uint8, device="cuda")
+        call, _ = mra.prepare(q, k, v, mask, out=out, workspace=ws, **kw)
+        for _ in range(20):
+            call()
+        warm = percentiles(time_each(call, calls))
+        cold = percentiles(time_each(call, calls, scrub))
+        tokens = w.B * w.N
+        for r in (warm, cold):
+            r["tokens_per_s"] = round(tokens / (r["median_us"] * 1e-6), 1)
+        res[w.name] = {"warm": warm, "cold": cold}
+        if cfg == "C4":
+            replay = lambda: mra.debug_replay(q, k, v, 3, 1, mask, out=out, workspace=ws, **kw)
+            a = percentiles(time_each(replay, calls, scrub))
+            nbytes = 4.0 * w.B * w.H * w.N * w.d * 2
+            gbs = nbytes / (a["median_us"] * 1e-6) / 1e9
+            attn_cold = dict(a, workload=w.name, algorithmic_bytes=int(nbytes), achieved_GBs=round(gbs, 1),
+                             frac_of_peak=round(gbs / PEAK_HBM_GBS, 4),
+                             frac_of_measured_copy=round(gbs / copy_gbs, 4) if copy_gbs else None,
+                             regime="cold: a 1 GiB write before each launch; Q, K, V and the workspace come "
+                                    "from HBM")
+        del q, k, v, out, ws
+    del scrub
+    return {"regimes": res, "attn_cold": attn_cold}
+
+
 def load_traffic(stage: str, workload: str):
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
@@ -142,6 +253,7 @@ def cpu_baseline(w, seconds: float = 10.0):
         if el >= seconds or runs >= 200:
             break
     return {"value": w.B * w.N * runs / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": "the whole %s workload (%d heads), %d runs in %.1f s" % (w.name, w.B * w.H, runs, el)}
 
 
@@ -309,6 +421,8 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-bigbird", action="store_true")
     ap.add_argument("--no-head128", action="store_true")
+    ap.add_argument("--no-regimes", action="store_true", help="skip the warm/cold per-call records")
+    ap.add_argument("--calls", type=int, default=200, help="calls per regime record")
     ap.add_argument("--only-head128", action="store_true",
                     help="only time the forward pass on 128-channel heads (N=4096 bf16 full mode)")
     ap.add_argument("--only-bigbird", action="store_true",
@@ -437,6 +551,8 @@ def main():
             "unit": "GB/s", "duration_us": round(dom_s * 1e6, 2),
             "timing": "replay" if dom in replay_ms else "events"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["regime"] = ("warm: back-to-back relaunches on a workspace the previous call filled; inputs and "
+                      "workspace resident in the 256 MB MALL" if dom in replay_ms else "warm: back-to-back calls")
     roof["traffic"] = load_traffic(dom, w.name)
     roof["algorithmic_bytes"] = int(amount)
     if dom == "attn":
@@ -467,6 +583,11 @@ def main():
         "profiled_ms_per_step": round(prof_wall, 5),
         "roofline": roof,
     }
+    if not args.no_regimes:
+        cb = copy_bandwidth()
+        rec["copy_bandwidth"] = cb
+        roof["frac_of_measured_copy"] = round(roof["achieved"] / cb["GBs"], 4)
+        rec.update(bench_regimes(mra, ("C3", "C4", "C5"), args.calls, cb["GBs"]))
     if not args.no_backward:
         rec["backward"] = [bench_backward(mra, args.steps, args.warmup, cfg) for cfg in ("C3", "C4")]
     if not args.no_bigbird:

@@ -3,11 +3,13 @@ against the CPU oracle's gradients (oracle.mra_backward), in sparse and full
 mode.
 
 The gradients run in bf16 operands with fp32 accumulation: the inputs, P and
-dS enter the products rounded to bf16 (relative error up to 2^-9 each), and
-D_t = dO_t . O_t uses the forward's bf16 output.  The bound is taken relative
-to each gradient tensor's scale: max |err| <= 2^-5 max |ref| and
-sum |err| / sum |ref| <= 2^-7 (a few bf16 roundings, with the cancellation in
-dP - D), written below as TOL_BWD.
+dS enter the products rounded to bf16 (unit roundoff u = 2^-9 each), and
+D_t = dO_t . O_t uses the forward's bf16 output.  Each gradient element is a
+sum of terms carrying about two such roundings (P or dS, and D through the
+cancellation in dP - D), so its error relative to the tensor's scale is a few
+u: the bounds below are max |err| <= 8u max |ref| and
+sum |err| / sum |ref| <= 3u (TOL_BWD).  Measured over every bf16 case in the
+GPU suite: at most 4.6u (C4's dq) and 2.0u.
 """
 import numpy as np
 import pytest
@@ -18,13 +20,14 @@ import workloads
 
 pytestmark = pytest.mark.gpu
 
-TOL_BWD = dict(max_rel_to_scale=2.0 ** -5, mean_rel=2.0 ** -7)
-# fp32 inputs: fp32 products and sums (rounding 2^-24 per operation over
-# contractions of 64 channels or 32 tokens per block and a few hundred
-# blocks), the hardware exp2 (about 2^-22 relative) and the cancellation in
-# dP - D; relative to each tensor's scale, max |err| <= 2^-13 max |ref| and
-# sum |err| / sum |ref| <= 2^-16.
-TOL_BWD32 = dict(max_rel_to_scale=2.0 ** -13, mean_rel=2.0 ** -16)
+U_BF16 = 2.0 ** -9
+TOL_BWD = dict(max_rel_to_scale=8 * U_BF16, mean_rel=3 * U_BF16)
+# fp32 inputs: fp32 products and sums (unit roundoff 2^-24, over contractions
+# of 64 channels or 32 tokens per block and a few hundred blocks), the
+# hardware exp2 (about 2^-22 relative) and the cancellation in dP - D;
+# relative to each tensor's scale, max |err| <= 2^-17 max |ref| and
+# sum |err| / sum |ref| <= 2^-20.  Measured: at most 2.7e-6 and 3.6e-7.
+TOL_BWD32 = dict(max_rel_to_scale=2.0 ** -17, mean_rel=2.0 ** -20)
 
 
 @pytest.fixture(scope="module")

@@ -113,7 +113,7 @@ def test_bigbird_matches_mra_sparse_on_the_same_cells(mra):
 
 
 
-TOL_BWD = dict(max_rel_to_scale=2.0 ** -5, mean_rel=2.0 ** -7)
+from test_gpu_backward import TOL_BWD  # noqa: E402  (the bf16 gradient bounds, derived there)
 
 
 @pytest.mark.parametrize("name,kw", [

@@ -13,7 +13,15 @@ import workloads
 
 pytestmark = pytest.mark.gpu
 
-TOL_BWD = dict(max_rel_to_scale=2.0 ** -5, mean_rel=2.0 ** -7)
+from test_gpu_backward import TOL_BWD  # noqa: E402  (the bf16 gradient bounds, derived there)
+
+# The whole layer in bf16 against the same layer with dense attention: the
+# projections, LayerNorm and feed-forward block add bf16 roundings of their
+# own on both sides, and the weight gradients sum over every token.  Measured:
+# output and input gradient at most 6.7e-3 / 3.3e-3 (max / mean relative),
+# weight gradients 4.6e-3 / 4.8e-3.
+TOL_LAYER = dict(max_rel=2.0 ** -6, mean_rel=2.0 ** -7)
+TOL_LAYER_WEIGHTS = dict(max_rel=2.0 ** -6, mean_rel=2.0 ** -6)
 
 
 @pytest.fixture(scope="module")
@@ -132,9 +140,9 @@ def test_layer_with_every_block_selected_matches_dense_layer(layer):
     y.backward(gy.cuda())
     ref, xr, yr = dense_layer_reference(mod, x)
     yr.backward(gy.float())
-    close("y", y.detach().float().cpu().numpy(), yr.detach().numpy(), max_rel=2 ** -4, mean_rel=2 ** -6)
-    close("dx", x.grad.float().cpu().numpy(), xr.grad.numpy(), max_rel=2 ** -4, mean_rel=2 ** -6)
+    close("y", y.detach().float().cpu().numpy(), yr.detach().numpy(), **TOL_LAYER)
+    close("dx", x.grad.float().cpu().numpy(), xr.grad.numpy(), **TOL_LAYER)
     for name in ("attention.query.weight", "attention.key.weight", "attention.value.weight"):
         got = dict(mod.named_parameters())[name].grad.float().cpu().numpy()
         want = dict(ref.named_parameters())[name].grad.numpy()
-        close(name, got, want, max_rel=2 ** -4, mean_rel=2 ** -5)
+        close(name, got, want, **TOL_LAYER_WEIGHTS)

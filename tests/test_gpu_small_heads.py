@@ -81,7 +81,9 @@ def test_small_heads_backward(mra, dtype, mode):
     torch.cuda.synchronize()
     ref = oracle.mra_backward(w.q, w.k, w.v, gt.float().numpy()[..., :d], None, w.block_per_row, mode, 0,
                               w.prior_diag)
-    tol = (2.0 ** -5, 2.0 ** -7) if dtype == "bf16" else (2.0 ** -13, 2.0 ** -16)
+    from test_gpu_backward import TOL_BWD, TOL_BWD32
+    t = TOL_BWD if dtype == "bf16" else TOL_BWD32
+    tol = (t["max_rel_to_scale"], t["mean_rel"])
     for label, a, b in zip(("dq", "dk", "dv"), grads, ref):
         a = a.float().cpu().numpy()
         assert np.all(a[..., d:] == 0), label
