@@ -4,7 +4,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C4]
 
 A step is one call of the whole forward pass (pooling, low-res logits, top-k
-selection, block attention, low-res attention with the merge) on inputs already
+selection, block attention with the low-res merge) on inputs already
 resident in HBM.  The default workload is the clustered N=4096 bf16 full-mode
 case (B=2, H=12, d=64, block_per_row=4), the one configuration at N=4096 that
 runs every stage.  W untimed warm-up steps, then exactly K timed steps
@@ -15,7 +15,7 @@ Besides tokens/s the line carries:
     on the library's stream (a second loop of K calls through
     mra_attention_fwd_profiled, each call with its own events, one
     synchronisation at the end);
-  * for the block attention and the join kernel, `replay_us`: the average of
+  * for the block attention, `replay_us`: the average of
     K back-to-back relaunches of that kernel alone (mra_debug_replay) between
     one pair of events on the same stream, which leaves out the cost of the
     events between the kernels of a call;
@@ -82,7 +82,7 @@ PEAK_FP32_TFLOPS = 157.3     # MI355X fp32 matrix
 METRIC = "MRA-2 fwd tokens/s and sparse-block MFMA % of peak, N=4096 bf16, 1 MI355X"
 KERNEL_SOURCES = {
     "pool": "mra_pool.hip", "logits": "mra_select.hip", "select": "mra_select.hip",
-    "attn": "mra_attn.hip", "finish": "mra_finish.hip",
+    "attn": "mra_attn.hip",
 }
 
 
@@ -114,7 +114,7 @@ def algorithmic(w, stage: str, sel_blocks: int) -> tuple[float, str]:
         return 2 * BH * nb * d * 4 + BH * nb * nb * 4 + BH * nb * 4 + lowres, "byte"
     if stage == "select":      # logits and row maxima in; K block indices out
         return BH * nb * nb * 4 + BH * nb * 4 + BH * K * 4, "byte"
-    return None, "byte"        # finish: only the rows split into several segments; no fixed volume
+    raise ValueError(stage)
 
 
 def selected_valid_blocks(w) -> int:
@@ -515,10 +515,10 @@ def main():
     avg_ms = {s: sum(ev[2 * si].elapsed_time(ev[2 * si + 1]) for ev in evs) / args.steps
               for si, s in enumerate(stages)}
 
-    # attention and the join kernel alone: back-to-back relaunches on the
-    # workspace the last call filled, one pair of events around them
+    # attention alone: back-to-back relaunches on the workspace the last call
+    # filled, one pair of events around them
     replay_ms = {}
-    for si in (3, 4):
+    for si in (3,):
         r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         mra.debug_replay(q, k, v, si, 2, mask, **kw)
         r0.record()
@@ -531,9 +531,6 @@ def main():
     kernels = {}
     for s, t in avg_ms.items():
         amount, unit = algorithmic(w, s, sel_blocks)
-        if amount is None:
-            kernels[s] = {"avg_us": round(t * 1e3, 2)}
-            continue
         rate = amount / (replay_ms.get(s, t) * 1e-3)
         kernels[s] = {"avg_us": round(t * 1e3, 2), "gbs": round(rate / 1e9, 1),
                       "hbm_frac": round(rate / 1e9 / PEAK_HBM_GBS, 4)}
@@ -544,7 +541,7 @@ def main():
     attn_tflops = attn_flops / (replay_ms["attn"] * 1e-3) / 1e12
     kernels["attn"]["tflops"] = round(attn_tflops, 2)
     kernels["attn"]["mfma_frac"] = round(attn_tflops / mfma_peak, 4)
-    dom = max((s for s in avg_ms if algorithmic(w, s, sel_blocks)[0] is not None), key=avg_ms.get)
+    dom = max(avg_ms, key=avg_ms.get)
     amount, unit = algorithmic(w, dom, sel_blocks)
     dom_s = replay_ms.get(dom, avg_ms[dom]) * 1e-3
     roof = {"kernel": dom, "bound": "hbm", "achieved": round(amount / dom_s / 1e9, 1), "peak": PEAK_HBM_GBS,

@@ -233,7 +233,7 @@ def attention(q, k, v, mask=None, block_per_row=4, approx_mode="full", initial_p
 def attention_noalloc(q, k, v, mask=None, block_per_row=4, approx_mode="full", initial_prior_first_n_blocks=0,
                       initial_prior_diagonal_n_blocks=0, out=None, scale_dim=0):
     """attention() through mra_attention_fwd_noalloc: the library's own fixed
-    device scratch (48 MiB per GPU) serves as the workspace, so the library
+    device scratch (64 MiB per GPU) serves as the workspace, so the library
     allocates nothing; calls on one GPU must not overlap.  Returns `out`."""
     _check_inputs(q, k, v, mask)
     B, H, N, d = q.shape
@@ -276,14 +276,14 @@ def prepare(q, k, v, mask=None, block_per_row=4, approx_mode="full", initial_pri
     return call, out
 
 
-STAGES = ("pool", "logits", "select", "attn", "finish")
+STAGES = ("pool", "logits", "select", "attn")
 
 
 def attention_profiled(q, k, v, events, mask=None, block_per_row=4, approx_mode="full",
                        initial_prior_first_n_blocks=0, initial_prior_diagonal_n_blocks=0, out=None,
                        workspace=None, scale_dim=0):
     """attention() plus HIP event records around each kernel launch.
-    events: 10 torch.cuda.Event(enable_timing=True) (already recorded once, so
+    events: 8 torch.cuda.Event(enable_timing=True) (already recorded once, so
     that their handles exist), entry 2s / 2s+1 bracketing stage STAGES[s]."""
     _check_inputs(q, k, v, mask)
     B, H, N, d = q.shape
@@ -292,7 +292,7 @@ def attention_profiled(q, k, v, events, mask=None, block_per_row=4, approx_mode=
     ws_bytes = workspace_size(B, H, N, d, q.dtype, block_per_row, approx_mode)
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-    arr = (ctypes.c_void_p * 10)(*[e.cuda_event if e is not None else None for e in events])
+    arr = (ctypes.c_void_p * 8)(*[e.cuda_event if e is not None else None for e in events])
     dims = _dims(B, H, N, d, DTYPES[q.dtype], scale_dim)
     st = lib().mra_attention_fwd_profiled(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(mask),
                                           block_per_row, MODES.get(approx_mode, -1), initial_prior_first_n_blocks,
@@ -358,7 +358,7 @@ def attention_backward(q, k, v, out, dout, workspace, mask=None, block_per_row=4
 
 def debug_replay(q, k, v, stage, count, mask=None, block_per_row=4, approx_mode="full",
                  initial_prior_first_n_blocks=0, initial_prior_diagonal_n_blocks=0, out=None, workspace=None, scale_dim=0):
-    """Relaunch stage STAGES[stage] (3 attn or 4 finish only) `count` times on
+    """Relaunch stage STAGES[stage] (3 attn only) `count` times on
     the current stream, on a workspace and out that a forward call with the
     same arguments has filled; for timing the kernel alone."""
     _check_inputs(q, k, v, mask)

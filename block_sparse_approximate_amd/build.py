@@ -28,7 +28,6 @@ UNITS = {
     "mra_pool": ["-ffp-contract=off"],
     "mra_select": ["-ffp-contract=off"],
     "mra_attn": [],
-    "mra_finish": [],
     "mra_bwd": [],
     "mra_api": [],
 }

@@ -5,8 +5,9 @@
 //             histogram
 //   logits    step 1 low-res logits, row maxima, selection-key histogram
 //   select    step 2 top-K selection: bitmap, CSR, attention stream records
-//   attn      step 3 block attention; finishes rows that fit one segment
-//   finish    step 4 low-res attention (full mode) and merge of segments
+//   attn      steps 3 and 4: block attention, the low-res merge (full mode)
+//             and the join of rows cut into several segments or with no
+//             selected block
 // Everything after the argument checks is asynchronous; nothing here waits.
 #include <string.h>
 
@@ -54,11 +55,13 @@ bool carve(const mra_dims& d, int32_t bpr, int32_t mode, Layout* L) {
     L->recs = take(BH * (size_t)L->K * sizeof(BlkRec));
     L->merge_rows = take(BH * nb * 16);
     L->n_merge = take(BH * 4);
+    L->join_cnt = take(BH * nb * 4);
     L->lo_all = mode == MRA_APPROX_FULL ? take(BH * nb * dd * 4) : 0;
     L->ll_all = mode == MRA_APPROX_FULL ? take(BH * nb * 4) : 0;
     L->part_o = take(BH * (size_t)L->max_items * kBlock * dd * 4);
     L->part_ml = take(BH * (size_t)L->max_items * 2 * kBlock * 4);
     L->part_corr = mode == MRA_APPROX_FULL ? take(BH * (size_t)L->max_items * corr_stride(d.head_dim) * 4) : 0;
+    L->park = take(BH * (size_t)attn_grid_waves_per_head(L->BH, L->K) * park_floats(d.head_dim) * 4);
     L->cand = take(BH * (size_t)kSelCap * 8);
     L->ncand = take(BH * kCandStride * 4);
     L->st_m = take(BH * (size_t)L->N * 4);
@@ -167,11 +170,13 @@ Params make_params(const mra_dims& d, const Layout& L, int32_t mode, int32_t pf,
     p.recs = reinterpret_cast<BlkRec*>(w + L.recs);
     p.merge_rows = reinterpret_cast<int4*>(w + L.merge_rows);
     p.n_merge = reinterpret_cast<int32_t*>(w + L.n_merge);
+    p.join_cnt = reinterpret_cast<uint32_t*>(w + L.join_cnt);
     p.lo_all = L.lo_all ? reinterpret_cast<float*>(w + L.lo_all) : nullptr;
     p.ll_all = L.ll_all ? reinterpret_cast<float*>(w + L.ll_all) : nullptr;
     p.part_o = reinterpret_cast<float*>(w + L.part_o);
     p.part_ml = reinterpret_cast<float*>(w + L.part_ml);
     p.part_corr = L.part_corr ? reinterpret_cast<float*>(w + L.part_corr) : nullptr;
+    p.park = reinterpret_cast<float*>(w + L.park);
     p.cand = reinterpret_cast<uint64_t*>(w + L.cand);
     p.ncand = reinterpret_cast<uint32_t*>(w + L.ncand);
     p.st_m = reinterpret_cast<float*>(w + L.st_m);
@@ -240,7 +245,7 @@ MRA_API const char* mra_status_string(int32_t s) {
         case MRA_ERR_WORKSPACE: return "workspace missing or too small";
         case MRA_ERR_HIP: return "a HIP launch failed";
         case MRA_ERR_ALIGN: return "a pointer is not aligned (tensors 16 bytes, workspace 256 bytes)";
-        case MRA_ERR_STAGE: return "stage cannot be replayed (3 and 4 only) or count < 1";
+        case MRA_ERR_STAGE: return "stage cannot be replayed (3 only) or count < 1";
         case MRA_ERR_SCRATCH: return "the sizes need more workspace than the allocation-free entry point holds";
         default: return "unknown status";
     }
@@ -277,7 +282,7 @@ static mra_status run_front(const Params& p, hipStream_t s) {
 static bool bad_ranking(int32_t r) { return r != MRA_RANK_ROW_NORMALIZED && r != MRA_RANK_RAW_LOGITS; }
 static bool bad_band(int32_t b) { return b != MRA_BAND_SYMMETRIC && b != MRA_BAND_EXACT; }
 
-// The launch sequence; ev (10 events or null) brackets each stage.
+// The launch sequence; ev (8 events or null) brackets each of the four stages.
 static mra_status run_forward(const mra_dims* dims, const void* q, const void* k, const void* v,
                               const uint8_t* mask, int32_t block_per_row, int32_t approx_mode, int32_t prior_first,
                               int32_t prior_diag, void* out, void* workspace, size_t workspace_bytes, void* stream,
@@ -308,9 +313,6 @@ static mra_status run_forward(const mra_dims* dims, const void* q, const void* k
     if (e == hipSuccess) e = mark(6);
     if (e == hipSuccess) e = launch_attn(p, s);
     if (e == hipSuccess) e = mark(7);
-    if (e == hipSuccess) e = mark(8);
-    if (e == hipSuccess) e = launch_finish(p, s);
-    if (e == hipSuccess) e = mark(9);
     return e == hipSuccess ? MRA_OK : MRA_ERR_HIP;
 }
 
@@ -487,7 +489,6 @@ MRA_API mra_status mra_bigbird_fwd(const mra_dims* dims, const void* q, const vo
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (launch_bigbird_layout(p, s) != hipSuccess) return MRA_ERR_HIP;
     if (launch_attn(p, s) != hipSuccess) return MRA_ERR_HIP;
-    if (launch_finish(p, s) != hipSuccess) return MRA_ERR_HIP;
     return MRA_OK;
 }
 
@@ -523,7 +524,7 @@ MRA_API mra_status mra_bigbird_bwd(const mra_dims* dims, const void* q, const vo
 // Host code never uses the array's name as an address: each device's copy is
 // looked up once with hipGetSymbolAddress (with that device current) and
 // only that pointer is passed to kernels.
-constexpr size_t kScratchBytes = size_t(48) << 20;
+constexpr size_t kScratchBytes = size_t(64) << 20;
 constexpr int kMaxDevices = 64;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
@@ -580,11 +581,11 @@ MRA_API mra_status mra_debug_replay(const mra_dims* dims, const void* q, const v
     mra_status st = check_call(dims, q, k, v, mask, block_per_row, approx_mode, prior_first, prior_diag, out,
                                workspace, workspace_bytes, true, &L);
     if (st != MRA_OK) return st;
-    if ((stage != 3 && stage != 4) || count < 1) return MRA_ERR_STAGE;
+    if (stage != 3 || count < 1) return MRA_ERR_STAGE;
     const Params p = make_params(*dims, L, approx_mode, prior_first, prior_diag, q, k, v, mask, out, workspace);
     hipStream_t s = static_cast<hipStream_t>(stream);
     for (int32_t c = 0; c < count; c++)
-        if ((stage == 3 ? launch_attn(p, s) : launch_finish(p, s)) != hipSuccess) return MRA_ERR_HIP;
+        if (launch_attn(p, s) != hipSuccess) return MRA_ERR_HIP;
     return MRA_OK;
 }
 

@@ -4,20 +4,24 @@
 //
 // Work decomposition: the selector lists every selected block of a head in
 // CSR order (block row, then key block), each row cut into segments of at
-// most kChunk blocks.  W waves share a head: wave k takes the blocks
-// [k*K/W, (k+1)*K/W) of that list, moved to the next segment boundaries, so
-// every wave gets about the same number of blocks whatever the row lengths.
-// A wave streams through its blocks in batches: it issues the K, V and Q
-// loads of two blocks at once, then computes them, while the other wave on
-// its SIMD does the same half a batch out of step.
+// most kChunk blocks.  The G workgroups of a head split that list into G
+// ranges of about K/G blocks, each moved to the nearest segment start, and
+// the kWaves waves of a workgroup split its range exactly into kWaves equal
+// parts, wherever those cuts fall: every wave gets the same number of blocks
+// whatever the row lengths.  A segment cut between two waves is finished by
+// the wave holding its first block, after the workgroup's one barrier, from
+// its own accumulators and the pieces the next waves parked (see below).
+// A wave streams through its blocks one at a time: each block stages its K,
+// V (and Q) in LDS and then issues the next block's loads, which arrive
+// while it is computed; the other wave on the SIMD computes meanwhile.
 //
 // Per key block j of a segment of query block row i:
 //   S^T = K_j Q_i^T           4 x MFMA 32x32x16 bf16 (fp32: 32 x 32x32x2 f32);
-//                             bf16 K_j is loaded straight into LDS as whole
-//                             rows and read back in the operand layout
+//                             bf16 K_j is loaded as whole rows, stored in LDS
+//                             and read back in the operand layout
 //   online max / exp2 / sum   in registers: lane l holds query l%32 and 16 of
 //                             its 32 keys, so row reductions need one swap
-//                             with lane l^32
+//                             between the two halves of the wave
 //   O^T += V_j^T P^T          V_j staged through LDS and read back transposed
 //                             with ds_read_b64_tr_b16; P goes straight from
 //                             the S^T accumulators into the B operand
@@ -37,7 +41,25 @@
 // with M the larger of the high-res max m and the low-res row max m_i (both
 // in log2 units).  Other segments write un-normalised partials (O, running
 // max, sum, and in full mode the segment's sums of w vhat_j and of w) that
-// the finish kernel joins.
+// the last of them joins.
+//
+// Joins without a separate kernel, at two levels:
+//   * within a workgroup: a wave whose part starts inside a segment parks
+//     its piece of it (O, running max, sum, and in full mode its sums of
+//     w vhat_j and of w) in its slot with plain stores; after the barrier
+//     the wave holding the segment's first block adds the parked pieces of
+//     the next waves to its own and finishes the segment as if it had done
+//     it alone;
+//   * across workgroups: a row cut into several segments (only rows longer
+//     than kChunk blocks) is joined by the wave that ends its last segment
+//     to arrive.  Every segment of a cut row stores its partials with
+//     agent-scope (write-through) stores; after its part, the wave waits for
+//     them to complete and adds one to each such row's counter; the wave
+//     that completes a count reads the partials back with agent-scope loads,
+//     writes the row and sets the counter back to zero.  Only these partials
+//     take the coherent path, so no cache-wide writeback is needed.
+// Rows with no selected block are written last, listed rows k, k + W, ... by
+// wave k of the head.
 //
 // Workgroups are placed XCD-aware: workgroup g runs on XCD g % 8, and all
 // waves of head bh are on XCD bh % 8, so a head's K/V re-reads stay in one L2.
@@ -53,8 +75,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 // 16 bytes of a K, V or Q row.  A native vector, so copies are plain loads and
-// stores (HIP's uint4 struct is copied with memcpy, which can keep a batch's
-// register slots in scratch memory).
+// stores (HIP's uint4 struct is copied with memcpy, which can keep a load
+// slot's registers in scratch memory).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
@@ -66,13 +88,25 @@ __host__ __device__ constexpr int q_stride_b(int hd) { return hd + 8; }    // bf
 __host__ __device__ constexpr int v_stride_f(int hd) { return hd + 4; }    // fp32 V
 constexpr int kWindow = 64;     // block records a wave holds (one per lane)
 constexpr float kLazyMax = 8.0f;   // log2 headroom of the running max (probabilities <= 256)
-// blocks per wave before segment alignment: an end moves up to kChunk - 1
-// blocks forward, a start up to kChunk / 2 back
-constexpr int kMaxRun = kWindow - kChunk - kChunk / 2;
+// Blocks per wave, on average over a workgroup's range, at most: a
+// workgroup's range grows by up to kChunk / 2 blocks at each end when they
+// move to segment starts, and each of its kWaves parts must fit the window.
+constexpr int kMaxRun = (kWaves * kWindow - 2 * kChunk - 2 * kWaves) / kWaves;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 __device__ __forceinline__ int rl(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
+// x combined with its value in lane l ^ 32, by one lane swap between the two
+// halves of the wave (lanes l < 32 hold the lower operand of the pair in the
+// swap's first result, so both halves combine the pair in the same order)
+__device__ __forceinline__ float xhalf_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // key index held by accumulator register r of a 32x32 MFMA tile in lane l
 __device__ __forceinline__ int acc_row(int r, int lane) { return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); }
@@ -94,24 +128,21 @@ __device__ __forceinline__ int nearest_segment_start(int x, uint32_t info, int64
 // DT: 1 bf16, 0 fp32; HD: channels per head (64 or 128)
 template <int DT, int HD> struct Cfg;
 template <int HD> struct Cfg<1, HD> {       // bf16: 16 bytes per lane per 8 elements
-    static constexpr int kBatch = 2;        // blocks whose loads are in flight together
-    static constexpr int kKV = HD / 16;     // 16-byte pieces per lane for one V (or Q) block
-    static constexpr bool kKDirect = true;  // K goes straight from memory to LDS
+    static constexpr int kKV = HD / 16;     // 16-byte pieces per lane for one K, V or Q block
     using Elem = uint16_t;
 };
 template <int HD> struct Cfg<0, HD> {       // fp32: twice the registers per block
-    static constexpr int kBatch = 1;
     static constexpr int kKV = HD / 8;
-    static constexpr bool kKDirect = false;
     using Elem = float;
 };
 
 // bf16 K block in LDS: 32 token rows of 2 HD bytes, the 16-byte chunk c of
 // row r at a swizzled position of the row: c ^ ((r / 2) mod 8) for 128-byte
-// rows, c ^ (r mod 16) for 256-byte ones.  The direct loads place the chunks
-// so (whole rows per HD / 8 lanes, i.e. full cache lines), and the MFMA
-// operand reads (lane: one row, one chunk) then hit distinct banks in each
-// 16-lane phase.
+// rows, c ^ (r mod 16) for 256-byte ones.  K is loaded as whole rows (full
+// cache lines) and stored so, and the MFMA operand reads (lane: one row, one
+// chunk) then hit distinct banks in each 16-lane phase.  (Loads straight
+// into LDS would save the registers, but the compiler then drains every
+// load in flight before each LDS access, which serialises the blocks.)
 template <int HD>
 __device__ __forceinline__ int swz_key(int row) { return HD == 64 ? row >> 1 : row; }
 template <int HD>
@@ -119,31 +150,31 @@ __device__ __forceinline__ int k_swz(int row, int chunk) {
     return row * HD + ((chunk ^ swz_key<HD>(row)) & (HD / 8 - 1)) * 8;
 }
 
-// Per-wave LDS.  bf16: the K blocks of a batch (k_swz), V_j (read back
-// transposed) and Q_i; fp32: V_j.
+// Per-wave LDS.  bf16: K_j (k_swz), V_j (read back transposed) and Q_i;
+// fp32: V_j.
 template <int DT, int HD> struct StageBuf;
 template <int HD> struct StageBuf<1, HD> {
-    uint16_t kring[Cfg<1, HD>::kBatch][kBlock * HD];
+    uint16_t k[kBlock * HD];
     uint16_t v[kBlock * v_stride_b(HD)];
     uint16_t qs[kBlock * q_stride_b(HD)];
+    int pend[kWindow];   // rows of the cut segments this wave ended, counted after its range
 };
 template <int HD> struct StageBuf<0, HD> {
     float v[kBlock * v_stride_f(HD)];
+    int pend[kWindow];
 };
 
-// The attention kernel's dynamic LDS: kWaves StageBufs.  The direct loads
-// address it through this symbol, so that the compiler sees they write LDS
-// only (and can keep a batch's register slots in registers).
+// The attention kernel's dynamic LDS: kWaves StageBufs.
 extern __shared__ __align__(16) unsigned char attn_smem[];
 
 // Full mode keeps one low-res value per channel in lanes: channel lane + 64 x,
 // x < HD / 64.
 template <int DT, int HD>
 struct Slot {
-    u32x4 k[Cfg<DT, HD>::kKDirect ? 1 : Cfg<DT, HD>::kKV];   // (unused when K goes straight to LDS)
+    u32x4 k[Cfg<DT, HD>::kKV];
     u32x4 v[Cfg<DT, HD>::kKV];
     u32x4 q[Cfg<DT, HD>::kKV];   // Q of the block's row
-    uint32_t qm;                 // and its mask word (segment's first block)
+    uint32_t qm;                 // and its mask word
     float vh[HD / 64];           // full mode: vhat_j at this lane's channels
     float lo[HD / 64];           // full mode: lo_all_i at this lane's channels (segment's first block)
 };
@@ -153,8 +184,10 @@ struct Wave {
     // record window: lane t holds the record of block a + t, and in full mode
     // the low-res row max and weight sum of that block's row
     uint32_t wij, wk, winfo;
-    float ww, wm, wll;
-    int a;
+    float ww, wm, wll;       // full mode: the cell's low-res weight, its row's max and weight sum
+    int a;                   // first block of the window (= start)
+    int start, end;          // the wave's blocks [start, end)
+    float* park;             // the wave's slot for a piece of a segment that another wave finishes
     int bh, b, nb, lane, n, h;
     int wave;                // the wave's index in its workgroup (its StageBuf)
     const typename Cfg<DT, HD>::Elem* Qg;
@@ -162,15 +195,15 @@ struct Wave {
     const typename Cfg<DT, HD>::Elem* Vg;
 };
 
-// Issue the loads of stream block e into a batch slot: K_j, V_j, vhat_j at
-// this lane's channel (full mode), and when the block starts a segment Q_i,
-// the mask word of row i and lo_all_i at this lane's channel (full mode).
+// Issue the loads of stream block e into the load slot: K_j, V_j, Q_i, the
+// mask word of row i, and in full mode vhat_j and lo_all_i at this lane's
+// channel.
 __device__ __forceinline__ int rec_i(uint32_t ij) { return (int)(ij & 0xFFFFu); }
 __device__ __forceinline__ int rec_j(uint32_t ij) { return (int)(ij >> 16); }
 
 template <int DT, int HD, bool FULL>
 __device__ __forceinline__ void issue(const Params& p, const Wave<DT, HD>& W, int e, Slot<DT, HD>& s,
-                                      StageBuf<DT, HD>& sb, int u) {
+                                      StageBuf<DT, HD>& sb) {
     constexpr int kKV = Cfg<DT, HD>::kKV;
     const int we = e - W.a;
     const uint32_t ij = (uint32_t)rl((int)W.wij, we);
@@ -184,28 +217,19 @@ __device__ __forceinline__ void issue(const Params& p, const Wave<DT, HD>& W, in
         const uint16_t* Vb = W.Vg + (size_t)j * kBlock * HD;
         const uint16_t* Qb = W.Qg + (size_t)i * kBlock * HD;
         const int off = (lane / kRowLanes) * HD + (lane % kRowLanes) * 8;
-        // K_j straight into LDS slot u, 1 KiB (whole token rows) per load:
-        // lane l fetches the chunk that belongs at its LDS position (a load
-        // of every row's 32-byte operand piece instead would cost the
+        // K_j and V_j: whole token rows per HD / 8 lanes, 1 KiB per load (a
+        // load of every row's 32-byte operand piece instead would cost the
         // address unit several times more)
-        typedef __attribute__((address_space(3))) void lds_void;
-        using SB = StageBuf<1, HD>;
-        const size_t kbase = (size_t)W.wave * sizeof(SB) + offsetof(SB, kring) + (size_t)u * sizeof(sb.kring[0]);
 #pragma unroll
-        for (int x = 0; x < kKV; x++) {
-            const int r = kRowsPerLoad * x + lane / kRowLanes, pos = lane % kRowLanes;
-            const int c = (pos ^ swz_key<HD>(r)) & (kRowLanes - 1);   // the chunk k_swz puts at pos
-            __builtin_amdgcn_global_load_lds(Kb + r * HD + 8 * c, (lds_void*)(attn_smem + kbase + x * 1024), 16, 0, 0);
-        }
+        for (int x = 0; x < kKV; x++) s.k[x] = *reinterpret_cast<const u32x4*>(Kb + off + kRowsPerLoad * x * HD);
 #pragma unroll
         for (int x = 0; x < kKV; x++) s.v[x] = *reinterpret_cast<const u32x4*>(Vb + off + kRowsPerLoad * x * HD);
-        // V_j and Q_i: whole token rows per HD / 8 lanes, so every load is
-        // full cache lines; Q_i once per segment, by its first block (the
-        // other blocks leave s.q unset: only a segment's first block reads it)
-        if (info_pos((uint32_t)rl((int)W.winfo, we)) == 0) {
+        // Q_i likewise.  Every block loads Q_i (only a piece's first
+        // block stages it; the others hit the cache): with the same loads for
+        // every block the waits for a slot's data count exactly, rather than
+        // draining every load in flight at each piece start.
 #pragma unroll
-            for (int x = 0; x < kKV; x++) s.q[x] = *reinterpret_cast<const u32x4*>(Qb + off + kRowsPerLoad * x * HD);
-        }
+        for (int x = 0; x < kKV; x++) s.q[x] = *reinterpret_cast<const u32x4*>(Qb + off + kRowsPerLoad * x * HD);
     } else {
         // lane l: token l % 32, channels HD / 2 * (l / 32) .. + HD / 2 - 1 of K and Q
         const float* Kb = W.Kg + (size_t)j * kBlock * HD;
@@ -224,19 +248,12 @@ __device__ __forceinline__ void issue(const Params& p, const Wave<DT, HD>& W, in
         for (int c4 = 0; c4 < kKV; c4++)
             s.q[c4] = *reinterpret_cast<const u32x4*>(Qb + n * HD + (HD / 2) * h + 4 * c4);
     }
-    // once per segment, by its first block: the row's mask word (uniform, so
-    // through the scalar cache) and in full mode lo_all_i; every block: vhat_j
-    typedef __attribute__((address_space(4))) const uint32_t const_u32;
-    if (info_pos((uint32_t)rl((int)W.winfo, we)) == 0) {
-        s.qm = *reinterpret_cast<const_u32*>((uintptr_t)(p.mbits + (size_t)W.b * W.nb + i));
-        if constexpr (FULL) {
+    // every block, for the same reason: the row's mask word (a vector load,
+    // so that it joins the same count), in full mode lo_all_i and vhat_j
+    s.qm = p.mbits[(size_t)W.b * W.nb + i];
+    if constexpr (FULL) {
 #pragma unroll
-            for (int x = 0; x < HD / 64; x++) s.lo[x] = p.lo_all[((size_t)W.bh * W.nb + i) * HD + lane + 64 * x];
-        }
-    } else {
-        s.qm = 0u;
-#pragma unroll
-        for (int x = 0; x < HD / 64; x++) s.lo[x] = 0.f;
+        for (int x = 0; x < HD / 64; x++) s.lo[x] = p.lo_all[((size_t)W.bh * W.nb + i) * HD + lane + 64 * x];
     }
     if constexpr (FULL) {
 #pragma unroll
@@ -252,14 +269,174 @@ struct Acc {
     float sw;             // full mode: sum of their weights w
     float lo[HD / 64];    // full mode: lo_all_i at this lane's channels
     uint32_t qm;          // valid-token mask word of the segment's row
+    int npend;            // entries of the wave's pending-join list
+    int jend;             // >= 0: the piece held at the end of the range belongs to a segment that
+                          //   goes on into the next waves and ends at stream block jend
 };
+
+// Partials of cut rows go through agent-scope (coherent, write-through)
+// stores and loads, so that whichever wave joins the row sees them.
+__device__ __forceinline__ void store4_coherent(float* dst, float a, float b, float c, float d) {
+    uint64_t* q = reinterpret_cast<uint64_t*>(dst);
+    const uint64_t lo = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+    const uint64_t hi = (uint64_t)__float_as_uint(c) | ((uint64_t)__float_as_uint(d) << 32);
+    __hip_atomic_store(q, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(float* dst, float v) {
+    __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* src) {
+    return __hip_atomic_load(const_cast<float*>(src), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float4 load4_coherent(const float* src) {
+    uint64_t* q = reinterpret_cast<uint64_t*>(const_cast<float*>(src));
+    const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_float4(__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
+                       __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32)));
+}
+
+// Write block row i of head W.bh from nseg segment partials (items first ..
+// first + nseg - 1), and in full mode the row's low-resolution part
+// ([MRA] "第四步"), per query token t with M the largest of the maxima:
+//   out_t = (sum_c O_c 2^(m_c - M) + lo 2^(m_i log2e - M))
+//         / (sum_c l_c 2^(m_c - M) + ll 2^(m_i log2e - M)),
+//   lo = lo_all_i - sum_c corr_c,  ll = ll_all_i - sum_c sw_c;
+// 0 when the denominator is 0 or the token is padding.  nseg = 0 is a row
+// with no selected block.  Lane l holds token l % 32 and the channels of the
+// attention accumulators' layout; lo_lds: HD floats of the wave's LDS.
+template <int DT, int HD, bool FULL>
+__device__ __forceinline__ void join_row(const Params& p, int bh, int b, int nb, int lane, int i, int first, int nseg,
+                                      float* lo_lds) {
+    constexpr int kSeg = HD == 64 ? 2 : 1;   // segments whose loads are in flight together
+    const int n = lane & 31, h = lane >> 5;
+    const size_t pbase = (size_t)bh * p.max_items;
+    const size_t row = (size_t)bh * nb + i;
+    // the row's own inputs, loaded with the first segments' partials
+    const uint32_t qm = p.mbits[(size_t)b * nb + i];
+    float lo_in[HD / 64], ll_in = 0.f, mrow = 0.f;
+    if constexpr (FULL) {
+#pragma unroll
+        for (int x = 0; x < HD / 64; x++) lo_in[x] = p.lo_all[row * HD + lane + 64 * x];
+        ll_in = p.ll_all[row];
+        mrow = p.rowmax[row];
+    }
+    float M = -__builtin_inff(), den = 0.f, sw = 0.f;
+    float acc[HD / 2], corr[HD / 64];
+#pragma unroll
+    for (int e = 0; e < HD / 2; e++) acc[e] = 0.f;
+#pragma unroll
+    for (int x = 0; x < HD / 64; x++) corr[x] = 0.f;
+    for (int c0 = 0; c0 < nseg; c0 += kSeg) {
+        float mc[kSeg], lc[kSeg];
+        float4 oc[kSeg][HD / 8];
+#pragma unroll
+        for (int c = 0; c < kSeg; c++) {
+            const bool ok = c0 + c < nseg;
+            const size_t pidx = pbase + (size_t)min(first + (ok ? c0 + c : 0), p.max_items - 1);
+            mc[c] = ok ? load_coherent(p.part_ml + pidx * 64 + n) : -__builtin_inff();
+            lc[c] = ok ? load_coherent(p.part_ml + pidx * 64 + 32 + n) : 0.f;
+            const float* po = p.part_o + (pidx * kBlock + n) * HD;
+#pragma unroll
+            for (int mt = 0; mt < HD / 32; mt++)
+#pragma unroll
+                for (int gq = 0; gq < 4; gq++)
+                    oc[c][mt * 4 + gq] = ok ? load4_coherent(po + 32 * mt + 8 * gq + 4 * h)
+                                            : make_float4(0.f, 0.f, 0.f, 0.f);
+            if constexpr (FULL) {
+                if (ok) {
+                    const float* pc = p.part_corr + pidx * corr_stride(HD);
+#pragma unroll
+                    for (int x = 0; x < HD / 64; x++) corr[x] += load_coherent(pc + lane + 64 * x);
+                    sw += load_coherent(pc + HD);
+                }
+            }
+        }
+        float Mb = M;
+#pragma unroll
+        for (int c = 0; c < kSeg; c++) Mb = fmaxf(Mb, mc[c]);
+        if (Mb != -__builtin_inff()) {
+            const float sM = M == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(M - Mb);
+            den *= sM;
+#pragma unroll
+            for (int e = 0; e < HD / 2; e++) acc[e] *= sM;
+#pragma unroll
+            for (int c = 0; c < kSeg; c++) {
+                const float f = mc[c] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mc[c] - Mb);
+                den += lc[c] * f;
+#pragma unroll
+                for (int x = 0; x < HD / 8; x++) {
+                    acc[4 * x] += oc[c][x].x * f;
+                    acc[4 * x + 1] += oc[c][x].y * f;
+                    acc[4 * x + 2] += oc[c][x].z * f;
+                    acc[4 * x + 3] += oc[c][x].w * f;
+                }
+            }
+            M = Mb;
+        }
+    }
+    float Mu = M;   // the max that den and the probabilities are relative to
+    if constexpr (FULL) {
+        // the row's low-res part: lo_all minus the segments' corrections, one channel per lane
+#pragma unroll
+        for (int x = 0; x < HD / 64; x++) lo_lds[lane + 64 * x] = lo_in[x] - corr[x];
+        const float ll = fmaxf(ll_in - sw, 0.f), mi2 = mrow * kLog2e;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const float Mf = fmaxf(M, mi2);
+        if (Mf != -__builtin_inff()) {
+            const float sM = M == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(M - Mf);
+            const float f = __builtin_amdgcn_exp2f(mi2 - Mf);
+            den = den * sM + ll * f;
+            Mu = Mf;
+#pragma unroll
+            for (int mt = 0; mt < HD / 32; mt++)
+#pragma unroll
+                for (int gq = 0; gq < 4; gq++) {
+                    const float4 lo = *reinterpret_cast<const float4*>(lo_lds + 32 * mt + 8 * gq + 4 * h);
+                    float* a = acc + 4 * (mt * 4 + gq);
+                    a[0] = a[0] * sM + lo.x * f;
+                    a[1] = a[1] * sM + lo.y * f;
+                    a[2] = a[2] * sM + lo.z * f;
+                    a[3] = a[3] * sM + lo.w * f;
+                }
+        }
+    }
+    const bool valid = (qm >> n) & 1u;
+    const float inv = (valid && den > 0.f) ? 1.0f / den : 0.f;
+    const int tok = i * kBlock + n;
+    if (h == 0 && p.save_stats) {   // the token's softmax statistics, for the backward pass
+        const size_t st = (size_t)bh * p.N + tok;
+        p.st_m[st] = Mu == -__builtin_inff() ? 0.f : Mu;
+        p.st_linv[st] = inv;
+    }
+    const size_t orow = ((size_t)bh * p.N + tok) * HD;
+#pragma unroll
+    for (int mt = 0; mt < HD / 32; mt++)
+#pragma unroll
+        for (int gq = 0; gq < 4; gq++) {
+            const int d0 = 32 * mt + 8 * gq + 4 * h;
+            const float* a = acc + 4 * (mt * 4 + gq);
+            if constexpr (DT == 1) {
+                uint2 pk;
+                pk.x = (uint32_t)float_to_bf16(a[0] * inv) | ((uint32_t)float_to_bf16(a[1] * inv) << 16);
+                pk.y = (uint32_t)float_to_bf16(a[2] * inv) | ((uint32_t)float_to_bf16(a[3] * inv) << 16);
+                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + orow + d0) = pk;
+            } else {
+                *reinterpret_cast<float4*>(static_cast<float*>(p.out) + orow + d0) =
+                    make_float4(a[0] * inv, a[1] * inv, a[2] * inv, a[3] * inv);
+            }
+        }
+}
 
 // Finish a segment: a whole row writes its output, otherwise a partial.
 template <int DT, int HD, bool FULL>
-__device__ __forceinline__ void finish_segment(const Params& p, const Wave<DT, HD>& W, const Acc<DT, HD>& A, int we,
-                                               int i, uint32_t info, float* lo_lds) {
+__device__ __forceinline__ void finish_segment(const Params& p, const Wave<DT, HD>& W, Acc<DT, HD>& A, int we,
+                                               int i, uint32_t info, float* lo_lds, int* pend) {
     const int n = W.n, h = W.h;
-    const float ltot = A.lsum + __shfl_xor(A.lsum, 32, 64);
+    const float ltot = xhalf_sum(A.lsum);
     const int tok = i * kBlock + n;
     if (info_whole(info)) {
         const bool valid = (A.qm >> n) & 1u;
@@ -322,25 +499,89 @@ __device__ __forceinline__ void finish_segment(const Params& p, const Wave<DT, H
             for (int gq = 0; gq < 4; gq++) {
                 const int d0 = 32 * mt + 8 * gq + 4 * h;
                 const f32x16& oo = A.o[mt];
-                *reinterpret_cast<float4*>(po + d0) = make_float4(oo[4 * gq], oo[4 * gq + 1], oo[4 * gq + 2], oo[4 * gq + 3]);
+                store4_coherent(po + d0, oo[4 * gq], oo[4 * gq + 1], oo[4 * gq + 2], oo[4 * gq + 3]);
             }
         if (h == 0) {
-            p.part_ml[pidx * 64 + n] = A.mrun;
-            p.part_ml[pidx * 64 + 32 + n] = ltot;
+            store_coherent(p.part_ml + pidx * 64 + n, A.mrun);
+            store_coherent(p.part_ml + pidx * 64 + 32 + n, ltot);
         }
         if constexpr (FULL) {   // the segment's share of the low-res correction
             float* pc = p.part_corr + pidx * corr_stride(HD);
 #pragma unroll
-            for (int x = 0; x < HD / 64; x++) pc[W.lane + 64 * x] = A.corr[x];
-            if (W.lane == 0) pc[HD] = A.sw;
+            for (int x = 0; x < HD / 64; x++) store_coherent(pc + W.lane + 64 * x, A.corr[x]);
+            if (W.lane == 0) store_coherent(pc + HD, A.sw);
+        }
+        // counted after the range (the count's atomics and the wait for
+        // these stores to complete are taken once, together)
+        if (A.npend < kWindow) {   // a range of at most kWindow blocks ends at most kWindow segments
+            if (W.lane == 0) pend[A.npend] = i;
+            A.npend++;
+        } else if (W.lane == 0) {
+            atomicOr(reinterpret_cast<unsigned int*>(p.error), 4u);
         }
     }
+}
+
+// A wave's piece of a segment that another wave of the workgroup finishes,
+// in its slot: O^T (float4 x of every lane together), then per lane the
+// running max, the sum, and in full mode the low-res correction and weight
+// sum.  Plain stores: the reader is in the same workgroup, after a barrier.
+template <int HD> __host__ __device__ constexpr int park_m_off() { return 64 * (HD / 2); }
+template <int DT, int HD, bool FULL>
+__device__ __forceinline__ void park_piece(const Wave<DT, HD>& W, const Acc<DT, HD>& A) {
+    float4* o4 = reinterpret_cast<float4*>(W.park);
+#pragma unroll
+    for (int mt = 0; mt < HD / 32; mt++)
+#pragma unroll
+        for (int gq = 0; gq < 4; gq++)
+            o4[(mt * 4 + gq) * 64 + W.lane] =
+                make_float4(A.o[mt][4 * gq], A.o[mt][4 * gq + 1], A.o[mt][4 * gq + 2], A.o[mt][4 * gq + 3]);
+    float* t = W.park + park_m_off<HD>();
+    t[W.lane] = A.mrun;
+    t[64 + W.lane] = A.lsum;
+    if constexpr (FULL) {
+#pragma unroll
+        for (int x = 0; x < HD / 64; x++) t[128 + 64 * x + W.lane] = A.corr[x];
+        t[128 + HD + W.lane] = A.sw;
+    }
+}
+
+// Add a parked piece (slot src) of the segment held in A: both are relative
+// to their own running maxima, the sum to the larger of the two.
+template <int DT, int HD, bool FULL>
+__device__ __forceinline__ void merge_piece(const float* src, int lane, Acc<DT, HD>& A) {
+    const float4* o4 = reinterpret_cast<const float4*>(src);
+    float4 po[HD / 8];
+#pragma unroll
+    for (int x = 0; x < HD / 8; x++) po[x] = o4[x * 64 + lane];
+    const float* t = src + park_m_off<HD>();
+    const float mp = t[lane], lp = t[64 + lane];
+    if constexpr (FULL) {
+#pragma unroll
+        for (int x = 0; x < HD / 64; x++) A.corr[x] += t[128 + 64 * x + lane];
+        A.sw += t[128 + HD + lane];
+    }
+    const float M = fmaxf(A.mrun, mp);
+    const float sa = A.mrun == -__builtin_inff() ? 0.f : fast_exp2(A.mrun - M);
+    const float sp = mp == -__builtin_inff() ? 0.f : fast_exp2(mp - M);
+    A.lsum = A.lsum * sa + lp * sp;
+    A.mrun = M;
+#pragma unroll
+    for (int mt = 0; mt < HD / 32; mt++)
+#pragma unroll
+        for (int gq = 0; gq < 4; gq++) {
+            const float4 v = po[mt * 4 + gq];
+            A.o[mt][4 * gq] = A.o[mt][4 * gq] * sa + v.x * sp;
+            A.o[mt][4 * gq + 1] = A.o[mt][4 * gq + 1] * sa + v.y * sp;
+            A.o[mt][4 * gq + 2] = A.o[mt][4 * gq + 2] * sa + v.z * sp;
+            A.o[mt][4 * gq + 3] = A.o[mt][4 * gq + 3] * sa + v.w * sp;
+        }
 }
 
 // One block of the stream: S^T, online softmax, O^T += V^T P^T.
 template <int DT, int HD, bool FULL>
 __device__ __forceinline__ void process(const Params& p, const Wave<DT, HD>& W, int e, Slot<DT, HD>& s,
-                                        Acc<DT, HD>& A, StageBuf<DT, HD>& sb, int u, float scale2) {
+                                        Acc<DT, HD>& A, StageBuf<DT, HD>& sb, float scale2, int next) {
     constexpr int kKV = Cfg<DT, HD>::kKV;
     auto* vs = sb.v;
     const int we = e - W.a;
@@ -348,7 +589,8 @@ __device__ __forceinline__ void process(const Params& p, const Wave<DT, HD>& W, 
     const uint32_t kb = (uint32_t)rl((int)W.wk, we);
     const uint32_t info = (uint32_t)rl((int)W.winfo, we);
     const int lane = W.lane, n = W.n, h = W.h;
-    if (info_pos(info) == 0) {   // a segment starts: alpha = 0 below clears O and l
+    const bool piece_start = info_pos(info) == 0 || e == W.start;
+    if (piece_start) {   // a segment (or the wave's piece of one) starts: alpha = 0 below clears O and l
         A.mrun = -__builtin_inff();
         A.qm = s.qm;
         if constexpr (FULL) {
@@ -370,31 +612,45 @@ __device__ __forceinline__ void process(const Params& p, const Wave<DT, HD>& W, 
 #pragma unroll
     for (int r = 0; r < 16; r++) S[r] = 0.f;
     if constexpr (DT == 1) {
-        // stage V_j (and Q_i when the segment starts) in this wave's LDS
-        // region; K_j (already in slot u) and Q are read back one token row
-        // per lane (the MFMA operand layout: lane l holds token l % 32,
-        // channels 16 kc + 8 (l / 32))
+        // stage K_j, V_j (and Q_i when a piece starts) in this wave's LDS
+        // region; K and Q are read back one token row per lane (the MFMA
+        // operand layout: lane l holds token l % 32, channels 16 kc + 8 (l / 32))
         constexpr int kRowLanes = HD / 8, kRowsPerLoad = 64 / kRowLanes;
         constexpr int VS = v_stride_b(HD), QS = q_stride_b(HD);
         uint16_t* qs = sb.qs;
         const int r0 = lane / kRowLanes, c0 = (lane % kRowLanes) * 8;
 #pragma unroll
         for (int x = 0; x < kKV; x++)
+            *reinterpret_cast<u32x4*>(sb.k + k_swz<HD>(r0 + kRowsPerLoad * x, lane % kRowLanes)) = s.k[x];
+#pragma unroll
+        for (int x = 0; x < kKV; x++)
             *reinterpret_cast<u32x4*>(vs + (r0 + kRowsPerLoad * x) * VS + c0) = s.v[x];
-        if (info_pos(info) == 0) {
+        if (piece_start) {
 #pragma unroll
             for (int x = 0; x < kKV; x++)
                 *reinterpret_cast<u32x4*>(qs + (r0 + kRowsPerLoad * x) * QS + c0) = s.q[x];
         }
+        // the slot is free once staged: the next block's loads go out now,
+        // to arrive while this block is computed
+        issue<DT, HD, FULL>(p, W, next, s, sb);
+        __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // every operand read first, then the MFMA chain (one LDS round trip)
+        u32x4 ka[HD / 16], qa[HD / 16];
 #pragma unroll
         for (int kc = 0; kc < HD / 16; kc++) {
-            const u32x4 ka = *reinterpret_cast<const u32x4*>(sb.kring[u] + k_swz<HD>(n, 2 * kc + h));
-            const u32x4 qa = *reinterpret_cast<const u32x4*>(qs + n * QS + 16 * kc + 8 * h);
-            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka), as_bf16x8(qa), S, 0, 0, 0);
+            ka[kc] = *reinterpret_cast<const u32x4*>(sb.k + k_swz<HD>(n, 2 * kc + h));
+            qa[kc] = *reinterpret_cast<const u32x4*>(qs + n * QS + 16 * kc + 8 * h);
         }
+#pragma unroll
+        for (int kc = 0; kc < HD / 16; kc++)
+            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[kc]), as_bf16x8(qa[kc]), S, 0, 0, 0);
+        // keep the reads together ahead of the MFMAs (the scheduler would
+        // otherwise interleave them and wait for each pair)
+        __builtin_amdgcn_sched_group_barrier(0x100, HD / 8, 0);   // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, HD / 16, 0);  // MFMA
     } else {
         constexpr int kRowLanes = HD / 4, kRowsPerLoad = 64 / kRowLanes;
         constexpr int VS = v_stride_f(HD);
@@ -411,6 +667,9 @@ __device__ __forceinline__ void process(const Params& p, const Wave<DT, HD>& W, 
             S = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.z, qf.z, S, 0, 0, 0);
             S = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.w, qf.w, S, 0, 0, 0);
         }
+        // K and Q are used, V is staged: the next block's loads go out now
+        issue<DT, HD, FULL>(p, W, next, s, sb);
+        __builtin_amdgcn_sched_barrier(0);
     }
     // online softmax in log2 units: max over the 32 keys of each query row
     float bm = -__builtin_inff();
@@ -424,7 +683,7 @@ __device__ __forceinline__ void process(const Params& p, const Wave<DT, HD>& W, 
             bm = fmaxf(bm, S[r]);
         }
     }
-    bm = fmaxf(bm, __shfl_xor(bm, 32, 64)) * scale2;
+    bm = xhalf_max(bm) * scale2;
     // The running max moves only when a block's max exceeds it by more than
     // kLazyMax (log2 units), so most blocks keep alpha = 1 and skip the
     // rescale of O; the probabilities then stay below 2^kLazyMax.  O and l are
@@ -456,8 +715,10 @@ __device__ __forceinline__ void process(const Params& p, const Wave<DT, HD>& W, 
         for (int kc2 = 0; kc2 < 2; kc2++)
 #pragma unroll
             for (int x = 0; x < 8; x++) pb[kc2][x] = static_cast<__bf16>(S[8 * kc2 + x]);
-        // O^T += V_j^T P^T ; A operand read transposed from LDS
+        // O^T += V_j^T P^T ; A operand read transposed from LDS, every read
+        // first, then the MFMAs
         const int g16 = lane >> 4, s16 = lane & 15;
+        bf16x8 av[2][HD / 32];
 #pragma unroll
         for (int kc2 = 0; kc2 < 2; kc2++) {
 #pragma unroll
@@ -469,10 +730,16 @@ __device__ __forceinline__ void process(const Params& p, const Wave<DT, HD>& W, 
                 const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vs + (row + 8) * VS + col));
                 const short __attribute__((ext_vector_type(8))) a8 = {lo[0], lo[1], lo[2], lo[3],
                                                                       hi[0], hi[1], hi[2], hi[3]};
-                const bf16x8 av = __builtin_bit_cast(bf16x8, a8);
-                A.o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kc2], A.o[mt], 0, 0, 0);
+                av[kc2][mt] = __builtin_bit_cast(bf16x8, a8);
             }
         }
+#pragma unroll
+        for (int kc2 = 0; kc2 < 2; kc2++)
+#pragma unroll
+            for (int mt = 0; mt < HD / 32; mt++)
+                A.o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[kc2][mt], pb[kc2], A.o[mt], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * (HD / 32), 0);   // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * (HD / 32), 0);   // MFMA
     } else {
         constexpr int VS = v_stride_f(HD);
 #pragma unroll
@@ -486,26 +753,80 @@ __device__ __forceinline__ void process(const Params& p, const Wave<DT, HD>& W, 
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (info_pos(info) == info_len(info) - 1)
-        finish_segment<DT, HD, FULL>(p, W, A, we, i, info, reinterpret_cast<float*>(vs));
+    // The end of a piece: a segment that started in this range and ends here
+    // is finished; a piece of a segment that another wave started is parked
+    // for it; a segment that started here and goes on past the range is
+    // kept in A for the join after the workgroup barrier.
+    const bool seg_end = info_pos(info) == info_len(info) - 1;
+    if (seg_end || e == W.end - 1) {
+        const bool started_here = e - info_pos(info) >= W.start;
+        if (seg_end && started_here)
+            finish_segment<DT, HD, FULL>(p, W, A, we, i, info, reinterpret_cast<float*>(vs), sb.pend);
+        else if (!started_here)
+            park_piece<DT, HD, FULL>(W, A);
+        else
+            A.jend = e - info_pos(info) + info_len(info) - 1;
+    }
 }
 
 
-// Range k of the WPH ranges of head bh's record stream, by one wave.
+// The blocks [W.start, W.end) of the wave's record window.
+template <int DT, int HD, bool FULL>
+__device__ __forceinline__ void run_blocks(const Params& p, Wave<DT, HD>& W, StageBuf<DT, HD>& sb, Acc<DT, HD>& A) {
+    const int bh = W.bh;
+    const size_t head_off = (size_t)bh * p.N * HD;
+    using E = typename Cfg<DT, HD>::Elem;
+    W.Qg = static_cast<const E*>(p.q) + head_off;
+    W.Kg = static_cast<const E*>(p.k) + head_off;
+    W.Vg = static_cast<const E*>(p.v) + head_off;
+    const float scale2 = (1.0f / __builtin_sqrtf((float)p.dscale)) * kLog2e;
+    const int start = W.start, end = W.end;
+
+    // One slot: each block stages its data in LDS and then issues the next
+    // block's loads (past the end, the last block again, so that every block
+    // issues the same loads and the wait counts stay exact); they arrive
+    // while the block is computed, and the second wave on the SIMD computes
+    // while this one waits.
+    Slot<DT, HD> sl;
+    issue<DT, HD, FULL>(p, W, start, sl, sb);
+    // the cell's low-res weight, formed as the low-res sums formed it (0 past
+    // the stream's end, where the mask word is 0)
+    if constexpr (FULL) W.ww = lowres_weight(W.ww, W.wm, __popc(W.wk));
+    for (int e = start; e < end; e++) process<DT, HD, FULL>(p, W, e, sl, A, sb, scale2, min(e + 1, end - 1));
+}
+
+// Wave k of the WPH waves of head bh; waves k with the same k / kWaves are
+// one workgroup.  The workgroup takes range k / kWaves of the head's record
+// stream (its ends moved to the nearest segment starts) and splits it into
+// kWaves equal parts, one per wave, wherever those cuts fall.  A segment cut
+// by them is finished by the wave holding its first block, after the
+// workgroup's barrier, from its own piece and the parked pieces of the next
+// waves.  All waves of the workgroup reach that barrier once per call.
 template <int DT, int HD, bool FULL>
 __device__ __forceinline__ void run_range(const Params& p, int bh, int k, int WPH, int lane, int wave,
                                           StageBuf<DT, HD>& sb) {
     // the head's stream: K records (a static layout fills row_ptr[nb] of its
     // capacity K)
     const int64_t K = p.attn_dyn ? min((int64_t)p.row_ptr[(size_t)bh * (p.nb + 1) + p.nb], p.K) : p.K;
-    const int a = (int)((int64_t)k * K / WPH);
-    const int bnd = (int)((int64_t)(k + 1) * K / WPH);
-    // the record window starts half a segment before a: the range's first
-    // block may move back that far
-    const int a0 = max(a - kChunk / 2, 0);
+    const int G = WPH / kWaves, g = k / kWaves;
+    const int an = (int)((int64_t)g * K / G), bn = (int)((int64_t)(g + 1) * K / G);
     const BlkRec* R = p.recs + (size_t)bh * p.K;
+    const uint32_t info_a = an < K ? R[an].info : 0u;
+    const uint32_t info_b = bn < K ? R[bn].info : 0u;
+    // for after the range: the head's listed rows and the first this wave takes
+    const int nm = min(p.n_merge[bh], p.nb);
+    int4 dsc = p.merge_rows[(size_t)bh * p.nb + min(k, p.nb - 1)];
+    // The workgroup's range [S, E): both ends moved to the nearest segment
+    // start (the next workgroup's range starts where this one ends, since
+    // both round the same block index the same way); wave `wave` takes
+    // [S + wave T / kWaves, S + (wave + 1) T / kWaves).
+    const int S = nearest_segment_start(an, info_a, K);
+    const int T = max(nearest_segment_start(bn, info_b, K) - S, 0);
     Wave<DT, HD> W;
-    W.a = a0;
+    W.start = S + wave * T / kWaves;
+    W.end = S + (wave + 1) * T / kWaves;
+    W.a = W.start;
+    W.park = p.park + ((size_t)bh * WPH + k) * park_floats(HD);
     W.bh = bh;
     W.b = bh / p.H;
     W.nb = p.nb;
@@ -515,63 +836,96 @@ __device__ __forceinline__ void run_range(const Params& p, int bh, int k, int WP
     W.h = lane >> 5;
     {
         int4 r = make_int4(0, 0, 0, 0);
-        if (a0 + lane < K) r = *reinterpret_cast<const int4*>(R + a0 + lane);
+        if (W.a + lane < K) r = *reinterpret_cast<const int4*>(R + W.a + lane);
         W.wij = (uint32_t)r.x;
         W.wk = (uint32_t)r.y;
         W.winfo = (uint32_t)r.w;
         W.ww = 0.f;
         W.wm = 0.f;
         W.wll = 0.f;
-        if (FULL && a0 + lane < K) {
-            // the cell's low-res weight, formed as the low-res sums formed it
+        if (FULL && W.a + lane < K) {
+            // the cell's logit (its low-res weight is formed once the first
+            // block's loads are out), the row's max and weight sum
             const size_t row = (size_t)bh * p.nb + min(rec_i(W.wij), p.nb - 1);
-            const float sij = p.logits[row * p.nb + min(rec_j(W.wij), p.nb - 1)];
+            W.ww = p.logits[row * p.nb + min(rec_j(W.wij), p.nb - 1)];
             W.wm = p.rowmax[row];
             W.wll = p.ll_all[row];
-            W.ww = lowres_weight(sij, W.wm, __popc(W.wk));
         }
     }
-    const uint32_t info_b = bnd < K ? R[bnd].info : 0u;
-    // Move both ends of [a, bnd) to the nearest segment start; the next
-    // wave's range starts where this one ends, since both round the same
-    // block index the same way.
-    const int start = nearest_segment_start(a, (uint32_t)rl((int)W.winfo, a - a0), K);
-    const int end = nearest_segment_start(bnd, info_b, K);
-    if (start >= end) return;
-    if (start < a0 || end - a0 > kWindow) {   // the window must hold every block of the range
-        if (lane == 0) atomicOr(reinterpret_cast<unsigned int*>(p.error), 4u);
-        return;
-    }
-
-    const size_t head_off = (size_t)bh * p.N * HD;
-    using E = typename Cfg<DT, HD>::Elem;
-    W.Qg = static_cast<const E*>(p.q) + head_off;
-    W.Kg = static_cast<const E*>(p.k) + head_off;
-    W.Vg = static_cast<const E*>(p.v) + head_off;
-    const float scale2 = (1.0f / __builtin_sqrtf((float)p.dscale)) * kLog2e;
-
-    // Blocks go in batches: the loads of a whole batch are issued, then the
-    // batch is computed.  Past the end the last block is fetched again, so
-    // every batch issues the same loads and the wait counts stay exact; the
-    // second wave on the SIMD computes while this one waits.
-    constexpr int BATCH = Cfg<DT, HD>::kBatch;
     Acc<DT, HD> A;
     A.mrun = -__builtin_inff();
     A.lsum = 0.f;
+    A.npend = 0;
+    A.jend = -1;
 #pragma unroll
     for (int mt = 0; mt < HD / 32; mt++)
 #pragma unroll
         for (int r = 0; r < 16; r++) A.o[mt][r] = 0.f;   // finite, so alpha = 0 clears them
-    for (int e0 = start; e0 < end; e0 += BATCH) {
-        Slot<DT, HD> sl[BATCH];
-#pragma unroll
-        for (int u = 0; u < BATCH; u++) issue<DT, HD, FULL>(p, W, min(e0 + u, end - 1), sl[u], sb, u);
-        // keep the loads together: the scheduler must not sink them into the
-        // compute of the batch
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int u = 0; u < BATCH; u++)
-            if (e0 + u < end) process<DT, HD, FULL>(p, W, e0 + u, sl[u], A, sb, u, scale2);
+    if (W.end - W.start > kWindow) {   // the window must hold every block of the range
+        if (lane == 0) atomicOr(reinterpret_cast<unsigned int*>(p.error), 4u);
+    } else if (W.start < W.end) {
+        run_blocks<DT, HD, FULL>(p, W, sb, A);
+    }
+    // the parked pieces are written; the next waves' pieces of a segment
+    // held in A are read after this barrier
+    __syncthreads();
+    if (A.jend >= 0) {
+        for (int x = wave + 1; x < kWaves; x++) {
+            const int ax = S + x * T / kWaves, bx = S + (x + 1) * T / kWaves;
+            if (ax > A.jend) break;
+            if (ax < bx) merge_piece<DT, HD, FULL>(W.park + (size_t)(x - wave) * park_floats(HD), lane, A);
+        }
+        const int we = W.end - 1 - W.a;
+        const uint32_t info = (uint32_t)rl((int)W.winfo, we);
+        const int i = min(rec_i((uint32_t)rl((int)W.wij, we)), p.nb - 1);
+        finish_segment<DT, HD, FULL>(p, W, A, we, i, info, reinterpret_cast<float*>(sb.v), sb.pend);
+    }
+    const int npend = A.npend;
+    // Then count the cut segments this wave ended, one lane per segment,
+    // once their partials are stored; the wave that completes a row's count
+    // joins the row.  Then the head's rows with no selected block, listed
+    // rows k, k + WPH, ...
+    uint64_t joins = 0;        // lanes whose segment completed its row
+    int jrow = 0, jfirst = 0, jn = 0;
+    if (npend > 0) {
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): every partial store has completed
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        bool last = false;
+        if (lane < npend) {
+            jrow = min(max(sb.pend[lane], 0), p.nb - 1);
+            const uint32_t old = __hip_atomic_fetch_add(p.join_cnt + (size_t)bh * p.nb + jrow, 1u,
+                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int* ip = p.item_ptr + (size_t)bh * (p.nb + 1) + jrow;
+            jfirst = ip[0];
+            jn = ip[1] - jfirst;
+            last = (int)old + 1 == jn;
+        }
+        joins = __builtin_amdgcn_ballot_w64(last);
+    }
+    for (int s = k;;) {
+        int i, first = 0, nseg = 0;
+        const bool cut = joins != 0;
+        if (cut) {
+            const int t = __builtin_ctzll(joins);
+            joins &= joins - 1;
+            i = rl(jrow, t);
+            first = rl(jfirst, t);
+            nseg = rl(jn, t);
+        } else {
+            if (s >= nm) break;
+            if (s != k) dsc = p.merge_rows[(size_t)bh * p.nb + s];
+            s += WPH;
+            if (dsc.z != 0) continue;
+            i = min(max(dsc.x, 0), p.nb - 1);
+        }
+        join_row<DT, HD, FULL>(p, bh, W.b, p.nb, lane, i, first, nseg, reinterpret_cast<float*>(sb.v));
+        // back to zero for the next launch on this workspace (every segment has counted)
+        if (cut && lane == 0)
+            __hip_atomic_store(p.join_cnt + (size_t)bh * p.nb + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -582,7 +936,9 @@ template <int DT, int HD, bool FULL>
 __global__ __launch_bounds__(kThreads, HD == 64 ? 2 : 1) void attn_kernel(Params p) {
     StageBuf<DT, HD>* stage = reinterpret_cast<StageBuf<DT, HD>*>(attn_smem);   // one per wave
     const int xcd = blockIdx.x & 7;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // the wave index is uniform: made so for the compiler, so that ranges,
+    // loop bounds and addresses derived from it stay in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int wx = (blockIdx.x >> 3) * kWaves + wave;      // wave index within its XCD
     const int WPH = p.attn_wph;
     if (p.attn_seq) {
@@ -593,7 +949,8 @@ __global__ __launch_bounds__(kThreads, HD == 64 ? 2 : 1) void attn_kernel(Params
     } else {
         const int hm = wx / WPH;
         const int bh = xcd + 8 * hm;
-        if (bh < p.BH) run_range<DT, HD, FULL>(p, bh, wx - hm * WPH, WPH, lane, wave, stage[wave]);
+        if (bh < p.BH)
+            run_range<DT, HD, FULL>(p, bh, wx - hm * WPH, WPH, lane, wave, stage[wave]);
     }
 }
 
@@ -611,10 +968,14 @@ bool attn_heads_in_turn(int BH, int64_t K) {
 int attn_grid_waves_per_head(int BH, int64_t K) {
     const int heads_per_xcd = (BH + 7) / 8;
     int64_t w = attn_heads_in_turn(BH, K) ? kWavesPerXcd : kWavesPerXcd / heads_per_xcd;
-    if (w < 1) w = 1;
     const int64_t hi = (K + 1) / 2;                   // at least about two blocks a wave
     if (w > hi) w = hi;
-    const int64_t lo = (K + kMaxRun - 1) / kMaxRun;    // keep each range inside one record window
+    // whole workgroups, rounded down so that the grid stays within one
+    // round of resident workgroups
+    w = w / kWaves * kWaves;
+    if (w < kWaves) w = kWaves;
+    // keep each range inside one record window
+    const int64_t lo = ((K + kMaxRun - 1) / kMaxRun + kWaves - 1) / kWaves * kWaves;
     if (w < lo) w = lo;
     return (int)w;
 }

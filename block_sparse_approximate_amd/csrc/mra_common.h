@@ -20,6 +20,9 @@ constexpr int kChunk = 16;              // max selected key blocks per segment o
 constexpr int kMaxHeadDim = 128;        // widest head the forward kernels take
 // floats per segment's low-res correction: hd channels, weight sum, pad
 __host__ __device__ constexpr int corr_stride(int hd) { return hd + 4; }
+// floats per parked piece of a segment (attention): O^T, per lane the
+// running max and sum, the low-res correction and weight sum
+__host__ __device__ constexpr int park_floats(int hd) { return 32 * hd + 128 + hd + 64; }
 constexpr int kSelCap = 4096;           // selection candidates one head's boundary bin may hold
 constexpr int kCandStride = 32;         // u32 per head's candidate counter: one 128-byte line each
 constexpr float kLog2e = 1.4426950408889634f;
@@ -53,7 +56,8 @@ struct Layout {
     int64_t K;            // selection budget per (batch, head)
     int32_t max_items;    // segments per head, upper bound
     size_t qhat, khat, vhat, cnt, mbits, logits, keys, rowmax, hist, thresh, row_ptr, col, selbits, item_ptr, recs,
-        merge_rows, n_merge, lo_all, ll_all, part_o, part_ml, part_corr, cand, ncand, st_m, st_linv, total;
+        merge_rows, n_merge, join_cnt, lo_all, ll_all, part_o, part_ml, part_corr, park, cand, ncand, st_m, st_linv,
+        total;
 };
 
 // Everything a kernel needs, passed by value.
@@ -92,11 +96,15 @@ struct Params {
     int4* merge_rows;      // [BH, nb] rows the final kernel must combine (0 or >1 segments):
                            //   (row, first segment, number of segments, 0)
     int32_t* n_merge;      // [BH]
+    uint32_t* join_cnt;    // [BH, nb] segments of a cut row that have stored their partials (the
+                           //   selector clears it; the last segment joins the row and clears it again)
     float* lo_all;         // [BH, nb, d] full mode: sum over every key block j of w_ij vhat_j
     float* ll_all;         // [BH, nb]    full mode: sum over every key block j of w_ij
     float* part_o;         // [BH, max_items, 32, d] un-normalised high-res numerators
     float* part_ml;        // [BH, max_items, 2, 32] running max (log2 units) and sum
     float* part_corr;      // [BH, max_items, corr_stride(d)] full mode: the segment's sum of w vhat_j, then of w
+    float* park;           // [BH, attn_wph, park_floats(d)] attention: per wave, a piece of a segment
+                           //   that another wave of its workgroup finishes
     uint64_t* cand;        // [BH, kSelCap] boundary-bin cells found by the pre-marking pass
     uint32_t* ncand;       // [BH, kCandStride] their number, in word 0 (cleared by the pooling kernel)
     // backward (mra_attention_bwd)
@@ -196,7 +204,6 @@ hipError_t launch_logits_given(const Params& p, hipStream_t s);
 hipError_t launch_premark(const Params& p, hipStream_t s);
 hipError_t launch_select(const Params& p, hipStream_t s);
 hipError_t launch_attn(const Params& p, hipStream_t s);
-hipError_t launch_finish(const Params& p, hipStream_t s);
 hipError_t launch_bigbird_layout(const Params& p, hipStream_t s);
 int bwd_max_chunks(int nb, int64_t K);
 hipError_t launch_bwd(const Params& p, hipStream_t s);

@@ -851,6 +851,7 @@ __device__ __forceinline__ void emit_stream(const Params& p, int bh, const uint3
             item_ptr[i] = ei;
             rc[i] = ec;
             ic[i] = ei;
+            p.join_cnt[(size_t)bh * nb + i] = 0u;
             if (mf) p.merge_rows[(size_t)bh * nb + em] = make_int4(i, ei, it, 0);
         }
         if (tid == 0) {
@@ -1257,6 +1258,7 @@ __device__ __forceinline__ void select_rows(const Params& p, int bh, int t, unsi
                 if ((uint32_t)(i - row0) < (uint32_t)kTileRows) {
                     row_ptr[i] = ec;
                     item_ptr[i] = ei;
+                    p.join_cnt[(size_t)bh * nb + i] = 0u;
                     if (mfc[q]) p.merge_rows[(size_t)bh * nb + em] = make_int4(i, ei, itc[q], 0);
                 }
             }

@@ -68,8 +68,8 @@ typedef enum {
     MRA_ERR_WORKSPACE = 10, /* a workspace NULL or smaller than its size query returns */
     MRA_ERR_HIP = 11,       /* a HIP call failed */
     MRA_ERR_ALIGN = 12,     /* a tensor pointer is not 16-byte aligned */
-    MRA_ERR_STAGE = 13,     /* mra_debug_replay: a stage other than 3 or 4, or count < 1 */
-    MRA_ERR_SCRATCH = 14    /* mra_attention_fwd_noalloc: the sizes need more than its 48 MiB scratch */
+    MRA_ERR_STAGE = 13,     /* mra_debug_replay: a stage other than 3, or count < 1 */
+    MRA_ERR_SCRATCH = 14    /* mra_attention_fwd_noalloc: the sizes need more than its 64 MiB scratch */
 } mra_status;
 
 /* Bits of a workspace's device error word (mra_workspace_error).  The
@@ -185,10 +185,10 @@ mra_status mra_attention_fwd(const mra_dims* dims, const void* q, const void* k,
 /* mra_attention_fwd for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): the same kernels, with no workspace argument.  The workspace
- * is a fixed 48 MiB device array inside the library, one copy per GPU, held
+ * is a fixed 64 MiB device array inside the library, one copy per GPU, held
  * until the process ends; the call allocates nothing.  Sizes whose
- * mra_workspace_size exceeds 48 MiB return MRA_ERR_SCRATCH (B=2, H=12,
- * N=4096 full mode needs 40.2 MiB).  Every call on one GPU shares that GPU's
+ * mra_workspace_size exceeds 64 MiB return MRA_ERR_SCRATCH (B=2, H=12,
+ * N=4096 full mode needs 58.8 MiB).  Every call on one GPU shares that GPU's
  * array, so calls that overlap in time on one GPU (other streams, other
  * threads) race and must be serialised by the caller; each call clears what
  * it needs cleared.  Its device error word is not exposed.  Other arguments
@@ -210,11 +210,11 @@ mra_status mra_attention_fwd_ex(const mra_dims* dims, const void* q, const void*
 
 /* Profiling variant of mra_attention_fwd: the same work, plus a
  * hipEventRecord on `stream` before and after each kernel launch.
- *   events  array of 10 hipEvent_t created by the caller (with timing);
- *           entries 2s and 2s+1 bracket kernel s: 0 pooling, 1 low-res
- *           logits, 2 top-k selection, 3 block attention, 4 low-res
- *           attention and merge.  NULL entries are skipped.  The events stay
- *           owned by the caller. */
+ *   events  array of 8 hipEvent_t created by the caller (with timing);
+ *           entries 2s and 2s+1 bracket stage s: 0 pooling, 1 low-res
+ *           logits, 2 top-k selection, 3 block attention with the low-res
+ *           merge and the join of rows cut into several segments.  NULL
+ *           entries are skipped.  The events stay owned by the caller. */
 mra_status mra_attention_fwd_profiled(const mra_dims* dims, const void* q, const void* k, const void* v,
                                       const uint8_t* mask, int32_t block_per_row, int32_t approx_mode,
                                       int32_t prior_first, int32_t prior_diag, void* out, void* workspace,
@@ -341,10 +341,11 @@ mra_status mra_workspace_error(const void* workspace, size_t workspace_bytes, vo
 
 /* Timing hook: relaunches one stage of the forward pass `count` times in a
  * row on `stream`, on a workspace that a call of mra_attention_fwd with the
- * same arguments has filled (stream order: after that call).  Only the two
- * stages that read nothing they write are accepted: 3 (block attention) and
- * 4 (join of cut rows with the low-res part); each relaunch rewrites the same
- * output.  A pair of events around the call then times the kernel alone,
+ * same arguments has filled (stream order: after that call).  Only stage 3
+ * (block attention, low-res merge and join) is accepted: it leaves the
+ * workspace as it found it (its per-row join counters end at zero) and each
+ * relaunch rewrites the same output.  A pair of events around the call then
+ * times the kernel alone,
  * with no event between its launches.  The arguments are checked as for
  * mra_attention_fwd; MRA_ERR_STAGE for another stage or count < 1. */
 mra_status mra_debug_replay(const mra_dims* dims, const void* q, const void* k, const void* v,

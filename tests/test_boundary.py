@@ -97,7 +97,7 @@ def call(dims=(1, 2, 512, 64, 1), q=Q, k=K, v=V, mask=None, bpr=4, mode=0, pf=0,
     (dict(ws=None), 10), (dict(ws_bytes=1024), 10),
     (dict(q=Q + 8), 12), (dict(mask=0x60000004), 12), (dict(ws=W + 16), 12),
     # the workspace is written while the inputs are read: it may overlap none of them
-    (dict(ws=Q - 256), 9), (dict(ws=V + 4096, ws_bytes=1 << 20), 9), (dict(mask=W + 4096), 9),
+    (dict(ws=Q - 256), 9), (dict(ws=V + 4096, ws_bytes=4 << 20), 9), (dict(mask=W + 4096), 9),
 ])
 def test_attention_fwd_rejects_bad_arguments(kw, status):
     assert call(**kw) == status
@@ -146,7 +146,7 @@ def test_debug_replay_rejects_bad_arguments():
     d = mra._Dims(1, 2, 512, 64, 1)
     args = lambda stage, count, ws_bytes=1 << 40: (ctypes.byref(d), Q, K, V, None, 4, 0, 0, 0, O, W, ws_bytes,
                                                    stage, count, None)
-    for stage in (0, 1, 2, 5, -1):
+    for stage in (0, 1, 2, 4, 5, -1):
         assert L.mra_debug_replay(*args(stage, 1)) == 13
     assert L.mra_debug_replay(*args(3, 0)) == 13
     assert L.mra_debug_replay(*args(3, 1, 16)) == 10

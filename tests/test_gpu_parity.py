@@ -212,8 +212,8 @@ EDGE = [
     ("heads-in-turn-bh9", dict(B=1, H=9, N=12288, block_per_row=8)),
     ("priors-over-budget", dict(B=1, H=2, N=2048, block_per_row=1, prior_first=3, prior_diag=5,
                                 approx_mode="sparse")),
-    # many heads: the join kernel takes 4 workgroups per head (2 where a head has 2 block rows), each
-    # joining several rows; half the sequences are padded, so many rows have no selected block
+    # many heads, each with few waves that write several rows with no selected block; half the
+    # sequences are padded, so many rows have none
     ("many-heads-bh512-masked", dict(B=32, H=16, N=256, block_per_row=2, prior_first=1,
                                      mask=np.repeat(np.arange(256)[None, :] < np.array([[256], [96]]), 16,
                                                     axis=0).astype(np.uint8))),
@@ -248,6 +248,33 @@ def test_fp32_all_selected_equals_dense(mra):
     got = run_gpu(mra, w)
     ref = oracle.dense_forward(w.q, w.k, w.v)
     assert np.abs(got - ref).max() <= 1e-4
+
+
+@pytest.mark.parametrize("name", ["long-rows-full", "long-rows-sparse", "long-rows-fp32", "heads-in-turn-bh9",
+                                  "many-heads-bh512-masked"])
+def test_attention_relaunch_rewrites_the_same_output(mra, name):
+    # The attention kernel joins cut rows through per-row counters in the
+    # workspace that it sets back to zero: relaunching it on the workspace of
+    # a call must give the call's output bit for bit, every time.
+    w = small(name, **dict(EDGE)[name])
+    print("case", name, w, flush=True)
+    q, k, v, mask = dev(w, "q"), dev(w, "k"), dev(w, "v"), dev_mask(w)
+    kw = dict(block_per_row=w.block_per_row, approx_mode=w.approx_mode,
+              initial_prior_first_n_blocks=w.prior_first, initial_prior_diagonal_n_blocks=w.prior_diag)
+    B, H, N, d = q.shape
+    ws = torch.empty(mra.workspace_size(B, H, N, d, q.dtype, w.block_per_row, w.approx_mode),
+                     dtype=torch.uint8, device=q.device)
+    out = mra.attention(q, k, v, mask, out=torch.empty_like(q), workspace=ws, **kw)
+    first = out.clone()
+    torch.cuda.synchronize()
+    assert_close(w, first.float().cpu().numpy().astype(np.float64), run_oracle(w)[0])
+    for _ in range(3):
+        out.zero_()
+        mra.debug_replay(q, k, v, 3, 4, mask, out=out, workspace=ws, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16 if w.dtype == "bf16" else torch.int32),
+                           first.view(torch.int16 if w.dtype == "bf16" else torch.int32))
+    assert mra.workspace_error(ws) == 0
 
 
 def test_run_to_run_bitwise_determinism(mra):

@@ -54,7 +54,7 @@ def test_noalloc_matches_workspace_forward_twice(mra, mode):
 
 
 def test_noalloc_rejects_sizes_beyond_its_scratch(mra):
-    # N = 16384 with 16 heads needs 147 MiB of workspace: refused on the host
+    # N = 16384 with 16 heads needs 183 MiB of workspace: refused on the host
     d = mra._Dims(1, 16, 16384, 64, 1)
     x = torch.empty(16, dtype=torch.bfloat16, device="cuda")
     st = mra.lib().mra_attention_fwd_noalloc(ctypes.byref(d), x.data_ptr(), x.data_ptr(), x.data_ptr(), None, 8,
