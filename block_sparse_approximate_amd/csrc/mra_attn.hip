@@ -421,8 +421,8 @@ __device__ __forceinline__ void join_row(const Params& p, int bh, int b, int nb,
             const float* a = acc + 4 * (mt * 4 + gq);
             if constexpr (DT == 1) {
                 uint2 pk;
-                pk.x = (uint32_t)float_to_bf16(a[0] * inv) | ((uint32_t)float_to_bf16(a[1] * inv) << 16);
-                pk.y = (uint32_t)float_to_bf16(a[2] * inv) | ((uint32_t)float_to_bf16(a[3] * inv) << 16);
+                pk.x = pack_bf16x2(a[0] * inv, a[1] * inv);
+                pk.y = pack_bf16x2(a[2] * inv, a[3] * inv);
                 *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + orow + d0) = pk;
             } else {
                 *reinterpret_cast<float4*>(static_cast<float*>(p.out) + orow + d0) =
@@ -443,9 +443,6 @@ __device__ __forceinline__ void finish_segment(const Params& p, const Wave<DT, H
         float a = 1.f, bw = 0.f, den = ltot;
         float Mu = A.mrun;   // the max that den and the probabilities are relative to
         if constexpr (FULL) {
-            // low-res part of the row without the selected blocks, one channel per lane
-#pragma unroll
-            for (int x = 0; x < HD / 64; x++) lo_lds[W.lane + 64 * x] = A.lo[x] - A.corr[x];
             const float mi2 = __int_as_float(rl(__float_as_int(W.wm), we)) * kLog2e;
             const float ll = fmaxf(__int_as_float(rl(__float_as_int(W.wll), we)) - A.sw, 0.f);
             const float M = fmaxf(A.mrun, mi2);
@@ -453,9 +450,6 @@ __device__ __forceinline__ void finish_segment(const Params& p, const Wave<DT, H
             bw = M == -__builtin_inff() ? 0.f : fast_exp2(mi2 - M);
             den = ltot * a + ll * bw;
             Mu = M;
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
         const float inv = (valid && den > 0.f) ? 1.0f / den : 0.f;
         const float sa = a * inv, sb = bw * inv;
@@ -465,27 +459,61 @@ __device__ __forceinline__ void finish_segment(const Params& p, const Wave<DT, H
             p.st_linv[st] = inv;
         }
         const size_t orow = ((size_t)W.bh * p.N + tok) * HD;
+        if constexpr (DT == 1) {
 #pragma unroll
-        for (int mt = 0; mt < HD / 32; mt++) {
+            for (int mt = 0; mt < HD / 32; mt++) {
+                f32x16 o = A.o[mt];
 #pragma unroll
-            for (int gq = 0; gq < 4; gq++) {
-                const int d0 = 32 * mt + 8 * gq + 4 * h;
-                const f32x16& oo = A.o[mt];
-                float v0 = oo[4 * gq] * sa, v1 = oo[4 * gq + 1] * sa;
-                float v2 = oo[4 * gq + 2] * sa, v3 = oo[4 * gq + 3] * sa;
+                for (int r = 0; r < 16; r++) o[r] *= sa;
                 if constexpr (FULL) {
-                    const float4 lo = *reinterpret_cast<const float4*>(lo_lds + d0);
-                    v0 = __builtin_fmaf(lo.x, sb, v0);
-                    v1 = __builtin_fmaf(lo.y, sb, v1);
-                    v2 = __builtin_fmaf(lo.z, sb, v2);
-                    v3 = __builtin_fmaf(lo.w, sb, v3);
+                    // The row's low-res part lo = lo_all - sum_sel w vhat_j
+                    // (lane l holds channel l + 64 x) enters as the rank-1
+                    // update lo sb^T on the matrix core: A is the tile's 32
+                    // channels in lanes 0..31 (k = 0; lanes 32..63, k = 1,
+                    // give 0), B is sb of the 32 tokens likewise, C the
+                    // scaled O^T tile.
+                    float lc = A.lo[mt / 2] - A.corr[mt / 2];
+                    if (mt & 1) {   // channels 32 .. 63 of the pair: from the upper half
+                        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(lc), __float_as_uint(lc),
+                                                                        false, false);
+                        lc = __uint_as_float(r[1]);
+                    }
+                    o = __builtin_amdgcn_mfma_f32_32x32x2f32(W.lane < 32 ? lc : 0.f, W.lane < 32 ? sb : 0.f, o, 0, 0,
+                                                             0);
                 }
-                if constexpr (DT == 1) {
+#pragma unroll
+                for (int gq = 0; gq < 4; gq++) {
                     uint2 pk;
-                    pk.x = (uint32_t)float_to_bf16(v0) | ((uint32_t)float_to_bf16(v1) << 16);
-                    pk.y = (uint32_t)float_to_bf16(v2) | ((uint32_t)float_to_bf16(v3) << 16);
-                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + orow + d0) = pk;
-                } else {
+                    pk.x = pack_bf16x2(o[4 * gq], o[4 * gq + 1]);
+                    pk.y = pack_bf16x2(o[4 * gq + 2], o[4 * gq + 3]);
+                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + orow + 32 * mt + 8 * gq + 4 * h) = pk;
+                }
+            }
+        } else {
+            // fp32 (registers are scarcer here): lo goes through LDS, one
+            // channel per lane in, four channels per lane out
+            if constexpr (FULL) {
+#pragma unroll
+                for (int x = 0; x < HD / 64; x++) lo_lds[W.lane + 64 * x] = A.lo[x] - A.corr[x];
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            }
+#pragma unroll
+            for (int mt = 0; mt < HD / 32; mt++) {
+#pragma unroll
+                for (int gq = 0; gq < 4; gq++) {
+                    const int d0 = 32 * mt + 8 * gq + 4 * h;
+                    const f32x16& oo = A.o[mt];
+                    float v0 = oo[4 * gq] * sa, v1 = oo[4 * gq + 1] * sa;
+                    float v2 = oo[4 * gq + 2] * sa, v3 = oo[4 * gq + 3] * sa;
+                    if constexpr (FULL) {
+                        const float4 lo = *reinterpret_cast<const float4*>(lo_lds + d0);
+                        v0 = __builtin_fmaf(lo.x, sb, v0);
+                        v1 = __builtin_fmaf(lo.y, sb, v1);
+                        v2 = __builtin_fmaf(lo.z, sb, v2);
+                        v3 = __builtin_fmaf(lo.w, sb, v3);
+                    }
                     *reinterpret_cast<float4*>(static_cast<float*>(p.out) + orow + d0) = make_float4(v0, v1, v2, v3);
                 }
             }
@@ -795,16 +823,33 @@ __device__ __forceinline__ void run_blocks(const Params& p, Wave<DT, HD>& W, Sta
     for (int e = start; e < end; e++) process<DT, HD, FULL>(p, W, e, sl, A, sb, scale2, min(e + 1, end - 1));
 }
 
+// Relative costs of the work in a wave's part, in eighths of a block: every
+// block, and on top each segment end (the output or partial it writes) and
+// each segment start (Q staged, accumulators reset).  Measured on MI355X: a
+// segment end costs about three quarters of a block, a start about 0.4.
+constexpr int kCostBlock = 8, kCostEnd = 6, kCostStart = 3;
+
+// The cost of the stream before block e (whose record info is given), in
+// eighths of a block: the segments before e's segment have all started and
+// ended, and e's own segment has started unless e is its first block.
+__device__ __forceinline__ int64_t cost_before(int64_t e, int item, int pos) {
+    return kCostBlock * e + (int64_t)(kCostEnd + kCostStart) * item + (pos > 0 ? kCostStart : 0);
+}
+
 // Wave k of the WPH waves of head bh; waves k with the same k / kWaves are
 // one workgroup.  The workgroup takes range k / kWaves of the head's record
 // stream (its ends moved to the nearest segment starts) and splits it into
-// kWaves equal parts, one per wave, wherever those cuts fall.  A segment cut
-// by them is finished by the wave holding its first block, after the
-// workgroup's barrier, from its own piece and the parked pieces of the next
-// waves.  All waves of the workgroup reach that barrier once per call.
+// kWaves parts of equal cost, one per wave, wherever those cuts fall: each
+// cut is the first block at which the cost before it reaches its share,
+// searched within m blocks of the equal-block cut (so that every wave finds
+// the same cuts in its own record window).  A segment cut by them is
+// finished by the wave holding its first block, after the workgroup's
+// barrier, from its own piece and the parked pieces of the next waves.  All
+// waves of the workgroup reach that barrier once per call; wg_cut (LDS)
+// passes the cuts to the joiners.
 template <int DT, int HD, bool FULL>
 __device__ __forceinline__ void run_range(const Params& p, int bh, int k, int WPH, int lane, int wave,
-                                          StageBuf<DT, HD>& sb) {
+                                          StageBuf<DT, HD>& sb, int* wg_cut) {
     // the head's stream: K records (a static layout fills row_ptr[nb] of its
     // capacity K)
     const int64_t K = p.attn_dyn ? min((int64_t)p.row_ptr[(size_t)bh * (p.nb + 1) + p.nb], p.K) : p.K;
@@ -813,19 +858,29 @@ __device__ __forceinline__ void run_range(const Params& p, int bh, int k, int WP
     const BlkRec* R = p.recs + (size_t)bh * p.K;
     const uint32_t info_a = an < K ? R[an].info : 0u;
     const uint32_t info_b = bn < K ? R[bn].info : 0u;
+    const uint32_t info_z = K > 0 ? R[K - 1].info : 0u;   // the stream's last block
     // for after the range: the head's listed rows and the first this wave takes
     const int nm = min(p.n_merge[bh], p.nb);
     int4 dsc = p.merge_rows[(size_t)bh * p.nb + min(k, p.nb - 1)];
     // The workgroup's range [S, E): both ends moved to the nearest segment
     // start (the next workgroup's range starts where this one ends, since
-    // both round the same block index the same way); wave `wave` takes
-    // [S + wave T / kWaves, S + (wave + 1) T / kWaves).
+    // both round the same block index the same way).
     const int S = nearest_segment_start(an, info_a, K);
-    const int T = max(nearest_segment_start(bn, info_b, K) - S, 0);
+    const int E = max(nearest_segment_start(bn, info_b, K), S);
+    const int T = E - S;
+    // the segment index (item) of a segment start x reached from block y
+    auto item_at = [&](int x, int y, uint32_t info_y) {
+        if (x >= K) return info_item(info_z) + 1;
+        return info_item(info_y) + (x == y - info_pos(info_y) ? 0 : 1);
+    };
+    const int64_t c0 = cost_before(S, item_at(S, an, info_a), 0);
+    const int64_t c4 = cost_before(E, item_at(E, bn, info_b), 0);
+    // equal-block cuts c_w and the search margin m around them
+    const int q = T / kWaves, qc = (T + kWaves - 1) / kWaves;
+    const int m = max(0, min(16, min((q - 1) / 2, (kWindow - 1 - qc) / 2)));
+    const int cw = S + wave * T / kWaves, cn = S + (wave + 1) * T / kWaves;
     Wave<DT, HD> W;
-    W.start = S + wave * T / kWaves;
-    W.end = S + (wave + 1) * T / kWaves;
-    W.a = W.start;
+    W.a = wave == 0 ? S : cw - m;   // the window: [cw - m, cn + m] is inside it
     W.park = p.park + ((size_t)bh * WPH + k) * park_floats(HD);
     W.bh = bh;
     W.b = bh / p.H;
@@ -852,6 +907,23 @@ __device__ __forceinline__ void run_range(const Params& p, int bh, int k, int WP
             W.wll = p.ll_all[row];
         }
     }
+    {
+        // The cuts of this wave's part: the first block in [c - m, c + m]
+        // whose cost before it reaches the cut's share (else c + m).
+        const int64_t e = W.a + lane;
+        const int64_t pc = cost_before(e, info_item(W.winfo), info_pos(W.winfo));
+        auto cut = [&](int w, int c) {
+            if (w == 0) return S;
+            if (w == kWaves) return E;
+            const int64_t target = c0 + (c4 - c0) * w / kWaves;
+            const uint64_t hit = __builtin_amdgcn_ballot_w64(e >= c - m && e <= c + m && e < K && pc >= target);
+            return hit ? W.a + (int)__builtin_ctzll(hit) : c + m;
+        };
+        W.start = cut(wave, cw);
+        W.end = cut(wave + 1, cn);
+        if (lane == 0) wg_cut[wave] = W.start;
+        if (lane == 0 && wave == kWaves - 1) wg_cut[kWaves] = W.end;
+    }
     Acc<DT, HD> A;
     A.mrun = -__builtin_inff();
     A.lsum = 0.f;
@@ -861,7 +933,7 @@ __device__ __forceinline__ void run_range(const Params& p, int bh, int k, int WP
     for (int mt = 0; mt < HD / 32; mt++)
 #pragma unroll
         for (int r = 0; r < 16; r++) A.o[mt][r] = 0.f;   // finite, so alpha = 0 clears them
-    if (W.end - W.start > kWindow) {   // the window must hold every block of the range
+    if (W.start < W.a || W.end - W.a > kWindow) {   // the window must hold every block of the part
         if (lane == 0) atomicOr(reinterpret_cast<unsigned int*>(p.error), 4u);
     } else if (W.start < W.end) {
         run_blocks<DT, HD, FULL>(p, W, sb, A);
@@ -871,7 +943,7 @@ __device__ __forceinline__ void run_range(const Params& p, int bh, int k, int WP
     __syncthreads();
     if (A.jend >= 0) {
         for (int x = wave + 1; x < kWaves; x++) {
-            const int ax = S + x * T / kWaves, bx = S + (x + 1) * T / kWaves;
+            const int ax = wg_cut[x], bx = wg_cut[x + 1];
             if (ax > A.jend) break;
             if (ax < bx) merge_piece<DT, HD, FULL>(W.park + (size_t)(x - wave) * park_floats(HD), lane, A);
         }
@@ -935,6 +1007,10 @@ __device__ __forceinline__ void run_range(const Params& p, int bh, int k, int WP
 template <int DT, int HD, bool FULL>
 __global__ __launch_bounds__(kThreads, HD == 64 ? 2 : 1) void attn_kernel(Params p) {
     StageBuf<DT, HD>* stage = reinterpret_cast<StageBuf<DT, HD>*>(attn_smem);   // one per wave
+    // the cuts of the workgroup's range between its waves; two sets, so that
+    // a wave that starts the next head in turn does not overwrite the cuts a
+    // slower wave may still be reading for the previous one
+    __shared__ int wg_cut[2][kWaves + 1];
     const int xcd = blockIdx.x & 7;
     // the wave index is uniform: made so for the compiler, so that ranges,
     // loop bounds and addresses derived from it stay in scalar registers
@@ -945,12 +1021,13 @@ __global__ __launch_bounds__(kThreads, HD == 64 ? 2 : 1) void attn_kernel(Params
         // every wave of the XCD takes range wx of each of the XCD's heads in
         // turn, so the XCD's L2 holds one head's K and V at a time
         if (wx >= WPH) return;
-        for (int bh = xcd; bh < p.BH; bh += 8) run_range<DT, HD, FULL>(p, bh, wx, WPH, lane, wave, stage[wave]);
+        for (int bh = xcd; bh < p.BH; bh += 8)
+            run_range<DT, HD, FULL>(p, bh, wx, WPH, lane, wave, stage[wave], wg_cut[(bh >> 3) & 1]);
     } else {
         const int hm = wx / WPH;
         const int bh = xcd + 8 * hm;
         if (bh < p.BH)
-            run_range<DT, HD, FULL>(p, bh, wx - hm * WPH, WPH, lane, wave, stage[wave]);
+            run_range<DT, HD, FULL>(p, bh, wx - hm * WPH, WPH, lane, wave, stage[wave], wg_cut[0]);
     }
 }
 

@@ -174,8 +174,8 @@ __device__ __forceinline__ void store_rows(uint16_t* g, const f32x16 (&a)[HD / 3
                 x[0] += ad.x * aw; x[1] += ad.y * aw; x[2] += ad.z * aw; x[3] += ad.w * aw;
             }
             uint2 pk;
-            pk.x = (uint32_t)float_to_bf16(x[0]) | ((uint32_t)float_to_bf16(x[1]) << 16);
-            pk.y = (uint32_t)float_to_bf16(x[2]) | ((uint32_t)float_to_bf16(x[3]) << 16);
+            pk.x = pack_bf16x2(x[0], x[1]);
+            pk.y = pack_bf16x2(x[2], x[3]);
             *reinterpret_cast<uint2*>(g + n * HD + d0) = pk;
         }
 }
@@ -1046,10 +1046,10 @@ __device__ __forceinline__ void reduce_one(const float* part, int first, int nch
         for (int x = 0; x < kCh / 8; x++) {
             const float* v = acc + 8 * x;
             uint4 pk;
-            pk.x = (uint32_t)float_to_bf16(v[0]) | ((uint32_t)float_to_bf16(v[1]) << 16);
-            pk.y = (uint32_t)float_to_bf16(v[2]) | ((uint32_t)float_to_bf16(v[3]) << 16);
-            pk.z = (uint32_t)float_to_bf16(v[4]) | ((uint32_t)float_to_bf16(v[5]) << 16);
-            pk.w = (uint32_t)float_to_bf16(v[6]) | ((uint32_t)float_to_bf16(v[7]) << 16);
+            pk.x = pack_bf16x2(v[0], v[1]);
+            pk.y = pack_bf16x2(v[2], v[3]);
+            pk.z = pack_bf16x2(v[4], v[5]);
+            pk.w = pack_bf16x2(v[6], v[7]);
             reinterpret_cast<uint4*>(static_cast<uint16_t*>(dst_v) + tok * HD + cg)[x] = pk;
         }
     } else {

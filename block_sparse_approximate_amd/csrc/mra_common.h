@@ -187,11 +187,12 @@ __device__ __forceinline__ float lowres_weight(float s, float m, int cnt) {
     return cnt > 0 ? (float)cnt * __builtin_amdgcn_exp2f((s - m) * kLog2e) : 0.0f;
 }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs).
-__device__ __forceinline__ uint16_t float_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+// Two fp32 values -> two bf16 (round to nearest even, the hardware
+// conversion), low half first.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    const bf16x2_t v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 }  // namespace mra
