@@ -431,6 +431,124 @@ __device__ __forceinline__ void join_row(const Params& p, int bh, int b, int nb,
         }
 }
 
+// Tokens 8 part .. 8 part + 7 of block row i, cut into nseg segments (items
+// first .. first + nseg - 1), joined from the segments' partials as
+// join_row does, by one wave of the workgroup that joins the row (the
+// workgroup's four waves take a quarter of the tokens each).  Lane l takes
+// token 8 part + l / 8 and the HD / 8 channels from (l % 8) HD / 8, so a
+// lane holds only HD / 8 values of a segment and kSeg segments' loads are in
+// flight together.
+template <int DT, int HD, bool FULL>
+__device__ __forceinline__ void join_part(const Params& p, int bh, int b, int nb, int lane, int part, int i, int first,
+                                          int nseg) {
+    constexpr int kCh = HD / 8, kF4 = kCh / 4;
+    constexpr int kSeg = (HD == 64 ? 8 : 4) / (DT == 1 ? 1 : 2);   // fp32: the registers are scarcer
+    const int t = part * 8 + (lane >> 3), c0 = (lane & 7) * kCh;
+    const size_t pbase = (size_t)bh * p.max_items;
+    const size_t row = (size_t)bh * nb + i;
+    const uint32_t qm = p.mbits[(size_t)b * nb + i];
+    float lo_in[kCh], ll_in = 0.f, mrow = 0.f;
+    if constexpr (FULL) {
+#pragma unroll
+        for (int x = 0; x < kF4; x++) {
+            const float4 v = *reinterpret_cast<const float4*>(p.lo_all + row * HD + c0 + 4 * x);
+            lo_in[4 * x] = v.x; lo_in[4 * x + 1] = v.y; lo_in[4 * x + 2] = v.z; lo_in[4 * x + 3] = v.w;
+        }
+        ll_in = p.ll_all[row];
+        mrow = p.rowmax[row];
+    }
+    float M = -__builtin_inff(), den = 0.f, sw = 0.f, acc[kCh], corr[kCh];
+#pragma unroll
+    for (int e = 0; e < kCh; e++) acc[e] = corr[e] = 0.f;
+    for (int c0s = 0; c0s < nseg; c0s += kSeg) {
+        float mc[kSeg], lc[kSeg];
+        float4 oc[kSeg][kF4];
+#pragma unroll
+        for (int c = 0; c < kSeg; c++) {
+            const bool ok = c0s + c < nseg;
+            const size_t pidx = pbase + (size_t)min(first + (ok ? c0s + c : 0), p.max_items - 1);
+            mc[c] = ok ? load_coherent(p.part_ml + pidx * 64 + t) : -__builtin_inff();
+            lc[c] = ok ? load_coherent(p.part_ml + pidx * 64 + 32 + t) : 0.f;
+#pragma unroll
+            for (int x = 0; x < kF4; x++)
+                oc[c][x] = ok ? load4_coherent(p.part_o + (pidx * kBlock + t) * HD + c0 + 4 * x)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+            if constexpr (FULL) {
+                if (ok) {
+                    const float* pc = p.part_corr + pidx * corr_stride(HD);
+#pragma unroll
+                    for (int x = 0; x < kF4; x++) {
+                        const float4 v = load4_coherent(pc + c0 + 4 * x);
+                        corr[4 * x] += v.x; corr[4 * x + 1] += v.y; corr[4 * x + 2] += v.z; corr[4 * x + 3] += v.w;
+                    }
+                    sw += load_coherent(pc + HD);
+                }
+            }
+        }
+        float Mb = M;
+#pragma unroll
+        for (int c = 0; c < kSeg; c++) Mb = fmaxf(Mb, mc[c]);
+        if (Mb != -__builtin_inff()) {
+            const float sM = M == -__builtin_inff() ? 0.f : fast_exp2(M - Mb);
+            den *= sM;
+#pragma unroll
+            for (int e = 0; e < kCh; e++) acc[e] *= sM;
+#pragma unroll
+            for (int c = 0; c < kSeg; c++) {
+                const float f = mc[c] == -__builtin_inff() ? 0.f : fast_exp2(mc[c] - Mb);
+                den += lc[c] * f;
+#pragma unroll
+                for (int x = 0; x < kF4; x++) {
+                    acc[4 * x] += oc[c][x].x * f;
+                    acc[4 * x + 1] += oc[c][x].y * f;
+                    acc[4 * x + 2] += oc[c][x].z * f;
+                    acc[4 * x + 3] += oc[c][x].w * f;
+                }
+            }
+            M = Mb;
+        }
+    }
+    float Mu = M;   // the max that den and the probabilities are relative to
+    if constexpr (FULL) {
+        // the row's low-res part: lo_all minus the segments' corrections
+        const float ll = fmaxf(ll_in - sw, 0.f), mi2 = mrow * kLog2e;
+        const float Mf = fmaxf(M, mi2);
+        if (Mf != -__builtin_inff()) {
+            const float sM = M == -__builtin_inff() ? 0.f : fast_exp2(M - Mf);
+            const float f = fast_exp2(mi2 - Mf);
+            den = den * sM + ll * f;
+            Mu = Mf;
+#pragma unroll
+            for (int e = 0; e < kCh; e++) acc[e] = acc[e] * sM + (lo_in[e] - corr[e]) * f;
+        }
+    }
+    const bool valid = (qm >> t) & 1u;
+    const float inv = (valid && den > 0.f) ? 1.0f / den : 0.f;
+    const int tok = i * kBlock + t;
+    if ((lane & 7) == 0 && p.save_stats) {   // the token's softmax statistics, for the backward pass
+        const size_t st = (size_t)bh * p.N + tok;
+        p.st_m[st] = Mu == -__builtin_inff() ? 0.f : Mu;
+        p.st_linv[st] = inv;
+    }
+    const size_t orow = ((size_t)bh * p.N + tok) * HD + c0;
+    if constexpr (DT == 1) {
+#pragma unroll
+        for (int x = 0; x < kCh / 8; x++) {
+            uint4 pk;
+            pk.x = pack_bf16x2(acc[8 * x] * inv, acc[8 * x + 1] * inv);
+            pk.y = pack_bf16x2(acc[8 * x + 2] * inv, acc[8 * x + 3] * inv);
+            pk.z = pack_bf16x2(acc[8 * x + 4] * inv, acc[8 * x + 5] * inv);
+            pk.w = pack_bf16x2(acc[8 * x + 6] * inv, acc[8 * x + 7] * inv);
+            reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + orow)[x] = pk;
+        }
+    } else {
+#pragma unroll
+        for (int x = 0; x < kF4; x++)
+            reinterpret_cast<float4*>(static_cast<float*>(p.out) + orow)[x] =
+                make_float4(acc[4 * x] * inv, acc[4 * x + 1] * inv, acc[4 * x + 2] * inv, acc[4 * x + 3] * inv);
+    }
+}
+
 // Finish a segment: a whole row writes its output, otherwise a partial.
 template <int DT, int HD, bool FULL>
 __device__ __forceinline__ void finish_segment(const Params& p, const Wave<DT, HD>& W, Acc<DT, HD>& A, int we,
@@ -849,7 +967,7 @@ __device__ __forceinline__ int64_t cost_before(int64_t e, int item, int pos) {
 // passes the cuts to the joiners.
 template <int DT, int HD, bool FULL>
 __device__ __forceinline__ void run_range(const Params& p, int bh, int k, int WPH, int lane, int wave,
-                                          StageBuf<DT, HD>& sb, int* wg_cut) {
+                                          StageBuf<DT, HD>& sb, int* wg_cut, int4* wg_join, int* wg_njoin) {
     // the head's stream: K records (a static layout fills row_ptr[nb] of its
     // capacity K)
     const int64_t K = p.attn_dyn ? min((int64_t)p.row_ptr[(size_t)bh * (p.nb + 1) + p.nb], p.K) : p.K;
@@ -954,9 +1072,11 @@ __device__ __forceinline__ void run_range(const Params& p, int bh, int k, int WP
     }
     const int npend = A.npend;
     // Then count the cut segments this wave ended, one lane per segment,
-    // once their partials are stored; the wave that completes a row's count
-    // joins the row.  Then the head's rows with no selected block, listed
-    // rows k, k + WPH, ...
+    // once their partials are stored; a segment that completes its row's
+    // count puts the row on the workgroup's join list.  After a second
+    // barrier the workgroup's four waves join every listed row together, a
+    // quarter of its tokens each.  Then the head's rows with no selected
+    // block, listed rows k, k + WPH, ... by this wave alone.
     uint64_t joins = 0;        // lanes whose segment completed its row
     int jrow = 0, jfirst = 0, jn = 0;
     if (npend > 0) {
@@ -978,26 +1098,30 @@ __device__ __forceinline__ void run_range(const Params& p, int bh, int k, int WP
         }
         joins = __builtin_amdgcn_ballot_w64(last);
     }
-    for (int s = k;;) {
-        int i, first = 0, nseg = 0;
-        const bool cut = joins != 0;
-        if (cut) {
-            const int t = __builtin_ctzll(joins);
-            joins &= joins - 1;
-            i = rl(jrow, t);
-            first = rl(jfirst, t);
-            nseg = rl(jn, t);
-        } else {
-            if (s >= nm) break;
-            if (s != k) dsc = p.merge_rows[(size_t)bh * p.nb + s];
-            s += WPH;
-            if (dsc.z != 0) continue;
-            i = min(max(dsc.x, 0), p.nb - 1);
+    {
+        // this wave's rows to join, packed into its part of the list
+        const int slot = __builtin_popcountll(joins & ((1ull << lane) - 1ull));
+        if ((joins >> lane) & 1ull) wg_join[wave * kWindow + slot] = make_int4(jrow, jfirst, jn, 0);
+        if (lane == 0) wg_njoin[wave] = __builtin_popcountll(joins);
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int w = 0; w < kWaves; w++) {
+        const int nj = wg_njoin[w];
+        for (int x = 0; x < nj; x++) {
+            const int4 jd = wg_join[w * kWindow + x];
+            join_part<DT, HD, FULL>(p, bh, W.b, p.nb, lane, wave, jd.x, jd.y, jd.z);
+            // back to zero for the next launch on this workspace (every segment has counted)
+            if (wave == 0 && lane == 0)
+                __hip_atomic_store(p.join_cnt + (size_t)bh * p.nb + jd.x, 0u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
         }
-        join_row<DT, HD, FULL>(p, bh, W.b, p.nb, lane, i, first, nseg, reinterpret_cast<float*>(sb.v));
-        // back to zero for the next launch on this workspace (every segment has counted)
-        if (cut && lane == 0)
-            __hip_atomic_store(p.join_cnt + (size_t)bh * p.nb + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    for (int s = k; s < nm; s += WPH) {
+        if (s != k) dsc = p.merge_rows[(size_t)bh * p.nb + s];
+        if (dsc.z == 0)
+            join_row<DT, HD, FULL>(p, bh, W.b, p.nb, lane, min(max(dsc.x, 0), p.nb - 1), 0, 0,
+                                   reinterpret_cast<float*>(sb.v));
     }
 }
 
@@ -1011,6 +1135,11 @@ __global__ __launch_bounds__(kThreads, HD == 64 ? 2 : 1) void attn_kernel(Params
     // a wave that starts the next head in turn does not overwrite the cuts a
     // slower wave may still be reading for the previous one
     __shared__ int wg_cut[2][kWaves + 1];
+    // the rows the workgroup joins together after its second barrier: (row,
+    // first segment, segments) per wave's completed rows (a wave ends at most
+    // kWindow segments), and their number per wave
+    __shared__ int4 wg_join[kWaves * kWindow];
+    __shared__ int wg_njoin[kWaves];
     const int xcd = blockIdx.x & 7;
     // the wave index is uniform: made so for the compiler, so that ranges,
     // loop bounds and addresses derived from it stay in scalar registers
@@ -1022,12 +1151,14 @@ __global__ __launch_bounds__(kThreads, HD == 64 ? 2 : 1) void attn_kernel(Params
         // turn, so the XCD's L2 holds one head's K and V at a time
         if (wx >= WPH) return;
         for (int bh = xcd; bh < p.BH; bh += 8)
-            run_range<DT, HD, FULL>(p, bh, wx, WPH, lane, wave, stage[wave], wg_cut[(bh >> 3) & 1]);
+            run_range<DT, HD, FULL>(p, bh, wx, WPH, lane, wave, stage[wave], wg_cut[(bh >> 3) & 1], wg_join,
+                                    wg_njoin);
     } else {
         const int hm = wx / WPH;
         const int bh = xcd + 8 * hm;
         if (bh < p.BH)
-            run_range<DT, HD, FULL>(p, bh, wx - hm * WPH, WPH, lane, wave, stage[wave], wg_cut[0]);
+            run_range<DT, HD, FULL>(p, bh, wx - hm * WPH, WPH, lane, wave, stage[wave], wg_cut[0], wg_join,
+                                    wg_njoin);
     }
 }
 
