@@ -754,9 +754,18 @@ __device__ __forceinline__ void process(const Params& p, const Wave<DT, HD>& W, 
         for (int x = 0; x < HD / 64; x++) A.corr[x] = __builtin_fmaf(w, s.vh[x], A.corr[x]);
         A.sw += w;
     }
+    // The padded keys of block j enter as the accumulator's start: -inf for a
+    // padded key, 0 otherwise (the MFMAs add the products to it, and -inf
+    // plus a finite product stays -inf), so no masking pass follows.  Blocks
+    // without padded keys, the common case, start from 0; the two cases run
+    // separate MFMA chains, which keeps S in one register tuple.
     f32x16 S;
+    auto key_start = [&]() {
+        f32x16 c;
 #pragma unroll
-    for (int r = 0; r < 16; r++) S[r] = 0.f;
+        for (int r = 0; r < 16; r++) c[r] = ((kb >> acc_row(r, lane)) & 1u) ? 0.f : -__builtin_inff();
+        return c;
+    };
     if constexpr (DT == 1) {
         // stage K_j, V_j (and Q_i when a piece starts) in this wave's LDS
         // region; K and Q are read back one token row per lane (the MFMA
@@ -790,13 +799,24 @@ __device__ __forceinline__ void process(const Params& p, const Wave<DT, HD>& W, 
             ka[kc] = *reinterpret_cast<const u32x4*>(sb.k + k_swz<HD>(n, 2 * kc + h));
             qa[kc] = *reinterpret_cast<const u32x4*>(qs + n * QS + 16 * kc + 8 * h);
         }
+        if (kb == 0xFFFFFFFFu) {
+            f32x16 z;
 #pragma unroll
-        for (int kc = 0; kc < HD / 16; kc++)
-            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[kc]), as_bf16x8(qa[kc]), S, 0, 0, 0);
-        // keep the reads together ahead of the MFMAs (the scheduler would
-        // otherwise interleave them and wait for each pair)
-        __builtin_amdgcn_sched_group_barrier(0x100, HD / 8, 0);   // LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, HD / 16, 0);  // MFMA
+            for (int r = 0; r < 16; r++) z[r] = 0.f;
+            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[0]), as_bf16x8(qa[0]), z, 0, 0, 0);
+#pragma unroll
+            for (int kc = 1; kc < HD / 16; kc++)
+                S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[kc]), as_bf16x8(qa[kc]), S, 0, 0, 0);
+            // keep the reads together ahead of the MFMAs (the scheduler would
+            // otherwise interleave them and wait for each pair)
+            __builtin_amdgcn_sched_group_barrier(0x100, HD / 8, 0);   // LDS reads
+            __builtin_amdgcn_sched_group_barrier(0x008, HD / 16, 0);  // MFMA
+        } else {
+            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[0]), as_bf16x8(qa[0]), key_start(), 0, 0, 0);
+#pragma unroll
+            for (int kc = 1; kc < HD / 16; kc++)
+                S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[kc]), as_bf16x8(qa[kc]), S, 0, 0, 0);
+        }
     } else {
         constexpr int kRowLanes = HD / 4, kRowsPerLoad = 64 / kRowLanes;
         constexpr int VS = v_stride_f(HD);
@@ -804,6 +824,7 @@ __device__ __forceinline__ void process(const Params& p, const Wave<DT, HD>& W, 
         for (int x = 0; x < kKV; x++)
             *reinterpret_cast<u32x4*>(vs + (lane / kRowLanes + kRowsPerLoad * x) * VS + (lane % kRowLanes) * 4) =
                 s.v[x];
+        S = key_start();
 #pragma unroll
         for (int c4 = 0; c4 < kKV; c4++) {
             const float4 kf = __builtin_bit_cast(float4, s.k[c4]);
@@ -819,16 +840,8 @@ __device__ __forceinline__ void process(const Params& p, const Wave<DT, HD>& W, 
     }
     // online softmax in log2 units: max over the 32 keys of each query row
     float bm = -__builtin_inff();
-    if (kb == 0xFFFFFFFFu) {
 #pragma unroll
-        for (int r = 0; r < 16; r++) bm = fmaxf(bm, S[r]);
-    } else {
-#pragma unroll
-        for (int r = 0; r < 16; r++) {
-            S[r] = ((kb >> acc_row(r, lane)) & 1u) ? S[r] : -__builtin_inff();
-            bm = fmaxf(bm, S[r]);
-        }
-    }
+    for (int r = 0; r < 16; r++) bm = fmaxf(bm, S[r]);
     bm = xhalf_max(bm) * scale2;
     // The running max moves only when a block's max exceeds it by more than
     // kLazyMax (log2 units), so most blocks keep alpha = 1 and skip the
