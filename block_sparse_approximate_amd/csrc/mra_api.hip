@@ -33,7 +33,7 @@ bool carve(const mra_dims& d, int32_t bpr, int32_t mode, Layout* L) {
     L->BH = d.batch * d.heads;
     L->K = mra_num_block(d.seq_len, bpr);
     if (L->K < 0) return false;
-    L->max_items = L->nb + (int32_t)((L->K + kChunk - 1) / kChunk);
+    L->max_items = L->nb + (int32_t)((L->K + kChunkMin - 1) / kChunkMin);   // segments of kChunkMin or more
     const size_t BH = (size_t)L->BH, nb = (size_t)L->nb, dd = (size_t)d.head_dim;
     const size_t words = (nb + 31) / 32;
     size_t o = 256;  // first 256 bytes: device error word
@@ -152,6 +152,7 @@ Params make_params(const mra_dims& d, const Layout& L, int32_t mode, int32_t pf,
     p.max_items = L.max_items;
     p.attn_wph = attn_grid_waves_per_head(L.BH, L.K);
     p.attn_seq = attn_heads_in_turn(L.BH, L.K) ? 1 : 0;
+    attn_segments(L.BH, L.K, &p.seg_whole, &p.chunk);
     p.q = q; p.k = k; p.v = v; p.mask = mask; p.out = out;
     p.qhat = reinterpret_cast<float*>(w + L.qhat);
     p.khat = reinterpret_cast<float*>(w + L.khat);

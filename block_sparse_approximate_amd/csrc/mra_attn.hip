@@ -3,8 +3,9 @@
 // sparse-dense matmul and reduce-sum do, in one pass with an online row max.
 //
 // Work decomposition: the selector lists every selected block of a head in
-// CSR order (block row, then key block), each row cut into segments of at
-// most kChunk blocks.  The G workgroups of a head split that list into G
+// CSR order (block row, then key block); a row longer than p.seg_whole
+// blocks is cut into segments of p.chunk blocks (both chosen at launch from
+// the workgroups' share of the head).  The G workgroups of a head split that list into G
 // ranges of about K/G blocks, each moved to the nearest segment start, and
 // the kWaves waves of a workgroup split its range exactly into kWaves equal
 // parts, wherever those cuts fall: every wave gets the same number of blocks
@@ -51,7 +52,7 @@
 //     the next waves to its own and finishes the segment as if it had done
 //     it alone;
 //   * across workgroups: a row cut into several segments (only rows longer
-//     than kChunk blocks) is joined by the wave that ends its last segment
+//     than p.seg_whole blocks) is joined by the wave that ends its last segment
 //     to arrive.  Every segment of a cut row stores its partials with
 //     agent-scope (write-through) stores; after its part, the wave waits for
 //     them to complete and adds one to each such row's counter; the wave
@@ -89,9 +90,10 @@ __host__ __device__ constexpr int v_stride_f(int hd) { return hd + 4; }    // fp
 constexpr int kWindow = 64;     // block records a wave holds (one per lane)
 constexpr float kLazyMax = 8.0f;   // log2 headroom of the running max (probabilities <= 256)
 // Blocks per wave, on average over a workgroup's range, at most: a
-// workgroup's range grows by up to kChunk / 2 blocks at each end when they
-// move to segment starts, and each of its kWaves parts must fit the window.
-constexpr int kMaxRun = (kWaves * kWindow - 2 * kChunk - 2 * kWaves) / kWaves;
+// workgroup's range grows by up to half a segment at each end when they
+// move to segment starts, and each of its kWaves parts must fit the window
+// (the launch keeps the segment lengths within what this leaves).
+constexpr int kMaxRun = (kWaves * kWindow - 2 * kChunkMin - 2 * kWaves) / kWaves;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
@@ -1199,6 +1201,26 @@ int attn_grid_waves_per_head(int BH, int64_t K) {
     const int64_t lo = ((K + kMaxRun - 1) / kMaxRun + kWaves - 1) / kWaves * kWaves;
     if (w < lo) w = lo;
     return (int)w;
+}
+
+// Segment lengths.  A row of up to one workgroup's share of the head is one
+// segment: moving a range end to a segment start then unbalances the
+// workgroups by at most half a row, and the row needs no join.  A longer
+// row is cut into segments of about half that share, whose partials go
+// through memory and a join.  Both within [kChunkMin, kChunkMax], and short
+// enough that a range grown by half a segment at each end still splits into
+// parts the record window holds (kWaves parts of at most kWindow - 1 blocks).
+void attn_segments(int BH, int64_t K, int32_t* seg_whole, int32_t* chunk) {
+    const int64_t G = attn_grid_waves_per_head(BH, K) / kWaves;
+    const int64_t r = (K + G - 1) / G;   // blocks per workgroup range, before the moves
+    const int64_t fit = (int64_t)kWaves * (kWindow - 1) - r - 2;
+    auto clamp = [&](int64_t c) {
+        if (c > fit) c = fit;
+        if (c > kChunkMax) c = kChunkMax;
+        return (int32_t)(c < kChunkMin ? kChunkMin : c);
+    };
+    *seg_whole = clamp(r);
+    *chunk = clamp(r / 2);
 }
 
 // Launch one instantiation with kWaves stage buffers of dynamic LDS (bf16

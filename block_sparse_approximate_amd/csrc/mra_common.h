@@ -16,7 +16,10 @@ constexpr int kHeadDim = 64;            // head dims this build accepts
 constexpr int kHistBits = 12;           // first radix digit of the selection key
 constexpr int kHistBins = 1 << kHistBits;
 constexpr float kPriorBias = 5000.0f;   // [MRA] step 2: 5e3 bias for forced blocks
-constexpr int kChunk = 16;              // max selected key blocks per segment of a row
+// Segments of a row (selected key blocks): the attention's launch chooses
+// their lengths between these two (the record's length field holds 6 bits)
+constexpr int kChunkMin = 16;
+constexpr int kChunkMax = 63;
 constexpr int kMaxHeadDim = 128;        // widest head the forward kernels take
 // floats per segment's low-res correction: hd channels, weight sum, pad
 __host__ __device__ constexpr int corr_stride(int hd) { return hd + 4; }
@@ -28,15 +31,16 @@ constexpr int kCandStride = 32;         // u32 per head's candidate counter: one
 constexpr float kLog2e = 1.4426950408889634f;
 
 // One selected block, in the head's CSR order (block row ascending, then key
-// block ascending).  A block row's selection is cut into segments of at most
-// kChunk blocks; a segment is the unit whose partial softmax the attention
-// kernel produces.
+// block ascending).  A block row of at most Params::seg_whole selected blocks
+// is one segment; a longer one is cut into segments of Params::chunk blocks
+// (the last one shorter).  A segment is the unit whose partial softmax the
+// attention kernel produces.
 //   ij    query block row i (bits 0..15) and key block j (bits 16..31)
 //   kmask valid-token mask word of key block j
 //   rsv   0 (keeps a record 16 bytes, one load per lane)
 //   info  bits  0..17  segment (item) index within the head
 //               18..23 position of the block within its segment
-//               24..29 segment length (1..kChunk)
+//               24..29 segment length (1..63)
 //               30     the segment is the whole row
 struct BlkRec {
     uint32_t ij;
@@ -49,6 +53,10 @@ __host__ __device__ constexpr uint32_t rec_ij(int i, int j) { return (uint32_t)i
 __host__ __device__ constexpr uint32_t rec_info(int item, int pos, int len, bool whole) {
     return (uint32_t)item | ((uint32_t)pos << 18) | ((uint32_t)len << 24) | (whole ? (1u << 30) : 0u);
 }
+
+// Segment length of a block row of n selected blocks (n itself when the row
+// is one segment).
+__host__ __device__ constexpr int row_seg_len(int n, int seg_whole, int chunk) { return n <= seg_whole ? n : chunk; }
 
 // Workspace carve, shared by the host dispatcher and the kernels.
 struct Layout {
@@ -73,6 +81,8 @@ struct Params {
     int32_t band_exact;    // 1: the diagonal prior band is exactly prior_diag blocks wide
     int32_t save_stats;    // 1: store each token's softmax statistics (st_m, st_linv) for the backward
     int32_t max_items;
+    int32_t seg_whole;     // rows of at most this many selected blocks are one segment
+    int32_t chunk;         // longer rows: segments of this many blocks (both kChunkMin..kChunkMax)
     const void* q;
     const void* k;
     const void* v;
@@ -210,4 +220,5 @@ int bwd_max_chunks(int nb, int64_t K);
 hipError_t launch_bwd(const Params& p, hipStream_t s);
 int attn_grid_waves_per_head(int BH, int64_t K);
 bool attn_heads_in_turn(int BH, int64_t K);
+void attn_segments(int BH, int64_t K, int32_t* seg_whole, int32_t* chunk);
 }  // namespace mra

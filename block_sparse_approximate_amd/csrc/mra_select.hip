@@ -22,7 +22,7 @@
 //     over those candidates find the K-th largest key T;
 //   * the selected set {key >= T} is written as a bitmap, as CSR (row_ptr,
 //     col ascending) and as the attention stream: one record per selected
-//     block, rows cut into segments of at most kChunk blocks.
+//     block, rows longer than p.seg_whole blocks cut into segments of p.chunk.
 // A thread holds 16 cell keys in registers (the whole head up to N = 4096;
 // longer heads are walked in tiles of 16384 cells with the next tile in
 // flight), and wave w's cells of a tile are 64 consecutive cells, so one
@@ -840,7 +840,8 @@ __device__ __forceinline__ void emit_stream(const Params& p, int bh, const uint3
         int c = 0;
         if (i < nb)
             for (int w = 0; w < words; w++) c += __popc(bitmap[i * words + w]);
-        const int it = (c + kChunk - 1) / kChunk;
+        const int sl = row_seg_len(c, p.seg_whole, p.chunk);
+        const int it = c > 0 ? (c + sl - 1) / sl : 0;
         const int mf = (i < nb && it != 1) ? 1 : 0;   // no selected block, or several segments
         const uint64_t v = (uint64_t)c | ((uint64_t)it << 32) | ((uint64_t)mf << 48);
         uint64_t tot;
@@ -910,9 +911,9 @@ __device__ __forceinline__ void emit_stream(const Params& p, int bh, const uint3
         }
         const int j = w * 32 + pos;
         col[e] = j;
-        const int nit = (n + kChunk - 1) / kChunk, sg = rank / kChunk;
-        const int len = min(kChunk, n - sg * kChunk);
-        recs[e] = BlkRec{rec_ij(i, j), mbv[j], 0u, rec_info(ic[i] + sg, rank - sg * kChunk, len, nit == 1)};
+        const int ch = row_seg_len(n, p.seg_whole, p.chunk), nit = (n + ch - 1) / ch, sg = rank / ch;
+        const int len = min(ch, n - sg * ch);
+        recs[e] = BlkRec{rec_ij(i, j), mbv[j], 0u, rec_info(ic[i] + sg, rank - sg * ch, len, nit == 1)};
     }
 }
 
@@ -1241,7 +1242,8 @@ __device__ __forceinline__ void select_rows(const Params& p, int bh, int t, unsi
                 if (gpr == 2) c += (int)gcnt[i * gpr + 1];
             }
             cc[q] = c;
-            itc[q] = (c + kChunk - 1) / kChunk;
+            const int sl = row_seg_len(c, p.seg_whole, p.chunk);
+            itc[q] = c > 0 ? (c + sl - 1) / sl : 0;
             mfc[q] = (i < nb && itc[q] != 1) ? 1 : 0;   // no selected block, or several segments
         }
         // counts in bits 0..19 and join flags in 20..31 of one word; segments in another
@@ -1307,9 +1309,9 @@ __device__ __forceinline__ void select_rows(const Params& p, int bh, int t, unsi
         }
         const int j = w * 32 + nth_set_bit(bits, (uint32_t)r + 1u);
         col[e] = j;
-        const int nit = (n + kChunk - 1) / kChunk, sg = rank_in_row / kChunk;
-        const int len = min(kChunk, n - sg * kChunk);
-        recs[e] = BlkRec{rec_ij(i, j), mbv[j], 0u, rec_info(ic[i] + sg, rank_in_row - sg * kChunk, len, nit == 1)};
+        const int ch = row_seg_len(n, p.seg_whole, p.chunk), nit = (n + ch - 1) / ch, sg = rank_in_row / ch;
+        const int len = min(ch, n - sg * ch);
+        recs[e] = BlkRec{rec_ij(i, j), mbv[j], 0u, rec_info(ic[i] + sg, rank_in_row - sg * ch, len, nit == 1)};
     }
 }
 

@@ -218,6 +218,11 @@ EDGE = [
                                      mask=np.repeat(np.arange(256)[None, :] < np.array([[256], [96]]), 16,
                                                     axis=0).astype(np.uint8))),
     ("many-heads-bh1024-nb2", dict(B=64, H=16, N=64, block_per_row=1, approx_mode="sparse")),
+    # 32 heads of 1024 selected blocks over 16 workgroups each (64 blocks a workgroup): rows of up
+    # to 63 blocks stay one segment, longer ones (the prior's first rows, 128 blocks) are cut
+    # into segments of 32
+    ("long-segments-full", dict(B=4, H=8, N=4096, block_per_row=8, prior_first=1)),
+    ("long-segments-sparse", dict(B=4, H=8, N=4096, block_per_row=8, prior_first=2, approx_mode="sparse")),
 ]
 
 
@@ -251,7 +256,7 @@ def test_fp32_all_selected_equals_dense(mra):
 
 
 @pytest.mark.parametrize("name", ["long-rows-full", "long-rows-sparse", "long-rows-fp32", "heads-in-turn-bh9",
-                                  "many-heads-bh512-masked"])
+                                  "many-heads-bh512-masked", "long-segments-full", "long-segments-sparse"])
 def test_attention_relaunch_rewrites_the_same_output(mra, name):
     # The attention kernel joins cut rows through per-row counters in the
     # workspace that it sets back to zero: relaunching it on the workspace of
