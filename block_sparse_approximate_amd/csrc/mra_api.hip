@@ -61,7 +61,7 @@ bool carve(const mra_dims& d, int32_t bpr, int32_t mode, Layout* L) {
     L->part_o = take(BH * (size_t)L->max_items * kBlock * dd * 4);
     L->part_ml = take(BH * (size_t)L->max_items * 2 * kBlock * 4);
     L->part_corr = mode == MRA_APPROX_FULL ? take(BH * (size_t)L->max_items * corr_stride(d.head_dim) * 4) : 0;
-    L->park = take(BH * (size_t)attn_grid_waves_per_head(L->BH, L->K) * park_floats(d.head_dim) * 4);
+    L->park = take(BH * (size_t)attn_grid_waves_per_head(L->BH, L->K, d.head_dim) * park_floats(d.head_dim) * 4);
     L->cand = take(BH * (size_t)kSelCap * 8);
     L->ncand = take(BH * kCandStride * 4);
     L->st_m = take(BH * (size_t)L->N * 4);
@@ -150,9 +150,9 @@ Params make_params(const mra_dims& d, const Layout& L, int32_t mode, int32_t pf,
     p.band_exact = band == MRA_BAND_EXACT ? 1 : 0;
     p.save_stats = save_stats ? 1 : 0;
     p.max_items = L.max_items;
-    p.attn_wph = attn_grid_waves_per_head(L.BH, L.K);
-    p.attn_seq = attn_heads_in_turn(L.BH, L.K) ? 1 : 0;
-    attn_segments(L.BH, L.K, &p.seg_whole, &p.chunk);
+    p.attn_wph = attn_grid_waves_per_head(L.BH, L.K, L.d);
+    p.attn_seq = attn_heads_in_turn(L.BH, L.K, L.d) ? 1 : 0;
+    attn_segments(L.BH, L.K, L.d, &p.seg_whole, &p.chunk);
     p.q = q; p.k = k; p.v = v; p.mask = mask; p.out = out;
     p.qhat = reinterpret_cast<float*>(w + L.qhat);
     p.khat = reinterpret_cast<float*>(w + L.khat);

@@ -88,6 +88,8 @@ __host__ __device__ constexpr int v_stride_b(int hd) { return hd + 16; }   // bf
 __host__ __device__ constexpr int q_stride_b(int hd) { return hd + 8; }    // bf16 Q: row r's 16-byte reads start at bank group r
 __host__ __device__ constexpr int v_stride_f(int hd) { return hd + 4; }    // fp32 V
 constexpr int kWindow = 64;     // block records a wave holds (one per lane)
+// blocks whose loads a wave keeps in flight
+template <int HD> __host__ __device__ constexpr int kSlots() { return 1; }
 constexpr float kLazyMax = 8.0f;   // log2 headroom of the running max (probabilities <= 256)
 // Blocks per wave, on average over a workgroup's range, at most: a
 // workgroup's range grows by up to half a segment at each end when they
@@ -726,8 +728,9 @@ __device__ __forceinline__ void merge_piece(const float* src, int lane, Acc<DT, 
         }
 }
 
-// One block of the stream: S^T, online softmax, O^T += V^T P^T.
-template <int DT, int HD, bool FULL>
+// One block of the stream: S^T, online softmax, O^T += V^T P^T.  Once the
+// slot's data is staged, the slot is refilled with block `next` (ISSUE).
+template <int DT, int HD, bool FULL, bool ISSUE = true>
 __device__ __forceinline__ void process(const Params& p, const Wave<DT, HD>& W, int e, Slot<DT, HD>& s,
                                         Acc<DT, HD>& A, StageBuf<DT, HD>& sb, float scale2, int next) {
     constexpr int kKV = Cfg<DT, HD>::kKV;
@@ -789,7 +792,7 @@ __device__ __forceinline__ void process(const Params& p, const Wave<DT, HD>& W, 
         }
         // the slot is free once staged: the next block's loads go out now,
         // to arrive while this block is computed
-        issue<DT, HD, FULL>(p, W, next, s, sb);
+        if constexpr (ISSUE) issue<DT, HD, FULL>(p, W, next, s, sb);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -837,7 +840,7 @@ __device__ __forceinline__ void process(const Params& p, const Wave<DT, HD>& W, 
             S = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.w, qf.w, S, 0, 0, 0);
         }
         // K and Q are used, V is staged: the next block's loads go out now
-        issue<DT, HD, FULL>(p, W, next, s, sb);
+        if constexpr (ISSUE) issue<DT, HD, FULL>(p, W, next, s, sb);
         __builtin_amdgcn_sched_barrier(0);
     }
     // online softmax in log2 units: max over the 32 keys of each query row
@@ -943,17 +946,28 @@ __device__ __forceinline__ void run_blocks(const Params& p, Wave<DT, HD>& W, Sta
     const float scale2 = (1.0f / __builtin_sqrtf((float)p.dscale)) * kLog2e;
     const int start = W.start, end = W.end;
 
-    // One slot: each block stages its data in LDS and then issues the next
-    // block's loads (past the end, the last block again, so that every block
-    // issues the same loads and the wait counts stay exact); they arrive
-    // while the block is computed, and the second wave on the SIMD computes
-    // while this one waits.
-    Slot<DT, HD> sl;
-    issue<DT, HD, FULL>(p, W, start, sl, sb);
+    // kSlots load slots in a ring: each block stages its slot's data in LDS
+    // and then refills the slot with the block kSlots ahead (past the end,
+    // the last block again, so that every block of the ring issues the same
+    // loads and the wait counts stay exact); they arrive while the blocks
+    // in between are computed.  The last blocks, fewer than kSlots, issue
+    // nothing.
+    constexpr int NS = kSlots<HD>();
+    Slot<DT, HD> sl[NS];
+#pragma unroll
+    for (int x = 0; x < NS; x++) issue<DT, HD, FULL>(p, W, min(start + x, end - 1), sl[x], sb);
     // the cell's low-res weight, formed as the low-res sums formed it (0 past
     // the stream's end, where the mask word is 0)
     if constexpr (FULL) W.ww = lowres_weight(W.ww, W.wm, __popc(W.wk));
-    for (int e = start; e < end; e++) process<DT, HD, FULL>(p, W, e, sl, A, sb, scale2, min(e + 1, end - 1));
+    int e = start;
+    for (; e + NS <= end; e += NS) {
+#pragma unroll
+        for (int x = 0; x < NS; x++)
+            process<DT, HD, FULL>(p, W, e + x, sl[x], A, sb, scale2, min(e + x + NS, end - 1));
+    }
+#pragma unroll
+    for (int x = 0; x + 1 < NS; x++)
+        if (e + x < end) process<DT, HD, FULL, false>(p, W, e + x, sl[x], A, sb, scale2, 0);
 }
 
 // Relative costs of the work in a wave's part, in eighths of a block: every
@@ -1182,15 +1196,19 @@ __global__ __launch_bounds__(kThreads, HD == 64 ? 2 : 1) void attn_kernel(Params
 // Heads whose ranges would still hold at least this many blocks each when
 // every wave of an XCD shares one head are taken in turn.
 constexpr int64_t kTurnMinBlocks = 12;
-constexpr int kWavesPerXcd = 256;                     // about 2048 waves on the chip
+// Waves resident on one XCD (32 CUs): two workgroups of kWaves per CU for
+// 64-channel heads, one for 128-channel heads (see attn_kernel's bounds).
+// A grid of more would run a second round of workgroups.
+int waves_per_xcd(int hd) { return 32 * kWaves * (hd == 64 ? 2 : 1); }
 
-bool attn_heads_in_turn(int BH, int64_t K) {
-    return (BH + 7) / 8 >= 2 && K >= kTurnMinBlocks * kWavesPerXcd;
+bool attn_heads_in_turn(int BH, int64_t K, int hd) {
+    return (BH + 7) / 8 >= 2 && K >= kTurnMinBlocks * waves_per_xcd(hd);
 }
 
-int attn_grid_waves_per_head(int BH, int64_t K) {
+int attn_grid_waves_per_head(int BH, int64_t K, int hd) {
     const int heads_per_xcd = (BH + 7) / 8;
-    int64_t w = attn_heads_in_turn(BH, K) ? kWavesPerXcd : kWavesPerXcd / heads_per_xcd;
+    const int wx = waves_per_xcd(hd);
+    int64_t w = attn_heads_in_turn(BH, K, hd) ? wx : wx / heads_per_xcd;
     const int64_t hi = (K + 1) / 2;                   // at least about two blocks a wave
     if (w > hi) w = hi;
     // whole workgroups, rounded down so that the grid stays within one
@@ -1210,8 +1228,8 @@ int attn_grid_waves_per_head(int BH, int64_t K) {
 // through memory and a join.  Both within [kChunkMin, kChunkMax], and short
 // enough that a range grown by half a segment at each end still splits into
 // parts the record window holds (kWaves parts of at most kWindow - 1 blocks).
-void attn_segments(int BH, int64_t K, int32_t* seg_whole, int32_t* chunk) {
-    const int64_t G = attn_grid_waves_per_head(BH, K) / kWaves;
+void attn_segments(int BH, int64_t K, int hd, int32_t* seg_whole, int32_t* chunk) {
+    const int64_t G = attn_grid_waves_per_head(BH, K, hd) / kWaves;
     const int64_t r = (K + G - 1) / G;   // blocks per workgroup range, before the moves
     const int64_t fit = (int64_t)kWaves * (kWindow - 1) - r - 2;
     auto clamp = [&](int64_t c) {

@@ -218,7 +218,7 @@ hipError_t launch_attn(const Params& p, hipStream_t s);
 hipError_t launch_bigbird_layout(const Params& p, hipStream_t s);
 int bwd_max_chunks(int nb, int64_t K);
 hipError_t launch_bwd(const Params& p, hipStream_t s);
-int attn_grid_waves_per_head(int BH, int64_t K);
-bool attn_heads_in_turn(int BH, int64_t K);
-void attn_segments(int BH, int64_t K, int32_t* seg_whole, int32_t* chunk);
+int attn_grid_waves_per_head(int BH, int64_t K, int hd);
+bool attn_heads_in_turn(int BH, int64_t K, int hd);
+void attn_segments(int BH, int64_t K, int hd, int32_t* seg_whole, int32_t* chunk);
 }  // namespace mra
