@@ -822,13 +822,14 @@ __global__ __launch_bounds__(kSelThreads) void premark_kernel(Params p) {
 // words), into what the attention and join kernels read: the CSR (row_ptr,
 // col), the bitmap in memory, the segment pointers, the rows the join
 // kernel combines and one record per selected block.  mbv: the blocks' mask
-// words in LDS (written before the call; read after its barriers).  expect:
-// the number of selected cells the caller made (the error word's bit 2
-// flags another count), or -1 when the count is the layout's own (it must
-// stay within the stream's capacity p.K).  Called by a whole kSelThreads
-// workgroup.
+// words in LDS (written before the call; read after its barriers).  wp: LDS
+// for nb * words 16-bit counts (each bitmap word's set bits before it in its
+// row).  expect: the number of selected cells the caller made (the error
+// word's bit 2 flags another count), or -1 when the count is the layout's
+// own (it must stay within the stream's capacity p.K).  Called by a whole
+// kSelThreads workgroup.
 __device__ __forceinline__ void emit_stream(const Params& p, int bh, const uint32_t* bitmap, const uint32_t* mbv, int* rc,
-                            int* ic, uint64_t* scan64, int64_t expect) {
+                            int* ic, uint64_t* scan64, uint16_t* wp, int64_t expect) {
     const int nb = p.nb, words = p.words;
     const int tid = threadIdx.x;
     // CSR row pointers, segment (item) pointers and the rows the final kernel
@@ -839,7 +840,10 @@ __device__ __forceinline__ void emit_stream(const Params& p, int bh, const uint3
         const int i = tid;
         int c = 0;
         if (i < nb)
-            for (int w = 0; w < words; w++) c += __popc(bitmap[i * words + w]);
+            for (int w = 0; w < words; w++) {
+                wp[i * words + w] = (uint16_t)c;
+                c += __popc(bitmap[i * words + w]);
+            }
         const int sl = row_seg_len(c, p.seg_whole, p.chunk);
         const int it = c > 0 ? (c + sl - 1) / sl : 0;
         const int mf = (i < nb && it != 1) ? 1 : 0;   // no selected block, or several segments
@@ -870,50 +874,31 @@ __device__ __forceinline__ void emit_stream(const Params& p, int bh, const uint3
     // the bitmap in memory
     uint32_t* gbits = p.selbits + (size_t)bh * nb * words;
     for (int x = tid; x < nb * words; x += kSelThreads) gbits[x] = bitmap[x];
-    // column lists and the attention stream records: one thread per selected
-    // cell e (CSR order).  Its block row is the last row whose start is at
-    // most e; its key block is the bit of rank e - start among the set bits
-    // of that row's bitmap.
+    // column lists and the attention stream records: one thread per bitmap
+    // word (x = i * words + w), for the set bits of that word in order; the
+    // k-th of them is cell rc[i] + wp[x] + k of the stream.
     int32_t* col = p.col + (size_t)bh * p.K;
     BlkRec* recs = p.recs + (size_t)bh * p.K;
     const int tcap = (int)min((int64_t)rc[nb], p.K);
-    for (int e = tid; e < tcap; e += kSelThreads) {
-        int lo = 0, hi = nb - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (rc[mid] <= e) lo = mid;
-            else hi = mid - 1;
-        }
-        const int i = lo, o = rc[i], n = rc[i + 1] - o, rank = e - o;
-        // the word that holds the cell, then the bit: halve the word five
-        // times, keeping the half that holds the remaining rank
-        const uint32_t* row = bitmap + i * words;
-        int r = rank, w = 0;
-        uint32_t bits = row[0];
-        int c = __popc(bits);
-        while (r >= c && w + 1 < words) {
-            r -= c;
-            bits = row[++w];
-            c = __popc(bits);
-        }
-        int pos = 0;
-#pragma unroll
-        for (int half = 16; half > 0; half >>= 1) {
-            const uint32_t low = bits & ((1u << half) - 1u);
-            const int cl = __popc(low);
-            if (r >= cl) {
-                r -= cl;
-                bits >>= half;
-                pos += half;
-            } else {
-                bits = low;
+    for (int x = tid; x < nb * words; x += kSelThreads) {
+        uint32_t bits = bitmap[x];
+        if (bits == 0u) continue;
+        const int i = x / words, w = x - i * words;
+        const int o = rc[i], n = rc[i + 1] - o;
+        const int ch = row_seg_len(n, p.seg_whole, p.chunk), nit = (n + ch - 1) / ch;
+        int rank = wp[x];
+        while (bits != 0u) {
+            const int j = w * 32 + __builtin_ctz(bits);
+            bits &= bits - 1u;
+            const int e = o + rank;
+            if (e < tcap) {
+                col[e] = j;
+                const int sg = rank / ch;
+                recs[e] = BlkRec{rec_ij(i, j), mbv[j], 0u,
+                                 rec_info(ic[i] + sg, rank - sg * ch, min(ch, n - sg * ch), nit == 1)};
             }
+            rank++;
         }
-        const int j = w * 32 + pos;
-        col[e] = j;
-        const int ch = row_seg_len(n, p.seg_whole, p.chunk), nit = (n + ch - 1) / ch, sg = rank / ch;
-        const int len = min(ch, n - sg * ch);
-        recs[e] = BlkRec{rec_ij(i, j), mbv[j], 0u, rec_info(ic[i] + sg, rank - sg * ch, len, nit == 1)};
     }
 }
 
@@ -1500,7 +1485,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
 
     // the records' input, loaded in the prologue (read after the scan's barriers)
     if (tid < nb) mbv[tid] = mv;
-    emit_stream(p, bh, bitmap, mbv, rc, ic, scan64, p.K);
+    emit_stream(p, bh, bitmap, mbv, rc, ic, scan64, reinterpret_cast<uint16_t*>(hist), p.K);
 }
 
 // ---------------------------------------------------------------- BigBird layout
@@ -1577,7 +1562,8 @@ __global__ __launch_bounds__(kSelThreads) void bigbird_layout_kernel(Params p) {
             }
         }
     }
-    emit_stream(p, bh, bitmap, mbv, rc, ic, scan64, -1);
+    // the word counts go where the selector keeps its histogram
+    emit_stream(p, bh, bitmap, mbv, rc, ic, scan64, reinterpret_cast<uint16_t*>(smem + L.hist), -1);
 }
 
 }  // namespace
