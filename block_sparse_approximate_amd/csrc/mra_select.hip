@@ -68,9 +68,6 @@ constexpr int kMaxColTiles = 4;   // column tiles of kCT key blocks (N <= 16384)
 __host__ __device__ constexpr int hat_stride(int hd) { return hd + 4; }
                                   // fall on banks 4l .. 4l + 3, distinct over each 16-lane phase
 
-// Rows of the low-res weight tile: nb + 4 floats (the pad spreads the rows
-// over the LDS banks for the MFMA operand reads).
-__host__ __device__ inline int wl_stride(int nb) { return nb + 4; }
 
 __host__ __device__ inline LogitsLds logits_lds(int nb, int hd) {
     LogitsLds L;
@@ -596,135 +593,114 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(Params p) {
 }
 
 // ---------------------------------------------------------------- low-res sums
-// Full mode, [MRA] "第四步": the low-resolution attention of 32 block rows of
+// Full mode, [MRA] "第四步": the low-resolution attention of 64 block rows of
 // head bh over every key block, selected or not,
 //   lo_all_i = sum_j w_ij vhat_j,  ll_all_i = sum_j w_ij,  w_ij = cnt_j exp(S_ij - m_i),
 // from which the block attention later takes the selected cells back out.
 // These workgroups ride in the selector's launch: they need only the logits
-// kernel's output, so they run on the CUs the per-head selectors leave idle.
-// The product runs on v_mfma_f32_16x16x4f32: wave w takes the 16-row tile
-// w / 8, the 16-channel tile (w / 2) % 4 and the key half w % 2 of each key
-// tile; A lane l holds W[l % 16][k = l / 16], B lane l holds
-// vhat[k = l / 16][l % 16], and accumulator e of lane l is row 4 (l / 16) + e,
-// channel l % 16.
-constexpr int kLoRows = 32;
-// key blocks per staged vhat tile: 128 for 64-channel heads, 64 for 128
+// kernel's output, so they run on the CUs the per-head selectors leave idle
+// (64 rows a workgroup, so that at N = 16384 they and the selectors fit one
+// round of one workgroup per CU).  Key blocks go by tiles of kKT: the
+// workgroup forms the tile's weights (thread t: row t / 16, keys t % 16 +
+// 16 m) and stages the tile's vhat rows, then the product runs on
+// v_mfma_f32_16x16x4f32: wave w takes the 16-row tile w / 4 and the
+// 16-channel tiles w % 4 + 4 x; A lane l holds W[l % 16][k = l / 16], B lane
+// l holds vhat[k = l / 16][l % 16], and accumulator e of lane l is row
+// 4 (l / 16) + e, channel l % 16.
+constexpr int kLoRows = 64;
+// key blocks per tile: 128 for 64-channel heads, 64 for 128
 __host__ __device__ constexpr int lowres_keys(int hd) { return hd == 64 ? kCT : kCT / 2; }
+// floats per weight-tile row (4 of pad: the 16 rows an MFMA operand reads
+// start 4 banks apart)
+__host__ __device__ constexpr int wt_stride(int hd) { return lowres_keys(hd) + 4; }
 
-__host__ __device__ inline size_t lowres_lds(int nb, int hd) {
-    return align16((size_t)kLoRows * wl_stride(nb) * 4) + align16((size_t)lowres_keys(hd) * hat_stride(hd) * 4) +
-           align16(2 * 8 * 64 * 4 * 4);
+__host__ __device__ inline size_t lowres_lds(int /*nb*/, int hd) {
+    return align16((size_t)kLoRows * wt_stride(hd) * 4) + align16((size_t)lowres_keys(hd) * hat_stride(hd) * 4);
 }
 
 template <int HD>
 __device__ __forceinline__ void lowres_rows(const Params& p, int bh, int row0, unsigned char* smem) {
     constexpr int kVtStride = hat_stride(HD);
-    constexpr int kKT = lowres_keys(HD);     // key blocks per vhat tile
+    constexpr int kKT = lowres_keys(HD);     // key blocks per tile
+    constexpr int kWS = wt_stride(HD);
     constexpr int kCTW = HD / 64;            // 16-channel tiles per wave
-    const int nb = p.nb, nbp = wl_stride(nb);
+    constexpr int kM = kKT / 16;             // weights per thread and tile
+    const int nb = p.nb;
     const int b = bh / p.H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     float* wl = reinterpret_cast<float*>(smem);
-    float* vt = reinterpret_cast<float*>(smem + align16((size_t)kLoRows * nbp * 4));
-    float* red = vt + align16((size_t)kKT * kVtStride * 4) / 4;
+    float* vt = reinterpret_cast<float*>(smem + align16((size_t)kLoRows * kWS * 4));
     const float* S = p.logits + (size_t)bh * nb * nb;
     const float* vh = p.vhat + (size_t)bh * nb * HD;
     const int* cnt = p.cnt + (size_t)b * nb;
     constexpr int kVLoads = kKT * (HD / 4) / kSelThreads;   // float4s of one vhat tile per thread
+    const int r = tid >> 4, kq = tid & 15;                   // this thread's row and first key of a tile
+    const int row = row0 + r;
+    const bool rok = row < nb;
 
-    // vhat tile 0 in flight first; the weights: wave w owns rows 2w, 2w + 1
+    // a tile's inputs: vhat rows, and this thread's logits and key counts
     float4 vv[kVLoads];
+    float sv[kM];
+    int cv[kM];
+    auto fetch = [&](int j0) {
 #pragma unroll
-    for (int e = 0; e < kVLoads; e++) {
-        const int x = tid + e * kSelThreads, j = x / (HD / 4);
-        vv[e] = j < nb ? *reinterpret_cast<const float4*>(vh + (size_t)j * HD + (x % (HD / 4)) * 4)
-                       : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    constexpr int kJ = kMaxColTiles * kCT / 64;   // key blocks per lane (nb <= 512)
-    const int ia = row0 + 2 * wave, ib = ia + 1;   // this wave's two rows
-    float sa[kJ], sb[kJ];
-    int cv[kJ];
-#pragma unroll
-    for (int t = 0; t < kJ; t++) {
-        const int j = lane + 64 * t;
-        cv[t] = j < nb ? cnt[j] : 0;
-        sa[t] = (ia < nb && j < nb) ? S[(size_t)ia * nb + j] : 0.f;
-        sb[t] = (ib < nb && j < nb) ? S[(size_t)ib * nb + j] : 0.f;
-    }
-    const float ma = ia < nb ? p.rowmax[(size_t)bh * nb + ia] : 0.f;
-    const float mb = ib < nb ? p.rowmax[(size_t)bh * nb + ib] : 0.f;
-    float la = 0.f, lb = 0.f;
-#pragma unroll
-    for (int t = 0; t < kJ; t++) {
-        const int j = lane + 64 * t;
-        if (j < nb) {
-            const float wa = ia < nb ? lowres_weight(sa[t], ma, cv[t]) : 0.f;
-            const float wb = ib < nb ? lowres_weight(sb[t], mb, cv[t]) : 0.f;
-            wl[(2 * wave) * nbp + j] = wa;
-            wl[(2 * wave + 1) * nbp + j] = wb;
-            la += wa;
-            lb += wb;
+        for (int e = 0; e < kVLoads; e++) {
+            const int x = tid + e * kSelThreads, j = j0 + x / (HD / 4);
+            vv[e] = j < nb ? *reinterpret_cast<const float4*>(vh + (size_t)j * HD + (x % (HD / 4)) * 4)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
         }
-    }
-    la = wave_sum(la);
-    lb = wave_sum(lb);
-    if (lane == 0) {
-        if (ia < nb) p.ll_all[(size_t)bh * nb + ia] = la;
-        if (ib < nb) p.ll_all[(size_t)bh * nb + ib] = lb;
-    }
-    // wave w: row tile w / 8, 16-channel tiles c = (w / 2) % 4 + 4 x (x < HD / 64),
-    // key half w % 2
-    const int rt = wave >> 3, ct = (wave >> 1) & 3, kh2 = wave & 1;
+#pragma unroll
+        for (int m = 0; m < kM; m++) {
+            const int j = j0 + kq + 16 * m;
+            cv[m] = j < nb ? cnt[j] : 0;
+            sv[m] = (rok && j < nb) ? S[(size_t)row * nb + j] : 0.f;
+        }
+    };
+    fetch(0);
+    const float mrow = rok ? p.rowmax[(size_t)bh * nb + row] : 0.f;
+    float lsum = 0.f;
+    // wave w: row tile w / 4, 16-channel tiles w % 4 + 4 x
+    const int rt = wave >> 2, ct = wave & 3;
     typedef float f32x4 __attribute__((ext_vector_type(4)));
     f32x4 acc[kCTW];
 #pragma unroll
     for (int x = 0; x < kCTW; x++) acc[x] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int j0 = 0; j0 < nb; j0 += kKT) {
-        __syncthreads();   // the weights are in place; every wave is done with the previous tile
+        __syncthreads();   // every wave is done with the previous tile
+#pragma unroll
+        for (int m = 0; m < kM; m++) {
+            const int j = j0 + kq + 16 * m;
+            const float w = (rok && j < nb) ? lowres_weight(sv[m], mrow, cv[m]) : 0.f;
+            wl[r * kWS + kq + 16 * m] = w;
+            lsum += w;
+        }
 #pragma unroll
         for (int e = 0; e < kVLoads; e++) {
             const int x = tid + e * kSelThreads;
             *reinterpret_cast<float4*>(vt + (x / (HD / 4)) * kVtStride + (x % (HD / 4)) * 4) = vv[e];
         }
         __syncthreads();
-        if (j0 + kKT < nb) {
+        if (j0 + kKT < nb) fetch(j0 + kKT);   // in flight during this tile
+        const float* wa = wl + (rt * 16 + (lane & 15)) * kWS + (lane >> 4);
+        const float* vb = vt + (lane >> 4) * kVtStride + ct * 16 + (lane & 15);
 #pragma unroll
-            for (int e = 0; e < kVLoads; e++) {
-                const int x = tid + e * kSelThreads, j = j0 + kKT + x / (HD / 4);
-                vv[e] = j < nb ? *reinterpret_cast<const float4*>(vh + (size_t)j * HD + (x % (HD / 4)) * 4)
-                               : make_float4(0.f, 0.f, 0.f, 0.f);
-            }
-        }
-        const int jn = min(kKT, nb - j0);
+        for (int k4 = 0; k4 < kKT; k4 += 4) {
+            const float a = wa[k4];
 #pragma unroll
-        for (int k4 = 0; k4 < kKT / 2; k4 += 4) {
-            const int k = kh2 * (kKT / 2) + k4 + (lane >> 4);
-            const bool ok = k < jn;
-            const float a = ok ? wl[(rt * 16 + (lane & 15)) * nbp + j0 + k] : 0.f;
-#pragma unroll
-            for (int x = 0; x < kCTW; x++) {
-                const float bv = ok ? vt[k * kVtStride + (ct + 4 * x) * 16 + (lane & 15)] : 0.f;
-                acc[x] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, acc[x], 0, 0, 0);
-            }
+            for (int x = 0; x < kCTW; x++)
+                acc[x] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, vb[k4 * kVtStride + 64 * x], acc[x], 0, 0, 0);
         }
     }
+    // the row's weight sum over its 16 threads (lanes 16 (l / 16) .. + 15 of the wave)
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) lsum += __shfl_xor(lsum, o, 16);
+    if (kq == 0 && rok) p.ll_all[(size_t)bh * nb + row] = lsum;
 #pragma unroll
     for (int x = 0; x < kCTW; x++) {
-        const int tile = rt * 4 + ct + 8 * x;   // 0 .. 8 kCTW - 1
-        if (kh2 == 1) *reinterpret_cast<f32x4*>(red + (tile * 64 + lane) * 4) = acc[x];
-    }
-    __syncthreads();
-    if (kh2 == 0) {
 #pragma unroll
-        for (int x = 0; x < kCTW; x++) {
-            const int tile = rt * 4 + ct + 8 * x;
-            const f32x4 o = *reinterpret_cast<const f32x4*>(red + (tile * 64 + lane) * 4);
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int row = row0 + rt * 16 + 4 * (lane >> 4) + e;
-                if (row < nb)
-                    p.lo_all[((size_t)bh * nb + row) * HD + (ct + 4 * x) * 16 + (lane & 15)] = acc[x][e] + o[e];
-            }
+        for (int e = 0; e < 4; e++) {
+            const int orow = row0 + rt * 16 + 4 * (lane >> 4) + e;
+            if (orow < nb) p.lo_all[((size_t)bh * nb + orow) * HD + (ct + 4 * x) * 16 + (lane & 15)] = acc[x][e];
         }
     }
 }
