@@ -851,29 +851,41 @@ __device__ __forceinline__ void emit_stream(const Params& p, int bh, const uint3
     uint32_t* gbits = p.selbits + (size_t)bh * nb * words;
     for (int x = tid; x < nb * words; x += kSelThreads) gbits[x] = bitmap[x];
     // column lists and the attention stream records: one thread per bitmap
-    // word (x = i * words + w), for the set bits of that word in order; the
-    // k-th of them is cell rc[i] + wp[x] + k of the stream.
+    // word (x = i * words + w), or per half of one (hf) when the halves
+    // still fit the workgroup, for its set bits in order; the k-th set bit
+    // of word x is cell rc[i] + wp[x] + k of the stream.
     int32_t* col = p.col + (size_t)bh * p.K;
     BlkRec* recs = p.recs + (size_t)bh * p.K;
     const int tcap = (int)min((int64_t)rc[nb], p.K);
-    for (int x = tid; x < nb * words; x += kSelThreads) {
-        uint32_t bits = bitmap[x];
+    const int halves = 2 * nb * words <= kSelThreads ? 1 : 0;
+    for (int hx = tid; hx < (nb * words) << halves; hx += kSelThreads) {
+        const int x = hx >> halves, hf = hx & halves;
+        const uint32_t word = bitmap[x];
+        uint32_t bits = halves ? (hf ? word >> 16 : word & 0xFFFFu) : word;
         if (bits == 0u) continue;
         const int i = x / words, w = x - i * words;
         const int o = rc[i], n = rc[i + 1] - o;
-        const int ch = row_seg_len(n, p.seg_whole, p.chunk), nit = (n + ch - 1) / ch;
-        int rank = wp[x];
+        const int ch = row_seg_len(n, p.seg_whole, p.chunk);
+        const bool whole = n <= ch;
+        const int rank0 = wp[x] + (hf ? __popc(word & 0xFFFFu) : 0);
+        // the first bit's segment and position; later bits step them
+        int sg = rank0 / ch, pos = rank0 - sg * ch;
+        int item = ic[i] + sg, len = min(ch, n - sg * ch);
+        int e = o + rank0;
         while (bits != 0u) {
-            const int j = w * 32 + __builtin_ctz(bits);
+            const int j = w * 32 + 16 * hf + __builtin_ctz(bits);
             bits &= bits - 1u;
-            const int e = o + rank;
             if (e < tcap) {
                 col[e] = j;
-                const int sg = rank / ch;
-                recs[e] = BlkRec{rec_ij(i, j), mbv[j], 0u,
-                                 rec_info(ic[i] + sg, rank - sg * ch, min(ch, n - sg * ch), nit == 1)};
+                recs[e] = BlkRec{rec_ij(i, j), mbv[j], 0u, rec_info(item, pos, len, whole)};
             }
-            rank++;
+            e++;
+            if (++pos == ch) {
+                pos = 0;
+                item++;
+                sg++;
+                len = min(ch, n - sg * ch);
+            }
         }
     }
 }
