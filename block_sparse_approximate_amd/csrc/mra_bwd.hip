@@ -214,6 +214,22 @@ __device__ __forceinline__ bool head_slot(int BH, int per_head, int* bh, int* id
     return *bh < BH;
 }
 
+// The same grid for the chunk kernels, with the heads of an XCD interleaved:
+// its workgroups take chunk group idx of each of its heads in turn, so that
+// every head's first (longest) chunks start in the first round.
+__device__ __forceinline__ bool head_slot_interleaved(int BH, int per_head, int* bh, int* idx) {
+    if (BH >= 8) {
+        const int hpx = (BH + 7) / 8;
+        const int xcd = blockIdx.x & 7, k = blockIdx.x >> 3, hl = k % hpx;
+        *bh = xcd + 8 * hl;
+        *idx = k / hpx;
+    } else {
+        *bh = blockIdx.x % BH;
+        *idx = blockIdx.x / BH;
+    }
+    return *bh < BH && *idx < per_head;
+}
+
 inline unsigned head_grid(int BH, int per_head) {
     return (unsigned)(BH >= 8 ? 8 * (int64_t)((BH + 7) / 8) * per_head : (int64_t)BH * per_head);
 }
@@ -313,14 +329,49 @@ __global__ __launch_bounds__(kTrThreads) void plan_kernel(Params p) {
     int4* rch = p.bwd_rch + (size_t)bh * maxch;
     int4* cch = p.bwd_cch + (size_t)bh * maxch;
     int* cstart = reinterpret_cast<int*>(cbits + nb * words);
+    // The chunk lists go longest first (the chunk kernels' waves take them
+    // in list order, so the long ones start in the first round and the
+    // short ones fill in behind them): a count of chunks per length, its
+    // scan from the longest length down, then each thread's chunks placed
+    // in their length's range.  A chunk keeps its partial slot (slot = its
+    // index among its row's or column's chunks, from rbase / cbase), so the
+    // order changes only which wave computes it when.
+    __shared__ int lcnt[2][kChunkB + 1], lnext[2][kChunkB + 1];
+    if (x < 2 * (kChunkB + 1)) (&lcnt[0][0])[x] = 0;
+    __syncthreads();
+    const int rlast = on ? (e1 - e0) - kChunkB * (nr - 1) : 0;   // length of the row's last chunk
+    const int clast = on ? ccount - kChunkB * (nc - 1) : 0;
+    if (on) {
+        if (nr > 1) atomicAdd(&lcnt[0][kChunkB], nr - 1);
+        atomicAdd(&lcnt[0][rlast], 1);
+        if (nc > 1) atomicAdd(&lcnt[1][kChunkB], nc - 1);
+        atomicAdd(&lcnt[1][clast], 1);
+    }
+    __syncthreads();
+    if (x < 2) {
+        int acc = 0;
+        for (int L = kChunkB; L >= 0; L--) {
+            lnext[x][L] = acc;
+            acc += lcnt[x][L];
+        }
+    }
+    __syncthreads();
     if (on) {
         cptr[x] = cpos;
         cstart[x] = cpos;
-        for (int c = 0; c < nr && rbase + c < maxch; c++)
-            rch[rbase + c] = make_int4(x, e0 + c * kChunkB, min(e0 + (c + 1) * kChunkB, e1), nr > 1 ? rbase + c : -1);
+        const int rf = nr > 1 ? atomicAdd(&lnext[0][kChunkB], nr - 1) : 0, rl = atomicAdd(&lnext[0][rlast], 1);
+        for (int c = 0; c < nr; c++) {
+            const int at = c + 1 < nr ? rf + c : rl;
+            if (at < maxch)
+                rch[at] = make_int4(x, e0 + c * kChunkB, min(e0 + (c + 1) * kChunkB, e1), nr > 1 ? rbase + c : -1);
+        }
         const int c0 = cpos, c1 = min(cpos + ccount, K);
-        for (int c = 0; c < nc && cbase + c < maxch; c++)
-            cch[cbase + c] = make_int4(x, c0 + c * kChunkB, min(c0 + (c + 1) * kChunkB, c1), nc > 1 ? cbase + c : -1);
+        const int cf = nc > 1 ? atomicAdd(&lnext[1][kChunkB], nc - 1) : 0, cl = atomicAdd(&lnext[1][clast], 1);
+        for (int c = 0; c < nc; c++) {
+            const int at = c + 1 < nc ? cf + c : cl;
+            if (at < maxch)
+                cch[at] = make_int4(x, c0 + c * kChunkB, min(c0 + (c + 1) * kChunkB, c1), nc > 1 ? cbase + c : -1);
+        }
         if (nr > 1) p.bwd_rmul[(size_t)bh * nb + rm] = make_int4(x, rbase, nr, 0);
         if (nc > 1) p.bwd_cmul[(size_t)bh * nb + cm] = make_int4(x, cbase, nc, 0);
     }
@@ -589,7 +640,7 @@ __global__ __launch_bounds__(64 * chunk_waves(HD)) void dq_kernel(Params p) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nb = p.nb, maxch = p.bwd_maxch;
     int bh, wg;
-    if (!head_slot(p.BH, (maxch + kWaves - 1) / kWaves, &bh, &wg)) return;
+    if (!head_slot_interleaved(p.BH, (maxch + kWaves - 1) / kWaves, &bh, &wg)) return;
     const int cid = wg * kWaves + wave;
     if (cid >= p.bwd_count[bh].x) return;
     const int4 dsc = p.bwd_rch[(size_t)bh * maxch + cid];
@@ -681,7 +732,7 @@ __global__ __launch_bounds__(64 * chunk_waves(HD)) void dkv_kernel(Params p) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nb = p.nb, maxch = p.bwd_maxch;
     int bh, wg;
-    if (!head_slot(p.BH, (maxch + kWaves - 1) / kWaves, &bh, &wg)) return;
+    if (!head_slot_interleaved(p.BH, (maxch + kWaves - 1) / kWaves, &bh, &wg)) return;
     const int cid = wg * kWaves + wave;
     if (cid >= p.bwd_count[bh].y) return;
     const int4 dsc = p.bwd_cch[(size_t)bh * maxch + cid];
@@ -714,9 +765,11 @@ __global__ __launch_bounds__(64 * chunk_waves(HD)) void dkv_kernel(Params p) {
         sl = p.st_linv[t];
         sd = p.st_d[t];
     };
-    if (c0 < c1) fetch(c0);
-    stage<HD>(ks, static_cast<const uint16_t*>(p.k) + coloff, lane);
-    stage<HD>(vs, static_cast<const uint16_t*>(p.v) + coloff, lane);
+    if (c0 < c1) {   // a column with no selected row needs neither its K nor its V
+        fetch(c0);
+        stage<HD>(ks, static_cast<const uint16_t*>(p.k) + coloff, lane);
+        stage<HD>(vs, static_cast<const uint16_t*>(p.v) + coloff, lane);
+    }
     const bool kvalid = (p.mbits[(size_t)b * nb + j] >> n) & 1u;   // lane = key n
 
     f32x16 dk[kMT], dv[kMT];
@@ -850,7 +903,7 @@ __global__ __launch_bounds__(64) void dq32_kernel(Params p) {
     const int lane = threadIdx.x & 63;
     const int nb = p.nb, maxch = p.bwd_maxch;
     int bh, cid;
-    if (!head_slot(p.BH, maxch, &bh, &cid)) return;
+    if (!head_slot_interleaved(p.BH, maxch, &bh, &cid)) return;
     if (cid >= p.bwd_count[bh].x) return;
     const int4 dsc = p.bwd_rch[(size_t)bh * maxch + cid];
     const int i = min(max(dsc.x, 0), nb - 1), b = bh / p.H;
@@ -921,7 +974,7 @@ __global__ __launch_bounds__(64) void dkv32_kernel(Params p) {
     const int lane = threadIdx.x & 63;
     const int nb = p.nb, maxch = p.bwd_maxch;
     int bh, cid;
-    if (!head_slot(p.BH, maxch, &bh, &cid)) return;
+    if (!head_slot_interleaved(p.BH, maxch, &bh, &cid)) return;
     if (cid >= p.bwd_count[bh].y) return;
     const int4 dsc = p.bwd_cch[(size_t)bh * maxch + cid];
     const int j = min(max(dsc.x, 0), nb - 1), b = bh / p.H;
