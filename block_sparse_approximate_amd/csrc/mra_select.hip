@@ -1293,7 +1293,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
     const int nb = p.nb;
     // workgroups [0, BH_pad) select, one per head (BH_pad = BH rounded up to
     // a multiple of 8, so workgroup bh runs on XCD bh % 8); in full mode the
-    // rest sum the low-res attention of 32 rows each, placed on the XCD of
+    // rest sum the low-res attention of kLoRows rows each, placed on the XCD of
     // their head
     const int bh_pad = 8 * ((p.BH + 7) / 8);
     const int tiles = row_tiled(nb) ? nb / kTileRows : 1;   // selecting workgroups per head
