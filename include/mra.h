@@ -188,7 +188,7 @@ mra_status mra_attention_fwd(const mra_dims* dims, const void* q, const void* k,
  * is a fixed 64 MiB device array inside the library, one copy per GPU, held
  * until the process ends; the call allocates nothing.  Sizes whose
  * mra_workspace_size exceeds 64 MiB return MRA_ERR_SCRATCH (B=2, H=12,
- * N=4096 full mode needs 58.8 MiB).  Every call on one GPU shares that GPU's
+ * N=4096 full mode needs 57.9 MiB).  Every call on one GPU shares that GPU's
  * array, so calls that overlap in time on one GPU (other streams, other
  * threads) race and must be serialised by the caller; each call clears what
  * it needs cleared.  Its device error word is not exposed.  Other arguments
