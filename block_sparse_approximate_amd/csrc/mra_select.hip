@@ -54,6 +54,7 @@ constexpr int kTileCells = kSelThreads * kCells;   // 16384
 constexpr int kCap = kSelCap;                      // selection candidates held in LDS
 constexpr int kDigitBits = 8;                      // radix digit over the candidates
 constexpr int kDigitBins = 1 << kDigitBits;
+constexpr int kRankSet = 64;                       // candidates few enough to be ranked pairwise
 
 __host__ __device__ inline size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
 
@@ -152,6 +153,29 @@ __device__ __forceinline__ uint32_t wave_scan_incl(uint32_t x) {
 __device__ __forceinline__ uint64_t wave_scan_incl(uint64_t x) {
     const uint32_t lo = wave_scan_incl((uint32_t)x), hi = wave_scan_incl((uint32_t)(x >> 32));
     return ((uint64_t)hi << 32) | lo;
+}
+
+// Lane E of `old` takes the wave-uniform value v (v_writelane_b32).  The
+// compiler does not look into the asm for hazards, so it waits itself: five
+// wait states cover an SGPR or EXEC written by the VALU just before (two and
+// four needed) and a previous write of `old` by v_writelane.
+template <int E>
+__device__ __forceinline__ uint32_t write_lane(uint32_t old, uint32_t v) {
+    asm("s_nop 4\n\tv_writelane_b32 %0, %1, %2" : "+v"(old) : "s"(v), "n"(E));
+    return old;
+}
+
+// f(IntC<E>{}) for E = B .. N - 1, each E a compile-time constant.
+template <int V>
+struct IntC {
+    static constexpr int value = V;
+};
+template <int B, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < N) {
+        f(IntC<B>{});
+        static_for<B + 1, N>(f);
+    }
 }
 
 // Max and sum over the 64 lanes of a wave by DPP (the result in every lane).
@@ -902,9 +926,11 @@ __device__ __forceinline__ BinPick pick_bin_wave(const uint32_t* h, uint32_t nee
         const int lane = threadIdx.x;
         const uint4* hv = reinterpret_cast<const uint4*>(h + (63 - lane) * kPer);
         uint32_t local = 0;
+        // lane l starts its range at quad l % 16, so that the lanes of one
+        // read fall on different LDS banks
 #pragma unroll
         for (int e = 0; e < kPer / 4; e++) {
-            const uint4 c = hv[e];
+            const uint4 c = hv[(e + lane) & (kPer / 4 - 1)];
             local += c.x + c.y + c.z + c.w;
         }
         const uint32_t above = wave_scan_incl(local) - local;
@@ -945,8 +971,6 @@ __device__ __forceinline__ int nth_set_bit(uint64_t m, uint32_t n) {
     return pos;
 }
 
-constexpr int kRankSet = 64;   // candidates few enough to be ranked pairwise
-
 // The threshold key T: the need-th largest of the candidates whose top pbits
 // key bits are `prefix`.  While more than kRankSet of them remain, digit
 // passes narrow the prefix (every thread adds its candidates to a 256-bin
@@ -963,9 +987,26 @@ __device__ __forceinline__ uint64_t threshold_key(const uint64_t* cand, uint32_t
         const int db = (64 - pbits) < kDigitBits ? (64 - pbits) : kDigitBits;
         if (tid < kDigitBins) dig[tid] = 0u;
         __syncthreads();
-        for (uint32_t c = tid; c < ncand; c += kSelThreads) {
-            const uint64_t k64 = cand[c];
-            if (matches(k64)) atomicAdd(&dig[(uint32_t)((k64 >> (64 - pbits - db)) & ((1ull << db) - 1))], 1u);
+        for (uint32_t c0 = 0; c0 < ncand; c0 += kSelThreads) {
+            const uint32_t c = c0 + tid;
+            bool hit = false;
+            uint32_t dg = 0;
+            if (c < ncand) {
+                const uint64_t k64 = cand[c];
+                hit = matches(k64);
+                dg = (uint32_t)((k64 >> (64 - pbits - db)) & ((1ull << db) - 1));
+            }
+            // a wave whose hits share one digit (tie-heavy scores) adds them
+            // with one atomic instead of one per lane on the same bin
+            const uint64_t m = __ballot(hit);
+            if (m) {
+                const uint32_t d0 = (uint32_t)__builtin_amdgcn_readlane((int)dg, __builtin_ctzll(m));
+                if (__ballot(hit && dg != d0) == 0) {
+                    if (lane == 0) atomicAdd(&dig[d0], (uint32_t)__popcll(m));
+                } else if (hit) {
+                    atomicAdd(&dig[dg], 1u);
+                }
+            }
         }
         __syncthreads();
         if (tid < 64) {
@@ -1032,55 +1073,62 @@ __device__ __forceinline__ uint64_t threshold_key(const uint64_t* cand, uint32_t
     return ((uint64_t)small[20] << 32) | small[21];
 }
 
-// The marking pass of select_rows over every cell of a one-tile head (kv:
-// the thread's cell keys, cell tid + e * kSelThreads in kv[e]; a wave's 64
-// consecutive cells, group g = e * kSelWaves + wave, lie in one block row).
-// Cells whose key prefix is above `prefix` are selected for sure: their
-// count goes to gcnt[g], and the workgroup's own rows (row0 .. + kTileRows)
-// get their bitmap words.  Cells whose prefix equals it are candidates: each
-// wave places its own with one LDS atomic on small[8].  kNarrow: the prefix
-// has at most 32 bits (a prefix of the score key alone).
-template <bool kNarrow>
-__device__ __forceinline__ void mark_groups(const uint32_t (&kv)[kCells], uint32_t ncell, int lnb, int nb, int words,
-                                            int row0, uint64_t prefix, int pbits, uint32_t* gcnt, uint32_t* bitmap,
-                                            uint64_t* cand, uint32_t* small) {
+// The marking pass of select_rows over every cell of a one-tile head of
+// 1 << kLnb block rows (kv: the thread's cell keys, cell tid + e * kSelThreads
+// in kv[e]; a wave's 64 consecutive cells, group g = e * kSelWaves + wave, lie
+// in one block row).  Cells whose key prefix is above `prefix` are selected
+// for sure: their count goes to gcnt[g], and the workgroup's own rows (row0 ..
+// + kTileRows) get their bitmap words.  Cells whose prefix equals it are
+// candidates: each wave places its own with one LDS atomic on small[8].
+// kNarrow: the prefix has at most 32 bits (a prefix of the score key alone).
+// Per group the loop only takes the two ballots: the sure-cell ballot goes
+// into lane e of two registers, and after the loop each lane e < kCells
+// counts and stores group e's, so that the scalar unit, which the 16 waves
+// of the workgroup share, does one popcount per group.
+template <bool kNarrow, int kLnb>
+__device__ __forceinline__ void mark_groups(const uint32_t (&kv)[kCells], int words, int row0, uint64_t prefix,
+                                            int pbits, uint32_t* gcnt, uint32_t* bitmap, uint64_t* cand,
+                                            uint32_t* small) {
+    constexpr int kNb = 1 << kLnb;
+    constexpr int kE = kNb * kNb / kSelThreads < kCells ? kNb * kNb / kSelThreads : kCells;   // groups with cells
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint32_t wbase = (uint32_t)__builtin_amdgcn_readfirstlane((int)threadIdx.x - lane);
     const uint64_t lt_mask = (1ull << lane) - 1ull;
+    // narrow prefix: top = key >> sh is above p32 when key > hi, and equal
+    // to it when key >= lo and not above
     const uint32_t sh = kNarrow ? (uint32_t)(32 - pbits) : 0u, p32 = (uint32_t)prefix;
-    // the groups of the workgroup's rows: e in [e_own, e_own + kTileRows * nb / kSelThreads)
-    const uint32_t own_lo = (uint32_t)row0 << lnb, own_hi = own_lo + ((uint32_t)kTileRows << lnb);
-    uint64_t mh[kCells];
-    uint32_t mys = 0, tot = 0;
-#pragma unroll
-    for (int e = 0; e < kCells; e++) {
-        const uint32_t x0 = (uint32_t)e * kSelThreads + wbase;
-        uint64_t ms = 0, mhe = 0;
-        if (x0 < ncell) {
-            if constexpr (kNarrow) {
-                const uint32_t top = kv[e] >> sh;
-                ms = __ballot(top > p32);
-                mhe = __ballot(top == p32);
-            } else {
-                const uint64_t top = cell_key64(kv[e], x0 + lane) >> (64 - pbits);
-                ms = __ballot(top > prefix);
-                mhe = __ballot(top == prefix);
-            }
-            if (x0 - own_lo < own_hi - own_lo && lane == 0)
-                *reinterpret_cast<uint2*>(bitmap + ((x0 - own_lo) >> lnb) * words + ((x0 & (uint32_t)(nb - 1)) >> 5)) =
-                    make_uint2((uint32_t)ms, (uint32_t)(ms >> 32));
+    const uint32_t lo = kNarrow ? p32 << sh : 0u;
+    const uint32_t hi = kNarrow ? (uint32_t)((((uint64_t)p32 + 1u) << sh) - 1u) : 0u;
+    uint64_t mh[kE];
+    uint32_t s_lo = 0u, s_hi = 0u, tot = 0;
+    static_for<0, kE>([&](auto ec) {
+        constexpr int e = decltype(ec)::value;
+        uint64_t ms;
+        if constexpr (kNarrow) {
+            ms = __ballot(kv[e] > hi);
+            mh[e] = __ballot(kv[e] >= lo) & ~ms;
+        } else {
+            const uint64_t top = cell_key64(kv[e], (uint32_t)e * kSelThreads + wbase + lane) >> (64 - pbits);
+            ms = __ballot(top > prefix);
+            mh[e] = __ballot(top == prefix);
         }
-        mh[e] = mhe;
-        tot += (uint32_t)__popcll(mhe);
-        mys = lane == e ? (uint32_t)__popcll(ms) : mys;
+        s_lo = write_lane<e>(s_lo, (uint32_t)ms);
+        s_hi = write_lane<e>(s_hi, (uint32_t)(ms >> 32));
+        tot += (uint32_t)__popcll(mh[e]);
+    });
+    if (lane < kCells) {
+        gcnt[lane * kSelWaves + wave] = (uint32_t)(__popc(s_lo) + __popc(s_hi));   // 0 past the head's cells
+        const uint32_t x0 = (uint32_t)lane * kSelThreads + wbase;
+        const uint32_t r = (x0 >> kLnb) - (uint32_t)row0;
+        if (r < (uint32_t)kTileRows)
+            *reinterpret_cast<uint2*>(bitmap + r * words + ((x0 & (uint32_t)(kNb - 1)) >> 5)) = make_uint2(s_lo, s_hi);
     }
-    if (lane < kCells) gcnt[lane * kSelWaves + wave] = mys;
     if (tot) {
         uint32_t at = 0;
         if (lane == 0) at = atomicAdd(&small[8], tot);
         at = (uint32_t)__builtin_amdgcn_readfirstlane((int)at);
 #pragma unroll
-        for (int e = 0; e < kCells; e++) {
+        for (int e = 0; e < kE; e++) {
             if (mh[e]) {
                 if ((mh[e] >> lane) & 1ull) {
                     const uint32_t pos = at + (uint32_t)__popcll(mh[e] & lt_mask);
@@ -1168,11 +1216,13 @@ __device__ __forceinline__ void select_rows(const Params& p, int bh, int t, unsi
     // bin are selected for sure (their count per group, and this workgroup's
     // rows' bitmap words); cells inside it are candidates, placed in the list
     // with one LDS atomic per wave.
-    const uint32_t wbase = (uint32_t)__builtin_amdgcn_readfirstlane(tid - lane);
-    if (pbits <= 32)
-        mark_groups<true>(kv, ncell, lnb, nb, words, row0, prefix, pbits, gcnt, bitmap, cand, small);
-    else
-        mark_groups<false>(kv, ncell, lnb, nb, words, row0, prefix, pbits, gcnt, bitmap, cand, small);
+    if (lnb == 7) {
+        if (pbits <= 32) mark_groups<true, 7>(kv, words, row0, prefix, pbits, gcnt, bitmap, cand, small);
+        else mark_groups<false, 7>(kv, words, row0, prefix, pbits, gcnt, bitmap, cand, small);
+    } else {
+        if (pbits <= 32) mark_groups<true, 6>(kv, words, row0, prefix, pbits, gcnt, bitmap, cand, small);
+        else mark_groups<false, 6>(kv, words, row0, prefix, pbits, gcnt, bitmap, cand, small);
+    }
     __syncthreads();
     const uint32_t ncand_all = small[8];
     const uint32_t ncand = ncand_all < (uint32_t)kCap ? ncand_all : (uint32_t)kCap;
