@@ -31,7 +31,7 @@ UNITS = {
     "mra_bwd": [],
     "mra_api": [],
 }
-HEADERS = ["mra_common.h", os.path.join("..", "..", "include", "mra.h")]
+HEADERS = ["mra_common.h", "mra_pool_unit.h", os.path.join("..", "..", "include", "mra.h")]
 
 
 def _stale(target: str, deps: list[str]) -> bool:

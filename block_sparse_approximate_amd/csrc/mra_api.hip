@@ -153,6 +153,7 @@ Params make_params(const mra_dims& d, const Layout& L, int32_t mode, int32_t pf,
     p.attn_wph = attn_grid_waves_per_head(L.BH, L.K, L.d);
     p.attn_seq = attn_heads_in_turn(L.BH, L.K, L.d) ? 1 : 0;
     attn_segments(L.BH, L.K, L.d, &p.seg_whole, &p.chunk);
+    p.v_in_logits = v != nullptr && v_pooled_in_logits(mode, L.BH, L.nb) ? 1 : 0;
     p.q = q; p.k = k; p.v = v; p.mask = mask; p.out = out;
     p.qhat = reinterpret_cast<float*>(w + L.qhat);
     p.khat = reinterpret_cast<float*>(w + L.khat);

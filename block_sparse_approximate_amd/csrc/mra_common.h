@@ -83,6 +83,7 @@ struct Params {
     int32_t max_items;
     int32_t seg_whole;     // rows of at most this many selected blocks are one segment
     int32_t chunk;         // longer rows: segments of this many blocks (both kChunkMin..kChunkMax)
+    int32_t v_in_logits;   // 1: full mode's V is pooled by extra workgroups of the logits launch
     const void* q;
     const void* k;
     const void* v;
@@ -211,6 +212,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 namespace mra {
 hipError_t launch_pool(const Params& p, hipStream_t s);
 hipError_t launch_logits(const Params& p, hipStream_t s);
+bool v_pooled_in_logits(int mode, int BH, int nb);
 hipError_t launch_logits_given(const Params& p, hipStream_t s);
 hipError_t launch_premark(const Params& p, hipStream_t s);
 hipError_t launch_select(const Params& p, hipStream_t s);

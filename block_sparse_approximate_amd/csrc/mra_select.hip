@@ -35,7 +35,7 @@
 // workgroup's output visible to another, with no device-wide fences.
 // The translation unit is built with -ffp-contract=off so that every fp32
 // operation is the one written.
-#include "mra_common.h"
+#include "mra_pool_unit.h"
 
 namespace mra {
 namespace {
@@ -448,6 +448,30 @@ __device__ __forceinline__ void mark_cells_fast(int nb, int words, uint32_t magi
     }
 }
 
+// ---------------------------------------------------------------- V pooling
+// Full mode's V is needed first by the low-res sums in the selector launch,
+// so where the logits workgroups leave CUs free (at most one of them per
+// CU) the logits launch pools V with extra workgroups (g counts them from
+// 0): kVUnitsPerGroup units per workgroup, thread tid in unit tid /
+// kVUnitStride; workgroup g runs on XCD g % 8 with the head's other stages.
+__host__ __device__ inline int v_groups_per_head(int nb, int dt, int hd) {
+    const int units = (nb + v_unit_blocks(dt, hd) - 1) / v_unit_blocks(dt, hd);
+    return (units + kVUnitsPerGroup - 1) / kVUnitsPerGroup;
+}
+
+template <int DT, int HD>
+__device__ __forceinline__ void pool_v(const Params& p, int g, unsigned char* smem) {
+    constexpr int kUB = v_unit_blocks(DT, HD);
+    const int per_head = v_groups_per_head(p.nb, DT, HD);
+    const int xcd = g & 7, slot = g >> 3;
+    const int hm = slot / per_head;
+    const int bh = xcd + 8 * hm;
+    const int unit = (slot - hm * per_head) * kVUnitsPerGroup + (int)threadIdx.x / kVUnitStride;
+    const int blk0 = unit * kUB;
+    pool_unit<DT, HD, kUB>(p, 2, bh, blk0, bh < p.BH && blk0 < p.nb, (int)threadIdx.x % kVUnitStride,
+                           smem + (size_t)((int)threadIdx.x / kVUnitStride) * kVUnitBytes);
+}
+
 // ---------------------------------------------------------------- logits
 // Wave w owns block rows ra = row0 + 2w and rb = ra + 1 of the workgroup's 16;
 // lane l owns key blocks 128 t + l and 128 t + 64 + l of every column tile
@@ -464,6 +488,12 @@ __global__ __launch_bounds__(kLgThreads) void logits_kernel(Params p) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int nb = p.nb;
     const int tiles_per_head = (nb + kRT - 1) / kRT;
+    const int n_lg = 8 * ((p.BH + 7) / 8) * tiles_per_head;   // logits workgroups; V pooling after them
+    if (!kGiven && (int)blockIdx.x >= n_lg) {
+        if (p.dtype == 1) pool_v<1, HD>(p, (int)blockIdx.x - n_lg, smem);
+        else pool_v<0, HD>(p, (int)blockIdx.x - n_lg, smem);
+        return;
+    }
     // workgroup g runs on XCD g % 8; head bh's tiles all go to XCD bh % 8
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int hm = slot / tiles_per_head;
@@ -1613,9 +1643,29 @@ static hipError_t launch_logits_t(const Params& p, hipStream_t s) {
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (a1 != hipSuccess) return a1;
     const int heads_per_xcd = (p.BH + 7) / 8;
-    hipLaunchKernelGGL((logits_kernel<kGiven, HD>), dim3(8 * heads_per_xcd * tiles_per_head), dim3(kLgThreads),
-                       logits_lds(p.nb, HD).total, s, p);
+    int grid = 8 * heads_per_xcd * tiles_per_head;
+    size_t lds = logits_lds(p.nb, HD).total;
+    if (!kGiven && p.v_in_logits) {
+        grid += 8 * heads_per_xcd * v_groups_per_head(p.nb, p.dtype, HD);
+        if (lds < (size_t)kVUnitsPerGroup * kVUnitBytes) lds = (size_t)kVUnitsPerGroup * kVUnitBytes;
+    }
+    hipLaunchKernelGGL((logits_kernel<kGiven, HD>), dim3(grid), dim3(kLgThreads), lds, s, p);
     return hipGetLastError();
+}
+
+// Whether the logits launch pools V: full mode, and its logits workgroups
+// at most one per CU of the device, so that the V workgroups run beside them.
+bool v_pooled_in_logits(int mode, int BH, int nb) {
+    if (mode != 0) return false;
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return false;
+        cus[dev] = n;
+    }
+    return 8 * ((BH + 7) / 8) * ((nb + kRT - 1) / kRT) <= cus[dev];
 }
 
 hipError_t launch_logits(const Params& p, hipStream_t s) {
