@@ -33,7 +33,8 @@ RANKINGS = {"row_normalized": 0, "raw_logits": 1}
 BANDS = {"symmetric": 0, "exact": 1}
 # bits of a workspace's device error word (include/mra.h MRA_DEVERR_*)
 DEVICE_ERRORS = {1: "selector candidate list", 2: "selection or segment count", 4: "attention record window",
-                 8: "backward plan", 16: "forward kept no softmax statistics"}
+                 8: "backward plan", 16: "forward kept no softmax statistics",
+                 32: "selector wait for the head's logits"}
 # When set (environment MRA_CHECK_DEVICE_ERRORS=1, or assigned), every forward
 # and backward call waits for its stream and raises MraDeviceError if a
 # kernel flagged an inconsistency.  Off by default: the check synchronises.

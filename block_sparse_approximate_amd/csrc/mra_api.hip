@@ -655,6 +655,7 @@ MRA_API mra_status mra_debug_select(const mra_dims* dims, const float* logits, c
     if (e == hipSuccess) e = hipMemsetAsync(p.ncand, 0, BH * kCandStride * 4, s);
     if (e == hipSuccess) e = hipMemsetAsync(p.error, 0, 4, s);
     if (e != hipSuccess) return MRA_ERR_HIP;
+    p.logits_given = 1;
     if (launch_logits_given(p, s) != hipSuccess) return MRA_ERR_HIP;
     if (launch_premark(p, s) != hipSuccess) return MRA_ERR_HIP;
     if (launch_select(p, s) != hipSuccess) return MRA_ERR_HIP;

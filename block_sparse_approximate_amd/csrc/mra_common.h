@@ -83,7 +83,10 @@ struct Params {
     int32_t max_items;
     int32_t seg_whole;     // rows of at most this many selected blocks are one segment
     int32_t chunk;         // longer rows: segments of this many blocks (both kChunkMin..kChunkMax)
-    int32_t v_in_logits;   // 1: full mode's V is pooled by extra workgroups of the logits launch
+    int32_t v_in_logits;   // 1: full mode's V is pooled by extra workgroups of the logits launch (of the
+                           //   fused logits and selection launch for N = 2048, 4096)
+    int32_t logits_given;  // 1: the logits are already in `logits` (selector hook); step 1 forms only
+                           //   row maxima, keys and the histogram from them
     const void* q;
     const void* k;
     const void* v;
@@ -117,7 +120,8 @@ struct Params {
     float* park;           // [BH, attn_wph, park_floats(d)] attention: per wave, a piece of a segment
                            //   that another wave of its workgroup finishes
     uint64_t* cand;        // [BH, kSelCap] boundary-bin cells found by the pre-marking pass
-    uint32_t* ncand;       // [BH, kCandStride] their number, in word 0 (cleared by the pooling kernel)
+    uint32_t* ncand;       // [BH, kCandStride] their number, in word 0; in word 1 the count of the head's
+                           //   workgroups whose logits are stored (both cleared by the pooling kernel)
     // backward (mra_attention_bwd)
     const void* fout;      // [B, H, N, d] the forward's output
     const void* dout;      // [B, H, N, d] dL/d out

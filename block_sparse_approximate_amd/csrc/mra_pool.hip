@@ -41,7 +41,11 @@ __global__ __launch_bounds__(kPoolMaxThreads) void pool_kernel(Params p, int nte
             p.error[1] = p.save_stats;   // the backward checks that the statistics were kept
         }
         for (size_t w = gt; w < zero_words; w += stride) p.hist[w] = 0u;
-        if (gt < p.BH) p.ncand[(size_t)gt * kCandStride] = 0u;
+        if (gt < p.BH) {
+            p.ncand[(size_t)gt * kCandStride] = 0u;       // pre-marked candidates
+            p.ncand[(size_t)gt * kCandStride + 1] = 0u;   // workgroups of the head whose logits are stored
+            p.ncand[(size_t)gt * kCandStride + 2] = 0u;   // workgroups of the head whose V pooling is stored
+        }
     }
     // workgroup g runs on XCD g % 8; every workgroup of head bh goes to XCD
     // bh % 8, the XCD whose L2 the later stages of that head use

@@ -28,11 +28,18 @@
 // flight), and wave w's cells of a tile are 64 consecutive cells, so one
 // ballot is 64 consecutive bits of the selection.
 //
+// lgsel_kernel: for heads of 64 or 128 block rows (N = 2048, 4096) the
+// logits and the selection run in one launch: the head's workgroups form 16
+// block rows of logits each, add one to the head's arrival count, and the
+// first nb / 32 of them wait for the count and select 32 rows each as
+// select_kernel's row tiles do (see the comment above lgsel_kernel).
+//
 // premark_kernel: for heads longer than one tile (with nb a multiple of 64)
 // the marking pass runs before the selector, one workgroup per tile, so the
 // selector only loads the bitmap of sure cells and the candidate list.
-// The kernels are separate launches: the kernel boundary is what makes one
-// workgroup's output visible to another, with no device-wide fences.
+// Apart from lgsel_kernel's per-head count, the kernels are separate
+// launches: the kernel boundary is what makes one workgroup's output visible
+// to another, with no device-wide fences.
 // The translation unit is built with -ffp-contract=off so that every fp32
 // operation is the one written.
 #include "mra_pool_unit.h"
@@ -1556,6 +1563,296 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
     emit_stream(p, bh, bitmap, mbv, rc, ic, scan64, reinterpret_cast<uint16_t*>(hist), p.K);
 }
 
+// ---------------------------------------------------------------- logits and selection in one launch
+// One-tile heads (row_tiled(nb): N = 2048 or 4096) run step 1's logits and
+// step 2's selection in one launch, which saves a launch and its ramp between
+// them.  Head bh has nb / kFusedRows workgroups, all on the head's XCD.
+// Workgroup t first forms block rows 16 t .. 16 t + 15 as logits_kernel
+// does (wave w: row 16 t + w; lane l: key blocks l and l + 64): logits, row
+// maxima, keys and the histogram, added into the head's.  Once its stores and
+// adds have completed it adds one to the head's arrival count (ncand word 1).
+// Workgroups t < nb / kTileRows then wait for the count to reach every
+// workgroup of the head and select rows 32 t .. 32 t + 31 (select_rows); in
+// full mode the next ones then sum the low-resolution attention of 64 rows
+// each (lowres_rows); the others end after their logits.
+// What a workgroup stored is in its XCD's L2 once the stores have completed,
+// and the waiting workgroups, on the same XCD, have not read those lines
+// before, so plain loads see it.  An XCD starts its workgroups in slot order
+// and a head's workgroups have consecutive slots, so the heads that wait are
+// complete before later slots need their CUs.  The wait is bounded all the
+// same: after kWaitPolls polls the workgroup sets error bit 32 and goes on.
+constexpr int kFusedRows = kSelWaves;          // block rows per workgroup in the logits phase
+constexpr uint32_t kWaitPolls = 1u << 18;
+constexpr uint32_t kErrWait = 32u;
+
+// The workgroup's stores and atomics have all completed (each thread waits
+// for its own, then the barrier), then one count goes up.
+__device__ __forceinline__ void arrive(uint32_t* count) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__host__ __device__ inline size_t fused_logits_lds(int hd) {
+    return align16((size_t)kFusedRows * hat_stride(hd) * 4) + align16((size_t)kCT * hat_stride(hd) * 4) +
+           kHistBins * 4;
+}
+
+// V pooling without staging (full mode, in lgsel_kernel): lane l of wave w
+// pools channels 2 (l % (HD / 2)) and + 1 of one block, reading its 32 token
+// words straight into registers (a wave's loads of one token are whole
+// 128-byte rows), then sums the valid ones in token order from +0 and divides
+// by the count, as pool_unit does; the block's mask word is the one pooling
+// stored.  Workgroup g pools 16 * 128 / HD consecutive blocks of one head;
+// returns the head, or -1 for a workgroup past the last head.
+__host__ __device__ constexpr int v_direct_blocks(int hd) { return kSelWaves * (128 / hd); }
+__host__ __device__ inline int v_direct_groups(int nb, int hd) {
+    return (nb + v_direct_blocks(hd) - 1) / v_direct_blocks(hd);
+}
+
+template <int DT, int HD>
+__device__ __forceinline__ int pool_v_direct(const Params& p, int g) {
+    constexpr int kPairs = HD / 2;   // lanes per block
+    const int per_head = v_direct_groups(p.nb, HD);
+    const int xcd = g & 7, slot = g >> 3;
+    const int hm = slot / per_head;
+    const int bh = xcd + 8 * hm;
+    if (bh >= p.BH) return -1;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int blk = (slot - hm * per_head) * v_direct_blocks(HD) + wave * (64 / kPairs) + lane / kPairs;
+    const int cp = lane % kPairs;
+    if (blk < p.nb) {
+        const uint32_t bits = p.mbits[(size_t)(bh / p.H) * p.nb + blk];
+        float a0 = 0.0f, a1 = 0.0f;
+        if constexpr (DT == 1) {
+            const uint32_t* src =
+                static_cast<const uint32_t*>(p.v) + ((size_t)bh * p.N + (size_t)blk * kBlock) * kPairs + cp;
+            uint32_t w[kBlock];
+#pragma unroll
+            for (int x = 0; x < kBlock; x++) w[x] = src[(size_t)x * kPairs];
+#pragma unroll
+            for (int x = 0; x < kBlock; x++) {
+                if ((bits >> x) & 1u) {
+                    a0 = a0 + __uint_as_float(w[x] << 16);
+                    a1 = a1 + __uint_as_float(w[x] & 0xFFFF0000u);
+                }
+            }
+        } else {
+            const float2* src =
+                static_cast<const float2*>(p.v) + ((size_t)bh * p.N + (size_t)blk * kBlock) * kPairs + cp;
+            float2 w[kBlock];
+#pragma unroll
+            for (int x = 0; x < kBlock; x++) w[x] = src[(size_t)x * kPairs];
+#pragma unroll
+            for (int x = 0; x < kBlock; x++) {
+                if ((bits >> x) & 1u) {
+                    a0 = a0 + w[x].x;
+                    a1 = a1 + w[x].y;
+                }
+            }
+        }
+        const int count = __popc(bits);
+        const float fc = (float)count;
+        *reinterpret_cast<float2*>(p.vhat + ((size_t)bh * p.nb + blk) * HD + 2 * cp) =
+            count > 0 ? make_float2(a0 / fc, a1 / fc) : make_float2(0.0f, 0.0f);
+    }
+    return bh;
+}
+
+template <bool kGiven, int HD>
+__device__ __forceinline__ void fused_logits(const Params& p, int bh, int row0, unsigned char* smem) {
+    constexpr int kHatStride = hat_stride(HD);
+    constexpr int kKL = kCT * (HD / 4) / kSelThreads;   // float4s of the head's khat per thread (nb <= kCT)
+    const int nb = p.nb;
+    const int b = bh / p.H;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const float tau = (float)(1.0 / __builtin_sqrt((double)p.dscale));
+    float* qS = reinterpret_cast<float*>(smem);
+    float* kS = reinterpret_cast<float*>(smem + align16((size_t)kFusedRows * kHatStride * 4));
+    uint32_t* hist = reinterpret_cast<uint32_t*>(smem + align16((size_t)kFusedRows * kHatStride * 4) +
+                                                 align16((size_t)kCT * kHatStride * 4));
+    const float* qh = p.qhat + (size_t)bh * nb * HD;
+    const float* kh = p.khat + (size_t)bh * nb * HD;
+    const int* cnt = p.cnt + (size_t)b * nb;
+    float* Sg = p.logits + (size_t)bh * nb * nb;
+    // waves 0 .. 7 form the logits (the staged khat is read once per two
+    // rows, which keeps the LDS reads at the pace of the fmas); wave w owns
+    // rows ra = row0 + 2 w and ra + 1, lane l key blocks l and l + 64
+    const bool lw = wave < kFusedRows / 2;
+    const int ra = row0 + 2 * (wave & (kFusedRows / 2 - 1)), rb = ra + 1;   // < nb: nb is a multiple of 16
+    const int j0 = lane, j1 = lane + 64;                                      // j0 < nb always (nb >= 64)
+
+    // every global load of the prologue first, then the LDS stores
+    float4 qv = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 kv[kKL];
+    float sc[4] = {0.f, 0.f, 0.f, 0.f};   // logits of (ra, j0), (ra, j1), (rb, j0), (rb, j1)
+    if (!kGiven) {
+        if (tid < kFusedRows * HD / 4) {
+            const int r = tid / (HD / 4), c4 = (tid % (HD / 4)) * 4;
+            qv = *reinterpret_cast<const float4*>(qh + (size_t)(row0 + r) * HD + c4);
+        }
+#pragma unroll
+        for (int e = 0; e < kKL; e++) {
+            const int x = tid + e * kSelThreads, jj = x / (HD / 4), c4 = (x % (HD / 4)) * 4;
+            kv[e] = jj < nb ? *reinterpret_cast<const float4*>(kh + (size_t)jj * HD + c4)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    } else if (lw) {
+        sc[0] = Sg[(size_t)ra * nb + j0];
+        sc[1] = j1 < nb ? Sg[(size_t)ra * nb + j1] : 0.f;
+        sc[2] = Sg[(size_t)rb * nb + j0];
+        sc[3] = j1 < nb ? Sg[(size_t)rb * nb + j1] : 0.f;
+    }
+    const int c0 = cnt[j0];
+    const int c1 = j1 < nb ? cnt[j1] : 0;
+    const int cia = cnt[ra], cib = cnt[rb];
+    for (int x = tid; x < kHistBins; x += kSelThreads) hist[x] = 0u;
+    if (!kGiven) {
+        if (tid < kFusedRows * HD / 4) {
+            const int r = tid / (HD / 4), c4 = (tid % (HD / 4)) * 4;
+            *reinterpret_cast<float4*>(qS + r * kHatStride + c4) = qv;
+        }
+#pragma unroll
+        for (int e = 0; e < kKL; e++) {
+            const int x = tid + e * kSelThreads;
+            *reinterpret_cast<float4*>(kS + (x / (HD / 4)) * kHatStride + (x % (HD / 4)) * 4) = kv[e];
+        }
+    }
+    __syncthreads();
+
+    if (lw) {
+        // the lane's four logits, each an fma chain over the channels in order
+        if (!kGiven) {
+            const float* qa = qS + (ra - row0) * kHatStride;
+            const float* qb = qa + kHatStride;
+            const float* k0 = kS + j0 * kHatStride;
+            const float* k1 = kS + j1 * kHatStride;
+            float a00 = 0.f, a01 = 0.f, a10 = 0.f, a11 = 0.f;
+#pragma unroll 4
+            for (int c = 0; c < HD; c += 4) {
+                const float4 x0 = *reinterpret_cast<const float4*>(k0 + c);
+                const float4 x1 = *reinterpret_cast<const float4*>(k1 + c);
+                const float4 ya = *reinterpret_cast<const float4*>(qa + c);
+                const float4 yb = *reinterpret_cast<const float4*>(qb + c);
+                a00 = __builtin_fmaf(ya.x, x0.x, a00);
+                a01 = __builtin_fmaf(ya.x, x1.x, a01);
+                a10 = __builtin_fmaf(yb.x, x0.x, a10);
+                a11 = __builtin_fmaf(yb.x, x1.x, a11);
+                a00 = __builtin_fmaf(ya.y, x0.y, a00);
+                a01 = __builtin_fmaf(ya.y, x1.y, a01);
+                a10 = __builtin_fmaf(yb.y, x0.y, a10);
+                a11 = __builtin_fmaf(yb.y, x1.y, a11);
+                a00 = __builtin_fmaf(ya.z, x0.z, a00);
+                a01 = __builtin_fmaf(ya.z, x1.z, a01);
+                a10 = __builtin_fmaf(yb.z, x0.z, a10);
+                a11 = __builtin_fmaf(yb.z, x1.z, a11);
+                a00 = __builtin_fmaf(ya.w, x0.w, a00);
+                a01 = __builtin_fmaf(ya.w, x1.w, a01);
+                a10 = __builtin_fmaf(yb.w, x0.w, a10);
+                a11 = __builtin_fmaf(yb.w, x1.w, a11);
+            }
+            sc[0] = a00 * tau;
+            sc[1] = a01 * tau;
+            sc[2] = a10 * tau;
+            sc[3] = a11 * tau;
+        }
+
+        // the row maxima over non-empty key blocks (exact), then scores, keys
+        // and the histogram of their top 12 bits
+        float ma = -__builtin_inff(), mb = -__builtin_inff();
+        if (c0 > 0) {
+            ma = fmaxf(ma, sc[0]);
+            mb = fmaxf(mb, sc[2]);
+        }
+        if (c1 > 0) {
+            ma = fmaxf(ma, sc[1]);
+            mb = fmaxf(mb, sc[3]);
+        }
+        ma = wave_max(ma);
+        mb = wave_max(mb);
+        uint32_t* Kg = p.keys + (size_t)bh * nb * nb;
+        const int pf = p.prior_first, pd = p.prior_diag;
+        const bool raw = p.rank_raw != 0, exact = p.band_exact != 0;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int i = q < 2 ? ra : rb, j = (q & 1) ? j1 : j0;
+            if (j < nb) {
+                const float sv = sc[q];
+                if (!kGiven) Sg[(size_t)i * nb + j] = sv;
+                const float s = cell_score(sv, q < 2 ? ma : mb, i, j, (q < 2 ? cia : cib) > 0,
+                                           ((q & 1) ? c1 : c0) > 0, pf, pd, raw, exact);
+                const uint32_t key = float_key(s);
+                Kg[(size_t)i * nb + j] = key;
+                atomicAdd(&hist[key >> (32 - kHistBits)], 1u);
+            }
+        }
+        if (lane == 0) {
+            p.rowmax[(size_t)bh * nb + ra] = ma;
+            p.rowmax[(size_t)bh * nb + rb] = mb;
+        }
+    }
+    __syncthreads();
+    uint32_t* gh = p.hist + (size_t)bh * kHistBins;
+    for (int x = tid; x < kHistBins; x += kSelThreads)
+        if (hist[x]) atomicAdd(&gh[x], hist[x]);
+
+    // arrive: every store and histogram add of the workgroup has completed
+    // before the count goes up
+    arrive(p.ncand + (size_t)bh * kCandStride + 1);
+}
+
+// Wait until `count` reaches n (bounded).
+__device__ __forceinline__ void wait_count(const Params& p, uint32_t* count, uint32_t n) {
+    if (threadIdx.x == 0) {
+        uint32_t polls = 0;
+        while (__hip_atomic_fetch_add(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n) {
+            if (++polls == kWaitPolls) {
+                atomicOr(reinterpret_cast<unsigned int*>(p.error), kErrWait);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+    }
+    __syncthreads();
+}
+
+template <bool kGiven, int HD>
+__global__ __launch_bounds__(kSelThreads) void lgsel_kernel(Params p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int nb = p.nb;
+    const int lt = nb / kFusedRows;   // logits workgroups per head
+    const int heads_per_xcd = (p.BH + 7) / 8;
+    const int n_lg = 8 * heads_per_xcd * lt;
+    // workgroup g runs on XCD g % 8; head bh's workgroups go to XCD bh % 8,
+    // in consecutive slots
+    if ((int)blockIdx.x >= n_lg) {
+        // full mode: V pooled by the workgroups after the logits ones, on the
+        // CUs those leave free; the low-res workgroups of the head wait for them
+        const int bh = p.dtype == 1 ? pool_v_direct<1, HD>(p, (int)blockIdx.x - n_lg)
+                                    : pool_v_direct<0, HD>(p, (int)blockIdx.x - n_lg);
+        if (bh >= 0) arrive(p.ncand + (size_t)bh * kCandStride + 2);
+        return;
+    }
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int hm = slot / lt, t = slot - hm * lt;
+    const int bh = xcd + 8 * hm;
+    if (bh >= p.BH) return;
+    fused_logits<kGiven, HD>(p, bh, t * kFusedRows, smem);
+    const int nsel = nb / kTileRows;
+    const int nlow = p.mode == 0 ? (nb + kLoRows - 1) / kLoRows : 0;
+    if (t >= nsel + nlow) return;
+    wait_count(p, p.ncand + (size_t)bh * kCandStride + 1, (uint32_t)lt);
+    if (t < nsel) {
+        select_rows(p, bh, t, smem);
+    } else {
+        if (p.v_in_logits)
+            wait_count(p, p.ncand + (size_t)bh * kCandStride + 2, (uint32_t)v_direct_groups(nb, HD));
+        lowres_rows<HD>(p, bh, (t - nsel) * kLoRows, smem);
+    }
+}
+
 // ---------------------------------------------------------------- BigBird layout
 // A static block-sparse pattern as a selection of 32-token blocks, for the
 // same attention and join kernels ([BigBird]: a window of three blocks, two
@@ -1638,6 +1935,7 @@ __global__ __launch_bounds__(kSelThreads) void bigbird_layout_kernel(Params p) {
 
 template <bool kGiven, int HD>
 static hipError_t launch_logits_t(const Params& p, hipStream_t s) {
+    if (row_tiled(p.nb)) return hipSuccess;   // the selection launch forms the logits (lgsel_kernel)
     const int tiles_per_head = (p.nb + kRT - 1) / kRT;
     static const hipError_t a1 = hipFuncSetAttribute(reinterpret_cast<const void*>(&logits_kernel<kGiven, HD>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
@@ -1657,6 +1955,7 @@ static hipError_t launch_logits_t(const Params& p, hipStream_t s) {
 // at most one per CU of the device, so that the V workgroups run beside them.
 bool v_pooled_in_logits(int mode, int BH, int nb) {
     if (mode != 0) return false;
+    if (row_tiled(nb)) return true;   // lgsel_kernel: V workgroups after the logits ones
     static int cus[64] = {0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
@@ -1684,7 +1983,26 @@ hipError_t launch_premark(const Params& p, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <bool kGiven, int HD>
+static hipError_t launch_lgsel_t(const Params& p, hipStream_t s) {
+    static const hipError_t a = hipFuncSetAttribute(reinterpret_cast<const void*>(&lgsel_kernel<kGiven, HD>),
+                                                    hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (a != hipSuccess) return a;
+    size_t lds = fused_logits_lds(HD);
+    if (tile_lds(p.nb).total > lds) lds = tile_lds(p.nb).total;
+    if (p.mode == 0 && lowres_lds(p.nb, HD) > lds) lds = lowres_lds(p.nb, HD);
+    const int heads_per_xcd = (p.BH + 7) / 8;
+    int grid = 8 * heads_per_xcd * (p.nb / kFusedRows);
+    if (!kGiven && p.v_in_logits) grid += 8 * heads_per_xcd * v_direct_groups(p.nb, HD);
+    hipLaunchKernelGGL((lgsel_kernel<kGiven, HD>), dim3(grid), dim3(kSelThreads), lds, s, p);
+    return hipGetLastError();
+}
+
 hipError_t launch_select(const Params& p, hipStream_t s) {
+    if (row_tiled(p.nb)) {
+        if (p.logits_given) return p.d == 128 ? launch_lgsel_t<true, 128>(p, s) : launch_lgsel_t<true, 64>(p, s);
+        return p.d == 128 ? launch_lgsel_t<false, 128>(p, s) : launch_lgsel_t<false, 64>(p, s);
+    }
     static const hipError_t a2 = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (a2 != hipSuccess) return a2;

@@ -89,13 +89,18 @@ typedef enum {
  *                          (gradients undefined)
  *   MRA_DEVERR_NO_STATS    backward: the forward call did not save the
  *                          softmax statistics (mra_options.save_stats = 0;
- *                          gradients undefined) */
+ *                          gradients undefined)
+ *   MRA_DEVERR_WAIT        selector (N = 2048 or 4096): a workgroup gave up
+ *                          waiting for the other workgroups of its head to
+ *                          store their logits, i.e. the device did not run
+ *                          them (selection and output undefined) */
 enum {
     MRA_DEVERR_CANDIDATES = 1,
     MRA_DEVERR_STREAM = 2,
     MRA_DEVERR_WINDOW = 4,
     MRA_DEVERR_BWD_PLAN = 8,
-    MRA_DEVERR_NO_STATS = 16
+    MRA_DEVERR_NO_STATS = 16,
+    MRA_DEVERR_WAIT = 32
 };
 
 typedef enum { MRA_F32 = 0, MRA_BF16 = 1 } mra_dtype;
