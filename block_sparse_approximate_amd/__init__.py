@@ -55,6 +55,7 @@ SIGNATURES = {
     "mra_debug_stages": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P,
                           _P, _P, _SZ, _P], ctypes.c_int),
     "mra_debug_select": ([_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P], ctypes.c_int),
+    "mra_debug_wait_timeout": ([_P, _P, _P, _P, _I32, _I32, ctypes.c_uint32, _P, _SZ, _P], ctypes.c_int),
     "mra_workspace_error": ([_P, _SZ, _P, ctypes.POINTER(ctypes.c_uint32)], ctypes.c_int),
     "mra_attention_fwd_noalloc": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P], ctypes.c_int),
     "mra_bigbird_workspace_size": ([_P, _I32, _I32, ctypes.POINTER(_SZ)], ctypes.c_int),
@@ -429,6 +430,22 @@ def debug_select(logits, count, batch, heads, block_per_row=4, initial_prior_fir
                                 ws_bytes, _stream(logits))
     _check(st, "mra_debug_select")
     return sel[:, :, :K]
+
+
+def debug_wait_timeout(q, k, v, polls=16, block_per_row=4, approx_mode="full"):
+    """Pooling and the logits-and-selection launch (seq_len 2048 or 4096)
+    with every workgroup's wait for its head made to run out after `polls`
+    polls; returns the workspace's device error word (MRA_DEVERR_WAIT is
+    expected).  A test of the error path: the selection is not meant for use."""
+    _check_inputs(q, k, v, None)
+    B, H, N, d = q.shape
+    ws_bytes = workspace_size(B, H, N, d, q.dtype, block_per_row, approx_mode)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    dims = _dims(B, H, N, d, DTYPES[q.dtype], 0)
+    _check(lib().mra_debug_wait_timeout(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), block_per_row,
+                                        MODES.get(approx_mode, -1), polls, _ptr(ws), ws_bytes, _stream(q)),
+           "mra_debug_wait_timeout")
+    return workspace_error(ws)
 
 
 def bigbird_workspace_size(batch, heads, seq_len, head_dim=64, dtype=torch.bfloat16, block_size=64,

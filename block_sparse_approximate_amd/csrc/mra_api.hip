@@ -630,6 +630,21 @@ MRA_API mra_status mra_debug_stages(const mra_dims* dims, const void* q, const v
     return MRA_OK;
 }
 
+MRA_API mra_status mra_debug_wait_timeout(const mra_dims* dims, const void* q, const void* k, const void* v,
+                                          int32_t block_per_row, int32_t approx_mode, uint32_t polls,
+                                          void* workspace, size_t workspace_bytes, void* stream) {
+    Layout L;
+    mra_status st = check_call(dims, q, k, v, nullptr, block_per_row, approx_mode, 0, 0, nullptr, workspace,
+                               workspace_bytes, false, &L);
+    if (st != MRA_OK) return st;
+    if (!fused_select(L.nb)) return MRA_ERR_SEQ_LEN;
+    if (polls < 1 || polls > (1u << 16)) return MRA_ERR_STAGE;
+    Params p = make_params(*dims, L, approx_mode, 0, 0, q, k, v, nullptr, nullptr, workspace);
+    p.wait_polls = polls;
+    p.wait_extra = 1;
+    return run_front(p, static_cast<hipStream_t>(stream));
+}
+
 MRA_API mra_status mra_debug_select(const mra_dims* dims, const float* logits, const int32_t* count,
                                     int32_t block_per_row, int32_t prior_first, int32_t prior_diag,
                                     int32_t score_ranking, int32_t diag_band, int32_t* sel, void* workspace,

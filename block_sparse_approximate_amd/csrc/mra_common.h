@@ -87,6 +87,10 @@ struct Params {
                            //   fused logits and selection launch for N = 2048, 4096)
     int32_t logits_given;  // 1: the logits are already in `logits` (selector hook); step 1 forms only
                            //   row maxima, keys and the histogram from them
+    uint32_t wait_polls;   // polls of a workgroup's bounded wait for its head's other workgroups
+                           //   (0: the default limit)
+    uint32_t wait_extra;   // added to the count waited for (0; 1 makes every wait run out, a test
+                           //   of the error path)
     const void* q;
     const void* k;
     const void* v;
@@ -220,6 +224,7 @@ bool v_pooled_in_logits(int mode, int BH, int nb);
 hipError_t launch_logits_given(const Params& p, hipStream_t s);
 hipError_t launch_premark(const Params& p, hipStream_t s);
 hipError_t launch_select(const Params& p, hipStream_t s);
+bool fused_select(int nb);   // logits and selection in one launch (heads of 64 or 128 block rows)
 hipError_t launch_attn(const Params& p, hipStream_t s);
 hipError_t launch_bigbird_layout(const Params& p, hipStream_t s);
 int bwd_max_chunks(int nb, int64_t K);

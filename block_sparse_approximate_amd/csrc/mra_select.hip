@@ -1803,12 +1803,14 @@ __device__ __forceinline__ void fused_logits(const Params& p, int bh, int row0, 
     arrive(p.ncand + (size_t)bh * kCandStride + 1);
 }
 
-// Wait until `count` reaches n (bounded).
+// Wait until `count` reaches n (bounded: p.wait_polls polls, kWaitPolls when 0).
 __device__ __forceinline__ void wait_count(const Params& p, uint32_t* count, uint32_t n) {
     if (threadIdx.x == 0) {
+        const uint32_t limit = p.wait_polls ? p.wait_polls : kWaitPolls;
+        n += p.wait_extra;
         uint32_t polls = 0;
         while (__hip_atomic_fetch_add(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n) {
-            if (++polls == kWaitPolls) {
+            if (++polls >= limit) {
                 atomicOr(reinterpret_cast<unsigned int*>(p.error), kErrWait);
                 break;
             }
@@ -1997,6 +1999,8 @@ static hipError_t launch_lgsel_t(const Params& p, hipStream_t s) {
     hipLaunchKernelGGL((lgsel_kernel<kGiven, HD>), dim3(grid), dim3(kSelThreads), lds, s, p);
     return hipGetLastError();
 }
+
+bool fused_select(int nb) { return row_tiled(nb); }
 
 hipError_t launch_select(const Params& p, hipStream_t s) {
     if (row_tiled(p.nb)) {

@@ -68,7 +68,8 @@ typedef enum {
     MRA_ERR_WORKSPACE = 10, /* a workspace NULL or smaller than its size query returns */
     MRA_ERR_HIP = 11,       /* a HIP call failed */
     MRA_ERR_ALIGN = 12,     /* a tensor pointer is not 16-byte aligned */
-    MRA_ERR_STAGE = 13,     /* mra_debug_replay: a stage other than 3, or count < 1 */
+    MRA_ERR_STAGE = 13,     /* mra_debug_replay: a stage other than 3, or count < 1;
+                               mra_debug_wait_timeout: polls out of range */
     MRA_ERR_SCRATCH = 14    /* mra_attention_fwd_noalloc: the sizes need more than its 64 MiB scratch */
 } mra_status;
 
@@ -243,6 +244,21 @@ mra_status mra_debug_stages(const mra_dims* dims, const void* q, const void* k, 
                             int32_t diag_band, float* qhat, float* khat,
                             float* vhat, int32_t* count, float* logits, float* rowmax, int32_t* sel,
                             int32_t* error, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Test hook for the selector's bounded wait (heads of 64 or 128 block rows,
+ * seq_len 2048 or 4096, where one launch forms the logits and selects): runs
+ * pooling and that launch as mra_debug_stages does (no mask, no priors), but
+ * with every workgroup waiting for one workgroup more than its head has, for
+ * at most `polls` polls (1 .. 65536).  Each wait runs out, sets
+ * MRA_DEVERR_WAIT in the workspace's error word (read it with
+ * mra_workspace_error) and the workgroup goes on, so the launch ends however
+ * the device schedules it.  The selection it leaves is not meant for use.
+ * Callers: tests of the error path.  Returns MRA_ERR_SEQ_LEN for other
+ * sequence lengths, MRA_ERR_STAGE for polls out of range, otherwise as
+ * mra_debug_stages. */
+mra_status mra_debug_wait_timeout(const mra_dims* dims, const void* q, const void* k, const void* v,
+                                  int32_t block_per_row, int32_t approx_mode, uint32_t polls, void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 /* Stage hook: the step-2 selector alone on caller-given logits, so that its
  * result can be compared with the oracle's on identical fp32 inputs.

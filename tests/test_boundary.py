@@ -23,7 +23,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     L = mra.lib()
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 19
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(mra.SIGNATURES)
@@ -139,6 +139,19 @@ def test_debug_select_rejects_bad_arguments():
     assert L.mra_debug_select(ctypes.byref(d), Q, K, 4, -1, 0, 0, 0, O, W, 1 << 40, None) == 8
     assert L.mra_debug_select(ctypes.byref(d), Q, K, 4, 0, 0, 2, 0, O, W, 1 << 40, None) == 6
     assert L.mra_debug_select(ctypes.byref(d), Q, K, 4, 0, 2, 0, 3, O, W, 1 << 40, None) == 8
+
+
+def test_debug_wait_timeout_rejects_bad_arguments():
+    L = mra.lib()
+    d = mra._Dims(1, 2, 4096, 64, 1)
+    assert L.mra_debug_wait_timeout(None, Q, K, V, 4, 0, 8, W, 1 << 40, None) == 1
+    assert L.mra_debug_wait_timeout(ctypes.byref(d), Q, K, V, 4, 0, 8, W, 16, None) == 10
+    assert L.mra_debug_wait_timeout(ctypes.byref(d), Q, K, V, 4, 0, 0, W, 1 << 40, None) == 13
+    assert L.mra_debug_wait_timeout(ctypes.byref(d), Q, K, V, 4, 0, (1 << 16) + 1, W, 1 << 40, None) == 13
+    # only heads of 64 or 128 block rows form logits and select in one launch
+    for n in (1024, 8192):
+        d = mra._Dims(1, 2, n, 64, 1)
+        assert L.mra_debug_wait_timeout(ctypes.byref(d), Q, K, V, 4, 0, 8, W, 1 << 40, None) == 3
 
 
 def test_debug_replay_rejects_bad_arguments():

@@ -11,6 +11,8 @@
 Inputs come from workloads.py (seeded); the five named workloads run at
 full size.
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -427,3 +429,27 @@ def test_backward_without_saved_statistics_is_flagged(mra):
     # the next forward call clears the word
     mra.attention(q, k, v, None, block_per_row=2, workspace=ws, save_stats=True)
     assert mra.workspace_error(ws) == 0
+
+
+@pytest.mark.parametrize("N,mode", [(4096, "full"), (2048, "sparse")])
+def test_selector_wait_runs_out_and_is_flagged(mra, N, mode):
+    # At N = 2048 and 4096 the head's workgroups meet on a count inside one
+    # launch.  The hook makes every wait look for one workgroup more than the
+    # head has, so each wait runs out after a few polls: the launch still
+    # ends, MRA_DEVERR_WAIT is set, and the next forward call on the same
+    # workspace starts from cleared counts and matches a fresh workspace.
+    w = small("wait-" + mode, 1, 2, N, block_per_row=2, approx_mode=mode)
+    q, k, v = dev(w, "q"), dev(w, "k"), dev(w, "v")
+    print("case wait timeout", N, mode, flush=True)
+    word = mra.debug_wait_timeout(q, k, v, polls=8, block_per_row=2, approx_mode=mode)
+    assert word & 32
+    ws = torch.empty(mra.workspace_size(1, 2, N, 64, q.dtype, 2, mode), dtype=torch.uint8, device="cuda")
+    mra.lib().mra_debug_wait_timeout(ctypes.byref(mra._dims(1, 2, N, 64, 1)), mra._ptr(q), mra._ptr(k),
+                                     mra._ptr(v), 2, mra.MODES[mode], 8, mra._ptr(ws), ws.numel(),
+                                     mra._stream(q))
+    assert mra.workspace_error(ws) & 32
+    out = mra.attention(q, k, v, None, block_per_row=2, approx_mode=mode, workspace=ws)
+    assert mra.workspace_error(ws) == 0
+    ref = mra.attention(q, k, v, None, block_per_row=2, approx_mode=mode)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
