@@ -102,7 +102,8 @@ def algorithmic(w, stage: str, sel_blocks: int) -> tuple[float, str]:
     BH, nb = B * H, N // 32
     es = 2 if w.dtype == "bf16" else 4
     full = w.approx_mode == "full"
-    ntens = 3 if full else 2
+    fused = nb in (64, 128)    # one launch forms the logits, selects and (full mode) pools V
+    ntens = 3 if full and not fused else 2
     K = nb * w.block_per_row if nb * w.block_per_row < nb * nb else nb * nb
     mask_b = 0 if w.mask is None else B * N
     if stage == "attn":        # Q, K, V read once and O written once (its arithmetic intensity is far
@@ -114,8 +115,9 @@ def algorithmic(w, stage: str, sel_blocks: int) -> tuple[float, str]:
         return 2 * BH * nb * d * 4 + BH * nb * nb * 4 + BH * nb * 4 + lowres, "byte"
     if stage == "select":      # logits and row maxima in; K block indices out
         return BH * nb * nb * 4 + BH * nb * 4 + BH * K * 4, "byte"
-    if stage == "logits+select":   # one launch for both (N = 2048, 4096)
-        return algorithmic(w, "logits", sel_blocks)[0] + algorithmic(w, "select", sel_blocks)[0], "byte"
+    if stage == "logits+select":   # one launch for both (N = 2048, 4096), which also pools V in full mode
+        v = BH * N * d * es + BH * nb * d * 4 if full else 0
+        return algorithmic(w, "logits", sel_blocks)[0] + algorithmic(w, "select", sel_blocks)[0] + v, "byte"
     raise ValueError(stage)
 
 

@@ -1378,28 +1378,20 @@ __device__ __forceinline__ void select_rows(const Params& p, int bh, int t, unsi
 __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int nb = p.nb;
+    // (heads of 64 or 128 block rows are selected by lgsel_kernel)
     // workgroups [0, BH_pad) select, one per head (BH_pad = BH rounded up to
     // a multiple of 8, so workgroup bh runs on XCD bh % 8); in full mode the
     // rest sum the low-res attention of kLoRows rows each, placed on the XCD of
     // their head
     const int bh_pad = 8 * ((p.BH + 7) / 8);
-    const int tiles = row_tiled(nb) ? nb / kTileRows : 1;   // selecting workgroups per head
-    if ((int)blockIdx.x >= bh_pad * tiles) {
-        const int g = blockIdx.x - bh_pad * tiles, xcd = g & 7, slot = g >> 3;
+    if ((int)blockIdx.x >= bh_pad) {
+        const int g = blockIdx.x - bh_pad, xcd = g & 7, slot = g >> 3;
         const int tiles = (nb + kLoRows - 1) / kLoRows;
         const int hm = slot / tiles, lbh = xcd + 8 * hm;
         if (lbh < p.BH) {
             if (p.d == 128) lowres_rows<128>(p, lbh, (slot - hm * tiles) * kLoRows, smem);
             else lowres_rows<64>(p, lbh, (slot - hm * tiles) * kLoRows, smem);
         }
-        return;
-    }
-    if (row_tiled(nb)) {
-        // workgroup g runs on XCD g % 8: the row tiles of head bh go to XCD bh % 8
-        const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-        const int hm = slot / tiles, t = slot - hm * tiles;
-        const int tbh = xcd + 8 * hm;
-        if (tbh < p.BH) select_rows(p, tbh, t, smem);
         return;
     }
     const int bh = blockIdx.x;
@@ -2012,10 +2004,9 @@ hipError_t launch_select(const Params& p, hipStream_t s) {
     if (a2 != hipSuccess) return a2;
     const int bh_pad = 8 * ((p.BH + 7) / 8);
     const int lowres_wgs = p.mode == 0 ? bh_pad * ((p.nb + kLoRows - 1) / kLoRows) : 0;
-    const int sel_wgs = row_tiled(p.nb) ? bh_pad * (p.nb / kTileRows) : bh_pad;
-    size_t lds = row_tiled(p.nb) ? tile_lds(p.nb).total : select_lds(p.nb).total;
+    size_t lds = select_lds(p.nb).total;
     if (p.mode == 0 && lowres_lds(p.nb, p.d) > lds) lds = lowres_lds(p.nb, p.d);
-    hipLaunchKernelGGL(select_kernel, dim3(sel_wgs + lowres_wgs), dim3(kSelThreads), lds, s, p);
+    hipLaunchKernelGGL(select_kernel, dim3(bh_pad + lowres_wgs), dim3(kSelThreads), lds, s, p);
     return hipGetLastError();
 }
 
