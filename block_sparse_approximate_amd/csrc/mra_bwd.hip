@@ -441,8 +441,8 @@ constexpr int kLrThreads = kLrWaves * 64;
 constexpr int kLrTile = 64;            // key blocks (query blocks) per staged tile
 // dynamic LDS of the low-res kernels (128-channel tiles exceed static LDS)
 __host__ __device__ constexpr size_t lr_rows_lds(int hd) {
-    return ((size_t)kLrTile * (hd + 1) + (size_t)kLrTile * hd + (size_t)kLrWaves * hd + 2 * kLrWaves * kLrTile +
-            kLrWaves * kBlock) * 4;
+    return ((size_t)kLrTile * (hd + 4) + (size_t)kLrTile * (hd + 1) + (size_t)kLrWaves * (hd + 1) +
+            2 * kLrWaves * (kLrTile + 1) + kLrWaves * kBlock) * 4;
 }
 __host__ __device__ constexpr size_t lr_cols_lds(int hd) {
     return (2 * (size_t)kLrTile * hd + 2 * kLrWaves * kLrTile) * 4;
@@ -451,21 +451,25 @@ __host__ __device__ constexpr size_t lr_cols_lds(int hd) {
 // Workgroup (bh, rows i0 .. i0 + 7), wave w takes row i = i0 + w:
 //   phase 1: a_t, D_t of the row's tokens; g_i (lane = channel, and channel
 //            + 64 for 128-channel heads), c_i
-//   phase 2: per tile of kLrTile key blocks (vhat, khat staged): lane = j
-//            forms w_ij (the forward's weight, 0 for selected or empty cells)
-//            and e_ij; then lane = channel adds e_ij khat_j to dqhat_i.  E and
-//            W go out transposed ([j][i], 8 consecutive rows per j).
+//   phase 2: per tile of kLrTile key blocks (vhat, khat staged): wave = row,
+//            lane = j forms w_ij (the forward's weight, 0 for selected or
+//            empty cells); then on the matrix core T = G Vhat^T (waves 0..3,
+//            16 key blocks each), e_ij = w_ij (T_ij - c_i), and
+//            dqhat += E Khat (wave w: channels 16 w ..).  E and W go out
+//            transposed ([j][i], 8 consecutive rows per j).
 template <int DT, int HD>
 __global__ __launch_bounds__(kLrThreads) void lr_rows_kernel(Params p) {
     constexpr int kCx = HD / 64;   // channels per lane
-    // kt [kLrTile][HD] first (16-byte stores), then vt [kLrTile][HD + 1] (stride HD + 1: lane j reads row j
-    // without bank conflicts), gs [kLrWaves][HD], es and ws [kLrWaves][kLrTile], al [kLrWaves][kBlock]
+    // kt [kLrTile][HD + 4] first (16-byte stores), then vt [kLrTile][HD + 1], gs [kLrWaves][HD + 1], es and
+    // ws [kLrWaves][kLrTile + 1], al [kLrWaves][kBlock]; the padded strides spread the MFMA operand reads
+    // (16 rows or keys by 4 columns a read) over the banks
     extern __shared__ __align__(16) float lrs[];
-    float (*kt)[HD] = reinterpret_cast<float (*)[HD]>(lrs);
-    float (*vt)[HD + 1] = reinterpret_cast<float (*)[HD + 1]>(lrs + kLrTile * HD);
-    float (*gs)[HD] = reinterpret_cast<float (*)[HD]>(lrs + kLrTile * HD + kLrTile * (HD + 1));
-    float (*es)[kLrTile] = reinterpret_cast<float (*)[kLrTile]>(lrs + kLrTile * HD + kLrTile * (HD + 1) + kLrWaves * HD);
-    float (*ws)[kLrTile] = es + kLrWaves;
+    float (*kt)[HD + 4] = reinterpret_cast<float (*)[HD + 4]>(lrs);
+    float (*vt)[HD + 1] = reinterpret_cast<float (*)[HD + 1]>(lrs + kLrTile * (HD + 4));
+    float (*gs)[HD + 1] = reinterpret_cast<float (*)[HD + 1]>(lrs + kLrTile * (HD + 4) + kLrTile * (HD + 1));
+    float (*es)[kLrTile + 1] = reinterpret_cast<float (*)[kLrTile + 1]>(lrs + kLrTile * (HD + 4) + kLrTile * (HD + 1) +
+                                                                        kLrWaves * (HD + 1));
+    float (*ws)[kLrTile + 1] = es + kLrWaves;
     float (*al)[kBlock] = reinterpret_cast<float (*)[kBlock]>(ws + kLrWaves);
     const int nb = p.nb, groups = (nb + kLrWaves - 1) / kLrWaves;
     int bh, grp;
@@ -478,10 +482,49 @@ __global__ __launch_bounds__(kLrThreads) void lr_rows_kernel(Params p) {
     const size_t hrow = (size_t)bh * nb + (act ? i : 0);
     const float mi = p.rowmax[hrow];
 
+    // a tile's inputs, one tile ahead: vhat and khat rows, and this lane's
+    // logit, key count and selection word for the weight of (row, key block)
+    const float* S = p.logits + hrow * nb;
+    const uint32_t* sbits = p.selbits + hrow * p.words;
+    const int32_t* cnt = p.cnt + (size_t)b * nb;
+    const float* vh = p.vhat + (size_t)bh * nb * HD;
+    const float* kh = p.khat + (size_t)bh * nb * HD;
+    constexpr int kTL = kLrTile * (HD / 4) / kLrThreads;   // float4s of a tile per thread and tensor
+    float4 tv[kTL], tk[kTL];
+    float tS = 0.f;
+    int tc = 0;
+    uint32_t tb = 0xFFFFFFFFu;
+    auto fetch_tile = [&](int j0) {
+#pragma unroll
+        for (int e = 0; e < kTL; e++) {
+            const int x = tid + e * kLrThreads, j = j0 + x / (HD / 4), c4 = (x % (HD / 4)) * 4;
+            tv[e] = j < nb ? *reinterpret_cast<const float4*>(vh + (size_t)j * HD + c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+            tk[e] = j < nb ? *reinterpret_cast<const float4*>(kh + (size_t)j * HD + c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        const int j = j0 + lane;
+        tS = act && j < nb ? S[j] : 0.f;
+        tc = j < nb ? cnt[j] : 0;
+        tb = act && j < nb ? sbits[j >> 5] : 0xFFFFFFFFu;
+    };
+    fetch_tile(0);
+
     float ci = 0.f;
     if (act) {
         const size_t rowoff = ((size_t)bh * p.N + (size_t)i * kBlock) * HD;
         const int n = lane & 31, h = lane >> 5;
+        // dO at this lane's channels for every token of the row, loaded with the
+        // row's first loads: g_i below then needs no further round trip
+        float dv[kCx][kBlock];
+#pragma unroll
+        for (int x = 0; x < kCx; x++) {
+#pragma unroll
+            for (int u = 0; u < kBlock; u++) {
+                if constexpr (DT == 1)
+                    dv[x][u] = bf16_to_float(static_cast<const uint16_t*>(p.dout)[rowoff + u * HD + lane + 64 * x]);
+                else
+                    dv[x][u] = static_cast<const float*>(p.dout)[rowoff + u * HD + lane + 64 * x];
+            }
+        }
         float D;
         if constexpr (DT == 1)
             D = row_dot<HD>(static_cast<const uint16_t*>(p.dout) + rowoff,
@@ -499,72 +542,78 @@ __global__ __launch_bounds__(kLrThreads) void lr_rows_kernel(Params p) {
         for (int x = 0; x < kCx; x++) {
             const int c = lane + 64 * x;
             float g = 0.f;
-            if constexpr (DT == 1) {
-                const uint16_t* dO = static_cast<const uint16_t*>(p.dout) + rowoff;
-#pragma unroll 8
-                for (int u = 0; u < kBlock; u++) g += al[wave][u] * bf16_to_float(dO[u * HD + c]);
-            } else {
-                const float* dO = static_cast<const float*>(p.dout) + rowoff;
-#pragma unroll 8
-                for (int u = 0; u < kBlock; u++) g += al[wave][u] * dO[u * HD + c];
-            }
+#pragma unroll
+            for (int u = 0; u < kBlock; u++) g += al[wave][u] * dv[x][u];
             gs[wave][c] = g;
             p.bwd_g[hrow * HD + c] = g;
         }
         if (lane == 0) p.bwd_c[hrow] = ci;
-    }
-
-    const float* S = p.logits + hrow * nb;
-    const uint32_t* sbits = p.selbits + hrow * p.words;
-    const int32_t* cnt = p.cnt + (size_t)b * nb;
-    const float* vh = p.vhat + (size_t)bh * nb * HD;
-    const float* kh = p.khat + (size_t)bh * nb * HD;
-    float dqh[kCx];
+    } else {
 #pragma unroll
-    for (int x = 0; x < kCx; x++) dqh[x] = 0.f;
+        for (int x = 0; x < kCx; x++) gs[wave][lane + 64 * x] = 0.f;   // rows past the head: T = 0
+    }
+    if (lane == 0) al[wave][0] = ci;   // al is free now: row c_i for the tile products
+
+    // the tile products on v_mfma_f32_16x16x4f32 (16-row tiles, rows 8 .. 15
+    // zero): A lane l holds X[l % 16][k = l / 16], B lane l holds Y[k = l / 16]
+    // [l % 16], accumulator e of lane l is row 4 (l / 16) + e, column l % 16
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    const int l16 = lane & 15, k4 = lane >> 4;
+    f32x4 dq = {0.f, 0.f, 0.f, 0.f};   // wave w < HD / 16: dqhat of channels 16 w .. 16 w + 15
     for (int j0 = 0; j0 < nb; j0 += kLrTile) {
         __syncthreads();   // every wave is done with the previous tile
-        for (int x = tid; x < kLrTile * (HD / 4); x += kLrThreads) {
-            const int r = x / (HD / 4), c4 = (x % (HD / 4)) * 4, j = j0 + r;
-            float4 vv = make_float4(0.f, 0.f, 0.f, 0.f), kk = vv;
-            if (j < nb) {
-                vv = *reinterpret_cast<const float4*>(vh + (size_t)j * HD + c4);
-                kk = *reinterpret_cast<const float4*>(kh + (size_t)j * HD + c4);
+#pragma unroll
+        for (int e = 0; e < kTL; e++) {
+            const int x = tid + e * kLrThreads, r = x / (HD / 4), c4 = (x % (HD / 4)) * 4;
+            vt[r][c4] = tv[e].x; vt[r][c4 + 1] = tv[e].y; vt[r][c4 + 2] = tv[e].z; vt[r][c4 + 3] = tv[e].w;
+            *reinterpret_cast<float4*>(&kt[r][c4]) = tk[e];
+        }
+        // w_ij of the tile (wave = row, lane = key block)
+        {
+            const int j = j0 + lane;
+            ws[wave][lane] = (act && j < nb && !((tb >> (j & 31)) & 1u)) ? lowres_weight(tS, mi, tc) : 0.f;
+        }
+        if (j0 + kLrTile < nb) fetch_tile(j0 + kLrTile);   // in flight during this tile
+        __syncthreads();
+        // T = G Vhat^T (waves 0 .. 3: 16 key blocks each), then e_ij = w_ij (T_ij - c_i)
+        if (wave < kLrTile / 16) {
+            f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+            for (int k0 = 0; k0 < HD; k0 += 4) {
+                const float a = l16 < kLrWaves ? gs[l16][k0 + k4] : 0.f;
+                t = __builtin_amdgcn_mfma_f32_16x16x4f32(a, vt[16 * wave + l16][k0 + k4], t, 0, 0, 0);
             }
-            vt[r][c4] = vv.x; vt[r][c4 + 1] = vv.y; vt[r][c4 + 2] = vv.z; vt[r][c4 + 3] = vv.w;
-            *reinterpret_cast<float4*>(&kt[r][c4]) = kk;
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int r = 4 * k4 + e;
+                if (r < kLrWaves) es[r][16 * wave + l16] = ws[r][16 * wave + l16] * (t[e] - al[r][0]);
+            }
         }
         __syncthreads();
-        if (act) {
-            if (lane < kLrTile) {
-                const int j = j0 + lane;
-                float w = 0.f;
-                if (j < nb && !((sbits[j >> 5] >> (j & 31)) & 1u)) w = lowres_weight(S[j], mi, cnt[j]);
-                float T = 0.f;
-#pragma unroll 16
-                for (int c = 0; c < HD; c++) T += gs[wave][c] * vt[lane][c];
-                es[wave][lane] = w * (T - ci);
-                ws[wave][lane] = w;
+        // dqhat += E Khat (wave w < HD / 16: channels 16 w .. 16 w + 15)
+        if (wave < HD / 16) {
+#pragma unroll 8
+            for (int k0 = 0; k0 < kLrTile; k0 += 4) {
+                const float a = l16 < kLrWaves ? es[l16][k0 + k4] : 0.f;
+                dq = __builtin_amdgcn_mfma_f32_16x16x4f32(a, kt[k0 + k4][16 * wave + l16], dq, 0, 0, 0);
             }
-            wave_sync_lds();
-#pragma unroll
-            for (int x = 0; x < kCx; x++)
-#pragma unroll 16
-                for (int u = 0; u < kLrTile; u++) dqh[x] += es[wave][u] * kt[u][lane + 64 * x];
         }
         __syncthreads();   // the tile's e and w of every row
         if (tid < 2 * kLrTile) {
             const int u = tid & (kLrTile - 1), j = j0 + u;
             if (j < nb) {
                 float* dst = (tid < kLrTile ? p.bwd_et : p.bwd_wt) + ((size_t)bh * nb + j) * nb + i0;
-                const float (*src)[kLrTile] = tid < kLrTile ? es : ws;
+                const float (*src)[kLrTile + 1] = tid < kLrTile ? es : ws;
                 for (int r = 0; r < kLrWaves && i0 + r < nb; r++) dst[r] = src[r][u];
             }
         }
     }
-    if (act) {
+    if (wave < HD / 16) {
 #pragma unroll
-        for (int x = 0; x < kCx; x++) p.bwd_dqh[hrow * HD + lane + 64 * x] = tau * dqh[x];
+        for (int e = 0; e < 4; e++) {
+            const int r = 4 * k4 + e;
+            if (r < kLrWaves && i0 + r < nb) p.bwd_dqh[((size_t)bh * nb + i0 + r) * HD + 16 * wave + l16] = tau * dq[e];
+        }
     }
 }
 
@@ -595,23 +644,33 @@ __global__ __launch_bounds__(kLrThreads) void lr_cols_kernel(Params p) {
     float dv[kCx], dk[kCx];
 #pragma unroll
     for (int x = 0; x < kCx; x++) dv[x] = dk[x] = 0.f;
+    // a tile's inputs, one tile ahead: g and qhat rows, and this lane's e and w
+    constexpr int kTL = kLrTile * (HD / 4) / kLrThreads;   // float4s of a tile per thread and tensor
+    float4 tg[kTL], tq[kTL];
+    float te = 0.f, tw = 0.f;
+    auto fetch_tile = [&](int r0) {
+#pragma unroll
+        for (int e = 0; e < kTL; e++) {
+            const int x = tid + e * kLrThreads, i = r0 + x / (HD / 4), c4 = (x % (HD / 4)) * 4;
+            tg[e] = i < nb ? *reinterpret_cast<const float4*>(gh + (size_t)i * HD + c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+            tq[e] = i < nb ? *reinterpret_cast<const float4*>(qh + (size_t)i * HD + c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        const int i = r0 + lane;
+        te = act && i < nb ? p.bwd_et[col + i] : 0.f;
+        tw = act && i < nb ? p.bwd_wt[col + i] : 0.f;
+    };
+    fetch_tile(0);
     for (int r0 = 0; r0 < nb; r0 += kLrTile) {
         __syncthreads();
-        for (int x = tid; x < kLrTile * (HD / 4); x += kLrThreads) {
-            const int r = x / (HD / 4), c4 = (x % (HD / 4)) * 4, i = r0 + r;
-            float4 gg = make_float4(0.f, 0.f, 0.f, 0.f), qq = gg;
-            if (i < nb) {
-                gg = *reinterpret_cast<const float4*>(gh + (size_t)i * HD + c4);
-                qq = *reinterpret_cast<const float4*>(qh + (size_t)i * HD + c4);
-            }
-            *reinterpret_cast<float4*>(&gt[r][c4]) = gg;
-            *reinterpret_cast<float4*>(&qt[r][c4]) = qq;
+#pragma unroll
+        for (int e = 0; e < kTL; e++) {
+            const int x = tid + e * kLrThreads, r = x / (HD / 4), c4 = (x % (HD / 4)) * 4;
+            *reinterpret_cast<float4*>(&gt[r][c4]) = tg[e];
+            *reinterpret_cast<float4*>(&qt[r][c4]) = tq[e];
         }
-        if (act && lane < kLrTile) {
-            const int i = r0 + lane;
-            es[wave][lane] = i < nb ? p.bwd_et[col + i] : 0.f;
-            ws[wave][lane] = i < nb ? p.bwd_wt[col + i] : 0.f;
-        }
+        es[wave][lane] = te;
+        ws[wave][lane] = tw;
+        if (r0 + kLrTile < nb) fetch_tile(r0 + kLrTile);   // in flight during this tile
         __syncthreads();
         if (act) {
 #pragma unroll
