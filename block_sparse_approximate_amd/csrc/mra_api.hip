@@ -153,7 +153,7 @@ Params make_params(const mra_dims& d, const Layout& L, int32_t mode, int32_t pf,
     p.attn_wph = attn_grid_waves_per_head(L.BH, L.K, L.d);
     p.attn_seq = attn_heads_in_turn(L.BH, L.K, L.d) ? 1 : 0;
     attn_segments(L.BH, L.K, L.d, &p.seg_whole, &p.chunk);
-    p.v_in_logits = v != nullptr && v_pooled_in_logits(mode, L.BH, L.nb) ? 1 : 0;
+    p.v_in_logits = v != nullptr && v_pooled_in_logits(mode, L.BH, L.nb, L.d) ? 1 : 0;
     p.q = q; p.k = k; p.v = v; p.mask = mask; p.out = out;
     p.qhat = reinterpret_cast<float*>(w + L.qhat);
     p.khat = reinterpret_cast<float*>(w + L.khat);
@@ -637,8 +637,8 @@ MRA_API mra_status mra_debug_wait_timeout(const mra_dims* dims, const void* q, c
     mra_status st = check_call(dims, q, k, v, nullptr, block_per_row, approx_mode, 0, 0, nullptr, workspace,
                                workspace_bytes, false, &L);
     if (st != MRA_OK) return st;
-    if (!fused_select(L.nb)) return MRA_ERR_SEQ_LEN;
     if (polls < 1 || polls > (1u << 16)) return MRA_ERR_STAGE;
+    if (!fused_select(L.BH, L.nb, L.d, approx_mode)) return MRA_ERR_SEQ_LEN;
     Params p = make_params(*dims, L, approx_mode, 0, 0, q, k, v, nullptr, nullptr, workspace);
     p.wait_polls = polls;
     p.wait_extra = 1;

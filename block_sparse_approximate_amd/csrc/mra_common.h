@@ -220,11 +220,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 namespace mra {
 hipError_t launch_pool(const Params& p, hipStream_t s);
 hipError_t launch_logits(const Params& p, hipStream_t s);
-bool v_pooled_in_logits(int mode, int BH, int nb);
+bool v_pooled_in_logits(int mode, int BH, int nb, int d);
 hipError_t launch_logits_given(const Params& p, hipStream_t s);
 hipError_t launch_premark(const Params& p, hipStream_t s);
 hipError_t launch_select(const Params& p, hipStream_t s);
-bool fused_select(int nb);   // logits and selection in one launch (heads of 64 or 128 block rows)
+bool fused_select(int BH, int nb, int d, int mode);   // logits and selection in one launch
 hipError_t launch_attn(const Params& p, hipStream_t s);
 hipError_t launch_bigbird_layout(const Params& p, hipStream_t s);
 int bwd_max_chunks(int nb, int64_t K);

@@ -1929,7 +1929,7 @@ __global__ __launch_bounds__(kSelThreads) void bigbird_layout_kernel(Params p) {
 
 template <bool kGiven, int HD>
 static hipError_t launch_logits_t(const Params& p, hipStream_t s) {
-    if (row_tiled(p.nb)) return hipSuccess;   // the selection launch forms the logits (lgsel_kernel)
+    if (fused_select(p.BH, p.nb, p.d, p.mode)) return hipSuccess;   // lgsel_kernel forms the logits
     const int tiles_per_head = (p.nb + kRT - 1) / kRT;
     static const hipError_t a1 = hipFuncSetAttribute(reinterpret_cast<const void*>(&logits_kernel<kGiven, HD>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
@@ -1947,9 +1947,9 @@ static hipError_t launch_logits_t(const Params& p, hipStream_t s) {
 
 // Whether the logits launch pools V: full mode, and its logits workgroups
 // at most one per CU of the device, so that the V workgroups run beside them.
-bool v_pooled_in_logits(int mode, int BH, int nb) {
+bool v_pooled_in_logits(int mode, int BH, int nb, int d) {
     if (mode != 0) return false;
-    if (row_tiled(nb)) return true;   // lgsel_kernel: V workgroups after the logits ones
+    if (fused_select(BH, nb, d, mode)) return true;   // lgsel_kernel: V workgroups after the logits ones
     static int cus[64] = {0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
@@ -1977,14 +1977,20 @@ hipError_t launch_premark(const Params& p, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int HD>
+static size_t lgsel_lds(int nb, int mode) {
+    size_t lds = fused_logits_lds(HD);
+    if (tile_lds(nb).total > lds) lds = tile_lds(nb).total;
+    if (mode == 0 && lowres_lds(nb, HD) > lds) lds = lowres_lds(nb, HD);
+    return lds;
+}
+
 template <bool kGiven, int HD>
 static hipError_t launch_lgsel_t(const Params& p, hipStream_t s) {
     static const hipError_t a = hipFuncSetAttribute(reinterpret_cast<const void*>(&lgsel_kernel<kGiven, HD>),
                                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (a != hipSuccess) return a;
-    size_t lds = fused_logits_lds(HD);
-    if (tile_lds(p.nb).total > lds) lds = tile_lds(p.nb).total;
-    if (p.mode == 0 && lowres_lds(p.nb, HD) > lds) lds = lowres_lds(p.nb, HD);
+    const size_t lds = lgsel_lds<HD>(p.nb, p.mode);
     const int heads_per_xcd = (p.BH + 7) / 8;
     int grid = 8 * heads_per_xcd * (p.nb / kFusedRows);
     if (!kGiven && p.v_in_logits) grid += 8 * heads_per_xcd * v_direct_groups(p.nb, HD);
@@ -1992,10 +1998,40 @@ static hipError_t launch_lgsel_t(const Params& p, hipStream_t s) {
     return hipGetLastError();
 }
 
-bool fused_select(int nb) { return row_tiled(nb); }
+// Whether heads of nb block rows take the one-launch logits and selection:
+// heads of 64 or 128 block rows, and every logits workgroup of the launch
+// resident on the device at once (its occupancy times the CU count).  The
+// workgroups of a head wait for one another, and the low-res ones for the V
+// workgroups after all logits workgroups; with every logits workgroup
+// resident, the V workgroups get the CUs that the logits-only and selecting
+// workgroups free, so every wait ends.  Larger grids take the separate
+// logits and selection launches.
+bool fused_select(int BH, int nb, int d, int mode) {
+    if (!row_tiled(nb) || (d != 64 && d != 128)) return false;
+    static int cap[64][2][2] = {};   // resident workgroups per device, head size and mode
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+    int& c = cap[dev][d == 128][mode == 0];
+    if (c == 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            return false;
+        // the LDS of the larger head size of rows (128) bounds both
+        const hipError_t e =
+            d == 128 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                           &per_cu, reinterpret_cast<const void*>(&lgsel_kernel<false, 128>), kSelThreads,
+                           lgsel_lds<128>(128, mode))
+                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                           &per_cu, reinterpret_cast<const void*>(&lgsel_kernel<false, 64>), kSelThreads,
+                           lgsel_lds<64>(128, mode));
+        if (e != hipSuccess || per_cu <= 0) return false;
+        c = per_cu * cus;
+    }
+    return 8 * ((BH + 7) / 8) * (nb / kFusedRows) <= c;
+}
 
 hipError_t launch_select(const Params& p, hipStream_t s) {
-    if (row_tiled(p.nb)) {
+    if (fused_select(p.BH, p.nb, p.d, p.mode)) {
         if (p.logits_given) return p.d == 128 ? launch_lgsel_t<true, 128>(p, s) : launch_lgsel_t<true, 64>(p, s);
         return p.d == 128 ? launch_lgsel_t<false, 128>(p, s) : launch_lgsel_t<false, 64>(p, s);
     }

@@ -253,9 +253,10 @@ mra_status mra_debug_stages(const mra_dims* dims, const void* q, const void* k, 
  * MRA_DEVERR_WAIT in the workspace's error word (read it with
  * mra_workspace_error) and the workgroup goes on, so the launch ends however
  * the device schedules it.  The selection it leaves is not meant for use.
- * Callers: tests of the error path.  Returns MRA_ERR_SEQ_LEN for other
- * sequence lengths, MRA_ERR_STAGE for polls out of range, otherwise as
- * mra_debug_stages. */
+ * Callers: tests of the error path.  Returns MRA_ERR_STAGE for polls out of
+ * range, MRA_ERR_SEQ_LEN for other sequence lengths or for sizes that take
+ * the separate logits and selection launches (more heads than the device
+ * holds at once, or no device), otherwise as mra_debug_stages. */
 mra_status mra_debug_wait_timeout(const mra_dims* dims, const void* q, const void* k, const void* v,
                                   int32_t block_per_row, int32_t approx_mode, uint32_t polls, void* workspace,
                                   size_t workspace_bytes, void* stream);

@@ -149,7 +149,8 @@ def test_debug_wait_timeout_rejects_bad_arguments():
     assert L.mra_debug_wait_timeout(ctypes.byref(d), Q, K, V, 4, 0, 0, W, 1 << 40, None) == 13
     assert L.mra_debug_wait_timeout(ctypes.byref(d), Q, K, V, 4, 0, (1 << 16) + 1, W, 1 << 40, None) == 13
     # only heads of 64 or 128 block rows form logits and select in one launch
-    for n in (1024, 8192):
+    # (and without a device no size does)
+    for n in (1024, 8192, 4096):
         d = mra._Dims(1, 2, n, 64, 1)
         assert L.mra_debug_wait_timeout(ctypes.byref(d), Q, K, V, 4, 0, 8, W, 1 << 40, None) == 3
 

@@ -453,3 +453,31 @@ def test_selector_wait_runs_out_and_is_flagged(mra, N, mode):
     ref = mra.attention(q, k, v, None, block_per_row=2, approx_mode=mode)
     torch.cuda.synchronize()
     assert torch.equal(out, ref)
+
+
+@pytest.mark.parametrize("mode", ["full", "sparse"])
+def test_many_heads_match_per_batch_calls(mra, mode):
+    # 64 heads at N = 4096: more logits workgroups than the device holds at
+    # once, so the call takes the separate logits and selection launches,
+    # while one batch row (16 heads) takes the one-launch path.  Every head's
+    # pooled means, logits and selection depend on that head alone, so both
+    # must agree bit for bit; the outputs agree within the bf16 output
+    # tolerance (the attention's work split, and so its summation order,
+    # follows the number of heads).  No call may flag an error.
+    B, H, N = 4, 16, 4096
+    w = small("many-heads-" + mode, B, H, N, seed=12, approx_mode=mode)
+    q, k, v = dev(w, "q"), dev(w, "k"), dev(w, "v")
+    print("case many heads", B, H, N, mode, flush=True)
+    ws = torch.empty(mra.workspace_size(B, H, N, 64, q.dtype, 4, mode), dtype=torch.uint8, device="cuda")
+    out = mra.attention(q, k, v, None, block_per_row=4, approx_mode=mode, workspace=ws)
+    assert mra.workspace_error(ws) == 0
+    st = mra.debug_stages(q, k, v, None, block_per_row=4, approx_mode=mode)
+    for b in range(B):
+        qb, kb, vb = q[b:b + 1].contiguous(), k[b:b + 1].contiguous(), v[b:b + 1].contiguous()
+        ob = mra.attention(qb, kb, vb, None, block_per_row=4, approx_mode=mode)
+        sb = mra.debug_stages(qb, kb, vb, None, block_per_row=4, approx_mode=mode)
+        torch.cuda.synchronize()
+        assert int(sb["error"].item()) == 0 and int(st["error"].item()) == 0
+        for name in ("logits", "rowmax", "sel"):
+            assert torch.equal(st[name][b:b + 1], sb[name]), (b, name)
+        assert torch.allclose(out[b:b + 1].float(), ob.float(), atol=2e-2, rtol=2e-2), b
