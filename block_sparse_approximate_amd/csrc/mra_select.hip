@@ -28,11 +28,13 @@
 // flight), and wave w's cells of a tile are 64 consecutive cells, so one
 // ballot is 64 consecutive bits of the selection.
 //
-// lgsel_kernel: for heads of 64 or 128 block rows (N = 2048, 4096) the
+// lgsel_kernel: for heads of 64 or 128 block rows (N = 2048, 4096), when
+// all of its logits workgroups fit the device at once (fused_select), the
 // logits and the selection run in one launch: the head's workgroups form 16
 // block rows of logits each, add one to the head's arrival count, and the
-// first nb / 32 of them wait for the count and select 32 rows each as
-// select_kernel's row tiles do (see the comment above lgsel_kernel).
+// first nb / 32 of them wait for the count and select 32 rows each
+// (select_rows; see the comment above lgsel_kernel).  Otherwise the
+// separate logits_kernel and select_kernel launches below run.
 //
 // premark_kernel: for heads longer than one tile (with nb a multiple of 64)
 // the marking pass runs before the selector, one workgroup per tile, so the
