@@ -1571,10 +1571,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
 // each (lowres_rows); the others end after their logits.
 // What a workgroup stored is in its XCD's L2 once the stores have completed,
 // and the waiting workgroups, on the same XCD, have not read those lines
-// before, so plain loads see it.  An XCD starts its workgroups in slot order
-// and a head's workgroups have consecutive slots, so the heads that wait are
-// complete before later slots need their CUs.  The wait is bounded all the
-// same: after kWaitPolls polls the workgroup sets error bit 32 and goes on.
+// before, so plain loads see it.  The launch is used only when all of its
+// logits workgroups are resident at once (fused_select), so every workgroup
+// a head's workgroups wait for is running, and the V workgroups after them
+// get the CUs that logits-only and selecting workgroups free.  The wait is
+// bounded all the same: after kWaitPolls polls the workgroup sets error bit
+// 32 (MRA_DEVERR_WAIT) and goes on.
 constexpr int kFusedRows = kSelWaves;          // block rows per workgroup in the logits phase
 constexpr uint32_t kWaitPolls = 1u << 18;
 constexpr uint32_t kErrWait = 32u;
